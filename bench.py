@@ -1,0 +1,272 @@
+"""Benchmark of the TurboQuant decode hot path on one MI355X.
+
+One step = one pass of the whole path over the dense 28-layer workload
+(28 layers, 4 KV heads, 28 query heads (GQA 7), head_dim 128, batch 1,
+8192 cached tokens, K 4 bits = 3 Lloyd-Max + 1 QJL, V 4 bits MSE-only):
+  1. compress the step's new token (K and V, all 4 KV heads of all 28 layers,
+     one tq_compress_kv call) into slot 8191 of the packed cache;
+  2. decode attention for all 28 query heads of all 28 layers over the 8192
+     packed tokens (one tq_decode_attention call).
+Inputs are seeded synthetic bf16 K/V (per-channel log-normal scales, two
+outlier channels per head) already resident in HBM.  The timed loop rotates
+among enough cache copies to exceed twice the 256 MB Infinity Cache, so
+decode reads come from HBM.
+
+Prints one JSON line: metric / value (algorithmic GB/s of the step), the
+decode kernel's roofline, bulk-compression throughput, and the float64 CPU
+oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="w2")
+    p.add_argument("--copies", type=int, default=0, help="cache copies (0 = enough to exceed 2x the MALL)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--copy-probe", action="store_true", help="also run a plain copy of known size (PMC scaling)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import kv_cache_quantization_norm_amd as tq
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = wl.BY_SHORT[args.workload]
+    assert len(w.seq_lens) == 1 and not w.layer_modes, "the timed step covers single-sequence symmetric workloads"
+    L, H, HQ, T, D = w.n_layers, w.n_kv_heads, w.n_q_heads, w.seq_lens[0], w.head_dim
+    fmt = tq.make_format(D, w.k_bits, w.v_bits)
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+    stream = torch.cuda.current_stream()
+
+    # ---------------- setup: tables, inputs, bulk compression of the cache
+    t0 = time.time()
+    tables = tq.Tables.create(fmt, list(range(L)), dev)
+    K = torch.empty((L, T, H, D), dtype=dt, device=dev)
+    V = torch.empty_like(K)
+    for layer in range(L):
+        k, v = wl.gen_kv(w, layer)
+        K[layer].copy_(torch.from_numpy(k).to(dt))
+        V[layer].copy_(torch.from_numpy(v).to(dt))
+    Q = torch.from_numpy(np.stack([wl.gen_q(w, layer) for layer in range(L)])).to(dev).contiguous()
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+    cap = (T + 31) // 32 * 32
+    base = tq.Cache.allocate(fmt, L, H, cap, dev)
+    # Bulk compression of the whole 28-layer prefill, timed.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tq.tq_compress_kv(fmt, tables, base, K, V, slot0=0)  # warm
+    torch.cuda.synchronize()
+    reps = 5
+    ev0.record(stream)
+    for _ in range(reps):
+        tq.tq_compress_kv(fmt, tables, base, K, V, slot0=0)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    bulk_ms = ev0.elapsed_time(ev1) / reps
+    cache_bytes = base.nbytes()
+    n_copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / cache_bytes) + 1)
+    caches = [base] + [tq.Cache(fmt, L, H, cap, {k: (None if t is None else t.clone()) for k, t in base.planes.items()})
+                       for _ in range(n_copies - 1)]
+    log(f"cache {cache_bytes / 1e6:.1f} MB x {n_copies} copies; bulk compress {bulk_ms:.3f} ms")
+
+    # the step's new token: token T-1 of every layer
+    k_new = K[:, T - 1:T].contiguous()
+    v_new = V[:, T - 1:T].contiguous()
+    seq_start = torch.zeros(1, dtype=torch.int64, device=dev)
+    seq_len = torch.full((1,), T, dtype=torch.int32, device=dev)
+    ws = tq.workspace_for(fmt, base, 1, HQ, T, dev)
+    out = torch.empty((L, 1, HQ, D), device=dev)
+
+    def step(c):
+        tq.tq_compress_kv(fmt, tables, c, k_new, v_new, slot0=T - 1, stream=stream)
+        tq.tq_decode_attention(fmt, tables, c, Q, seq_start, seq_len, T, out, ws, stream=stream)
+
+    def decode_only(c):
+        tq.tq_decode_attention(fmt, tables, c, Q, seq_start, seq_len, T, out, ws, stream=stream)
+
+    # ---------------- timed steps
+    for i in range(args.warmup):
+        step(caches[i % n_copies])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(caches[i % n_copies])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = e0.elapsed_time(e1) / args.steps
+
+    # decode call alone (query prep + fused decode/combine kernel), same rotation
+    for i in range(args.warmup):
+        decode_only(caches[i % n_copies])
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        decode_only(caches[i % n_copies])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    decode_ms = e0.elapsed_time(e1) / args.steps
+
+    # per-layer calls (as a model would issue them): 28 decode calls of one layer
+    per_layer = [tq.Cache(fmt, 1, H, cap, {k: (None if t is None else t.view(L, -1)[l])
+                                           for k, t in base.planes.items()}) for l in range(L)]
+    layer_tables = []
+    for l in range(L):
+        lt = tq.Tables(fmt, tables.pi[l:l + 1], tables.s[l:l + 1], tables.pi_s[l:l + 1], tables.k_centroids,
+                       tables.k_boundaries, tables.v_centroids, tables.v_boundaries, {})
+        layer_tables.append(lt)
+    ws1 = tq.workspace_for(fmt, per_layer[0], 1, HQ, T, dev)
+    q_l = [Q[l:l + 1].contiguous() for l in range(L)]
+    out_l = torch.empty((1, 1, HQ, D), device=dev)
+    for _ in range(3):
+        for l in range(L):
+            tq.tq_decode_attention(fmt, layer_tables[l], per_layer[l], q_l[l], seq_start, seq_len, T, out_l, ws1,
+                                   stream=stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    nrep = 10
+    for _ in range(nrep):
+        for l in range(L):
+            tq.tq_decode_attention(fmt, layer_tables[l], per_layer[l], q_l[l], seq_start, seq_len, T, out_l, ws1,
+                                   stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_layer_ms = e0.elapsed_time(e1) / nrep
+
+    # ---------------- algorithmic bytes
+    k_rec = D * (w.k_bits - 1) // 8 + D // 8 + 8
+    v_rec = D * w.v_bits // 8 + 4
+    records = L * H * T * (k_rec + v_rec)
+    tables_bytes = L * 3 * D * D * 4            # Pi, S and S Pi^T, read once per step
+    qo = 2 * L * HQ * D * 4
+    new_tok = L * H * 2 * D * (2 if dt != torch.float32 else 4) + L * H * (k_rec + v_rec)
+    step_bytes = records + qo + tables_bytes + new_tok
+    decode_bytes = records + qo + L * 2 * D * D * 4   # Pi and S
+    step_gbs = step_bytes / (step_ms * 1e-3) / 1e9
+    decode_gbs = decode_bytes / (decode_ms * 1e-3) / 1e9
+    bulk_tokens = L * T
+    result = {
+        "metric": "decode-attention GB/s & % HBM roofline; compress Mtokens/s per KV head",
+        "value": round(step_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (MFMA f16 hi+lo operands, f32 accumulation)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": L, "kv_heads": H, "q_heads": HQ, "head_dim": D,
+                   "batch": 1, "cached_tokens": T, "k_bits": w.k_bits, "v_bits": w.v_bits,
+                   "kv_dtype": w.dtype, "layers_per_call": L, "cache_copies": n_copies,
+                   "step": "append-compress 1 token x 28 layers + decode attention x 28 layers"},
+        "roofline": {"bound": "hbm", "achieved": round(decode_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(decode_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel<3,4> (timed call = qprep_kernel + decode_kernel)",
+                     "bytes_per_launch": decode_bytes, "us_per_launch": round(decode_ms * 1e3, 2)},
+        "decode_step_bytes": step_bytes,
+        "per_layer_calls": {"us_per_step": round(per_layer_ms * 1e3, 2),
+                            "GBs": round(decode_bytes / (per_layer_ms * 1e-3) / 1e9, 1)},
+        "compress": {"what": f"bulk prefill {T} tokens x {L} layers x {H} KV heads, one call",
+                     "ms": round(bulk_ms, 4),
+                     "mtokens_per_s_per_kv_head": round(bulk_tokens / (bulk_ms * 1e-3) / 1e6, 2),
+                     "mtoken_heads_per_s": round(bulk_tokens * H / (bulk_ms * 1e-3) / 1e6, 2)},
+        "wall_s_timed": round(wall, 4),
+    }
+
+    if args.copy_probe:
+        n = 1 << 28  # 1 GiB of float32 read + 1 GiB written
+        a = torch.empty(n, device=dev)
+        b = torch.empty(n, device=dev)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = 2 * n * 4
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, result)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, budget_s, gpu_result):
+    """The float64 oracle decoding a bounded sample of the same workload:
+    whole layers (all KV and query heads, all 8192 tokens), oracle-compressed
+    first (untimed), until about budget_s seconds of decode work."""
+    import workloads as wl
+    from oracle import attention, codebook, quant, rotation
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    fmt = quant.Format(w.head_dim, w.k_bits, w.v_bits)
+    cbk = codebook.codebook(w.head_dim, fmt.k_mse_bits)
+    cbv = codebook.codebook(w.head_dim, fmt.v_bits)
+    T = w.seq_lens[0]
+    cap = (T + 31) // 32 * 32
+    k_rec = fmt.k_record_bytes()
+    v_rec = fmt.v_record_bytes()
+    dec_s = comp_s = 0.0
+    layers = 0
+    tok_heads = 0
+    for layer in range(w.n_layers):
+        pi, s = rotation.layer_rotations(w.head_dim, layer)
+        k, v = wl.gen_kv(w, layer)
+        cache = quant.empty_cache(fmt, w.n_kv_heads, cap)
+        t0 = time.perf_counter()
+        quant.compress_into(cache, k.astype(np.float64), v.astype(np.float64), np.arange(T), pi, s, cbk, cbv)
+        comp_s += time.perf_counter() - t0
+        q = wl.gen_q(w, layer)
+        t0 = time.perf_counter()
+        attention.decode_attention(cache, q, [0], [T], pi, s, cbk, cbv)
+        dec_s += time.perf_counter() - t0
+        layers += 1
+        tok_heads += T * w.n_kv_heads
+        log(f"cpu oracle layer {layer}: decode {dec_s:.1f}s compress {comp_s:.1f}s")
+        if dec_s >= budget_s:
+            break
+    bytes_ = layers * w.n_kv_heads * T * (k_rec + v_rec) + 2 * layers * w.n_q_heads * w.head_dim * 4 \
+        + layers * 2 * w.head_dim * w.head_dim * 4
+    return {"value": round(bytes_ / dec_s / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{layers} of {w.n_layers} layers, full 8192-token cache, all heads (decode only, "
+                      f"{dec_s:.1f}s); oracle compression of the same sample {comp_s:.1f}s = "
+                      f"{tok_heads / comp_s / 1e6:.4f} Mtoken-heads/s",
+            "compress_mtoken_heads_per_s": round(tok_heads / comp_s / 1e6, 5)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * tq.h - C ABI of the TurboQuant KV-cache library for AMD MI355X (gfx950).
+ *
+ * What the library computes (page titles and sections of the TurboQuant pages):
+ *   "TurboQuant QJL投影深度剖析" (QJL deep-dive), section 2: a key x is stored as
+ *   ||x||, the (b-1)-bit Lloyd-Max codes of the rotated unit vector Pi x/||x||,
+ *   the signs of S r for the residual r = x - x~ (d bits in d/8 bytes) and ||r||.
+ *   Section 5: the record is (codes, sign bytes, ||r||, ||x||), bit-packed, and
+ *   <q, x~> + ||r|| sqrt(pi/2)/d <S q, signs> estimates <q, x> without bias.
+ *   Section 6: scores use the forward-rotated query Pi q against the centroids
+ *   and the pre-sketched query S q against the signs; decode attention runs an
+ *   online softmax over the whole packed cache in one pass; each layer seeds
+ *   its own Pi/S with 42 + 7 * layer.
+ *   "TurboQuant MLX port" write-up (cf-1.com), 背景: values use the MSE-only
+ *   path (codes + ||v||); 直接构造缓存: key_bits = 0 keeps K in fp16.
+ *
+ * Conventions shared by every call
+ *   - d (head_dim) is 128 for the device calls.
+ *   - All device pointers are plain device (HBM) addresses owned by the
+ *     caller; the library never allocates, frees or retains device memory and
+ *     keeps no mutable global state, so calls on different streams may run
+ *     concurrently.  `stream` is a hipStream_t (NULL = the default stream).
+ *   - Device calls validate their host-side arguments synchronously and
+ *     return a status; kernels are then enqueued on `stream` and never trap.
+ *     TQ_ERR_HIP reports a failed launch.  tq_last_error() gives a
+ *     thread-local message for the last failing call.  No C++ exception
+ *     crosses this boundary.
+ *   - NaN inputs propagate to the affected norms and outputs; a zero vector
+ *     compresses to zero norms and contributes nothing.
+ *
+ * Packed cache layout (one set of planes for n_layers layers, each plane laid
+ * out [layer][kv_head][...]; capacity is a multiple of 32 slots):
+ *   k_idx   uint8  [L][H][capacity][d*(k_bits-1)/8]  LSB-first codes, coord j at
+ *                                                      bits [j*m, (j+1)*m), m = k_bits-1
+ *   k_sign  uint8  [L][H][capacity][d/8]             bit j = (S r)_j >= 0
+ *   k_norm  float  [L][H][capacity]                  ||x||
+ *   k_rnorm float  [L][H][capacity]                  ||r||
+ *   k_f16   half   [L][H][capacity][d]               keys kept in fp16 (k_bits = 0)
+ *   v_idx   uint8  [L][H][capacity/32][d][4*v_bits]  per 32-slot block and coord j,
+ *                                                      slot p of the block at bits
+ *                                                      [p*v_bits, (p+1)*v_bits)
+ *   v_norm  float  [L][H][capacity]                  ||v||
+ *   v_f16   half   [L][H][capacity/32][d][32]        values kept in fp16 (v_bits = 0)
+ * Planes that a format does not use may be NULL.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t tq_status;
+enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad layout */
+  TQ_ERR_UNSUPPORTED = 2, /* d != 128 on device, bit width out of range */
+  TQ_ERR_WORKSPACE = 3,   /* workspace too small */
+  TQ_ERR_HIP = 4          /* a HIP launch failed */
+};
+
+enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_BF16 = 1, TQ_DTYPE_F16 = 2 };
+
+/* Storage format.  k_bits: 0 keeps keys in fp16, else 2..5 total bits per
+ * coordinate = (k_bits-1) Lloyd-Max bits + 1 QJL sign bit.  v_bits: 0 keeps
+ * values in fp16, else 1, 2 or 4 MSE-only bits. */
+typedef struct tq_format {
+  int32_t d;
+  int32_t k_bits;
+  int32_t v_bits;
+} tq_format;
+
+/* Per-layer tables in device memory (fp32).  pi, s and pi_s hold n_layers
+ * consecutive row-major d x d matrices (layer l at offset l*d*d): the rotation
+ * Pi (y = Pi x), the QJL sketch S and their product M = S Pi^T, as written by
+ * tq_make_rotations.  Codebooks are shared by all layers: 2^m ascending
+ * centroids and 2^m - 1 boundaries for the key (m = k_bits-1) and value
+ * (m = v_bits) quantisers, as written by tq_make_codebook (rounded to fp32). */
+typedef struct tq_tables {
+  const float* pi;
+  const float* s;
+  const float* pi_s;
+  const float* k_centroids;
+  const float* k_boundaries;
+  const float* v_centroids;
+  const float* v_boundaries;
+} tq_tables;
+
+/* Device planes of a packed cache (layout above). */
+typedef struct tq_cache {
+  int32_t n_layers;
+  int32_t n_kv_heads;
+  int64_t capacity;
+  uint8_t* k_idx;
+  uint8_t* k_sign;
+  float* k_norm;
+  float* k_rnorm;
+  void* k_f16;
+  uint8_t* v_idx;
+  float* v_norm;
+  void* v_f16;
+} tq_cache;
+
+/* Seed of a layer's Pi/S stream: 42 + 7 * layer (QJL deep-dive, section 6). */
+uint64_t tq_layer_seed(int32_t layer);
+
+/* Host.  Builds Pi (Haar orthogonal: Q * diag(sign R_ii) of the Householder
+ * QR of a d x d matrix of normals 0..d*d-1) and S (normals d*d..2*d*d-1), both
+ * from the SplitMix64 + Box-Muller stream of `seed` (QJL deep-dive, section 2
+ * steps 1 and 3), and optionally M = S Pi^T, computed in double from the fp32
+ * Pi and S.  Outputs are fp32 row-major d x d in caller-owned host memory;
+ * pi_s may be NULL.  3 <= d <= 1024.  Deterministic. */
+tq_status tq_make_rotations(int32_t d, uint64_t seed, float* pi, float* s, float* pi_s);
+
+/* Host.  Lloyd-Max quantiser (QJL deep-dive, section 2 step 2) for one
+ * coordinate of a uniformly random unit vector in R^d, density
+ * Gamma(d/2)/(sqrt(pi) Gamma((d-1)/2)) (1-t^2)^((d-3)/2) on [-1, 1].
+ * Writes 2^bits ascending centroids and 2^bits - 1 boundaries (midpoints) in
+ * double to caller-owned host arrays.  1 <= bits <= 8, 3 <= d <= 65536. */
+tq_status tq_make_codebook(int32_t d, int32_t bits, double* centroids, double* boundaries);
+
+/* Byte sizes of the eight cache planes for a format, in the order
+ * k_idx, k_sign, k_norm, k_rnorm, k_f16, v_idx, v_norm, v_f16 (0 = unused). */
+tq_status tq_cache_plane_bytes(const tq_format* fmt, int32_t n_layers, int32_t n_kv_heads,
+                               int64_t capacity, size_t out_bytes[8]);
+
+/* Workspace bytes tq_decode_attention and tq_score need for these sizes
+ * (0 on invalid input). */
+size_t tq_decode_workspace_bytes(const tq_format* fmt, int32_t n_layers, int32_t batch,
+                                 int32_t n_kv_heads, int32_t n_q_heads, int64_t max_seq_len);
+
+/* Device.  Compresses keys and values and writes them into the cache
+ * (QJL deep-dive, section 2; MLX write-up, 背景).  k and v are device arrays
+ * [n_layers][n_tokens][n_kv_heads][d] of `dtype` (TQ_DTYPE_F32/BF16/F16) for
+ * cache layers layer0 .. layer0+n_layers-1.  Token i goes to slot
+ * slots[i] (device int64 array, same for every layer) or, when slots is
+ * NULL, to slot0 + i.  Slots must be distinct within one call and lie in
+ * [0, capacity); out-of-range slots are skipped by the kernel.  Records of
+ * other slots are left untouched.  Enqueued on `stream`. */
+tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                         const void* k, const void* v, int32_t dtype, int32_t layer0,
+                         int32_t n_layers, int64_t n_tokens, const int64_t* slots, int64_t slot0,
+                         void* stream);
+
+/* Device.  Single-query decode attention over the packed cache for every
+ * layer of the cache (QJL deep-dive, sections 5 and 6): for query head h
+ * (KV head h / (n_q_heads / n_kv_heads)), logits
+ *   l_t = scale * (||x_t|| <Pi q, c[idx_t]> + ||r_t|| sqrt(pi/2)/d <S q, 2 s_t - 1>)
+ * (scale * <q, k_t> for fp16 keys), softmax over the sequence's tokens and
+ * out = sum_t p_t v~_t with v~_t = ||v_t|| Pi^T c_v[idx_t] (fp16 values as
+ * stored).  q and out are device float [n_layers][batch][n_q_heads][d].
+ * seq_start (int64) and seq_len (int32) are device arrays [batch]: sequence
+ * b occupies slots [seq_start[b], seq_start[b] + seq_len[b]); seq_start must
+ * be a multiple of 32; the kernels clamp a sequence to the capacity and to max_seq_len and treat
+ * a misaligned or negative start as empty.  An empty sequence gives a zero
+ * output row.  max_seq_len (host) bounds every seq_len and sizes the token
+ * split.  scale = 0 means 1/sqrt(d).  n_q_heads must be a multiple of
+ * n_kv_heads.  workspace: device scratch of at least
+ * tq_decode_workspace_bytes(...) bytes; enqueued on `stream`. */
+tq_status tq_decode_attention(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                              const float* q, int32_t batch, int32_t n_q_heads,
+                              const int64_t* seq_start, const int32_t* seq_len,
+                              int64_t max_seq_len, float scale, float* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Device.  The scoring half of tq_decode_attention alone (the pages' separate
+ * MSE-score and QJL-score kernels, QJL deep-dive section 6): writes the
+ * logits l_t defined above to logits[n_layers][batch][n_q_heads][max_seq_len]
+ * (device float; entries at t >= seq_len[b] are left untouched).  Same
+ * arguments and workspace as tq_decode_attention. */
+tq_status tq_score(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                   const float* q, int32_t batch, int32_t n_q_heads, const int64_t* seq_start,
+                   const int32_t* seq_len, int64_t max_seq_len, float scale, float* logits,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* tq_status_string(tq_status status);
+
+/* Thread-local detail message of the last failing call on this thread ("" if
+ * none). */
+const char* tq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

@@ -1,0 +1,298 @@
+"""Python binding of libtq, the TurboQuant KV-cache library for MI355X.
+
+Argument marshalling only: every step of compression and decode attention
+runs in libtq's HIP kernels (or, for the table generators, its host C++).
+PyTorch supplies device memory and the current stream.  The entry points
+keep the C names (tq_make_rotations, tq_make_codebook, tq_compress_kv,
+tq_decode_attention, tq_score, ...); `Tables` and `Cache` allocate the device
+arrays those calls take.
+
+Importing this package fails loudly if libtq.so has not been built; there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = range(5)
+TQ_DTYPE_F32, TQ_DTYPE_BF16, TQ_DTYPE_F16 = 0, 1, 2
+VBLOCK = 32
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str):
+        super().__init__(f"{what}: {status_name(status)}: {detail}")
+        self.status = status
+
+
+class tq_format(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32)]
+
+
+class tq_tables(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("pi", "s", "pi_s", "k_centroids", "k_boundaries", "v_centroids", "v_boundaries")]
+
+
+class tq_cache(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("capacity", ctypes.c_int64)] + \
+               [(n, ctypes.c_void_p) for n in
+                ("k_idx", "k_sign", "k_norm", "k_rnorm", "k_f16", "v_idx", "v_norm", "v_f16")]
+
+
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"libtq.so is not built ({path}); run __graft_entry__.build() or "
+                          "python -m kv_cache_quantization_norm_amd.build")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    fmtp = ctypes.POINTER(tq_format)
+    tabp = ctypes.POINTER(tq_tables)
+    cachep = ctypes.POINTER(tq_cache)
+    sig = {
+        "tq_layer_seed": (ctypes.c_uint64, [I32]),
+        "tq_make_rotations": (I32, [I32, ctypes.c_uint64, P, P, P]),
+        "tq_make_codebook": (I32, [I32, I32, P, P]),
+        "tq_cache_plane_bytes": (I32, [fmtp, I32, I32, I64, P]),
+        "tq_decode_workspace_bytes": (SZ, [fmtp, I32, I32, I32, I32, I64]),
+        "tq_compress_kv": (I32, [fmtp, tabp, cachep, P, P, I32, I32, I32, I64, P, I64, P]),
+        "tq_decode_attention": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P, SZ, P]),
+        "tq_score": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P, SZ, P]),
+        "tq_status_string": (ctypes.c_char_p, [I32]),
+        "tq_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("tq_layer_seed", "tq_make_rotations", "tq_make_codebook", "tq_cache_plane_bytes",
+            "tq_decode_workspace_bytes", "tq_compress_kv", "tq_decode_attention", "tq_score",
+            "tq_status_string", "tq_last_error")
+
+
+def status_name(st: int) -> str:
+    return _lib.tq_status_string(st).decode()
+
+
+def _check(st: int, what: str):
+    if st != TQ_OK:
+        raise TQError(st, what, _lib.tq_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ----------------------------------------------------------------------------
+# Host calls
+
+
+def tq_layer_seed(layer: int) -> int:
+    return int(_lib.tq_layer_seed(layer))
+
+
+def tq_make_rotations(d: int, seed: int, with_pi_s: bool = True):
+    """Returns (pi, s, pi_s) as float32 numpy arrays [d, d] (pi_s None if not asked)."""
+    pi = np.empty((d, d), np.float32)
+    s = np.empty((d, d), np.float32)
+    m = np.empty((d, d), np.float32) if with_pi_s else None
+    _check(_lib.tq_make_rotations(d, seed, pi.ctypes.data, s.ctypes.data, m.ctypes.data if m is not None else None),
+           "tq_make_rotations")
+    return pi, s, m
+
+
+def tq_make_codebook(d: int, bits: int):
+    """Returns (centroids [2^bits], boundaries [2^bits - 1]) float64."""
+    c = np.empty(1 << bits, np.float64)
+    t = np.empty(max(1, (1 << bits) - 1), np.float64)
+    _check(_lib.tq_make_codebook(d, bits, c.ctypes.data, t.ctypes.data), "tq_make_codebook")
+    return c, t[: (1 << bits) - 1]
+
+
+def make_format(d: int = 128, k_bits: int = 4, v_bits: int = 4) -> tq_format:
+    return tq_format(d, k_bits, v_bits)
+
+
+PLANES = ("k_idx", "k_sign", "k_norm", "k_rnorm", "k_f16", "v_idx", "v_norm", "v_f16")
+
+
+def tq_cache_plane_bytes(fmt: tq_format, n_layers: int, n_kv_heads: int, capacity: int) -> List[int]:
+    out = (ctypes.c_size_t * 8)()
+    _check(_lib.tq_cache_plane_bytes(ctypes.byref(fmt), n_layers, n_kv_heads, capacity, out),
+           "tq_cache_plane_bytes")
+    return list(out)
+
+
+def tq_decode_workspace_bytes(fmt: tq_format, n_layers: int, batch: int, n_kv_heads: int, n_q_heads: int,
+                              max_seq_len: int) -> int:
+    return int(_lib.tq_decode_workspace_bytes(ctypes.byref(fmt), n_layers, batch, n_kv_heads, n_q_heads,
+                                              max_seq_len))
+
+
+# ----------------------------------------------------------------------------
+# Device arrays
+
+
+@dataclass
+class Tables:
+    """Device tables for n_layers layers: Pi, S, S Pi^T per layer (fp32) and the
+    key / value codebooks (fp32)."""
+    fmt: tq_format
+    pi: object
+    s: object
+    pi_s: object
+    k_centroids: object
+    k_boundaries: object
+    v_centroids: object
+    v_boundaries: object
+    host: dict
+
+    @classmethod
+    def create(cls, fmt: tq_format, layers: Sequence[int], device="cuda"):
+        import torch
+        d = fmt.d
+        pis, ss, ms = [], [], []
+        for layer in layers:
+            pi, s, m = tq_make_rotations(d, tq_layer_seed(layer))
+            pis.append(pi)
+            ss.append(s)
+            ms.append(m)
+        host = dict(pi=np.stack(pis), s=np.stack(ss), pi_s=np.stack(ms))
+        dev = {k: torch.from_numpy(v).to(device) for k, v in host.items()}
+
+        def cb(bits):
+            if bits <= 0:
+                return None, None
+            c, t = tq_make_codebook(d, bits)
+            host[f"c{bits}"] = (c, t)
+            return (torch.from_numpy(c.astype(np.float32)).to(device),
+                    torch.from_numpy(t.astype(np.float32)).to(device) if len(t) else
+                    torch.zeros(1, dtype=torch.float32, device=device))
+
+        kc, kb = cb(fmt.k_bits - 1 if fmt.k_bits > 0 else 0)
+        vc, vb = cb(fmt.v_bits)
+        return cls(fmt, dev["pi"], dev["s"], dev["pi_s"], kc, kb, vc, vb, host)
+
+    def struct(self) -> tq_tables:
+        return tq_tables(*[_ptr(x) for x in (self.pi, self.s, self.pi_s, self.k_centroids, self.k_boundaries,
+                                             self.v_centroids, self.v_boundaries)])
+
+
+@dataclass
+class Cache:
+    """Zero-initialised device planes of a packed cache."""
+    fmt: tq_format
+    n_layers: int
+    n_kv_heads: int
+    capacity: int
+    planes: dict
+
+    @classmethod
+    def allocate(cls, fmt: tq_format, n_layers: int, n_kv_heads: int, capacity: int, device="cuda"):
+        import torch
+        sizes = tq_cache_plane_bytes(fmt, n_layers, n_kv_heads, capacity)
+        planes = {}
+        for name, nbytes in zip(PLANES, sizes):
+            if nbytes == 0:
+                planes[name] = None
+                continue
+            if name in ("k_norm", "k_rnorm", "v_norm"):
+                planes[name] = torch.zeros(nbytes // 4, dtype=torch.float32, device=device)
+            elif name in ("k_f16", "v_f16"):
+                planes[name] = torch.zeros(nbytes // 2, dtype=torch.float16, device=device)
+            else:
+                planes[name] = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        return cls(fmt, n_layers, n_kv_heads, capacity, planes)
+
+    def struct(self) -> tq_cache:
+        return tq_cache(self.n_layers, self.n_kv_heads, self.capacity,
+                        *[_ptr(self.planes[n]) for n in PLANES])
+
+    def nbytes(self) -> int:
+        return sum(p.numel() * p.element_size() for p in self.planes.values() if p is not None)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.float32: TQ_DTYPE_F32, torch.bfloat16: TQ_DTYPE_BF16, torch.float16: TQ_DTYPE_F16}[t.dtype]
+
+
+# ----------------------------------------------------------------------------
+# Device calls
+
+
+def tq_compress_kv(fmt: tq_format, tables: Tables, cache: Cache, k, v, layer0: int = 0, slots=None,
+                   slot0: int = 0, stream=None):
+    """k, v: contiguous device tensors [n_layers][n_tokens][n_kv_heads][d]
+    (float32, bfloat16 or float16); slots: optional device int64 [n_tokens]."""
+    assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape and k.dtype == v.dtype
+    n_layers, n_tokens = int(k.shape[0]), int(k.shape[1])
+    tb, cs = tables.struct(), cache.struct()
+    _check(_lib.tq_compress_kv(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(k), _ptr(v),
+                               _dtype_code(k), layer0, n_layers, n_tokens, _ptr(slots), slot0, _stream(stream)),
+           "tq_compress_kv")
+
+
+def workspace_for(fmt: tq_format, cache: Cache, batch: int, n_q_heads: int, max_seq_len: int, device="cuda"):
+    import torch
+    nbytes = tq_decode_workspace_bytes(fmt, cache.n_layers, batch, cache.n_kv_heads, n_q_heads, max_seq_len)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def tq_decode_attention(fmt: tq_format, tables: Tables, cache: Cache, q, seq_start, seq_len, max_seq_len: int,
+                        out, workspace, scale: float = 0.0, stream=None):
+    """q, out: device float32 [n_layers][batch][n_q_heads][d]; seq_start int64 and
+    seq_len int32 device tensors [batch]."""
+    n_layers, batch, hq, d = q.shape
+    assert n_layers == cache.n_layers and q.is_contiguous() and out.is_contiguous()
+    tb, cs = tables.struct(), cache.struct()
+    _check(_lib.tq_decode_attention(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(q), batch, hq,
+                                    _ptr(seq_start), _ptr(seq_len), max_seq_len, scale, _ptr(out), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)),
+           "tq_decode_attention")
+
+
+def tq_score(fmt: tq_format, tables: Tables, cache: Cache, q, seq_start, seq_len, max_seq_len: int, logits,
+             workspace, scale: float = 0.0, stream=None):
+    """logits: device float32 [n_layers][batch][n_q_heads][max_seq_len]."""
+    n_layers, batch, hq, d = q.shape
+    assert n_layers == cache.n_layers and q.is_contiguous() and logits.is_contiguous()
+    tb, cs = tables.struct(), cache.struct()
+    _check(_lib.tq_score(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(q), batch, hq,
+                         _ptr(seq_start), _ptr(seq_len), max_seq_len, scale, _ptr(logits), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(stream)),
+           "tq_score")
+
+
+def raw_call(name: str, *args):
+    """Calls a C entry point with raw arguments and returns its status (for
+    argument-validation tests)."""
+    return getattr(_lib, name)(*args)

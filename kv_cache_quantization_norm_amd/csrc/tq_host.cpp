@@ -1,0 +1,339 @@
+// Host half of libtq: the seeded Pi/S generator, the Lloyd-Max codebook
+// solver, plane and workspace sizing, status strings.
+//
+// Pages: "TurboQuant QJL投影深度剖析", section 2 (rotation from a QR
+// decomposition, Lloyd-Max codebook for the rotated-coordinate law, Gaussian
+// QJL sketch) and section 6 (seed 42 + 7 * layer per layer).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+namespace {
+thread_local char g_last_error[512] = "";
+}
+
+tq_status fail(tq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+tq_status check_format(const tq_format* f, bool device) {
+  if (!f) return fail(TQ_ERR_INVALID_ARG, "format is NULL");
+  if (f->d < 8 || f->d % 8 != 0) return fail(TQ_ERR_INVALID_ARG, "d=%d must be a positive multiple of 8", f->d);
+  if (f->k_bits < 0 || f->k_bits == 1 || f->k_bits > 5)
+    return fail(TQ_ERR_UNSUPPORTED, "k_bits=%d (0 for fp16 keys, else 2..5)", f->k_bits);
+  if (!(f->v_bits == 0 || f->v_bits == 1 || f->v_bits == 2 || f->v_bits == 4))
+    return fail(TQ_ERR_UNSUPPORTED, "v_bits=%d (0 for fp16 values, else 1, 2 or 4)", f->v_bits);
+  if (device && f->d != 128) return fail(TQ_ERR_UNSUPPORTED, "device kernels need d=128, got %d", f->d);
+  return TQ_OK;
+}
+
+SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_heads,
+                      int64_t max_seq_len) {
+  SplitPlan p;
+  const int group = n_q_heads / n_kv_heads;
+  p.n_head_groups = (group + kMaxGroup - 1) / kMaxGroup;
+  const int64_t wg_tokens = int64_t(kChunk) * kWaves;  // 128
+  const int64_t problems = int64_t(n_layers) * batch * n_kv_heads * p.n_head_groups;
+  const int64_t len = max_seq_len > 0 ? max_seq_len : 1;
+  // One resident round of workgroups (2 per CU at 2 waves per SIMD): as many
+  // splits per problem as fit, each at least one 128-token group.
+  int64_t splits = kResidentWorkgroups / problems;
+  if (splits < 1) splits = 1;
+  int64_t units = (len + splits * wg_tokens - 1) / (splits * wg_tokens);
+  if (units < 1) units = 1;
+  p.split_tokens = units * wg_tokens;
+  p.n_splits = (len + p.split_tokens - 1) / p.split_tokens;
+  auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
+  p.qprep_bytes = align(size_t(n_layers) * batch * n_q_heads * 2 * d * sizeof(float));
+  p.partial_bytes = align(size_t(n_layers) * batch * n_q_heads * p.n_splits * (d + 2) * sizeof(float));
+  p.total_bytes = p.qprep_bytes + p.partial_bytes;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// Seeded normal stream: SplitMix64 (Steele, Lea, Flood 2014) output n of seed
+// s is mix(s + (n+1) * 0x9E3779B97F4A7C15); a uniform is
+// ((z >> 11) + 0.5) * 2^-53; normal i = sqrt(-2 ln u_{2i}) cos(2 pi u_{2i+1})
+// (Box-Muller, cosine branch).
+namespace {
+
+inline uint64_t splitmix_at(uint64_t seed, uint64_t n) {
+  uint64_t z = seed + (n + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+inline double uniform_at(uint64_t seed, uint64_t n) {
+  return (double(splitmix_at(seed, n) >> 11) + 0.5) * 0x1.0p-53;
+}
+
+inline double normal_at(uint64_t seed, uint64_t i) {
+  const double u1 = uniform_at(seed, 2 * i);
+  const double u2 = uniform_at(seed, 2 * i + 1);
+  return std::sqrt(-2.0 * std::log(u1)) * std::cos(2.0 * M_PI * u2);
+}
+
+// Householder QR of the row-major n x n matrix a (overwritten by R); returns
+// Q explicitly in q (row-major).
+void householder_qr(int n, std::vector<double>& a, std::vector<double>& q) {
+  std::vector<double> vs(size_t(n) * n, 0.0);  // reflector k stored in row k (entries k..n-1)
+  std::vector<double> w(n);
+  for (int k = 0; k < n; ++k) {
+    double norm2 = 0.0;
+    for (int i = k; i < n; ++i) norm2 += a[size_t(i) * n + k] * a[size_t(i) * n + k];
+    const double norm = std::sqrt(norm2);
+    double* v = &vs[size_t(k) * n];
+    if (norm == 0.0) continue;
+    const double x0 = a[size_t(k) * n + k];
+    const double alpha = x0 >= 0 ? -norm : norm;  // reflect onto alpha e_k, no cancellation
+    for (int i = k; i < n; ++i) v[i] = a[size_t(i) * n + k];
+    v[k] -= alpha;
+    double vn2 = 0.0;
+    for (int i = k; i < n; ++i) vn2 += v[i] * v[i];
+    const double vn = std::sqrt(vn2);
+    if (vn == 0.0) continue;
+    for (int i = k; i < n; ++i) v[i] /= vn;
+    // A[k:, k:] -= 2 v (v^T A[k:, k:])
+    for (int j = k; j < n; ++j) {
+      double dot = 0.0;
+      for (int i = k; i < n; ++i) dot += v[i] * a[size_t(i) * n + j];
+      for (int i = k; i < n; ++i) a[size_t(i) * n + j] -= 2.0 * v[i] * dot;
+    }
+  }
+  // Q = H_0 H_1 ... H_{n-1}: apply the reflectors to I from the last one.
+  q.assign(size_t(n) * n, 0.0);
+  for (int i = 0; i < n; ++i) q[size_t(i) * n + i] = 1.0;
+  for (int k = n - 1; k >= 0; --k) {
+    const double* v = &vs[size_t(k) * n];
+    for (int j = 0; j < n; ++j) {
+      double dot = 0.0;
+      for (int i = k; i < n; ++i) dot += v[i] * q[size_t(i) * n + j];
+      if (dot == 0.0) continue;
+      for (int i = k; i < n; ++i) q[size_t(i) * n + j] -= 2.0 * v[i] * dot;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Coordinate law f_d(t) = C (1 - t^2)^((d-3)/2) and its Lloyd-Max quantiser.
+
+struct GaussLegendre {
+  std::vector<double> x, w;  // nodes / weights on [-1, 1]
+  explicit GaussLegendre(int n) : x(n), w(n) {
+    // Newton iteration on P_n from the Chebyshev-like first guess.
+    for (int i = 0; i < n; ++i) {
+      double z = std::cos(M_PI * (i + 0.75) / (n + 0.5));
+      double dp = 1.0;
+      for (int it = 0; it < 100; ++it) {
+        double p0 = 1.0, p1 = z;
+        for (int k = 2; k <= n; ++k) {
+          const double p2 = ((2.0 * k - 1.0) * z * p1 - (k - 1.0) * p0) / k;
+          p0 = p1;
+          p1 = p2;
+        }
+        dp = n * (z * p1 - p0) / (z * z - 1.0);
+        const double dz = p1 / dp;
+        z -= dz;
+        if (std::fabs(dz) < 1e-17) break;
+      }
+      double p0 = 1.0, p1 = z;
+      for (int k = 2; k <= n; ++k) {
+        const double p2 = ((2.0 * k - 1.0) * z * p1 - (k - 1.0) * p0) / k;
+        p0 = p1;
+        p1 = p2;
+      }
+      dp = n * (z * p1 - p0) / (z * z - 1.0);
+      x[i] = z;
+      w[i] = 2.0 / ((1.0 - z * z) * dp * dp);
+    }
+  }
+};
+
+struct CoordinateLaw {
+  int d;
+  double c;      // normalising constant
+  double e;      // exponent (d-3)/2
+  double scale;  // typical spread 1/sqrt(d)
+  GaussLegendre gl{24};
+
+  explicit CoordinateLaw(int d_) : d(d_) {
+    c = std::exp(std::lgamma(d / 2.0) - std::lgamma((d - 1) / 2.0)) / std::sqrt(M_PI);
+    e = (d - 3) / 2.0;
+    scale = 1.0 / std::sqrt(double(d));
+  }
+  double density(double t) const {
+    const double u = 1.0 - t * t;
+    return u <= 0.0 ? 0.0 : c * std::pow(u, e);
+  }
+  // int_0^t f (t may be negative), composite Gauss-Legendre on panels no
+  // wider than a quarter of the spread.
+  double mass_from_zero(double t) const {
+    if (t == 0.0) return 0.0;
+    const double sgn = t < 0 ? -1.0 : 1.0;
+    const double b = std::fmin(std::fabs(t), 1.0);
+    int panels = int(std::ceil(b / (0.25 * scale)));
+    if (panels < 1) panels = 1;
+    const double h = b / panels;
+    double sum = 0.0;
+    for (int p = 0; p < panels; ++p) {
+      const double a0 = p * h, mid = a0 + 0.5 * h;
+      double ps = 0.0;
+      for (size_t i = 0; i < gl.x.size(); ++i) ps += gl.w[i] * density(mid + 0.5 * h * gl.x[i]);
+      sum += 0.5 * h * ps;
+    }
+    return sgn * sum;
+  }
+  // Closed-form first moment: int_a^b t f(t) dt.
+  double first_moment(double a, double b) const {
+    const double ex = (d - 1) / 2.0;
+    const double ua = std::fmax(0.0, 1.0 - a * a), ub = std::fmax(0.0, 1.0 - b * b);
+    return c / (d - 1) * (std::pow(ua, ex) - std::pow(ub, ex));
+  }
+};
+
+}  // namespace
+}  // namespace tq
+
+extern "C" {
+
+uint64_t tq_layer_seed(int32_t layer) { return uint64_t(42 + 7 * int64_t(layer)); }
+
+tq_status tq_make_rotations(int32_t d, uint64_t seed, float* pi, float* s, float* pi_s) {
+  using namespace tq;
+  clear_error();
+  if (d < 3 || d > 1024) return fail(TQ_ERR_INVALID_ARG, "d=%d out of [3, 1024]", d);
+  if (!pi || !s) return fail(TQ_ERR_INVALID_ARG, "pi and s must be non-NULL");
+  const size_t n2 = size_t(d) * d;
+  std::vector<double> g(n2), q;
+  for (size_t i = 0; i < n2; ++i) g[i] = normal_at(seed, i);
+  householder_qr(d, g, q);  // g now holds R
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) {
+      const double r = g[size_t(j) * d + j];
+      const double sg = r < 0 ? -1.0 : 1.0;
+      pi[size_t(i) * d + j] = float(q[size_t(i) * d + j] * sg);
+    }
+  for (size_t i = 0; i < n2; ++i) s[i] = float(normal_at(seed, n2 + i));
+  if (pi_s) {
+    // M = S Pi^T from the stored fp32 values, accumulated in double.
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) {
+        double acc = 0.0;
+        for (int k = 0; k < d; ++k) acc += double(s[size_t(i) * d + k]) * double(pi[size_t(j) * d + k]);
+        pi_s[size_t(i) * d + j] = float(acc);
+      }
+  }
+  return TQ_OK;
+}
+
+tq_status tq_make_codebook(int32_t d, int32_t bits, double* centroids, double* boundaries) {
+  using namespace tq;
+  clear_error();
+  if (d < 3 || d > 65536) return fail(TQ_ERR_INVALID_ARG, "d=%d out of [3, 65536]", d);
+  if (bits < 1 || bits > 8) return fail(TQ_ERR_INVALID_ARG, "bits=%d out of [1, 8]", bits);
+  if (!centroids || (bits > 0 && !boundaries)) return fail(TQ_ERR_INVALID_ARG, "NULL output");
+  const int n = 1 << bits;
+  CoordinateLaw law(d);
+  // Start from the cell mid-quantiles (bisection on the CDF).
+  std::vector<double> c(n), t(n - 1), cdf(n + 1);
+  for (int k = 0; k < n; ++k) {
+    const double target = (k + 0.5) / n - 0.5;  // mass from zero
+    double lo = -1.0, hi = 1.0;
+    for (int it = 0; it < 80; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      if (law.mass_from_zero(mid) < target) lo = mid; else hi = mid;
+    }
+    c[k] = 0.5 * (lo + hi);
+  }
+  // Lloyd iteration: boundaries at midpoints, centroids at cell means.
+  for (int it = 0; it < 200000; ++it) {
+    for (int k = 0; k + 1 < n; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
+    cdf[0] = -0.5;
+    cdf[n] = 0.5;
+    for (int k = 0; k + 1 < n; ++k) cdf[k + 1] = law.mass_from_zero(t[k]);
+    double step = 0.0;
+    for (int k = 0; k < n; ++k) {
+      const double a = k == 0 ? -1.0 : t[k - 1];
+      const double b = k == n - 1 ? 1.0 : t[k];
+      const double m0 = cdf[k + 1] - cdf[k];
+      const double ck = law.first_moment(a, b) / m0;
+      step = std::fmax(step, std::fabs(ck - c[k]));
+      c[k] = ck;
+    }
+    if (step < 1e-15) break;
+  }
+  // The law is symmetric: project onto exact antisymmetry (removes rounding
+  // noise; the middle boundary becomes exactly 0).
+  std::vector<double> cs(n);
+  for (int k = 0; k < n; ++k) cs[k] = 0.5 * (c[k] - c[n - 1 - k]);
+  for (int k = 0; k < n; ++k) centroids[k] = cs[k];
+  for (int k = 0; k + 1 < n; ++k) boundaries[k] = 0.5 * (cs[k] + cs[k + 1]);
+  return TQ_OK;
+}
+
+tq_status tq_cache_plane_bytes(const tq_format* fmt, int32_t n_layers, int32_t n_kv_heads,
+                               int64_t capacity, size_t out_bytes[8]) {
+  using namespace tq;
+  clear_error();
+  tq_status st = check_format(fmt, false);
+  if (st) return st;
+  if (!out_bytes) return fail(TQ_ERR_INVALID_ARG, "out_bytes is NULL");
+  if (n_layers <= 0 || n_kv_heads <= 0 || capacity <= 0 || capacity % kVBlock)
+    return fail(TQ_ERR_INVALID_ARG, "bad sizes (layers=%d heads=%d capacity=%lld; capacity must be a positive multiple of 32)",
+                n_layers, n_kv_heads, (long long)capacity);
+  const size_t slots = size_t(n_layers) * n_kv_heads * size_t(capacity);
+  const size_t d = size_t(fmt->d);
+  for (int i = 0; i < 8; ++i) out_bytes[i] = 0;
+  if (fmt->k_bits > 0) {
+    out_bytes[0] = slots * d * size_t(fmt->k_bits - 1) / 8;
+    out_bytes[1] = slots * d / 8;
+    out_bytes[2] = slots * 4;
+    out_bytes[3] = slots * 4;
+  } else {
+    out_bytes[4] = slots * d * 2;
+  }
+  if (fmt->v_bits > 0) {
+    out_bytes[5] = slots * d * size_t(fmt->v_bits) / 8;
+    out_bytes[6] = slots * 4;
+  } else {
+    out_bytes[7] = slots * d * 2;
+  }
+  return TQ_OK;
+}
+
+size_t tq_decode_workspace_bytes(const tq_format* fmt, int32_t n_layers, int32_t batch,
+                                 int32_t n_kv_heads, int32_t n_q_heads, int64_t max_seq_len) {
+  using namespace tq;
+  if (check_format(fmt, false) != TQ_OK || n_layers <= 0 || batch <= 0 || n_kv_heads <= 0 ||
+      n_q_heads <= 0 || n_q_heads % n_kv_heads || max_seq_len < 0)
+    return 0;
+  return plan_decode(fmt->d, n_layers, batch, n_kv_heads, n_q_heads, max_seq_len).total_bytes;
+}
+
+const char* tq_status_string(tq_status st) {
+  switch (st) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_ERR_INVALID_ARG: return "TQ_ERR_INVALID_ARG";
+    case TQ_ERR_UNSUPPORTED: return "TQ_ERR_UNSUPPORTED";
+    case TQ_ERR_WORKSPACE: return "TQ_ERR_WORKSPACE";
+    case TQ_ERR_HIP: return "TQ_ERR_HIP";
+    default: return "TQ_ERR_UNKNOWN";
+  }
+}
+
+const char* tq_last_error(void) { return tq::g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,1215 @@
+// Device half of libtq: compression into the packed cache and single-query
+// decode attention on it, for CDNA4 (gfx950), d = 128.
+//
+// Pages ("TurboQuant QJL投影深度剖析"):
+//   section 2 - key = ||x||, Lloyd-Max codes of Pi x/||x||, signs of S r, ||r||;
+//   section 5 - the record and the unbiased estimator
+//               <q, x~> + ||r|| sqrt(pi/2)/d <S q, signs>;
+//   section 6 - scoring with Pi q against centroids and S q against signs,
+//               decode attention as one pass with an online softmax.
+// MLX write-up, 背景: values take the MSE-only path.
+//
+// Kernels
+//   compress_kernel  one workgroup per (16-token tile, layer); each wave takes
+//                    heads w, w+4, ...  Rotation y = Pi x and the sketch
+//                    z = (S Pi^T)(y - c[idx]) run as fp32 MFMA 16x16x4 with Pi
+//                    and S Pi^T staged in LDS in operand order.
+//   qprep_kernel     Pi q and S q per (layer, batch, query head).
+//   decode_kernel    one workgroup of 4 waves per (token split, KV head and
+//                    head group, layer x batch).  Each wave streams 32-token
+//                    chunks: unpack codes through LDS tables into fp16 MFMA
+//                    operands, score G <= 16 query heads with
+//                    v_mfma_f32_16x16x32_f16 (codes x Pi q, signs x S q), run
+//                    the online softmax, and accumulate values in the rotated
+//                    domain with a second MFMA (P x codes).  Pi^T is applied
+//                    once, after the split combine.
+//   combine_kernel   merges the split partials of a (layer, batch, KV head)
+//                    and applies Pi^T.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr int D = 128;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ floatx4 mfma16x16x32(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16x16x4f32(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float load_elem(const void* p, int dtype, int64_t i) {
+  if (dtype == TQ_DTYPE_F32) return static_cast<const float*>(p)[i];
+  const uint16_t h = static_cast<const uint16_t*>(p)[i];
+  if (dtype == TQ_DTYPE_BF16) return __uint_as_float(uint32_t(h) << 16);
+  _Float16 f;
+  __builtin_memcpy(&f, &h, 2);
+  return float(f);
+}
+
+__device__ __forceinline__ uint16_t f16_bits(float x) {
+  _Float16 h = _Float16(x);
+  uint16_t u;
+  __builtin_memcpy(&u, &h, 2);
+  return u;
+}
+
+// ===========================================================================
+// Compression
+
+struct CompressArgs {
+  const void* k;
+  const void* v;
+  int dtype;
+  int layer0;
+  int64_t n_tokens;
+  const int64_t* slots;
+  int64_t slot0;
+  int H;
+  int64_t capacity;
+  int mk;  // key MSE bits, 0 = fp16 keys
+  int bv;  // value bits, 0 = fp16 values
+  int64_t tiles_per_wg;
+  const float* pi;
+  const float* pi_s;
+  const float* kc;
+  const float* kb;
+  const float* vc;
+  const float* vb;
+  uint8_t* k_idx;
+  uint8_t* k_sign;
+  float* k_norm;
+  float* k_rnorm;
+  uint16_t* k_f16;
+  uint8_t* v_idx;
+  float* v_norm;
+  uint16_t* v_f16;
+};
+
+constexpr int kCompressTile = 16;  // tokens per wave step
+
+// Shared memory of the compress kernel: Pi and S Pi^T in MFMA operand order
+// plus per-wave packing scratch.
+struct CompressSmem {
+  float pi_op[D * D];    // [(tile*32 + s)*64 + q*16 + i] = Pi[16 tile + i][32 q + s]
+  float m_op[D * D];     // [(tile'*32 + tile*4 + r)*64 + q*16 + i] = M[16 tile' + i][16 tile + 4 q + r]
+  float kc[16], kb[16], vc[16], vb[16];
+  uint32_t rec[kWaves][kCompressTile * 16];   // packed key codes per token (<= 16 dwords)
+  uint32_t srec[kWaves][kCompressTile * 4];   // packed signs per token
+  uint32_t vrec[kWaves][D * 2];               // value codes of 16 tokens per coordinate
+};
+
+// Lane (t = lane % 16, q = lane / 16) holds coordinates 32q .. 32q+31 of token t.
+__device__ __forceinline__ void load_token_slab(const CompressArgs& a, const void* base, int layer_rel,
+                                                int64_t tok, int h, int q, bool valid, float (&xr)[32]) {
+  if (!valid) {
+#pragma unroll
+    for (int s = 0; s < 32; ++s) xr[s] = 0.f;
+    return;
+  }
+  const int64_t off = ((int64_t(layer_rel) * a.n_tokens + tok) * a.H + h) * D + 32 * q;
+  if (a.dtype == TQ_DTYPE_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float4 f = p[u];
+      xr[4 * u] = f.x; xr[4 * u + 1] = f.y; xr[4 * u + 2] = f.z; xr[4 * u + 3] = f.w;
+    }
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      u32x4 w = p[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = w[e] & 0xFFFFu, hi = w[e] >> 16;
+        if (a.dtype == TQ_DTYPE_BF16) {
+          xr[8 * u + 2 * e] = __uint_as_float(lo << 16);
+          xr[8 * u + 2 * e + 1] = __uint_as_float(hi << 16);
+        } else {
+          _Float16 f0, f1;
+          uint16_t l16 = uint16_t(lo), h16 = uint16_t(hi);
+          __builtin_memcpy(&f0, &l16, 2);
+          __builtin_memcpy(&f1, &h16, 2);
+          xr[8 * u + 2 * e] = float(f0);
+          xr[8 * u + 2 * e + 1] = float(f1);
+        }
+      }
+    }
+  }
+}
+
+// Norm and y = Pi x / ||x|| for the wave's 16 tokens.  On return lane (t, q)
+// holds y[16 tile + 4 q + r] of token t in y[tile][r].
+__device__ __forceinline__ float rotate_tile(const CompressSmem& sm, const float (&xr)[32], int lane,
+                                             float (&y)[8][4]) {
+  float ss = 0.f;
+#pragma unroll
+  for (int s = 0; s < 32; ++s) ss = fmaf(xr[s], xr[s], ss);
+  ss += shfl_xor(ss, 16);
+  ss += shfl_xor(ss, 32);
+  const float n = sqrtf(ss);
+  // n = 0 -> y = 0; NaN -> NaN everywhere.
+  const float inv = n > 0.f ? 1.0f / n : (n == 0.f ? 0.f : n);
+#pragma unroll
+  for (int tile = 0; tile < 8; ++tile) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 32; ++s) acc = mfma16x16x4f32(sm.pi_op[(tile * 32 + s) * 64 + lane], xr[s], acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[tile][r] = acc[r] * inv;
+  }
+  return n;
+}
+
+template <int NB>
+__device__ __forceinline__ uint32_t quantize(float y, const float* bnd) {
+  uint32_t idx = 0;
+#pragma unroll
+  for (int k = 0; k < NB; ++k) idx += (y >= bnd[k]) ? 1u : 0u;
+  return idx;
+}
+
+__device__ __forceinline__ uint32_t quantize_dyn(float y, const float* bnd, int nb) {
+  switch (nb) {
+    case 1: return quantize<1>(y, bnd);
+    case 3: return quantize<3>(y, bnd);
+    case 7: return quantize<7>(y, bnd);
+    default: return quantize<15>(y, bnd);
+  }
+}
+
+// OR the 4 consecutive m-bit codes `chunk` (coordinates 16 tile + 4 q .. +3)
+// into a token record in LDS.
+__device__ __forceinline__ void or_bits(uint32_t* rec, int bitpos, uint32_t chunk, int nbits) {
+  const int w = bitpos >> 5, sh = bitpos & 31;
+  atomicOr(&rec[w], chunk << sh);
+  if (sh + nbits > 32) atomicOr(&rec[w + 1], chunk >> (32 - sh));
+}
+
+__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  CompressSmem& sm = *reinterpret_cast<CompressSmem*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = lane & 15, q = lane >> 4;
+  const int layer_rel = blockIdx.y;
+  const int layer = a.layer0 + layer_rel;
+  const bool need_rot = a.mk > 0 || a.bv > 0;
+
+  // Stage Pi (and M) in operand order; all global loads of a thread are
+  // issued before its LDS writes.
+  if (need_rot) {
+    const float4* src = reinterpret_cast<const float4*>(a.pi + int64_t(layer) * D * D);
+    float4 buf[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) buf[u] = src[tid + 256 * u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = 4 * (tid + 256 * u), row = e >> 7, col = e & 127;
+      const int tile = row >> 4, i = row & 15, qq = col >> 5, s0 = col & 31;
+      float* dst = &sm.pi_op[(tile * 32 + s0) * 64 + qq * 16 + i];
+      dst[0] = buf[u].x; dst[64] = buf[u].y; dst[128] = buf[u].z; dst[192] = buf[u].w;
+    }
+  }
+  if (a.mk > 0) {
+    const float4* src = reinterpret_cast<const float4*>(a.pi_s + int64_t(layer) * D * D);
+    float4 buf[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) buf[u] = src[tid + 256 * u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = 4 * (tid + 256 * u), row = e >> 7, col = e & 127;
+      const int tp = row >> 4, i = row & 15, tile = col >> 4, qq = (col >> 2) & 3;
+      float* dst = &sm.m_op[(tp * 32 + tile * 4) * 64 + qq * 16 + i];
+      dst[0] = buf[u].x; dst[64] = buf[u].y; dst[128] = buf[u].z; dst[192] = buf[u].w;
+    }
+  }
+  if (tid < 16) {
+    const int nk = a.mk > 0 ? (1 << a.mk) : 0, nv = a.bv > 0 ? (1 << a.bv) : 0;
+    sm.kc[tid] = tid < nk ? a.kc[tid] : 0.f;
+    sm.kb[tid] = tid + 1 < nk ? a.kb[tid] : INFINITY;
+    sm.vc[tid] = tid < nv ? a.vc[tid] : 0.f;
+    sm.vb[tid] = tid + 1 < nv ? a.vb[tid] : INFINITY;
+  }
+  __syncthreads();
+
+  const int64_t n_tiles = (a.n_tokens + kCompressTile - 1) / kCompressTile;
+  const int64_t tile_lo = int64_t(blockIdx.x) * a.tiles_per_wg;
+  const int64_t tile_hi = tile_lo + a.tiles_per_wg < n_tiles ? tile_lo + a.tiles_per_wg : n_tiles;
+  for (int64_t tl = tile_lo; tl < tile_hi; ++tl) {
+  const int64_t tok0 = tl * kCompressTile;
+  const int64_t tok = tok0 + t;
+  const bool tok_ok = tok < a.n_tokens;
+  int64_t slot = -1;
+  if (tok_ok) slot = a.slots ? a.slots[tok] : a.slot0 + tok;
+  const bool valid = tok_ok && slot >= 0 && slot < a.capacity;
+  // Fast value path: 16 contiguous, 16-aligned, all-valid slots.
+  bool contiguous = (a.slots == nullptr) && (tok0 + kCompressTile <= a.n_tokens) &&
+                    ((a.slot0 + tok0) % kCompressTile == 0) && (a.slot0 + tok0 >= 0) &&
+                    (a.slot0 + tok0 + kCompressTile <= a.capacity);
+
+  uint32_t* rec = sm.rec[wave];
+  uint32_t* srec = sm.srec[wave];
+  uint32_t* vrec = sm.vrec[wave];
+  const int kwords = 4 * a.mk;  // dwords per key code record
+
+  for (int h = wave; h < a.H; h += kWaves) {
+    const int64_t plane = int64_t(layer) * a.H + h;  // [layer][head]
+    float xr[32];
+    float y[8][4];
+    // ---------------- keys
+    load_token_slab(a, a.k, layer_rel, tok, h, q, valid, xr);
+    if (a.mk == 0) {
+      if (valid) {
+        uint16_t* dst = a.k_f16 + (plane * a.capacity + slot) * D + 32 * q;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = uint32_t(f16_bits(xr[8 * u + 2 * e])) | (uint32_t(f16_bits(xr[8 * u + 2 * e + 1])) << 16);
+          reinterpret_cast<u32x4*>(dst)[u] = w;
+        }
+      }
+    } else {
+      const float n = rotate_tile(sm, xr, lane, y);
+      const int nb = (1 << a.mk) - 1;
+      for (int e = lane; e < kCompressTile * 16; e += 64) rec[e] = 0u;
+      srec[lane] = 0u;
+      wave_sync();
+      float a2 = 0.f;
+      float res[8][4];
+#pragma unroll
+      for (int tile = 0; tile < 8; ++tile) {
+        uint32_t chunk = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t idx = quantize_dyn(y[tile][r], sm.kb, nb);
+          chunk |= idx << (r * a.mk);
+          res[tile][r] = y[tile][r] - sm.kc[idx];
+          a2 = fmaf(res[tile][r], res[tile][r], a2);
+        }
+        or_bits(rec + t * 16, (16 * tile + 4 * q) * a.mk, chunk, 4 * a.mk);
+      }
+      a2 += shfl_xor(a2, 16);
+      a2 += shfl_xor(a2, 32);
+      const float rnorm = n * sqrtf(a2);
+      // z = M (y - c[idx]); sign of n * z (a zero key gives all ones).
+#pragma unroll
+      for (int tp = 0; tp < 8; ++tp) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tile = 0; tile < 8; ++tile)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc = mfma16x16x4f32(sm.m_op[(tp * 32 + tile * 4 + r) * 64 + lane], res[tile][r], acc);
+        uint32_t bits = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bits |= (acc[r] * n >= 0.f ? 1u : 0u) << r;
+        or_bits(srec + t * 4, 16 * tp + 4 * q, bits, 4);
+      }
+      wave_sync();
+      if (valid && q == 0) {
+        a.k_norm[plane * a.capacity + slot] = n;
+        a.k_rnorm[plane * a.capacity + slot] = rnorm;
+      }
+      // Write the records: 16 tokens x kwords dwords, then 16 x 4 sign dwords.
+      for (int e = lane; e < kCompressTile * kwords; e += 64) {
+        const int tt = e / kwords, w = e - tt * kwords;
+        const int64_t tk = tok0 + tt;
+        if (tk >= a.n_tokens) continue;
+        const int64_t sl = a.slots ? a.slots[tk] : a.slot0 + tk;
+        if (sl < 0 || sl >= a.capacity) continue;
+        reinterpret_cast<uint32_t*>(a.k_idx + (plane * a.capacity + sl) * (16 * a.mk))[w] = rec[tt * 16 + w];
+      }
+      {
+        const int tt = lane >> 2, w = lane & 3;
+        const int64_t tk = tok0 + tt;
+        if (tk < a.n_tokens) {
+          const int64_t sl = a.slots ? a.slots[tk] : a.slot0 + tk;
+          if (sl >= 0 && sl < a.capacity)
+            reinterpret_cast<uint32_t*>(a.k_sign + (plane * a.capacity + sl) * 16)[w] = srec[tt * 4 + w];
+        }
+      }
+      wave_sync();
+    }
+    // ---------------- values
+    load_token_slab(a, a.v, layer_rel, tok, h, q, valid, xr);
+    if (a.bv == 0) {
+      if (valid) {
+        // [plane][slot/32][coord][32] fp16
+        uint16_t* dst = a.v_f16 + ((plane * (a.capacity / kVBlock) + slot / kVBlock) * D) * kVBlock + (slot % kVBlock);
+#pragma unroll
+        for (int s = 0; s < 32; ++s) dst[(32 * q + s) * kVBlock] = f16_bits(xr[s]);
+      }
+    } else {
+      const float n = rotate_tile(sm, xr, lane, y);
+      const int nb = (1 << a.bv) - 1;
+      if (valid && q == 0) a.v_norm[plane * a.capacity + slot] = n;
+      const int64_t gbytes = 4 * a.bv;  // bytes per (block, coordinate) group
+      uint8_t* vplane = a.v_idx + plane * (a.capacity / kVBlock) * D * gbytes;
+      if (contiguous && a.bv >= 2) {
+        // The wave owns whole dwords: 16 tokens x bv bits per coordinate.
+        const int dw = a.bv / 2;  // dwords per coordinate for 16 tokens
+        for (int e = lane; e < D * dw; e += 64) vrec[e] = 0u;
+        wave_sync();
+#pragma unroll
+        for (int tile = 0; tile < 8; ++tile)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t idx = quantize_dyn(y[tile][r], sm.vb, nb);
+            const int c = 16 * tile + 4 * q + r;
+            const int bit = t * a.bv;
+            atomicOr(&vrec[c * dw + (bit >> 5)], idx << (bit & 31));
+          }
+        wave_sync();
+        const int64_t s0 = a.slot0 + tok0;
+        const int64_t blk = s0 / kVBlock;
+        const int half = int(s0 % kVBlock) / kCompressTile;  // which 16-slot half of the block
+        for (int e = lane; e < D * dw; e += 64) {
+          const int c = e / dw, w = e - c * dw;
+          uint32_t* g = reinterpret_cast<uint32_t*>(vplane + (blk * D + c) * gbytes);
+          g[half * dw + w] = vrec[e];
+        }
+        wave_sync();
+      } else if (valid) {
+        const int64_t blk = slot / kVBlock;
+        const int p = int(slot % kVBlock);
+        const int bit = p * a.bv;
+        const uint32_t mask = ((1u << a.bv) - 1u) << (bit & 31);
+#pragma unroll
+        for (int tile = 0; tile < 8; ++tile)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t idx = quantize_dyn(y[tile][r], sm.vb, nb);
+            const int c = 16 * tile + 4 * q + r;
+            uint32_t* g = reinterpret_cast<uint32_t*>(vplane + (blk * D + c) * gbytes) + (bit >> 5);
+            atomicAnd(g, ~mask);
+            atomicOr(g, idx << (bit & 31));
+          }
+      }
+    }
+  }
+  }  // token tiles
+}
+
+// ===========================================================================
+// Decode
+
+struct DecodeArgs {
+  int n_layers, batch, H, Hq, G, n_hg;
+  int64_t capacity;
+  int64_t split_tokens;
+  int n_splits;
+  const uint8_t* k_idx;
+  const uint8_t* k_sign;
+  const float* k_norm;
+  const float* k_rnorm;
+  const uint16_t* k_f16;
+  const uint8_t* v_idx;
+  const float* v_norm;
+  const uint16_t* v_f16;
+  const float* qprep;   // [L][B][Hq][2][D]
+  const float* kc;
+  const float* vc;
+  const int64_t* seq_start;
+  const int32_t* seq_len;
+  float* partial;       // [L][B][Hq][n_splits][D + 2]
+  float* logits;        // score mode: [L][B][Hq][max_len]
+  int64_t max_len;
+  float scale;
+  float kappa;
+};
+
+// DPP row broadcast: every lane of a 16-lane row reads lane E of its row.
+template <int E>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + E, 0xF, 0xF,
+                                                               false));
+}
+template <int B>
+__device__ __forceinline__ void row_bcast8(float v, float (&o)[8]) {
+  o[0] = row_bcast<B + 0>(v); o[1] = row_bcast<B + 1>(v); o[2] = row_bcast<B + 2>(v); o[3] = row_bcast<B + 3>(v);
+  o[4] = row_bcast<B + 4>(v); o[5] = row_bcast<B + 5>(v); o[6] = row_bcast<B + 6>(v); o[7] = row_bcast<B + 7>(v);
+}
+
+// LDS lookup tables: a group of NG codes indexes an entry of NG fp16
+// centroids.  Group sizes: m = 1: 8 codes (byte index), m = 2: 4 codes (byte
+// index), m = 3: 2 codes (6-bit index), m = 4: 2 codes (byte index).  With
+// HILO each entry holds the fp16 rounding c_hi of the NG centroids followed by
+// the fp16 rounding of the remainders c - c_hi, so one LDS read yields both
+// halves of a two-term fp16 representation (about 22 significant bits).
+template <int M, bool HILO> struct Lut {
+  static constexpr int NG = M == 1 ? 8 : (M == 2 ? 4 : 2);
+  static constexpr int ENTRIES = 1 << (NG * M);
+  static constexpr int ENTRY_WORDS = (NG / 2) * (HILO ? 2 : 1);
+  static constexpr int WORDS = ENTRIES * ENTRY_WORDS;
+};
+
+template <int M, bool HILO>
+__device__ __forceinline__ void build_lut(uint32_t* lut, const float* cent, int tid) {
+  using L = Lut<M, HILO>;
+  for (int x = tid; x < L::ENTRIES; x += 256) {
+#pragma unroll
+    for (int e = 0; e < L::NG; e += 2) {
+      const float c0 = cent[(x >> (e * M)) & ((1 << M) - 1)];
+      const float c1 = cent[(x >> ((e + 1) * M)) & ((1 << M) - 1)];
+      const _Float16 h0 = _Float16(c0), h1 = _Float16(c1);
+      uint16_t b0, b1;
+      __builtin_memcpy(&b0, &h0, 2);
+      __builtin_memcpy(&b1, &h1, 2);
+      lut[x * L::ENTRY_WORDS + e / 2] = uint32_t(b0) | (uint32_t(b1) << 16);
+      if constexpr (HILO) {
+        const uint32_t l0 = f16_bits(c0 - float(h0)), l1 = f16_bits(c1 - float(h1));
+        lut[x * L::ENTRY_WORDS + L::NG / 2 + e / 2] = l0 | (l1 << 16);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ half8 as_half8(u32x4 w) {
+  half8 h;
+  __builtin_memcpy(&h, &w, 16);
+  return h;
+}
+
+// 8 consecutive m-bit codes (LSB-first in `bits`) -> 8 fp16 centroids.
+template <int M>
+__device__ __forceinline__ half8 deq8(uint32_t bits, const uint32_t* lut) {
+  u32x4 w;
+  if constexpr (M == 1) {
+    w = *reinterpret_cast<const u32x4*>(lut + (bits & 0xFFu) * 4);
+  } else if constexpr (M == 2) {
+    u32x2 a0 = *reinterpret_cast<const u32x2*>(lut + (bits & 0xFFu) * 2);
+    u32x2 a1 = *reinterpret_cast<const u32x2*>(lut + ((bits >> 8) & 0xFFu) * 2);
+    w = u32x4{a0[0], a0[1], a1[0], a1[1]};
+  } else if constexpr (M == 3) {
+    w = u32x4{lut[bits & 63u], lut[(bits >> 6) & 63u], lut[(bits >> 12) & 63u], lut[(bits >> 18) & 63u]};
+  } else {
+    w = u32x4{lut[bits & 0xFFu], lut[(bits >> 8) & 0xFFu], lut[(bits >> 16) & 0xFFu], lut[bits >> 24]};
+  }
+  return as_half8(w);
+}
+
+// Same with two-term (hi, lo) centroids from a HILO table.
+template <int M>
+__device__ __forceinline__ void deq8_hilo(uint32_t bits, const uint32_t* lut, half8& hi, half8& lo) {
+  if constexpr (M == 1) {
+    const u32x4* e = reinterpret_cast<const u32x4*>(lut + (bits & 0xFFu) * 8);
+    hi = as_half8(e[0]);
+    lo = as_half8(e[1]);
+  } else if constexpr (M == 2) {
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(lut + (bits & 0xFFu) * 4);
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(lut + ((bits >> 8) & 0xFFu) * 4);
+    hi = as_half8(u32x4{a0[0], a0[1], a1[0], a1[1]});
+    lo = as_half8(u32x4{a0[2], a0[3], a1[2], a1[3]});
+  } else {
+    constexpr uint32_t mask = M == 3 ? 63u : 0xFFu;
+    constexpr int sh = 2 * M;
+    const u32x2 e0 = *reinterpret_cast<const u32x2*>(lut + (bits & mask) * 2);
+    const u32x2 e1 = *reinterpret_cast<const u32x2*>(lut + ((bits >> sh) & mask) * 2);
+    const u32x2 e2 = *reinterpret_cast<const u32x2*>(lut + ((bits >> (2 * sh)) & mask) * 2);
+    const u32x2 e3 = *reinterpret_cast<const u32x2*>(lut + ((bits >> (3 * sh)) & mask) * 2);
+    hi = as_half8(u32x4{e0[0], e1[0], e2[0], e3[0]});
+    lo = as_half8(u32x4{e0[1], e1[1], e2[1], e3[1]});
+  }
+}
+
+// Bits [8 m s, 8 m s + 8 m) of a lane's 32-coordinate slab (m dwords).
+template <int M, int N>
+__device__ __forceinline__ uint32_t slab_bits(const uint32_t (&w)[N], int s) {
+  if constexpr (M == 1) return (w[0] >> (8 * s)) & 0xFFu;
+  else if constexpr (M == 2) return (w[s >> 1] >> (16 * (s & 1))) & 0xFFFFu;
+  else if constexpr (M == 3) {
+    // 24-bit windows of the 96-bit slab (funnel shifts of adjacent words)
+    if (s == 0) return w[0] & 0xFFFFFFu;
+    if (s == 1) return __builtin_amdgcn_alignbit(w[1], w[0], 24) & 0xFFFFFFu;
+    if (s == 2) return __builtin_amdgcn_alignbit(w[2], w[1], 16) & 0xFFFFFFu;
+    return w[2] >> 8;
+  } else return w[s];
+}
+
+template <int MK, int BV, bool SCORE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
+  constexpr int KW = MK > 0 ? Lut<MK, true>::WORDS : 1;
+  constexpr int VW = BV > 0 ? Lut<BV, false>::WORDS : 1;
+  __shared__ __align__(16) uint32_t lut_k[KW];
+  __shared__ __align__(16) uint32_t lut_v[VW];
+  __shared__ __align__(16) uint32_t lut_s[256 * 4];
+  __shared__ float mw[kWaves][16], lw[kWaves][16];
+  __shared__ float accsum[16][D];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, q = lane >> 4;   // MFMA column (head / coordinate) and k-group
+  const int split = blockIdx.x;
+  const int hk = blockIdx.y / a.n_hg, hg = blockIdx.y % a.n_hg;
+  const int layer = blockIdx.z / a.batch, b = blockIdx.z % a.batch;
+
+  // Sequence range, clamped to the cache.
+  const int64_t start = a.seq_start[b];
+  int64_t len = a.seq_len[b];
+  if (start < 0 || (start % kVBlock) != 0 || start >= a.capacity || len < 0) len = 0;
+  if (len > a.capacity - start) len = a.capacity - start;
+  if (len > a.max_len) len = a.max_len;   // tokens past max_seq_len are ignored
+  const int64_t t_lo = int64_t(split) * a.split_tokens;
+  const int64_t t_hi = t_lo + a.split_tokens < len ? t_lo + a.split_tokens : len;
+
+  // Tables.
+  if constexpr (MK > 0) build_lut<MK, true>(lut_k, a.kc, tid);
+  if constexpr (BV > 0) build_lut<BV, false>(lut_v, a.vc, tid);
+  if constexpr (MK > 0) {
+    for (int x = tid; x < 256; x += 256) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t lo = ((x >> e) & 1) ? 0x3C00u : 0xBC00u;
+        const uint32_t hi = ((x >> (e + 1)) & 1) ? 0x3C00u : 0xBC00u;
+        lut_s[x * 4 + e / 2] = lo | (hi << 16);
+      }
+    }
+  }
+  if constexpr (!SCORE)
+    for (int e = tid; e < 16 * D; e += 256) (&accsum[0][0])[e] = 0.f;
+  __syncthreads();
+
+  // Query operands: lane (col = head g, q) holds Pi q and S q at coordinates
+  // 32 q + 8 s + e as fp16 hi + lo pairs.
+  const int g_local = hg * kMaxGroup + col;
+  const bool head_ok = g_local < a.G;
+  const int h = hk * a.G + (head_ok ? g_local : 0);
+  half8 qrh[4], qrl[4], qsh[4], qsl[4];
+  {
+    const float4* qp = reinterpret_cast<const float4*>(
+        a.qprep + ((int64_t(layer) * a.batch + b) * a.Hq + h) * 2 * D + 32 * q);
+    const float keep = head_ok ? 1.f : 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float4 r0 = qp[2 * s], r1 = qp[2 * s + 1];
+      const float4 z0 = qp[D / 4 + 2 * s], z1 = qp[D / 4 + 2 * s + 1];
+      const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+      const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float r = rv[e] * keep, z = zv[e] * keep;
+        const _Float16 rh = _Float16(r), zh = _Float16(z);
+        qrh[s][e] = rh;
+        qrl[s][e] = _Float16(r - float(rh));
+        qsh[s][e] = zh;
+        qsl[s][e] = _Float16(z - float(zh));
+      }
+    }
+  }
+
+  const int64_t plane = int64_t(layer) * a.H + hk;
+  const int64_t slot_base = plane * a.capacity + start;   // slot index of token 0
+  constexpr int KREC = MK > 0 ? 16 * MK : 2 * D;          // bytes per key code record
+
+  float m_run = -INFINITY, l_run = 0.f, sig = 0.f;
+  floatx4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // Global data one lane needs for one 32-token chunk.  Every address lies in
+  // the chunk's 32-slot block, which the clamped sequence range keeps inside
+  // the cache, so the loads are unconditional; tokens past the end of the
+  // sequence are masked after loading.
+  constexpr int MKW = MK > 0 ? MK : 1;
+  // Packed codes are loaded one chunk ahead (double-buffered); norms and fp16
+  // planes are loaded at the top of their own chunk to bound register use.
+  constexpr bool kPrefetch = MK > 0 && BV > 0;
+  // Norms: lane (col, q) loads one key norm (col < 8) or residual norm
+  // (col >= 8) of token 8 q + col % 8 and one value norm; the 16 lanes of a
+  // row then read them from each other with DPP row broadcasts.
+  struct Chunk {
+    uint32_t kw[2][MKW];
+    uint32_t sg[2];
+    uint32_t vw[8];
+    float nrm[2];
+  };
+  struct ChunkLate {
+    half8 kf[MK > 0 ? 1 : 2][MK > 0 ? 1 : 4];
+    half8 vf[BV > 0 ? 1 : 8];
+  };
+  const int64_t vplane = plane * (a.capacity / kVBlock);
+  auto load_late = [&](int64_t c0, ChunkLate& C) {
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const int64_t tk = slot_base + c0 + 8 * (col >> 2) + 4 * T + (col & 3);
+      if constexpr (MK == 0) {
+        const half8* kp = reinterpret_cast<const half8*>(a.k_f16 + tk * D + 32 * q);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) C.kf[T][s2] = kp[s2];
+      }
+    }
+    if constexpr (BV == 0) {
+      const int64_t blk = (start + c0) / kVBlock;
+#pragma unroll
+      for (int vb = 0; vb < 8; ++vb)
+        C.vf[vb] = *reinterpret_cast<const half8*>(
+            a.v_f16 + ((vplane + blk) * D + 16 * vb + col) * kVBlock + 8 * q);
+    }
+  };
+  auto load_chunk = [&](int64_t c0, Chunk& C) {
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const int64_t tk = slot_base + c0 + 8 * (col >> 2) + 4 * T + (col & 3);
+      if constexpr (MK > 0) {
+        const uint32_t* kp = reinterpret_cast<const uint32_t*>(a.k_idx + tk * KREC) + q * MK;
+        if constexpr (MK == 4) {
+          const u32x4 v4 = *reinterpret_cast<const u32x4*>(kp);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) C.kw[T][u] = v4[u];
+        } else if constexpr (MK == 2) {
+          const u32x2 v2 = *reinterpret_cast<const u32x2*>(kp);
+          C.kw[T][0] = v2[0];
+          C.kw[T][1] = v2[1];
+        } else {
+#pragma unroll
+          for (int u = 0; u < MK; ++u) C.kw[T][u] = kp[u];
+        }
+        C.sg[T] = reinterpret_cast<const uint32_t*>(a.k_sign + tk * 16)[q];
+      }
+    }
+    {
+      const int64_t tn = slot_base + c0 + 8 * q + (col & 7);
+      if constexpr (MK > 0) C.nrm[0] = col < 8 ? a.k_norm[tn] : a.k_rnorm[tn];
+      if constexpr (BV > 0) C.nrm[1] = a.v_norm[tn];
+    }
+    const int64_t blk = (start + c0) / kVBlock;   // chunks are block aligned
+    if constexpr (BV > 0) {
+#pragma unroll
+      for (int vb = 0; vb < 8; ++vb) {
+        const uint32_t* grp = reinterpret_cast<const uint32_t*>(
+            a.v_idx + ((vplane + blk) * D + 16 * vb + col) * (4 * BV));
+        C.vw[vb] = grp[BV == 4 ? q : (BV == 2 ? (q >> 1) : 0)];
+      }
+    }
+  };
+
+  // process(c0, cur): everything one chunk needs after its loads.
+  auto process = [&](int64_t c0, const Chunk& cur) {
+    ChunkLate late;
+    if constexpr (MK == 0 || BV == 0) load_late(c0, late);
+    // ---- scores: tile T row col -> token 8 (col/4) + 4 T + col%4
+    floatx4 sm_[2], sq_[2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      sm_[T] = floatx4{0.f, 0.f, 0.f, 0.f};
+      sq_[T] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (MK > 0) {
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          half8 kh, kl;
+          deq8_hilo<MK>(slab_bits<MK>(cur.kw[T], s2), lut_k, kh, kl);
+          sm_[T] = mfma16x16x32(kh, qrh[s2], sm_[T]);
+          sm_[T] = mfma16x16x32(kh, qrl[s2], sm_[T]);
+          sm_[T] = mfma16x16x32(kl, qrh[s2], sm_[T]);
+          const half8 sd = *reinterpret_cast<const half8*>(lut_s + ((cur.sg[T] >> (8 * s2)) & 0xFFu) * 4);
+          sq_[T] = mfma16x16x32(sd, qsh[s2], sq_[T]);
+          sq_[T] = mfma16x16x32(sd, qsl[s2], sq_[T]);
+        }
+      } else {
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          sm_[T] = mfma16x16x32(late.kf[T][s2], qrh[s2], sm_[T]);
+          sm_[T] = mfma16x16x32(late.kf[T][s2], qrl[s2], sm_[T]);
+        }
+      }
+    }
+    // ---- logits of lane (g = col, q): tokens 8 q + e, e = 4 T + r
+    const int64_t tb = c0 + 8 * q;
+    float lg[8];
+    float kn[8], rn[8];
+    if constexpr (MK > 0) {
+      row_bcast8<0>(cur.nrm[0], kn);
+      row_bcast8<8>(cur.nrm[0], rn);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool ok = tb + e < t_hi;
+      const float smv = sm_[e >> 2][e & 3];
+      float l;
+      if constexpr (MK > 0) {
+        l = a.scale * fmaf(kn[e], smv, a.kappa * rn[e] * sq_[e >> 2][e & 3]);
+      } else {
+        l = a.scale * smv;
+      }
+      lg[e] = ok ? l : -INFINITY;
+    }
+    if constexpr (SCORE) {
+      if (head_ok) {
+        float* out = a.logits + ((int64_t(layer) * a.batch + b) * a.Hq + h) * a.max_len;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (tb + e < t_hi) out[tb + e] = lg[e];
+      }
+    } else {
+      // ---- online softmax (per head; max across the 4 k-groups)
+      float mc = lg[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mc = fmaxf(mc, lg[e]);
+      mc = fmaxf(mc, shfl_xor(mc, 16));
+      mc = fmaxf(mc, shfl_xor(mc, 32));
+      const float m_new = fmaxf(m_run, mc);
+      float vn[8];
+      if constexpr (BV > 0) row_bcast8<0>(cur.nrm[1], vn);
+      float vmax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (BV > 0) vn[e] = (tb + e < t_hi) ? vn[e] : 0.f;
+        else vn[e] = 1.f;
+        vmax = fmaxf(vmax, vn[e]);
+      }
+      vmax = fmaxf(vmax, shfl_xor(vmax, 16));
+      vmax = fmaxf(vmax, shfl_xor(vmax, 32));
+      const float sig_new = fmaxf(fmaxf(sig, vmax), 1e-30f);
+      float p[8];
+      float alpha = 1.f;
+      if (m_new == -INFINITY) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = 0.f;
+      } else {
+        alpha = __expf(m_run - m_new);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = __expf(lg[e] - m_new);
+      }
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) psum += p[e];
+      l_run = l_run * alpha + psum;
+      // The value accumulator is rescaled only when a running maximum moved
+      // (rare after the first chunks); the branch is uniform over the wave.
+      const bool moved = (m_new != m_run) || (sig_new != sig);
+      if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+        const float factor = moved ? alpha * (sig / sig_new) : 1.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] *= factor;
+      }
+      m_run = m_new;
+      sig = sig_new;
+      // P'' = p * ||v|| / sig as fp16 hi + lo (B operand: lane (g, q), tokens 8 q + e)
+      half8 ph, pl;
+      const float inv_sig = 1.0f / sig;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pv = p[e] * vn[e] * inv_sig;
+        const _Float16 hh = _Float16(pv);
+        ph[e] = hh;
+        pl[e] = _Float16(pv - float(hh));
+      }
+      // ---- values: A operand lane (i = col, q) = coordinate 16 vb + i, tokens 8 q .. 8 q + 7
+#pragma unroll
+      for (int vb = 0; vb < 8; ++vb) {
+        half8 vd;
+        if constexpr (BV > 0) {
+          uint32_t bits = cur.vw[vb];
+          if constexpr (BV == 2) bits = (bits >> (16 * (q & 1))) & 0xFFFFu;
+          else if constexpr (BV == 1) bits = (bits >> (8 * q)) & 0xFFu;
+          vd = deq8<BV>(bits, lut_v);
+        } else {
+          vd = late.vf[vb];
+          if (c0 + kChunk > t_hi) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (tb + e >= t_hi) vd[e] = _Float16(0.f);
+          }
+        }
+        acc[vb] = mfma16x16x32(vd, ph, acc[vb]);
+        acc[vb] = mfma16x16x32(vd, pl, acc[vb]);
+      }
+    }
+  };
+
+  const int64_t n_chunks = t_hi > t_lo ? (t_hi - t_lo + kChunk - 1) / kChunk : 0;
+  if constexpr (kPrefetch) {
+    // The loads of chunk i+1 are issued before chunk i is processed; all of a
+    // chunk's global data is in its buffer, so processing never waits on the
+    // newer loads (the wait lands on the copy at the end of the iteration).
+    Chunk cur, nxt;
+    if (wave < n_chunks) load_chunk(t_lo + int64_t(wave) * kChunk, cur);
+#pragma unroll 1
+    for (int64_t ci = wave; ci < n_chunks; ci += kWaves) {
+      if (ci + kWaves < n_chunks) load_chunk(t_lo + (ci + kWaves) * kChunk, nxt);
+      process(t_lo + ci * kChunk, cur);
+      cur = nxt;
+    }
+  } else {
+#pragma unroll 1
+    for (int64_t ci = wave; ci < n_chunks; ci += kWaves) {
+      Chunk cur;
+      load_chunk(t_lo + ci * kChunk, cur);
+      process(t_lo + ci * kChunk, cur);
+    }
+  }
+
+  if constexpr (!SCORE) {
+    // ---- merge the 4 waves and write this split's partial
+    float l_tot = l_run + shfl_xor(l_run, 16);
+    l_tot += shfl_xor(l_tot, 32);
+    if (q == 0) {
+      mw[wave][col] = m_run;
+      lw[wave][col] = l_tot;
+    }
+    __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w][col]);
+    const float f = (m_run == -INFINITY) ? 0.f : __expf(m_run - M) * sig;
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) atomicAdd(&accsum[col][16 * vb + 4 * q + r], acc[vb][r] * f);
+    __syncthreads();
+    const int64_t pbase = (int64_t(layer) * a.batch + b) * a.Hq;
+    const int ng = a.G - hg * kMaxGroup < kMaxGroup ? a.G - hg * kMaxGroup : kMaxGroup;
+    for (int e = tid; e < ng * (D + 2); e += 256) {
+      const int g = e / (D + 2), i = e - g * (D + 2);
+      const int hh = hk * a.G + hg * kMaxGroup + g;
+      float v;
+      if (i == 0) {
+        v = -INFINITY;
+        for (int w = 0; w < kWaves; ++w) v = fmaxf(v, mw[w][g]);
+      } else if (i == 1) {
+        float Mg = -INFINITY;
+        for (int w = 0; w < kWaves; ++w) Mg = fmaxf(Mg, mw[w][g]);
+        v = 0.f;
+        for (int w = 0; w < kWaves; ++w)
+          if (mw[w][g] != -INFINITY) v += lw[w][g] * __expf(mw[w][g] - Mg);
+      } else {
+        v = accsum[g][i - 2];
+      }
+      a.partial[((pbase + hh) * a.n_splits + split) * (D + 2) + i] = v;
+    }
+
+  }
+}
+
+__global__ __launch_bounds__(128) void qprep_kernel(const float* q, const float* pi, const float* s,
+                                                    float* qprep, int batch, int Hq, int rotate) {
+  __shared__ float qv[D];
+  const int h = blockIdx.x, b = blockIdx.y, layer = blockIdx.z, i = threadIdx.x;
+  const int64_t row = (int64_t(layer) * batch + b) * Hq + h;
+  qv[i] = q[row * D + i];
+  __syncthreads();
+  float* out = qprep + row * 2 * D;
+  if (!rotate) {
+    out[i] = qv[i];
+    out[D + i] = 0.f;
+    return;
+  }
+  const float4* P = reinterpret_cast<const float4*>(pi + int64_t(layer) * D * D + int64_t(i) * D);
+  const float4* S = reinterpret_cast<const float4*>(s + int64_t(layer) * D * D + int64_t(i) * D);
+  float r = 0.f, z = 0.f;
+#pragma unroll
+  for (int j = 0; j < D / 4; ++j) {
+    const float4 pv = P[j], sv = S[j];
+    r = fmaf(pv.x, qv[4 * j], r); r = fmaf(pv.y, qv[4 * j + 1], r);
+    r = fmaf(pv.z, qv[4 * j + 2], r); r = fmaf(pv.w, qv[4 * j + 3], r);
+    z = fmaf(sv.x, qv[4 * j], z); z = fmaf(sv.y, qv[4 * j + 1], z);
+    z = fmaf(sv.z, qv[4 * j + 2], z); z = fmaf(sv.w, qv[4 * j + 3], z);
+  }
+  out[i] = r;
+  out[D + i] = z;
+}
+
+// Merges the split partials of one (layer, batch, KV head): every query head
+// of the group, out = Pi^T (acc / l) (acc / l for fp16 values).  Pi is staged
+// in LDS with one round of vector loads.
+__global__ __launch_bounds__(256) void combine_kernel(const float* partial, const float* pi, float* out, int batch,
+                                                      int H, int Hq, int n_splits, int rotate) {
+  __shared__ float pim[D * D];
+  __shared__ float res[kMaxGroup][D];
+  __shared__ float Mh[kMaxGroup], Lh[kMaxGroup];
+  const int hk = blockIdx.x, b = blockIdx.y, layer = blockIdx.z, tid = threadIdx.x;
+  const int G = Hq / H;
+  if (rotate) {
+    const float4* src = reinterpret_cast<const float4*>(pi + int64_t(layer) * D * D);
+    float4 buf[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) buf[u] = src[tid + 256 * u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) reinterpret_cast<float4*>(pim)[tid + 256 * u] = buf[u];
+  }
+  for (int g0 = 0; g0 < G; g0 += kMaxGroup) {
+    const int ng = G - g0 < kMaxGroup ? G - g0 : kMaxGroup;
+    const int64_t row0 = (int64_t(layer) * batch + b) * Hq + hk * G + g0;
+    // per-head max and normaliser over the splits: 16 threads per head
+    {
+      const int g = tid >> 4, sub = tid & 15;
+      float M = -INFINITY, L = 0.f;
+      if (g < ng) {
+        const float* P = partial + (row0 + g) * int64_t(n_splits) * (D + 2);
+        for (int sp = sub; sp < n_splits; sp += 16) M = fmaxf(M, P[int64_t(sp) * (D + 2)]);
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 16));
+      if (g < ng) {
+        const float* P = partial + (row0 + g) * int64_t(n_splits) * (D + 2);
+        for (int sp = sub; sp < n_splits; sp += 16) {
+          const float ms = P[int64_t(sp) * (D + 2)];
+          L += ms == -INFINITY ? 0.f : P[int64_t(sp) * (D + 2) + 1] * __expf(ms - M);
+        }
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) L += __shfl_xor(L, o, 16);
+      if (g < ng && sub == 0) {
+        Mh[g] = M;
+        Lh[g] = L;
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < ng * D; e += 256) {
+      const int g = e / D, i = e - g * D;
+      const float* P = partial + (row0 + g) * int64_t(n_splits) * (D + 2);
+      const float M = Mh[g], L = Lh[g];
+      float acc = 0.f;
+#pragma unroll 8
+      for (int sp = 0; sp < n_splits; ++sp) {
+        const float ms = P[int64_t(sp) * (D + 2)];
+        const float as = P[int64_t(sp) * (D + 2) + 2 + i];
+        acc += ms == -INFINITY ? 0.f : as * __expf(ms - M);
+      }
+      // L is 0 only for an empty sequence; NaN must propagate.
+      res[g][i] = (L > 0.f || L != L) ? acc / L : 0.f;
+    }
+    __syncthreads();
+    for (int e = tid; e < ng * D; e += 256) {
+      const int g = e / D, i = e - g * D;
+      float o;
+      if (rotate) {
+        o = 0.f;
+#pragma unroll 8
+        for (int j = 0; j < D; ++j) o = fmaf(pim[j * D + i], res[g][j], o);
+      } else {
+        o = res[g][i];
+      }
+      out[(row0 + g) * D + i] = o;
+    }
+    __syncthreads();
+  }
+}
+
+template <bool SCORE>
+tq_status launch_decode(int mk, int bv, const DecodeArgs& args, dim3 grid, hipStream_t st) {
+#define TQ_DEC(MK_, BV_)                                                                       \
+  if (mk == MK_ && bv == BV_) {                                                                \
+    hipLaunchKernelGGL((decode_kernel<MK_, BV_, SCORE>), grid, dim3(256), 0, st, args);       \
+    return TQ_OK;                                                                              \
+  }
+#define TQ_DEC_V(MK_) TQ_DEC(MK_, 0) TQ_DEC(MK_, 1) TQ_DEC(MK_, 2) TQ_DEC(MK_, 4)
+  if constexpr (SCORE) {
+    // Scores do not read values: one instantiation per key format.
+    TQ_DEC(0, 0) TQ_DEC(1, 0) TQ_DEC(2, 0) TQ_DEC(3, 0) TQ_DEC(4, 0)
+  } else {
+    TQ_DEC_V(0) TQ_DEC_V(1) TQ_DEC_V(2) TQ_DEC_V(3) TQ_DEC_V(4)
+  }
+#undef TQ_DEC_V
+#undef TQ_DEC
+  return fail(TQ_ERR_UNSUPPORTED, "no decode kernel for key bits %d / value bits %d", mk, bv);
+}
+
+tq_status check_tables(const tq_format* f, const tq_tables* t, bool need_sketch) {
+  if (!t) return fail(TQ_ERR_INVALID_ARG, "tables is NULL");
+  const bool rot = f->k_bits > 0 || f->v_bits > 0;
+  if (rot && !t->pi) return fail(TQ_ERR_INVALID_ARG, "tables->pi is NULL");
+  if (f->k_bits > 0 && (!t->k_centroids || !t->k_boundaries))
+    return fail(TQ_ERR_INVALID_ARG, "key codebook is NULL");
+  if (f->v_bits > 0 && (!t->v_centroids || !t->v_boundaries))
+    return fail(TQ_ERR_INVALID_ARG, "value codebook is NULL");
+  if (f->k_bits > 0 && need_sketch && !t->pi_s) return fail(TQ_ERR_INVALID_ARG, "tables->pi_s is NULL");
+  if (f->k_bits > 0 && !need_sketch && !t->s) return fail(TQ_ERR_INVALID_ARG, "tables->s is NULL");
+  return TQ_OK;
+}
+
+tq_status check_cache(const tq_format* f, const tq_cache* c) {
+  if (!c) return fail(TQ_ERR_INVALID_ARG, "cache is NULL");
+  if (c->n_layers <= 0 || c->n_kv_heads <= 0 || c->capacity <= 0 || c->capacity % kVBlock)
+    return fail(TQ_ERR_INVALID_ARG, "cache sizes (layers=%d heads=%d capacity=%lld; capacity a positive multiple of 32)",
+                c->n_layers, c->n_kv_heads, (long long)c->capacity);
+  if (f->k_bits > 0 && (!c->k_idx || !c->k_sign || !c->k_norm || !c->k_rnorm))
+    return fail(TQ_ERR_INVALID_ARG, "key planes are NULL");
+  if (f->k_bits == 0 && !c->k_f16) return fail(TQ_ERR_INVALID_ARG, "k_f16 plane is NULL");
+  if (f->v_bits > 0 && (!c->v_idx || !c->v_norm)) return fail(TQ_ERR_INVALID_ARG, "value planes are NULL");
+  if (f->v_bits == 0 && !c->v_f16) return fail(TQ_ERR_INVALID_ARG, "v_f16 plane is NULL");
+  return TQ_OK;
+}
+
+tq_status launch_status(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TQ_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return TQ_OK;
+}
+
+template <bool SCORE>
+tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                        const float* q, int32_t batch, int32_t n_q_heads, const int64_t* seq_start,
+                        const int32_t* seq_len, int64_t max_seq_len, float scale, float* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  tq_status st = check_format(fmt, true);
+  if (st) return st;
+  if ((st = check_tables(fmt, tables, false))) return st;
+  if ((st = check_cache(fmt, cache))) return st;
+  if (!q || !out || !seq_start || !seq_len) return fail(TQ_ERR_INVALID_ARG, "q/out/seq_start/seq_len is NULL");
+  if (batch <= 0 || n_q_heads <= 0 || n_q_heads % cache->n_kv_heads)
+    return fail(TQ_ERR_INVALID_ARG, "batch=%d n_q_heads=%d (must be a positive multiple of n_kv_heads=%d)",
+                batch, n_q_heads, cache->n_kv_heads);
+  if (max_seq_len < 0) return fail(TQ_ERR_INVALID_ARG, "max_seq_len < 0");
+  if (int64_t(cache->n_layers) * batch > 65535)
+    return fail(TQ_ERR_INVALID_ARG, "n_layers * batch exceeds 65535");
+  const SplitPlan plan = plan_decode(fmt->d, cache->n_layers, batch, cache->n_kv_heads, n_q_heads, max_seq_len);
+  if (plan.n_splits > 0x7FFFFFFF) return fail(TQ_ERR_INVALID_ARG, "too many splits");
+  if (!workspace || workspace_bytes < plan.total_bytes)
+    return fail(TQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, plan.total_bytes);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  float* qprep = static_cast<float*>(workspace);
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.qprep_bytes);
+  const int mk = fmt->k_bits > 0 ? fmt->k_bits - 1 : 0;
+  const int bv = fmt->v_bits;
+  hipLaunchKernelGGL(qprep_kernel, dim3(n_q_heads, batch, cache->n_layers), dim3(128), 0, hs, q,
+                     tables->pi, tables->s, qprep, batch, n_q_heads, fmt->k_bits > 0 ? 1 : 0);
+  if ((st = launch_status("qprep"))) return st;
+  if (max_seq_len == 0 && SCORE) return TQ_OK;
+
+  DecodeArgs a{};
+  a.n_layers = cache->n_layers;
+  a.batch = batch;
+  a.H = cache->n_kv_heads;
+  a.Hq = n_q_heads;
+  a.G = n_q_heads / cache->n_kv_heads;
+  a.n_hg = plan.n_head_groups;
+  a.capacity = cache->capacity;
+  a.split_tokens = plan.split_tokens;
+  a.n_splits = int(plan.n_splits);
+  a.k_idx = cache->k_idx;
+  a.k_sign = cache->k_sign;
+  a.k_norm = cache->k_norm;
+  a.k_rnorm = cache->k_rnorm;
+  a.k_f16 = static_cast<const uint16_t*>(cache->k_f16);
+  a.v_idx = cache->v_idx;
+  a.v_norm = cache->v_norm;
+  a.v_f16 = static_cast<const uint16_t*>(cache->v_f16);
+  a.qprep = qprep;
+  a.kc = tables->k_centroids;
+  a.vc = tables->v_centroids;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
+  a.partial = partial;
+  a.logits = out;
+  a.max_len = max_seq_len;
+  a.scale = scale != 0.f ? scale : 1.0f / std::sqrt(float(fmt->d));
+  a.kappa = float(std::sqrt(M_PI / 2.0) / fmt->d);
+  const int64_t gy = int64_t(cache->n_kv_heads) * plan.n_head_groups;
+  if (gy > 65535) return fail(TQ_ERR_INVALID_ARG, "too many KV heads x head groups");
+  dim3 grid(unsigned(plan.n_splits), unsigned(gy), unsigned(cache->n_layers * batch));
+  if ((st = launch_decode<SCORE>(mk, SCORE ? 0 : bv, a, grid, hs))) return st;
+  if ((st = launch_status("decode"))) return st;
+  if (!SCORE) {
+    hipLaunchKernelGGL(combine_kernel, dim3(cache->n_kv_heads, batch, cache->n_layers), dim3(256), 0, hs, partial,
+                       tables->pi, out, batch, cache->n_kv_heads, n_q_heads, int(plan.n_splits), bv > 0 ? 1 : 0);
+    if ((st = launch_status("combine"))) return st;
+  }
+  return TQ_OK;
+}
+
+}  // namespace
+}  // namespace tq
+
+extern "C" {
+
+tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                         const void* k, const void* v, int32_t dtype, int32_t layer0,
+                         int32_t n_layers, int64_t n_tokens, const int64_t* slots, int64_t slot0,
+                         void* stream) {
+  using namespace tq;
+  clear_error();
+  tq_status st = check_format(fmt, true);
+  if (st) return st;
+  if ((st = check_tables(fmt, tables, true))) return st;
+  if ((st = check_cache(fmt, cache))) return st;
+  if (dtype != TQ_DTYPE_F32 && dtype != TQ_DTYPE_BF16 && dtype != TQ_DTYPE_F16)
+    return fail(TQ_ERR_INVALID_ARG, "dtype=%d", dtype);
+  if (n_tokens < 0 || n_layers < 0 || layer0 < 0 || layer0 + n_layers > cache->n_layers)
+    return fail(TQ_ERR_INVALID_ARG, "layers [%d, %d) tokens %lld outside the cache", layer0, layer0 + n_layers,
+                (long long)n_tokens);
+  if (n_tokens == 0 || n_layers == 0) return TQ_OK;
+  if (!k || !v) return fail(TQ_ERR_INVALID_ARG, "k or v is NULL");
+  const int64_t tiles = (n_tokens + kCompressTile - 1) / kCompressTile;
+  // Several 16-token tiles per workgroup amortise the Pi / S Pi^T staging;
+  // aim at about 1536 workgroups in the call.
+  int64_t tpw = (tiles * n_layers + 1535) / 1536;
+  if (tpw < 1) tpw = 1;
+  const int64_t wgs = (tiles + tpw - 1) / tpw;
+  if (wgs > 0x7FFFFFFF || n_layers > 65535) return fail(TQ_ERR_INVALID_ARG, "too many tokens or layers");
+  CompressArgs a{};
+  a.k = k;
+  a.v = v;
+  a.dtype = dtype;
+  a.layer0 = layer0;
+  a.n_tokens = n_tokens;
+  a.slots = slots;
+  a.slot0 = slot0;
+  a.H = cache->n_kv_heads;
+  a.capacity = cache->capacity;
+  a.mk = fmt->k_bits > 0 ? fmt->k_bits - 1 : 0;
+  a.bv = fmt->v_bits;
+  a.tiles_per_wg = tpw;
+  a.pi = tables->pi;
+  a.pi_s = tables->pi_s;
+  a.kc = tables->k_centroids;
+  a.kb = tables->k_boundaries;
+  a.vc = tables->v_centroids;
+  a.vb = tables->v_boundaries;
+  a.k_idx = cache->k_idx;
+  a.k_sign = cache->k_sign;
+  a.k_norm = cache->k_norm;
+  a.k_rnorm = cache->k_rnorm;
+  a.k_f16 = static_cast<uint16_t*>(cache->k_f16);
+  a.v_idx = cache->v_idx;
+  a.v_norm = cache->v_norm;
+  a.v_f16 = static_cast<uint16_t*>(cache->v_f16);
+  const size_t smem = sizeof(CompressSmem);
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(compress_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, int(smem)) != hipSuccess)
+    return fail(TQ_ERR_HIP, "cannot raise the LDS limit to %zu bytes", smem);
+  hipLaunchKernelGGL(compress_kernel, dim3(unsigned(wgs), unsigned(n_layers)), dim3(256), smem,
+                     static_cast<hipStream_t>(stream), a);
+  return launch_status("compress");
+}
+
+tq_status tq_decode_attention(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                              const float* q, int32_t batch, int32_t n_q_heads,
+                              const int64_t* seq_start, const int32_t* seq_len,
+                              int64_t max_seq_len, float scale, float* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return tq::decode_common<false>(fmt, tables, cache, q, batch, n_q_heads, seq_start, seq_len, max_seq_len,
+                                  scale, out, workspace, workspace_bytes, stream);
+}
+
+tq_status tq_score(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                   const float* q, int32_t batch, int32_t n_q_heads, const int64_t* seq_start,
+                   const int32_t* seq_len, int64_t max_seq_len, float scale, float* logits,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  return tq::decode_common<true>(fmt, tables, cache, q, batch, n_q_heads, seq_start, seq_len, max_seq_len,
+                                 scale, logits, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

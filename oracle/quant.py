@@ -87,13 +87,16 @@ def _normalise(x: np.ndarray):
     return n, xhat
 
 
-def compress_v(x: np.ndarray, pi: np.ndarray, centroids, boundaries):
+def compress_v(x: np.ndarray, pi: np.ndarray, centroids, boundaries, return_y: bool = False):
     """MSE-only (PolarQuant) compression of rows of x [N, d].
-    Returns (idx uint8 [N, d], norm float64 [N])."""
+    Returns (idx uint8 [N, d], norm float64 [N]) and, with return_y, the
+    rotated unit vectors y (for locating coordinates near a boundary)."""
     n, xhat = _normalise(x)
     y = xhat @ pi.T                       # y = Pi x/||x||, one row per vector
     # NaN input: keep y NaN so the decision gives code 0 as in IEEE compares.
     y = np.where(np.isnan(n)[..., None], np.nan, y)
+    if return_y:
+        return decide(y, boundaries), n, y
     return decide(y, boundaries), n
 
 
@@ -101,13 +104,16 @@ def compress_k(x: np.ndarray, pi: np.ndarray, s: np.ndarray, centroids, boundari
     """TurboQuantProd compression of rows of x [N, d] with a (k_bits-1)-bit
     codebook.  Returns dict(idx, sign (0/1 uint8), norm, rnorm)."""
     x = np.asarray(x, np.float64)
-    idx, n = compress_v(x, pi, centroids, boundaries)
+    idx, n, y = compress_v(x, pi, centroids, boundaries, return_y=True)
     xt = n[..., None] * (np.asarray(centroids)[idx] @ pi)   # ||x|| Pi^T c[idx]
     r = x - xt
     sr = r @ s.T                                             # S r
     sign = (sr >= 0).astype(np.uint8)
     rnorm = np.linalg.norm(r, axis=-1)
-    return dict(idx=idx, sign=sign, norm=n, rnorm=rnorm)
+    # y and S r / ||x|| are returned for locating decisions near a boundary.
+    with np.errstate(invalid="ignore", divide="ignore"):
+        sr_rel = sr / np.where(n > 0, n, 1.0)[..., None]
+    return dict(idx=idx, sign=sign, norm=n, rnorm=rnorm, y=y, sr_rel=sr_rel)
 
 
 def dequantize_mse(idx, norm, pi, centroids):
@@ -216,12 +222,12 @@ def compress_into(cache: dict, k: np.ndarray, v: np.ndarray, slots: np.ndarray,
         else:
             cache["k_f16"][hh, slots] = np.asarray(k[:, hh], np.float16)
         if fmt.v_bits > 0:
-            idx, nv = compress_v(v[:, hh], pi, *cb_v)
+            idx, nv, yv = compress_v(v[:, hh], pi, *cb_v, return_y=True)
             cache["v_norm"][hh, slots] = nv.astype(np.float32)
             full = unpack_v_blocks(cache["v_idx"][hh], fmt.v_bits)
             full[slots] = idx
             cache["v_idx"][hh] = pack_v_blocks(full, fmt.v_bits)
-            out[("v", hh)] = dict(idx=idx, norm=nv)
+            out[("v", hh)] = dict(idx=idx, norm=nv, y=yv)
         else:
             full = f16_v_unblock(cache["v_f16"][hh]).copy()
             full[slots] = np.asarray(v[:, hh], np.float16)

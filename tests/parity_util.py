@@ -1,0 +1,206 @@
+"""Helpers shared by the GPU parity tests: build oracle caches for a workload,
+move packed planes between the oracle layout and the device, and compare
+codes with the near-boundary allowance.
+
+Test infrastructure: it calls the oracle and the HIP library side by side,
+and never feeds anything the library produced into the oracle.
+"""
+import math
+from typing import Dict, List, Tuple
+
+import numpy as np
+
+import workloads as wl
+from oracle import attention, codebook, quant, rotation
+
+D = 128
+NEAR = 1e-6          # a decision within this distance of its threshold may differ
+MAX_MISMATCH_RATE = 1e-5
+
+
+def layer_format(w: wl.Workload, layer: int) -> quant.Format:
+    mode = w.modes()[layer]
+    if mode == wl.MODE_TQ:
+        return quant.Format(D, w.k_bits, w.v_bits)
+    if mode == wl.MODE_KF16:
+        return quant.Format(D, 0, w.v_bits)
+    return quant.Format(D, 0, 0)
+
+
+def layer_groups(w: wl.Workload) -> List[Tuple[quant.Format, List[int]]]:
+    """Consecutive layers that share a storage format."""
+    groups: List[Tuple[quant.Format, List[int]]] = []
+    for layer in range(w.n_layers):
+        f = layer_format(w, layer)
+        if groups and groups[-1][0] == f:
+            groups[-1][1].append(layer)
+        else:
+            groups.append((f, [layer]))
+    return groups
+
+
+def tq_format(f: quant.Format):
+    import kv_cache_quantization_norm_amd as tq
+    return tq.make_format(f.d, f.k_bits, f.v_bits)
+
+
+def slots_of(w: wl.Workload):
+    starts, lens, cap = wl.seq_layout(w)
+    slots = np.concatenate([np.arange(s, s + n) for s, n in zip(starts, lens)]).astype(np.int64)
+    return starts, lens, max(cap, 32), slots
+
+
+def oracle_tables(fmt: quant.Format, layer: int):
+    pi, s = rotation.layer_rotations(D, layer)
+    cbk = codebook.codebook(D, fmt.k_mse_bits) if fmt.k_bits else None
+    cbv = codebook.codebook(D, fmt.v_bits) if fmt.v_bits else None
+    return pi, s, cbk, cbv
+
+
+def oracle_compress_layer(w: wl.Workload, layer: int, fmt: quant.Format, k, v, slots, capacity):
+    pi, s, cbk, cbv = oracle_tables(fmt, layer)
+    cache = quant.empty_cache(fmt, w.n_kv_heads, capacity)
+    details = quant.compress_into(cache, k.astype(np.float64), v.astype(np.float64), slots, pi, s, cbk, cbv)
+    return cache, details
+
+
+PLANE_DTYPES = {"k_idx": np.uint8, "k_sign": np.uint8, "k_norm": np.float32, "k_rnorm": np.float32,
+                "k_f16": np.float16, "v_idx": np.uint8, "v_norm": np.float32, "v_f16": np.float16}
+
+
+def upload_cache(caches: List[dict], fmt: quant.Format, device="cuda"):
+    """Device cache holding the given per-layer oracle caches."""
+    import torch
+    import kv_cache_quantization_norm_amd as tq
+    h, cap = caches[0]["n_kv_heads"], caches[0]["capacity"]
+    dev = tq.Cache.allocate(tq_format(fmt), len(caches), h, cap, device)
+    for name, t in dev.planes.items():
+        if t is None:
+            continue
+        host = np.stack([c[name] for c in caches]).reshape(-1)
+        if host.dtype == np.float16:
+            t.copy_(torch.from_numpy(host.view(np.int16)).view(torch.float16))
+        else:
+            t.copy_(torch.from_numpy(np.ascontiguousarray(host)))
+    return dev
+
+
+def download_cache(dev, fmt: quant.Format) -> List[dict]:
+    """Per-layer oracle-layout copies of a device cache."""
+    out = []
+    shapes = quant.empty_cache(fmt, dev.n_kv_heads, dev.capacity)
+    host = {}
+    for name, t in dev.planes.items():
+        if t is None:
+            continue
+        a = t.cpu().numpy()
+        host[name] = a.reshape((dev.n_layers,) + shapes[name].shape)
+    for l in range(dev.n_layers):
+        c = dict(fmt=fmt, n_kv_heads=dev.n_kv_heads, capacity=dev.capacity)
+        for name, a in host.items():
+            c[name] = a[l]
+        out.append(c)
+    return out
+
+
+def near_boundary(y: np.ndarray, boundaries) -> np.ndarray:
+    t = np.asarray(boundaries, np.float64)
+    return np.min(np.abs(np.asarray(y, np.float64)[..., None] - t), axis=-1) < NEAR
+
+
+def compare_layer(gpu: dict, ora: dict, details: Dict, fmt: quant.Format, slots: np.ndarray,
+                  cbk, cbv) -> Dict[str, int]:
+    """Checks one layer's device planes against the oracle.  Returns counts."""
+    stats = dict(coords=0, k_mismatch=0, s_mismatch=0, v_mismatch=0, tokens_skipped_for_signs=0)
+    h_n = ora["n_kv_heads"]
+    for h in range(h_n):
+        if fmt.k_bits > 0:
+            det = details[("k", h)]
+            gi = quant.unpack_bits(gpu["k_idx"][h, slots], fmt.k_mse_bits, D)
+            bad = gi != det["idx"]
+            if bad.any():
+                assert np.all(near_boundary(det["y"][bad], cbk[1])), "key code mismatch away from a boundary"
+            stats["k_mismatch"] += int(bad.sum())
+            stats["coords"] += bad.size
+            # norms
+            np.testing.assert_allclose(gpu["k_norm"][h, slots], det["norm"], rtol=1e-6, atol=1e-30)
+            np.testing.assert_allclose(gpu["k_rnorm"][h, slots], det["rnorm"], rtol=2e-6, atol=1e-6 * det["norm"].max())
+            # signs, on tokens whose codes agree (a code flip changes the residual)
+            same = ~bad.any(axis=1)
+            stats["tokens_skipped_for_signs"] += int((~same).sum())
+            gs = quant.unpack_bits(gpu["k_sign"][h, slots], 1, D)
+            sbad = (gs != det["sign"]) & same[:, None]
+            if sbad.any():
+                assert np.all(np.abs(det["sr_rel"][sbad]) < NEAR), "sign mismatch away from zero"
+            stats["s_mismatch"] += int(sbad.sum())
+            if not bad.any() and not sbad.any():
+                assert np.array_equal(gpu["k_idx"][h, slots], ora["k_idx"][h, slots])
+                assert np.array_equal(gpu["k_sign"][h, slots], ora["k_sign"][h, slots])
+        else:
+            assert np.array_equal(gpu["k_f16"][h, slots].view(np.uint16), ora["k_f16"][h, slots].view(np.uint16))
+        if fmt.v_bits > 0:
+            det = details[("v", h)]
+            gv = quant.unpack_v_blocks(gpu["v_idx"][h], fmt.v_bits)[slots]
+            bad = gv != det["idx"]
+            if bad.any():
+                assert np.all(near_boundary(det["y"][bad], cbv[1])), "value code mismatch away from a boundary"
+            stats["v_mismatch"] += int(bad.sum())
+            stats["coords"] += bad.size
+            np.testing.assert_allclose(gpu["v_norm"][h, slots], det["norm"], rtol=1e-6, atol=1e-30)
+        else:
+            gv = quant.f16_v_unblock(gpu["v_f16"][h])[slots].view(np.uint16)
+            ov = quant.f16_v_unblock(ora["v_f16"][h])[slots].view(np.uint16)
+            assert np.array_equal(gv, ov)
+    return stats
+
+
+def check_logits(gpu_logits: np.ndarray, ora_logits: Dict, lens, hq, tol=1e-3):
+    """|dl_t| <= tol * max_t |l_t| per query row.  Returns the worst ratio."""
+    worst, where = 0.0, None
+    for b, n in enumerate(lens):
+        for h in range(hq):
+            ref = ora_logits[(b, h)]
+            if n == 0:
+                continue
+            got = gpu_logits[b, h, :n]
+            scale = np.max(np.abs(ref))
+            err = np.max(np.abs(got - ref))
+            if err / scale > worst:
+                worst, where = err / scale, (b, h, n, float(scale), float(err))
+    assert worst <= tol, f"logit error {worst:.3e} of the row maximum exceeds {tol} at (b, h, len, max, err) {where}"
+    return worst
+
+
+def check_outputs(gpu_out: np.ndarray, ora_out: np.ndarray, tol=2e-3):
+    err = float(np.max(np.abs(gpu_out.astype(np.float64) - ora_out)))
+    assert err <= tol, f"output max-abs error {err:.3e} exceeds {tol}"
+    return err
+
+
+def sanitize_near_boundary(fmt: quant.Format, layer: int, k: np.ndarray, v: np.ndarray,
+                           heads=None) -> Tuple[np.ndarray, np.ndarray, int]:
+    """Zero the key and value of every (token, head) whose oracle compression
+    has a decision within NEAR of its threshold (a code, or a QJL sign).
+
+    Such a decision may legitimately go either way, and one flipped key code
+    changes that token's whole residual sketch, so end-to-end outputs are only
+    unique away from these inputs.  The flags come from the oracle alone; a zero
+    vector compresses deterministically on both sides.  Returns the new arrays
+    and the number of (token, head) pairs zeroed."""
+    pi, s, cbk, cbv = oracle_tables(fmt, layer)
+    k = k.copy()
+    v = v.copy()
+    zeroed = 0
+    for h in (range(k.shape[1]) if heads is None else heads):
+        flag = np.zeros(k.shape[0], bool)
+        if fmt.k_bits > 0:
+            rec = quant.compress_k(k[:, h].astype(np.float64), pi, s, *cbk)
+            flag |= near_boundary(rec["y"], cbk[1]).any(axis=1)
+            flag |= (np.abs(rec["sr_rel"]) < NEAR).any(axis=1)
+        if fmt.v_bits > 0:
+            _, _, y = quant.compress_v(v[:, h].astype(np.float64), pi, *cbv, return_y=True)
+            flag |= near_boundary(y, cbv[1]).any(axis=1)
+        k[flag, h] = 0.0
+        v[flag, h] = 0.0
+        zeroed += int(flag.sum())
+    return k, v, zeroed

@@ -1,0 +1,290 @@
+"""GPU parity: the HIP library against the float64 oracle, through the C ABI.
+
+Compression: codes bit-exact except decisions within 1e-6 of their threshold
+(at most a 1e-5 fraction of coordinates), norms to 1e-6 relative.
+Decode: the oracle's own packed cache is uploaded and decoded on the GPU;
+logits within 1e-3 of each row's largest magnitude, outputs within 2e-3
+max-abs.  End to end: GPU compress + GPU decode against oracle compress +
+oracle decode, same output bound.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import attention, quant
+from tests import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import kv_cache_quantization_norm_amd  # noqa: F401  (fails loudly if libtq.so is missing)
+    yield
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _torch_dtype(w):
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.dtype]
+
+
+CASES = {
+    "w1": wl.W1,
+    "w2_4L_ragged": wl.reduced(wl.W2, (1000,), n_layers=4),
+    "w3_6L_asym": wl.reduced(wl.W3, (700,), n_layers=6),
+    "w4_h8_t3000": wl.reduced(wl.W4, (3000,)),
+    "w5_ragged5": wl.reduced(wl.W5, (100, 0, 333, 64, 1)),
+    "g20_k5v1": wl.Workload("g20_k5v1", 1, 2, 40, (257,), 5, 1, "f16", 0.3, 1, 5.0),
+    "g1_k2v2": wl.Workload("g1_k2v2", 2, 3, 3, (95, 31), 2, 2, "f32", 0.0, 0, 1.0),
+}
+
+
+def _inputs(w, layers, fmt=None, sanitize=False):
+    ks, vs = [], []
+    for layer in layers:
+        k, v = wl.gen_kv(w, layer)
+        if sanitize:
+            k, v, n = pu.sanitize_near_boundary(fmt, layer, k, v)
+            _say("layer", layer, "zeroed near-boundary (token, head) pairs:", n)
+        ks.append(k)
+        vs.append(v)
+    return np.stack(ks), np.stack(vs)
+
+
+def _run_group(w, fmt, layers, dev_compress=True, sanitize=False):
+    """Compress a group of layers on the GPU and with the oracle."""
+    import kv_cache_quantization_norm_amd as tq
+    starts, lens, cap, slots = pu.slots_of(w)
+    K, V = _inputs(w, layers, fmt, sanitize)
+    tfmt = pu.tq_format(fmt)
+    tables = tq.Tables.create(tfmt, layers)
+    ora_caches, ora_details = [], []
+    for i, layer in enumerate(layers):
+        c, det = pu.oracle_compress_layer(w, layer, fmt, K[i], V[i], slots, cap)
+        ora_caches.append(c)
+        ora_details.append(det)
+    dev = None
+    if dev_compress:
+        dev = tq.Cache.allocate(tfmt, len(layers), w.n_kv_heads, cap)
+        dt = _torch_dtype(w)
+        kt = torch.from_numpy(K).to("cuda", dt).contiguous()
+        vt = torch.from_numpy(V).to("cuda", dt).contiguous()
+        st = torch.from_numpy(slots).cuda()
+        if len(w.seq_lens) == 1:
+            tq.tq_compress_kv(tfmt, tables, dev, kt, vt, layer0=0, slots=None, slot0=int(starts[0]))
+        else:
+            tq.tq_compress_kv(tfmt, tables, dev, kt, vt, layer0=0, slots=st)
+        torch.cuda.synchronize()
+    return tables, dev, ora_caches, ora_details, (starts, lens, cap, slots)
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_compress_parity(case):
+    w = CASES[case]
+    _say("compress", case)
+    total = dict(coords=0, k_mismatch=0, s_mismatch=0, v_mismatch=0)
+    for fmt, layers in pu.layer_groups(w):
+        tables, dev, ora_caches, ora_details, (starts, lens, cap, slots) = _run_group(w, fmt, layers)
+        gpu_caches = pu.download_cache(dev, fmt)
+        for i, layer in enumerate(layers):
+            _, _, cbk, cbv = pu.oracle_tables(fmt, layer)
+            st = pu.compare_layer(gpu_caches[i], ora_caches[i], ora_details[i], fmt, slots, cbk, cbv)
+            for k in total:
+                total[k] += st[k]
+            # slots outside the sequences stay zero
+            used = np.zeros(cap, bool)
+            used[slots] = True
+            for name in ("k_norm", "v_norm"):
+                if name in gpu_caches[i]:
+                    assert np.all(gpu_caches[i][name][:, ~used] == 0)
+    _say("mismatches", total)
+    if total["coords"]:
+        rate = (total["k_mismatch"] + total["v_mismatch"]) / total["coords"]
+        assert rate <= pu.MAX_MISMATCH_RATE, rate
+
+
+def _decode_gpu(fmt, tables, dev, Q, starts, lens, want_logits=True):
+    import kv_cache_quantization_norm_amd as tq
+    tfmt = pu.tq_format(fmt)
+    n_layers, batch, hq, _ = Q.shape
+    max_len = int(max(lens)) if len(lens) else 0
+    qt = torch.from_numpy(Q).cuda().contiguous()
+    st = torch.from_numpy(np.asarray(starts, np.int64)).cuda()
+    ln = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+    ws = tq.workspace_for(tfmt, dev, batch, hq, max_len)
+    out = torch.full((n_layers, batch, hq, 128), float("nan"), device="cuda")
+    tq.tq_decode_attention(tfmt, tables, dev, qt, st, ln, max_len, out, ws)
+    logits = None
+    if want_logits:
+        logits = torch.full((n_layers, batch, hq, max(max_len, 1)), float("nan"), device="cuda")
+        tq.tq_score(tfmt, tables, dev, qt, st, ln, max_len, logits, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (logits.cpu().numpy() if logits is not None else None)
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_decode_parity_on_oracle_cache(case):
+    w = CASES[case]
+    _say("decode", case)
+    for fmt, layers in pu.layer_groups(w):
+        tables, _, ora_caches, _, (starts, lens, cap, slots) = _run_group(w, fmt, layers, dev_compress=False)
+        dev = pu.upload_cache(ora_caches, fmt)
+        Q = np.stack([wl.gen_q(w, layer) for layer in layers])
+        out, logits = _decode_gpu(fmt, tables, dev, Q, starts, lens)
+        worst_l, worst_o = 0.0, 0.0
+        for i, layer in enumerate(layers):
+            pi, s, cbk, cbv = pu.oracle_tables(fmt, layer)
+            ref, ref_logits = attention.decode_attention(ora_caches[i], Q[i], starts, lens, pi, s, cbk, cbv,
+                                                         return_logits=True)
+            worst_l = max(worst_l, pu.check_logits(logits[i], ref_logits, lens, w.n_q_heads))
+            worst_o = max(worst_o, pu.check_outputs(out[i], ref))
+            for b, n in enumerate(lens):
+                if n == 0:
+                    assert np.all(out[i, b] == 0)
+        _say("format", fmt, "worst logit rel", f"{worst_l:.2e}", "worst out abs", f"{worst_o:.2e}")
+
+
+@pytest.mark.parametrize("case", ["w1", "w2_4L_ragged", "w3_6L_asym", "w5_ragged5"])
+def test_end_to_end(case):
+    """GPU compress + GPU decode against oracle compress + oracle decode, on
+    inputs with no decision within 1e-6 of its threshold (there the output is
+    unique; near-threshold behaviour is covered by test_compress_parity)."""
+    w = CASES[case]
+    _say("end-to-end", case)
+    for fmt, layers in pu.layer_groups(w):
+        tables, dev, ora_caches, ora_details, (starts, lens, cap, slots) = _run_group(w, fmt, layers, sanitize=True)
+        gpu_caches = pu.download_cache(dev, fmt)
+        for i, layer in enumerate(layers):
+            _, _, cbk, cbv = pu.oracle_tables(fmt, layer)
+            st = pu.compare_layer(gpu_caches[i], ora_caches[i], ora_details[i], fmt, slots, cbk, cbv)
+            assert st["k_mismatch"] == st["v_mismatch"] == st["s_mismatch"] == 0, st
+        Q = np.stack([wl.gen_q(w, layer) for layer in layers])
+        out, _ = _decode_gpu(fmt, tables, dev, Q, starts, lens, want_logits=False)
+        for i, layer in enumerate(layers):
+            pi, s, cbk, cbv = pu.oracle_tables(fmt, layer)
+            ref = attention.decode_attention(ora_caches[i], Q[i], starts, lens, pi, s, cbk, cbv)
+            pu.check_outputs(out[i], ref)
+
+
+def test_degenerate_vectors_and_nan():
+    """Zero keys/values compress to zero norms and contribute nothing; a NaN key
+    makes its sequence's outputs NaN and leaves other sequences finite."""
+    import kv_cache_quantization_norm_amd as tq
+    _say("degenerate")
+    w = wl.Workload("degenerate", 1, 1, 2, (40, 40), 4, 4, "f32", 0.0, 0, 1.0)
+    fmt = pu.layer_format(w, 0)
+    starts, lens, cap, slots = pu.slots_of(w)
+    K, V = _inputs(w, [0])
+    K[0, 3] = 0.0
+    V[0, 5] = 0.0
+    K[0, 50, 0, 7] = np.nan       # second sequence (starts at slot 64 -> token index 40..79)
+    tfmt = pu.tq_format(fmt)
+    tables = tq.Tables.create(tfmt, [0])
+    dev = tq.Cache.allocate(tfmt, 1, 1, cap)
+    tq.tq_compress_kv(tfmt, tables, dev, torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(),
+                      slots=torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    g = pu.download_cache(dev, fmt)[0]
+    s3 = slots[3]
+    assert g["k_norm"][0, s3] == 0 and g["k_rnorm"][0, s3] == 0
+    assert np.all(quant.unpack_bits(g["k_sign"][0, s3:s3 + 1], 1, 128) == 1)
+    assert np.all(quant.unpack_bits(g["k_idx"][0, s3:s3 + 1], 3, 128) == 4)
+    assert g["v_norm"][0, slots[5]] == 0
+    s50 = slots[50]
+    assert np.isnan(g["k_norm"][0, s50]) and np.isnan(g["k_rnorm"][0, s50])
+    assert np.all(quant.unpack_bits(g["k_idx"][0, s50:s50 + 1], 3, 128) == 0)
+    Q = wl.gen_q(w, 0)[None]
+    out, _ = _decode_gpu(fmt, tables, dev, Q, starts, lens, want_logits=False)
+    assert np.all(np.isfinite(out[0, 0])) and np.all(np.isnan(out[0, 1]))
+    # matches the oracle on the finite sequence
+    c, _ = pu.oracle_compress_layer(w, 0, fmt, K[0], V[0], slots, cap)
+    pi, s, cbk, cbv = pu.oracle_tables(fmt, 0)
+    ref = attention.decode_attention(c, Q[0][:1], starts[:1], lens[:1], pi, s, cbk, cbv)
+    pu.check_outputs(out[0, :1], ref)
+
+
+def test_overwrite_slot_and_append():
+    """Re-compressing into used slots replaces their records (value codes are
+    rewritten inside shared 32-slot groups), one token at a time."""
+    import kv_cache_quantization_norm_amd as tq
+    _say("append")
+    w = wl.Workload("append", 2, 2, 4, (70,), 4, 2, "bf16", 0.5, 1, 10.0)
+    fmt = pu.layer_format(w, 0)
+    starts, lens, cap, slots = pu.slots_of(w)
+    K, V = _inputs(w, [0, 1])
+    tfmt = pu.tq_format(fmt)
+    tables = tq.Tables.create(tfmt, [0, 1])
+    dev = tq.Cache.allocate(tfmt, 2, 2, cap)
+    dt = torch.bfloat16
+    # first fill with garbage (shifted tokens), then append the real tokens one by one
+    kt = torch.from_numpy(np.roll(K, 3, axis=1)).to("cuda", dt).contiguous()
+    vt = torch.from_numpy(np.roll(V, 5, axis=1)).to("cuda", dt).contiguous()
+    tq.tq_compress_kv(tfmt, tables, dev, kt, vt, slot0=0)
+    kr = torch.from_numpy(K).to("cuda", dt)
+    vr = torch.from_numpy(V).to("cuda", dt)
+    for i in range(70):
+        tq.tq_compress_kv(tfmt, tables, dev, kr[:, i:i + 1].contiguous(), vr[:, i:i + 1].contiguous(), slot0=i)
+    torch.cuda.synchronize()
+    gpu = pu.download_cache(dev, fmt)
+    for layer in (0, 1):
+        c, det = pu.oracle_compress_layer(w, layer, fmt, K[layer], V[layer], slots, cap)
+        _, _, cbk, cbv = pu.oracle_tables(fmt, layer)
+        pu.compare_layer(gpu[layer], c, det, fmt, slots, cbk, cbv)
+
+
+@pytest.mark.parametrize("short", ["w2", "w4"])
+def test_full_size_sampled(short):
+    """Full workload size in the benchmark's launch configuration (every layer in
+    one compress call and one decode call); the oracle recomputes sampled
+    (layer, KV head) pairs end to end."""
+    import kv_cache_quantization_norm_amd as tq
+    w = wl.BY_SHORT[short]
+    _say("full-size", w.name)
+    fmt, layers = pu.layer_groups(w)[0]
+    starts, lens, cap, slots = pu.slots_of(w)
+    tfmt = pu.tq_format(fmt)
+    tables = tq.Tables.create(tfmt, layers)
+    dev = tq.Cache.allocate(tfmt, len(layers), w.n_kv_heads, cap)
+    dt = _torch_dtype(w)
+    rs = np.random.default_rng(1)
+    samples = [(int(rs.integers(len(layers))), int(rs.integers(w.n_kv_heads))) for _ in range(2)]
+    sampled_inputs = {}
+    for i, layer in enumerate(layers):
+        k, v = wl.gen_kv(w, layer)
+        heads = [kvh for li, kvh in samples if li == i]
+        if heads:
+            # sampled heads: no decision within 1e-6 of its threshold (see test_end_to_end)
+            k, v, n = pu.sanitize_near_boundary(fmt, layer, k, v, heads=heads)
+            _say("layer", layer, "heads", heads, "zeroed", n)
+            sampled_inputs[i] = (k, v)
+        kt = torch.from_numpy(k).to("cuda", dt)[None].contiguous()
+        vt = torch.from_numpy(v).to("cuda", dt)[None].contiguous()
+        tq.tq_compress_kv(tfmt, tables, dev, kt, vt, layer0=i, slot0=0)
+    Q = np.stack([wl.gen_q(w, layer) for layer in layers])
+    out, _ = _decode_gpu(fmt, tables, dev, Q, starts, lens, want_logits=False)
+    G = w.group
+    for li, kvh in samples:
+        layer = layers[li]
+        k, v = sampled_inputs[li]
+        one = w.with_(n_kv_heads=1, n_q_heads=G, name=w.name + "_one_head")
+        c, det = pu.oracle_compress_layer(one, layer, fmt, k[:, kvh:kvh + 1], v[:, kvh:kvh + 1], slots, cap)
+        pi, s, cbk, cbv = pu.oracle_tables(fmt, layer)
+        gl = pu.download_cache(dev, fmt)[li]
+        sub = {n: (a[kvh:kvh + 1] if isinstance(a, np.ndarray) else a) for n, a in gl.items()}
+        sub["n_kv_heads"] = 1
+        st = pu.compare_layer(sub, c, det, fmt, slots, cbk, cbv)
+        _say("sample", layer, kvh, st)
+        qh = Q[li][:, kvh * G:(kvh + 1) * G]
+        ref = attention.decode_attention(c, qh, starts, lens, pi, s, cbk, cbv)
+        err = pu.check_outputs(out[li][:, kvh * G:(kvh + 1) * G], ref)
+        _say("sample out err", f"{err:.2e}")

@@ -1,0 +1,121 @@
+"""The C ABI on the CPU: the library loads, exports what include/tq.h declares,
+its host generators agree with the oracle, and the device entry points reject
+bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_quantization_norm_amd as tq
+from oracle import codebook, quant, rotation
+from tests.conftest import ROOT, load_golden
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(tq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(tq.EXPORTED)
+
+
+def test_layer_seed_matches_page():
+    g = load_golden("page_constants.json")["layer_seed"]
+    for layer, seed in g["examples"].items():
+        assert tq.tq_layer_seed(int(layer)) == seed
+
+
+@pytest.mark.parametrize("d,layer", [(128, 0), (128, 5), (64, 1), (16, 27)])
+def test_rotations_match_oracle(d, layer):
+    seed = tq.tq_layer_seed(layer)
+    pi, s, m = tq.tq_make_rotations(d, seed)
+    opi, os_ = rotation.make_rotations(d, seed)   # fp32-stored values as float64
+    assert np.max(np.abs(pi.astype(np.float64) - opi)) <= 1e-6
+    assert np.mean(pi.astype(np.float64) == opi) > 0.999
+    assert np.max(np.abs(s.astype(np.float64) - os_)) <= 1e-6
+    assert np.mean(s.astype(np.float64) == os_) > 0.999
+    ref_m = os_ @ opi.T
+    assert np.max(np.abs(m.astype(np.float64) - ref_m)) <= 2e-5 * max(1.0, np.max(np.abs(ref_m)))
+    p64 = pi.astype(np.float64)
+    assert np.max(np.abs(p64.T @ p64 - np.eye(d))) < 2e-6
+
+
+@pytest.mark.parametrize("d,bits", [(128, 1), (128, 2), (128, 3), (128, 4), (64, 2), (32, 3)])
+def test_codebook_matches_oracle(d, bits):
+    c, t = tq.tq_make_codebook(d, bits)
+    oc, ot = codebook.codebook(d, bits)
+    assert np.max(np.abs(c - oc)) < 1e-12
+    assert np.max(np.abs(t - ot)) < 1e-12
+    assert np.array_equal(c, -c[::-1]) and t[len(t) // 2] == 0.0
+    # fp32 tables (what the device uses) round identically
+    assert np.array_equal(c.astype(np.float32), oc.astype(np.float32))
+    assert np.array_equal(t.astype(np.float32), ot.astype(np.float32))
+
+
+@pytest.mark.parametrize("kb,vb", [(3, 2), (4, 4), (0, 4), (0, 0), (5, 1), (2, 2)])
+def test_plane_sizes_match_oracle_layout(kb, vb):
+    fmt = tq.make_format(128, kb, vb)
+    sizes = dict(zip(tq.PLANES, tq.tq_cache_plane_bytes(fmt, 3, 2, 96)))
+    ocs = [quant.empty_cache(quant.Format(128, kb, vb), 2, 96) for _ in range(3)]
+    for name, nbytes in sizes.items():
+        if nbytes == 0:
+            assert name not in ocs[0]
+        else:
+            assert nbytes == 3 * ocs[0][name].nbytes, name
+
+
+def test_workspace_query():
+    fmt = tq.make_format(128, 4, 4)
+    n = tq.tq_decode_workspace_bytes(fmt, 28, 1, 4, 28, 8192)
+    assert n > 28 * 28 * 2 * 128 * 4
+    assert tq.tq_decode_workspace_bytes(fmt, 1, 1, 4, 6, 10) == 0  # 6 % 4 != 0
+
+
+FAKE = 0x1000  # never dereferenced: validation fails first
+
+
+def _tables_struct(fmt):
+    return tq.tq_tables(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def _cache_struct(layers=1, heads=1, cap=64):
+    return tq.tq_cache(layers, heads, cap, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def test_device_calls_validate_before_launch():
+    r = tq.raw_call
+    P = ctypes.byref
+    fmt = tq.make_format(128, 4, 4)
+    tb, cs = _tables_struct(fmt), _cache_struct()
+    # unsupported format on device
+    assert r("tq_compress_kv", P(tq.make_format(64, 4, 4)), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_UNSUPPORTED
+    assert r("tq_compress_kv", P(tq.make_format(128, 4, 3)), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_UNSUPPORTED
+    assert r("tq_compress_kv", P(tq.make_format(128, 6, 4)), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_UNSUPPORTED
+    # NULL and inconsistent arguments
+    assert r("tq_compress_kv", P(fmt), None, P(cs), FAKE, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_INVALID_ARG
+    assert r("tq_compress_kv", P(fmt), P(tb), P(_cache_struct(cap=50)), FAKE, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_INVALID_ARG
+    assert r("tq_compress_kv", P(fmt), P(tb), P(cs), FAKE, FAKE, 7, 0, 1, 1, None, 0, None) == tq.TQ_ERR_INVALID_ARG
+    assert r("tq_compress_kv", P(fmt), P(tb), P(cs), FAKE, FAKE, 0, 1, 1, 1, None, 0, None) == tq.TQ_ERR_INVALID_ARG
+    assert r("tq_compress_kv", P(fmt), P(tb), P(cs), None, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_INVALID_ARG
+    # nothing to do is fine without a GPU
+    assert r("tq_compress_kv", P(fmt), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 0, None, 0, None) == tq.TQ_OK
+    # decode: heads not a multiple, too-small workspace
+    cs4 = _cache_struct(heads=4)
+    assert r("tq_decode_attention", P(fmt), P(tb), P(cs4), FAKE, 1, 6, FAKE, FAKE, 64, 0.0, FAKE, FAKE, 1 << 30, None) == tq.TQ_ERR_INVALID_ARG
+    assert r("tq_decode_attention", P(fmt), P(tb), P(cs4), FAKE, 1, 8, FAKE, FAKE, 64, 0.0, FAKE, FAKE, 16, None) == tq.TQ_ERR_WORKSPACE
+    assert r("tq_score", P(fmt), P(tb), P(cs4), FAKE, 1, 8, FAKE, FAKE, 64, 0.0, FAKE, None, 1 << 30, None) == tq.TQ_ERR_WORKSPACE
+    assert r("tq_decode_attention", P(fmt), P(tb), P(cs4), None, 1, 8, FAKE, FAKE, 64, 0.0, FAKE, FAKE, 1 << 30, None) == tq.TQ_ERR_INVALID_ARG
+    assert "workspace" in tq._lib.tq_last_error().decode() or tq._lib.tq_last_error().decode()
+    assert tq.status_name(tq.TQ_ERR_WORKSPACE) == "TQ_ERR_WORKSPACE"
+    # host generators
+    assert r("tq_make_rotations", 2, 1, FAKE, FAKE, None) == tq.TQ_ERR_INVALID_ARG
+    assert r("tq_make_codebook", 128, 9, FAKE, FAKE) == tq.TQ_ERR_INVALID_ARG
