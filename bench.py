@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--copy-probe", action="store_true", help="also run a plain copy of known size (PMC scaling)")
+    p.add_argument("--per-layer", action="store_true",
+                   help="also time 28 one-layer decode calls per step (adds one-layer decode launches to a profile)")
     return p.parse_args()
 
 
@@ -140,31 +142,29 @@ def main():
     torch.cuda.synchronize()
     decode_ms = e0.elapsed_time(e1) / args.steps
 
-    # per-layer calls (as a model would issue them): 28 decode calls of one layer
-    per_layer = [tq.Cache(fmt, 1, H, cap, {k: (None if t is None else t.view(L, -1)[l])
-                                           for k, t in base.planes.items()}) for l in range(L)]
-    layer_tables = []
-    for l in range(L):
-        lt = tq.Tables(fmt, tables.pi[l:l + 1], tables.s[l:l + 1], tables.pi_s[l:l + 1], tables.k_centroids,
-                       tables.k_boundaries, tables.v_centroids, tables.v_boundaries, {})
-        layer_tables.append(lt)
-    ws1 = tq.workspace_for(fmt, per_layer[0], 1, HQ, T, dev)
-    q_l = [Q[l:l + 1].contiguous() for l in range(L)]
-    out_l = torch.empty((1, 1, HQ, D), device=dev)
-    for _ in range(3):
-        for l in range(L):
-            tq.tq_decode_attention(fmt, layer_tables[l], per_layer[l], q_l[l], seq_start, seq_len, T, out_l, ws1,
-                                   stream=stream)
+    # the dominant kernel alone: the staged entry points, with events around
+    # the partials launch (decode_kernel) only, on the stream it runs on
+    def staged(c, ev=None):
+        tq.tq_decode_prepare(fmt, tables, c, Q, T, ws, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        tq.tq_decode_partials(fmt, tables, c, 1, HQ, seq_start, seq_len, T, ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        tq.tq_decode_combine(fmt, tables, c, 1, HQ, T, out, ws, stream=stream)
+
+    for i in range(args.warmup):
+        staged(caches[i % n_copies])
     torch.cuda.synchronize()
-    e0.record(stream)
-    nrep = 10
-    for _ in range(nrep):
-        for l in range(L):
-            tq.tq_decode_attention(fmt, layer_tables[l], per_layer[l], q_l[l], seq_start, seq_len, T, out_l, ws1,
-                                   stream=stream)
-    e1.record(stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        staged(caches[i % n_copies], evs[i])
     torch.cuda.synchronize()
-    per_layer_ms = e0.elapsed_time(e1) / nrep
+    kern_us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+
+    per_layer_ms = None
+    if args.per_layer:
+        per_layer_ms = time_per_layer(tq, fmt, tables, base, Q, seq_start, seq_len, T, stream, dev)
 
     # ---------------- algorithmic bytes
     k_rec = D * (w.k_bits - 1) // 8 + D // 8 + 8
@@ -175,8 +175,13 @@ def main():
     new_tok = L * H * 2 * D * (2 if dt != torch.float32 else 4) + L * H * (k_rec + v_rec)
     step_bytes = records + qo + tables_bytes + new_tok
     decode_bytes = records + qo + L * 2 * D * D * 4   # Pi and S
+    kernel_bytes = records + L * HQ * 2 * D * 4       # packed records + the prepared queries (Pi q, S q)
+    n_splits = ws_splits(tq, fmt, base, HQ, T)
+    split_overhead = L * HQ * n_splits * (D + 2) * 4  # fp32 partials written for the combine
     step_gbs = step_bytes / (step_ms * 1e-3) / 1e9
     decode_gbs = decode_bytes / (decode_ms * 1e-3) / 1e9
+    kern_mean = float(kern_us.mean())
+    kern_gbs = kernel_bytes / (kern_mean * 1e-6) / 1e9
     bulk_tokens = L * T
     result = {
         "metric": "decode-attention GB/s & % HBM roofline; compress Mtokens/s per KV head",
@@ -195,19 +200,26 @@ def main():
                    "batch": 1, "cached_tokens": T, "k_bits": w.k_bits, "v_bits": w.v_bits,
                    "kv_dtype": w.dtype, "layers_per_call": L, "cache_copies": n_copies,
                    "step": "append-compress 1 token x 28 layers + decode attention x 28 layers"},
-        "roofline": {"bound": "hbm", "achieved": round(decode_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(decode_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_kernel<3,4> (timed call = qprep_kernel + decode_kernel)",
-                     "bytes_per_launch": decode_bytes, "us_per_launch": round(decode_ms * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"decode_kernel<{max(w.k_bits - 1, 0)},{w.v_bits},false>",
+                     "bytes_per_launch": kernel_bytes, "us_per_launch": round(kern_mean, 2),
+                     "us_median": round(float(np.median(kern_us)), 2),
+                     "us_p10": round(float(np.percentile(kern_us, 10)), 2),
+                     "us_p90": round(float(np.percentile(kern_us, 90)), 2),
+                     "split_partials_bytes": split_overhead},
+        "decode_call": {"us": round(decode_ms * 1e3, 2), "GBs": round(decode_gbs, 1),
+                        "bytes": decode_bytes, "kernels": "qprep_kernel + decode_kernel + combine_kernel"},
         "decode_step_bytes": step_bytes,
-        "per_layer_calls": {"us_per_step": round(per_layer_ms * 1e3, 2),
-                            "GBs": round(decode_bytes / (per_layer_ms * 1e-3) / 1e9, 1)},
         "compress": {"what": f"bulk prefill {T} tokens x {L} layers x {H} KV heads, one call",
                      "ms": round(bulk_ms, 4),
                      "mtokens_per_s_per_kv_head": round(bulk_tokens / (bulk_ms * 1e-3) / 1e6, 2),
                      "mtoken_heads_per_s": round(bulk_tokens * H / (bulk_ms * 1e-3) / 1e6, 2)},
         "wall_s_timed": round(wall, 4),
     }
+    if per_layer_ms is not None:
+        result["per_layer_calls"] = {"us_per_step": round(per_layer_ms * 1e3, 2),
+                                     "GBs": round(decode_bytes / (per_layer_ms * 1e-3) / 1e9, 1)}
 
     if args.copy_probe:
         n = 1 << 28  # 1 GiB of float32 read + 1 GiB written
@@ -220,6 +232,47 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, result)
     print(json.dumps(result), flush=True)
+
+
+def ws_splits(tq, fmt, cache, hq, t):
+    """Token splits of a decode call: the workspace holds the prepared queries
+    and (d + 2) fp32 per (layer, query head, split)."""
+    d = fmt.d
+    total = tq._lib.tq_decode_workspace_bytes(tq.ctypes.byref(fmt), cache.n_layers, 1, cache.n_kv_heads, hq, t)
+    qprep = cache.n_layers * hq * 2 * d * 4
+    return (total - qprep) // (cache.n_layers * hq * (d + 2) * 4)
+
+
+def time_per_layer(tq, fmt, tables, base, Q, seq_start, seq_len, T, stream, dev):
+    """28 one-layer decode calls per step, as a model would issue them."""
+    import torch
+    L, H, cap = base.n_layers, base.n_kv_heads, base.capacity
+    HQ, D = Q.shape[2], Q.shape[3]
+    per_layer = [tq.Cache(fmt, 1, H, cap, {k: (None if t is None else t.view(L, -1)[l])
+                                           for k, t in base.planes.items()}) for l in range(L)]
+    layer_tables = []
+    for l in range(L):
+        lt = tq.Tables(fmt, tables.pi[l:l + 1], tables.s[l:l + 1], tables.pi_s[l:l + 1], tables.k_centroids,
+                       tables.k_boundaries, tables.v_centroids, tables.v_boundaries, {})
+        layer_tables.append(lt)
+    ws1 = tq.workspace_for(fmt, per_layer[0], 1, HQ, T, dev)
+    q_l = [Q[l:l + 1].contiguous() for l in range(L)]
+    out_l = torch.empty((1, 1, HQ, D), device=dev)
+    for _ in range(3):
+        for l in range(L):
+            tq.tq_decode_attention(fmt, layer_tables[l], per_layer[l], q_l[l], seq_start, seq_len, T, out_l, ws1,
+                                   stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    nrep = 10
+    for _ in range(nrep):
+        for l in range(L):
+            tq.tq_decode_attention(fmt, layer_tables[l], per_layer[l], q_l[l], seq_start, seq_len, T, out_l, ws1,
+                                   stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / nrep
 
 
 def cpu_baseline(w, budget_s, gpu_result):

@@ -166,6 +166,31 @@ tq_status tq_decode_attention(const tq_format* fmt, const tq_tables* tables, con
                               int64_t max_seq_len, float scale, float* out, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Device.  tq_decode_attention in three stages, for callers that schedule
+ * them separately (and for timing the kernels one by one).  They take the same
+ * arguments as tq_decode_attention and share its workspace, which carries the
+ * prepared queries and the per-split partial results from one stage to the
+ * next:
+ *   tq_decode_prepare  - forward-rotated and pre-sketched queries Pi q, S q
+ *                        (QJL deep-dive, section 6: sketched once per query);
+ *   tq_decode_partials - scores every token split of every (layer, sequence,
+ *                        KV head) on the packed cache and accumulates its
+ *                        softmax-weighted values (online softmax per split);
+ *   tq_decode_combine  - merges the splits of each query head and applies Pi^T.
+ * Calling them in this order on one stream gives exactly tq_decode_attention's
+ * result; the max_seq_len / batch / head arguments must be the same in all
+ * three calls. */
+tq_status tq_decode_prepare(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, const float* q,
+                            int32_t batch, int32_t n_q_heads, int64_t max_seq_len, void* workspace,
+                            size_t workspace_bytes, void* stream);
+tq_status tq_decode_partials(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, int32_t batch,
+                             int32_t n_q_heads, const int64_t* seq_start, const int32_t* seq_len,
+                             int64_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
+                             void* stream);
+tq_status tq_decode_combine(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, int32_t batch,
+                            int32_t n_q_heads, int64_t max_seq_len, float* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Device.  The scoring half of tq_decode_attention alone (the pages' separate
  * MSE-score and QJL-score kernels, QJL deep-dive section 6): writes the
  * logits l_t defined above to logits[n_layers][batch][n_q_heads][max_seq_len]

@@ -67,6 +67,9 @@ def _load(path: str = LIB_PATH):
         "tq_compress_kv": (I32, [fmtp, tabp, cachep, P, P, I32, I32, I32, I64, P, I64, P]),
         "tq_decode_attention": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P, SZ, P]),
         "tq_score": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P, SZ, P]),
+        "tq_decode_prepare": (I32, [fmtp, tabp, cachep, P, I32, I32, I64, P, SZ, P]),
+        "tq_decode_partials": (I32, [fmtp, tabp, cachep, I32, I32, P, P, I64, F32, P, SZ, P]),
+        "tq_decode_combine": (I32, [fmtp, tabp, cachep, I32, I32, I64, P, P, SZ, P]),
         "tq_status_string": (ctypes.c_char_p, [I32]),
         "tq_last_error": (ctypes.c_char_p, []),
     }
@@ -80,6 +83,7 @@ def _load(path: str = LIB_PATH):
 _lib = _load()
 EXPORTED = ("tq_layer_seed", "tq_make_rotations", "tq_make_codebook", "tq_cache_plane_bytes",
             "tq_decode_workspace_bytes", "tq_compress_kv", "tq_decode_attention", "tq_score",
+            "tq_decode_prepare", "tq_decode_partials", "tq_decode_combine",
             "tq_status_string", "tq_last_error")
 
 
@@ -278,6 +282,31 @@ def tq_decode_attention(fmt: tq_format, tables: Tables, cache: Cache, q, seq_sta
                                     _ptr(seq_start), _ptr(seq_len), max_seq_len, scale, _ptr(out), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream)),
            "tq_decode_attention")
+
+
+def tq_decode_prepare(fmt: tq_format, tables: Tables, cache: Cache, q, max_seq_len: int, workspace, stream=None):
+    n_layers, batch, hq, d = q.shape
+    tb, cs = tables.struct(), cache.struct()
+    _check(_lib.tq_decode_prepare(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(q), batch, hq,
+                                  max_seq_len, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)), "tq_decode_prepare")
+
+
+def tq_decode_partials(fmt: tq_format, tables: Tables, cache: Cache, batch: int, n_q_heads: int, seq_start, seq_len,
+                       max_seq_len: int, workspace, scale: float = 0.0, stream=None):
+    tb, cs = tables.struct(), cache.struct()
+    _check(_lib.tq_decode_partials(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), batch, n_q_heads,
+                                   _ptr(seq_start), _ptr(seq_len), max_seq_len, scale, _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "tq_decode_partials")
+
+
+def tq_decode_combine(fmt: tq_format, tables: Tables, cache: Cache, batch: int, n_q_heads: int, max_seq_len: int,
+                      out, workspace, stream=None):
+    tb, cs = tables.struct(), cache.struct()
+    _check(_lib.tq_decode_combine(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), batch, n_q_heads,
+                                  max_seq_len, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)), "tq_decode_combine")
 
 
 def tq_score(fmt: tq_format, tables: Tables, cache: Cache, q, seq_start, seq_len, max_seq_len: int, logits,

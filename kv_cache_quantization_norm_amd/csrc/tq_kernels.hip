@@ -189,14 +189,6 @@ __device__ __forceinline__ uint32_t quantize(float y, const float* bnd) {
   return idx;
 }
 
-__device__ __forceinline__ uint32_t quantize_dyn(float y, const float* bnd, int nb) {
-  switch (nb) {
-    case 1: return quantize<1>(y, bnd);
-    case 3: return quantize<3>(y, bnd);
-    case 7: return quantize<7>(y, bnd);
-    default: return quantize<15>(y, bnd);
-  }
-}
 
 // OR the 4 consecutive m-bit codes `chunk` (coordinates 16 tile + 4 q .. +3)
 // into a token record in LDS.
@@ -206,6 +198,7 @@ __device__ __forceinline__ void or_bits(uint32_t* rec, int bitpos, uint32_t chun
   if (sh + nbits > 32) atomicOr(&rec[w + 1], chunk >> (32 - sh));
 }
 
+template <int MK, int BV>
 __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   CompressSmem& sm = *reinterpret_cast<CompressSmem*>(smem_raw);
@@ -213,7 +206,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   const int t = lane & 15, q = lane >> 4;
   const int layer_rel = blockIdx.y;
   const int layer = a.layer0 + layer_rel;
-  const bool need_rot = a.mk > 0 || a.bv > 0;
+  const bool need_rot = MK > 0 || BV > 0;
 
   // Stage Pi (and M) in operand order; all global loads of a thread are
   // issued before its LDS writes.
@@ -230,7 +223,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
       dst[0] = buf[u].x; dst[64] = buf[u].y; dst[128] = buf[u].z; dst[192] = buf[u].w;
     }
   }
-  if (a.mk > 0) {
+  if constexpr (MK > 0) {
     const float4* src = reinterpret_cast<const float4*>(a.pi_s + int64_t(layer) * D * D);
     float4 buf[16];
 #pragma unroll
@@ -244,7 +237,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
     }
   }
   if (tid < 16) {
-    const int nk = a.mk > 0 ? (1 << a.mk) : 0, nv = a.bv > 0 ? (1 << a.bv) : 0;
+    const int nk = MK > 0 ? (1 << MK) : 0, nv = BV > 0 ? (1 << BV) : 0;
     sm.kc[tid] = tid < nk ? a.kc[tid] : 0.f;
     sm.kb[tid] = tid + 1 < nk ? a.kb[tid] : INFINITY;
     sm.vc[tid] = tid < nv ? a.vc[tid] : 0.f;
@@ -270,7 +263,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   uint32_t* rec = sm.rec[wave];
   uint32_t* srec = sm.srec[wave];
   uint32_t* vrec = sm.vrec[wave];
-  const int kwords = 4 * a.mk;  // dwords per key code record
+  const int kwords = 4 * MK;  // dwords per key code record
 
   for (int h = wave; h < a.H; h += kWaves) {
     const int64_t plane = int64_t(layer) * a.H + h;  // [layer][head]
@@ -278,7 +271,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
     float y[8][4];
     // ---------------- keys
     load_token_slab(a, a.k, layer_rel, tok, h, q, valid, xr);
-    if (a.mk == 0) {
+    if constexpr (MK == 0) {
       if (valid) {
         uint16_t* dst = a.k_f16 + (plane * a.capacity + slot) * D + 32 * q;
 #pragma unroll
@@ -292,7 +285,6 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
       }
     } else {
       const float n = rotate_tile(sm, xr, lane, y);
-      const int nb = (1 << a.mk) - 1;
       for (int e = lane; e < kCompressTile * 16; e += 64) rec[e] = 0u;
       srec[lane] = 0u;
       wave_sync();
@@ -303,12 +295,12 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
         uint32_t chunk = 0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint32_t idx = quantize_dyn(y[tile][r], sm.kb, nb);
-          chunk |= idx << (r * a.mk);
+          const uint32_t idx = quantize<(1 << MK) - 1>(y[tile][r], sm.kb);
+          chunk |= idx << (r * MK);
           res[tile][r] = y[tile][r] - sm.kc[idx];
           a2 = fmaf(res[tile][r], res[tile][r], a2);
         }
-        or_bits(rec + t * 16, (16 * tile + 4 * q) * a.mk, chunk, 4 * a.mk);
+        or_bits(rec + t * 16, (16 * tile + 4 * q) * MK, chunk, 4 * MK);
       }
       a2 += shfl_xor(a2, 16);
       a2 += shfl_xor(a2, 32);
@@ -339,7 +331,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
         if (tk >= a.n_tokens) continue;
         const int64_t sl = a.slots ? a.slots[tk] : a.slot0 + tk;
         if (sl < 0 || sl >= a.capacity) continue;
-        reinterpret_cast<uint32_t*>(a.k_idx + (plane * a.capacity + sl) * (16 * a.mk))[w] = rec[tt * 16 + w];
+        reinterpret_cast<uint32_t*>(a.k_idx + (plane * a.capacity + sl) * (16 * MK))[w] = rec[tt * 16 + w];
       }
       {
         const int tt = lane >> 2, w = lane & 3;
@@ -354,7 +346,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
     }
     // ---------------- values
     load_token_slab(a, a.v, layer_rel, tok, h, q, valid, xr);
-    if (a.bv == 0) {
+    if constexpr (BV == 0) {
       if (valid) {
         // [plane][slot/32][coord][32] fp16
         uint16_t* dst = a.v_f16 + ((plane * (a.capacity / kVBlock) + slot / kVBlock) * D) * kVBlock + (slot % kVBlock);
@@ -363,22 +355,26 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
       }
     } else {
       const float n = rotate_tile(sm, xr, lane, y);
-      const int nb = (1 << a.bv) - 1;
       if (valid && q == 0) a.v_norm[plane * a.capacity + slot] = n;
-      const int64_t gbytes = 4 * a.bv;  // bytes per (block, coordinate) group
+      uint32_t vidx[8][4];
+#pragma unroll
+      for (int tile = 0; tile < 8; ++tile)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vidx[tile][r] = quantize<(1 << BV) - 1>(y[tile][r], sm.vb);
+      const int64_t gbytes = 4 * BV;  // bytes per (block, coordinate) group
       uint8_t* vplane = a.v_idx + plane * (a.capacity / kVBlock) * D * gbytes;
-      if (contiguous && a.bv >= 2) {
+      if (contiguous && BV >= 2) {
         // The wave owns whole dwords: 16 tokens x bv bits per coordinate.
-        const int dw = a.bv / 2;  // dwords per coordinate for 16 tokens
+        const int dw = BV / 2;  // dwords per coordinate for 16 tokens
         for (int e = lane; e < D * dw; e += 64) vrec[e] = 0u;
         wave_sync();
 #pragma unroll
         for (int tile = 0; tile < 8; ++tile)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint32_t idx = quantize_dyn(y[tile][r], sm.vb, nb);
+            const uint32_t idx = vidx[tile][r];
             const int c = 16 * tile + 4 * q + r;
-            const int bit = t * a.bv;
+            const int bit = t * BV;
             atomicOr(&vrec[c * dw + (bit >> 5)], idx << (bit & 31));
           }
         wave_sync();
@@ -394,13 +390,13 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
       } else if (valid) {
         const int64_t blk = slot / kVBlock;
         const int p = int(slot % kVBlock);
-        const int bit = p * a.bv;
-        const uint32_t mask = ((1u << a.bv) - 1u) << (bit & 31);
+        const int bit = p * BV;
+        const uint32_t mask = ((1u << BV) - 1u) << (bit & 31);
 #pragma unroll
         for (int tile = 0; tile < 8; ++tile)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint32_t idx = quantize_dyn(y[tile][r], sm.vb, nb);
+            const uint32_t idx = vidx[tile][r];
             const int c = 16 * tile + 4 * q + r;
             uint32_t* g = reinterpret_cast<uint32_t*>(vplane + (blk * D + c) * gbytes) + (bit >> 5);
             atomicAnd(g, ~mask);
@@ -586,8 +582,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   }
-  if constexpr (!SCORE)
-    for (int e = tid; e < 16 * D; e += 256) (&accsum[0][0])[e] = 0.f;
   __syncthreads();
 
   // Query operands: lane (col = head g, q) holds Pi q and S q at coordinates
@@ -873,11 +867,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w][col]);
     const float f = (m_run == -INFINITY) ? 0.f : __expf(m_run - M) * sig;
+    // Waves add their accumulators in wave order (each element belongs to one
+    // lane of each wave), so the result is the same on every run.
+    for (int w = 0; w < kWaves; ++w) {
+      if (wave == w) {
 #pragma unroll
-    for (int vb = 0; vb < 8; ++vb)
+        for (int vb = 0; vb < 8; ++vb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) atomicAdd(&accsum[col][16 * vb + 4 * q + r], acc[vb][r] * f);
-    __syncthreads();
+          for (int r = 0; r < 4; ++r) {
+            float& dst = accsum[col][16 * vb + 4 * q + r];
+            dst = (w == 0 ? 0.f : dst) + acc[vb][r] * f;
+          }
+      }
+      __syncthreads();
+    }
     const int64_t pbase = (int64_t(layer) * a.batch + b) * a.Hq;
     const int ng = a.G - hg * kMaxGroup < kMaxGroup ? a.G - hg * kMaxGroup : kMaxGroup;
     for (int e = tid; e < ng * (D + 2); e += 256) {
@@ -902,109 +905,111 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-__global__ __launch_bounds__(128) void qprep_kernel(const float* q, const float* pi, const float* s,
-                                                    float* qprep, int batch, int Hq, int rotate) {
-  __shared__ float qv[D];
-  const int h = blockIdx.x, b = blockIdx.y, layer = blockIdx.z, i = threadIdx.x;
-  const int64_t row = (int64_t(layer) * batch + b) * Hq + h;
-  qv[i] = q[row * D + i];
-  __syncthreads();
-  float* out = qprep + row * 2 * D;
-  if (!rotate) {
-    out[i] = qv[i];
-    out[D + i] = 0.f;
-    return;
-  }
-  const float4* P = reinterpret_cast<const float4*>(pi + int64_t(layer) * D * D + int64_t(i) * D);
-  const float4* S = reinterpret_cast<const float4*>(s + int64_t(layer) * D * D + int64_t(i) * D);
-  float r = 0.f, z = 0.f;
+// qr = Pi q (q itself for fp16 keys), qs = S q.  One block per (32-row
+// quarter, KV head) of a (layer, batch): thread t computes row
+// 32 * quarter + t % 32 of Pi q (t / 32 even) or S q (odd) for two of the
+// group's query heads per pass of eight.
+constexpr int kPrepHeads = 8;
+__global__ __launch_bounds__(256) void qprep_kernel(const float* q, const float* pi, const float* s,
+                                                    float* qprep, int batch, int H, int Hq, int rotate) {
+  __shared__ float qv[kPrepHeads][D];
+  const int hk = blockIdx.x >> 2, quarter = blockIdx.x & 3, b = blockIdx.y, layer = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int G = Hq / H;
+  const int i = 32 * quarter + (tid & 31), which = (tid >> 5) & 1, pair = tid >> 6;
+  const float4* mrow = reinterpret_cast<const float4*>((which ? s : pi) + int64_t(layer) * D * D + int64_t(i) * D);
+  for (int g0 = 0; g0 < G; g0 += kPrepHeads) {
+    const int ng = G - g0 < kPrepHeads ? G - g0 : kPrepHeads;
+    const int64_t row0 = (int64_t(layer) * batch + b) * Hq + int64_t(hk) * G + g0;
+    for (int e = tid; e < kPrepHeads * D; e += 256) qv[e / D][e % D] = (e / D) < ng ? q[row0 * D + e] : 0.f;
+    __syncthreads();
+    const int ga = 2 * pair, gb = 2 * pair + 1;
+    if (!rotate) {
+      if (ga < ng) qprep[(row0 + ga) * 2 * D + which * D + i] = which ? 0.f : qv[ga][i];
+      if (gb < ng) qprep[(row0 + gb) * 2 * D + which * D + i] = which ? 0.f : qv[gb][i];
+    } else if (ga < ng) {
+      float4 m4[32];
 #pragma unroll
-  for (int j = 0; j < D / 4; ++j) {
-    const float4 pv = P[j], sv = S[j];
-    r = fmaf(pv.x, qv[4 * j], r); r = fmaf(pv.y, qv[4 * j + 1], r);
-    r = fmaf(pv.z, qv[4 * j + 2], r); r = fmaf(pv.w, qv[4 * j + 3], r);
-    z = fmaf(sv.x, qv[4 * j], z); z = fmaf(sv.y, qv[4 * j + 1], z);
-    z = fmaf(sv.z, qv[4 * j + 2], z); z = fmaf(sv.w, qv[4 * j + 3], z);
+      for (int u = 0; u < 32; ++u) m4[u] = mrow[u];
+      float acc_a = 0.f, acc_b = 0.f;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int j = 4 * u;
+        acc_a = fmaf(m4[u].x, qv[ga][j], acc_a);
+        acc_a = fmaf(m4[u].y, qv[ga][j + 1], acc_a);
+        acc_a = fmaf(m4[u].z, qv[ga][j + 2], acc_a);
+        acc_a = fmaf(m4[u].w, qv[ga][j + 3], acc_a);
+        acc_b = fmaf(m4[u].x, qv[gb][j], acc_b);
+        acc_b = fmaf(m4[u].y, qv[gb][j + 1], acc_b);
+        acc_b = fmaf(m4[u].z, qv[gb][j + 2], acc_b);
+        acc_b = fmaf(m4[u].w, qv[gb][j + 3], acc_b);
+      }
+      qprep[(row0 + ga) * 2 * D + which * D + i] = acc_a;
+      if (gb < ng) qprep[(row0 + gb) * 2 * D + which * D + i] = acc_b;
+    }
+    __syncthreads();
   }
-  out[i] = r;
-  out[D + i] = z;
 }
 
-// Merges the split partials of one (layer, batch, KV head): every query head
-// of the group, out = Pi^T (acc / l) (acc / l for fp16 values).  Pi is staged
-// in LDS with one round of vector loads.
-__global__ __launch_bounds__(256) void combine_kernel(const float* partial, const float* pi, float* out, int batch,
-                                                      int H, int Hq, int n_splits, int rotate) {
+// Merges the split partials of one (layer, batch, query head) and writes
+// out = Pi^T (acc / l) (acc / l for fp16 values).  Pi is staged in LDS with
+// one round of vector loads.
+__global__ __launch_bounds__(128) void combine_kernel(const float* partial, const float* pi, float* out, int batch,
+                                                      int Hq, int n_splits, int rotate) {
   __shared__ float pim[D * D];
-  __shared__ float res[kMaxGroup][D];
-  __shared__ float Mh[kMaxGroup], Lh[kMaxGroup];
-  const int hk = blockIdx.x, b = blockIdx.y, layer = blockIdx.z, tid = threadIdx.x;
-  const int G = Hq / H;
+  __shared__ float res[D];
+  __shared__ float red[2][128];
+  const int h = blockIdx.x, b = blockIdx.y, layer = blockIdx.z, tid = threadIdx.x;
+  const int64_t row = (int64_t(layer) * batch + b) * Hq + h;
   if (rotate) {
     const float4* src = reinterpret_cast<const float4*>(pi + int64_t(layer) * D * D);
-    float4 buf[16];
+    float4 buf[32];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) buf[u] = src[tid + 256 * u];
+    for (int u = 0; u < 32; ++u) buf[u] = src[tid + 128 * u];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) reinterpret_cast<float4*>(pim)[tid + 256 * u] = buf[u];
+    for (int u = 0; u < 32; ++u) reinterpret_cast<float4*>(pim)[tid + 128 * u] = buf[u];
   }
-  for (int g0 = 0; g0 < G; g0 += kMaxGroup) {
-    const int ng = G - g0 < kMaxGroup ? G - g0 : kMaxGroup;
-    const int64_t row0 = (int64_t(layer) * batch + b) * Hq + hk * G + g0;
-    // per-head max and normaliser over the splits: 16 threads per head
-    {
-      const int g = tid >> 4, sub = tid & 15;
-      float M = -INFINITY, L = 0.f;
-      if (g < ng) {
-        const float* P = partial + (row0 + g) * int64_t(n_splits) * (D + 2);
-        for (int sp = sub; sp < n_splits; sp += 16) M = fmaxf(M, P[int64_t(sp) * (D + 2)]);
-      }
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 16));
-      if (g < ng) {
-        const float* P = partial + (row0 + g) * int64_t(n_splits) * (D + 2);
-        for (int sp = sub; sp < n_splits; sp += 16) {
-          const float ms = P[int64_t(sp) * (D + 2)];
-          L += ms == -INFINITY ? 0.f : P[int64_t(sp) * (D + 2) + 1] * __expf(ms - M);
-        }
-      }
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) L += __shfl_xor(L, o, 16);
-      if (g < ng && sub == 0) {
-        Mh[g] = M;
-        Lh[g] = L;
-      }
-    }
-    __syncthreads();
-    for (int e = tid; e < ng * D; e += 256) {
-      const int g = e / D, i = e - g * D;
-      const float* P = partial + (row0 + g) * int64_t(n_splits) * (D + 2);
-      const float M = Mh[g], L = Lh[g];
-      float acc = 0.f;
-#pragma unroll 8
-      for (int sp = 0; sp < n_splits; ++sp) {
-        const float ms = P[int64_t(sp) * (D + 2)];
-        const float as = P[int64_t(sp) * (D + 2) + 2 + i];
-        acc += ms == -INFINITY ? 0.f : as * __expf(ms - M);
-      }
-      // L is 0 only for an empty sequence; NaN must propagate.
-      res[g][i] = (L > 0.f || L != L) ? acc / L : 0.f;
-    }
-    __syncthreads();
-    for (int e = tid; e < ng * D; e += 256) {
-      const int g = e / D, i = e - g * D;
-      float o;
-      if (rotate) {
-        o = 0.f;
-#pragma unroll 8
-        for (int j = 0; j < D; ++j) o = fmaf(pim[j * D + i], res[g][j], o);
-      } else {
-        o = res[g][i];
-      }
-      out[(row0 + g) * D + i] = o;
-    }
+  const float* P = partial + row * int64_t(n_splits) * (D + 2);
+  float M = -INFINITY;
+  for (int sp = tid; sp < n_splits; sp += 128) M = fmaxf(M, P[int64_t(sp) * (D + 2)]);
+  red[0][tid] = M;
+  __syncthreads();
+  for (int w = 64; w > 0; w >>= 1) {
+    if (tid < w) red[0][tid] = fmaxf(red[0][tid], red[0][tid + w]);
     __syncthreads();
   }
+  M = red[0][0];
+  float L = 0.f;
+  for (int sp = tid; sp < n_splits; sp += 128) {
+    const float ms = P[int64_t(sp) * (D + 2)];
+    L += ms == -INFINITY ? 0.f : P[int64_t(sp) * (D + 2) + 1] * __expf(ms - M);
+  }
+  red[1][tid] = L;
+  __syncthreads();
+  for (int w = 64; w > 0; w >>= 1) {
+    if (tid < w) red[1][tid] += red[1][tid + w];
+    __syncthreads();
+  }
+  L = red[1][0];
+  float acc = 0.f;
+#pragma unroll 8
+  for (int sp = 0; sp < n_splits; ++sp) {
+    const float ms = P[int64_t(sp) * (D + 2)];
+    const float as = P[int64_t(sp) * (D + 2) + 2 + tid];
+    acc += ms == -INFINITY ? 0.f : as * __expf(ms - M);
+  }
+  // L is 0 only for an empty sequence; NaN must propagate.
+  const float v = (L > 0.f || L != L) ? acc / L : 0.f;
+  if (!rotate) {
+    out[row * D + tid] = v;
+    return;
+  }
+  res[tid] = v;
+  __syncthreads();
+  float o = 0.f;
+#pragma unroll 16
+  for (int j = 0; j < D; ++j) o = fmaf(pim[j * D + tid], res[j], o);
+  out[row * D + tid] = o;
 }
 
 template <bool SCORE>
@@ -1058,17 +1063,25 @@ tq_status launch_status(const char* what) {
   return TQ_OK;
 }
 
+// Decode stages: prepare the query operands (qprep_kernel), score / accumulate
+// the token splits (decode_kernel), merge the splits (combine_kernel).
+enum { kStagePrepare = 1, kStagePartials = 2, kStageCombine = 4, kStageAll = 7 };
+
 template <bool SCORE>
 tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
                         const float* q, int32_t batch, int32_t n_q_heads, const int64_t* seq_start,
                         const int32_t* seq_len, int64_t max_seq_len, float scale, float* out,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream, int stages) {
   clear_error();
   tq_status st = check_format(fmt, true);
   if (st) return st;
   if ((st = check_tables(fmt, tables, false))) return st;
   if ((st = check_cache(fmt, cache))) return st;
-  if (!q || !out || !seq_start || !seq_len) return fail(TQ_ERR_INVALID_ARG, "q/out/seq_start/seq_len is NULL");
+  if ((stages & kStagePrepare) && !q) return fail(TQ_ERR_INVALID_ARG, "q is NULL");
+  if ((stages & kStagePartials) && (!seq_start || !seq_len))
+    return fail(TQ_ERR_INVALID_ARG, "seq_start/seq_len is NULL");
+  if (((stages & kStageCombine) || (SCORE && (stages & kStagePartials))) && !out)
+    return fail(TQ_ERR_INVALID_ARG, "output is NULL");
   if (batch <= 0 || n_q_heads <= 0 || n_q_heads % cache->n_kv_heads)
     return fail(TQ_ERR_INVALID_ARG, "batch=%d n_q_heads=%d (must be a positive multiple of n_kv_heads=%d)",
                 batch, n_q_heads, cache->n_kv_heads);
@@ -1084,9 +1097,11 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.qprep_bytes);
   const int mk = fmt->k_bits > 0 ? fmt->k_bits - 1 : 0;
   const int bv = fmt->v_bits;
-  hipLaunchKernelGGL(qprep_kernel, dim3(n_q_heads, batch, cache->n_layers), dim3(128), 0, hs, q,
-                     tables->pi, tables->s, qprep, batch, n_q_heads, fmt->k_bits > 0 ? 1 : 0);
-  if ((st = launch_status("qprep"))) return st;
+  if (stages & kStagePrepare) {
+    hipLaunchKernelGGL(qprep_kernel, dim3(cache->n_kv_heads * 4, batch, cache->n_layers), dim3(256), 0, hs, q,
+                       tables->pi, tables->s, qprep, batch, cache->n_kv_heads, n_q_heads, fmt->k_bits > 0 ? 1 : 0);
+    if ((st = launch_status("qprep"))) return st;
+  }
   if (max_seq_len == 0 && SCORE) return TQ_OK;
 
   DecodeArgs a{};
@@ -1120,11 +1135,13 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   const int64_t gy = int64_t(cache->n_kv_heads) * plan.n_head_groups;
   if (gy > 65535) return fail(TQ_ERR_INVALID_ARG, "too many KV heads x head groups");
   dim3 grid(unsigned(plan.n_splits), unsigned(gy), unsigned(cache->n_layers * batch));
-  if ((st = launch_decode<SCORE>(mk, SCORE ? 0 : bv, a, grid, hs))) return st;
-  if ((st = launch_status("decode"))) return st;
-  if (!SCORE) {
-    hipLaunchKernelGGL(combine_kernel, dim3(cache->n_kv_heads, batch, cache->n_layers), dim3(256), 0, hs, partial,
-                       tables->pi, out, batch, cache->n_kv_heads, n_q_heads, int(plan.n_splits), bv > 0 ? 1 : 0);
+  if (stages & kStagePartials) {
+    if ((st = launch_decode<SCORE>(mk, SCORE ? 0 : bv, a, grid, hs))) return st;
+    if ((st = launch_status("decode"))) return st;
+  }
+  if (!SCORE && (stages & kStageCombine)) {
+    hipLaunchKernelGGL(combine_kernel, dim3(n_q_heads, batch, cache->n_layers), dim3(128), 0, hs, partial,
+                       tables->pi, out, batch, n_q_heads, int(plan.n_splits), bv > 0 ? 1 : 0);
     if ((st = launch_status("combine"))) return st;
   }
   return TQ_OK;
@@ -1187,11 +1204,19 @@ tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq
   a.v_norm = cache->v_norm;
   a.v_f16 = static_cast<uint16_t*>(cache->v_f16);
   const size_t smem = sizeof(CompressSmem);
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(compress_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, int(smem)) != hipSuccess)
+  const void* fn = nullptr;
+#define TQ_CMP(MK_, BV_) if (a.mk == MK_ && a.bv == BV_) fn = reinterpret_cast<const void*>(compress_kernel<MK_, BV_>);
+#define TQ_CMP_V(MK_) TQ_CMP(MK_, 0) TQ_CMP(MK_, 1) TQ_CMP(MK_, 2) TQ_CMP(MK_, 4)
+  TQ_CMP_V(0) TQ_CMP_V(1) TQ_CMP_V(2) TQ_CMP_V(3) TQ_CMP_V(4)
+#undef TQ_CMP_V
+#undef TQ_CMP
+  if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for key bits %d / value bits %d", a.mk, a.bv);
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(smem)) != hipSuccess)
     return fail(TQ_ERR_HIP, "cannot raise the LDS limit to %zu bytes", smem);
-  hipLaunchKernelGGL(compress_kernel, dim3(unsigned(wgs), unsigned(n_layers)), dim3(256), smem,
-                     static_cast<hipStream_t>(stream), a);
+  void* args[] = {&a};
+  if (hipLaunchKernel(fn, dim3(unsigned(wgs), unsigned(n_layers)), dim3(256), args, smem,
+                      static_cast<hipStream_t>(stream)) != hipSuccess)
+    return fail(TQ_ERR_HIP, "compress launch failed: %s", hipGetErrorString(hipGetLastError()));
   return launch_status("compress");
 }
 
@@ -1201,7 +1226,29 @@ tq_status tq_decode_attention(const tq_format* fmt, const tq_tables* tables, con
                               int64_t max_seq_len, float scale, float* out, void* workspace,
                               size_t workspace_bytes, void* stream) {
   return tq::decode_common<false>(fmt, tables, cache, q, batch, n_q_heads, seq_start, seq_len, max_seq_len,
-                                  scale, out, workspace, workspace_bytes, stream);
+                                  scale, out, workspace, workspace_bytes, stream, tq::kStageAll);
+}
+
+tq_status tq_decode_prepare(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, const float* q,
+                            int32_t batch, int32_t n_q_heads, int64_t max_seq_len, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return tq::decode_common<false>(fmt, tables, cache, q, batch, n_q_heads, nullptr, nullptr, max_seq_len, 0.f,
+                                  nullptr, workspace, workspace_bytes, stream, tq::kStagePrepare);
+}
+
+tq_status tq_decode_partials(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, int32_t batch,
+                             int32_t n_q_heads, const int64_t* seq_start, const int32_t* seq_len,
+                             int64_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return tq::decode_common<false>(fmt, tables, cache, nullptr, batch, n_q_heads, seq_start, seq_len, max_seq_len,
+                                  scale, nullptr, workspace, workspace_bytes, stream, tq::kStagePartials);
+}
+
+tq_status tq_decode_combine(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, int32_t batch,
+                            int32_t n_q_heads, int64_t max_seq_len, float* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return tq::decode_common<false>(fmt, tables, cache, nullptr, batch, n_q_heads, nullptr, nullptr, max_seq_len, 0.f,
+                                  out, workspace, workspace_bytes, stream, tq::kStageCombine);
 }
 
 tq_status tq_score(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
@@ -1209,7 +1256,8 @@ tq_status tq_score(const tq_format* fmt, const tq_tables* tables, const tq_cache
                    const int32_t* seq_len, int64_t max_seq_len, float scale, float* logits,
                    void* workspace, size_t workspace_bytes, void* stream) {
   return tq::decode_common<true>(fmt, tables, cache, q, batch, n_q_heads, seq_start, seq_len, max_seq_len,
-                                 scale, logits, workspace, workspace_bytes, stream);
+                                 scale, logits, workspace, workspace_bytes, stream,
+                                 tq::kStagePrepare | tq::kStagePartials);
 }
 
 }  // extern "C"

@@ -176,6 +176,36 @@ def test_end_to_end(case):
             pu.check_outputs(out[i], ref)
 
 
+@pytest.mark.parametrize("case", ["w5_ragged5", "w3_6L_asym"])
+def test_staged_decode_matches_one_call(case):
+    """tq_decode_prepare + tq_decode_partials + tq_decode_combine on one stream
+    give bit for bit what tq_decode_attention gives."""
+    import kv_cache_quantization_norm_amd as tq
+    w = CASES[case]
+    _say("staged", case)
+    for fmt, layers in pu.layer_groups(w):
+        tables, dev, _, _, (starts, lens, cap, slots) = _run_group(w, fmt, layers)
+        tfmt = pu.tq_format(fmt)
+        Q = np.stack([wl.gen_q(w, layer) for layer in layers])
+        n_layers, batch, hq, _ = Q.shape
+        max_len = int(max(lens))
+        qt = torch.from_numpy(Q).cuda().contiguous()
+        st = torch.from_numpy(np.asarray(starts, np.int64)).cuda()
+        ln = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+        ws = tq.workspace_for(tfmt, dev, batch, hq, max_len)
+        one = torch.full((n_layers, batch, hq, 128), float("nan"), device="cuda")
+        staged = torch.full_like(one, float("nan"))
+        tq.tq_decode_attention(tfmt, tables, dev, qt, st, ln, max_len, one, ws)
+        ws.fill_(0xFF)  # NaN everywhere: the staged calls must rewrite what they read
+        tq.tq_decode_prepare(tfmt, tables, dev, qt, max_len, ws)
+        tq.tq_decode_partials(tfmt, tables, dev, batch, hq, st, ln, max_len, ws)
+        tq.tq_decode_combine(tfmt, tables, dev, batch, hq, max_len, staged, ws)
+        torch.cuda.synchronize()
+        a, b = one.cpu().numpy(), staged.cpu().numpy()
+        assert not np.isnan(a).any()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 def test_degenerate_vectors_and_nan():
     """Zero keys/values compress to zero norms and contribute nothing; a NaN key
     makes its sequence's outputs NaN and leaves other sequences finite."""
