@@ -51,6 +51,25 @@ __device__ __forceinline__ floatx4 mfma16x16x4f32(float a, float b, floatx4 c) {
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 64 lanes, in a fixed order, returned to every lane: DPP within
+// each 16-lane row (quad swaps, then the half-row and row mirrors), then the
+// four row sums through readlane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
+  const int b = __builtin_bit_cast(int, v);
+  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
+}
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -406,6 +425,264 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
     }
   }
   }  // token tiles
+}
+
+// Few-token compression (appends during decode).  The tile kernel above
+// spends a 128 KB LDS staging of Pi and S Pi^T and a full pass of all eight
+// row blocks per wave on every 16-token tile, which for one token per head is
+// almost all waste.  Here one workgroup takes up to 8 (token, head) items of
+// one layer, flattened as item = token * H + head, and the MFMA columns are
+// the items' vectors: 8 keys and 8 values for the rotation, the 8 key
+// residuals for the sketch.  Wave w owns rows 32 w .. 32 w + 31 (two 16-row
+// blocks) of every product and reads its A operands (rows of Pi and S Pi^T)
+// straight from global memory; all global loads are issued at the start.
+constexpr int kAppendItems = 8;
+constexpr int kAppendStride = D + 4;  // padded LDS rows
+
+template <int MK, int BV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void compress_append_kernel(
+    CompressArgs a) {
+  __shared__ __align__(16) float xs[2 * kAppendItems][kAppendStride];  // K items, then V items
+  __shared__ __align__(16) float rs[kAppendItems][kAppendStride];      // key residual y - c[idx]
+  __shared__ float nrm[2 * kAppendItems];
+  __shared__ float rnrm[kAppendItems];
+  __shared__ uint32_t krec[kAppendItems][16];
+  __shared__ uint32_t srec[kAppendItems][4];
+  __shared__ int64_t slot_of[kAppendItems];
+  __shared__ float cb[4][16];  // key centroids, key boundaries, value centroids, value boundaries
+  constexpr bool ROT = MK > 0 || BV > 0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int layer_rel = blockIdx.y, layer = a.layer0 + layer_rel;
+  const int64_t n_items = a.n_tokens * a.H;
+  const int64_t item0 = int64_t(blockIdx.x) * kAppendItems;
+  const int ni = n_items - item0 < kAppendItems ? int(n_items - item0) : kAppendItems;
+
+  // ---------------- all global loads
+  // A operands, block n: row 32 wave + 16 n + r16, step v: columns 16 v + 4 kq .. + 3.
+  float4 ap[ROT ? 2 : 1][8], am[MK > 0 ? 2 : 1][8];
+  if constexpr (ROT) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const float4* src = reinterpret_cast<const float4*>(a.pi + int64_t(layer) * D * D +
+                                                          int64_t(32 * wave + 16 * n + r16) * D + 4 * kq);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) ap[n][v] = src[4 * v];
+    }
+  }
+  if constexpr (MK > 0) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const float4* src = reinterpret_cast<const float4*>(a.pi_s + int64_t(layer) * D * D +
+                                                          int64_t(32 * wave + 16 * n + r16) * D + 4 * kq);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) am[n][v] = src[4 * v];
+    }
+  }
+  float xin[8];
+  {
+    int64_t offs[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = tid + 256 * u, c = e >> 7, j = e & 127;
+      const int it = c & (kAppendItems - 1);
+      const int64_t item = item0 + (it < ni ? it : ni - 1);
+      offs[u] = ((int64_t(layer_rel) * a.n_tokens + item / a.H) * a.H + item % a.H) * D + j;
+    }
+    // u < 4: keys, u >= 4: values (e = tid + 256 u, vector e / 128).
+    if (a.dtype == TQ_DTYPE_F32) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) xin[u] = static_cast<const float*>(u < 4 ? a.k : a.v)[offs[u]];
+    } else {
+      uint16_t hv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) hv[u] = static_cast<const uint16_t*>(u < 4 ? a.k : a.v)[offs[u]];
+      if (a.dtype == TQ_DTYPE_BF16) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) xin[u] = __uint_as_float(uint32_t(hv[u]) << 16);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          _Float16 f;
+          __builtin_memcpy(&f, &hv[u], 2);
+          xin[u] = float(f);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int it = ((tid + 256 * u) >> 7) & (kAppendItems - 1);
+      if (it >= ni) xin[u] = 0.f;
+    }
+  }
+  int64_t slot = -1;
+  {
+    const int64_t tok = (item0 + (tid < ni ? tid : 0)) / a.H;
+    if (tid < kAppendItems && tid < ni) slot = a.slots ? a.slots[tok] : a.slot0 + tok;
+  }
+  // Codebooks: lane j of wave w holds entry j of table w (0 past the end; the
+  // boundary tables are padded with +inf).
+  float cbv = 0.f;
+  {
+    const int nk = MK > 0 ? (1 << MK) : 0, nv = BV > 0 ? (1 << BV) : 0;
+    const int j = lane;
+    if (j < 16) {
+      if (wave == 0 && j < nk) cbv = a.kc[j];
+      if (wave == 1) cbv = j + 1 < nk ? a.kb[j] : INFINITY;
+      if (wave == 2 && j < nv) cbv = a.vc[j];
+      if (wave == 3) cbv = j + 1 < nv ? a.vb[j] : INFINITY;
+    }
+  }
+  // Every global load above is in flight before any of them is waited on.
+  __builtin_amdgcn_sched_barrier(0);
+  if (tid < kAppendItems) slot_of[tid] = (slot < 0 || slot >= a.capacity) ? -1 : slot;
+  if (lane < 16) cb[wave][lane] = cbv;
+  for (int e = tid; e < kAppendItems * 16; e += 256) (&krec[0][0])[e] = 0u;
+  if (tid < kAppendItems * 4) (&srec[0][0])[tid] = 0u;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = tid + 256 * u;
+    xs[e >> 7][e & 127] = xin[u];
+  }
+  __syncthreads();
+  // Norms: wave w reduces vectors 4w .. 4w + 3.
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = 4 * wave + k;
+    const float x0 = xs[c][lane], x1 = xs[c][lane + 64];
+    const float ss = wave_sum(fmaf(x0, x0, x1 * x1));
+    if (lane == 0) nrm[c] = sqrtf(ss);
+  }
+  __syncthreads();
+
+  const int64_t vblocks = a.capacity / kVBlock;
+  // ---------------- rotation y = Pi x / ||x|| (column r16 = vector), quantisation
+  if constexpr (ROT) {
+    const float4* bx = reinterpret_cast<const float4*>(&xs[r16][4 * kq]);
+    float4 b4[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) b4[v] = bx[4 * v];
+    const bool is_k = r16 < kAppendItems;
+    const int it = r16 & (kAppendItems - 1);
+    const float n = nrm[r16];
+    // n = 0 -> y = 0; NaN -> NaN everywhere.
+    const float inv = n > 0.f ? 1.0f / n : (n == 0.f ? 0.f : n);
+    const int64_t slot = slot_of[it];
+    const int64_t plane = int64_t(layer) * a.H + (item0 + it) % a.H;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        acc = mfma16x16x4f32(ap[nb][v].x, b4[v].x, acc);
+        acc = mfma16x16x4f32(ap[nb][v].y, b4[v].y, acc);
+        acc = mfma16x16x4f32(ap[nb][v].z, b4[v].z, acc);
+        acc = mfma16x16x4f32(ap[nb][v].w, b4[v].w, acc);
+      }
+      const int row = 32 * wave + 16 * nb + 4 * kq;  // rows row .. row + 3 of this lane
+      if (it >= ni) continue;
+      if (is_k) {
+        if constexpr (MK > 0) {
+          uint32_t chunk = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float y = acc[r] * inv;
+            uint32_t idx = 0;
+#pragma unroll
+            for (int b = 0; b < (1 << MK) - 1; ++b) idx += (y >= cb[1][b]) ? 1u : 0u;
+            rs[it][row + r] = y - cb[0][idx];
+            chunk |= idx << (r * MK);
+          }
+          or_bits(&krec[it][0], row * MK, chunk, 4 * MK);
+        }
+      } else if constexpr (BV > 0) {
+        if (slot >= 0) {
+          const int bitp = int(slot % kVBlock) * BV;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float y = acc[r] * inv;
+            uint32_t idx = 0;
+#pragma unroll
+            for (int b = 0; b < (1 << BV) - 1; ++b) idx += (y >= cb[3][b]) ? 1u : 0u;
+            uint32_t* g = reinterpret_cast<uint32_t*>(a.v_idx + ((plane * vblocks + slot / kVBlock) * D + row + r) *
+                                                                     (4 * BV)) +
+                          (bitp >> 5);
+            atomicAnd(g, ~(((1u << BV) - 1u) << (bitp & 31)));
+            atomicOr(g, idx << (bitp & 31));
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---------------- key residual norm and QJL signs
+  if constexpr (MK > 0) {
+    // Residual norms: wave w reduces items 2w, 2w + 1.
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int it = 2 * wave + k;
+      const float r0 = rs[it][lane], r1 = rs[it][lane + 64];
+      const float ss = wave_sum(fmaf(r0, r0, r1 * r1));
+      if (lane == 0) rnrm[it] = nrm[it] * sqrtf(ss);
+    }
+    // z = (S Pi^T)(y - c[idx]) for columns r16 < 8; bit = [n z >= 0].
+    const int it = r16 & (kAppendItems - 1);
+    const float4* br = reinterpret_cast<const float4*>(&rs[it][4 * kq]);
+    float4 b4[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) b4[v] = br[4 * v];
+    const float n = nrm[it];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        acc = mfma16x16x4f32(am[nb][v].x, b4[v].x, acc);
+        acc = mfma16x16x4f32(am[nb][v].y, b4[v].y, acc);
+        acc = mfma16x16x4f32(am[nb][v].z, b4[v].z, acc);
+        acc = mfma16x16x4f32(am[nb][v].w, b4[v].w, acc);
+      }
+      const int row = 32 * wave + 16 * nb + 4 * kq;
+      if (r16 < kAppendItems && it < ni) {
+        uint32_t bits = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bits |= (acc[r] * n >= 0.f ? 1u : 0u) << r;
+        atomicOr(&srec[it][row >> 5], bits << (row & 31));
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---------------- records
+  for (int e = tid; e < kAppendItems * 32; e += 256) {
+    const int it = e >> 5, w = e & 31;
+    const int64_t slot = slot_of[it];
+    if (it >= ni || slot < 0) continue;
+    const int64_t plane = int64_t(layer) * a.H + (item0 + it) % a.H;
+    const int64_t rec = plane * a.capacity + slot;
+    if constexpr (MK > 0) {
+      if (w < 4 * MK) reinterpret_cast<uint32_t*>(a.k_idx + rec * (16 * MK))[w] = krec[it][w];
+      if (w >= 16 && w < 20) reinterpret_cast<uint32_t*>(a.k_sign + rec * 16)[w - 16] = srec[it][w - 16];
+      if (w == 20) a.k_norm[rec] = nrm[it];
+      if (w == 21) a.k_rnorm[rec] = rnrm[it];
+    }
+    if constexpr (BV > 0) {
+      if (w == 22) a.v_norm[rec] = nrm[kAppendItems + it];
+    }
+  }
+  if constexpr (MK == 0 || BV == 0) {
+    for (int e = tid; e < kAppendItems * D; e += 256) {
+      const int it = e >> 7, j = e & 127;
+      const int64_t slot = slot_of[it];
+      if (it >= ni || slot < 0) continue;
+      const int64_t plane = int64_t(layer) * a.H + (item0 + it) % a.H;
+      if constexpr (MK == 0) a.k_f16[(plane * a.capacity + slot) * D + j] = f16_bits(xs[it][j]);
+      if constexpr (BV == 0)
+        a.v_f16[((plane * vblocks + slot / kVBlock) * D + j) * kVBlock + slot % kVBlock] =
+            f16_bits(xs[kAppendItems + it][j]);
+    }
+  }
 }
 
 // ===========================================================================
@@ -905,111 +1182,165 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// qr = Pi q (q itself for fp16 keys), qs = S q.  One block per (32-row
-// quarter, KV head) of a (layer, batch): thread t computes row
-// 32 * quarter + t % 32 of Pi q (t / 32 even) or S q (odd) for two of the
-// group's query heads per pass of eight.
-constexpr int kPrepHeads = 8;
-__global__ __launch_bounds__(256) void qprep_kernel(const float* q, const float* pi, const float* s,
-                                                    float* qprep, int batch, int H, int Hq, int rotate) {
-  __shared__ float qv[kPrepHeads][D];
+// qr = Pi q (q itself for fp16 keys), qs = S q.  The products are
+// [Pi; S] (256 x 128) times the group's queries (128 x G) on fp32 MFMA
+// 16x16x4, with no LDS: wave w of block (quarter, KV head, batch, layer) owns
+// rows 16 bi .. 16 bi + 15 of [Pi; S], bi = 4 quarter + w.  Lane l holds row
+// 16 bi + l % 16 and query head l % 16 of the head block; its float4 pieces
+// 16 v + 4 (l / 16) .. + 3 of both are step v's four k-values, the same k on
+// the A and the B side, so the sum over k is exact in any order.
+template <bool ROT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void qprep_kernel(
+    const float* q, const float* pi, const float* s, float* qprep, int batch, int H, int Hq) {
   const int hk = blockIdx.x >> 2, quarter = blockIdx.x & 3, b = blockIdx.y, layer = blockIdx.z;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = Hq / H;
-  const int i = 32 * quarter + (tid & 31), which = (tid >> 5) & 1, pair = tid >> 6;
-  const float4* mrow = reinterpret_cast<const float4*>((which ? s : pi) + int64_t(layer) * D * D + int64_t(i) * D);
-  for (int g0 = 0; g0 < G; g0 += kPrepHeads) {
-    const int ng = G - g0 < kPrepHeads ? G - g0 : kPrepHeads;
-    const int64_t row0 = (int64_t(layer) * batch + b) * Hq + int64_t(hk) * G + g0;
-    for (int e = tid; e < kPrepHeads * D; e += 256) qv[e / D][e % D] = (e / D) < ng ? q[row0 * D + e] : 0.f;
-    __syncthreads();
-    const int ga = 2 * pair, gb = 2 * pair + 1;
-    if (!rotate) {
-      if (ga < ng) qprep[(row0 + ga) * 2 * D + which * D + i] = which ? 0.f : qv[ga][i];
-      if (gb < ng) qprep[(row0 + gb) * 2 * D + which * D + i] = which ? 0.f : qv[gb][i];
-    } else if (ga < ng) {
-      float4 m4[32];
-#pragma unroll
-      for (int u = 0; u < 32; ++u) m4[u] = mrow[u];
-      float acc_a = 0.f, acc_b = 0.f;
-#pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const int j = 4 * u;
-        acc_a = fmaf(m4[u].x, qv[ga][j], acc_a);
-        acc_a = fmaf(m4[u].y, qv[ga][j + 1], acc_a);
-        acc_a = fmaf(m4[u].z, qv[ga][j + 2], acc_a);
-        acc_a = fmaf(m4[u].w, qv[ga][j + 3], acc_a);
-        acc_b = fmaf(m4[u].x, qv[gb][j], acc_b);
-        acc_b = fmaf(m4[u].y, qv[gb][j + 1], acc_b);
-        acc_b = fmaf(m4[u].z, qv[gb][j + 2], acc_b);
-        acc_b = fmaf(m4[u].w, qv[gb][j + 3], acc_b);
-      }
-      qprep[(row0 + ga) * 2 * D + which * D + i] = acc_a;
-      if (gb < ng) qprep[(row0 + gb) * 2 * D + which * D + i] = acc_b;
+  const int64_t row0 = (int64_t(layer) * batch + b) * Hq + int64_t(hk) * G;
+  if constexpr (!ROT) {
+    // fp16 keys are scored against q itself; no sketch.
+    for (int e = quarter * 256 + tid; e < G * D; e += 1024) {
+      const int g = e >> 7, i = e & 127;
+      qprep[(row0 + g) * 2 * D + i] = q[(row0 + g) * D + i];
+      qprep[(row0 + g) * 2 * D + D + i] = 0.f;
     }
-    __syncthreads();
+    return;
+  } else {
+    const int bi = 4 * quarter + wave, mat = bi >> 3, i0 = 16 * (bi & 7);
+    const int r16 = lane & 15, kq = lane >> 4;
+    const float4* arow =
+        reinterpret_cast<const float4*>((mat ? s : pi) + int64_t(layer) * D * D + int64_t(i0 + r16) * D + 4 * kq);
+    float4 a4[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) a4[v] = arow[4 * v];
+    for (int g0 = 0; g0 < G; g0 += 16) {
+      const int g = g0 + r16;
+      const float4* qrow = reinterpret_cast<const float4*>(q + (row0 + (g < G ? g : G - 1)) * D + 4 * kq);
+      float4 b4[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) b4[v] = qrow[4 * v];
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        acc = mfma16x16x4f32(a4[v].x, b4[v].x, acc);
+        acc = mfma16x16x4f32(a4[v].y, b4[v].y, acc);
+        acc = mfma16x16x4f32(a4[v].z, b4[v].z, acc);
+        acc = mfma16x16x4f32(a4[v].w, b4[v].w, acc);
+      }
+      // D: rows i0 + 4 kq + r, column (head) l % 16.
+      if (g < G) {
+        float4 o = {acc[0], acc[1], acc[2], acc[3]};
+        *reinterpret_cast<float4*>(qprep + (row0 + g) * 2 * D + mat * D + i0 + 4 * kq) = o;
+      }
+    }
   }
 }
 
-// Merges the split partials of one (layer, batch, query head) and writes
-// out = Pi^T (acc / l) (acc / l for fp16 values).  Pi is staged in LDS with
-// one round of vector loads.
-__global__ __launch_bounds__(128) void combine_kernel(const float* partial, const float* pi, float* out, int batch,
-                                                      int Hq, int n_splits, int rotate) {
-  __shared__ float pim[D * D];
-  __shared__ float res[D];
-  __shared__ float red[2][128];
-  const int h = blockIdx.x, b = blockIdx.y, layer = blockIdx.z, tid = threadIdx.x;
-  const int64_t row = (int64_t(layer) * batch + b) * Hq + h;
-  if (rotate) {
-    const float4* src = reinterpret_cast<const float4*>(pi + int64_t(layer) * D * D);
-    float4 buf[32];
+// Merges the split partials of one (layer, batch, KV head) for every query
+// head of its group and writes out = Pi^T (acc / l) (acc / l for fp16
+// values).  Merge: thread t works on coordinate t % 128 of heads t / 128,
+// t / 128 + 2, ...; the partials are read in batches of 4 splits x 8 heads
+// with clamped (always valid) addresses so that a batch's loads are in flight
+// together, and merged with a running maximum.  Pi^T: fp32 MFMA 16x16x4 with
+// D[i][g] = sum_j Pi[j][i] res[g][j]; wave w owns output rows 32 w .. 32 w + 31
+// (two 16-row blocks); its A operands (columns of Pi) are loaded from global
+// memory at the start, before the merge, and res comes from LDS.
+constexpr int kCombineHeads = 16;
+template <bool ROT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void combine_kernel(
+    const float* partial, const float* pi, float* out, int batch, int H, int Hq, int n_splits) {
+  constexpr bool rotate = ROT;
+  __shared__ __align__(16) float res[kCombineHeads][D];
+  const int hk = blockIdx.x, b = blockIdx.y, layer = blockIdx.z, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, r16 = lane & 15, kq = lane >> 4;
+  const int i = tid & 127, half = tid >> 7;
+  const int G = Hq / H;
+  // A operands: block n (rows 32 wave + 16 n + r16), step (v, c): Pi[16 v + 4 kq + c][row].
+  float pa[ROT ? 2 : 1][32];
+  if constexpr (ROT) {
+    const float* pil = pi + int64_t(layer) * D * D;
 #pragma unroll
-    for (int u = 0; u < 32; ++u) buf[u] = src[tid + 128 * u];
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
-    for (int u = 0; u < 32; ++u) reinterpret_cast<float4*>(pim)[tid + 128 * u] = buf[u];
+      for (int v = 0; v < 8; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) pa[n][4 * v + c] = pil[int64_t(16 * v + 4 * kq + c) * D + 32 * wave + 16 * n + r16];
   }
-  const float* P = partial + row * int64_t(n_splits) * (D + 2);
-  float M = -INFINITY;
-  for (int sp = tid; sp < n_splits; sp += 128) M = fmaxf(M, P[int64_t(sp) * (D + 2)]);
-  red[0][tid] = M;
-  __syncthreads();
-  for (int w = 64; w > 0; w >>= 1) {
-    if (tid < w) red[0][tid] = fmaxf(red[0][tid], red[0][tid + w]);
+  constexpr int NH = kCombineHeads / 2, SB = 4;
+  for (int g0 = 0; g0 < G; g0 += kCombineHeads) {
+    const int ng = G - g0 < kCombineHeads ? G - g0 : kCombineHeads;
+    const int64_t row0 = (int64_t(layer) * batch + b) * Hq + int64_t(hk) * G + g0;
+    float M[NH], L[NH], A[NH];
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+      M[k] = -INFINITY;
+      L[k] = 0.f;
+      A[k] = 0.f;
+    }
+    for (int sp0 = 0; sp0 < n_splits; sp0 += SB) {
+      float ms[NH][SB], ls[NH][SB], as[NH][SB];
+#pragma unroll
+      for (int k = 0; k < NH; ++k) {
+        const int g = half + 2 * k < ng ? half + 2 * k : ng - 1;
+        const float* P = partial + (row0 + g) * int64_t(n_splits) * (D + 2);
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const int64_t sp = sp0 + u < n_splits ? sp0 + u : n_splits - 1;
+          ms[k][u] = P[sp * (D + 2)];
+          ls[k][u] = P[sp * (D + 2) + 1];
+          as[k][u] = P[sp * (D + 2) + 2 + i];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NH; ++k) {
+        float Mn = M[k];
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+          if (sp0 + u < n_splits) Mn = fmaxf(Mn, ms[k][u]);
+        const float f0 = M[k] == -INFINITY ? 0.f : __expf(M[k] - Mn);
+        L[k] *= f0;
+        A[k] *= f0;
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const float f = (sp0 + u >= n_splits || ms[k][u] == -INFINITY) ? 0.f : __expf(ms[k][u] - Mn);
+          L[k] = fmaf(ls[k][u], f, L[k]);
+          A[k] = fmaf(as[k][u], f, A[k]);
+        }
+        M[k] = Mn;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+      const int g = half + 2 * k;
+      // L is 0 only for an empty sequence; NaN must propagate.
+      const float v = (L[k] > 0.f || L[k] != L[k]) ? A[k] / L[k] : 0.f;
+      if (rotate)
+        res[g][i] = g < ng ? v : 0.f;
+      else if (g < ng)
+        out[(row0 + g) * D + i] = v;
+    }
+    if constexpr (!ROT) continue;
+    __syncthreads();
+    const float4* bres = reinterpret_cast<const float4*>(&res[r16][4 * kq]);
+    float4 b4[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) b4[v] = bres[4 * v];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        acc = mfma16x16x4f32(pa[n][4 * v + 0], b4[v].x, acc);
+        acc = mfma16x16x4f32(pa[n][4 * v + 1], b4[v].y, acc);
+        acc = mfma16x16x4f32(pa[n][4 * v + 2], b4[v].z, acc);
+        acc = mfma16x16x4f32(pa[n][4 * v + 3], b4[v].w, acc);
+      }
+      if (r16 < ng) {
+        float4 o = {acc[0], acc[1], acc[2], acc[3]};
+        *reinterpret_cast<float4*>(out + (row0 + r16) * D + 32 * wave + 16 * n + 4 * kq) = o;
+      }
+    }
     __syncthreads();
   }
-  M = red[0][0];
-  float L = 0.f;
-  for (int sp = tid; sp < n_splits; sp += 128) {
-    const float ms = P[int64_t(sp) * (D + 2)];
-    L += ms == -INFINITY ? 0.f : P[int64_t(sp) * (D + 2) + 1] * __expf(ms - M);
-  }
-  red[1][tid] = L;
-  __syncthreads();
-  for (int w = 64; w > 0; w >>= 1) {
-    if (tid < w) red[1][tid] += red[1][tid + w];
-    __syncthreads();
-  }
-  L = red[1][0];
-  float acc = 0.f;
-#pragma unroll 8
-  for (int sp = 0; sp < n_splits; ++sp) {
-    const float ms = P[int64_t(sp) * (D + 2)];
-    const float as = P[int64_t(sp) * (D + 2) + 2 + tid];
-    acc += ms == -INFINITY ? 0.f : as * __expf(ms - M);
-  }
-  // L is 0 only for an empty sequence; NaN must propagate.
-  const float v = (L > 0.f || L != L) ? acc / L : 0.f;
-  if (!rotate) {
-    out[row * D + tid] = v;
-    return;
-  }
-  res[tid] = v;
-  __syncthreads();
-  float o = 0.f;
-#pragma unroll 16
-  for (int j = 0; j < D; ++j) o = fmaf(pim[j * D + tid], res[j], o);
-  out[row * D + tid] = o;
 }
 
 template <bool SCORE>
@@ -1098,8 +1429,13 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   const int mk = fmt->k_bits > 0 ? fmt->k_bits - 1 : 0;
   const int bv = fmt->v_bits;
   if (stages & kStagePrepare) {
-    hipLaunchKernelGGL(qprep_kernel, dim3(cache->n_kv_heads * 4, batch, cache->n_layers), dim3(256), 0, hs, q,
-                       tables->pi, tables->s, qprep, batch, cache->n_kv_heads, n_q_heads, fmt->k_bits > 0 ? 1 : 0);
+    const dim3 qgrid(cache->n_kv_heads * 4, batch, cache->n_layers);
+    if (fmt->k_bits > 0)
+      hipLaunchKernelGGL(qprep_kernel<true>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qprep, batch,
+                         cache->n_kv_heads, n_q_heads);
+    else
+      hipLaunchKernelGGL(qprep_kernel<false>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qprep, batch,
+                         cache->n_kv_heads, n_q_heads);
     if ((st = launch_status("qprep"))) return st;
   }
   if (max_seq_len == 0 && SCORE) return TQ_OK;
@@ -1140,8 +1476,13 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
     if ((st = launch_status("decode"))) return st;
   }
   if (!SCORE && (stages & kStageCombine)) {
-    hipLaunchKernelGGL(combine_kernel, dim3(n_q_heads, batch, cache->n_layers), dim3(128), 0, hs, partial,
-                       tables->pi, out, batch, n_q_heads, int(plan.n_splits), bv > 0 ? 1 : 0);
+    const dim3 cgrid(cache->n_kv_heads, batch, cache->n_layers);
+    if (bv > 0)
+      hipLaunchKernelGGL(combine_kernel<true>, cgrid, dim3(256), 0, hs, partial, tables->pi, out, batch,
+                         cache->n_kv_heads, n_q_heads, int(plan.n_splits));
+    else
+      hipLaunchKernelGGL(combine_kernel<false>, cgrid, dim3(256), 0, hs, partial, tables->pi, out, batch,
+                         cache->n_kv_heads, n_q_heads, int(plan.n_splits));
     if ((st = launch_status("combine"))) return st;
   }
   return TQ_OK;
@@ -1203,6 +1544,22 @@ tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq
   a.v_idx = cache->v_idx;
   a.v_norm = cache->v_norm;
   a.v_f16 = static_cast<uint16_t*>(cache->v_f16);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (n_tokens < kCompressTile) {
+    // Appends: the VALU kernel, 8 (token, head) items per workgroup.
+    const int64_t groups = (n_tokens * a.H + kAppendItems - 1) / kAppendItems;
+#define TQ_APP(MK_, BV_)                                                                               \
+  if (a.mk == MK_ && a.bv == BV_) {                                                                    \
+    hipLaunchKernelGGL((compress_append_kernel<MK_, BV_>), dim3(unsigned(groups), unsigned(n_layers)), \
+                       dim3(256), 0, hs, a);                                                           \
+    return launch_status("compress (append)");                                                         \
+  }
+#define TQ_APP_V(MK_) TQ_APP(MK_, 0) TQ_APP(MK_, 1) TQ_APP(MK_, 2) TQ_APP(MK_, 4)
+    TQ_APP_V(0) TQ_APP_V(1) TQ_APP_V(2) TQ_APP_V(3) TQ_APP_V(4)
+#undef TQ_APP_V
+#undef TQ_APP
+    return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for key bits %d / value bits %d", a.mk, a.bv);
+  }
   const size_t smem = sizeof(CompressSmem);
   const void* fn = nullptr;
 #define TQ_CMP(MK_, BV_) if (a.mk == MK_ && a.bv == BV_) fn = reinterpret_cast<const void*>(compress_kernel<MK_, BV_>);
@@ -1214,8 +1571,7 @@ tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq
   if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(smem)) != hipSuccess)
     return fail(TQ_ERR_HIP, "cannot raise the LDS limit to %zu bytes", smem);
   void* args[] = {&a};
-  if (hipLaunchKernel(fn, dim3(unsigned(wgs), unsigned(n_layers)), dim3(256), args, smem,
-                      static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (hipLaunchKernel(fn, dim3(unsigned(wgs), unsigned(n_layers)), dim3(256), args, smem, hs) != hipSuccess)
     return fail(TQ_ERR_HIP, "compress launch failed: %s", hipGetErrorString(hipGetLastError()));
   return launch_status("compress");
 }
