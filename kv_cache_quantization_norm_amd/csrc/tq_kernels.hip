@@ -53,7 +53,7 @@ __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v,
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 // Sum over the 64 lanes, in a fixed order, returned to every lane: DPP within
 // each 16-lane row (quad swaps, then the half-row and row mirrors), then the
@@ -716,8 +716,7 @@ struct DecodeArgs {
 // DPP row broadcast: every lane of a 16-lane row reads lane E of its row.
 template <int E>
 __device__ __forceinline__ float row_bcast(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + E, 0xF, 0xF,
-                                                               false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + E, 0xF, 0xF, false));
 }
 template <int B>
 __device__ __forceinline__ void row_bcast8(float v, float (&o)[8]) {
@@ -893,6 +892,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t slot_base = plane * a.capacity + start;   // slot index of token 0
   constexpr int KREC = MK > 0 ? 16 * MK : 2 * D;          // bytes per key code record
 
+  // Scores are kept in base-2 units (scaled by log2 e) so that the softmax
+  // weights are plain exp2; tq_score writes natural-unit logits.
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float kscale = SCORE ? a.scale : a.scale * kLog2e;
+  const float kscale_r = kscale * a.kappa;
   float m_run = -INFINITY, l_run = 0.f, sig = 0.f;
   floatx4 acc[8];
 #pragma unroll
@@ -1007,23 +1011,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     // ---- logits of lane (g = col, q): tokens 8 q + e, e = 4 T + r
     const int64_t tb = c0 + 8 * q;
+    // Only the last chunk of a split can be partial (a uniform branch).
+    const bool full = c0 + kChunk <= t_hi;
+    const int64_t rem = t_hi - tb;   // valid tokens of this lane's 8 (may be <= 0)
     float lg[8];
     float kn[8], rn[8];
     if constexpr (MK > 0) {
-      row_bcast8<0>(cur.nrm[0], kn);
-      row_bcast8<8>(cur.nrm[0], rn);
+      // Norms pre-multiplied by the logit scale (key norm) or scale * kappa (residual norm).
+      const float nsc = cur.nrm[0] * (col < 8 ? kscale : kscale_r);
+      row_bcast8<0>(nsc, kn);
+      row_bcast8<8>(nsc, rn);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const bool ok = tb + e < t_hi;
       const float smv = sm_[e >> 2][e & 3];
       float l;
       if constexpr (MK > 0) {
-        l = a.scale * fmaf(kn[e], smv, a.kappa * rn[e] * sq_[e >> 2][e & 3]);
+        l = fmaf(kn[e], smv, rn[e] * sq_[e >> 2][e & 3]);
       } else {
-        l = a.scale * smv;
+        l = kscale * smv;
       }
-      lg[e] = ok ? l : -INFINITY;
+      lg[e] = (full || e < rem) ? l : -INFINITY;
     }
     if constexpr (SCORE) {
       if (head_ok) {
@@ -1045,7 +1053,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       float vmax = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if constexpr (BV > 0) vn[e] = (tb + e < t_hi) ? vn[e] : 0.f;
+        if constexpr (BV > 0) vn[e] = (full || e < rem) ? vn[e] : 0.f;
         else vn[e] = 1.f;
         vmax = fmaxf(vmax, vn[e]);
       }
@@ -1058,9 +1066,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = 0.f;
       } else {
-        alpha = __expf(m_run - m_new);
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = __expf(lg[e] - m_new);
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(lg[e] - m_new);
       }
       float psum = 0.f;
 #pragma unroll
@@ -1143,7 +1151,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w][col]);
-    const float f = (m_run == -INFINITY) ? 0.f : __expf(m_run - M) * sig;
+    const float f = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M) * sig;
     // Waves add their accumulators in wave order (each element belongs to one
     // lane of each wave), so the result is the same on every run.
     for (int w = 0; w < kWaves; ++w) {
@@ -1172,7 +1180,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int w = 0; w < kWaves; ++w) Mg = fmaxf(Mg, mw[w][g]);
         v = 0.f;
         for (int w = 0; w < kWaves; ++w)
-          if (mw[w][g] != -INFINITY) v += lw[w][g] * __expf(mw[w][g] - Mg);
+          if (mw[w][g] != -INFINITY) v += lw[w][g] * __builtin_amdgcn_exp2f(mw[w][g] - Mg);
       } else {
         v = accsum[g][i - 2];
       }
@@ -1296,12 +1304,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
         for (int u = 0; u < SB; ++u)
           if (sp0 + u < n_splits) Mn = fmaxf(Mn, ms[k][u]);
-        const float f0 = M[k] == -INFINITY ? 0.f : __expf(M[k] - Mn);
+        const float f0 = M[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[k] - Mn);
         L[k] *= f0;
         A[k] *= f0;
 #pragma unroll
         for (int u = 0; u < SB; ++u) {
-          const float f = (sp0 + u >= n_splits || ms[k][u] == -INFINITY) ? 0.f : __expf(ms[k][u] - Mn);
+          const float f =
+              (sp0 + u >= n_splits || ms[k][u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[k][u] - Mn);
           L[k] = fmaf(ls[k][u], f, L[k]);
           A[k] = fmaf(as[k][u], f, A[k]);
         }
