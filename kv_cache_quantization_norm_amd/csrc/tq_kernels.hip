@@ -58,6 +58,19 @@ __device__ __forceinline__ float dpp_f(float v) {
 // Sum over the 64 lanes, in a fixed order, returned to every lane: DPP within
 // each 16-lane row (quad swaps, then the half-row and row mirrors), then the
 // four row sums through readlane.
+// Maximum over the 64 lanes (NaN ignored, as fmaxf does), returned to every lane.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  const int b = __builtin_bit_cast(int, v);
+  return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))),
+               fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48))));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
@@ -782,27 +795,70 @@ __device__ __forceinline__ half8 deq8(uint32_t bits, const uint32_t* lut) {
   return as_half8(w);
 }
 
-// Same with two-term (hi, lo) centroids from a HILO table.
+// Key tables.  A key code group of NC codes (NC m = 12 bits for m = 3, 8
+// bits otherwise) indexes one entry in each of two tables: the fp16 roundings
+// c_hi of its NC centroids, and the fp16 roundings of the remainders c - c_hi
+// (together about 22 significant bits).  Each lookup lands straight in an MFMA
+// operand (8 consecutive coordinates = 8 / NC entries), with no repacking.
+// The NC-code tables are assembled from two-code pair tables.
+template <int M> struct KLut {
+  static constexpr int NC = M == 1 ? 8 : (M == 4 ? 2 : 4);  // codes per entry
+  static constexpr int E = 1 << (NC * M);                   // entries per table
+  static constexpr int EW = NC / 2;                         // dwords per entry
+  static constexpr int PAIRS = 1 << (2 * M);                // two-code pair entries
+};
+
+// Pair tables: entry x (two codes, x = c0 | c1 << M) = fp16 pair (c0, c1).
 template <int M>
-__device__ __forceinline__ void deq8_hilo(uint32_t bits, const uint32_t* lut, half8& hi, half8& lo) {
+__device__ __forceinline__ void build_kpairs(uint32_t* phi, uint32_t* plo, const float* cent, int tid) {
+  for (int x = tid; x < KLut<M>::PAIRS; x += 256) {
+    const float c0 = cent[x & ((1 << M) - 1)], c1 = cent[x >> M];
+    const float r0 = c0 - float(_Float16(c0)), r1 = c1 - float(_Float16(c1));
+    phi[x] = uint32_t(f16_bits(c0)) | (uint32_t(f16_bits(c1)) << 16);
+    plo[x] = uint32_t(f16_bits(r0)) | (uint32_t(f16_bits(r1)) << 16);
+  }
+}
+// NC-code tables from the pair tables (after a barrier): dword k of entry x is
+// the pair of codes 2k, 2k + 1.
+template <int M>
+__device__ __forceinline__ void build_ktab(uint32_t* khi, uint32_t* klo, const uint32_t* phi, const uint32_t* plo,
+                                           int tid) {
+  using K = KLut<M>;
+  if constexpr (K::NC == 2) return;  // the pair tables are the tables
+  for (int x = tid; x < K::E; x += 256) {
+#pragma unroll
+    for (int k = 0; k < K::EW; ++k) {
+      const int pr = (x >> (2 * M * k)) & (K::PAIRS - 1);
+      khi[x * K::EW + k] = phi[pr];
+      klo[x * K::EW + k] = plo[pr];
+    }
+  }
+}
+
+// 8 consecutive m-bit key codes (LSB-first in `bits`) -> fp16 hi and lo halves.
+template <int M>
+__device__ __forceinline__ void deq8_k(uint32_t bits, const uint32_t* khi, const uint32_t* klo, half8& hi, half8& lo) {
   if constexpr (M == 1) {
-    const u32x4* e = reinterpret_cast<const u32x4*>(lut + (bits & 0xFFu) * 8);
-    hi = as_half8(e[0]);
-    lo = as_half8(e[1]);
-  } else if constexpr (M == 2) {
-    const u32x4 a0 = *reinterpret_cast<const u32x4*>(lut + (bits & 0xFFu) * 4);
-    const u32x4 a1 = *reinterpret_cast<const u32x4*>(lut + ((bits >> 8) & 0xFFu) * 4);
-    hi = as_half8(u32x4{a0[0], a0[1], a1[0], a1[1]});
-    lo = as_half8(u32x4{a0[2], a0[3], a1[2], a1[3]});
+    hi = as_half8(*reinterpret_cast<const u32x4*>(khi + (bits & 0xFFu) * 4));
+    lo = as_half8(*reinterpret_cast<const u32x4*>(klo + (bits & 0xFFu) * 4));
+  } else if constexpr (M == 4) {
+    const uint32_t i0 = bits & 0xFFu, i1 = (bits >> 8) & 0xFFu, i2 = (bits >> 16) & 0xFFu, i3 = bits >> 24;
+    hi = as_half8(u32x4{khi[i0], khi[i1], khi[i2], khi[i3]});
+    lo = as_half8(u32x4{klo[i0], klo[i1], klo[i2], klo[i3]});
   } else {
-    constexpr uint32_t mask = M == 3 ? 63u : 0xFFu;
-    constexpr int sh = 2 * M;
-    const u32x2 e0 = *reinterpret_cast<const u32x2*>(lut + (bits & mask) * 2);
-    const u32x2 e1 = *reinterpret_cast<const u32x2*>(lut + ((bits >> sh) & mask) * 2);
-    const u32x2 e2 = *reinterpret_cast<const u32x2*>(lut + ((bits >> (2 * sh)) & mask) * 2);
-    const u32x2 e3 = *reinterpret_cast<const u32x2*>(lut + ((bits >> (3 * sh)) & mask) * 2);
-    hi = as_half8(u32x4{e0[0], e1[0], e2[0], e3[0]});
-    lo = as_half8(u32x4{e0[1], e1[1], e2[1], e3[1]});
+    constexpr uint32_t mask = M == 3 ? 0xFFFu : 0xFFu;
+    // Byte offsets of the two entries.  The low-half reads take opaque copies
+    // of the offsets so that they are not fused with the high-half reads into
+    // one wider read (which would interleave the halves in registers).
+    const uint32_t a0 = (bits & mask) * 8, a1 = ((bits >> (4 * M)) & mask) * 8;
+    uint32_t b0 = a0, b1 = a1;
+    asm volatile("" : "+v"(b0), "+v"(b1));
+    const char* ph = reinterpret_cast<const char*>(khi);
+    const char* pl = reinterpret_cast<const char*>(klo);
+    const u32x2 h0 = *reinterpret_cast<const u32x2*>(ph + a0), h1 = *reinterpret_cast<const u32x2*>(ph + a1);
+    const u32x2 l0 = *reinterpret_cast<const u32x2*>(pl + b0), l1 = *reinterpret_cast<const u32x2*>(pl + b1);
+    hi = as_half8(u32x4{h0[0], h0[1], h1[0], h1[1]});
+    lo = as_half8(u32x4{l0[0], l0[1], l1[0], l1[1]});
   }
 }
 
@@ -822,13 +878,34 @@ __device__ __forceinline__ uint32_t slab_bits(const uint32_t (&w)[N], int s) {
 
 template <int MK, int BV, bool SCORE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
-  constexpr int KW = MK > 0 ? Lut<MK, true>::WORDS : 1;
+  using KL = KLut<(MK > 0 ? MK : 1)>;
+  constexpr int KT = MK > 0 ? KL::E * KL::EW : 1;                        // dwords per key table
+  constexpr int KP = MK > 0 && KL::NC > 2 ? KL::PAIRS : 1;                // pair-table dwords (if separate)
   constexpr int VW = BV > 0 ? Lut<BV, false>::WORDS : 1;
-  __shared__ __align__(16) uint32_t lut_k[KW];
-  __shared__ __align__(16) uint32_t lut_v[VW];
-  __shared__ __align__(16) uint32_t lut_s[256 * 4];
-  __shared__ float mw[kWaves][16], lw[kWaves][16];
-  __shared__ float accsum[16][D];
+  // One LDS block with fixed offsets, the tables read in the token loop
+  // first so that every one of them is addressed with an immediate offset
+  // (below 64 KB): value table, sign table, key high and low tables.
+  constexpr int OFF_V = 0;
+  constexpr int OFF_S = OFF_V + ((VW * 4 + 15) / 16) * 16;
+  constexpr int OFF_KHI = OFF_S + 256 * 16;
+  constexpr int OFF_KLO = OFF_KHI + KT * 4;
+  constexpr int OFF_PHI = OFF_KLO + KT * 4;
+  constexpr int OFF_PLO = OFF_PHI + KP * 4;
+  constexpr int OFF_MW = OFF_PLO + KP * 4;
+  constexpr int OFF_LW = OFF_MW + kWaves * 16 * 4;
+  constexpr int OFF_ACC = OFF_LW + kWaves * 16 * 4;
+  constexpr int LDS_BYTES = OFF_ACC + 16 * D * 4;
+  static_assert(OFF_KLO < 65536, "table offsets must fit the LDS immediate");
+  __shared__ __align__(16) unsigned char dsm[LDS_BYTES];
+  uint32_t* const lut_v = reinterpret_cast<uint32_t*>(dsm + OFF_V);
+  uint32_t* const lut_s = reinterpret_cast<uint32_t*>(dsm + OFF_S);
+  uint32_t* const lut_khi = reinterpret_cast<uint32_t*>(dsm + OFF_KHI);
+  uint32_t* const lut_klo = reinterpret_cast<uint32_t*>(dsm + OFF_KLO);
+  uint32_t* const pair_hi = reinterpret_cast<uint32_t*>(dsm + OFF_PHI);
+  uint32_t* const pair_lo = reinterpret_cast<uint32_t*>(dsm + OFF_PLO);
+  float(*const mw)[16] = reinterpret_cast<float(*)[16]>(dsm + OFF_MW);
+  float(*const lw)[16] = reinterpret_cast<float(*)[16]>(dsm + OFF_LW);
+  float(*const accsum)[D] = reinterpret_cast<float(*)[D]>(dsm + OFF_ACC);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, q = lane >> 4;   // MFMA column (head / coordinate) and k-group
@@ -846,7 +923,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t t_hi = t_lo + a.split_tokens < len ? t_lo + a.split_tokens : len;
 
   // Tables.
-  if constexpr (MK > 0) build_lut<MK, true>(lut_k, a.kc, tid);
+  if constexpr (MK > 0) {
+    if constexpr (KL::NC > 2)
+      build_kpairs<MK>(pair_hi, pair_lo, a.kc, tid);
+    else
+      build_kpairs<MK>(lut_khi, lut_klo, a.kc, tid);
+  }
   if constexpr (BV > 0) build_lut<BV, false>(lut_v, a.vc, tid);
   if constexpr (MK > 0) {
     for (int x = tid; x < 256; x += 256) {
@@ -859,6 +941,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   __syncthreads();
+  if constexpr (MK > 0 && KL::NC > 2) {
+    build_ktab<MK>(lut_khi, lut_klo, pair_hi, pair_lo, tid);
+    __syncthreads();
+  }
 
   // Query operands: lane (col = head g, q) holds Pi q and S q at coordinates
   // 32 q + 8 s + e as fp16 hi + lo pairs.
@@ -897,7 +983,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr float kLog2e = 1.4426950408889634f;
   const float kscale = SCORE ? a.scale : a.scale * kLog2e;
   const float kscale_r = kscale * a.kappa;
-  float m_run = -INFINITY, l_run = 0.f, sig = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  float sig = BV > 0 ? 0.f : 1.f, inv_sig = 1.f;   // value-norm normaliser (uniform over the wave)
   floatx4 acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -993,7 +1080,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
           half8 kh, kl;
-          deq8_hilo<MK>(slab_bits<MK>(cur.kw[T], s2), lut_k, kh, kl);
+          deq8_k<MK>(slab_bits<MK>(cur.kw[T], s2), lut_khi, lut_klo, kh, kl);
           sm_[T] = mfma16x16x32(kh, qrh[s2], sm_[T]);
           sm_[T] = mfma16x16x32(kh, qrl[s2], sm_[T]);
           sm_[T] = mfma16x16x32(kl, qrh[s2], sm_[T]);
@@ -1042,54 +1129,52 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     } else {
       // ---- online softmax (per head; max across the 4 k-groups)
-      float mc = lg[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mc = fmaxf(mc, lg[e]);
-      mc = fmaxf(mc, shfl_xor(mc, 16));
-      mc = fmaxf(mc, shfl_xor(mc, 32));
-      const float m_new = fmaxf(m_run, mc);
-      float vn[8];
-      if constexpr (BV > 0) row_bcast8<0>(cur.nrm[1], vn);
-      float vmax = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if constexpr (BV > 0) vn[e] = (full || e < rem) ? vn[e] : 0.f;
-        else vn[e] = 1.f;
-        vmax = fmaxf(vmax, vn[e]);
+      float cmax = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])),
+                         fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));
+      cmax = fmaxf(cmax, shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, shfl_xor(cmax, 32));
+      // Value norms are normalised by sig, the running maximum of ||v|| over
+      // the wave's tokens (uniform over the wave), so P'' below stays <= 1.
+      float vl = 1.f;
+      float sig_new = sig;
+      if constexpr (BV > 0) {
+        vl = (full || (col & 7) < rem) ? cur.nrm[1] : 0.f;   // this lane's token 8 q + col % 8
+        sig_new = fmaxf(fmaxf(sig, wave_max(vl)), 1e-30f);
       }
-      vmax = fmaxf(vmax, shfl_xor(vmax, 16));
-      vmax = fmaxf(vmax, shfl_xor(vmax, 32));
-      const float sig_new = fmaxf(fmaxf(sig, vmax), 1e-30f);
-      float p[8];
-      float alpha = 1.f;
-      if (m_new == -INFINITY) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = 0.f;
-      } else {
-        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(lg[e] - m_new);
-      }
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) psum += p[e];
-      l_run = l_run * alpha + psum;
-      // The value accumulator is rescaled only when a running maximum moved
-      // (rare after the first chunks); the branch is uniform over the wave.
-      const bool moved = (m_new != m_run) || (sig_new != sig);
-      if (__builtin_amdgcn_ballot_w64(moved) != 0) {
-        const float factor = moved ? alpha * (sig / sig_new) : 1.f;
+      // Rescale only when a running maximum moved (rare after the first
+      // chunks); the branch is uniform over the wave.
+      const bool grow = cmax > m_run;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0 || sig_new != sig) {
+        const float m_new = grow ? cmax : m_run;
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float factor = alpha * (sig / sig_new);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] *= factor;
+        l_run *= alpha;
+        m_run = m_new;
+        sig = sig_new;
+        inv_sig = 1.0f / sig;
       }
-      m_run = m_new;
-      sig = sig_new;
-      // P'' = p * ||v|| / sig as fp16 hi + lo (B operand: lane (g, q), tokens 8 q + e)
-      half8 ph, pl;
-      const float inv_sig = 1.0f / sig;
+      float p[8];
+      float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pv = p[e] * vn[e] * inv_sig;
+        p[e] = __builtin_amdgcn_exp2f(lg[e] - m_run);
+        psum += p[e];
+      }
+      l_run += psum;
+      float vn[8];
+      if constexpr (BV > 0) {
+        row_bcast8<0>(vl * inv_sig, vn);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vn[e] = 1.f;
+      }
+      // P'' = p * ||v|| / sig as fp16 hi + lo (B operand: lane (g, q), tokens 8 q + e)
+      half8 ph, pl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pv = p[e] * vn[e];
         const _Float16 hh = _Float16(pv);
         ph[e] = hh;
         pl[e] = _Float16(pv - float(hh));
