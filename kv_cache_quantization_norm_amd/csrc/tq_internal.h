@@ -15,7 +15,7 @@ void clear_error();
 constexpr int kVBlock = 32;      // slots per value block
 constexpr int kChunk = 32;       // tokens per decode chunk (one wave step)
 constexpr int kWaves = 4;        // waves per decode workgroup
-constexpr int kMaxGroup = 16;    // query heads handled by one decode workgroup
+constexpr int kMaxGroup = 8;     // query heads handled by one decode workgroup
 constexpr int kResidentWorkgroups = 512;  // 256 CUs x 2 decode workgroups
 
 // Format checks shared by all entry points.  `device` additionally requires

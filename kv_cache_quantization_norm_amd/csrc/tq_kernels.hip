@@ -946,16 +946,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
   }
 
-  // Query operands: lane (col = head g, q) holds Pi q and S q at coordinates
-  // 32 q + 8 s + e as fp16 hi + lo pairs.
-  const int g_local = hg * kMaxGroup + col;
+  // Scores are kept in base-2 units (scaled by log2 e) so that the softmax
+  // weights are plain exp2; tq_score writes natural-unit logits.
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float kscale = SCORE ? a.scale : a.scale * kLog2e;
+  const float kscale_r = kscale * a.kappa;
+
+  // Query operands (MFMA B operands).  Columns 0..7 are the group's query
+  // heads as fp16 high parts, columns 8..15 the same heads as fp16
+  // remainders, so one MFMA forms both halves of every product; lanes col and
+  // col ^ 8 then add their results (DPP row rotate by 8).  Lane (col, q) holds
+  // coordinates 32 q + 8 s + e of Pi q * scale and S q * scale * kappa.
+  const int g_local = hg * kMaxGroup + (col & 7);
   const bool head_ok = g_local < a.G;
+  const bool lo_half = col >= 8;
   const int h = hk * a.G + (head_ok ? g_local : 0);
-  half8 qrh[4], qrl[4], qsh[4], qsl[4];
+  half8 qr[4], qs[4];
   {
     const float4* qp = reinterpret_cast<const float4*>(
         a.qprep + ((int64_t(layer) * a.batch + b) * a.Hq + h) * 2 * D + 32 * q);
-    const float keep = head_ok ? 1.f : 0.f;
+    const float kr = head_ok ? kscale : 0.f, ks = head_ok ? kscale_r : 0.f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const float4 r0 = qp[2 * s], r1 = qp[2 * s + 1];
@@ -964,12 +974,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float r = rv[e] * keep, z = zv[e] * keep;
+        const float r = rv[e] * kr, z = zv[e] * ks;
         const _Float16 rh = _Float16(r), zh = _Float16(z);
-        qrh[s][e] = rh;
-        qrl[s][e] = _Float16(r - float(rh));
-        qsh[s][e] = zh;
-        qsl[s][e] = _Float16(z - float(zh));
+        qr[s][e] = lo_half ? _Float16(r - float(rh)) : rh;
+        qs[s][e] = lo_half ? _Float16(z - float(zh)) : zh;
       }
     }
   }
@@ -978,11 +986,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t slot_base = plane * a.capacity + start;   // slot index of token 0
   constexpr int KREC = MK > 0 ? 16 * MK : 2 * D;          // bytes per key code record
 
-  // Scores are kept in base-2 units (scaled by log2 e) so that the softmax
-  // weights are plain exp2; tq_score writes natural-unit logits.
-  constexpr float kLog2e = 1.4426950408889634f;
-  const float kscale = SCORE ? a.scale : a.scale * kLog2e;
-  const float kscale_r = kscale * a.kappa;
   float m_run = -INFINITY, l_run = 0.f;
   float sig = BV > 0 ? 0.f : 1.f, inv_sig = 1.f;   // value-norm normaliser (uniform over the wave)
   floatx4 acc[8];
@@ -994,9 +997,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // the cache, so the loads are unconditional; tokens past the end of the
   // sequence are masked after loading.
   constexpr int MKW = MK > 0 ? MK : 1;
-  // Packed codes are loaded one chunk ahead (double-buffered); norms and fp16
-  // planes are loaded at the top of their own chunk to bound register use.
-  constexpr bool kPrefetch = MK > 0 && BV > 0;
+  // Packed key and value planes go through the software pipeline below;
+  // fp16 planes are loaded at the top of their own chunk.
+  constexpr bool kPrefetch = MK > 0 && BV > 0 && !SCORE;
   // Norms: lane (col, q) loads one key norm (col < 8) or residual norm
   // (col >= 8) of token 8 q + col % 8 and one value norm; the 16 lanes of a
   // row then read them from each other with DPP row broadcasts.
@@ -1066,12 +1069,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
-  // process(c0, cur): everything one chunk needs after its loads.
-  auto process = [&](int64_t c0, const Chunk& cur) {
-    ChunkLate late;
-    if constexpr (MK == 0 || BV == 0) load_late(c0, late);
-    // ---- scores: tile T row col -> token 8 (col/4) + 4 T + col%4
-    floatx4 sm_[2], sq_[2];
+  // ---- scores of one chunk: tile T row col -> token 8 (col/4) + 4 T + col%4
+  auto score = [&](const uint32_t (&kw)[2][MKW], const uint32_t (&sg)[2], const ChunkLate& late,
+                   floatx4 (&sm_)[2], floatx4 (&sq_)[2]) {
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
       sm_[T] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -1080,52 +1080,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
           half8 kh, kl;
-          deq8_k<MK>(slab_bits<MK>(cur.kw[T], s2), lut_khi, lut_klo, kh, kl);
-          sm_[T] = mfma16x16x32(kh, qrh[s2], sm_[T]);
-          sm_[T] = mfma16x16x32(kh, qrl[s2], sm_[T]);
-          sm_[T] = mfma16x16x32(kl, qrh[s2], sm_[T]);
-          const half8 sd = *reinterpret_cast<const half8*>(lut_s + ((cur.sg[T] >> (8 * s2)) & 0xFFu) * 4);
-          sq_[T] = mfma16x16x32(sd, qsh[s2], sq_[T]);
-          sq_[T] = mfma16x16x32(sd, qsl[s2], sq_[T]);
+          deq8_k<MK>(slab_bits<MK>(kw[T], s2), lut_khi, lut_klo, kh, kl);
+          sm_[T] = mfma16x16x32(kh, qr[s2], sm_[T]);
+          sm_[T] = mfma16x16x32(kl, qr[s2], sm_[T]);
+          const half8 sd = *reinterpret_cast<const half8*>(lut_s + ((sg[T] >> (8 * s2)) & 0xFFu) * 4);
+          sq_[T] = mfma16x16x32(sd, qs[s2], sq_[T]);
         }
       } else {
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          sm_[T] = mfma16x16x32(late.kf[T][s2], qrh[s2], sm_[T]);
-          sm_[T] = mfma16x16x32(late.kf[T][s2], qrl[s2], sm_[T]);
-        }
+        for (int s2 = 0; s2 < 4; ++s2) sm_[T] = mfma16x16x32(late.kf[T][s2], qr[s2], sm_[T]);
       }
     }
-    // ---- logits of lane (g = col, q): tokens 8 q + e, e = 4 T + r
+  };
+
+  // ---- logits, online softmax and value accumulation of one chunk.  With
+  // `valid` false every token of the chunk is masked (a pipeline slot past the
+  // wave's last chunk).  The code is branch-free (the rescale is applied every
+  // chunk) so that the compiler can interleave it with the next chunk's scores.
+  auto attend = [&](int64_t c0, bool valid, const float (&nrm)[2], const uint32_t (&vw)[8], const ChunkLate& late,
+                    const floatx4 (&sm_)[2], const floatx4 (&sq_)[2]) {
     const int64_t tb = c0 + 8 * q;
-    // Only the last chunk of a split can be partial (a uniform branch).
-    const bool full = c0 + kChunk <= t_hi;
-    const int64_t rem = t_hi - tb;   // valid tokens of this lane's 8 (may be <= 0)
+    const bool full = valid && c0 + kChunk <= t_hi;
+    const int64_t rem = valid ? t_hi - tb : 0;   // valid tokens of this lane's 8 (may be <= 0)
     float lg[8];
     float kn[8], rn[8];
     if constexpr (MK > 0) {
-      // Norms pre-multiplied by the logit scale (key norm) or scale * kappa (residual norm).
-      const float nsc = cur.nrm[0] * (col < 8 ? kscale : kscale_r);
-      row_bcast8<0>(nsc, kn);
-      row_bcast8<8>(nsc, rn);
+      // Key norm (lanes col < 8) and residual norm of token 8 q + col % 8.
+      row_bcast8<0>(nrm[0], kn);
+      row_bcast8<8>(nrm[0], rn);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float smv = sm_[e >> 2][e & 3];
-      float l;
+      float t;
       if constexpr (MK > 0) {
-        l = fmaf(kn[e], smv, rn[e] * sq_[e >> 2][e & 3]);
+        t = fmaf(kn[e], smv, rn[e] * sq_[e >> 2][e & 3]);
       } else {
-        l = kscale * smv;
+        t = smv;
       }
+      const float l = t + dpp_f<0x128>(t);   // high part + remainder part (row rotate by 8)
       lg[e] = (full || e < rem) ? l : -INFINITY;
     }
     if constexpr (SCORE) {
-      if (head_ok) {
+      if (head_ok && !lo_half) {
         float* out = a.logits + ((int64_t(layer) * a.batch + b) * a.Hq + h) * a.max_len;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (tb + e < t_hi) out[tb + e] = lg[e];
+          if (e < rem) out[tb + e] = lg[e];
       }
     } else {
       // ---- online softmax (per head; max across the 4 k-groups)
@@ -1138,12 +1139,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       float vl = 1.f;
       float sig_new = sig;
       if constexpr (BV > 0) {
-        vl = (full || (col & 7) < rem) ? cur.nrm[1] : 0.f;   // this lane's token 8 q + col % 8
+        vl = (full || (col & 7) < rem) ? nrm[1] : 0.f;   // this lane's token 8 q + col % 8
         sig_new = fmaxf(fmaxf(sig, wave_max(vl)), 1e-30f);
       }
       // Rescale only when a running maximum moved (rare after the first
       // chunks); the branch is uniform over the wave.
-      const bool grow = cmax > m_run;
+      const bool grow = cmax > m_run;   // NaN logits do not move the maximum
       if (__builtin_amdgcn_ballot_w64(grow) != 0 || sig_new != sig) {
         const float m_new = grow ? cmax : m_run;
         const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -1170,77 +1171,143 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int e = 0; e < 8; ++e) vn[e] = 1.f;
       }
-      // P'' = p * ||v|| / sig as fp16 hi + lo (B operand: lane (g, q), tokens 8 q + e)
-      half8 ph, pl;
+      // P'' = p * ||v|| / sig in fp16: high part in columns 0..7, remainder in
+      // columns 8..15 (B operand: lane (col, q), tokens 8 q + e).
+      half8 pp;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float pv = p[e] * vn[e];
         const _Float16 hh = _Float16(pv);
-        ph[e] = hh;
-        pl[e] = _Float16(pv - float(hh));
+        pp[e] = lo_half ? _Float16(pv - float(hh)) : hh;
       }
       // ---- values: A operand lane (i = col, q) = coordinate 16 vb + i, tokens 8 q .. 8 q + 7
 #pragma unroll
       for (int vb = 0; vb < 8; ++vb) {
         half8 vd;
         if constexpr (BV > 0) {
-          uint32_t bits = cur.vw[vb];
+          uint32_t bits = vw[vb];
           if constexpr (BV == 2) bits = (bits >> (16 * (q & 1))) & 0xFFFFu;
           else if constexpr (BV == 1) bits = (bits >> (8 * q)) & 0xFFu;
           vd = deq8<BV>(bits, lut_v);
         } else {
           vd = late.vf[vb];
-          if (c0 + kChunk > t_hi) {
+          if (!full) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              if (tb + e >= t_hi) vd[e] = _Float16(0.f);
+              if (e >= rem) vd[e] = _Float16(0.f);
           }
         }
-        acc[vb] = mfma16x16x32(vd, ph, acc[vb]);
-        acc[vb] = mfma16x16x32(vd, pl, acc[vb]);
+        acc[vb] = mfma16x16x32(vd, pp, acc[vb]);
       }
     }
   };
 
   const int64_t n_chunks = t_hi > t_lo ? (t_hi - t_lo + kChunk - 1) / kChunk : 0;
   if constexpr (kPrefetch) {
-    // The loads of chunk i+1 are issued before chunk i is processed; all of a
-    // chunk's global data is in its buffer, so processing never waits on the
-    // newer loads (the wait lands on the copy at the end of the iteration).
-    Chunk cur, nxt;
-    if (wave < n_chunks) load_chunk(t_lo + int64_t(wave) * kChunk, cur);
+    // Software pipeline over the wave's chunks (chunk i = wave + 4 i): while
+    // chunk i is attended, chunk i+1 is scored and the key data of chunk i+2
+    // and the value data of chunk i+1 are loaded.  The loop is unrolled twice
+    // so the two register sets swap roles without copies.  Indices past the
+    // wave's last chunk are clamped to it (in-bounds loads, masked results).
+    struct KData {
+      uint32_t kw[2][MKW];
+      uint32_t sg[2];
+    };
+    struct VData {
+      uint32_t vw[8];
+      float nrm[2];
+    };
+    auto load_k = [&](int64_t c0, KData& K) {
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        const int64_t tk = slot_base + c0 + 8 * (col >> 2) + 4 * T + (col & 3);
+        const uint32_t* kp = reinterpret_cast<const uint32_t*>(a.k_idx + tk * KREC) + q * MK;
+        if constexpr (MK == 4) {
+          const u32x4 v4 = *reinterpret_cast<const u32x4*>(kp);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) K.kw[T][u] = v4[u];
+        } else if constexpr (MK == 2) {
+          const u32x2 v2 = *reinterpret_cast<const u32x2*>(kp);
+          K.kw[T][0] = v2[0];
+          K.kw[T][1] = v2[1];
+        } else {
+#pragma unroll
+          for (int u = 0; u < MK; ++u) K.kw[T][u] = kp[u];
+        }
+        K.sg[T] = reinterpret_cast<const uint32_t*>(a.k_sign + tk * 16)[q];
+      }
+    };
+    auto load_v = [&](int64_t c0, VData& V) {
+      const int64_t tn = slot_base + c0 + 8 * q + (col & 7);
+      V.nrm[0] = col < 8 ? a.k_norm[tn] : a.k_rnorm[tn];
+      V.nrm[1] = a.v_norm[tn];
+      const int64_t blk = (start + c0) / kVBlock;   // chunks are block aligned
+#pragma unroll
+      for (int vb = 0; vb < 8; ++vb) {
+        const uint32_t* grp = reinterpret_cast<const uint32_t*>(
+            a.v_idx + ((vplane + blk) * D + 16 * vb + col) * (4 * BV));
+        V.vw[vb] = grp[BV == 4 ? q : (BV == 2 ? (q >> 1) : 0)];
+      }
+    };
+    const int64_t nw = n_chunks > wave ? (n_chunks - wave + kWaves - 1) / kWaves : 0;
+    auto cidx = [&](int64_t i) { return t_lo + (wave + kWaves * (i < nw ? i : nw - 1)) * kChunk; };
+    if (nw > 0) {
+      const ChunkLate late{};
+      KData K0, K1;
+      VData V0, V1;
+      floatx4 m0[2], s0[2], m1[2], s1[2];
+      load_k(cidx(0), K0);
+      load_k(cidx(1), K1);
+      load_v(cidx(0), V0);
+      score(K0.kw, K0.sg, late, m0, s0);
 #pragma unroll 1
-    for (int64_t ci = wave; ci < n_chunks; ci += kWaves) {
-      if (ci + kWaves < n_chunks) load_chunk(t_lo + (ci + kWaves) * kChunk, nxt);
-      process(t_lo + ci * kChunk, cur);
-      cur = nxt;
+      for (int64_t i = 0; i < nw; i += 2) {
+        load_k(cidx(i + 2), K0);
+        load_v(cidx(i + 1), V1);
+        score(K1.kw, K1.sg, late, m1, s1);
+        attend(cidx(i), true, V0.nrm, V0.vw, late, m0, s0);
+        load_k(cidx(i + 3), K1);
+        load_v(cidx(i + 2), V0);
+        score(K0.kw, K0.sg, late, m0, s0);
+        attend(cidx(i + 1), i + 1 < nw, V1.nrm, V1.vw, late, m1, s1);
+      }
     }
   } else {
 #pragma unroll 1
     for (int64_t ci = wave; ci < n_chunks; ci += kWaves) {
+      const int64_t c0 = t_lo + ci * kChunk;
       Chunk cur;
-      load_chunk(t_lo + ci * kChunk, cur);
-      process(t_lo + ci * kChunk, cur);
+      load_chunk(c0, cur);
+      ChunkLate late;
+      if constexpr (MK == 0 || BV == 0) load_late(c0, late);
+      floatx4 sm_[2], sq_[2];
+      score(cur.kw, cur.sg, late, sm_, sq_);
+      attend(c0, true, cur.nrm, cur.vw, late, sm_, sq_);
     }
   }
 
   if constexpr (!SCORE) {
-    // ---- merge the 4 waves and write this split's partial
+    // ---- merge the 4 waves and write this split's partial.  First add the
+    // remainder columns of the value accumulators to the high-part columns.
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[vb][r] += dpp_f<0x128>(acc[vb][r]);
     float l_tot = l_run + shfl_xor(l_run, 16);
     l_tot += shfl_xor(l_tot, 32);
-    if (q == 0) {
+    if (q == 0 && !lo_half) {
       mw[wave][col] = m_run;
       lw[wave][col] = l_tot;
     }
     __syncthreads();
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w][col]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w][col & 7]);
     const float f = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M) * sig;
     // Waves add their accumulators in wave order (each element belongs to one
     // lane of each wave), so the result is the same on every run.
     for (int w = 0; w < kWaves; ++w) {
-      if (wave == w) {
+      if (wave == w && !lo_half) {
 #pragma unroll
         for (int vb = 0; vb < 8; ++vb)
 #pragma unroll
