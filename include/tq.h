@@ -78,7 +78,10 @@ typedef struct tq_format {
  * Pi (y = Pi x), the QJL sketch S and their product M = S Pi^T, as written by
  * tq_make_rotations.  Codebooks are shared by all layers: 2^m ascending
  * centroids and 2^m - 1 boundaries for the key (m = k_bits-1) and value
- * (m = v_bits) quantisers, as written by tq_make_codebook (rounded to fp32). */
+ * (m = v_bits) quantisers, as written by tq_make_codebook (rounded to fp32).
+ * The kernels apply the centroids (reconstruction values) at their stored
+ * precision, fp16 (each rounded to nearest); the boundaries are compared in
+ * fp32. */
 typedef struct tq_tables {
   const float* pi;
   const float* s;

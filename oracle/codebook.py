@@ -24,6 +24,13 @@ Readings:
     unique because f_d is log-concave for d >= 3).  The final centroids are
     projected onto exact antisymmetry, c_k = -c_{n-1-k}, which only removes
     rounding noise and makes the middle boundary exactly 0 for every even n.
+  * Storage precision (the pages store the codebook but do not say at what
+    precision): the reconstruction values are stored in fp16, the precision
+    the attention kernels consume, and dequantisation and the key residual use
+    these stored values; the decision boundaries stay the midpoints of the
+    exact solution (compared in fp32).  Rounding moves each centroid by at
+    most 2^-11 of its value; the coordinate MSE changes by far less than the
+    gap between bit widths (pinned in the tests).
 """
 import math
 
@@ -89,9 +96,22 @@ _CACHE = {}
 
 
 def codebook(d: int, bits: int):
-    """Cached (centroids, boundaries) for (d, bits)."""
+    """Cached exact (centroids, boundaries) for (d, bits)."""
     key = (d, bits)
     if key not in _CACHE:
         c, t, _ = lloyd_max(d, bits)
         _CACHE[key] = (c, t)
     return _CACHE[key]
+
+
+def stored_centroids(c) -> np.ndarray:
+    """Reconstruction values as stored: rounded to fp16 (nearest, ties to
+    even), returned as float64."""
+    return np.asarray(c, np.float64).astype(np.float16).astype(np.float64)
+
+
+def stored_codebook(d: int, bits: int):
+    """(stored centroids, exact boundaries): the codebook that compression and
+    dequantisation apply."""
+    c, t = codebook(d, bits)
+    return stored_centroids(c), t

@@ -52,8 +52,8 @@ def slots_of(w: wl.Workload):
 
 def oracle_tables(fmt: quant.Format, layer: int):
     pi, s = rotation.layer_rotations(D, layer)
-    cbk = codebook.codebook(D, fmt.k_mse_bits) if fmt.k_bits else None
-    cbv = codebook.codebook(D, fmt.v_bits) if fmt.v_bits else None
+    cbk = codebook.stored_codebook(D, fmt.k_mse_bits) if fmt.k_bits else None
+    cbv = codebook.stored_codebook(D, fmt.v_bits) if fmt.v_bits else None
     return pi, s, cbk, cbv
 
 

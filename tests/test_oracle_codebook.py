@@ -98,3 +98,31 @@ def test_distortion_falls_with_bits():
     assert all(a > b for a, b in zip(mses, mses[1:]))
     # Each extra bit buys close to the high-resolution 6 dB (x4) at 3-4 bits.
     assert 3.0 < mses[2] / mses[3] < 4.2
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_stored_centroids_are_fp16_and_cost_almost_nothing(bits):
+    """The stored reconstruction values are the fp16 roundings of the exact
+    centroids: representable in fp16, still antisymmetric, within half an fp16
+    ulp of the exact values, and their distortion (independent quadrature,
+    exact boundaries) exceeds the optimum by less than 1e-5 of it."""
+    d = 128
+    c, t = codebook.codebook(d, bits)
+    cs, ts = codebook.stored_codebook(d, bits)
+    assert np.array_equal(ts, t)
+    assert np.array_equal(cs.astype(np.float16).astype(np.float64), cs)
+    assert np.array_equal(cs, -cs[::-1])
+    ulp = np.spacing(np.abs(c).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(cs - c) <= 0.5 * ulp)
+
+    def distortion(cc):
+        edges = np.concatenate(([-1.0], t, [1.0]))
+        tot = 0.0
+        for k in range(len(cc)):
+            v, _ = integrate.quad(lambda x: (x - cc[k]) ** 2 * beta_density(x, d), edges[k], edges[k + 1],
+                                  epsabs=1e-16, epsrel=1e-12, limit=200)
+            tot += v
+        return tot
+
+    base, stored = distortion(c), distortion(cs)
+    assert base <= stored < base * (1 + 1e-5)
