@@ -270,9 +270,10 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   }
   if (tid < 16) {
     const int nk = MK > 0 ? (1 << MK) : 0, nv = BV > 0 ? (1 << BV) : 0;
-    sm.kc[tid] = tid < nk ? a.kc[tid] : 0.f;
+    // Reconstruction values are applied at their stored (fp16) precision.
+    sm.kc[tid] = tid < nk ? float(_Float16(a.kc[tid])) : 0.f;
     sm.kb[tid] = tid + 1 < nk ? a.kb[tid] : INFINITY;
-    sm.vc[tid] = tid < nv ? a.vc[tid] : 0.f;
+    sm.vc[tid] = tid < nv ? float(_Float16(a.vc[tid])) : 0.f;
     sm.vb[tid] = tid + 1 < nv ? a.vb[tid] : INFINITY;
   }
   __syncthreads();
@@ -540,9 +541,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const int nk = MK > 0 ? (1 << MK) : 0, nv = BV > 0 ? (1 << BV) : 0;
     const int j = lane;
     if (j < 16) {
-      if (wave == 0 && j < nk) cbv = a.kc[j];
+      if (wave == 0 && j < nk) cbv = float(_Float16(a.kc[j]));   // stored (fp16) reconstruction value
       if (wave == 1) cbv = j + 1 < nk ? a.kb[j] : INFINITY;
-      if (wave == 2 && j < nv) cbv = a.vc[j];
+      if (wave == 2 && j < nv) cbv = float(_Float16(a.vc[j]));
       if (wave == 3) cbv = j + 1 < nv ? a.vb[j] : INFINITY;
     }
   }
@@ -796,69 +797,48 @@ __device__ __forceinline__ half8 deq8(uint32_t bits, const uint32_t* lut) {
 }
 
 // Key tables.  A key code group of NC codes (NC m = 12 bits for m = 3, 8
-// bits otherwise) indexes one entry in each of two tables: the fp16 roundings
-// c_hi of its NC centroids, and the fp16 roundings of the remainders c - c_hi
-// (together about 22 significant bits).  Each lookup lands straight in an MFMA
-// operand (8 consecutive coordinates = 8 / NC entries), with no repacking.
-// The NC-code tables are assembled from two-code pair tables.
+// bits otherwise) indexes one table entry holding its NC centroids in fp16
+// (the stored precision of the reconstruction values, so the lookup is exact).
+// Each lookup lands straight in an MFMA operand (8 consecutive coordinates =
+// 8 / NC entries), with no repacking.  The NC-code table is assembled from a
+// two-code pair table.
 template <int M> struct KLut {
   static constexpr int NC = M == 1 ? 8 : (M == 4 ? 2 : 4);  // codes per entry
-  static constexpr int E = 1 << (NC * M);                   // entries per table
+  static constexpr int E = 1 << (NC * M);                   // entries
   static constexpr int EW = NC / 2;                         // dwords per entry
   static constexpr int PAIRS = 1 << (2 * M);                // two-code pair entries
 };
 
-// Pair tables: entry x (two codes, x = c0 | c1 << M) = fp16 pair (c0, c1).
+// Pair table: entry x (two codes, x = c0 | c1 << M) = fp16 pair (c0, c1).
 template <int M>
-__device__ __forceinline__ void build_kpairs(uint32_t* phi, uint32_t* plo, const float* cent, int tid) {
-  for (int x = tid; x < KLut<M>::PAIRS; x += 256) {
-    const float c0 = cent[x & ((1 << M) - 1)], c1 = cent[x >> M];
-    const float r0 = c0 - float(_Float16(c0)), r1 = c1 - float(_Float16(c1));
-    phi[x] = uint32_t(f16_bits(c0)) | (uint32_t(f16_bits(c1)) << 16);
-    plo[x] = uint32_t(f16_bits(r0)) | (uint32_t(f16_bits(r1)) << 16);
-  }
+__device__ __forceinline__ void build_kpairs(uint32_t* phi, const float* cent, int tid) {
+  for (int x = tid; x < KLut<M>::PAIRS; x += 256)
+    phi[x] = uint32_t(f16_bits(cent[x & ((1 << M) - 1)])) | (uint32_t(f16_bits(cent[x >> M])) << 16);
 }
-// NC-code tables from the pair tables (after a barrier): dword k of entry x is
+// NC-code table from the pair table (after a barrier): dword k of entry x is
 // the pair of codes 2k, 2k + 1.
 template <int M>
-__device__ __forceinline__ void build_ktab(uint32_t* khi, uint32_t* klo, const uint32_t* phi, const uint32_t* plo,
-                                           int tid) {
+__device__ __forceinline__ void build_ktab(uint32_t* khi, const uint32_t* phi, int tid) {
   using K = KLut<M>;
-  if constexpr (K::NC == 2) return;  // the pair tables are the tables
+  if constexpr (K::NC == 2) return;  // the pair table is the table
   for (int x = tid; x < K::E; x += 256) {
 #pragma unroll
-    for (int k = 0; k < K::EW; ++k) {
-      const int pr = (x >> (2 * M * k)) & (K::PAIRS - 1);
-      khi[x * K::EW + k] = phi[pr];
-      klo[x * K::EW + k] = plo[pr];
-    }
+    for (int k = 0; k < K::EW; ++k) khi[x * K::EW + k] = phi[(x >> (2 * M * k)) & (K::PAIRS - 1)];
   }
 }
 
-// 8 consecutive m-bit key codes (LSB-first in `bits`) -> fp16 hi and lo halves.
+// 8 consecutive m-bit key codes (LSB-first in `bits`) -> 8 fp16 centroids.
 template <int M>
-__device__ __forceinline__ void deq8_k(uint32_t bits, const uint32_t* khi, const uint32_t* klo, half8& hi, half8& lo) {
+__device__ __forceinline__ half8 deq8_k(uint32_t bits, const uint32_t* khi) {
   if constexpr (M == 1) {
-    hi = as_half8(*reinterpret_cast<const u32x4*>(khi + (bits & 0xFFu) * 4));
-    lo = as_half8(*reinterpret_cast<const u32x4*>(klo + (bits & 0xFFu) * 4));
+    return as_half8(*reinterpret_cast<const u32x4*>(khi + (bits & 0xFFu) * 4));
   } else if constexpr (M == 4) {
-    const uint32_t i0 = bits & 0xFFu, i1 = (bits >> 8) & 0xFFu, i2 = (bits >> 16) & 0xFFu, i3 = bits >> 24;
-    hi = as_half8(u32x4{khi[i0], khi[i1], khi[i2], khi[i3]});
-    lo = as_half8(u32x4{klo[i0], klo[i1], klo[i2], klo[i3]});
+    return as_half8(u32x4{khi[bits & 0xFFu], khi[(bits >> 8) & 0xFFu], khi[(bits >> 16) & 0xFFu], khi[bits >> 24]});
   } else {
     constexpr uint32_t mask = M == 3 ? 0xFFFu : 0xFFu;
-    // Byte offsets of the two entries.  The low-half reads take opaque copies
-    // of the offsets so that they are not fused with the high-half reads into
-    // one wider read (which would interleave the halves in registers).
-    const uint32_t a0 = (bits & mask) * 8, a1 = ((bits >> (4 * M)) & mask) * 8;
-    uint32_t b0 = a0, b1 = a1;
-    asm volatile("" : "+v"(b0), "+v"(b1));
-    const char* ph = reinterpret_cast<const char*>(khi);
-    const char* pl = reinterpret_cast<const char*>(klo);
-    const u32x2 h0 = *reinterpret_cast<const u32x2*>(ph + a0), h1 = *reinterpret_cast<const u32x2*>(ph + a1);
-    const u32x2 l0 = *reinterpret_cast<const u32x2*>(pl + b0), l1 = *reinterpret_cast<const u32x2*>(pl + b1);
-    hi = as_half8(u32x4{h0[0], h0[1], h1[0], h1[1]});
-    lo = as_half8(u32x4{l0[0], l0[1], l1[0], l1[1]});
+    const u32x2 h0 = *reinterpret_cast<const u32x2*>(khi + (bits & mask) * 2);
+    const u32x2 h1 = *reinterpret_cast<const u32x2*>(khi + ((bits >> (4 * M)) & mask) * 2);
+    return as_half8(u32x4{h0[0], h0[1], h1[0], h1[1]});
   }
 }
 
@@ -879,30 +859,26 @@ __device__ __forceinline__ uint32_t slab_bits(const uint32_t (&w)[N], int s) {
 template <int MK, int BV, bool SCORE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
   using KL = KLut<(MK > 0 ? MK : 1)>;
-  constexpr int KT = MK > 0 ? KL::E * KL::EW : 1;                        // dwords per key table
+  constexpr int KT = MK > 0 ? KL::E * KL::EW : 1;                        // dwords of the key table
   constexpr int KP = MK > 0 && KL::NC > 2 ? KL::PAIRS : 1;                // pair-table dwords (if separate)
   constexpr int VW = BV > 0 ? Lut<BV, false>::WORDS : 1;
   // One LDS block with fixed offsets, the tables read in the token loop
   // first so that every one of them is addressed with an immediate offset
-  // (below 64 KB): value table, sign table, key high and low tables.
+  // (below 64 KB): value table, sign table, key table.
   constexpr int OFF_V = 0;
   constexpr int OFF_S = OFF_V + ((VW * 4 + 15) / 16) * 16;
   constexpr int OFF_KHI = OFF_S + 256 * 16;
-  constexpr int OFF_KLO = OFF_KHI + KT * 4;
-  constexpr int OFF_PHI = OFF_KLO + KT * 4;
-  constexpr int OFF_PLO = OFF_PHI + KP * 4;
-  constexpr int OFF_MW = OFF_PLO + KP * 4;
+  constexpr int OFF_PHI = OFF_KHI + KT * 4;
+  constexpr int OFF_MW = OFF_PHI + KP * 4;
   constexpr int OFF_LW = OFF_MW + kWaves * 16 * 4;
   constexpr int OFF_ACC = OFF_LW + kWaves * 16 * 4;
   constexpr int LDS_BYTES = OFF_ACC + 16 * D * 4;
-  static_assert(OFF_KLO < 65536, "table offsets must fit the LDS immediate");
+  static_assert(OFF_KHI < 65536, "table offsets must fit the LDS immediate");
   __shared__ __align__(16) unsigned char dsm[LDS_BYTES];
   uint32_t* const lut_v = reinterpret_cast<uint32_t*>(dsm + OFF_V);
   uint32_t* const lut_s = reinterpret_cast<uint32_t*>(dsm + OFF_S);
   uint32_t* const lut_khi = reinterpret_cast<uint32_t*>(dsm + OFF_KHI);
-  uint32_t* const lut_klo = reinterpret_cast<uint32_t*>(dsm + OFF_KLO);
   uint32_t* const pair_hi = reinterpret_cast<uint32_t*>(dsm + OFF_PHI);
-  uint32_t* const pair_lo = reinterpret_cast<uint32_t*>(dsm + OFF_PLO);
   float(*const mw)[16] = reinterpret_cast<float(*)[16]>(dsm + OFF_MW);
   float(*const lw)[16] = reinterpret_cast<float(*)[16]>(dsm + OFF_LW);
   float(*const accsum)[D] = reinterpret_cast<float(*)[D]>(dsm + OFF_ACC);
@@ -925,9 +901,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Tables.
   if constexpr (MK > 0) {
     if constexpr (KL::NC > 2)
-      build_kpairs<MK>(pair_hi, pair_lo, a.kc, tid);
+      build_kpairs<MK>(pair_hi, a.kc, tid);
     else
-      build_kpairs<MK>(lut_khi, lut_klo, a.kc, tid);
+      build_kpairs<MK>(lut_khi, a.kc, tid);
   }
   if constexpr (BV > 0) build_lut<BV, false>(lut_v, a.vc, tid);
   if constexpr (MK > 0) {
@@ -942,7 +918,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   __syncthreads();
   if constexpr (MK > 0 && KL::NC > 2) {
-    build_ktab<MK>(lut_khi, lut_klo, pair_hi, pair_lo, tid);
+    build_ktab<MK>(lut_khi, pair_hi, tid);
     __syncthreads();
   }
 
@@ -1079,10 +1055,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if constexpr (MK > 0) {
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-          half8 kh, kl;
-          deq8_k<MK>(slab_bits<MK>(kw[T], s2), lut_khi, lut_klo, kh, kl);
+          const half8 kh = deq8_k<MK>(slab_bits<MK>(kw[T], s2), lut_khi);
           sm_[T] = mfma16x16x32(kh, qr[s2], sm_[T]);
-          sm_[T] = mfma16x16x32(kl, qr[s2], sm_[T]);
           const half8 sd = *reinterpret_cast<const half8*>(lut_s + ((sg[T] >> (8 * s2)) & 0xFFu) * 4);
           sq_[T] = mfma16x16x32(sd, qs[s2], sq_[T]);
         }
