@@ -53,7 +53,9 @@ __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v,
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  // bound_ctrl set and every lane a valid source: the move can fold into the
+  // arithmetic that consumes it (a DPP operand).
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 // Sum over the 64 lanes, in a fixed order, returned to every lane: DPP within
 // each 16-lane row (quad swaps, then the half-row and row mirrors), then the
@@ -730,7 +732,7 @@ struct DecodeArgs {
 // DPP row broadcast: every lane of a 16-lane row reads lane E of its row.
 template <int E>
 __device__ __forceinline__ float row_bcast(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + E, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + E, 0xF, 0xF, true));
 }
 template <int B>
 __device__ __forceinline__ void row_bcast8(float v, float (&o)[8]) {
@@ -869,7 +871,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int OFF_S = OFF_V + ((VW * 4 + 15) / 16) * 16;
   constexpr int OFF_KHI = OFF_S + 256 * 16;
   constexpr int OFF_PHI = OFF_KHI + KT * 4;
-  constexpr int OFF_MW = OFF_PHI + KP * 4;
+  constexpr int OFF_NX = OFF_PHI + KP * 4;   // per-wave norm exchange, 128 floats each
+  constexpr int OFF_MW = OFF_NX + kWaves * 128 * 4;
   constexpr int OFF_LW = OFF_MW + kWaves * 16 * 4;
   constexpr int OFF_ACC = OFF_LW + kWaves * 16 * 4;
   constexpr int LDS_BYTES = OFF_ACC + 16 * D * 4;
@@ -879,6 +882,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   uint32_t* const lut_s = reinterpret_cast<uint32_t*>(dsm + OFF_S);
   uint32_t* const lut_khi = reinterpret_cast<uint32_t*>(dsm + OFF_KHI);
   uint32_t* const pair_hi = reinterpret_cast<uint32_t*>(dsm + OFF_PHI);
+  float* const nxch = reinterpret_cast<float*>(dsm + OFF_NX);
   float(*const mw)[16] = reinterpret_cast<float(*)[16]>(dsm + OFF_MW);
   float(*const lw)[16] = reinterpret_cast<float(*)[16]>(dsm + OFF_LW);
   float(*const accsum)[D] = reinterpret_cast<float(*)[D]>(dsm + OFF_ACC);
@@ -1071,17 +1075,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // `valid` false every token of the chunk is masked (a pipeline slot past the
   // wave's last chunk).  The code is branch-free (the rescale is applied every
   // chunk) so that the compiler can interleave it with the next chunk's scores.
-  auto attend = [&](int64_t c0, bool valid, const float (&nrm)[2], const uint32_t (&vw)[8], const ChunkLate& late,
+  // crel: first token of the chunk relative to the split start t_lo.
+  const int span = int(t_hi - t_lo);   // tokens of this split (may be <= 0)
+  auto attend = [&](int crel, bool valid, const float (&nrm)[2], const uint32_t (&vw)[8], const ChunkLate& late,
                     const floatx4 (&sm_)[2], const floatx4 (&sq_)[2]) {
-    const int64_t tb = c0 + 8 * q;
-    const bool full = valid && c0 + kChunk <= t_hi;
-    const int64_t rem = valid ? t_hi - tb : 0;   // valid tokens of this lane's 8 (may be <= 0)
+    const bool full = valid && crel + kChunk <= span;                // uniform over the wave
+    const int rem = valid ? span - (crel + 8 * q) : 0;              // valid tokens of this lane's 8 (may be <= 0)
     float lg[8];
-    float kn[8], rn[8];
-    if constexpr (MK > 0) {
-      // Key norm (lanes col < 8) and residual norm of token 8 q + col % 8.
-      row_bcast8<0>(nrm[0], kn);
-      row_bcast8<8>(nrm[0], rn);
+    float kn[8], rn[8], vn[8];
+    // Value norms are normalised by sig, the running maximum of ||v|| over
+    // the wave's tokens (uniform over the wave), so P'' below stays <= 1.
+    float sig_new = sig, inv_new = inv_sig;
+    float vl = 0.f;
+    if constexpr (BV > 0 && !SCORE) {
+      vl = nrm[1];   // this lane's token 8 q + col % 8
+      if (!full) vl = (col & 7) < rem ? vl : 0.f;
+      sig_new = fmaxf(fmaxf(sig, wave_max(vl)), 1e-30f);
+      inv_new = sig_new == sig ? inv_sig : __builtin_amdgcn_rcpf(sig_new);
+    }
+    {
+      // Lane (col, q) holds the key norm (col < 8) or the residual norm
+      // (col >= 8) and the value norm of token 8 q + col % 8.  The 16 lanes of
+      // a row need all 8 tokens' norms: exchange them through this wave's LDS
+      // slot (in-order within the wave, so no barrier).
+      float* nx = nxch + wave * 128;
+      nx[lane] = nrm[0];
+      if constexpr (BV > 0 && !SCORE) nx[64 + lane] = vl * inv_new;
+      const float4* n4 = reinterpret_cast<const float4*>(nx + 16 * q);
+      if constexpr (MK > 0) {
+        const float4 a0 = n4[0], a1 = n4[1], b0 = n4[2], b1 = n4[3];
+        kn[0] = a0.x; kn[1] = a0.y; kn[2] = a0.z; kn[3] = a0.w; kn[4] = a1.x; kn[5] = a1.y; kn[6] = a1.z; kn[7] = a1.w;
+        rn[0] = b0.x; rn[1] = b0.y; rn[2] = b0.z; rn[3] = b0.w; rn[4] = b1.x; rn[5] = b1.y; rn[6] = b1.z; rn[7] = b1.w;
+      }
+      if constexpr (BV > 0 && !SCORE) {
+        const float4 c0 = n4[16], c1 = n4[17];
+        vn[0] = c0.x; vn[1] = c0.y; vn[2] = c0.z; vn[3] = c0.w; vn[4] = c1.x; vn[5] = c1.y; vn[6] = c1.z; vn[7] = c1.w;
+      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -1092,15 +1121,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       } else {
         t = smv;
       }
-      const float l = t + dpp_f<0x128>(t);   // high part + remainder part (row rotate by 8)
-      lg[e] = (full || e < rem) ? l : -INFINITY;
+      lg[e] = t + dpp_f<0x128>(t);   // high part + remainder part (row rotate by 8)
+    }
+    if (!full) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lg[e] = e < rem ? lg[e] : -INFINITY;
     }
     if constexpr (SCORE) {
       if (head_ok && !lo_half) {
-        float* out = a.logits + ((int64_t(layer) * a.batch + b) * a.Hq + h) * a.max_len;
+        float* out = a.logits + ((int64_t(layer) * a.batch + b) * a.Hq + h) * a.max_len + t_lo + crel + 8 * q;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (e < rem) out[tb + e] = lg[e];
+          if (e < rem) out[e] = lg[e];
       }
     } else {
       // ---- online softmax (per head; max across the 4 k-groups)
@@ -1108,27 +1140,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                          fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));
       cmax = fmaxf(cmax, shfl_xor(cmax, 16));
       cmax = fmaxf(cmax, shfl_xor(cmax, 32));
-      // Value norms are normalised by sig, the running maximum of ||v|| over
-      // the wave's tokens (uniform over the wave), so P'' below stays <= 1.
-      float vl = 1.f;
-      float sig_new = sig;
-      if constexpr (BV > 0) {
-        vl = (full || (col & 7) < rem) ? nrm[1] : 0.f;   // this lane's token 8 q + col % 8
-        sig_new = fmaxf(fmaxf(sig, wave_max(vl)), 1e-30f);
-      }
       // Rescale only when a running maximum moved (rare after the first
       // chunks); the branch is uniform over the wave.
       const bool grow = cmax > m_run;   // NaN logits do not move the maximum
       if (__builtin_amdgcn_ballot_w64(grow) != 0 || sig_new != sig) {
         const float m_new = grow ? cmax : m_run;
         const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        const float factor = alpha * (sig / sig_new);
+        const float factor = alpha * sig * inv_new;
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] *= factor;
         l_run *= alpha;
         m_run = m_new;
         sig = sig_new;
-        inv_sig = 1.0f / sig;
+        inv_sig = inv_new;
       }
       float p[8];
       float psum = 0.f;
@@ -1138,10 +1162,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         psum += p[e];
       }
       l_run += psum;
-      float vn[8];
-      if constexpr (BV > 0) {
-        row_bcast8<0>(vl * inv_sig, vn);
-      } else {
+      if constexpr (BV == 0) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) vn[e] = 1.f;
       }
@@ -1165,7 +1186,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           vd = deq8<BV>(bits, lut_v);
         } else {
           vd = late.vf[vb];
-          if (!full) {
+          if (!full) {   // fp16 values past the end may hold anything
 #pragma unroll
             for (int e = 0; e < 8; ++e)
               if (e >= rem) vd[e] = _Float16(0.f);
@@ -1191,59 +1212,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       uint32_t vw[8];
       float nrm[2];
     };
-    auto load_k = [&](int64_t c0, KData& K) {
+    // Per-wave uniform base addresses of the wave's first chunk (chunk i of
+    // the wave lies kWaves * kChunk slots further) and 32-bit per-lane byte
+    // offsets, so that every load is one scalar base plus a lane offset.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int64_t slot0w = slot_base + t_lo + int64_t(wv) * kChunk;
+    const uint8_t* const kbase = a.k_idx + slot0w * KREC;
+    const uint8_t* const sbase = a.k_sign + slot0w * 16;
+    const uint8_t* const nkbase = reinterpret_cast<const uint8_t*>(a.k_norm + slot0w);
+    const uint8_t* const nrbase = reinterpret_cast<const uint8_t*>(a.k_rnorm + slot0w);
+    const uint8_t* const nvbase = reinterpret_cast<const uint8_t*>(a.v_norm + slot0w);
+    const uint8_t* const vbase = a.v_idx + (vplane + (start + t_lo) / kVBlock + wv) * D * (4 * BV);
+    constexpr int64_t kStep = int64_t(kWaves) * kChunk;   // slots between two chunks of a wave
+    uint32_t koff[2], soff[2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const uint32_t tk = 8 * (col >> 2) + 4 * T + (col & 3);
+      koff[T] = tk * KREC + 4 * q * MK;
+      soff[T] = tk * 16 + 4 * q;
+    }
+    const uint32_t noff = 4 * (8 * q + (col & 7));
+    const uint32_t voff = (16 * 0 + col) * (4 * BV) + 4 * (BV == 4 ? q : (BV == 2 ? (q >> 1) : 0));
+    const int64_t nw = n_chunks > wv ? (n_chunks - wv + kWaves - 1) / kWaves : 0;   // uniform
+    auto clampi = [&](int64_t i) { return i < nw ? i : nw - 1; };   // uniform
+    auto load_k = [&](int64_t i, KData& K) {
+      const int64_t ic = clampi(i);
+      const uint8_t* kp = kbase + ic * kStep * KREC;
+      const uint8_t* sp = sbase + ic * kStep * 16;
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
-        const int64_t tk = slot_base + c0 + 8 * (col >> 2) + 4 * T + (col & 3);
-        const uint32_t* kp = reinterpret_cast<const uint32_t*>(a.k_idx + tk * KREC) + q * MK;
         if constexpr (MK == 4) {
-          const u32x4 v4 = *reinterpret_cast<const u32x4*>(kp);
+          const u32x4 v4 = *reinterpret_cast<const u32x4*>(kp + koff[T]);
 #pragma unroll
           for (int u = 0; u < 4; ++u) K.kw[T][u] = v4[u];
         } else if constexpr (MK == 2) {
-          const u32x2 v2 = *reinterpret_cast<const u32x2*>(kp);
+          const u32x2 v2 = *reinterpret_cast<const u32x2*>(kp + koff[T]);
           K.kw[T][0] = v2[0];
           K.kw[T][1] = v2[1];
         } else {
 #pragma unroll
-          for (int u = 0; u < MK; ++u) K.kw[T][u] = kp[u];
+          for (int u = 0; u < MK; ++u) K.kw[T][u] = *reinterpret_cast<const uint32_t*>(kp + koff[T] + 4 * u);
         }
-        K.sg[T] = reinterpret_cast<const uint32_t*>(a.k_sign + tk * 16)[q];
+        K.sg[T] = *reinterpret_cast<const uint32_t*>(sp + soff[T]);
       }
     };
-    auto load_v = [&](int64_t c0, VData& V) {
-      const int64_t tn = slot_base + c0 + 8 * q + (col & 7);
-      V.nrm[0] = col < 8 ? a.k_norm[tn] : a.k_rnorm[tn];
-      V.nrm[1] = a.v_norm[tn];
-      const int64_t blk = (start + c0) / kVBlock;   // chunks are block aligned
+    auto load_v = [&](int64_t i, VData& V) {
+      const int64_t ic = clampi(i);
+      const int64_t so = ic * kStep * 4;
+      const float nk = *reinterpret_cast<const float*>(nkbase + so + noff);
+      const float nr = *reinterpret_cast<const float*>(nrbase + so + noff);
+      V.nrm[0] = col < 8 ? nk : nr;
+      V.nrm[1] = *reinterpret_cast<const float*>(nvbase + so + noff);
+      const uint8_t* vp = vbase + ic * kWaves * D * (4 * BV);   // kWaves value blocks per step
 #pragma unroll
-      for (int vb = 0; vb < 8; ++vb) {
-        const uint32_t* grp = reinterpret_cast<const uint32_t*>(
-            a.v_idx + ((vplane + blk) * D + 16 * vb + col) * (4 * BV));
-        V.vw[vb] = grp[BV == 4 ? q : (BV == 2 ? (q >> 1) : 0)];
-      }
+      for (int vb = 0; vb < 8; ++vb)
+        V.vw[vb] = *reinterpret_cast<const uint32_t*>(vp + voff + 16 * vb * (4 * BV));
     };
-    const int64_t nw = n_chunks > wave ? (n_chunks - wave + kWaves - 1) / kWaves : 0;
-    auto cidx = [&](int64_t i) { return t_lo + (wave + kWaves * (i < nw ? i : nw - 1)) * kChunk; };
+    auto crel = [&](int64_t i) { return int(wv + kWaves * clampi(i)) * kChunk; };
     if (nw > 0) {
       const ChunkLate late{};
       KData K0, K1;
       VData V0, V1;
       floatx4 m0[2], s0[2], m1[2], s1[2];
-      load_k(cidx(0), K0);
-      load_k(cidx(1), K1);
-      load_v(cidx(0), V0);
+      load_k(0, K0);
+      load_k(1, K1);
+      load_v(0, V0);
       score(K0.kw, K0.sg, late, m0, s0);
 #pragma unroll 1
       for (int64_t i = 0; i < nw; i += 2) {
-        load_k(cidx(i + 2), K0);
-        load_v(cidx(i + 1), V1);
+        load_k(i + 2, K0);
+        load_v(i + 1, V1);
         score(K1.kw, K1.sg, late, m1, s1);
-        attend(cidx(i), true, V0.nrm, V0.vw, late, m0, s0);
-        load_k(cidx(i + 3), K1);
-        load_v(cidx(i + 2), V0);
+        attend(crel(i), true, V0.nrm, V0.vw, late, m0, s0);
+        load_k(i + 3, K1);
+        load_v(i + 2, V0);
         score(K0.kw, K0.sg, late, m0, s0);
-        attend(cidx(i + 1), i + 1 < nw, V1.nrm, V1.vw, late, m1, s1);
+        attend(crel(i + 1), i + 1 < nw, V1.nrm, V1.vw, late, m1, s1);
       }
     }
   } else {
@@ -1256,7 +1300,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if constexpr (MK == 0 || BV == 0) load_late(c0, late);
       floatx4 sm_[2], sq_[2];
       score(cur.kw, cur.sg, late, sm_, sq_);
-      attend(c0, true, cur.nrm, cur.vw, late, sm_, sq_);
+      attend(int(ci) * kChunk, true, cur.nrm, cur.vw, late, sm_, sq_);
     }
   }
 
