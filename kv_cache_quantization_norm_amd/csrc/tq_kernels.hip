@@ -818,14 +818,27 @@ __device__ __forceinline__ void build_kpairs(uint32_t* phi, const float* cent, i
     phi[x] = uint32_t(f16_bits(cent[x & ((1 << M) - 1)])) | (uint32_t(f16_bits(cent[x >> M])) << 16);
 }
 // NC-code table from the pair table (after a barrier): dword k of entry x is
-// the pair of codes 2k, 2k + 1.
+// the pair of codes 2k, 2k + 1.  Thread t writes entries t + 256 u; all its
+// pair-table reads are issued before its writes.
 template <int M>
 __device__ __forceinline__ void build_ktab(uint32_t* khi, const uint32_t* phi, int tid) {
   using K = KLut<M>;
+  static_assert(K::E % 256 == 0, "key table entries per thread");
   if constexpr (K::NC == 2) return;  // the pair table is the table
-  for (int x = tid; x < K::E; x += 256) {
+  constexpr int U = K::E / 256;
+  uint32_t w[U][K::EW];
 #pragma unroll
-    for (int k = 0; k < K::EW; ++k) khi[x * K::EW + k] = phi[(x >> (2 * M * k)) & (K::PAIRS - 1)];
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int k = 0; k < K::EW; ++k) w[u][k] = phi[((tid + 256 * u) >> (2 * M * k)) & (K::PAIRS - 1)];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    uint32_t* dst = khi + (tid + 256 * u) * K::EW;
+    if constexpr (K::EW == 2) {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{w[u][0], w[u][1]};
+    } else {
+      *reinterpret_cast<u32x4*>(dst) = u32x4{w[u][0], w[u][1], w[u][2], w[u][3]};
+    }
   }
 }
 
@@ -871,11 +884,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int OFF_S = OFF_V + ((VW * 4 + 15) / 16) * 16;
   constexpr int OFF_KHI = OFF_S + 256 * 16;
   constexpr int OFF_PHI = OFF_KHI + KT * 4;
-  constexpr int OFF_NX = OFF_PHI + KP * 4;   // per-wave norm exchange, 128 floats each
+  // After the token loop the key tables are dead: the wave merge reuses
+  // their space for the scaled accumulators of every wave.
+  constexpr int RED_BYTES = kWaves * kMaxGroup * D * 4;
+  constexpr int TAB_END = OFF_PHI + KP * 4;
+  constexpr int OFF_NX = (TAB_END > OFF_KHI + RED_BYTES ? TAB_END : OFF_KHI + RED_BYTES);   // per-wave norm exchange
   constexpr int OFF_MW = OFF_NX + kWaves * 128 * 4;
   constexpr int OFF_LW = OFF_MW + kWaves * 16 * 4;
-  constexpr int OFF_ACC = OFF_LW + kWaves * 16 * 4;
-  constexpr int LDS_BYTES = OFF_ACC + 16 * D * 4;
+  constexpr int LDS_BYTES = OFF_LW + kWaves * 16 * 4;
   static_assert(OFF_KHI < 65536, "table offsets must fit the LDS immediate");
   __shared__ __align__(16) unsigned char dsm[LDS_BYTES];
   uint32_t* const lut_v = reinterpret_cast<uint32_t*>(dsm + OFF_V);
@@ -885,7 +901,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float* const nxch = reinterpret_cast<float*>(dsm + OFF_NX);
   float(*const mw)[16] = reinterpret_cast<float(*)[16]>(dsm + OFF_MW);
   float(*const lw)[16] = reinterpret_cast<float(*)[16]>(dsm + OFF_LW);
-  float(*const accsum)[D] = reinterpret_cast<float(*)[D]>(dsm + OFF_ACC);
+  float* const red = reinterpret_cast<float*>(dsm + OFF_KHI);   // [wave][head][coordinate], after the loop
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, q = lane >> 4;   // MFMA column (head / coordinate) and k-group
@@ -1317,25 +1333,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       mw[wave][col] = m_run;
       lw[wave][col] = l_tot;
     }
-    __syncthreads();
+    __syncthreads();   // every wave is past its last table lookup
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w][col & 7]);
     const float f = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M) * sig;
-    // Waves add their accumulators in wave order (each element belongs to one
-    // lane of each wave), so the result is the same on every run.
-    for (int w = 0; w < kWaves; ++w) {
-      if (wave == w && !lo_half) {
+    if (!lo_half) {
+      float* rw = red + (wave * kMaxGroup + col) * D;
 #pragma unroll
-        for (int vb = 0; vb < 8; ++vb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float& dst = accsum[col][16 * vb + 4 * q + r];
-            dst = (w == 0 ? 0.f : dst) + acc[vb][r] * f;
-          }
+      for (int vb = 0; vb < 8; ++vb) {
+        const float4 v4 = {acc[vb][0] * f, acc[vb][1] * f, acc[vb][2] * f, acc[vb][3] * f};
+        *reinterpret_cast<float4*>(rw + 16 * vb + 4 * q) = v4;
       }
-      __syncthreads();
     }
+    __syncthreads();
+    // Sum the waves in wave order (the same result on every run) and write the
+    // split's partial: (max, sum of exponentials, accumulator[D]) per head.
     const int64_t pbase = (int64_t(layer) * a.batch + b) * a.Hq;
     const int ng = a.G - hg * kMaxGroup < kMaxGroup ? a.G - hg * kMaxGroup : kMaxGroup;
     for (int e = tid; e < ng * (D + 2); e += 256) {
@@ -1352,7 +1365,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int w = 0; w < kWaves; ++w)
           if (mw[w][g] != -INFINITY) v += lw[w][g] * __builtin_amdgcn_exp2f(mw[w][g] - Mg);
       } else {
-        v = accsum[g][i - 2];
+        v = red[g * D + (i - 2)];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) v += red[(w * kMaxGroup + g) * D + (i - 2)];
       }
       a.partial[((pbase + hh) * a.n_splits + split) * (D + 2) + i] = v;
     }
