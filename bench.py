@@ -176,8 +176,8 @@ def main():
     step_bytes = records + qo + tables_bytes + new_tok
     decode_bytes = records + qo + L * 2 * D * D * 4   # Pi and S
     kernel_bytes = records + L * HQ * 2 * D * 4       # packed records + the prepared queries (Pi q, S q)
-    n_splits = ws_splits(tq, fmt, base, HQ, T)
-    split_overhead = L * HQ * n_splits * (D + 2) * 4  # fp32 partials written for the combine
+    pieces = decode_pieces(L * H * -(-(HQ // H) // 8), T)
+    split_overhead = pieces * (HQ // H) * (D + 2) * 4  # fp32 partials written for the combine
     step_gbs = step_bytes / (step_ms * 1e-3) / 1e9
     decode_gbs = decode_bytes / (decode_ms * 1e-3) / 1e9
     kern_mean = float(kern_us.mean())
@@ -234,13 +234,17 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def ws_splits(tq, fmt, cache, hq, t):
-    """Token splits of a decode call: the workspace holds the prepared queries
-    and (d + 2) fp32 per (layer, query head, split)."""
-    d = fmt.d
-    total = tq._lib.tq_decode_workspace_bytes(tq.ctypes.byref(fmt), cache.n_layers, 1, cache.n_kv_heads, hq, t)
-    qprep = cache.n_layers * hq * 2 * d * 4
-    return (total - qprep) // (cache.n_layers * hq * (d + 2) * 4)
+def decode_pieces(problems, t, chunk=32, waves=8, max_workgroups=256):
+    """Number of (problem, workgroup) pieces of a decode call, each leaving one
+    partial per query head: the chunks of all problems (one problem = layer x
+    sequence x KV head with up to 8 query heads) are dealt to the workgroups in
+    equal contiguous ranges, and a range that crosses into a problem adds one
+    piece to it."""
+    cpp = -(-max(t, 1) // chunk)
+    total = problems * cpp
+    wgs = min(max_workgroups, -(-total // waves))
+    cpw = -(-total // wgs)
+    return sum((p * cpp + cpp - 1) // cpw - (p * cpp) // cpw + 1 for p in range(problems))
 
 
 def time_per_layer(tq, fmt, tables, base, Q, seq_start, seq_len, T, stream, dev):

@@ -159,8 +159,8 @@ tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq
  * b occupies slots [seq_start[b], seq_start[b] + seq_len[b]); seq_start must
  * be a multiple of 32; the kernels clamp a sequence to the capacity and to max_seq_len and treat
  * a misaligned or negative start as empty.  An empty sequence gives a zero
- * output row.  max_seq_len (host) bounds every seq_len and sizes the token
- * split.  scale = 0 means 1/sqrt(d).  n_q_heads must be a multiple of
+ * output row.  max_seq_len (host) bounds every seq_len and sizes the work
+ * decomposition.  scale = 0 means 1/sqrt(d).  n_q_heads must be a multiple of
  * n_kv_heads.  workspace: device scratch of at least
  * tq_decode_workspace_bytes(...) bytes; enqueued on `stream`. */
 tq_status tq_decode_attention(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
@@ -172,14 +172,15 @@ tq_status tq_decode_attention(const tq_format* fmt, const tq_tables* tables, con
 /* Device.  tq_decode_attention in three stages, for callers that schedule
  * them separately (and for timing the kernels one by one).  They take the same
  * arguments as tq_decode_attention and share its workspace, which carries the
- * prepared queries and the per-split partial results from one stage to the
+ * prepared queries and the partial results from one stage to the
  * next:
  *   tq_decode_prepare  - forward-rotated and pre-sketched queries Pi q, S q
  *                        (QJL deep-dive, section 6: sketched once per query);
- *   tq_decode_partials - scores every token split of every (layer, sequence,
- *                        KV head) on the packed cache and accumulates its
- *                        softmax-weighted values (online softmax per split);
- *   tq_decode_combine  - merges the splits of each query head and applies Pi^T.
+ *   tq_decode_partials - scores every token of every (layer, sequence, KV
+ *                        head) on the packed cache and accumulates the
+ *                        softmax-weighted values (online softmax) in pieces of
+ *                        equal size, one partial result per piece and head;
+ *   tq_decode_combine  - merges the pieces of each query head and applies Pi^T.
  * Calling them in this order on one stream gives exactly tq_decode_attention's
  * result; the max_seq_len / batch / head arguments must be the same in all
  * three calls. */

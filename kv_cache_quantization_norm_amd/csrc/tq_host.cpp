@@ -44,20 +44,20 @@ SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_he
   SplitPlan p;
   const int group = n_q_heads / n_kv_heads;
   p.n_head_groups = (group + kMaxGroup - 1) / kMaxGroup;
-  const int64_t wg_tokens = int64_t(kChunk) * kWaves;  // 128
-  const int64_t problems = int64_t(n_layers) * batch * n_kv_heads * p.n_head_groups;
+  p.problems = int64_t(n_layers) * batch * n_kv_heads * p.n_head_groups;
   const int64_t len = max_seq_len > 0 ? max_seq_len : 1;
-  // One resident round of workgroups (2 per CU at 2 waves per SIMD): as many
-  // splits per problem as fit, each at least one 128-token group.
-  int64_t splits = kResidentWorkgroups / problems;
-  if (splits < 1) splits = 1;
-  int64_t units = (len + splits * wg_tokens - 1) / (splits * wg_tokens);
-  if (units < 1) units = 1;
-  p.split_tokens = units * wg_tokens;
-  p.n_splits = (len + p.split_tokens - 1) / p.split_tokens;
+  p.chunks_per_problem = (len + kChunk - 1) / kChunk;
+  const int64_t total = p.problems * p.chunks_per_problem;
+  // One workgroup per CU, each with at least one chunk per wave.
+  int64_t wgs = (total + kDecodeWaves - 1) / kDecodeWaves;
+  if (wgs > kDecodeWorkgroups) wgs = kDecodeWorkgroups;
+  p.chunks_per_wg = (total + wgs - 1) / wgs;
+  p.n_workgroups = (total + p.chunks_per_wg - 1) / p.chunks_per_wg;
+  // A problem of C chunks overlaps at most ceil((C - 1) / W) + 1 ranges of W.
+  p.seg_max = (p.chunks_per_problem - 1 + p.chunks_per_wg - 1) / p.chunks_per_wg + 1;
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   p.qprep_bytes = align(size_t(n_layers) * batch * n_q_heads * 2 * d * sizeof(float));
-  p.partial_bytes = align(size_t(n_layers) * batch * n_q_heads * p.n_splits * (d + 2) * sizeof(float));
+  p.partial_bytes = align(size_t(n_layers) * batch * n_q_heads * p.seg_max * (d + 2) * sizeof(float));
   p.total_bytes = p.qprep_bytes + p.partial_bytes;
   return p;
 }

@@ -14,24 +14,36 @@ void clear_error();
 
 constexpr int kVBlock = 32;      // slots per value block
 constexpr int kChunk = 32;       // tokens per decode chunk (one wave step)
-constexpr int kWaves = 4;        // waves per decode workgroup
-constexpr int kMaxGroup = 8;     // query heads handled by one decode workgroup
-constexpr int kResidentWorkgroups = 512;  // 256 CUs x 2 decode workgroups
+constexpr int kWaves = 4;        // waves per compression workgroup
+constexpr int kDecodeWaves = 8;  // waves per decode workgroup (one workgroup per CU)
+constexpr int kDecodeWorkgroups = 256;   // decode workgroups: one per CU of an MI355X
+constexpr int kMaxGroup = 8;     // query heads handled by one decode wave
 
 // Format checks shared by all entry points.  `device` additionally requires
 // d == 128 and the bit widths the kernels implement.
 tq_status check_format(const tq_format* f, bool device);
 
+// Work decomposition of a decode / score call.  A problem is one (layer,
+// sequence, KV head, head group); its tokens are cut into 32-token chunks,
+// chunks_per_problem of them (from max_seq_len).  The chunks of all problems,
+// problem-major, are dealt to n_workgroups workgroups in equal contiguous
+// ranges of chunks_per_wg (the last one shorter), so every workgroup has the
+// same amount of work; a range may cover the end of one problem and the start
+// of the next.  Each (problem, workgroup) piece leaves one partial result in
+// its problem's segment slot (at most seg_max slots per problem).
 struct SplitPlan {
-  int64_t split_tokens = 0;
-  int64_t n_splits = 0;
+  int64_t problems = 0;
+  int64_t chunks_per_problem = 0;
+  int64_t chunks_per_wg = 0;
+  int64_t n_workgroups = 0;
+  int64_t seg_max = 0;
   int n_head_groups = 0;
   size_t qprep_bytes = 0;    // [L][B][Hq][2][d] fp32
-  size_t partial_bytes = 0;  // [L][B][Hq][n_splits][d + 2] fp32
+  size_t partial_bytes = 0;  // [L][B][Hq][seg_max][d + 2] fp32
   size_t total_bytes = 0;
 };
 
-// Token split and workspace layout of a decode / score call.
+// Work decomposition and workspace layout of a decode / score call.
 SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_heads,
                       int64_t max_seq_len);
 

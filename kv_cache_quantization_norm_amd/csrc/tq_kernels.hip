@@ -15,16 +15,18 @@
 //                    z = (S Pi^T)(y - c[idx]) run as fp32 MFMA 16x16x4 with Pi
 //                    and S Pi^T staged in LDS in operand order.
 //   qprep_kernel     Pi q and S q per (layer, batch, query head).
-//   decode_kernel    one workgroup of 4 waves per (token split, KV head and
-//                    head group, layer x batch).  Each wave streams 32-token
-//                    chunks: unpack codes through LDS tables into fp16 MFMA
-//                    operands, score G <= 16 query heads with
-//                    v_mfma_f32_16x16x32_f16 (codes x Pi q, signs x S q), run
-//                    the online softmax, and accumulate values in the rotated
-//                    domain with a second MFMA (P x codes).  Pi^T is applied
-//                    once, after the split combine.
-//   combine_kernel   merges the split partials of a (layer, batch, KV head)
-//                    and applies Pi^T.
+//   decode_kernel    workgroups of 4 waves, at most two per CU, each given an
+//                    equal run of 32-token chunks of the problem-major chunk
+//                    sequence (a problem is one layer x sequence x KV head x
+//                    group of <= 8 query heads).  Each wave streams chunks:
+//                    unpack codes through LDS tables into fp16 MFMA operands,
+//                    score the query heads with v_mfma_f32_16x16x32_f16 (codes
+//                    x Pi q, signs x S q), run the online softmax, and
+//                    accumulate values in the rotated domain with a second
+//                    MFMA (P x codes).  Every (problem, workgroup) piece leaves
+//                    one partial per query head.
+//   combine_kernel   merges the partials of a (layer, batch, KV head) and
+//                    applies Pi^T once.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -707,8 +709,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 struct DecodeArgs {
   int n_layers, batch, H, Hq, G, n_hg;
   int64_t capacity;
-  int64_t split_tokens;
-  int n_splits;
+  int chunks_per_problem;   // 32-token chunks per problem (from max_len)
+  int chunks_per_wg;        // chunks of every workgroup but the last
+  int total_chunks;         // problems x chunks_per_problem
+  int seg_max;              // partial slots per query head
   const uint8_t* k_idx;
   const uint8_t* k_sign;
   const float* k_norm;
@@ -722,7 +726,7 @@ struct DecodeArgs {
   const float* vc;
   const int64_t* seq_start;
   const int32_t* seq_len;
-  float* partial;       // [L][B][Hq][n_splits][D + 2]
+  float* partial;       // [L][B][Hq][seg_max][D + 2]
   float* logits;        // score mode: [L][B][Hq][max_len]
   int64_t max_len;
   float scale;
@@ -754,9 +758,9 @@ template <int M, bool HILO> struct Lut {
 };
 
 template <int M, bool HILO>
-__device__ __forceinline__ void build_lut(uint32_t* lut, const float* cent, int tid) {
+__device__ __forceinline__ void build_lut(uint32_t* lut, const float* cent, int tid, int nt = 256) {
   using L = Lut<M, HILO>;
-  for (int x = tid; x < L::ENTRIES; x += 256) {
+  for (int x = tid; x < L::ENTRIES; x += nt) {
 #pragma unroll
     for (int e = 0; e < L::NG; e += 2) {
       const float c0 = cent[(x >> (e * M)) & ((1 << M) - 1)];
@@ -813,31 +817,34 @@ template <int M> struct KLut {
 
 // Pair table: entry x (two codes, x = c0 | c1 << M) = fp16 pair (c0, c1).
 template <int M>
-__device__ __forceinline__ void build_kpairs(uint32_t* phi, const float* cent, int tid) {
-  for (int x = tid; x < KLut<M>::PAIRS; x += 256)
+__device__ __forceinline__ void build_kpairs(uint32_t* phi, const float* cent, int tid, int nt = 256) {
+  for (int x = tid; x < KLut<M>::PAIRS; x += nt)
     phi[x] = uint32_t(f16_bits(cent[x & ((1 << M) - 1)])) | (uint32_t(f16_bits(cent[x >> M])) << 16);
 }
 // NC-code table from the pair table (after a barrier): dword k of entry x is
-// the pair of codes 2k, 2k + 1.  Thread t writes entries t + 256 u; all its
-// pair-table reads are issued before its writes.
-template <int M>
+// the pair of codes 2k, 2k + 1.  Thread t of NT writes entries t + NT u; all
+// its pair-table reads are issued before its writes.
+template <int M, int NT = 256>
 __device__ __forceinline__ void build_ktab(uint32_t* khi, const uint32_t* phi, int tid) {
   using K = KLut<M>;
-  static_assert(K::E % 256 == 0, "key table entries per thread");
   if constexpr (K::NC == 2) return;  // the pair table is the table
-  constexpr int U = K::E / 256;
-  uint32_t w[U][K::EW];
+  else {
+    static_assert(K::E % NT == 0 || NT % K::E == 0, "key table entries per thread");
+    constexpr int U = (K::E + NT - 1) / NT;
+    if (K::E < NT && tid >= K::E) return;
+    uint32_t w[U][K::EW];
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int k = 0; k < K::EW; ++k) w[u][k] = phi[((tid + 256 * u) >> (2 * M * k)) & (K::PAIRS - 1)];
+      for (int k = 0; k < K::EW; ++k) w[u][k] = phi[((tid + NT * u) >> (2 * M * k)) & (K::PAIRS - 1)];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    uint32_t* dst = khi + (tid + 256 * u) * K::EW;
-    if constexpr (K::EW == 2) {
-      *reinterpret_cast<u32x2*>(dst) = u32x2{w[u][0], w[u][1]};
-    } else {
-      *reinterpret_cast<u32x4*>(dst) = u32x4{w[u][0], w[u][1], w[u][2], w[u][3]};
+    for (int u = 0; u < U; ++u) {
+      uint32_t* dst = khi + (tid + NT * u) * K::EW;
+      if constexpr (K::EW == 2) {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{w[u][0], w[u][1]};
+      } else {
+        *reinterpret_cast<u32x4*>(dst) = u32x4{w[u][0], w[u][1], w[u][2], w[u][3]};
+      }
     }
   }
 }
@@ -871,137 +878,222 @@ __device__ __forceinline__ uint32_t slab_bits(const uint32_t (&w)[N], int s) {
   } else return w[s];
 }
 
+// Lane-private value table for 4-bit values: entry e (two codes) of lane l's
+// copy sits at byte e * 256 + 4 l, so the 64 lanes of a lookup always hit 64
+// different banks.  One byte permute forms the address from the code byte and
+// the lane offset.
+__device__ __forceinline__ void build_vrep(uint32_t* lut, const float* cent, int tid, int nt) {
+  for (int x = tid; x < 256 * 16; x += nt) {   // entry x / 16, copies 4 (x % 16) .. + 3
+    const int e = x >> 4;
+    const uint32_t w = uint32_t(f16_bits(cent[e & 15])) | (uint32_t(f16_bits(cent[e >> 4])) << 16);
+    *reinterpret_cast<u32x4*>(lut + e * 64 + (x & 15) * 4) = u32x4{w, w, w, w};
+  }
+}
+__device__ __forceinline__ half8 deq8_vrep(uint32_t bits, uint32_t lane4, const uint32_t* lut) {
+  // byte 0 of the address: 4 lane; byte 1: code byte k; bytes 2, 3: zero
+  const unsigned char* base = reinterpret_cast<const unsigned char*>(lut);
+  const uint32_t a0 = __builtin_amdgcn_perm(bits, lane4, 0x0C0C0400u);
+  const uint32_t a1 = __builtin_amdgcn_perm(bits, lane4, 0x0C0C0500u);
+  const uint32_t a2 = __builtin_amdgcn_perm(bits, lane4, 0x0C0C0600u);
+  const uint32_t a3 = __builtin_amdgcn_perm(bits, lane4, 0x0C0C0700u);
+  return as_half8(u32x4{*reinterpret_cast<const uint32_t*>(base + a0), *reinterpret_cast<const uint32_t*>(base + a1),
+                        *reinterpret_cast<const uint32_t*>(base + a2), *reinterpret_cast<const uint32_t*>(base + a3)});
+}
+
+// Decode / score kernel: one workgroup of 8 waves per CU.  Workgroup w owns
+// the chunks [w * chunks_per_wg, ...) of the problem-major chunk sequence; it
+// takes them in groups of at most two problems (pieces A and B).  Inside a
+// group the waves draw chunks one at a time from an LDS ticket counter, A's
+// chunks first, so waves that run faster take more chunks and all of them
+// finish together.  Each wave keeps its own online-softmax state per piece;
+// at the end of the group the wave states of a piece are merged in LDS, in
+// wave order, into the piece's partial.
 template <int MK, int BV, bool SCORE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(
+    DecodeArgs a) {
   using KL = KLut<(MK > 0 ? MK : 1)>;
+  constexpr int NT = kDecodeWaves * 64;
   constexpr int KT = MK > 0 ? KL::E * KL::EW : 1;                        // dwords of the key table
   constexpr int KP = MK > 0 && KL::NC > 2 ? KL::PAIRS : 1;                // pair-table dwords (if separate)
-  constexpr int VW = BV > 0 ? Lut<BV, false>::WORDS : 1;
-  // One LDS block with fixed offsets, the tables read in the token loop
-  // first so that every one of them is addressed with an immediate offset
-  // (below 64 KB): value table, sign table, key table.
-  constexpr int OFF_V = 0;
-  constexpr int OFF_S = OFF_V + ((VW * 4 + 15) / 16) * 16;
-  constexpr int OFF_KHI = OFF_S + 256 * 16;
-  constexpr int OFF_PHI = OFF_KHI + KT * 4;
-  // After the token loop the key tables are dead: the wave merge reuses
-  // their space for the scaled accumulators of every wave.
-  constexpr int RED_BYTES = kWaves * kMaxGroup * D * 4;
-  constexpr int TAB_END = OFF_PHI + KP * 4;
-  constexpr int OFF_NX = (TAB_END > OFF_KHI + RED_BYTES ? TAB_END : OFF_KHI + RED_BYTES);   // per-wave norm exchange
-  constexpr int OFF_MW = OFF_NX + kWaves * 128 * 4;
-  constexpr int OFF_LW = OFF_MW + kWaves * 16 * 4;
-  constexpr int LDS_BYTES = OFF_LW + kWaves * 16 * 4;
-  static_assert(OFF_KHI < 65536, "table offsets must fit the LDS immediate");
-  __shared__ __align__(16) unsigned char dsm[LDS_BYTES];
-  uint32_t* const lut_v = reinterpret_cast<uint32_t*>(dsm + OFF_V);
-  uint32_t* const lut_s = reinterpret_cast<uint32_t*>(dsm + OFF_S);
-  uint32_t* const lut_khi = reinterpret_cast<uint32_t*>(dsm + OFF_KHI);
+  constexpr bool VREP = BV == 4;                                          // lane-private value table
+  constexpr int VW = VREP ? 256 * 64 : (BV > 0 ? Lut<BV, false>::WORDS : 1);
+  // Tables first, each starting below 64 KB so that lookups carry the table
+  // offset as an instruction immediate.
+  constexpr int OFF_K = 0;
+  constexpr int OFF_PHI = OFF_K + KT * 4;
+  constexpr int OFF_S = ((OFF_PHI + KP * 4 + 15) / 16) * 16;
+  constexpr int OFF_V = ((OFF_S + 256 * 16 + 255) / 256) * 256;
+  constexpr int OFF_RED = ((OFF_V + VW * 4 + 15) / 16) * 16;
+  constexpr int RED_BYTES = SCORE ? 0 : kDecodeWaves * kMaxGroup * D * 4;
+  constexpr int OFF_NX = OFF_RED + RED_BYTES;
+  constexpr int OFF_MW = OFF_NX + kDecodeWaves * 128 * 4;
+  constexpr int OFF_LW = OFF_MW + kDecodeWaves * 16 * 4;
+  constexpr int OFF_Q = OFF_LW + kDecodeWaves * 16 * 4;    // staged query operands [piece][r / z][s][lane]
+  constexpr int OFF_CNT = OFF_Q + 2 * 2 * 4 * 64 * 16;
+  constexpr int LDS_BYTES = OFF_CNT + 16;
+  static_assert(OFF_V < 65536, "tables must start below 64 KB");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
+  __shared__ __align__(256) unsigned char dsm[LDS_BYTES];
+  uint32_t* const lut_k = reinterpret_cast<uint32_t*>(dsm + OFF_K);
   uint32_t* const pair_hi = reinterpret_cast<uint32_t*>(dsm + OFF_PHI);
+  uint32_t* const lut_s = reinterpret_cast<uint32_t*>(dsm + OFF_S);
+  uint32_t* const lut_v = reinterpret_cast<uint32_t*>(dsm + OFF_V);
+  float* const red = reinterpret_cast<float*>(dsm + OFF_RED);   // [wave][head][coordinate]
   float* const nxch = reinterpret_cast<float*>(dsm + OFF_NX);
   float(*const mw)[16] = reinterpret_cast<float(*)[16]>(dsm + OFF_MW);
   float(*const lw)[16] = reinterpret_cast<float(*)[16]>(dsm + OFF_LW);
-  float* const red = reinterpret_cast<float*>(dsm + OFF_KHI);   // [wave][head][coordinate], after the loop
+  uint32_t* const counter = reinterpret_cast<uint32_t*>(dsm + OFF_CNT);
+  half8* const qstage = reinterpret_cast<half8*>(dsm + OFF_Q);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, q = lane >> 4;   // MFMA column (head / coordinate) and k-group
-  const int split = blockIdx.x;
-  const int hk = blockIdx.y / a.n_hg, hg = blockIdx.y % a.n_hg;
-  const int layer = blockIdx.z / a.batch, b = blockIdx.z % a.batch;
-
-  // Sequence range, clamped to the cache.
-  const int64_t start = a.seq_start[b];
-  int64_t len = a.seq_len[b];
-  if (start < 0 || (start % kVBlock) != 0 || start >= a.capacity || len < 0) len = 0;
-  if (len > a.capacity - start) len = a.capacity - start;
-  if (len > a.max_len) len = a.max_len;   // tokens past max_seq_len are ignored
-  const int64_t t_lo = int64_t(split) * a.split_tokens;
-  const int64_t t_hi = t_lo + a.split_tokens < len ? t_lo + a.split_tokens : len;
-
-  // Tables.
-  if constexpr (MK > 0) {
-    if constexpr (KL::NC > 2)
-      build_kpairs<MK>(pair_hi, a.kc, tid);
-    else
-      build_kpairs<MK>(lut_khi, a.kc, tid);
-  }
-  if constexpr (BV > 0) build_lut<BV, false>(lut_v, a.vc, tid);
-  if constexpr (MK > 0) {
-    for (int x = tid; x < 256; x += 256) {
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const uint32_t lo = ((x >> e) & 1) ? 0x3C00u : 0xBC00u;
-        const uint32_t hi = ((x >> (e + 1)) & 1) ? 0x3C00u : 0xBC00u;
-        lut_s[x * 4 + e / 2] = lo | (hi << 16);
-      }
-    }
-  }
-  __syncthreads();
-  if constexpr (MK > 0 && KL::NC > 2) {
-    build_ktab<MK>(lut_khi, pair_hi, tid);
-    __syncthreads();
-  }
+  const bool lo_half = col >= 8;
+  const uint32_t lane4 = uint32_t(lane) * 4;
 
   // Scores are kept in base-2 units (scaled by log2 e) so that the softmax
   // weights are plain exp2; tq_score writes natural-unit logits.
   constexpr float kLog2e = 1.4426950408889634f;
   const float kscale = SCORE ? a.scale : a.scale * kLog2e;
   const float kscale_r = kscale * a.kappa;
+  constexpr int KREC = MK > 0 ? 16 * MK : 2 * D;   // bytes per key code record
+  constexpr int MKW = MK > 0 ? MK : 1;
+  constexpr bool kPrefetch = MK > 0 && BV > 0 && !SCORE;
+  const int cpp = a.chunks_per_problem;
+  const int64_t vblocks = a.capacity / kVBlock;
 
-  // Query operands (MFMA B operands).  Columns 0..7 are the group's query
-  // heads as fp16 high parts, columns 8..15 the same heads as fp16
-  // remainders, so one MFMA forms both halves of every product; lanes col and
-  // col ^ 8 then add their results (DPP row rotate by 8).  Lane (col, q) holds
-  // coordinates 32 q + 8 s + e of Pi q * scale and S q * scale * kappa.
-  const int g_local = hg * kMaxGroup + (col & 7);
-  const bool head_ok = g_local < a.G;
-  const bool lo_half = col >= 8;
-  const int h = hk * a.G + (head_ok ? g_local : 0);
-  half8 qr[4], qs[4];
-  {
-    const float4* qp = reinterpret_cast<const float4*>(
-        a.qprep + ((int64_t(layer) * a.batch + b) * a.Hq + h) * 2 * D + 32 * q);
-    const float kr = head_ok ? kscale : 0.f, ks = head_ok ? kscale_r : 0.f;
+  // ---- problem context: problem = ((layer * batch + b) * H + hk) * n_hg + hg
+  struct Run {
+    int64_t slot_base;   // slot of token 0 of the sequence in its (layer, KV head) plane
+    int64_t vblk0;       // value block of token 0
+    int64_t len;         // tokens of the sequence (clamped)
+    int layer, b, hk, hg;
+  };
+  auto run_of = [&](int prob) {
+    Run r;
+    r.hg = prob % a.n_hg;
+    r.hk = (prob / a.n_hg) % a.H;
+    r.b = (prob / (a.n_hg * a.H)) % a.batch;
+    r.layer = prob / (a.n_hg * a.H * a.batch);
+    const int64_t start = a.seq_start[r.b];
+    int64_t len = a.seq_len[r.b];
+    if (start < 0 || (start % kVBlock) != 0 || start >= a.capacity || len < 0) len = 0;
+    if (len > a.capacity - start) len = a.capacity - start;
+    if (len > a.max_len) len = a.max_len;   // tokens past max_seq_len are ignored
+    const int64_t plane = int64_t(r.layer) * a.H + r.hk;
+    r.slot_base = plane * a.capacity + start;
+    r.vblk0 = plane * vblocks + start / kVBlock;
+    r.len = len;
+    return r;
+  };
+  // A group: chunks [g0, b_end) of the workgroup's range, covering piece A
+  // (problem pa from its chunk rel_a0) and, if has_b, piece B (problem pa + 1
+  // from its chunk 0).  Tickets 0 .. live_a - 1 are A's chunks that hold
+  // tokens, live_a .. n_tickets - 1 B's.
+  struct Group {
+    Run ra, rb;
+    int pa, a_end, b_end, rel_a0, live_a, n_tickets;
+    bool has_b;
+  };
+  auto group_of = [&](int g0, int c_last) {
+    Group G;
+    G.pa = g0 / cpp;
+    G.a_end = (G.pa + 1) * cpp < c_last ? (G.pa + 1) * cpp : c_last;
+    G.has_b = G.a_end < c_last;
+    G.b_end = G.has_b ? (G.a_end + cpp < c_last ? G.a_end + cpp : c_last) : G.a_end;
+    G.rel_a0 = g0 - G.pa * cpp;
+    G.ra = run_of(G.pa);
+    G.rb = G.has_b ? run_of(G.pa + 1) : G.ra;
+    int live_a = int((G.ra.len + kChunk - 1) / kChunk) - G.rel_a0;
+    live_a = live_a < 0 ? 0 : (live_a > G.a_end - g0 ? G.a_end - g0 : live_a);
+    int live_b = G.has_b ? int((G.rb.len + kChunk - 1) / kChunk) : 0;
+    live_b = live_b > G.b_end - G.a_end ? G.b_end - G.a_end : live_b;
+    G.live_a = live_a;
+    G.n_tickets = live_a + live_b;
+    return G;
+  };
+
+  // ---- staged query operands (MFMA B operands), per piece: columns 0..7 are
+  // the group's query heads as fp16 high parts, columns 8..15 the same heads
+  // as fp16 remainders, so one MFMA forms both halves of every product; lanes
+  // col and col ^ 8 then add their results (DPP row rotate by 8).  Lane (col,
+  // q) of step s holds coordinates 32 q + 8 s + e of Pi q * scale (r) and of
+  // S q * scale * kappa (z).  Each thread converts items tid and tid + NT of
+  // the 1024 (piece, r / z, s, lane) operands.
+  struct QItem {
+    float v[2][8];
+  };
+  auto stage_load = [&](const Group& G, QItem& Q) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const float4 r0 = qp[2 * s], r1 = qp[2 * s + 1];
-      const float4 z0 = qp[D / 4 + 2 * s], z1 = qp[D / 4 + 2 * s + 1];
-      const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-      const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+    for (int u = 0; u < 2; ++u) {
+      const int it = tid + NT * u;
+      const int piece = it >> 9, kind = (it >> 8) & 1, s4 = (it >> 6) & 3, l = it & 63;
+      const Run& Rp = piece ? G.rb : G.ra;
+      const int g_local = Rp.hg * kMaxGroup + (l & 7);
+      const int hh = Rp.hk * a.G + (g_local < a.G ? g_local : 0);
+      const float4* src = reinterpret_cast<const float4*>(
+          a.qprep + ((int64_t(Rp.layer) * a.batch + Rp.b) * a.Hq + hh) * 2 * D + kind * D + 32 * (l >> 4) + 8 * s4);
+      const float4 x0 = src[0], x1 = src[1];
+      Q.v[u][0] = x0.x; Q.v[u][1] = x0.y; Q.v[u][2] = x0.z; Q.v[u][3] = x0.w;
+      Q.v[u][4] = x1.x; Q.v[u][5] = x1.y; Q.v[u][6] = x1.z; Q.v[u][7] = x1.w;
+    }
+  };
+  auto stage_store = [&](const Group& G, const QItem& Q) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int it = tid + NT * u;
+      const int piece = it >> 9, kind = (it >> 8) & 1, l = it & 63;
+      const Run& Rp = piece ? G.rb : G.ra;
+      const bool ok = Rp.hg * kMaxGroup + (l & 7) < a.G;
+      const float sc = ok ? (kind ? kscale_r : kscale) : 0.f;
+      const bool lo = (l & 15) >= 8;
+      half8 o;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float r = rv[e] * kr, z = zv[e] * ks;
-        const _Float16 rh = _Float16(r), zh = _Float16(z);
-        qr[s][e] = lo_half ? _Float16(r - float(rh)) : rh;
-        qs[s][e] = lo_half ? _Float16(z - float(zh)) : zh;
+        const float x = Q.v[u][e] * sc;
+        const _Float16 xh = _Float16(x);
+        o[e] = lo ? _Float16(x - float(xh)) : xh;
       }
+      qstage[it] = o;
     }
-  }
+  };
 
-  const int64_t plane = int64_t(layer) * a.H + hk;
-  const int64_t slot_base = plane * a.capacity + start;   // slot index of token 0
-  constexpr int KREC = MK > 0 ? 16 * MK : 2 * D;          // bytes per key code record
-
+  // ---- the wave's current run: online-softmax state and query operands
   float m_run = -INFINITY, l_run = 0.f;
   float sig = BV > 0 ? 0.f : 1.f, inv_sig = 1.f;   // value-norm normaliser (uniform over the wave)
   floatx4 acc[8];
+  half8 qr[4], qs[4];
+  Run R{};
+  bool head_ok = false;
+  int h = 0;
+  auto start_run = [&](int piece) {
+    const int g_local = R.hg * kMaxGroup + (col & 7);
+    head_ok = g_local < a.G;
+    h = R.hk * a.G + (head_ok ? g_local : 0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int s4 = 0; s4 < 4; ++s4) {
+      qr[s4] = qstage[((piece * 2 + 0) * 4 + s4) * 64 + lane];
+      qs[s4] = qstage[((piece * 2 + 1) * 4 + s4) * 64 + lane];
+    }
+    m_run = -INFINITY;
+    l_run = 0.f;
+    sig = BV > 0 ? 0.f : 1.f;
+    inv_sig = 1.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  };
 
   // Global data one lane needs for one 32-token chunk.  Every address lies in
   // the chunk's 32-slot block, which the clamped sequence range keeps inside
   // the cache, so the loads are unconditional; tokens past the end of the
-  // sequence are masked after loading.
-  constexpr int MKW = MK > 0 ? MK : 1;
-  // Packed key and value planes go through the software pipeline below;
-  // fp16 planes are loaded at the top of their own chunk.
-  constexpr bool kPrefetch = MK > 0 && BV > 0 && !SCORE;
-  // Norms: lane (col, q) loads one key norm (col < 8) or residual norm
-  // (col >= 8) of token 8 q + col % 8 and one value norm; the 16 lanes of a
-  // row then read them from each other with DPP row broadcasts.
-  struct Chunk {
+  // sequence are masked after loading.  Norms: lane (col, q) loads one key
+  // norm (col < 8) or residual norm (col >= 8) of token 8 q + col % 8 and one
+  // value norm.
+  struct KData {
     uint32_t kw[2][MKW];
     uint32_t sg[2];
+  };
+  struct VData {
     uint32_t vw[8];
     float nrm[2];
   };
@@ -1009,76 +1101,92 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     half8 kf[MK > 0 ? 1 : 2][MK > 0 ? 1 : 4];
     half8 vf[BV > 0 ? 1 : 8];
   };
-  const int64_t vplane = plane * (a.capacity / kVBlock);
-  auto load_late = [&](int64_t c0, ChunkLate& C) {
+  uint32_t koff[2], soff[2];
 #pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      const int64_t tk = slot_base + c0 + 8 * (col >> 2) + 4 * T + (col & 3);
-      if constexpr (MK == 0) {
+  for (int T = 0; T < 2; ++T) {
+    const uint32_t tk = 8 * (col >> 2) + 4 * T + (col & 3);
+    koff[T] = tk * KREC + 4 * q * MKW;
+    soff[T] = tk * 16 + 4 * q;
+  }
+  const uint32_t noff = 4 * (8 * q + (col & 7));
+  const uint32_t voff = col * (4 * (BV > 0 ? BV : 1)) + 4 * (BV == 4 ? q : (BV == 2 ? (q >> 1) : 0));
+  // rel: chunk index within the problem (tokens 32 rel ..)
+  auto load_k = [&](int rel, KData& K) {
+    if constexpr (MK > 0) {
+      const int64_t slot0 = R.slot_base + int64_t(rel) * kChunk;
+      const uint8_t* kp = a.k_idx + slot0 * KREC;
+      const uint8_t* sp = a.k_sign + slot0 * 16;
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        if constexpr (MK == 4) {
+          const u32x4 v4 = *reinterpret_cast<const u32x4*>(kp + koff[T]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) K.kw[T][u] = v4[u];
+        } else if constexpr (MK == 2) {
+          const u32x2 v2 = *reinterpret_cast<const u32x2*>(kp + koff[T]);
+          K.kw[T][0] = v2[0];
+          K.kw[T][1] = v2[1];
+        } else {
+#pragma unroll
+          for (int u = 0; u < MK; ++u) K.kw[T][u] = *reinterpret_cast<const uint32_t*>(kp + koff[T] + 4 * u);
+        }
+        K.sg[T] = *reinterpret_cast<const uint32_t*>(sp + soff[T]);
+      }
+    }
+  };
+  auto load_v = [&](int rel, VData& V) {
+    const int64_t slot0 = R.slot_base + int64_t(rel) * kChunk;
+    if constexpr (MK > 0) {
+      const float nk = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.k_norm + slot0) + noff);
+      const float nr = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.k_rnorm + slot0) + noff);
+      V.nrm[0] = col < 8 ? nk : nr;
+    }
+    if constexpr (BV > 0) {
+      V.nrm[1] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.v_norm + slot0) + noff);
+      const uint8_t* vp = a.v_idx + (R.vblk0 + rel) * D * (4 * BV);
+#pragma unroll
+      for (int vb = 0; vb < 8; ++vb)
+        V.vw[vb] = *reinterpret_cast<const uint32_t*>(vp + voff + 16 * vb * (4 * BV));
+    }
+  };
+  auto load_late = [&](int rel, ChunkLate& C) {
+    if constexpr (MK == 0) {
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        const int64_t tk = R.slot_base + int64_t(rel) * kChunk + 8 * (col >> 2) + 4 * T + (col & 3);
         const half8* kp = reinterpret_cast<const half8*>(a.k_f16 + tk * D + 32 * q);
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) C.kf[T][s2] = kp[s2];
       }
     }
     if constexpr (BV == 0) {
-      const int64_t blk = (start + c0) / kVBlock;
 #pragma unroll
       for (int vb = 0; vb < 8; ++vb)
         C.vf[vb] = *reinterpret_cast<const half8*>(
-            a.v_f16 + ((vplane + blk) * D + 16 * vb + col) * kVBlock + 8 * q);
-    }
-  };
-  auto load_chunk = [&](int64_t c0, Chunk& C) {
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      const int64_t tk = slot_base + c0 + 8 * (col >> 2) + 4 * T + (col & 3);
-      if constexpr (MK > 0) {
-        const uint32_t* kp = reinterpret_cast<const uint32_t*>(a.k_idx + tk * KREC) + q * MK;
-        if constexpr (MK == 4) {
-          const u32x4 v4 = *reinterpret_cast<const u32x4*>(kp);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) C.kw[T][u] = v4[u];
-        } else if constexpr (MK == 2) {
-          const u32x2 v2 = *reinterpret_cast<const u32x2*>(kp);
-          C.kw[T][0] = v2[0];
-          C.kw[T][1] = v2[1];
-        } else {
-#pragma unroll
-          for (int u = 0; u < MK; ++u) C.kw[T][u] = kp[u];
-        }
-        C.sg[T] = reinterpret_cast<const uint32_t*>(a.k_sign + tk * 16)[q];
-      }
-    }
-    {
-      const int64_t tn = slot_base + c0 + 8 * q + (col & 7);
-      if constexpr (MK > 0) C.nrm[0] = col < 8 ? a.k_norm[tn] : a.k_rnorm[tn];
-      if constexpr (BV > 0) C.nrm[1] = a.v_norm[tn];
-    }
-    const int64_t blk = (start + c0) / kVBlock;   // chunks are block aligned
-    if constexpr (BV > 0) {
-#pragma unroll
-      for (int vb = 0; vb < 8; ++vb) {
-        const uint32_t* grp = reinterpret_cast<const uint32_t*>(
-            a.v_idx + ((vplane + blk) * D + 16 * vb + col) * (4 * BV));
-        C.vw[vb] = grp[BV == 4 ? q : (BV == 2 ? (q >> 1) : 0)];
-      }
+            a.v_f16 + ((R.vblk0 + rel) * D + 16 * vb + col) * kVBlock + 8 * q);
     }
   };
 
   // ---- scores of one chunk: tile T row col -> token 8 (col/4) + 4 T + col%4
-  auto score = [&](const uint32_t (&kw)[2][MKW], const uint32_t (&sg)[2], const ChunkLate& late,
-                   floatx4 (&sm_)[2], floatx4 (&sq_)[2]) {
+  auto score = [&](const KData& K, const ChunkLate& late, floatx4 (&sm_)[2], floatx4 (&sq_)[2]) {
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
       sm_[T] = floatx4{0.f, 0.f, 0.f, 0.f};
       sq_[T] = floatx4{0.f, 0.f, 0.f, 0.f};
       if constexpr (MK > 0) {
+        // all table lookups of the tile first, so that they are in flight
+        // together, then the products
+        half8 kh[4], sd[4];
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-          const half8 kh = deq8_k<MK>(slab_bits<MK>(kw[T], s2), lut_khi);
-          sm_[T] = mfma16x16x32(kh, qr[s2], sm_[T]);
-          const half8 sd = *reinterpret_cast<const half8*>(lut_s + ((sg[T] >> (8 * s2)) & 0xFFu) * 4);
-          sq_[T] = mfma16x16x32(sd, qs[s2], sq_[T]);
+          kh[s2] = deq8_k<MK>(slab_bits<MK>(K.kw[T], s2), lut_k);
+          sd[s2] = *reinterpret_cast<const half8*>(lut_s + ((K.sg[T] >> (8 * s2)) & 0xFFu) * 4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          sm_[T] = mfma16x16x32(kh[s2], qr[s2], sm_[T]);
+          sq_[T] = mfma16x16x32(sd[s2], qs[s2], sq_[T]);
         }
       } else {
 #pragma unroll
@@ -1087,27 +1195,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
-  // ---- logits, online softmax and value accumulation of one chunk.  With
-  // `valid` false every token of the chunk is masked (a pipeline slot past the
-  // wave's last chunk).  The code is branch-free (the rescale is applied every
-  // chunk) so that the compiler can interleave it with the next chunk's scores.
-  // crel: first token of the chunk relative to the split start t_lo.
-  const int span = int(t_hi - t_lo);   // tokens of this split (may be <= 0)
-  auto attend = [&](int crel, bool valid, const float (&nrm)[2], const uint32_t (&vw)[8], const ChunkLate& late,
-                    const floatx4 (&sm_)[2], const floatx4 (&sq_)[2]) {
-    const bool full = valid && crel + kChunk <= span;                // uniform over the wave
-    const int rem = valid ? span - (crel + 8 * q) : 0;              // valid tokens of this lane's 8 (may be <= 0)
+  // ---- logits, online softmax and value accumulation of one chunk (tokens
+  // 32 rel .. of the current run's sequence).
+  auto attend = [&](int rel, const VData& V, const ChunkLate& late, const floatx4 (&sm_)[2],
+                    const floatx4 (&sq_)[2]) {
+    const int64_t crel = int64_t(rel) * kChunk;
+    const bool full = crel + kChunk <= R.len;                                  // uniform over the wave
+    const int rem = int(R.len - crel > kChunk ? kChunk : R.len - crel) - 8 * q;  // valid tokens of this lane's 8
     float lg[8];
     float kn[8], rn[8], vn[8];
     // Value norms are normalised by sig, the running maximum of ||v|| over
-    // the wave's tokens (uniform over the wave), so P'' below stays <= 1.
-    float sig_new = sig, inv_new = inv_sig;
+    // the run's tokens (uniform over the wave), so P'' below stays <= 1.
     float vl = 0.f;
     if constexpr (BV > 0 && !SCORE) {
-      vl = nrm[1];   // this lane's token 8 q + col % 8
+      vl = V.nrm[1];   // this lane's token 8 q + col % 8
       if (!full) vl = (col & 7) < rem ? vl : 0.f;
-      sig_new = fmaxf(fmaxf(sig, wave_max(vl)), 1e-30f);
-      inv_new = sig_new == sig ? inv_sig : __builtin_amdgcn_rcpf(sig_new);
+      // only when some norm exceeds the current normaliser (rare after the
+      // first chunks) is the new wave maximum formed
+      if (__builtin_amdgcn_ballot_w64(vl > sig) != 0) {
+        const float sig_new = fmaxf(fmaxf(sig, wave_max(vl)), 1e-30f);
+        const float inv_new = __builtin_amdgcn_rcpf(sig_new);
+        // rescale the accumulators to the new normaliser
+        const float factor = sig * inv_new;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] *= factor;
+        sig = sig_new;
+        inv_sig = inv_new;
+      }
     }
     {
       // Lane (col, q) holds the key norm (col < 8) or the residual norm
@@ -1115,17 +1229,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // a row need all 8 tokens' norms: exchange them through this wave's LDS
       // slot (in-order within the wave, so no barrier).
       float* nx = nxch + wave * 128;
-      nx[lane] = nrm[0];
-      if constexpr (BV > 0 && !SCORE) nx[64 + lane] = vl * inv_new;
+      if constexpr (MK > 0) nx[lane] = V.nrm[0];
+      if constexpr (BV > 0 && !SCORE) nx[64 + lane] = vl * inv_sig;
       const float4* n4 = reinterpret_cast<const float4*>(nx + 16 * q);
       if constexpr (MK > 0) {
         const float4 a0 = n4[0], a1 = n4[1], b0 = n4[2], b1 = n4[3];
-        kn[0] = a0.x; kn[1] = a0.y; kn[2] = a0.z; kn[3] = a0.w; kn[4] = a1.x; kn[5] = a1.y; kn[6] = a1.z; kn[7] = a1.w;
-        rn[0] = b0.x; rn[1] = b0.y; rn[2] = b0.z; rn[3] = b0.w; rn[4] = b1.x; rn[5] = b1.y; rn[6] = b1.z; rn[7] = b1.w;
+        kn[0] = a0.x; kn[1] = a0.y; kn[2] = a0.z; kn[3] = a0.w;
+        kn[4] = a1.x; kn[5] = a1.y; kn[6] = a1.z; kn[7] = a1.w;
+        rn[0] = b0.x; rn[1] = b0.y; rn[2] = b0.z; rn[3] = b0.w;
+        rn[4] = b1.x; rn[5] = b1.y; rn[6] = b1.z; rn[7] = b1.w;
       }
       if constexpr (BV > 0 && !SCORE) {
         const float4 c0 = n4[16], c1 = n4[17];
-        vn[0] = c0.x; vn[1] = c0.y; vn[2] = c0.z; vn[3] = c0.w; vn[4] = c1.x; vn[5] = c1.y; vn[6] = c1.z; vn[7] = c1.w;
+        vn[0] = c0.x; vn[1] = c0.y; vn[2] = c0.z; vn[3] = c0.w;
+        vn[4] = c1.x; vn[5] = c1.y; vn[6] = c1.z; vn[7] = c1.w;
       }
     }
 #pragma unroll
@@ -1145,30 +1262,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     if constexpr (SCORE) {
       if (head_ok && !lo_half) {
-        float* out = a.logits + ((int64_t(layer) * a.batch + b) * a.Hq + h) * a.max_len + t_lo + crel + 8 * q;
+        float* out = a.logits + ((int64_t(R.layer) * a.batch + R.b) * a.Hq + h) * a.max_len + crel + 8 * q;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (e < rem) out[e] = lg[e];
       }
     } else {
-      // ---- online softmax (per head; max across the 4 k-groups)
-      float cmax = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])),
-                         fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));
-      cmax = fmaxf(cmax, shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, shfl_xor(cmax, 32));
-      // Rescale only when a running maximum moved (rare after the first
-      // chunks); the branch is uniform over the wave.
-      const bool grow = cmax > m_run;   // NaN logits do not move the maximum
-      if (__builtin_amdgcn_ballot_w64(grow) != 0 || sig_new != sig) {
-        const float m_new = grow ? cmax : m_run;
+      // ---- online softmax (per head).  Rescale only when some logit exceeds
+      // the running maximum (rare after the first chunks); the branch is
+      // uniform over the wave and forms the cross-row maximum only then.
+      const float lmax = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])),
+                               fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));
+      if (__builtin_amdgcn_ballot_w64(lmax > m_run) != 0) {   // NaN logits do not move the maximum
+        float cmax = fmaxf(lmax, shfl_xor(lmax, 16));
+        cmax = fmaxf(cmax, shfl_xor(cmax, 32));
+        const float m_new = cmax > m_run ? cmax : m_run;
         const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        const float factor = alpha * sig * inv_new;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] *= factor;
+        for (int i = 0; i < 8; ++i) acc[i] *= alpha;
         l_run *= alpha;
         m_run = m_new;
-        sig = sig_new;
-        inv_sig = inv_new;
       }
       float p[8];
       float psum = 0.f;
@@ -1191,187 +1304,259 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const _Float16 hh = _Float16(pv);
         pp[e] = lo_half ? _Float16(pv - float(hh)) : hh;
       }
-      // ---- values: A operand lane (i = col, q) = coordinate 16 vb + i, tokens 8 q .. 8 q + 7
+      // ---- values: A operand lane (i = col, q) = coordinate 16 vb + i,
+      // tokens 8 q .. 8 q + 7; the lookups of four blocks are issued together
 #pragma unroll
-      for (int vb = 0; vb < 8; ++vb) {
-        half8 vd;
-        if constexpr (BV > 0) {
-          uint32_t bits = vw[vb];
-          if constexpr (BV == 2) bits = (bits >> (16 * (q & 1))) & 0xFFFFu;
-          else if constexpr (BV == 1) bits = (bits >> (8 * q)) & 0xFFu;
-          vd = deq8<BV>(bits, lut_v);
-        } else {
-          vd = late.vf[vb];
-          if (!full) {   // fp16 values past the end may hold anything
+      for (int v0 = 0; v0 < 8; v0 += 4) {
+        half8 vd[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (e >= rem) vd[e] = _Float16(0.f);
+        for (int u = 0; u < 4; ++u) {
+          const int vb = v0 + u;
+          if constexpr (BV == 4) {
+            vd[u] = deq8_vrep(V.vw[vb], lane4, lut_v);
+          } else if constexpr (BV > 0) {
+            uint32_t bits = V.vw[vb];
+            if constexpr (BV == 2) bits = (bits >> (16 * (q & 1))) & 0xFFFFu;
+            else if constexpr (BV == 1) bits = (bits >> (8 * q)) & 0xFFu;
+            vd[u] = deq8<BV>(bits, lut_v);
+          } else {
+            vd[u] = late.vf[vb];
+            if (!full) {   // fp16 values past the end may hold anything
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (e >= rem) vd[u][e] = _Float16(0.f);
+            }
           }
         }
-        acc[vb] = mfma16x16x32(vd, pp, acc[vb]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[v0 + u] = mfma16x16x32(vd[u], pp, acc[v0 + u]);
       }
     }
   };
 
-  const int64_t n_chunks = t_hi > t_lo ? (t_hi - t_lo + kChunk - 1) / kChunk : 0;
-  if constexpr (kPrefetch) {
-    // Software pipeline over the wave's chunks (chunk i = wave + 4 i): while
-    // chunk i is attended, chunk i+1 is scored and the key data of chunk i+2
-    // and the value data of chunk i+1 are loaded.  The loop is unrolled twice
-    // so the two register sets swap roles without copies.  Indices past the
-    // wave's last chunk are clamped to it (in-bounds loads, masked results).
-    struct KData {
-      uint32_t kw[2][MKW];
-      uint32_t sg[2];
-    };
-    struct VData {
-      uint32_t vw[8];
-      float nrm[2];
-    };
-    // Per-wave uniform base addresses of the wave's first chunk (chunk i of
-    // the wave lies kWaves * kChunk slots further) and 32-bit per-lane byte
-    // offsets, so that every load is one scalar base plus a lane offset.
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const int64_t slot0w = slot_base + t_lo + int64_t(wv) * kChunk;
-    const uint8_t* const kbase = a.k_idx + slot0w * KREC;
-    const uint8_t* const sbase = a.k_sign + slot0w * 16;
-    const uint8_t* const nkbase = reinterpret_cast<const uint8_t*>(a.k_norm + slot0w);
-    const uint8_t* const nrbase = reinterpret_cast<const uint8_t*>(a.k_rnorm + slot0w);
-    const uint8_t* const nvbase = reinterpret_cast<const uint8_t*>(a.v_norm + slot0w);
-    const uint8_t* const vbase = a.v_idx + (vplane + (start + t_lo) / kVBlock + wv) * D * (4 * BV);
-    constexpr int64_t kStep = int64_t(kWaves) * kChunk;   // slots between two chunks of a wave
-    uint32_t koff[2], soff[2];
-#pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      const uint32_t tk = 8 * (col >> 2) + 4 * T + (col & 3);
-      koff[T] = tk * KREC + 4 * q * MK;
-      soff[T] = tk * 16 + 4 * q;
-    }
-    const uint32_t noff = 4 * (8 * q + (col & 7));
-    const uint32_t voff = (16 * 0 + col) * (4 * BV) + 4 * (BV == 4 ? q : (BV == 2 ? (q >> 1) : 0));
-    const int64_t nw = n_chunks > wv ? (n_chunks - wv + kWaves - 1) / kWaves : 0;   // uniform
-    auto clampi = [&](int64_t i) { return i < nw ? i : nw - 1; };   // uniform
-    auto load_k = [&](int64_t i, KData& K) {
-      const int64_t ic = clampi(i);
-      const uint8_t* kp = kbase + ic * kStep * KREC;
-      const uint8_t* sp = sbase + ic * kStep * 16;
-#pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        if constexpr (MK == 4) {
-          const u32x4 v4 = *reinterpret_cast<const u32x4*>(kp + koff[T]);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) K.kw[T][u] = v4[u];
-        } else if constexpr (MK == 2) {
-          const u32x2 v2 = *reinterpret_cast<const u32x2*>(kp + koff[T]);
-          K.kw[T][0] = v2[0];
-          K.kw[T][1] = v2[1];
-        } else {
-#pragma unroll
-          for (int u = 0; u < MK; ++u) K.kw[T][u] = *reinterpret_cast<const uint32_t*>(kp + koff[T] + 4 * u);
+  // Writes the wave's state into its merge slot (`have`), or marks the slot
+  // empty without touching the registers (which may hold another piece).
+  auto flush = [&](bool have) {
+    if constexpr (!SCORE) {
+      if (!have) {
+        if (q == 0 && !lo_half) {
+          mw[wave][col] = -INFINITY;
+          lw[wave][col] = 0.f;
         }
-        K.sg[T] = *reinterpret_cast<const uint32_t*>(sp + soff[T]);
+        return;
       }
-    };
-    auto load_v = [&](int64_t i, VData& V) {
-      const int64_t ic = clampi(i);
-      const int64_t so = ic * kStep * 4;
-      const float nk = *reinterpret_cast<const float*>(nkbase + so + noff);
-      const float nr = *reinterpret_cast<const float*>(nrbase + so + noff);
-      V.nrm[0] = col < 8 ? nk : nr;
-      V.nrm[1] = *reinterpret_cast<const float*>(nvbase + so + noff);
-      const uint8_t* vp = vbase + ic * kWaves * D * (4 * BV);   // kWaves value blocks per step
 #pragma unroll
       for (int vb = 0; vb < 8; ++vb)
-        V.vw[vb] = *reinterpret_cast<const uint32_t*>(vp + voff + 16 * vb * (4 * BV));
-    };
-    auto crel = [&](int64_t i) { return int(wv + kWaves * clampi(i)) * kChunk; };
-    if (nw > 0) {
-      const ChunkLate late{};
-      KData K0, K1;
-      VData V0, V1;
-      floatx4 m0[2], s0[2], m1[2], s1[2];
-      load_k(0, K0);
-      load_k(1, K1);
-      load_v(0, V0);
-      score(K0.kw, K0.sg, late, m0, s0);
-#pragma unroll 1
-      for (int64_t i = 0; i < nw; i += 2) {
-        load_k(i + 2, K0);
-        load_v(i + 1, V1);
-        score(K1.kw, K1.sg, late, m1, s1);
-        attend(crel(i), true, V0.nrm, V0.vw, late, m0, s0);
-        load_k(i + 3, K1);
-        load_v(i + 2, V0);
-        score(K0.kw, K0.sg, late, m0, s0);
-        attend(crel(i + 1), i + 1 < nw, V1.nrm, V1.vw, late, m1, s1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[vb][r] += dpp_f<0x128>(acc[vb][r]);
+      float l_tot = l_run + shfl_xor(l_run, 16);
+      l_tot += shfl_xor(l_tot, 32);
+      const bool live = m_run != -INFINITY;   // uniform per column
+      if (q == 0 && !lo_half) {
+        mw[wave][col] = live ? m_run : -INFINITY;
+        lw[wave][col] = live ? l_tot : 0.f;
+      }
+      if (live && !lo_half) {
+        float* rw = red + (wave * kMaxGroup + col) * D;
+#pragma unroll
+        for (int vb = 0; vb < 8; ++vb) {
+          const float4 v4 = {acc[vb][0] * sig, acc[vb][1] * sig, acc[vb][2] * sig, acc[vb][3] * sig};
+          *reinterpret_cast<float4*>(rw + 16 * vb + 4 * q) = v4;
+        }
       }
     }
-  } else {
-#pragma unroll 1
-    for (int64_t ci = wave; ci < n_chunks; ci += kWaves) {
-      const int64_t c0 = t_lo + ci * kChunk;
-      Chunk cur;
-      load_chunk(c0, cur);
-      ChunkLate late;
-      if constexpr (MK == 0 || BV == 0) load_late(c0, late);
-      floatx4 sm_[2], sq_[2];
-      score(cur.kw, cur.sg, late, sm_, sq_);
-      attend(int(ci) * kChunk, true, cur.nrm, cur.vw, late, sm_, sq_);
+  };
+  // Merges the wave slots (after a barrier) into the partial of the piece of
+  // problem context Rp, slot `seg`: (max, sum of exponentials, accumulator[D])
+  // per head, the waves summed in wave order (the same for every thread).
+  // Thread t handles coordinate t % 128 of heads t / 128 and t / 128 + 4.
+  auto merge = [&](const Run& Rp, int seg) {
+    if constexpr (!SCORE) {
+      const int ng = a.G - Rp.hg * kMaxGroup < kMaxGroup ? a.G - Rp.hg * kMaxGroup : kMaxGroup;
+      const int64_t pbase = (int64_t(Rp.layer) * a.batch + Rp.b) * a.Hq + Rp.hk * a.G + Rp.hg * kMaxGroup;
+      const int i = tid & (D - 1);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int g = (tid >> 7) + 4 * u;
+        if (g < ng) {
+          float M = -INFINITY;
+#pragma unroll
+          for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, mw[w][g]);
+          float av = 0.f, ls = 0.f;
+#pragma unroll
+          for (int w = 0; w < kDecodeWaves; ++w) {
+            const float mwg = mw[w][g];
+            if (mwg != -INFINITY) {
+              const float f = __builtin_amdgcn_exp2f(mwg - M);
+              av += red[(w * kMaxGroup + g) * D + i] * f;
+              ls += lw[w][g] * f;
+            }
+          }
+          float* P = a.partial + ((pbase + g) * a.seg_max + seg) * (D + 2);
+          P[2 + i] = av;
+          if (i == 0) {
+            P[0] = M;
+            P[1] = ls;
+          }
+        }
+      }
+    }
+  };
+
+  // Ticket draw: lane 0 takes the next ticket of the workgroup counter.
+  auto draw = [&]() -> uint32_t {
+    uint32_t v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return v;
+  };
+  auto uni = [](uint32_t v) { return int(__builtin_amdgcn_readfirstlane(v)); };
+
+  // ---- the first group's context, query operands and first chunk loads are
+  // issued before the tables are built, so their latency overlaps the build.
+  // Every group starts with fixed tickets: wave w takes w, w + 8 and w + 16,
+  // and counter value base + k is ticket 24 + k (base: the counter value at
+  // the start of the group).
+  const int c_first = int(blockIdx.x) * a.chunks_per_wg;
+  const int c_last = c_first + a.chunks_per_wg < a.total_chunks ? c_first + a.chunks_per_wg : a.total_chunks;
+  Group G = group_of(c_first, c_last);
+  QItem qitem;
+  stage_load(G, qitem);
+  KData K0, K1;
+  VData V0, V1;
+  bool pre = false;   // the first run's K0, K1, V0 are already loaded
+  if constexpr (kPrefetch) {
+    const int t0 = wave, t1 = wave + kDecodeWaves;
+    if (t0 < G.n_tickets) {
+      const bool in_a = t0 < G.live_a;
+      const int limit = in_a ? G.live_a : G.n_tickets;
+      const int rel0 = in_a ? G.rel_a0 : -G.live_a;
+      R = in_a ? G.ra : G.rb;
+      load_k(rel0 + t0, K0);
+      load_k(rel0 + (t1 < limit ? t1 : t0), K1);
+      load_v(rel0 + t0, V0);
+      pre = true;
     }
   }
 
-  if constexpr (!SCORE) {
-    // ---- merge the 4 waves and write this split's partial.  First add the
-    // remainder columns of the value accumulators to the high-part columns.
+  // ---- tables (built once, used for every chunk of the workgroup)
+  if constexpr (MK > 0) {
+    if constexpr (KL::NC > 2)
+      build_kpairs<MK>(pair_hi, a.kc, tid, NT);
+    else
+      build_kpairs<MK>(lut_k, a.kc, tid, NT);
+  }
+  if constexpr (VREP)
+    build_vrep(lut_v, a.vc, tid, NT);
+  else if constexpr (BV > 0)
+    build_lut<BV, false>(lut_v, a.vc, tid, NT);
+  if constexpr (MK > 0) {
+    for (int x = tid; x < 256; x += NT) {
 #pragma unroll
-    for (int vb = 0; vb < 8; ++vb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[vb][r] += dpp_f<0x128>(acc[vb][r]);
-    float l_tot = l_run + shfl_xor(l_run, 16);
-    l_tot += shfl_xor(l_tot, 32);
-    if (q == 0 && !lo_half) {
-      mw[wave][col] = m_run;
-      lw[wave][col] = l_tot;
-    }
-    __syncthreads();   // every wave is past its last table lookup
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w][col & 7]);
-    const float f = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M) * sig;
-    if (!lo_half) {
-      float* rw = red + (wave * kMaxGroup + col) * D;
-#pragma unroll
-      for (int vb = 0; vb < 8; ++vb) {
-        const float4 v4 = {acc[vb][0] * f, acc[vb][1] * f, acc[vb][2] * f, acc[vb][3] * f};
-        *reinterpret_cast<float4*>(rw + 16 * vb + 4 * q) = v4;
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t lo = ((x >> e) & 1) ? 0x3C00u : 0xBC00u;
+        const uint32_t hi = ((x >> (e + 1)) & 1) ? 0x3C00u : 0xBC00u;
+        lut_s[x * 4 + e / 2] = lo | (hi << 16);
       }
+    }
+  }
+  stage_store(G, qitem);
+  if (tid == 0) counter[0] = 0;
+  __syncthreads();
+  if constexpr (MK > 0 && KL::NC > 2) {
+    build_ktab<MK, NT>(lut_k, pair_hi, tid);
+    __syncthreads();
+  }
+
+  int base = -3 * kDecodeWaves;   // ticket t of the group is counter value base + t (t >= 24)
+#pragma unroll 1
+  for (int g0 = c_first; g0 < c_last;) {
+    if (g0 != c_first) {
+      G = group_of(g0, c_last);
+      stage_load(G, qitem);
+      stage_store(G, qitem);
+      __syncthreads();
+    }
+    // the wave's next three tickets (relative to base)
+    int t0 = wave, t1 = wave + kDecodeWaves, t2 = wave + 2 * kDecodeWaves;
+    bool had_a = false, had_b = false;
+#pragma unroll 1
+    while (t0 < G.n_tickets) {
+      const bool in_a = t0 < G.live_a;
+      const int limit = in_a ? G.live_a : G.n_tickets;
+      const int rel0 = in_a ? G.rel_a0 : -G.live_a;   // chunk of ticket t: rel0 + t
+      R = in_a ? G.ra : G.rb;
+      const int first = t0;
+      auto relc = [&](int t) { return rel0 + (t < limit ? t : first); };   // clamped to a ticket of the run
+      if constexpr (kPrefetch) {
+        // Software pipeline: while chunk t0 is attended, chunk t1 is scored and
+        // the key data of chunk t2 and the value data of chunk t1 are loaded.
+        // Unrolled twice so that the two register sets swap roles without
+        // copies.  Loads of tickets past the run are clamped to its first one.
+        const ChunkLate late{};
+        floatx4 m0[2], s0[2], m1[2], s1[2];
+        if (!pre) {
+          load_k(relc(t0), K0);
+          load_k(relc(t1), K1);
+          load_v(relc(t0), V0);
+        }
+        pre = false;
+        start_run(in_a ? 0 : 1);
+        score(K0, late, m0, s0);
+#pragma unroll 1
+        for (;;) {
+          const uint32_t d3 = draw();
+          load_k(relc(t2), K0);
+          load_v(relc(t1), V1);
+          score(K1, late, m1, s1);
+          attend(rel0 + t0, V0, late, m0, s0);
+          const int t3 = uni(d3) - base;
+          if (t1 >= limit) { t0 = t1; t1 = t2; t2 = t3; break; }
+          const uint32_t d4 = draw();
+          load_k(relc(t3), K1);
+          load_v(relc(t2), V0);
+          score(K0, late, m0, s0);
+          attend(rel0 + t1, V1, late, m1, s1);
+          const int t4 = uni(d4) - base;
+          if (t2 >= limit) { t0 = t2; t1 = t3; t2 = t4; break; }
+          t0 = t2; t1 = t3; t2 = t4;
+        }
+      } else {
+        start_run(in_a ? 0 : 1);
+#pragma unroll 1
+        while (t0 < limit) {
+          const uint32_t d3 = draw();
+          ChunkLate late;
+          load_k(rel0 + t0, K0);
+          load_v(rel0 + t0, V0);
+          if constexpr (MK == 0 || BV == 0) load_late(rel0 + t0, late);
+          floatx4 sm_[2], sq_[2];
+          score(K0, late, sm_, sq_);
+          attend(rel0 + t0, V0, late, sm_, sq_);
+          t0 = t1; t1 = t2; t2 = uni(d3) - base;
+        }
+      }
+      if (in_a) {
+        flush(true);
+        had_a = true;
+      } else {
+        had_b = true;
+      }
+    }
+    // ---- merge the group's pieces
+    if (!had_a) flush(false);
+    __syncthreads();
+    const int next_base = uni(counter[0]);   // every draw of the group is done
+    merge(G.ra, int(blockIdx.x) - (G.pa * cpp) / a.chunks_per_wg);
+    if (G.has_b) {
+      __syncthreads();
+      flush(had_b);
+      __syncthreads();
+      merge(G.rb, int(blockIdx.x) - G.a_end / a.chunks_per_wg);
     }
     __syncthreads();
-    // Sum the waves in wave order (the same result on every run) and write the
-    // split's partial: (max, sum of exponentials, accumulator[D]) per head.
-    const int64_t pbase = (int64_t(layer) * a.batch + b) * a.Hq;
-    const int ng = a.G - hg * kMaxGroup < kMaxGroup ? a.G - hg * kMaxGroup : kMaxGroup;
-    for (int e = tid; e < ng * (D + 2); e += 256) {
-      const int g = e / (D + 2), i = e - g * (D + 2);
-      const int hh = hk * a.G + hg * kMaxGroup + g;
-      float v;
-      if (i == 0) {
-        v = -INFINITY;
-        for (int w = 0; w < kWaves; ++w) v = fmaxf(v, mw[w][g]);
-      } else if (i == 1) {
-        float Mg = -INFINITY;
-        for (int w = 0; w < kWaves; ++w) Mg = fmaxf(Mg, mw[w][g]);
-        v = 0.f;
-        for (int w = 0; w < kWaves; ++w)
-          if (mw[w][g] != -INFINITY) v += lw[w][g] * __builtin_amdgcn_exp2f(mw[w][g] - Mg);
-      } else {
-        v = red[g * D + (i - 2)];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) v += red[(w * kMaxGroup + g) * D + (i - 2)];
-      }
-      a.partial[((pbase + hh) * a.n_splits + split) * (D + 2) + i] = v;
-    }
-
+    base = next_base - 3 * kDecodeWaves;
+    g0 = G.b_end;
   }
 }
 
@@ -1428,19 +1613,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }
 }
 
-// Merges the split partials of one (layer, batch, KV head) for every query
+// Merges the piece partials of one (layer, batch, KV head) for every query
 // head of its group and writes out = Pi^T (acc / l) (acc / l for fp16
 // values).  Merge: thread t works on coordinate t % 128 of heads t / 128,
-// t / 128 + 2, ...; the partials are read in batches of 4 splits x 8 heads
-// with clamped (always valid) addresses so that a batch's loads are in flight
-// together, and merged with a running maximum.  Pi^T: fp32 MFMA 16x16x4 with
+// t / 128 + 2, ...; a head's problem has one partial per workgroup whose
+// chunk run overlaps it (computed from the run length, the same arithmetic
+// as the decode kernel's slot index).  They are read in batches of 4 pieces x
+// 8 heads with clamped (always valid) addresses so that a batch's loads are
+// in flight together, and merged with a running maximum.  Pi^T: fp32 MFMA 16x16x4 with
 // D[i][g] = sum_j Pi[j][i] res[g][j]; wave w owns output rows 32 w .. 32 w + 31
 // (two 16-row blocks); its A operands (columns of Pi) are loaded from global
 // memory at the start, before the merge, and res comes from LDS.
 constexpr int kCombineHeads = 16;
 template <bool ROT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void combine_kernel(
-    const float* partial, const float* pi, float* out, int batch, int H, int Hq, int n_splits) {
+    const float* partial, const float* pi, float* out, int batch, int H, int Hq, int n_hg, int chunks_per_problem,
+    int chunks_per_wg, int seg_max) {
   constexpr bool rotate = ROT;
   __shared__ __align__(16) float res[kCombineHeads][D];
   const int hk = blockIdx.x, b = blockIdx.y, layer = blockIdx.z, tid = threadIdx.x;
@@ -1463,21 +1651,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const int ng = G - g0 < kCombineHeads ? G - g0 : kCombineHeads;
     const int64_t row0 = (int64_t(layer) * batch + b) * Hq + int64_t(hk) * G + g0;
     float M[NH], L[NH], A[NH];
+    int nseg[NH];   // partial slots written for the head's problem
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
       M[k] = -INFINITY;
       L[k] = 0.f;
       A[k] = 0.f;
+      const int g = g0 + (half + 2 * k < ng ? half + 2 * k : ng - 1);
+      const int prob = ((layer * batch + b) * H + hk) * n_hg + g / kMaxGroup;
+      const int first = prob * chunks_per_problem;
+      nseg[k] = (first + chunks_per_problem - 1) / chunks_per_wg - first / chunks_per_wg + 1;
     }
-    for (int sp0 = 0; sp0 < n_splits; sp0 += SB) {
+    for (int sp0 = 0; sp0 < seg_max; sp0 += SB) {
       float ms[NH][SB], ls[NH][SB], as[NH][SB];
 #pragma unroll
       for (int k = 0; k < NH; ++k) {
         const int g = half + 2 * k < ng ? half + 2 * k : ng - 1;
-        const float* P = partial + (row0 + g) * int64_t(n_splits) * (D + 2);
+        const float* P = partial + (row0 + g) * int64_t(seg_max) * (D + 2);
 #pragma unroll
         for (int u = 0; u < SB; ++u) {
-          const int64_t sp = sp0 + u < n_splits ? sp0 + u : n_splits - 1;
+          const int64_t sp = sp0 + u < nseg[k] ? sp0 + u : nseg[k] - 1;
           ms[k][u] = P[sp * (D + 2)];
           ls[k][u] = P[sp * (D + 2) + 1];
           as[k][u] = P[sp * (D + 2) + 2 + i];
@@ -1488,14 +1681,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         float Mn = M[k];
 #pragma unroll
         for (int u = 0; u < SB; ++u)
-          if (sp0 + u < n_splits) Mn = fmaxf(Mn, ms[k][u]);
+          if (sp0 + u < nseg[k]) Mn = fmaxf(Mn, ms[k][u]);
         const float f0 = M[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[k] - Mn);
         L[k] *= f0;
         A[k] *= f0;
 #pragma unroll
         for (int u = 0; u < SB; ++u) {
           const float f =
-              (sp0 + u >= n_splits || ms[k][u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[k][u] - Mn);
+              (sp0 + u >= nseg[k] || ms[k][u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[k][u] - Mn);
           L[k] = fmaf(ls[k][u], f, L[k]);
           A[k] = fmaf(as[k][u], f, A[k]);
         }
@@ -1541,7 +1734,7 @@ template <bool SCORE>
 tq_status launch_decode(int mk, int bv, const DecodeArgs& args, dim3 grid, hipStream_t st) {
 #define TQ_DEC(MK_, BV_)                                                                       \
   if (mk == MK_ && bv == BV_) {                                                                \
-    hipLaunchKernelGGL((decode_kernel<MK_, BV_, SCORE>), grid, dim3(256), 0, st, args);       \
+    hipLaunchKernelGGL((decode_kernel<MK_, BV_, SCORE>), grid, dim3(kDecodeWaves * 64), 0, st, args); \
     return TQ_OK;                                                                              \
   }
 #define TQ_DEC_V(MK_) TQ_DEC(MK_, 0) TQ_DEC(MK_, 1) TQ_DEC(MK_, 2) TQ_DEC(MK_, 4)
@@ -1589,7 +1782,7 @@ tq_status launch_status(const char* what) {
 }
 
 // Decode stages: prepare the query operands (qprep_kernel), score / accumulate
-// the token splits (decode_kernel), merge the splits (combine_kernel).
+// the chunk runs (decode_kernel), merge the pieces (combine_kernel).
 enum { kStagePrepare = 1, kStagePartials = 2, kStageCombine = 4, kStageAll = 7 };
 
 template <bool SCORE>
@@ -1614,7 +1807,8 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   if (int64_t(cache->n_layers) * batch > 65535)
     return fail(TQ_ERR_INVALID_ARG, "n_layers * batch exceeds 65535");
   const SplitPlan plan = plan_decode(fmt->d, cache->n_layers, batch, cache->n_kv_heads, n_q_heads, max_seq_len);
-  if (plan.n_splits > 0x7FFFFFFF) return fail(TQ_ERR_INVALID_ARG, "too many splits");
+  if (plan.problems * plan.chunks_per_problem > (int64_t(1) << 30))
+    return fail(TQ_ERR_INVALID_ARG, "too many 32-token chunks in one call");
   if (!workspace || workspace_bytes < plan.total_bytes)
     return fail(TQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, plan.total_bytes);
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -1642,8 +1836,10 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   a.G = n_q_heads / cache->n_kv_heads;
   a.n_hg = plan.n_head_groups;
   a.capacity = cache->capacity;
-  a.split_tokens = plan.split_tokens;
-  a.n_splits = int(plan.n_splits);
+  a.chunks_per_problem = int(plan.chunks_per_problem);
+  a.chunks_per_wg = int(plan.chunks_per_wg);
+  a.total_chunks = int(plan.problems * plan.chunks_per_problem);
+  a.seg_max = int(plan.seg_max);
   a.k_idx = cache->k_idx;
   a.k_sign = cache->k_sign;
   a.k_norm = cache->k_norm;
@@ -1662,9 +1858,7 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   a.max_len = max_seq_len;
   a.scale = scale != 0.f ? scale : 1.0f / std::sqrt(float(fmt->d));
   a.kappa = float(std::sqrt(M_PI / 2.0) / fmt->d);
-  const int64_t gy = int64_t(cache->n_kv_heads) * plan.n_head_groups;
-  if (gy > 65535) return fail(TQ_ERR_INVALID_ARG, "too many KV heads x head groups");
-  dim3 grid(unsigned(plan.n_splits), unsigned(gy), unsigned(cache->n_layers * batch));
+  const dim3 grid(unsigned(plan.n_workgroups));
   if (stages & kStagePartials) {
     if ((st = launch_decode<SCORE>(mk, SCORE ? 0 : bv, a, grid, hs))) return st;
     if ((st = launch_status("decode"))) return st;
@@ -1673,10 +1867,10 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
     const dim3 cgrid(cache->n_kv_heads, batch, cache->n_layers);
     if (bv > 0)
       hipLaunchKernelGGL(combine_kernel<true>, cgrid, dim3(256), 0, hs, partial, tables->pi, out, batch,
-                         cache->n_kv_heads, n_q_heads, int(plan.n_splits));
+                         cache->n_kv_heads, n_q_heads, a.n_hg, a.chunks_per_problem, a.chunks_per_wg, a.seg_max);
     else
       hipLaunchKernelGGL(combine_kernel<false>, cgrid, dim3(256), 0, hs, partial, tables->pi, out, batch,
-                         cache->n_kv_heads, n_q_heads, int(plan.n_splits));
+                         cache->n_kv_heads, n_q_heads, a.n_hg, a.chunks_per_problem, a.chunks_per_wg, a.seg_max);
     if ((st = launch_status("combine"))) return st;
   }
   return TQ_OK;

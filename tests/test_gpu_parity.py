@@ -179,7 +179,9 @@ def test_end_to_end(case):
 @pytest.mark.parametrize("case", ["w5_ragged5", "w3_6L_asym"])
 def test_staged_decode_matches_one_call(case):
     """tq_decode_prepare + tq_decode_partials + tq_decode_combine on one stream
-    give bit for bit what tq_decode_attention gives."""
+    give what tq_decode_attention gives.  The decode kernel deals chunks to its
+    waves dynamically, so two calls can round differently in the last bits:
+    the results agree to a relative 1e-5 of the output scale."""
     import kv_cache_quantization_norm_amd as tq
     w = CASES[case]
     _say("staged", case)
@@ -202,8 +204,9 @@ def test_staged_decode_matches_one_call(case):
         tq.tq_decode_combine(tfmt, tables, dev, batch, hq, max_len, staged, ws)
         torch.cuda.synchronize()
         a, b = one.cpu().numpy(), staged.cpu().numpy()
-        assert not np.isnan(a).any()
-        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+        assert not np.isnan(a).any() and not np.isnan(b).any()
+        scale = max(1.0, float(np.max(np.abs(a))))
+        assert float(np.max(np.abs(a - b))) <= 1e-5 * scale
 
 
 def test_degenerate_vectors_and_nan():
