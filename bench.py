@@ -30,6 +30,34 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_w2_dense28L_hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "kv_cache_quantization_norm_amd", "csrc", f)
+                  for f in ("tq_kernels.hip", "tq_host.cpp", "tq_internal.h")]
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode_kernel launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
+    for a plain copy of known size), or None when the summary was taken on
+    other kernel sources than the ones in this tree."""
+    try:
+        txt = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in txt.splitlines() if line.startswith(("traffic_bytes_per_launch:",
+                                                                                         "kernel_source_sha256:")))
+    if fields.get("kernel_source_sha256", "").strip() != kernel_source_digest():
+        return None
+    return int(fields["traffic_bytes_per_launch"].strip())
 MALL_BYTES = 256 << 20
 
 
@@ -201,7 +229,7 @@ def main():
                    "kv_dtype": w.dtype, "layers_per_call": L, "cache_copies": n_copies,
                    "step": "append-compress 1 token x 28 layers + decode attention x 28 layers"},
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": f"decode_kernel<{max(w.k_bits - 1, 0)},{w.v_bits},false>",
                      "bytes_per_launch": kernel_bytes, "us_per_launch": round(kern_mean, 2),
                      "us_median": round(float(np.median(kern_us)), 2),

@@ -1486,19 +1486,18 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       const int limit = in_a ? G.live_a : G.n_tickets;
       const int rel0 = in_a ? G.rel_a0 : -G.live_a;   // chunk of ticket t: rel0 + t
       R = in_a ? G.ra : G.rb;
-      const int first = t0;
-      auto relc = [&](int t) { return rel0 + (t < limit ? t : first); };   // clamped to a ticket of the run
       if constexpr (kPrefetch) {
         // Software pipeline: while chunk t0 is attended, chunk t1 is scored and
         // the key data of chunk t2 and the value data of chunk t1 are loaded.
         // Unrolled twice so that the two register sets swap roles without
-        // copies.  Loads of tickets past the run are clamped to its first one.
+        // copies.  A ticket past the run reloads the run's latest chunk (still
+        // in L2), whose copy is scored but never attended.
         const ChunkLate late{};
         floatx4 m0[2], s0[2], m1[2], s1[2];
         if (!pre) {
-          load_k(relc(t0), K0);
-          load_k(relc(t1), K1);
-          load_v(relc(t0), V0);
+          load_k(rel0 + t0, K0);
+          load_k(rel0 + (t1 < limit ? t1 : t0), K1);
+          load_v(rel0 + t0, V0);
         }
         pre = false;
         start_run(in_a ? 0 : 1);
@@ -1506,15 +1505,15 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
 #pragma unroll 1
         for (;;) {
           const uint32_t d3 = draw();
-          load_k(relc(t2), K0);
-          load_v(relc(t1), V1);
+          load_k(rel0 + (t2 < limit ? t2 : (t1 < limit ? t1 : t0)), K0);
+          load_v(rel0 + (t1 < limit ? t1 : t0), V1);
           score(K1, late, m1, s1);
           attend(rel0 + t0, V0, late, m0, s0);
           const int t3 = uni(d3) - base;
           if (t1 >= limit) { t0 = t1; t1 = t2; t2 = t3; break; }
           const uint32_t d4 = draw();
-          load_k(relc(t3), K1);
-          load_v(relc(t2), V0);
+          load_k(rel0 + (t3 < limit ? t3 : (t2 < limit ? t2 : t1)), K1);
+          load_v(rel0 + (t2 < limit ? t2 : t1), V0);
           score(K0, late, m0, s0);
           attend(rel0 + t1, V1, late, m1, s1);
           const int t4 = uni(d4) - base;
