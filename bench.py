@@ -262,16 +262,19 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def decode_pieces(problems, t, chunk=32, waves=8, max_workgroups=256):
+def decode_pieces(problems, t, chunk=32, waves=8, max_workgroups=256, crossing_chunks=16):
     """Number of (problem, workgroup) pieces of a decode call, each leaving one
-    partial per query head: the chunks of all problems (one problem = layer x
-    sequence x KV head with up to 8 query heads) are dealt to the workgroups in
-    equal contiguous ranges, and a range that crosses into a problem adds one
-    piece to it."""
+    partial per query head, following the library's work split: equal runs of
+    chunks over the problem-major chunk sequence, or, when that is nearly as
+    short, k = max_workgroups // problems aligned runs per problem."""
     cpp = -(-max(t, 1) // chunk)
     total = problems * cpp
     wgs = min(max_workgroups, -(-total // waves))
     cpw = -(-total // wgs)
+    k = min(max_workgroups // problems, cpp // waves)
+    if k >= 1 and cpp % cpw != 0 and -(-cpp // k) <= cpw + crossing_chunks:
+        cpw = -(-cpp // k)
+        cpp = k * cpw
     return sum((p * cpp + cpp - 1) // cpw - (p * cpp) // cpw + 1 for p in range(problems))
 
 

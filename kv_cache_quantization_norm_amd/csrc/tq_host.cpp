@@ -46,13 +46,32 @@ SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_he
   p.n_head_groups = (group + kMaxGroup - 1) / kMaxGroup;
   p.problems = int64_t(n_layers) * batch * n_kv_heads * p.n_head_groups;
   const int64_t len = max_seq_len > 0 ? max_seq_len : 1;
-  p.chunks_per_problem = (len + kChunk - 1) / kChunk;
-  const int64_t total = p.problems * p.chunks_per_problem;
-  // One workgroup per CU, each with at least one chunk per wave.
+  const int64_t cpp = (len + kChunk - 1) / kChunk;
+  const int64_t total = p.problems * cpp;
+  // Balanced split: one workgroup per CU, equal runs of chunks, each with at
+  // least one chunk per wave; a run may cross from one problem into the next.
   int64_t wgs = (total + kDecodeWaves - 1) / kDecodeWaves;
   if (wgs > kDecodeWorkgroups) wgs = kDecodeWorkgroups;
-  p.chunks_per_wg = (total + wgs - 1) / wgs;
-  p.n_workgroups = (total + p.chunks_per_wg - 1) / p.chunks_per_wg;
+  const int64_t cpw_b = (total + wgs - 1) / wgs;
+  p.chunks_per_problem = cpp;
+  p.chunks_per_wg = cpw_b;
+  // Aligned split: each problem cut into k equal runs (k workgroups per
+  // problem, k = CUs / problems), so that no run crosses a problem boundary.
+  // A crossing costs a workgroup about kCrossingChunks chunks of time (a
+  // second pipeline start and a second merge), so the aligned split is taken
+  // when its runs are at most that much longer than the balanced ones.  The
+  // problem is then padded to k runs of equal length; padding chunks hold no
+  // tokens and are never dealt.
+  int64_t k = kDecodeWorkgroups / p.problems;
+  if (k > cpp / kDecodeWaves) k = cpp / kDecodeWaves;   // at least one chunk per wave
+  if (k >= 1 && cpp % cpw_b != 0) {
+    const int64_t cpw_a = (cpp + k - 1) / k;
+    if (cpw_a <= cpw_b + kCrossingChunks) {
+      p.chunks_per_problem = k * cpw_a;
+      p.chunks_per_wg = cpw_a;
+    }
+  }
+  p.n_workgroups = (p.problems * p.chunks_per_problem + p.chunks_per_wg - 1) / p.chunks_per_wg;
   // A problem of C chunks overlaps at most ceil((C - 1) / W) + 1 ranges of W.
   p.seg_max = (p.chunks_per_problem - 1 + p.chunks_per_wg - 1) / p.chunks_per_wg + 1;
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };

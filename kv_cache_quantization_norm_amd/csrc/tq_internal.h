@@ -18,6 +18,7 @@ constexpr int kWaves = 4;        // waves per compression workgroup
 constexpr int kDecodeWaves = 8;  // waves per decode workgroup (one workgroup per CU)
 constexpr int kDecodeWorkgroups = 256;   // decode workgroups: one per CU of an MI355X
 constexpr int kMaxGroup = 8;     // query heads handled by one decode wave
+constexpr int kCrossingChunks = 16;   // measured cost of a problem change inside a decode workgroup, in chunks
 
 // Format checks shared by all entry points.  `device` additionally requires
 // d == 128 and the bit widths the kernels implement.
@@ -25,7 +26,8 @@ tq_status check_format(const tq_format* f, bool device);
 
 // Work decomposition of a decode / score call.  A problem is one (layer,
 // sequence, KV head, head group); its tokens are cut into 32-token chunks,
-// chunks_per_problem of them (from max_seq_len).  The chunks of all problems,
+// chunks_per_problem of them (from max_seq_len, possibly padded with chunks
+// that hold no tokens).  The chunks of all problems,
 // problem-major, are dealt to n_workgroups workgroups in equal contiguous
 // ranges of chunks_per_wg (the last one shorter), so every workgroup has the
 // same amount of work; a range may cover the end of one problem and the start
