@@ -53,6 +53,13 @@ def _load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"libtq.so is not built ({path}); run __graft_entry__.build() or "
                           "python -m kv_cache_quantization_norm_amd.build")
+    # libtq.so needs libamdhip64.so.7.  PyTorch ships its own copy of that
+    # runtime under a file name the dynamic loader does not match to the
+    # soname, so whichever loads first decides: if libtq.so came first the
+    # process would hold two HIP runtimes and the second to start sees no
+    # device.  Loading torch first makes libtq.so bind to torch's runtime, the
+    # one that owns the tensors and streams handed to it.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, I32, I64, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     fmtp = ctypes.POINTER(tq_format)
@@ -64,6 +71,7 @@ def _load(path: str = LIB_PATH):
         "tq_make_codebook": (I32, [I32, I32, P, P]),
         "tq_cache_plane_bytes": (I32, [fmtp, I32, I32, I64, P]),
         "tq_decode_workspace_bytes": (SZ, [fmtp, I32, I32, I32, I32, I64]),
+        "tq_decode_split": (I32, [fmtp, I32, I32, I32, I32, I64, P]),
         "tq_compress_kv": (I32, [fmtp, tabp, cachep, P, P, I32, I32, I32, I64, P, I64, P]),
         "tq_decode_attention": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P, SZ, P]),
         "tq_score": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P, SZ, P]),
@@ -82,7 +90,7 @@ def _load(path: str = LIB_PATH):
 
 _lib = _load()
 EXPORTED = ("tq_layer_seed", "tq_make_rotations", "tq_make_codebook", "tq_cache_plane_bytes",
-            "tq_decode_workspace_bytes", "tq_compress_kv", "tq_decode_attention", "tq_score",
+            "tq_decode_workspace_bytes", "tq_decode_split", "tq_compress_kv", "tq_decode_attention", "tq_score",
             "tq_decode_prepare", "tq_decode_partials", "tq_decode_combine",
             "tq_status_string", "tq_last_error")
 
@@ -153,6 +161,15 @@ def tq_cache_plane_bytes(fmt: tq_format, n_layers: int, n_kv_heads: int, capacit
     _check(_lib.tq_cache_plane_bytes(ctypes.byref(fmt), n_layers, n_kv_heads, capacity, out),
            "tq_cache_plane_bytes")
     return list(out)
+
+
+def tq_decode_split(fmt: tq_format, n_layers: int, batch: int, n_kv_heads: int, n_q_heads: int,
+                    max_seq_len: int) -> dict:
+    """The decode work split (see include/tq.h)."""
+    out = (ctypes.c_int64 * 5)()
+    _check(_lib.tq_decode_split(ctypes.byref(fmt), n_layers, batch, n_kv_heads, n_q_heads, max_seq_len, out),
+           "tq_decode_split")
+    return dict(zip(("problems", "chunks_per_problem", "chunks_per_wg", "n_workgroups", "pieces_max"), out))
 
 
 def tq_decode_workspace_bytes(fmt: tq_format, n_layers: int, batch: int, n_kv_heads: int, n_q_heads: int,

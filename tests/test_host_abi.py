@@ -28,6 +28,19 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(tq.EXPORTED)
 
 
+def test_one_hip_runtime_in_process():
+    """Importing the package before torch, then torch, must leave a single HIP
+    runtime mapped: a second copy would see no device."""
+    import subprocess
+    import sys
+    code = ("import kv_cache_quantization_norm_amd\n"
+            "import torch\n"
+            "print(';'.join(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l})))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300, check=True).stdout.strip().splitlines()[-1]
+    assert len(out.split(';')) == 1, out
+
+
 def test_layer_seed_matches_page():
     g = load_golden("page_constants.json")["layer_seed"]
     for layer, seed in g["examples"].items():
