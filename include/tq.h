@@ -135,6 +135,16 @@ tq_status tq_cache_plane_bytes(const tq_format* fmt, int32_t n_layers, int32_t n
 size_t tq_decode_workspace_bytes(const tq_format* fmt, int32_t n_layers, int32_t batch,
                                  int32_t n_kv_heads, int32_t n_q_heads, int64_t max_seq_len);
 
+/* Host.  The work split of a decode / score call for these sizes:
+ * out[0] problems (layer x sequence x KV head x group of <= 8 query heads),
+ * out[1] 32-token chunks per problem (from max_seq_len, possibly padded with
+ * chunks that hold no tokens), out[2] chunks per decode workgroup,
+ * out[3] decode workgroups, out[4] pieces per problem at most.  Workgroup w
+ * takes chunks [w out[2], (w + 1) out[2]) of the problem-major chunk sequence
+ * (the last run shorter).  TQ_ERR_INVALID_ARG on invalid sizes. */
+tq_status tq_decode_split(const tq_format* fmt, int32_t n_layers, int32_t batch, int32_t n_kv_heads,
+                          int32_t n_q_heads, int64_t max_seq_len, int64_t out[5]);
+
 /* Device.  Compresses keys and values and writes them into the cache
  * (QJL deep-dive, section 2; MLX write-up, 背景).  k and v are device arrays
  * [n_layers][n_tokens][n_kv_heads][d] of `dtype` (TQ_DTYPE_F32/BF16/F16) for
@@ -181,9 +191,10 @@ tq_status tq_decode_attention(const tq_format* fmt, const tq_tables* tables, con
  *                        softmax-weighted values (online softmax) in pieces of
  *                        equal size, one partial result per piece and head;
  *   tq_decode_combine  - merges the pieces of each query head and applies Pi^T.
- * Calling them in this order on one stream gives exactly tq_decode_attention's
- * result; the max_seq_len / batch / head arguments must be the same in all
- * three calls. */
+ * Calling them in this order on one stream gives tq_decode_attention's result.
+ * The decode kernel deals token chunks to its waves dynamically, so any two
+ * calls (staged or not) may differ in the last bits.  The max_seq_len / batch
+ * / head arguments must be the same in all three calls. */
 tq_status tq_decode_prepare(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, const float* q,
                             int32_t batch, int32_t n_q_heads, int64_t max_seq_len, void* workspace,
                             size_t workspace_bytes, void* stream);

@@ -333,6 +333,25 @@ tq_status tq_cache_plane_bytes(const tq_format* fmt, int32_t n_layers, int32_t n
   return TQ_OK;
 }
 
+tq_status tq_decode_split(const tq_format* fmt, int32_t n_layers, int32_t batch, int32_t n_kv_heads,
+                          int32_t n_q_heads, int64_t max_seq_len, int64_t out[5]) {
+  using namespace tq;
+  clear_error();
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "out is NULL");
+  tq_status st = check_format(fmt, false);
+  if (st) return st;
+  if (n_layers <= 0 || batch <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads ||
+      max_seq_len < 0)
+    return fail(TQ_ERR_INVALID_ARG, "sizes");
+  const SplitPlan p = plan_decode(fmt->d, n_layers, batch, n_kv_heads, n_q_heads, max_seq_len);
+  out[0] = p.problems;
+  out[1] = p.chunks_per_problem;
+  out[2] = p.chunks_per_wg;
+  out[3] = p.n_workgroups;
+  out[4] = p.seg_max;
+  return TQ_OK;
+}
+
 size_t tq_decode_workspace_bytes(const tq_format* fmt, int32_t n_layers, int32_t batch,
                                  int32_t n_kv_heads, int32_t n_q_heads, int64_t max_seq_len) {
   using namespace tq;

@@ -1955,8 +1955,9 @@ tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq
 #undef TQ_CMP_V
 #undef TQ_CMP
   if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for key bits %d / value bits %d", a.mk, a.bv);
-  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(smem)) != hipSuccess)
-    return fail(TQ_ERR_HIP, "cannot raise the LDS limit to %zu bytes", smem);
+  const hipError_t ae = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+  if (ae != hipSuccess)
+    return fail(TQ_ERR_HIP, "cannot raise the LDS limit to %zu bytes: %s", smem, hipGetErrorString(ae));
   void* args[] = {&a};
   if (hipLaunchKernel(fn, dim3(unsigned(wgs), unsigned(n_layers)), dim3(256), args, smem, hs) != hipSuccess)
     return fail(TQ_ERR_HIP, "compress launch failed: %s", hipGetErrorString(hipGetLastError()));

@@ -46,6 +46,13 @@ CASES = {
     "w5_ragged5": wl.reduced(wl.W5, (100, 0, 333, 64, 1)),
     "g20_k5v1": wl.Workload("g20_k5v1", 1, 2, 40, (257,), 5, 1, "f16", 0.3, 1, 5.0),
     "g1_k2v2": wl.Workload("g1_k2v2", 2, 3, 3, (95, 31), 2, 2, "f32", 0.0, 0, 1.0),
+    # 129 problems: the decode split deals balanced chunk runs that cross from
+    # one problem into the next (two pieces per workgroup)
+    "split_cross_b43": wl.Workload("split_cross_b43", 1, 3, 6, wl.ragged_lengths(42, 600, 1100, seed=3) + (1100,),
+                                   4, 4, "bf16", 0.5, 1, 10.0),
+    # 320 short problems: several groups of pieces per workgroup
+    "many_short_b40": wl.Workload("many_short_b40", 1, 8, 16, wl.ragged_lengths(39, 1, 200, seed=4) + (200,),
+                                  3, 2, "f32", 0.3, 0, 1.0),
 }
 
 

@@ -109,9 +109,12 @@ def round_to_bf16(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even), returned as
     float32 so both sides can upload identical values."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    out = rounded.astype(np.uint32).view(np.float32)
+    u = a.view(np.uint32)
+    # 32-bit arithmetic: only NaN / Inf bit patterns can wrap, and those are
+    # restored below.
+    with np.errstate(over="ignore"):
+        rounded = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)) << np.uint32(16)
+    out = rounded.view(np.float32)
     # Leave NaN/Inf untouched.
     bad = ~np.isfinite(a)
     if bad.any():
