@@ -757,22 +757,34 @@ template <int M, bool HILO> struct Lut {
   static constexpr int WORDS = ENTRIES * ENTRY_WORDS;
 };
 
+// Centroid k of a codebook held one entry per lane (lane l holds entry
+// l mod n, n a power of two): a cross-lane read, so every lane of the wave
+// must be active.
+__device__ __forceinline__ float lane_cent(float cl, int k) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(k << 2, __float_as_int(cl)));
+}
+
+// The table builders below run over whole waves (their trip counts are
+// uniform and a wave with no entry left skips as a unit) because they read the
+// codebook with lane_cent.
 template <int M, bool HILO>
-__device__ __forceinline__ void build_lut(uint32_t* lut, const float* cent, int tid, int nt = 256) {
+__device__ __forceinline__ void build_lut(uint32_t* lut, float cl, int tid, int nt = 256) {
   using L = Lut<M, HILO>;
-  for (int x = tid; x < L::ENTRIES; x += nt) {
+  for (int x0 = 0; x0 < L::ENTRIES; x0 += nt) {
+    if (x0 + (tid & ~63) >= L::ENTRIES) break;
+    const int x = x0 + tid;
 #pragma unroll
     for (int e = 0; e < L::NG; e += 2) {
-      const float c0 = cent[(x >> (e * M)) & ((1 << M) - 1)];
-      const float c1 = cent[(x >> ((e + 1) * M)) & ((1 << M) - 1)];
+      const float c0 = lane_cent(cl, (x >> (e * M)) & ((1 << M) - 1));
+      const float c1 = lane_cent(cl, (x >> ((e + 1) * M)) & ((1 << M) - 1));
       const _Float16 h0 = _Float16(c0), h1 = _Float16(c1);
       uint16_t b0, b1;
       __builtin_memcpy(&b0, &h0, 2);
       __builtin_memcpy(&b1, &h1, 2);
-      lut[x * L::ENTRY_WORDS + e / 2] = uint32_t(b0) | (uint32_t(b1) << 16);
+      if (x < L::ENTRIES) lut[x * L::ENTRY_WORDS + e / 2] = uint32_t(b0) | (uint32_t(b1) << 16);
       if constexpr (HILO) {
         const uint32_t l0 = f16_bits(c0 - float(h0)), l1 = f16_bits(c1 - float(h1));
-        lut[x * L::ENTRY_WORDS + L::NG / 2 + e / 2] = l0 | (l1 << 16);
+        if (x < L::ENTRIES) lut[x * L::ENTRY_WORDS + L::NG / 2 + e / 2] = l0 | (l1 << 16);
       }
     }
   }
@@ -817,9 +829,14 @@ template <int M> struct KLut {
 
 // Pair table: entry x (two codes, x = c0 | c1 << M) = fp16 pair (c0, c1).
 template <int M>
-__device__ __forceinline__ void build_kpairs(uint32_t* phi, const float* cent, int tid, int nt = 256) {
-  for (int x = tid; x < KLut<M>::PAIRS; x += nt)
-    phi[x] = uint32_t(f16_bits(cent[x & ((1 << M) - 1)])) | (uint32_t(f16_bits(cent[x >> M])) << 16);
+__device__ __forceinline__ void build_kpairs(uint32_t* phi, float cl, int tid, int nt = 256) {
+  constexpr int P = KLut<M>::PAIRS;
+  for (int x0 = 0; x0 < P; x0 += nt) {
+    if (x0 + (tid & ~63) >= P) break;
+    const int x = x0 + tid;
+    const float c0 = lane_cent(cl, x & ((1 << M) - 1)), c1 = lane_cent(cl, (x >> M) & ((1 << M) - 1));
+    if (x < P) phi[x] = uint32_t(f16_bits(c0)) | (uint32_t(f16_bits(c1)) << 16);
+  }
 }
 // NC-code table from the pair table (after a barrier): dword k of entry x is
 // the pair of codes 2k, 2k + 1.  Thread t of NT writes entries t + NT u; all
@@ -882,10 +899,10 @@ __device__ __forceinline__ uint32_t slab_bits(const uint32_t (&w)[N], int s) {
 // copy sits at byte e * 256 + 4 l, so the 64 lanes of a lookup always hit 64
 // different banks.  One byte permute forms the address from the code byte and
 // the lane offset.
-__device__ __forceinline__ void build_vrep(uint32_t* lut, const float* cent, int tid, int nt) {
-  for (int x = tid; x < 256 * 16; x += nt) {   // entry x / 16, copies 4 (x % 16) .. + 3
+__device__ __forceinline__ void build_vrep(uint32_t* lut, float cl, int tid, int nt) {
+  for (int x = tid; x < 256 * 16; x += nt) {   // entry x / 16, copies 4 (x % 16) .. + 3 (nt divides 4096)
     const int e = x >> 4;
-    const uint32_t w = uint32_t(f16_bits(cent[e & 15])) | (uint32_t(f16_bits(cent[e >> 4])) << 16);
+    const uint32_t w = uint32_t(f16_bits(lane_cent(cl, e & 15))) | (uint32_t(f16_bits(lane_cent(cl, e >> 4))) << 16);
     *reinterpret_cast<u32x4*>(lut + e * 64 + (x & 15) * 4) = u32x4{w, w, w, w};
   }
 }
@@ -969,15 +986,21 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     int64_t len;         // tokens of the sequence (clamped)
     int layer, b, hk, hg;
   };
-  auto run_of = [&](int prob) {
-    Run r;
+  auto ctx_of = [&](int prob) {
+    Run r{};
     r.hg = prob % a.n_hg;
     r.hk = (prob / a.n_hg) % a.H;
     r.b = (prob / (a.n_hg * a.H)) % a.batch;
     r.layer = prob / (a.n_hg * a.H * a.batch);
-    const int64_t start = a.seq_start[r.b];
-    int64_t len = a.seq_len[r.b];
-    if (start < 0 || (start % kVBlock) != 0 || start >= a.capacity || len < 0) len = 0;
+    return r;
+  };
+  // A sequence with an invalid start gets no tokens and slot 0 as its start,
+  // so that the chunk-0 loads issued for waves without work stay in bounds.
+  auto fill_run = [&](Run r, int64_t start, int64_t len) {
+    if (start < 0 || (start % kVBlock) != 0 || start >= a.capacity || len < 0) {
+      len = 0;
+      start = 0;
+    }
     if (len > a.capacity - start) len = a.capacity - start;
     if (len > a.max_len) len = a.max_len;   // tokens past max_seq_len are ignored
     const int64_t plane = int64_t(r.layer) * a.H + r.hk;
@@ -1002,8 +1025,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     G.has_b = G.a_end < c_last;
     G.b_end = G.has_b ? (G.a_end + cpp < c_last ? G.a_end + cpp : c_last) : G.a_end;
     G.rel_a0 = g0 - G.pa * cpp;
-    G.ra = run_of(G.pa);
-    G.rb = G.has_b ? run_of(G.pa + 1) : G.ra;
+    // both sequences' (start, length) are loaded together
+    const Run ca = ctx_of(G.pa), cb = ctx_of(G.has_b ? G.pa + 1 : G.pa);
+    const int64_t sa = a.seq_start[ca.b], sb = a.seq_start[cb.b];
+    const int64_t la = a.seq_len[ca.b], lb = a.seq_len[cb.b];
+    G.ra = fill_run(ca, sa, la);
+    G.rb = fill_run(cb, sb, lb);
     int live_a = int((G.ra.len + kChunk - 1) / kChunk) - G.rel_a0;
     live_a = live_a < 0 ? 0 : (live_a > G.a_end - g0 ? G.a_end - g0 : live_a);
     int live_b = G.has_b ? int((G.rb.len + kChunk - 1) / kChunk) : 0;
@@ -1023,12 +1050,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   struct QItem {
     float v[2][8];
   };
-  auto stage_load = [&](const Group& G, QItem& Q) {
+  // pa: problem of piece A; piece B is problem pa + 1 when has_b (else A again).
+  auto stage_load = [&](int pa, bool has_b, QItem& Q) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int it = tid + NT * u;
       const int piece = it >> 9, kind = (it >> 8) & 1, s4 = (it >> 6) & 3, l = it & 63;
-      const Run& Rp = piece ? G.rb : G.ra;
+      const Run Rp = ctx_of(pa + (piece && has_b ? 1 : 0));
       const int g_local = Rp.hg * kMaxGroup + (l & 7);
       const int hh = Rp.hk * a.G + (g_local < a.G ? g_local : 0);
       const float4* src = reinterpret_cast<const float4*>(
@@ -1038,12 +1066,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       Q.v[u][4] = x1.x; Q.v[u][5] = x1.y; Q.v[u][6] = x1.z; Q.v[u][7] = x1.w;
     }
   };
-  auto stage_store = [&](const Group& G, const QItem& Q) {
+  auto stage_store = [&](int pa, bool has_b, const QItem& Q) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int it = tid + NT * u;
       const int piece = it >> 9, kind = (it >> 8) & 1, l = it & 63;
-      const Run& Rp = piece ? G.rb : G.ra;
+      const Run Rp = ctx_of(pa + (piece && has_b ? 1 : 0));
       const bool ok = Rp.hg * kMaxGroup + (l & 7) < a.G;
       const float sc = ok ? (kind ? kscale_r : kscale) : 0.f;
       const bool lo = (l & 15) >= 8;
@@ -1417,39 +1445,51 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   // Every group starts with fixed tickets: wave w takes w, w + 8 and w + 16,
   // and counter value base + k is ticket 24 + k (base: the counter value at
   // the start of the group).
+  // Load order: codebooks, then the staged query operands, then the sequence
+  // table, so that the table build below (which needs only the codebooks)
+  // does not wait for the chunk loads that the sequence data unlocks.
+  float kcl = 0.f, vcl = 0.f;   // lane l: key / value centroid l mod (number of centroids)
+  if constexpr (MK > 0) kcl = a.kc[lane & ((1 << MK) - 1)];
+  if constexpr (BV > 0) vcl = a.vc[lane & ((1 << BV) - 1)];
   const int c_first = int(blockIdx.x) * a.chunks_per_wg;
   const int c_last = c_first + a.chunks_per_wg < a.total_chunks ? c_first + a.chunks_per_wg : a.total_chunks;
-  Group G = group_of(c_first, c_last);
   QItem qitem;
-  stage_load(G, qitem);
+  {
+    const int pa = c_first / cpp;
+    stage_load(pa, (pa + 1) * cpp < c_last, qitem);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  Group G = group_of(c_first, c_last);
   KData K0, K1;
   VData V0, V1;
   bool pre = false;   // the first run's K0, K1, V0 are already loaded
   if constexpr (kPrefetch) {
+    // Issued by every wave (no branch, so that the table build below waits
+    // only for the codebook loads); a wave without a ticket reads chunk 0 of
+    // piece A's sequence, which is in bounds and never used.
     const int t0 = wave, t1 = wave + kDecodeWaves;
-    if (t0 < G.n_tickets) {
-      const bool in_a = t0 < G.live_a;
-      const int limit = in_a ? G.live_a : G.n_tickets;
-      const int rel0 = in_a ? G.rel_a0 : -G.live_a;
-      R = in_a ? G.ra : G.rb;
-      load_k(rel0 + t0, K0);
-      load_k(rel0 + (t1 < limit ? t1 : t0), K1);
-      load_v(rel0 + t0, V0);
-      pre = true;
-    }
+    pre = t0 < G.n_tickets;
+    const bool in_a = t0 < G.live_a;
+    const int limit = in_a ? G.live_a : G.n_tickets;
+    const int rel0 = in_a ? G.rel_a0 : -G.live_a;
+    R = (in_a || !pre) ? G.ra : G.rb;
+    const int c0 = pre ? rel0 + t0 : 0, c1 = pre ? rel0 + (t1 < limit ? t1 : t0) : 0;
+    load_k(c0, K0);
+    load_k(c1, K1);
+    load_v(c0, V0);
   }
 
   // ---- tables (built once, used for every chunk of the workgroup)
   if constexpr (MK > 0) {
     if constexpr (KL::NC > 2)
-      build_kpairs<MK>(pair_hi, a.kc, tid, NT);
+      build_kpairs<MK>(pair_hi, kcl, tid, NT);
     else
-      build_kpairs<MK>(lut_k, a.kc, tid, NT);
+      build_kpairs<MK>(lut_k, kcl, tid, NT);
   }
   if constexpr (VREP)
-    build_vrep(lut_v, a.vc, tid, NT);
+    build_vrep(lut_v, vcl, tid, NT);
   else if constexpr (BV > 0)
-    build_lut<BV, false>(lut_v, a.vc, tid, NT);
+    build_lut<BV, false>(lut_v, vcl, tid, NT);
   if constexpr (MK > 0) {
     for (int x = tid; x < 256; x += NT) {
 #pragma unroll
@@ -1460,7 +1500,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       }
     }
   }
-  stage_store(G, qitem);
+  stage_store(G.pa, G.has_b, qitem);
   if (tid == 0) counter[0] = 0;
   __syncthreads();
   if constexpr (MK > 0 && KL::NC > 2) {
@@ -1473,8 +1513,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   for (int g0 = c_first; g0 < c_last;) {
     if (g0 != c_first) {
       G = group_of(g0, c_last);
-      stage_load(G, qitem);
-      stage_store(G, qitem);
+      stage_load(G.pa, G.has_b, qitem);
+      stage_store(G.pa, G.has_b, qitem);
       __syncthreads();
     }
     // the wave's next three tickets (relative to base)
