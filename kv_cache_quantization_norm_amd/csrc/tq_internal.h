@@ -14,7 +14,6 @@ void clear_error();
 
 constexpr int kVBlock = 32;      // slots per value block
 constexpr int kChunk = 32;       // tokens per decode chunk (one wave step)
-constexpr int kWaves = 4;        // waves per compression workgroup
 constexpr int kDecodeWaves = 8;  // waves per decode workgroup (one workgroup per CU)
 constexpr int kDecodeWorkgroups = 256;   // decode workgroups: one per CU of an MI355X
 constexpr int kMaxGroup = 8;     // query heads handled by one decode wave

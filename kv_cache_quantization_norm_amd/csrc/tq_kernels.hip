@@ -44,6 +44,12 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+__device__ __forceinline__ half8 as_half8(u32x4 w) {
+  half8 h;
+  __builtin_memcpy(&h, &w, 16);
+  return h;
+}
+
 __device__ __forceinline__ floatx4 mfma16x16x32(half8 a, half8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -124,7 +130,8 @@ struct CompressArgs {
   int64_t capacity;
   int mk;  // key MSE bits, 0 = fp16 keys
   int bv;  // value bits, 0 = fp16 values
-  int64_t tiles_per_wg;
+  int64_t tiles_per_wg;   // bulk kernel: tiles of the flattened (layer, tile) sequence per workgroup
+  int64_t total_tiles;
   const float* pi;
   const float* pi_s;
   const float* kc;
@@ -143,15 +150,26 @@ struct CompressArgs {
 
 constexpr int kCompressTile = 16;  // tokens per wave step
 
-// Shared memory of the compress kernel: Pi and S Pi^T in MFMA operand order
-// plus per-wave packing scratch.
+// Shared memory of the compress kernel.  Pi and M = S Pi^T are held as fp16
+// A operands of v_mfma_f32_16x16x32_f16, each matrix as its fp16 high part
+// and its remainder scaled by 2^11 (P = hi + 2^-11 lo), in operand order:
+//   ph / pl [(tile * 4 + s) * 64 + lane][e] = Pi[16 tile + lane % 16][32 (lane / 16) + 8 s + e]
+//   mh / ml [(tp * 4 + s) * 64 + lane][e]   = M[16 tp + lane % 16][c(s, lane / 16, e)],
+//     c(s, q, e) = 16 (2 s + e / 4) + 4 q + e % 4.
+// The sketch's contraction order follows the rotation's output layout, so each
+// lane's residual values are already its B operands.  Then the quantisation
+// tables of both codebooks and per-wave packing scratch.
+constexpr int kCompressWaves = 8;
+constexpr int kCompressWorkgroups = 256;   // one per CU
+constexpr int kQBuckets = 512;
 struct CompressSmem {
-  float pi_op[D * D];    // [(tile*32 + s)*64 + q*16 + i] = Pi[16 tile + i][32 q + s]
-  float m_op[D * D];     // [(tile'*32 + tile*4 + r)*64 + q*16 + i] = M[16 tile' + i][16 tile + 4 q + r]
-  float kc[16], kb[16], vc[16], vb[16];
-  uint32_t rec[kWaves][kCompressTile * 16];   // packed key codes per token (<= 16 dwords)
-  uint32_t srec[kWaves][kCompressTile * 4];   // packed signs per token
-  uint32_t vrec[kWaves][D * 2];               // value codes of 16 tokens per coordinate
+  half8 ph[8 * 4 * 64], pl[8 * 4 * 64];
+  half8 mh[8 * 4 * 64], ml[8 * 4 * 64];
+  u32x2 kq[kQBuckets], vq[kQBuckets];
+  float kc[16], vc[16];
+  uint32_t rec[kCompressWaves][kCompressTile * 16];   // packed key codes per token (<= 16 dwords)
+  uint32_t srec[kCompressWaves][kCompressTile * 4];   // packed signs per token
+  uint32_t vrec[kCompressWaves][D * 2];               // value codes of 16 tokens per coordinate
 };
 
 // Lane (t = lane % 16, q = lane / 16) holds coordinates 32q .. 32q+31 of token t.
@@ -194,10 +212,63 @@ __device__ __forceinline__ void load_token_slab(const CompressArgs& a, const voi
   }
 }
 
-// Norm and y = Pi x / ||x|| for the wave's 16 tokens.  On return lane (t, q)
-// holds y[16 tile + 4 q + r] of token t in y[tile][r].
-__device__ __forceinline__ float rotate_tile(const CompressSmem& sm, const float (&xr)[32], int lane,
-                                             float (&y)[8][4]) {
+// Quantisation table of a codebook with nb < 16 ascending boundaries t_k:
+// bucket u covers y in [-1/2 + u / 512, -1/2 + (u + 1) / 512), the first and
+// last buckets extended to -inf and +inf.  Entry u holds the number of
+// boundaries below L_u = -1/2 + (u - 1/2) / 512 and the first boundary at or
+// above L_u if it lies below L_u + 2 / 512 (+inf otherwise).  The rounded
+// bucket arithmetic puts y in a bucket u with y in [L_u, L_u + 2 / 512), so
+// the code #{k : y >= t_k} is count + [y >= boundary] as long as no two
+// boundaries are closer than 2 / 512: those of the d = 128 codebooks lie in
+// (-0.25, 0.25), more than 0.02 apart.
+__device__ __forceinline__ void build_qtab(u32x2* tab, const float* bnd, int nb, int tid, int nt) {
+  for (int u = tid; u < kQBuckets; u += nt) {
+    const float lo = -0.5f + (float(u) - 0.5f) / kQBuckets, hi = lo + 2.f / kQBuckets;
+    uint32_t cnt = 0;
+    float first = INFINITY;
+    for (int k = 0; k < nb; ++k) {
+      const float t = bnd[k];
+      if (t < lo)
+        ++cnt;
+      else if (t < first)
+        first = t;
+    }
+    tab[u] = u32x2{cnt, __float_as_uint(first < hi ? first : INFINITY)};
+  }
+}
+__device__ __forceinline__ uint32_t qcode(float y, const u32x2* tab) {
+  float u = fmaf(y, float(kQBuckets), 0.5f * kQBuckets);
+  u = fminf(fmaxf(u, 0.f), float(kQBuckets - 1));   // NaN -> bucket 0 -> code 0
+  const u32x2 e = tab[int(u)];
+  return e[0] + (y >= __uint_as_float(e[1]) ? 1u : 0u);
+}
+
+// Two floats -> fp16 pair (rounded toward zero), as a dword.
+__device__ __forceinline__ uint32_t pk16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+__device__ __forceinline__ float lo16(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w))); }
+__device__ __forceinline__ float hi16(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w >> 16))); }
+// High parts and remainders (times 2^11) of 8 floats as fp16 operands.
+__device__ __forceinline__ void split8(const float (&v)[8], half8& hi, half8& lo, bool want_lo) {
+  u32x4 h, l = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    h[p] = pk16(v[2 * p], v[2 * p + 1]);
+    if (want_lo) l[p] = pk16((v[2 * p] - lo16(h[p])) * 2048.f, (v[2 * p + 1] - hi16(h[p])) * 2048.f);
+  }
+  hi = as_half8(h);
+  lo = as_half8(l);
+}
+
+// Norm and y = Pi x / ||x|| for the wave's 16 tokens.  Lane (t, q) holds
+// coordinates 32 q .. 32 q + 31 of token t in xr; on return it holds
+// y[16 tile + 4 q + r] of token t in y[tile][r].  The B operand is
+// x' = x 2^e with 2^e ||x|| in [2^14, 2^15), in fp16: exact for bf16 and fp16
+// inputs (their significands fit), a high part plus a remainder (times 2^11)
+// for fp32 inputs (xhl).  a1 collects hi(Pi) hi(x'), a2 the remainder products.
+__device__ __forceinline__ float rotate16(const CompressSmem& sm, const float (&xr)[32], int lane, bool xhl,
+                                          float (&y)[8][4]) {
   float ss = 0.f;
 #pragma unroll
   for (int s = 0; s < 32; ++s) ss = fmaf(xr[s], xr[s], ss);
@@ -206,25 +277,70 @@ __device__ __forceinline__ float rotate_tile(const CompressSmem& sm, const float
   const float n = sqrtf(ss);
   // n = 0 -> y = 0; NaN -> NaN everywhere.
   const float inv = n > 0.f ? 1.0f / n : (n == 0.f ? 0.f : n);
+  const int e = (n > 0.f && n < INFINITY) ? 15 - __builtin_amdgcn_frexp_expf(n) : 0;
+  half8 xh[4], xl[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = __builtin_amdgcn_ldexpf(xr[8 * s + k], e);
+    split8(v, xh[s], xl[s], xhl);
+  }
+  const float sc = __builtin_amdgcn_ldexpf(inv, -e);
 #pragma unroll
   for (int tile = 0; tile < 8; ++tile) {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 32; ++s) acc = mfma16x16x4f32(sm.pi_op[(tile * 32 + s) * 64 + lane], xr[s], acc);
+    for (int s = 0; s < 4; ++s) {
+      const half8 ah = sm.ph[(tile * 4 + s) * 64 + lane], al = sm.pl[(tile * 4 + s) * 64 + lane];
+      a1 = mfma16x16x32(ah, xh[s], a1);
+      a2 = mfma16x16x32(al, xh[s], a2);
+      if (xhl) a2 = mfma16x16x32(ah, xl[s], a2);
+    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) y[tile][r] = acc[r] * inv;
+    for (int r = 0; r < 4; ++r) y[tile][r] = fmaf(a2[r], 0x1p-11f, a1[r]) * sc;
   }
   return n;
 }
 
-template <int NB>
-__device__ __forceinline__ uint32_t quantize(float y, const float* bnd) {
-  uint32_t idx = 0;
+// Stages a 128 x 128 fp32 matrix (row-major) as fp16 high / remainder A
+// operands.  Element (row, col) goes to operand entry ((row / 16) * 4 + s) *
+// 64 + q * 16 + row % 16, half e, with (s, q, e) from col in the rotation's
+// contraction order or (sketch) in the residual order.  512 threads, 8
+// float4 each, all loads issued before the LDS writes.
+__device__ __forceinline__ void stage_operands(half8* hi, half8* lo, const float* src, int tid, bool sketch) {
+  const float4* s4 = reinterpret_cast<const float4*>(src);
+  float4 buf[8];
 #pragma unroll
-  for (int k = 0; k < NB; ++k) idx += (y >= bnd[k]) ? 1u : 0u;
-  return idx;
+  for (int u = 0; u < 8; ++u) buf[u] = s4[tid + 512 * u];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e0 = 4 * (tid + 512 * u), row = e0 >> 7, col = e0 & 127;
+    int s, q, e;
+    if (!sketch) {
+      q = col >> 5;
+      s = (col >> 3) & 3;
+      e = col & 7;
+    } else {
+      const int tc = col >> 4;   // residual tile 2 s + e / 4
+      s = tc >> 1;
+      q = (col >> 2) & 3;
+      e = 4 * (tc & 1);
+    }
+    const int ent = ((row >> 4) * 4 + s) * 64 + q * 16 + (row & 15);
+    const float v[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
+    uint32_t h[2], l[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const _Float16 a = _Float16(v[2 * p]), b = _Float16(v[2 * p + 1]);
+      const _Float16 la = _Float16((v[2 * p] - float(a)) * 2048.f), lb = _Float16((v[2 * p + 1] - float(b)) * 2048.f);
+      h[p] = uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+      l[p] = uint32_t(__builtin_bit_cast(uint16_t, la)) | (uint32_t(__builtin_bit_cast(uint16_t, lb)) << 16);
+    }
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(&hi[ent]) + e) = u32x2{h[0], h[1]};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(&lo[ent]) + e) = u32x2{l[0], l[1]};
+  }
 }
-
 
 // OR the 4 consecutive m-bit codes `chunk` (coordinates 16 tile + 4 q .. +3)
 // into a token record in LDS.
@@ -235,57 +351,42 @@ __device__ __forceinline__ void or_bits(uint32_t* rec, int bitpos, uint32_t chun
 }
 
 template <int MK, int BV>
-__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
+__global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   CompressSmem& sm = *reinterpret_cast<CompressSmem*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = lane & 15, q = lane >> 4;
-  const int layer_rel = blockIdx.y;
-  const int layer = a.layer0 + layer_rel;
   const bool need_rot = MK > 0 || BV > 0;
-
-  // Stage Pi (and M) in operand order; all global loads of a thread are
-  // issued before its LDS writes.
-  if (need_rot) {
-    const float4* src = reinterpret_cast<const float4*>(a.pi + int64_t(layer) * D * D);
-    float4 buf[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) buf[u] = src[tid + 256 * u];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = 4 * (tid + 256 * u), row = e >> 7, col = e & 127;
-      const int tile = row >> 4, i = row & 15, qq = col >> 5, s0 = col & 31;
-      float* dst = &sm.pi_op[(tile * 32 + s0) * 64 + qq * 16 + i];
-      dst[0] = buf[u].x; dst[64] = buf[u].y; dst[128] = buf[u].z; dst[192] = buf[u].w;
-    }
-  }
-  if constexpr (MK > 0) {
-    const float4* src = reinterpret_cast<const float4*>(a.pi_s + int64_t(layer) * D * D);
-    float4 buf[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) buf[u] = src[tid + 256 * u];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = 4 * (tid + 256 * u), row = e >> 7, col = e & 127;
-      const int tp = row >> 4, i = row & 15, tile = col >> 4, qq = (col >> 2) & 3;
-      float* dst = &sm.m_op[(tp * 32 + tile * 4) * 64 + qq * 16 + i];
-      dst[0] = buf[u].x; dst[64] = buf[u].y; dst[128] = buf[u].z; dst[192] = buf[u].w;
-    }
-  }
+  const bool xhl = a.dtype == TQ_DTYPE_F32;   // fp32 inputs need a remainder operand
   if (tid < 16) {
     const int nk = MK > 0 ? (1 << MK) : 0, nv = BV > 0 ? (1 << BV) : 0;
     // Reconstruction values are applied at their stored (fp16) precision.
     sm.kc[tid] = tid < nk ? float(_Float16(a.kc[tid])) : 0.f;
-    sm.kb[tid] = tid + 1 < nk ? a.kb[tid] : INFINITY;
     sm.vc[tid] = tid < nv ? float(_Float16(a.vc[tid])) : 0.f;
-    sm.vb[tid] = tid + 1 < nv ? a.vb[tid] : INFINITY;
   }
+  if constexpr (MK > 0) build_qtab(sm.kq, a.kb, (1 << MK) - 1, tid, kCompressWaves * 64);
+  if constexpr (BV > 0) build_qtab(sm.vq, a.vb, (1 << BV) - 1, tid, kCompressWaves * 64);
   __syncthreads();
 
+  // The workgroup owns tiles [g_lo, g_hi) of the (layer, 16-token tile)
+  // sequence of the call, taken one layer segment at a time: the segment's
+  // Pi and M operands are staged, then its (tile, head) items are dealt round
+  // robin to the waves.
   const int64_t n_tiles = (a.n_tokens + kCompressTile - 1) / kCompressTile;
-  const int64_t tile_lo = int64_t(blockIdx.x) * a.tiles_per_wg;
-  const int64_t tile_hi = tile_lo + a.tiles_per_wg < n_tiles ? tile_lo + a.tiles_per_wg : n_tiles;
-  for (int64_t tl = tile_lo; tl < tile_hi; ++tl) {
+  const int64_t g_lo = int64_t(blockIdx.x) * a.tiles_per_wg;
+  const int64_t g_hi = g_lo + a.tiles_per_wg < a.total_tiles ? g_lo + a.tiles_per_wg : a.total_tiles;
+  for (int64_t g0 = g_lo; g0 < g_hi;) {
+  const int layer_rel = int(g0 / n_tiles);
+  const int layer = a.layer0 + layer_rel;
+  const int64_t g1 = (int64_t(layer_rel) + 1) * n_tiles < g_hi ? (int64_t(layer_rel) + 1) * n_tiles : g_hi;
+  if (g0 != g_lo) __syncthreads();   // every wave is done with the previous layer's operands
+  if (need_rot) stage_operands(sm.ph, sm.pl, a.pi + int64_t(layer) * D * D, tid, false);
+  if constexpr (MK > 0) stage_operands(sm.mh, sm.ml, a.pi_s + int64_t(layer) * D * D, tid, true);
+  __syncthreads();
+  const int64_t n_items = (g1 - g0) * a.H;
+  for (int64_t item = wave; item < n_items; item += kCompressWaves) {
+  const int64_t tl = g0 - int64_t(layer_rel) * n_tiles + item / a.H;
+  const int h = int(item % a.H);
   const int64_t tok0 = tl * kCompressTile;
   const int64_t tok = tok0 + t;
   const bool tok_ok = tok < a.n_tokens;
@@ -302,7 +403,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   uint32_t* vrec = sm.vrec[wave];
   const int kwords = 4 * MK;  // dwords per key code record
 
-  for (int h = wave; h < a.H; h += kWaves) {
+  {
     const int64_t plane = int64_t(layer) * a.H + h;  // [layer][head]
     float xr[32];
     float y[8][4];
@@ -321,7 +422,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
         }
       }
     } else {
-      const float n = rotate_tile(sm, xr, lane, y);
+      const float n = rotate16(sm, xr, lane, xhl, y);
       for (int e = lane; e < kCompressTile * 16; e += 64) rec[e] = 0u;
       srec[lane] = 0u;
       wave_sync();
@@ -332,7 +433,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
         uint32_t chunk = 0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint32_t idx = quantize<(1 << MK) - 1>(y[tile][r], sm.kb);
+          const uint32_t idx = qcode(y[tile][r], sm.kq);
           chunk |= idx << (r * MK);
           res[tile][r] = y[tile][r] - sm.kc[idx];
           a2 = fmaf(res[tile][r], res[tile][r], a2);
@@ -342,18 +443,30 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
       a2 += shfl_xor(a2, 16);
       a2 += shfl_xor(a2, 32);
       const float rnorm = n * sqrtf(a2);
-      // z = M (y - c[idx]); sign of n * z (a zero key gives all ones).
+      // z = M (y - c[idx]); sign of n * z (a zero key gives all ones).  B
+      // operand of step s: res[2 s + e / 4][e % 4] times 2^14, as an fp16
+      // high part and remainder; a1 collects hi(M) hi(res), a2 the rest.
+      half8 rh[4], rl[4];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = res[2 * s4 + (e >> 2)][e & 3] * 16384.f;
+        split8(v, rh[s4], rl[s4], true);
+      }
 #pragma unroll
       for (int tp = 0; tp < 8; ++tp) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int tile = 0; tile < 8; ++tile)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc = mfma16x16x4f32(sm.m_op[(tp * 32 + tile * 4 + r) * 64 + lane], res[tile][r], acc);
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const half8 mh = sm.mh[(tp * 4 + s4) * 64 + lane], ml = sm.ml[(tp * 4 + s4) * 64 + lane];
+          a1 = mfma16x16x32(mh, rh[s4], a1);
+          a2 = mfma16x16x32(mh, rl[s4], a2);
+          a2 = mfma16x16x32(ml, rh[s4], a2);
+        }
         uint32_t bits = 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bits |= (acc[r] * n >= 0.f ? 1u : 0u) << r;
+        for (int r = 0; r < 4; ++r) bits |= (fmaf(a2[r], 0x1p-11f, a1[r]) * n >= 0.f ? 1u : 0u) << r;
         or_bits(srec + t * 4, 16 * tp + 4 * q, bits, 4);
       }
       wave_sync();
@@ -391,13 +504,13 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
         for (int s = 0; s < 32; ++s) dst[(32 * q + s) * kVBlock] = f16_bits(xr[s]);
       }
     } else {
-      const float n = rotate_tile(sm, xr, lane, y);
+      const float n = rotate16(sm, xr, lane, xhl, y);
       if (valid && q == 0) a.v_norm[plane * a.capacity + slot] = n;
       uint32_t vidx[8][4];
 #pragma unroll
       for (int tile = 0; tile < 8; ++tile)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vidx[tile][r] = quantize<(1 << BV) - 1>(y[tile][r], sm.vb);
+        for (int r = 0; r < 4; ++r) vidx[tile][r] = qcode(y[tile][r], sm.vq);
       const int64_t gbytes = 4 * BV;  // bytes per (block, coordinate) group
       uint8_t* vplane = a.v_idx + plane * (a.capacity / kVBlock) * D * gbytes;
       if (contiguous && BV >= 2) {
@@ -442,7 +555,9 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
       }
     }
   }
-  }  // token tiles
+  }  // items
+  g0 = g1;
+  }  // layer segments
 }
 
 // Few-token compression (appends during decode).  The tile kernel above
@@ -788,12 +903,6 @@ __device__ __forceinline__ void build_lut(uint32_t* lut, float cl, int tid, int 
       }
     }
   }
-}
-
-__device__ __forceinline__ half8 as_half8(u32x4 w) {
-  half8 h;
-  __builtin_memcpy(&h, &w, 16);
-  return h;
 }
 
 // 8 consecutive m-bit codes (LSB-first in `bits`) -> 8 fp16 centroids.
@@ -1938,12 +2047,14 @@ tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq
   if (n_tokens == 0 || n_layers == 0) return TQ_OK;
   if (!k || !v) return fail(TQ_ERR_INVALID_ARG, "k or v is NULL");
   const int64_t tiles = (n_tokens + kCompressTile - 1) / kCompressTile;
-  // Several 16-token tiles per workgroup amortise the Pi / S Pi^T staging;
-  // aim at about 1536 workgroups in the call.
-  int64_t tpw = (tiles * n_layers + 1535) / 1536;
-  if (tpw < 1) tpw = 1;
-  const int64_t wgs = (tiles + tpw - 1) / tpw;
-  if (wgs > 0x7FFFFFFF || n_layers > 65535) return fail(TQ_ERR_INVALID_ARG, "too many tokens or layers");
+  // The bulk kernel holds one workgroup per CU (its LDS), so the flattened
+  // (layer, tile) sequence is cut into equal ranges for at most one workgroup
+  // per CU of an MI355X.
+  const int64_t total_tiles = tiles * n_layers;
+  int64_t wgs = total_tiles < kCompressWorkgroups ? total_tiles : kCompressWorkgroups;
+  const int64_t tpw = (total_tiles + wgs - 1) / wgs;
+  wgs = (total_tiles + tpw - 1) / tpw;
+  if (n_layers > 65535) return fail(TQ_ERR_INVALID_ARG, "too many layers");
   CompressArgs a{};
   a.k = k;
   a.v = v;
@@ -1957,6 +2068,7 @@ tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq
   a.mk = fmt->k_bits > 0 ? fmt->k_bits - 1 : 0;
   a.bv = fmt->v_bits;
   a.tiles_per_wg = tpw;
+  a.total_tiles = total_tiles;
   a.pi = tables->pi;
   a.pi_s = tables->pi_s;
   a.kc = tables->k_centroids;
@@ -1999,7 +2111,7 @@ tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq
   if (ae != hipSuccess)
     return fail(TQ_ERR_HIP, "cannot raise the LDS limit to %zu bytes: %s", smem, hipGetErrorString(ae));
   void* args[] = {&a};
-  if (hipLaunchKernel(fn, dim3(unsigned(wgs), unsigned(n_layers)), dim3(256), args, smem, hs) != hipSuccess)
+  if (hipLaunchKernel(fn, dim3(unsigned(wgs)), dim3(kCompressWaves * 64), args, smem, hs) != hipSuccess)
     return fail(TQ_ERR_HIP, "compress launch failed: %s", hipGetErrorString(hipGetLastError()));
   return launch_status("compress");
 }
