@@ -3,10 +3,12 @@
 One step = one pass of the whole path over the dense 28-layer workload
 (28 layers, 4 KV heads, 28 query heads (GQA 7), head_dim 128, batch 1,
 8192 cached tokens, K 4 bits = 3 Lloyd-Max + 1 QJL, V 4 bits MSE-only):
-  1. compress the step's new token (K and V, all 4 KV heads of all 28 layers,
-     one tq_compress_kv call) into slot 8191 of the packed cache;
+  1. compress the step's new token (K and V, all 4 KV heads of all 28 layers)
+     into slot 8191 of the packed cache and prepare the step's queries (one
+     tq_append_prepare call: one launch);
   2. decode attention for all 28 query heads of all 28 layers over the 8192
-     packed tokens (one tq_decode_attention call).
+     packed tokens (tq_decode_partials, tq_decode_combine).
+The same step made of tq_compress_kv + tq_decode_attention is timed beside it.
 Inputs are seeded synthetic bf16 K/V (per-channel log-normal scales, two
 outlier channels per head) already resident in HBM.  The timed loop rotates
 among enough cache copies to exceed twice the 256 MB Infinity Cache, so
@@ -139,6 +141,11 @@ def main():
     out = torch.empty((L, 1, HQ, D), device=dev)
 
     def step(c):
+        tq.tq_append_prepare(fmt, tables, c, k_new, v_new, Q, T, ws, slot0=T - 1, stream=stream)
+        tq.tq_decode_partials(fmt, tables, c, 1, HQ, seq_start, seq_len, T, ws, stream=stream)
+        tq.tq_decode_combine(fmt, tables, c, 1, HQ, T, out, ws, stream=stream)
+
+    def step_two_calls(c):
         tq.tq_compress_kv(fmt, tables, c, k_new, v_new, slot0=T - 1, stream=stream)
         tq.tq_decode_attention(fmt, tables, c, Q, seq_start, seq_len, T, out, ws, stream=stream)
 
@@ -159,7 +166,18 @@ def main():
     wall = time.perf_counter() - wall0
     step_ms = e0.elapsed_time(e1) / args.steps
 
-    # decode call alone (query prep + fused decode/combine kernel), same rotation
+    # the same step as tq_compress_kv + tq_decode_attention (four launches)
+    for i in range(args.warmup):
+        step_two_calls(caches[i % n_copies])
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step_two_calls(caches[i % n_copies])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_two_calls_ms = e0.elapsed_time(e1) / args.steps
+
+    # decode call alone (query prep + decode kernel + combine), same rotation
     for i in range(args.warmup):
         decode_only(caches[i % n_copies])
     torch.cuda.synchronize()
@@ -253,6 +271,8 @@ def main():
         "decode_call": {"us": round(decode_ms * 1e3, 2), "GBs": round(decode_gbs, 1),
                         "bytes": decode_bytes, "kernels": "qprep_kernel + decode_kernel + combine_kernel"},
         "decode_step_bytes": step_bytes,
+        "step_launches": "append_prepare_kernel + decode_kernel + combine_kernel",
+        "step_two_calls_us": round(step_two_calls_ms * 1e3, 2),
         "compress": {"what": f"bulk prefill {T} tokens x {L} layers x {H} KV heads, one call",
                      "ms": round(bulk_ms, 4),
                      "mtokens_per_s_per_kv_head": round(bulk_tokens / (bulk_ms * 1e-3) / 1e6, 2),

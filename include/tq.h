@@ -198,6 +198,23 @@ tq_status tq_decode_attention(const tq_format* fmt, const tq_tables* tables, con
 tq_status tq_decode_prepare(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, const float* q,
                             int32_t batch, int32_t n_q_heads, int64_t max_seq_len, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* Device.  A decode step's append and query preparation in one launch: the
+ * same result as tq_compress_kv(fmt, tables, cache, k, v, dtype, layer0,
+ * n_layers, n_tokens, slots, slot0, stream) followed by
+ * tq_decode_prepare(fmt, tables, cache, q, batch, n_q_heads, max_seq_len,
+ * workspace, workspace_bytes, stream), with their arguments, layouts,
+ * ownership and errors; both are checked before anything is enqueued.  The
+ * new tokens' records (QJL deep-dive, sections 2 and 5) and the sketched
+ * queries (section 6) do not depend on each other, so for fewer than 16
+ * tokens one kernel computes both; for 16 or more tokens the two calls are
+ * made one after the other.  Follow it with tq_decode_partials and
+ * tq_decode_combine on the same workspace. */
+tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                            const void* k, const void* v, int32_t dtype, int32_t layer0, int32_t n_layers,
+                            int64_t n_tokens, const int64_t* slots, int64_t slot0, const float* q, int32_t batch,
+                            int32_t n_q_heads, int64_t max_seq_len, void* workspace, size_t workspace_bytes,
+                            void* stream);
 tq_status tq_decode_partials(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, int32_t batch,
                              int32_t n_q_heads, const int64_t* seq_start, const int32_t* seq_len,
                              int64_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,

@@ -573,8 +573,7 @@ constexpr int kAppendItems = 8;
 constexpr int kAppendStride = D + 4;  // padded LDS rows
 
 template <int MK, int BV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void compress_append_kernel(
-    CompressArgs a) {
+__device__ __forceinline__ void append_body(const CompressArgs& a, int group, int layer_rel) {
   __shared__ __align__(16) float xs[2 * kAppendItems][kAppendStride];  // K items, then V items
   __shared__ __align__(16) float rs[kAppendItems][kAppendStride];      // key residual y - c[idx]
   __shared__ float nrm[2 * kAppendItems];
@@ -586,9 +585,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   constexpr bool ROT = MK > 0 || BV > 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
-  const int layer_rel = blockIdx.y, layer = a.layer0 + layer_rel;
+  const int layer = a.layer0 + layer_rel;
   const int64_t n_items = a.n_tokens * a.H;
-  const int64_t item0 = int64_t(blockIdx.x) * kAppendItems;
+  const int64_t item0 = int64_t(group) * kAppendItems;
   const int ni = n_items - item0 < kAppendItems ? int(n_items - item0) : kAppendItems;
 
   // ---------------- all global loads
@@ -816,6 +815,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
             f16_bits(xs[kAppendItems + it][j]);
     }
   }
+}
+template <int MK, int BV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void compress_append_kernel(
+    CompressArgs a) {
+  append_body<MK, BV>(a, blockIdx.x, blockIdx.y);
 }
 
 // ===========================================================================
@@ -1716,9 +1720,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
 // 16 v + 4 (l / 16) .. + 3 of both are step v's four k-values, the same k on
 // the A and the B side, so the sum over k is exact in any order.
 template <bool ROT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void qprep_kernel(
-    const float* q, const float* pi, const float* s, float* qprep, int batch, int H, int Hq) {
-  const int hk = blockIdx.x >> 2, quarter = blockIdx.x & 3, b = blockIdx.y, layer = blockIdx.z;
+__device__ __forceinline__ void qprep_body(const float* q, const float* pi, const float* s, float* qprep, int batch,
+                                           int H, int Hq, int bx, int b, int layer) {
+  const int hk = bx >> 2, quarter = bx & 3;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = Hq / H;
   const int64_t row0 = (int64_t(layer) * batch + b) * Hq + int64_t(hk) * G;
@@ -1759,6 +1763,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       }
     }
   }
+}
+template <bool ROT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void qprep_kernel(
+    const float* q, const float* pi, const float* s, float* qprep, int batch, int H, int Hq) {
+  qprep_body<ROT>(q, pi, s, qprep, batch, H, Hq, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// The append of a few tokens and the query preparation of the same decode
+// step in one launch (they are independent): workgroups [0, n_append) run
+// the append blocks (item group, layer), the others the query preparation
+// blocks (4 KV head + quarter, sequence, layer).
+template <int MK, int BV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void append_prepare_kernel(
+    CompressArgs a, int app_groups, int n_append, const float* q, const float* pi, const float* s, float* qprep,
+    int batch, int H, int Hq) {
+  const int bid = blockIdx.x;
+  if (bid < n_append) {
+    append_body<MK, BV>(a, bid % app_groups, bid / app_groups);
+    return;
+  }
+  const int r = bid - n_append, nx = H * 4;
+  qprep_body<(MK > 0)>(q, pi, s, qprep, batch, H, Hq, r % nx, (r / nx) % batch, r / (nx * batch));
 }
 
 // Merges the piece partials of one (layer, batch, KV head) for every query
@@ -1931,7 +1957,7 @@ tq_status launch_status(const char* what) {
 
 // Decode stages: prepare the query operands (qprep_kernel), score / accumulate
 // the chunk runs (decode_kernel), merge the pieces (combine_kernel).
-enum { kStagePrepare = 1, kStagePartials = 2, kStageCombine = 4, kStageAll = 7 };
+enum { kStagePrepare = 1, kStagePartials = 2, kStageCombine = 4, kStageAll = 7, kStageCheckOnly = 8 };
 
 template <bool SCORE>
 tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
@@ -1959,6 +1985,7 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
     return fail(TQ_ERR_INVALID_ARG, "too many 32-token chunks in one call");
   if (!workspace || workspace_bytes < plan.total_bytes)
     return fail(TQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, plan.total_bytes);
+  if (stages & kStageCheckOnly) return TQ_OK;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   float* qprep = static_cast<float*>(workspace);
   float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.qprep_bytes);
@@ -2027,14 +2054,13 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
 }  // namespace
 }  // namespace tq
 
-extern "C" {
-
-tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
-                         const void* k, const void* v, int32_t dtype, int32_t layer0,
-                         int32_t n_layers, int64_t n_tokens, const int64_t* slots, int64_t slot0,
-                         void* stream) {
-  using namespace tq;
-  clear_error();
+namespace tq {
+namespace {
+// Checks a compression call and fills its kernel arguments and bulk
+// workgroup count; `nothing` is set when no token or layer is to be written.
+tq_status compress_setup(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, const void* k,
+                         const void* v, int32_t dtype, int32_t layer0, int32_t n_layers, int64_t n_tokens,
+                         const int64_t* slots, int64_t slot0, CompressArgs& a, int64_t& wgs, bool& nothing) {
   tq_status st = check_format(fmt, true);
   if (st) return st;
   if ((st = check_tables(fmt, tables, true))) return st;
@@ -2044,18 +2070,18 @@ tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq
   if (n_tokens < 0 || n_layers < 0 || layer0 < 0 || layer0 + n_layers > cache->n_layers)
     return fail(TQ_ERR_INVALID_ARG, "layers [%d, %d) tokens %lld outside the cache", layer0, layer0 + n_layers,
                 (long long)n_tokens);
-  if (n_tokens == 0 || n_layers == 0) return TQ_OK;
+  nothing = n_tokens == 0 || n_layers == 0;
+  if (nothing) return TQ_OK;
   if (!k || !v) return fail(TQ_ERR_INVALID_ARG, "k or v is NULL");
   const int64_t tiles = (n_tokens + kCompressTile - 1) / kCompressTile;
   // The bulk kernel holds one workgroup per CU (its LDS), so the flattened
   // (layer, tile) sequence is cut into equal ranges for at most one workgroup
   // per CU of an MI355X.
   const int64_t total_tiles = tiles * n_layers;
-  int64_t wgs = total_tiles < kCompressWorkgroups ? total_tiles : kCompressWorkgroups;
+  wgs = total_tiles < kCompressWorkgroups ? total_tiles : kCompressWorkgroups;
   const int64_t tpw = (total_tiles + wgs - 1) / wgs;
   wgs = (total_tiles + tpw - 1) / tpw;
   if (n_layers > 65535) return fail(TQ_ERR_INVALID_ARG, "too many layers");
-  CompressArgs a{};
   a.k = k;
   a.v = v;
   a.dtype = dtype;
@@ -2083,9 +2109,28 @@ tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq
   a.v_idx = cache->v_idx;
   a.v_norm = cache->v_norm;
   a.v_f16 = static_cast<uint16_t*>(cache->v_f16);
+  return TQ_OK;
+}
+}  // namespace
+}  // namespace tq
+
+extern "C" {
+
+tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                         const void* k, const void* v, int32_t dtype, int32_t layer0,
+                         int32_t n_layers, int64_t n_tokens, const int64_t* slots, int64_t slot0,
+                         void* stream) {
+  using namespace tq;
+  clear_error();
+  CompressArgs a{};
+  int64_t wgs = 0;
+  bool nothing = false;
+  tq_status st = compress_setup(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0, a, wgs,
+                                nothing);
+  if (st || nothing) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (n_tokens < kCompressTile) {
-    // Appends: the VALU kernel, 8 (token, head) items per workgroup.
+    // Appends: 8 (token, head) items per workgroup.
     const int64_t groups = (n_tokens * a.H + kAppendItems - 1) / kAppendItems;
 #define TQ_APP(MK_, BV_)                                                                               \
   if (a.mk == MK_ && a.bv == BV_) {                                                                    \
@@ -2114,6 +2159,50 @@ tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq
   if (hipLaunchKernel(fn, dim3(unsigned(wgs)), dim3(kCompressWaves * 64), args, smem, hs) != hipSuccess)
     return fail(TQ_ERR_HIP, "compress launch failed: %s", hipGetErrorString(hipGetLastError()));
   return launch_status("compress");
+}
+
+tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                            const void* k, const void* v, int32_t dtype, int32_t layer0, int32_t n_layers,
+                            int64_t n_tokens, const int64_t* slots, int64_t slot0, const float* q, int32_t batch,
+                            int32_t n_q_heads, int64_t max_seq_len, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  using namespace tq;
+  // Both halves are checked before anything is launched.
+  tq_status st = decode_common<false>(fmt, tables, cache, q, batch, n_q_heads, nullptr, nullptr, max_seq_len, 0.f,
+                                      nullptr, workspace, workspace_bytes, stream, kStagePrepare | kStageCheckOnly);
+  if (st) return st;
+  CompressArgs a{};
+  int64_t wgs = 0;
+  bool nothing = false;
+  if ((st = compress_setup(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0, a, wgs,
+                           nothing)))
+    return st;
+  if (nothing || n_tokens >= kCompressTile) {
+    // Bulk (or no) compression: the two calls one after the other.
+    if (!nothing && (st = tq_compress_kv(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0,
+                                         stream)))
+      return st;
+    return tq_decode_prepare(fmt, tables, cache, q, batch, n_q_heads, max_seq_len, workspace, workspace_bytes,
+                             stream);
+  }
+  const int64_t groups = (n_tokens * a.H + kAppendItems - 1) / kAppendItems;
+  const int64_t n_append = groups * n_layers;
+  const int64_t n_prep = int64_t(cache->n_kv_heads) * 4 * batch * cache->n_layers;
+  if (n_append + n_prep > 0x7FFFFFFF) return fail(TQ_ERR_INVALID_ARG, "too many workgroups");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  float* qprep = static_cast<float*>(workspace);
+  const dim3 grid(unsigned(n_append + n_prep));
+#define TQ_AP(MK_, BV_)                                                                                          \
+  if (a.mk == MK_ && a.bv == BV_) {                                                                              \
+    hipLaunchKernelGGL((append_prepare_kernel<MK_, BV_>), grid, dim3(256), 0, hs, a, int(groups), int(n_append), \
+                       q, tables->pi, tables->s, qprep, batch, cache->n_kv_heads, n_q_heads);                  \
+    return launch_status("append + prepare");                                                                  \
+  }
+#define TQ_AP_V(MK_) TQ_AP(MK_, 0) TQ_AP(MK_, 1) TQ_AP(MK_, 2) TQ_AP(MK_, 4)
+  TQ_AP_V(0) TQ_AP_V(1) TQ_AP_V(2) TQ_AP_V(3) TQ_AP_V(4)
+#undef TQ_AP_V
+#undef TQ_AP
+  return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for key bits %d / value bits %d", a.mk, a.bv);
 }
 
 tq_status tq_decode_attention(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,

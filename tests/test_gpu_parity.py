@@ -282,6 +282,43 @@ def test_overwrite_slot_and_append():
         pu.compare_layer(gpu[layer], c, det, fmt, slots, cbk, cbv)
 
 
+@pytest.mark.parametrize("k_bits,v_bits,dtype,n_new", [(4, 4, "bf16", 1), (3, 2, "f32", 3), (0, 4, "bf16", 1),
+                                                         (5, 1, "f16", 20)])
+def test_append_prepare_matches_separate_calls(k_bits, v_bits, dtype, n_new):
+    """tq_append_prepare leaves the same cache records and workspace, bit for
+    bit, as tq_compress_kv followed by tq_decode_prepare (one kernel for a
+    few tokens, the two calls for 16 or more)."""
+    import kv_cache_quantization_norm_amd as tq
+    _say("append_prepare", k_bits, v_bits, dtype, n_new)
+    L, H, HQ, T = 3, 2, 14, 96
+    tfmt = tq.make_format(128, k_bits, v_bits)
+    tables = tq.Tables.create(tfmt, list(range(L)))
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    g = torch.Generator().manual_seed(11)
+    K = torch.randn(L, T, H, 128, generator=g).to("cuda", tdt)
+    V = torch.randn(L, T, H, 128, generator=g).to("cuda", tdt)
+    kn = torch.randn(L, n_new, H, 128, generator=g).to("cuda", tdt)
+    vn = torch.randn(L, n_new, H, 128, generator=g).to("cuda", tdt)
+    Q = torch.randn(L, 2, HQ, 128, generator=g).cuda()
+    base = tq.Cache.allocate(tfmt, L, H, T)
+    tq.tq_compress_kv(tfmt, tables, base, K, V, slot0=0)
+    copies = [tq.Cache(tfmt, L, H, T, {k: (None if t is None else t.clone()) for k, t in base.planes.items()})
+              for _ in range(2)]
+    ws = [tq.workspace_for(tfmt, base, 2, HQ, T) for _ in range(2)]
+    for w in ws:
+        w.zero_()
+    slot0 = 40
+    tq.tq_compress_kv(tfmt, tables, copies[0], kn, vn, slot0=slot0)
+    tq.tq_decode_prepare(tfmt, tables, copies[0], Q, T, ws[0])
+    tq.tq_append_prepare(tfmt, tables, copies[1], kn, vn, Q, T, ws[1], slot0=slot0)
+    torch.cuda.synchronize()
+    for name, t0 in copies[0].planes.items():
+        if t0 is None:
+            continue
+        assert torch.equal(t0, copies[1].planes[name]), name
+    assert torch.equal(ws[0], ws[1])
+
+
 @pytest.mark.parametrize("short", ["w2", "w4"])
 def test_full_size_sampled(short):
     """Full workload size in the benchmark's launch configuration (every layer in
