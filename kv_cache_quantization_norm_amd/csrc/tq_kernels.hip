@@ -1521,18 +1521,26 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       for (int u = 0; u < 2; ++u) {
         const int g = (tid >> 7) + 4 * u;
         if (g < ng) {
+          // all reads first (no branch between them), then the sums; an
+          // empty wave slot (maximum -inf) contributes nothing, whatever its
+          // accumulator holds
+          float mv[kDecodeWaves], rv[kDecodeWaves], lv[kDecodeWaves];
+#pragma unroll
+          for (int w = 0; w < kDecodeWaves; ++w) {
+            mv[w] = mw[w][g];
+            rv[w] = red[(w * kMaxGroup + g) * D + i];
+            lv[w] = lw[w][g];
+          }
           float M = -INFINITY;
 #pragma unroll
-          for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, mw[w][g]);
+          for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, mv[w]);
           float av = 0.f, ls = 0.f;
 #pragma unroll
           for (int w = 0; w < kDecodeWaves; ++w) {
-            const float mwg = mw[w][g];
-            if (mwg != -INFINITY) {
-              const float f = __builtin_amdgcn_exp2f(mwg - M);
-              av += red[(w * kMaxGroup + g) * D + i] * f;
-              ls += lw[w][g] * f;
-            }
+            const bool live = mv[w] != -INFINITY;
+            const float f = live ? __builtin_amdgcn_exp2f(mv[w] - M) : 0.f;
+            av += (live ? rv[w] : 0.f) * f;
+            ls += (live ? lv[w] : 0.f) * f;
           }
           float* P = a.partial + ((pbase + g) * a.seg_max + seg) * (D + 2);
           P[2 + i] = av;
