@@ -1128,6 +1128,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   // tokens, live_a .. n_tickets - 1 B's.
   struct Group {
     Run ra, rb;
+    int64_t sa, sb, va, vb;   // ticket u's first slot: (u < live_a ? sa : sb) + 32 u; value block likewise + u
     int pa, a_end, b_end, rel_a0, live_a, n_tickets;
     bool has_b;
   };
@@ -1150,8 +1151,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     live_b = live_b > G.b_end - G.a_end ? G.b_end - G.a_end : live_b;
     G.live_a = live_a;
     G.n_tickets = live_a + live_b;
+    G.sa = G.ra.slot_base + int64_t(G.rel_a0) * kChunk;
+    G.sb = G.rb.slot_base - int64_t(live_a) * kChunk;
+    G.va = G.ra.vblk0 + G.rel_a0;
+    G.vb = G.rb.vblk0 - live_a;
     return G;
   };
+
+  // Chunk of ticket u (< n_tickets) of group G: piece A's chunk rel_a0 + u,
+  // or piece B's chunk u - live_a.
+  auto slot_of = [&](const Group& G, int u) -> int64_t { return (u < G.live_a ? G.sa : G.sb) + int64_t(u) * kChunk; };
+  auto vblk_of = [&](const Group& G, int u) -> int64_t { return (u < G.live_a ? G.va : G.vb) + u; };
 
   // ---- staged query operands (MFMA B operands), per piece: columns 0..7 are
   // the group's query heads as fp16 high parts, columns 8..15 the same heads
@@ -1252,9 +1262,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   const uint32_t noff = 4 * (8 * q + (col & 7));
   const uint32_t voff = col * (4 * (BV > 0 ? BV : 1)) + 4 * (BV == 4 ? q : (BV == 2 ? (q >> 1) : 0));
   // rel: chunk index within the problem (tokens 32 rel ..)
-  auto load_k = [&](int rel, KData& K) {
+  // slot0: the chunk's first slot in its (layer, KV head) plane; vblk: its value block.
+  auto load_k = [&](int64_t slot0, KData& K) {
     if constexpr (MK > 0) {
-      const int64_t slot0 = R.slot_base + int64_t(rel) * kChunk;
       const uint8_t* kp = a.k_idx + slot0 * KREC;
       const uint8_t* sp = a.k_sign + slot0 * 16;
 #pragma unroll
@@ -1275,8 +1285,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       }
     }
   };
-  auto load_v = [&](int rel, VData& V) {
-    const int64_t slot0 = R.slot_base + int64_t(rel) * kChunk;
+  auto load_v = [&](int64_t slot0, int64_t vblk, VData& V) {
     if constexpr (MK > 0) {
       const float nk = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.k_norm + slot0) + noff);
       const float nr = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.k_rnorm + slot0) + noff);
@@ -1284,7 +1293,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     }
     if constexpr (BV > 0) {
       V.nrm[1] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.v_norm + slot0) + noff);
-      const uint8_t* vp = a.v_idx + (R.vblk0 + rel) * D * (4 * BV);
+      const uint8_t* vp = a.v_idx + vblk * D * (4 * BV);
 #pragma unroll
       for (int vb = 0; vb < 8; ++vb)
         V.vw[vb] = *reinterpret_cast<const uint32_t*>(vp + voff + 16 * vb * (4 * BV));
@@ -1590,14 +1599,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     // piece A's sequence, which is in bounds and never used.
     const int t0 = wave, t1 = wave + kDecodeWaves;
     pre = t0 < G.n_tickets;
-    const bool in_a = t0 < G.live_a;
-    const int limit = in_a ? G.live_a : G.n_tickets;
-    const int rel0 = in_a ? G.rel_a0 : -G.live_a;
-    R = (in_a || !pre) ? G.ra : G.rb;
-    const int c0 = pre ? rel0 + t0 : 0, c1 = pre ? rel0 + (t1 < limit ? t1 : t0) : 0;
-    load_k(c0, K0);
-    load_k(c1, K1);
-    load_v(c0, V0);
+    const int u1 = t1 < G.n_tickets ? t1 : t0;
+    const int64_t s0 = pre ? slot_of(G, t0) : G.ra.slot_base, s1 = pre ? slot_of(G, u1) : G.ra.slot_base;
+    load_k(s0, K0);
+    load_k(s1, K1);
+    load_v(s0, pre ? vblk_of(G, t0) : G.ra.vblk0, V0);
   }
 
   // ---- tables (built once, used for every chunk of the workgroup)
@@ -1633,6 +1639,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
 #pragma unroll 1
   for (int g0 = c_first; g0 < c_last;) {
     if (g0 != c_first) {
+      pre = false;
       G = group_of(g0, c_last);
       stage_load(G.pa, G.has_b, qitem);
       stage_store(G.pa, G.has_b, qitem);
@@ -1651,44 +1658,62 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
         // Software pipeline: while chunk t0 is attended, chunk t1 is scored and
         // the key data of chunk t2 and the value data of chunk t1 are loaded.
         // Unrolled twice so that the two register sets swap roles without
-        // copies.  A ticket past the run reloads the run's latest chunk (still
-        // in L2), whose copy is scored but never attended.
+        // copies.  Loads follow the tickets across the end of the run into
+        // the group's next piece, so a new run starts with its first chunks
+        // in flight (its first chunk is scored again with its own queries); a
+        // ticket past the group's end reloads the latest chunk (still in
+        // L2), whose copy is scored but never attended.
         const ChunkLate late{};
+        const int n = G.n_tickets;
         floatx4 m0[2], s0[2], m1[2], s1[2];
         if (!pre) {
-          load_k(rel0 + t0, K0);
-          load_k(rel0 + (t1 < limit ? t1 : t0), K1);
-          load_v(rel0 + t0, V0);
+          load_k(slot_of(G, t0), K0);
+          load_k(slot_of(G, t1 < n ? t1 : t0), K1);
+          load_v(slot_of(G, t0), vblk_of(G, t0), V0);
         }
-        pre = false;
         start_run(in_a ? 0 : 1);
         score(K0, late, m0, s0);
+        bool swap = false;
 #pragma unroll 1
         for (;;) {
           const uint32_t d3 = draw();
-          load_k(rel0 + (t2 < limit ? t2 : (t1 < limit ? t1 : t0)), K0);
-          load_v(rel0 + (t1 < limit ? t1 : t0), V1);
+          load_k(slot_of(G, t2 < n ? t2 : (t1 < n ? t1 : t0)), K0);
+          {
+            const int u = t1 < n ? t1 : t0;
+            load_v(slot_of(G, u), vblk_of(G, u), V1);
+          }
           score(K1, late, m1, s1);
           attend(rel0 + t0, V0, late, m0, s0);
           const int t3 = uni(d3) - base;
-          if (t1 >= limit) { t0 = t1; t1 = t2; t2 = t3; break; }
+          if (t1 >= limit) { t0 = t1; t1 = t2; t2 = t3; swap = true; break; }
           const uint32_t d4 = draw();
-          load_k(rel0 + (t3 < limit ? t3 : (t2 < limit ? t2 : t1)), K1);
-          load_v(rel0 + (t2 < limit ? t2 : t1), V0);
+          load_k(slot_of(G, t3 < n ? t3 : (t2 < n ? t2 : t1)), K1);
+          {
+            const int u = t2 < n ? t2 : t1;
+            load_v(slot_of(G, u), vblk_of(G, u), V0);
+          }
           score(K0, late, m0, s0);
           attend(rel0 + t1, V1, late, m1, s1);
           const int t4 = uni(d4) - base;
           if (t2 >= limit) { t0 = t2; t1 = t3; t2 = t4; break; }
           t0 = t2; t1 = t3; t2 = t4;
         }
+        // K0, K1 and V0 now hold the chunks of tickets t0 and t1
+        if (swap) {
+          const KData k = K0;
+          K0 = K1;
+          K1 = k;
+          V0 = V1;
+        }
+        pre = true;
       } else {
         start_run(in_a ? 0 : 1);
 #pragma unroll 1
         while (t0 < limit) {
           const uint32_t d3 = draw();
           ChunkLate late;
-          load_k(rel0 + t0, K0);
-          load_v(rel0 + t0, V0);
+          load_k(slot_of(G, t0), K0);
+          load_v(slot_of(G, t0), vblk_of(G, t0), V0);
           if constexpr (MK == 0 || BV == 0) load_late(rel0 + t0, late);
           floatx4 sm_[2], sq_[2];
           score(K0, late, sm_, sq_);
