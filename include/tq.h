@@ -158,6 +158,21 @@ tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq
                          int32_t n_layers, int64_t n_tokens, const int64_t* slots, int64_t slot0,
                          void* stream);
 
+/* Device.  tq_compress_kv with the bulk kernel (16 or more tokens) held to at
+ * most max_workgroups workgroups, hence CUs (0 means no bound; fewer tokens
+ * use the append kernel as in tq_compress_kv).  For compression that runs in
+ * the background on a second stream while decode calls run on another: the
+ * decode kernel of a call uses tq_decode_split(...)'s n_workgroups CUs, so a
+ * bound of 256 minus that count leaves it its CUs (the MLX write-up, section
+ * on the delegated cache, recompresses its packed store in the background).
+ * Records are the same as tq_compress_kv's, bit for bit.  Arguments,
+ * layouts, ownership and errors as tq_compress_kv; max_workgroups < 0 is
+ * TQ_ERR_INVALID_ARG. */
+tq_status tq_compress_kv_bounded(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                                 const void* k, const void* v, int32_t dtype, int32_t layer0, int32_t n_layers,
+                                 int64_t n_tokens, const int64_t* slots, int64_t slot0, int32_t max_workgroups,
+                                 void* stream);
+
 /* Device.  Single-query decode attention over the packed cache for every
  * layer of the cache (QJL deep-dive, sections 5 and 6): for query head h
  * (KV head h / (n_q_heads / n_kv_heads)), logits

@@ -73,6 +73,7 @@ def _load(path: str = LIB_PATH):
         "tq_decode_workspace_bytes": (SZ, [fmtp, I32, I32, I32, I32, I64]),
         "tq_decode_split": (I32, [fmtp, I32, I32, I32, I32, I64, P]),
         "tq_compress_kv": (I32, [fmtp, tabp, cachep, P, P, I32, I32, I32, I64, P, I64, P]),
+        "tq_compress_kv_bounded": (I32, [fmtp, tabp, cachep, P, P, I32, I32, I32, I64, P, I64, I32, P]),
         "tq_decode_attention": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P, SZ, P]),
         "tq_score": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P, SZ, P]),
         "tq_decode_prepare": (I32, [fmtp, tabp, cachep, P, I32, I32, I64, P, SZ, P]),
@@ -94,6 +95,7 @@ _lib = _load()
 EXPORTED = ("tq_layer_seed", "tq_make_rotations", "tq_make_codebook", "tq_cache_plane_bytes",
             "tq_decode_workspace_bytes", "tq_decode_split", "tq_compress_kv", "tq_decode_attention", "tq_score",
             "tq_decode_prepare", "tq_decode_partials", "tq_decode_combine", "tq_append_prepare",
+            "tq_compress_kv_bounded",
             "tq_status_string", "tq_last_error")
 
 
@@ -282,6 +284,17 @@ def tq_compress_kv(fmt: tq_format, tables: Tables, cache: Cache, k, v, layer0: i
     _check(_lib.tq_compress_kv(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(k), _ptr(v),
                                _dtype_code(k), layer0, n_layers, n_tokens, _ptr(slots), slot0, _stream(stream)),
            "tq_compress_kv")
+
+
+def tq_compress_kv_bounded(fmt: tq_format, tables: Tables, cache: Cache, k, v, max_workgroups: int, layer0: int = 0,
+                           slots=None, slot0: int = 0, stream=None):
+    """tq_compress_kv with the bulk kernel held to at most max_workgroups CUs."""
+    assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape and k.dtype == v.dtype
+    n_layers, n_tokens = int(k.shape[0]), int(k.shape[1])
+    tb, cs = tables.struct(), cache.struct()
+    _check(_lib.tq_compress_kv_bounded(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(k), _ptr(v),
+                                       _dtype_code(k), layer0, n_layers, n_tokens, _ptr(slots), slot0,
+                                       max_workgroups, _stream(stream)), "tq_compress_kv_bounded")
 
 
 def workspace_for(fmt: tq_format, cache: Cache, batch: int, n_q_heads: int, max_seq_len: int, device="cuda"):

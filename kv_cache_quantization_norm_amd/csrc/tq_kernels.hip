@@ -2093,7 +2093,8 @@ namespace {
 // workgroup count; `nothing` is set when no token or layer is to be written.
 tq_status compress_setup(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, const void* k,
                          const void* v, int32_t dtype, int32_t layer0, int32_t n_layers, int64_t n_tokens,
-                         const int64_t* slots, int64_t slot0, CompressArgs& a, int64_t& wgs, bool& nothing) {
+                         const int64_t* slots, int64_t slot0, int32_t max_workgroups, CompressArgs& a, int64_t& wgs,
+                         bool& nothing) {
   tq_status st = check_format(fmt, true);
   if (st) return st;
   if ((st = check_tables(fmt, tables, true))) return st;
@@ -2109,9 +2110,12 @@ tq_status compress_setup(const tq_format* fmt, const tq_tables* tables, const tq
   const int64_t tiles = (n_tokens + kCompressTile - 1) / kCompressTile;
   // The bulk kernel holds one workgroup per CU (its LDS), so the flattened
   // (layer, tile) sequence is cut into equal ranges for at most one workgroup
-  // per CU of an MI355X.
+  // per CU of an MI355X, or fewer when the caller bounds the count.
+  if (max_workgroups < 0) return fail(TQ_ERR_INVALID_ARG, "max_workgroups=%d", max_workgroups);
+  const int64_t cap_wgs = max_workgroups > 0 && max_workgroups < kCompressWorkgroups ? max_workgroups
+                                                                                       : kCompressWorkgroups;
   const int64_t total_tiles = tiles * n_layers;
-  wgs = total_tiles < kCompressWorkgroups ? total_tiles : kCompressWorkgroups;
+  wgs = total_tiles < cap_wgs ? total_tiles : cap_wgs;
   const int64_t tpw = (total_tiles + wgs - 1) / wgs;
   wgs = (total_tiles + tpw - 1) / tpw;
   if (n_layers > 65535) return fail(TQ_ERR_INVALID_ARG, "too many layers");
@@ -2153,13 +2157,21 @@ tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq
                          const void* k, const void* v, int32_t dtype, int32_t layer0,
                          int32_t n_layers, int64_t n_tokens, const int64_t* slots, int64_t slot0,
                          void* stream) {
+  return tq_compress_kv_bounded(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0, 0,
+                                stream);
+}
+
+tq_status tq_compress_kv_bounded(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                                 const void* k, const void* v, int32_t dtype, int32_t layer0, int32_t n_layers,
+                                 int64_t n_tokens, const int64_t* slots, int64_t slot0, int32_t max_workgroups,
+                                 void* stream) {
   using namespace tq;
   clear_error();
   CompressArgs a{};
   int64_t wgs = 0;
   bool nothing = false;
-  tq_status st = compress_setup(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0, a, wgs,
-                                nothing);
+  tq_status st = compress_setup(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0,
+                                max_workgroups, a, wgs, nothing);
   if (st || nothing) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (n_tokens < kCompressTile) {
@@ -2207,7 +2219,7 @@ tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const
   CompressArgs a{};
   int64_t wgs = 0;
   bool nothing = false;
-  if ((st = compress_setup(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0, a, wgs,
+  if ((st = compress_setup(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0, 0, a, wgs,
                            nothing)))
     return st;
   if (nothing || n_tokens >= kCompressTile) {

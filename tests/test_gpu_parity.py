@@ -319,6 +319,51 @@ def test_append_prepare_matches_separate_calls(k_bits, v_bits, dtype, n_new):
     assert torch.equal(ws[0], ws[1])
 
 
+def test_background_recompression_on_second_stream():
+    """Bulk compression on a second stream, concurrent with decode calls on
+    the main stream: the compressed records are bit-identical to a compression
+    made alone, and the decode outputs agree with a decode made alone (to the
+    last bits that the dynamic dealing of chunks may move)."""
+    import kv_cache_quantization_norm_amd as tq
+    _say("background recompression")
+    L, H, HQ, T, P = 2, 2, 14, 320, 600
+    tfmt = tq.make_format(128, 4, 4)
+    tables = tq.Tables.create(tfmt, list(range(L)))
+    g = torch.Generator().manual_seed(5)
+    K = torch.randn(L, T, H, 128, generator=g).to("cuda", torch.bfloat16)
+    V = torch.randn(L, T, H, 128, generator=g).to("cuda", torch.bfloat16)
+    K2 = torch.randn(L, P, H, 128, generator=g).to("cuda", torch.bfloat16)
+    V2 = torch.randn(L, P, H, 128, generator=g).to("cuda", torch.bfloat16)
+    Q = torch.randn(L, 1, HQ, 128, generator=g).cuda()
+    cache = tq.Cache.allocate(tfmt, L, H, T)
+    tq.tq_compress_kv(tfmt, tables, cache, K, V, slot0=0)
+    st = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ln = torch.full((1,), T, dtype=torch.int32, device="cuda")
+    ws = tq.workspace_for(tfmt, cache, 1, HQ, T)
+    ref_out = torch.empty(L, 1, HQ, 128, device="cuda")
+    tq.tq_decode_attention(tfmt, tables, cache, Q, st, ln, T, ref_out, ws)
+    ref_target = tq.Cache.allocate(tfmt, L, H, P + 32 - P % 32)
+    tq.tq_compress_kv(tfmt, tables, ref_target, K2, V2, slot0=0)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    target = tq.Cache.allocate(tfmt, L, H, P + 32 - P % 32)
+    outs = [torch.empty_like(ref_out) for _ in range(4)]
+    main = torch.cuda.current_stream()
+    side.wait_stream(main)
+    # the bulk kernel on the CUs that the decode kernel leaves free
+    free = max(1, 256 - tq.tq_decode_split(tfmt, L, 1, H, HQ, T)["n_workgroups"])
+    tq.tq_compress_kv_bounded(tfmt, tables, target, K2, V2, free, slot0=0, stream=side)
+    for o in outs:
+        tq.tq_decode_attention(tfmt, tables, cache, Q, st, ln, T, o, ws, stream=main)
+    torch.cuda.synchronize()
+    for name, t0 in ref_target.planes.items():
+        if t0 is not None:
+            assert torch.equal(t0, target.planes[name]), name
+    scale = float(ref_out.abs().max())
+    for o in outs:
+        assert float((o - ref_out).abs().max()) <= 1e-5 * scale
+
+
 @pytest.mark.parametrize("short", ["w2", "w4"])
 def test_full_size_sampled(short):
     """Full workload size in the benchmark's launch configuration (every layer in

@@ -125,6 +125,14 @@ def test_device_calls_validate_before_launch():
     assert r("tq_compress_kv", P(fmt), P(tb), P(cs), None, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_INVALID_ARG
     # nothing to do is fine without a GPU
     assert r("tq_compress_kv", P(fmt), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 0, None, 0, None) == tq.TQ_OK
+    # bounded bulk compression: a negative bound is refused, 0 means no bound
+    assert r("tq_compress_kv_bounded", P(fmt), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 64, None, 0, -1, None) == tq.TQ_ERR_INVALID_ARG
+    assert r("tq_compress_kv_bounded", P(fmt), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 0, None, 0, 0, None) == tq.TQ_OK
+    # the fused append + prepare checks the decode half first
+    assert r("tq_append_prepare", P(fmt), P(tb), P(_cache_struct(heads=4)), FAKE, FAKE, 0, 0, 1, 1, None, 0, FAKE,
+             1, 6, 64, FAKE, 1 << 30, None) == tq.TQ_ERR_INVALID_ARG
+    assert r("tq_append_prepare", P(fmt), P(tb), P(_cache_struct(heads=4)), FAKE, FAKE, 0, 0, 1, 1, None, 0, FAKE,
+             1, 8, 64, FAKE, 16, None) == tq.TQ_ERR_WORKSPACE
     # decode: heads not a multiple, too-small workspace
     cs4 = _cache_struct(heads=4)
     assert r("tq_decode_attention", P(fmt), P(tb), P(cs4), FAKE, 1, 6, FAKE, FAKE, 64, 0.0, FAKE, FAKE, 1 << 30, None) == tq.TQ_ERR_INVALID_ARG
