@@ -118,6 +118,43 @@ def decode_attention_rotated(cache: dict, q: np.ndarray, seq_start, seq_len, pi,
     return out
 
 
+def decode_attention_with_tail(cache: dict, tail: dict, q: np.ndarray, seq_start, seq_len, tail_start, tail_len,
+                               pi, s, cb_k, cb_v, scale: float = 0.0):
+    """Decode attention over a sequence held in two parts: its older tokens in
+    the packed cache (slots [seq_start[b], + seq_len[b])) and its recent ones
+    in `tail`, a cache of the fp16 format (slots [tail_start[b],
+    + tail_len[b])), with one softmax over all of them.
+
+    Pages: the MLX write-up (直接构造缓存, 限制) keeps the most recent tokens in
+    full precision and compresses the older ones; the QJL deep-dive (§六) has
+    the same recent-token buffer.  The plain definition: the logits and values
+    of both parts, concatenated (packed tokens first), then the two-pass
+    softmax and the weighted sum, in float64.  q [B][Hq][d] -> [B][Hq][d]."""
+    fmt = cache["fmt"]
+    d = fmt.d
+    assert tail["fmt"].k_bits == 0 and tail["fmt"].v_bits == 0 and tail["fmt"].d == d
+    if scale == 0.0:
+        scale = 1.0 / math.sqrt(d)
+    b_, hq, _ = q.shape
+    hkv = cache["n_kv_heads"]
+    g = hq // hkv
+    out = np.zeros((b_, hq, d))
+    for b in range(b_):
+        slots = np.arange(int(seq_start[b]), int(seq_start[b]) + int(seq_len[b]))
+        tslots = np.arange(int(tail_start[b]), int(tail_start[b]) + int(tail_len[b]))
+        for kvh in range(hkv):
+            kp, vals = quant.dequantize_cache(cache, pi, cb_k, cb_v, kvh, slots)
+            tkp, tvals = quant.dequantize_cache(tail, pi, cb_k, cb_v, kvh, tslots)
+            allv = np.concatenate([vals.reshape(-1, d), tvals.reshape(-1, d)])
+            for h in range(kvh * g, (kvh + 1) * g):
+                if len(allv) == 0:
+                    continue
+                lg = np.concatenate([key_logits(q[b, h], kp, s, scale) if len(slots) else np.zeros(0),
+                                     key_logits(q[b, h], tkp, s, scale) if len(tslots) else np.zeros(0)])
+                out[b, h] = softmax_two_pass(lg) @ allv
+    return out
+
+
 def attention_exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float = 0.0):
     """Textbook softmax(q K^T * scale) V for one query q [d], K, V [T, d]."""
     q = np.asarray(q, np.float64)

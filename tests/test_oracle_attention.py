@@ -130,3 +130,49 @@ def test_gqa_mapping_ragged_batch_and_empty_sequence():
     o3 = attention.decode_attention(c2, q, st, ln, pi, s, cbk, cbv)
     assert np.array_equal(o3[:, :3], out[:, :3])
     assert not np.allclose(o3[0, 3:], out[0, 3:])
+
+
+def _fp16_cache(n_kv, lens, starts, kv_list, pi, s):
+    fmt16 = quant.Format(128, 0, 0)
+    cap = max(32, max((st + (n + 31) // 32 * 32 for st, n in zip(starts, lens)), default=32))
+    tail = quant.empty_cache(fmt16, n_kv, cap)
+    for st, n, (k, v) in zip(starts, lens, kv_list):
+        if n:
+            quant.compress_into(tail, k, v, np.arange(st, st + n), pi, s, None, None)
+    return tail
+
+
+def test_tail_empty_equals_packed_decode():
+    fmt = quant.Format(128, 4, 4)
+    cache, q, st, ln, pi, s, cbk, cbv, _ = _build(fmt, 2, [120, 33], seed=6, g=3)
+    tail = _fp16_cache(2, [0, 0], [0, 0], [], pi, s)
+    a = attention.decode_attention(cache, q, st, ln, pi, s, cbk, cbv)
+    b = attention.decode_attention_with_tail(cache, tail, q, st, ln, [0, 0], [0, 0], pi, s, cbk, cbv)
+    assert np.array_equal(a, b)
+
+
+def test_tail_only_equals_textbook_attention():
+    # no packed tokens: softmax(q K^T / sqrt(d)) V over the fp16 tail
+    fmt = quant.Format(128, 3, 2)
+    cache, q, _, _, pi, s, cbk, cbv, _ = _build(fmt, 2, [40], seed=7, g=2)
+    rs = np.random.default_rng(70)
+    k, v = rs.standard_normal((57, 2, 128)), rs.standard_normal((57, 2, 128))
+    tail = _fp16_cache(2, [57], [0], [(k, v)], pi, s)
+    out = attention.decode_attention_with_tail(cache, tail, q, [0], [0], [0], [57], pi, s, cbk, cbv)
+    for h in range(4):
+        kk = k[:, h // 2].astype(np.float16).astype(np.float64)
+        vv = v[:, h // 2].astype(np.float16).astype(np.float64)
+        assert np.max(np.abs(attention.attention_exact(q[0, h], kk, vv) - out[0, h])) < 1e-12
+
+
+def test_tail_split_equals_one_softmax():
+    # an fp16 sequence split between a cache (older tokens) and a tail (recent
+    # ones) gives the single-cache result: one softmax over the union
+    fmt16 = quant.Format(128, 0, 0)
+    cache, q, st, ln, pi, s, _, _, kv = _build(fmt16, 2, [150], seed=8, g=2)
+    k, v = kv[0]
+    older = _fp16_cache(2, [100], [0], [(k[:100], v[:100])], pi, s)
+    recent = _fp16_cache(2, [50], [32], [(k[100:], v[100:])], pi, s)
+    full = attention.decode_attention(cache, q, st, ln, pi, s, None, None)
+    split = attention.decode_attention_with_tail(older, recent, q, [0], [100], [32], [50], pi, s, None, None)
+    assert np.max(np.abs(full - split)) < 1e-12
