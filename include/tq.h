@@ -194,6 +194,30 @@ tq_status tq_decode_attention(const tq_format* fmt, const tq_tables* tables, con
                               int64_t max_seq_len, float scale, float* out, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Device.  Decode attention over sequences held in two parts: the older
+ * tokens packed in `cache` and the most recent ones kept at full (fp16)
+ * precision in `tail`, a cache of the fp16 format (k_bits = v_bits = 0, same
+ * d, n_layers and n_kv_heads), with one softmax over both (the MLX write-up,
+ * sections on building the cache and on limits, and the QJL deep-dive,
+ * section 6: recent tokens stay uncompressed).  Sequence b holds packed slots
+ * [seq_start[b], + seq_len[b]) of `cache` and tail slots [tail_start[b],
+ * + tail_len[b]) of `tail`; both parts follow tq_decode_attention's rules
+ * (starts a multiple of 32, lengths clamped to the capacity and to
+ * max_seq_len / max_tail_len, misaligned or negative starts empty).  q, out,
+ * scale and the head mapping as in tq_decode_attention.  Tokens enter the
+ * tail with tq_compress_kv on the fp16 format (the values stored as fp16),
+ * and move to the packed cache with tq_compress_kv from those fp16 values.
+ * workspace: at least tq_decode_tail_workspace_bytes(...) bytes. */
+tq_status tq_decode_attention_tail(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                                   const tq_cache* tail, const float* q, int32_t batch, int32_t n_q_heads,
+                                   const int64_t* seq_start, const int32_t* seq_len, int64_t max_seq_len,
+                                   const int64_t* tail_start, const int32_t* tail_len, int64_t max_tail_len,
+                                   float scale, float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host.  Workspace bytes of tq_decode_attention_tail (0 for invalid sizes). */
+size_t tq_decode_tail_workspace_bytes(const tq_format* fmt, int32_t n_layers, int32_t batch, int32_t n_kv_heads,
+                                      int32_t n_q_heads, int64_t max_seq_len, int64_t max_tail_len);
+
 /* Device.  tq_decode_attention in three stages, for callers that schedule
  * them separately (and for timing the kernels one by one).  They take the same
  * arguments as tq_decode_attention and share its workspace, which carries the

@@ -74,6 +74,9 @@ def _load(path: str = LIB_PATH):
         "tq_decode_split": (I32, [fmtp, I32, I32, I32, I32, I64, P]),
         "tq_compress_kv": (I32, [fmtp, tabp, cachep, P, P, I32, I32, I32, I64, P, I64, P]),
         "tq_compress_kv_bounded": (I32, [fmtp, tabp, cachep, P, P, I32, I32, I32, I64, P, I64, I32, P]),
+        "tq_decode_attention_tail": (I32, [fmtp, tabp, cachep, cachep, P, I32, I32, P, P, I64, P, P, I64, F32, P, P,
+                                           SZ, P]),
+        "tq_decode_tail_workspace_bytes": (SZ, [fmtp, I32, I32, I32, I32, I64, I64]),
         "tq_decode_attention": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P, SZ, P]),
         "tq_score": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P, SZ, P]),
         "tq_decode_prepare": (I32, [fmtp, tabp, cachep, P, I32, I32, I64, P, SZ, P]),
@@ -95,7 +98,7 @@ _lib = _load()
 EXPORTED = ("tq_layer_seed", "tq_make_rotations", "tq_make_codebook", "tq_cache_plane_bytes",
             "tq_decode_workspace_bytes", "tq_decode_split", "tq_compress_kv", "tq_decode_attention", "tq_score",
             "tq_decode_prepare", "tq_decode_partials", "tq_decode_combine", "tq_append_prepare",
-            "tq_compress_kv_bounded",
+            "tq_compress_kv_bounded", "tq_decode_attention_tail", "tq_decode_tail_workspace_bytes",
             "tq_status_string", "tq_last_error")
 
 
@@ -336,6 +339,29 @@ def tq_append_prepare(fmt: tq_format, tables: Tables, cache: Cache, k, v, q, max
                                   _dtype_code(k), layer0, n_layers, n_tokens, _ptr(slots), slot0, _ptr(q), batch, hq,
                                   max_seq_len, _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _stream(stream)), "tq_append_prepare")
+
+
+def tail_workspace_for(fmt: tq_format, cache: Cache, batch: int, n_q_heads: int, max_seq_len: int,
+                       max_tail_len: int, device="cuda"):
+    import torch
+    nbytes = int(_lib.tq_decode_tail_workspace_bytes(ctypes.byref(fmt), cache.n_layers, batch, cache.n_kv_heads,
+                                                     n_q_heads, max_seq_len, max_tail_len))
+    if nbytes == 0:
+        raise TQError(TQ_ERR_INVALID_ARG, "tq_decode_tail_workspace_bytes", "invalid sizes")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def tq_decode_attention_tail(fmt: tq_format, tables: Tables, cache: Cache, tail: Cache, q, seq_start, seq_len,
+                             max_seq_len: int, tail_start, tail_len, max_tail_len: int, out, workspace,
+                             scale: float = 0.0, stream=None):
+    """Decode over a packed cache plus an fp16-format tail (one softmax)."""
+    n_layers, batch, hq, d = q.shape
+    tb, cs, ts = tables.struct(), cache.struct(), tail.struct()
+    _check(_lib.tq_decode_attention_tail(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), ctypes.byref(ts),
+                                         _ptr(q), batch, hq, _ptr(seq_start), _ptr(seq_len), max_seq_len,
+                                         _ptr(tail_start), _ptr(tail_len), max_tail_len, scale, _ptr(out),
+                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream(stream)), "tq_decode_attention_tail")
 
 
 def tq_decode_partials(fmt: tq_format, tables: Tables, cache: Cache, batch: int, n_q_heads: int, seq_start, seq_len,

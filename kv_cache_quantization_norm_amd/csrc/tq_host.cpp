@@ -81,6 +81,20 @@ SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_he
   return p;
 }
 
+TailPlan plan_decode_tail(int d, int n_layers, int batch, int n_kv_heads, int n_q_heads, int64_t max_seq_len,
+                          int64_t max_tail_len) {
+  TailPlan t;
+  t.packed = plan_decode(d, n_layers, batch, n_kv_heads, n_q_heads, max_seq_len);
+  t.tail = plan_decode(d, n_layers, batch, n_kv_heads, n_q_heads, max_tail_len);
+  t.seg_total = t.packed.seg_max + t.tail.seg_max;
+  auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
+  t.qplain_offset = t.packed.qprep_bytes;
+  t.partial_offset = 2 * t.packed.qprep_bytes;
+  t.total_bytes =
+      t.partial_offset + align(size_t(n_layers) * batch * n_q_heads * t.seg_total * (d + 2) * sizeof(float));
+  return t;
+}
+
 // ---------------------------------------------------------------------------
 // Seeded normal stream: SplitMix64 (Steele, Lea, Flood 2014) output n of seed
 // s is mix(s + (n+1) * 0x9E3779B97F4A7C15); a uniform is
@@ -359,6 +373,15 @@ size_t tq_decode_workspace_bytes(const tq_format* fmt, int32_t n_layers, int32_t
       n_q_heads <= 0 || n_q_heads % n_kv_heads || max_seq_len < 0)
     return 0;
   return plan_decode(fmt->d, n_layers, batch, n_kv_heads, n_q_heads, max_seq_len).total_bytes;
+}
+
+size_t tq_decode_tail_workspace_bytes(const tq_format* fmt, int32_t n_layers, int32_t batch, int32_t n_kv_heads,
+                                      int32_t n_q_heads, int64_t max_seq_len, int64_t max_tail_len) {
+  using namespace tq;
+  if (check_format(fmt, false) != TQ_OK || n_layers <= 0 || batch <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 ||
+      n_q_heads % n_kv_heads || max_seq_len < 0 || max_tail_len < 0)
+    return 0;
+  return plan_decode_tail(fmt->d, n_layers, batch, n_kv_heads, n_q_heads, max_seq_len, max_tail_len).total_bytes;
 }
 
 const char* tq_status_string(tq_status st) {

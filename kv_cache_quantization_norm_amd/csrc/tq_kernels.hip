@@ -832,6 +832,7 @@ struct DecodeArgs {
   int chunks_per_wg;        // chunks of every workgroup but the last
   int total_chunks;         // problems x chunks_per_problem
   int seg_max;              // partial slots per query head
+  int seg_base;             // first slot of this call's pieces
   const uint8_t* k_idx;
   const uint8_t* k_sign;
   const float* k_norm;
@@ -1551,7 +1552,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
             av += (live ? rv[w] : 0.f) * f;
             ls += (live ? lv[w] : 0.f) * f;
           }
-          float* P = a.partial + ((pbase + g) * a.seg_max + seg) * (D + 2);
+          float* P = a.partial + ((pbase + g) * a.seg_max + a.seg_base + seg) * (D + 2);
           P[2 + i] = av;
           if (i == 0) {
             P[0] = M;
@@ -1832,12 +1833,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 // (two 16-row blocks); its A operands (columns of Pi) are loaded from global
 // memory at the start, before the merge, and res comes from LDS.
 constexpr int kCombineHeads = 16;
+// A second set of pieces, from a decode over an fp16 tail of the same
+// sequences (tail_cpp > 0: its split's chunks per problem and per workgroup),
+// sits in the slots from tail_base on; it joins the same running merge, and
+// since fp16 values accumulate as stored (not rotated) its accumulator is added
+// after Pi^T.
 template <bool ROT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void combine_kernel(
     const float* partial, const float* pi, float* out, int batch, int H, int Hq, int n_hg, int chunks_per_problem,
-    int chunks_per_wg, int seg_max) {
+    int chunks_per_wg, int seg_max, int tail_cpp, int tail_cpw, int tail_base) {
   constexpr bool rotate = ROT;
   __shared__ __align__(16) float res[kCombineHeads][D];
+  __shared__ __align__(16) float resp[ROT ? kCombineHeads : 1][D];   // tail part (stored domain)
   const int hk = blockIdx.x, b = blockIdx.y, layer = blockIdx.z, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, r16 = lane & 15, kq = lane >> 4;
   const int i = tid & 127, half = tid >> 7;
@@ -1857,17 +1864,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   for (int g0 = 0; g0 < G; g0 += kCombineHeads) {
     const int ng = G - g0 < kCombineHeads ? G - g0 : kCombineHeads;
     const int64_t row0 = (int64_t(layer) * batch + b) * Hq + int64_t(hk) * G + g0;
-    float M[NH], L[NH], A[NH];
-    int nseg[NH];   // partial slots written for the head's problem
+    float M[NH], L[NH], A[NH], At[NH];
+    int nseg[NH], nsegt[NH];   // partial slots written for the head's problem (packed part, tail part)
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
       M[k] = -INFINITY;
       L[k] = 0.f;
       A[k] = 0.f;
+      At[k] = 0.f;
       const int g = g0 + (half + 2 * k < ng ? half + 2 * k : ng - 1);
       const int prob = ((layer * batch + b) * H + hk) * n_hg + g / kMaxGroup;
       const int first = prob * chunks_per_problem;
       nseg[k] = (first + chunks_per_problem - 1) / chunks_per_wg - first / chunks_per_wg + 1;
+      const int ft = prob * tail_cpp;
+      nsegt[k] = tail_cpp > 0 ? (ft + tail_cpp - 1) / tail_cpw - ft / tail_cpw + 1 : 0;
     }
     for (int sp0 = 0; sp0 < seg_max; sp0 += SB) {
       float ms[NH][SB], ls[NH][SB], as[NH][SB];
@@ -1902,15 +1912,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         M[k] = Mn;
       }
     }
+    // the tail's pieces (none unless tail_cpp > 0), into At (ROT) or A
+    for (int sp0 = 0; tail_cpp > 0 && sp0 < seg_max - tail_base; sp0 += SB) {
+      float ms[NH][SB], ls[NH][SB], as[NH][SB];
+#pragma unroll
+      for (int k = 0; k < NH; ++k) {
+        const int g = half + 2 * k < ng ? half + 2 * k : ng - 1;
+        const float* P = partial + ((row0 + g) * int64_t(seg_max) + tail_base) * (D + 2);
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const int64_t sp = sp0 + u < nsegt[k] ? sp0 + u : nsegt[k] - 1;
+          ms[k][u] = P[sp * (D + 2)];
+          ls[k][u] = P[sp * (D + 2) + 1];
+          as[k][u] = P[sp * (D + 2) + 2 + i];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NH; ++k) {
+        float Mn = M[k];
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+          if (sp0 + u < nsegt[k]) Mn = fmaxf(Mn, ms[k][u]);
+        const float f0 = M[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[k] - Mn);
+        L[k] *= f0;
+        A[k] *= f0;
+        At[k] *= f0;
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const float f =
+              (sp0 + u >= nsegt[k] || ms[k][u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[k][u] - Mn);
+          L[k] = fmaf(ls[k][u], f, L[k]);
+          if (rotate)
+            At[k] = fmaf(as[k][u], f, At[k]);
+          else
+            A[k] = fmaf(as[k][u], f, A[k]);
+        }
+        M[k] = Mn;
+      }
+    }
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
       const int g = half + 2 * k;
       // L is 0 only for an empty sequence; NaN must propagate.
-      const float v = (L[k] > 0.f || L[k] != L[k]) ? A[k] / L[k] : 0.f;
-      if (rotate)
+      const bool has = L[k] > 0.f || L[k] != L[k];
+      const float v = has ? A[k] / L[k] : 0.f;
+      if (rotate) {
         res[g][i] = g < ng ? v : 0.f;
-      else if (g < ng)
+        resp[g][i] = (g < ng && has) ? At[k] / L[k] : 0.f;
+      } else if (g < ng) {
         out[(row0 + g) * D + i] = v;
+      }
     }
     if constexpr (!ROT) continue;
     __syncthreads();
@@ -1929,7 +1980,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         acc = mfma16x16x4f32(pa[n][4 * v + 3], b4[v].w, acc);
       }
       if (r16 < ng) {
-        float4 o = {acc[0], acc[1], acc[2], acc[3]};
+        const float4 t = *reinterpret_cast<const float4*>(&resp[r16][32 * wave + 16 * n + 4 * kq]);
+        float4 o = {acc[0] + t.x, acc[1] + t.y, acc[2] + t.z, acc[3] + t.w};
         *reinterpret_cast<float4*>(out + (row0 + r16) * D + 32 * wave + 16 * n + 4 * kq) = o;
       }
     }
@@ -1988,6 +2040,44 @@ tq_status launch_status(const char* what) {
   return TQ_OK;
 }
 
+// Kernel arguments of a decode / score call over `cache` with work split
+// `plan` (one slot set: seg_max = plan.seg_max, seg_base = 0).
+DecodeArgs make_args(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, int32_t batch,
+                     int32_t n_q_heads, const int64_t* seq_start, const int32_t* seq_len, int64_t max_seq_len,
+                     float scale, const SplitPlan& plan, const float* qprep, float* partial, float* out) {
+  DecodeArgs a{};
+  a.n_layers = cache->n_layers;
+  a.batch = batch;
+  a.H = cache->n_kv_heads;
+  a.Hq = n_q_heads;
+  a.G = n_q_heads / cache->n_kv_heads;
+  a.n_hg = plan.n_head_groups;
+  a.capacity = cache->capacity;
+  a.chunks_per_problem = int(plan.chunks_per_problem);
+  a.chunks_per_wg = int(plan.chunks_per_wg);
+  a.total_chunks = int(plan.problems * plan.chunks_per_problem);
+  a.seg_max = int(plan.seg_max);
+  a.k_idx = cache->k_idx;
+  a.k_sign = cache->k_sign;
+  a.k_norm = cache->k_norm;
+  a.k_rnorm = cache->k_rnorm;
+  a.k_f16 = static_cast<const uint16_t*>(cache->k_f16);
+  a.v_idx = cache->v_idx;
+  a.v_norm = cache->v_norm;
+  a.v_f16 = static_cast<const uint16_t*>(cache->v_f16);
+  a.qprep = qprep;
+  a.kc = tables->k_centroids;
+  a.vc = tables->v_centroids;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
+  a.partial = partial;
+  a.logits = out;
+  a.max_len = max_seq_len;
+  a.scale = scale != 0.f ? scale : 1.0f / std::sqrt(float(fmt->d));
+  a.kappa = float(std::sqrt(M_PI / 2.0) / fmt->d);
+  return a;
+}
+
 // Decode stages: prepare the query operands (qprep_kernel), score / accumulate
 // the chunk runs (decode_kernel), merge the pieces (combine_kernel).
 enum { kStagePrepare = 1, kStagePartials = 2, kStageCombine = 4, kStageAll = 7, kStageCheckOnly = 8 };
@@ -2036,36 +2126,8 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   }
   if (max_seq_len == 0 && SCORE) return TQ_OK;
 
-  DecodeArgs a{};
-  a.n_layers = cache->n_layers;
-  a.batch = batch;
-  a.H = cache->n_kv_heads;
-  a.Hq = n_q_heads;
-  a.G = n_q_heads / cache->n_kv_heads;
-  a.n_hg = plan.n_head_groups;
-  a.capacity = cache->capacity;
-  a.chunks_per_problem = int(plan.chunks_per_problem);
-  a.chunks_per_wg = int(plan.chunks_per_wg);
-  a.total_chunks = int(plan.problems * plan.chunks_per_problem);
-  a.seg_max = int(plan.seg_max);
-  a.k_idx = cache->k_idx;
-  a.k_sign = cache->k_sign;
-  a.k_norm = cache->k_norm;
-  a.k_rnorm = cache->k_rnorm;
-  a.k_f16 = static_cast<const uint16_t*>(cache->k_f16);
-  a.v_idx = cache->v_idx;
-  a.v_norm = cache->v_norm;
-  a.v_f16 = static_cast<const uint16_t*>(cache->v_f16);
-  a.qprep = qprep;
-  a.kc = tables->k_centroids;
-  a.vc = tables->v_centroids;
-  a.seq_start = seq_start;
-  a.seq_len = seq_len;
-  a.partial = partial;
-  a.logits = out;
-  a.max_len = max_seq_len;
-  a.scale = scale != 0.f ? scale : 1.0f / std::sqrt(float(fmt->d));
-  a.kappa = float(std::sqrt(M_PI / 2.0) / fmt->d);
+  const DecodeArgs a = make_args(fmt, tables, cache, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, plan,
+                                 qprep, partial, out);
   const dim3 grid(unsigned(plan.n_workgroups));
   if (stages & kStagePartials) {
     if ((st = launch_decode<SCORE>(mk, SCORE ? 0 : bv, a, grid, hs))) return st;
@@ -2075,10 +2137,12 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
     const dim3 cgrid(cache->n_kv_heads, batch, cache->n_layers);
     if (bv > 0)
       hipLaunchKernelGGL(combine_kernel<true>, cgrid, dim3(256), 0, hs, partial, tables->pi, out, batch,
-                         cache->n_kv_heads, n_q_heads, a.n_hg, a.chunks_per_problem, a.chunks_per_wg, a.seg_max);
+                         cache->n_kv_heads, n_q_heads, a.n_hg, a.chunks_per_problem, a.chunks_per_wg, a.seg_max, 0, 0,
+                         0);
     else
       hipLaunchKernelGGL(combine_kernel<false>, cgrid, dim3(256), 0, hs, partial, tables->pi, out, batch,
-                         cache->n_kv_heads, n_q_heads, a.n_hg, a.chunks_per_problem, a.chunks_per_wg, a.seg_max);
+                         cache->n_kv_heads, n_q_heads, a.n_hg, a.chunks_per_problem, a.chunks_per_wg, a.seg_max, 0, 0,
+                         0);
     if ((st = launch_status("combine"))) return st;
   }
   return TQ_OK;
@@ -2089,6 +2153,78 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
 
 namespace tq {
 namespace {
+// Decode over a packed cache plus an fp16 tail (see tq_decode_attention_tail):
+// the queries are prepared for both parts, each part runs its decode kernel
+// into its own slots, and the combine merges the two piece sets.
+tq_status decode_tail(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, const tq_cache* tail,
+                      const float* q, int32_t batch, int32_t n_q_heads, const int64_t* seq_start,
+                      const int32_t* seq_len, int64_t max_seq_len, const int64_t* tail_start, const int32_t* tail_len,
+                      int64_t max_tail_len, float scale, float* out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  tq_status st = check_format(fmt, true);
+  if (st) return st;
+  if ((st = check_tables(fmt, tables, false))) return st;
+  if ((st = check_cache(fmt, cache))) return st;
+  const tq_format f16{fmt->d, 0, 0};
+  if (!tail) return fail(TQ_ERR_INVALID_ARG, "tail is NULL");
+  if ((st = check_cache(&f16, tail))) return st;
+  if (tail->n_layers != cache->n_layers || tail->n_kv_heads != cache->n_kv_heads)
+    return fail(TQ_ERR_INVALID_ARG, "tail has %d layers x %d KV heads, the cache %d x %d", tail->n_layers,
+                tail->n_kv_heads, cache->n_layers, cache->n_kv_heads);
+  if (!q || !out) return fail(TQ_ERR_INVALID_ARG, "q or out is NULL");
+  if (!seq_start || !seq_len || !tail_start || !tail_len)
+    return fail(TQ_ERR_INVALID_ARG, "seq_start/seq_len/tail_start/tail_len is NULL");
+  if (batch <= 0 || n_q_heads <= 0 || n_q_heads % cache->n_kv_heads)
+    return fail(TQ_ERR_INVALID_ARG, "batch=%d n_q_heads=%d (must be a positive multiple of n_kv_heads=%d)", batch,
+                n_q_heads, cache->n_kv_heads);
+  if (max_seq_len < 0 || max_tail_len < 0) return fail(TQ_ERR_INVALID_ARG, "max_seq_len or max_tail_len < 0");
+  if (int64_t(cache->n_layers) * batch > 65535) return fail(TQ_ERR_INVALID_ARG, "n_layers * batch exceeds 65535");
+  const TailPlan tp =
+      plan_decode_tail(fmt->d, cache->n_layers, batch, cache->n_kv_heads, n_q_heads, max_seq_len, max_tail_len);
+  if (tp.packed.problems * tp.packed.chunks_per_problem > (int64_t(1) << 30) ||
+      tp.tail.problems * tp.tail.chunks_per_problem > (int64_t(1) << 30))
+    return fail(TQ_ERR_INVALID_ARG, "too many 32-token chunks in one call");
+  if (!workspace || workspace_bytes < tp.total_bytes)
+    return fail(TQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, tp.total_bytes);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* qrot = reinterpret_cast<float*>(ws);
+  float* qplain = reinterpret_cast<float*>(ws + tp.qplain_offset);
+  float* partial = reinterpret_cast<float*>(ws + tp.partial_offset);
+  const int mk = fmt->k_bits > 0 ? fmt->k_bits - 1 : 0;
+  const int bv = fmt->v_bits;
+  const dim3 qgrid(cache->n_kv_heads * 4, batch, cache->n_layers);
+  if (fmt->k_bits > 0)
+    hipLaunchKernelGGL(qprep_kernel<true>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qrot, batch,
+                       cache->n_kv_heads, n_q_heads);
+  else
+    hipLaunchKernelGGL(qprep_kernel<false>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qrot, batch,
+                       cache->n_kv_heads, n_q_heads);
+  hipLaunchKernelGGL(qprep_kernel<false>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qplain, batch,
+                     cache->n_kv_heads, n_q_heads);
+  if ((st = launch_status("qprep"))) return st;
+  DecodeArgs ap = make_args(fmt, tables, cache, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, tp.packed,
+                            qrot, partial, nullptr);
+  ap.seg_max = int(tp.seg_total);
+  if ((st = launch_decode<false>(mk, bv, ap, dim3(unsigned(tp.packed.n_workgroups)), hs))) return st;
+  DecodeArgs at = make_args(&f16, tables, tail, batch, n_q_heads, tail_start, tail_len, max_tail_len, scale,
+                            tp.tail, qplain, partial, nullptr);
+  at.seg_max = int(tp.seg_total);
+  at.seg_base = int(tp.packed.seg_max);
+  if ((st = launch_decode<false>(0, 0, at, dim3(unsigned(tp.tail.n_workgroups)), hs))) return st;
+  if ((st = launch_status("decode"))) return st;
+  const dim3 cgrid(cache->n_kv_heads, batch, cache->n_layers);
+  if (bv > 0)
+    hipLaunchKernelGGL(combine_kernel<true>, cgrid, dim3(256), 0, hs, partial, tables->pi, out, batch,
+                       cache->n_kv_heads, n_q_heads, ap.n_hg, ap.chunks_per_problem, ap.chunks_per_wg,
+                       int(tp.seg_total), at.chunks_per_problem, at.chunks_per_wg, int(tp.packed.seg_max));
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, cgrid, dim3(256), 0, hs, partial, tables->pi, out, batch,
+                       cache->n_kv_heads, n_q_heads, ap.n_hg, ap.chunks_per_problem, ap.chunks_per_wg,
+                       int(tp.seg_total), at.chunks_per_problem, at.chunks_per_wg, int(tp.packed.seg_max));
+  return launch_status("combine");
+}
+
 // Checks a compression call and fills its kernel arguments and bulk
 // workgroup count; `nothing` is set when no token or layer is to be written.
 tq_status compress_setup(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, const void* k,
@@ -2248,6 +2384,16 @@ tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const
 #undef TQ_AP_V
 #undef TQ_AP
   return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for key bits %d / value bits %d", a.mk, a.bv);
+}
+
+tq_status tq_decode_attention_tail(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                                   const tq_cache* tail, const float* q, int32_t batch, int32_t n_q_heads,
+                                   const int64_t* seq_start, const int32_t* seq_len, int64_t max_seq_len,
+                                   const int64_t* tail_start, const int32_t* tail_len, int64_t max_tail_len,
+                                   float scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  tq::clear_error();
+  return tq::decode_tail(fmt, tables, cache, tail, q, batch, n_q_heads, seq_start, seq_len, max_seq_len, tail_start,
+                         tail_len, max_tail_len, scale, out, workspace, workspace_bytes, stream);
 }
 
 tq_status tq_decode_attention(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,

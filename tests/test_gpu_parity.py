@@ -319,6 +319,64 @@ def test_append_prepare_matches_separate_calls(k_bits, v_bits, dtype, n_new):
     assert torch.equal(ws[0], ws[1])
 
 
+@pytest.mark.parametrize("k_bits,v_bits", [(4, 4), (3, 2), (0, 4)])
+def test_decode_with_fp16_tail(k_bits, v_bits):
+    """Decode over a packed cache plus an fp16 tail of recent tokens (one
+    softmax over both parts) against the oracle on the GPU's own caches, for
+    ragged packed and tail lengths including empty parts."""
+    import kv_cache_quantization_norm_amd as tq
+    _say("tail", k_bits, v_bits)
+    L, H, HQ = 2, 2, 14
+    lens, tlens = [300, 0, 97, 64], [40, 12, 0, 33]
+    starts = [0, 320, 320, 448]
+    tstarts = [0, 64, 128, 128]
+    cap, tcap = 512, 192
+    fmt = quant.Format(128, k_bits, v_bits)
+    fmt16 = quant.Format(128, 0, 0)
+    tfmt, tfmt16 = pu.tq_format(fmt), pu.tq_format(fmt16)
+    tables = tq.Tables.create(tfmt, list(range(L)))
+    g = torch.Generator().manual_seed(21)
+    dev = tq.Cache.allocate(tfmt, L, H, cap)
+    tail = tq.Cache.allocate(tfmt16, L, H, tcap)
+    for b in range(4):
+        if lens[b]:
+            k = torch.randn(L, lens[b], H, 128, generator=g).to("cuda", torch.bfloat16)
+            v = torch.randn(L, lens[b], H, 128, generator=g).to("cuda", torch.bfloat16)
+            tq.tq_compress_kv(tfmt, tables, dev, k, v, slot0=starts[b])
+        if tlens[b]:
+            k = torch.randn(L, tlens[b], H, 128, generator=g).to("cuda", torch.bfloat16)
+            v = torch.randn(L, tlens[b], H, 128, generator=g).to("cuda", torch.bfloat16)
+            tq.tq_compress_kv(tfmt16, tables, tail, k, v, slot0=tstarts[b])
+    Q = torch.randn(L, 4, HQ, 128, generator=g).cuda()
+    st = torch.tensor(starts, dtype=torch.int64, device="cuda")
+    ln = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    tst = torch.tensor(tstarts, dtype=torch.int64, device="cuda")
+    tln = torch.tensor(tlens, dtype=torch.int32, device="cuda")
+    ws = tq.tail_workspace_for(tfmt, dev, 4, HQ, max(lens), max(tlens))
+    out = torch.full((L, 4, HQ, 128), float("nan"), device="cuda")
+    tq.tq_decode_attention_tail(tfmt, tables, dev, tail, Q, st, ln, max(lens), tst, tln, max(tlens), out, ws)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    ora, ora_t = pu.download_cache(dev, fmt), pu.download_cache(tail, fmt16)
+    qn = Q.cpu().numpy()
+    worst = 0.0
+    for layer in range(L):
+        pi, s, cbk, cbv = pu.oracle_tables(fmt, layer)
+        ref = attention.decode_attention_with_tail(ora[layer], ora_t[layer], qn[layer], starts, lens, tstarts, tlens,
+                                                   pi, s, cbk, cbv)
+        worst = max(worst, pu.check_outputs(out[layer], ref))
+    _say("tail worst out abs", f"{worst:.2e}")
+    # an empty tail gives tq_decode_attention's result (to the last bits that
+    # the dynamic dealing of chunks may move)
+    zero = torch.zeros(4, dtype=torch.int32, device="cuda")
+    out2 = torch.empty(L, 4, HQ, 128, device="cuda")
+    tq.tq_decode_attention_tail(tfmt, tables, dev, tail, Q, st, ln, max(lens), tst, zero, 0, out2, ws)
+    ref2 = torch.empty_like(out2)
+    tq.tq_decode_attention(tfmt, tables, dev, Q, st, ln, max(lens), ref2, tq.workspace_for(tfmt, dev, 4, HQ, max(lens)))
+    torch.cuda.synchronize()
+    assert float((out2 - ref2).abs().max()) <= 1e-5 * max(1.0, float(ref2.abs().max()))
+
+
 def test_background_recompression_on_second_stream():
     """Bulk compression on a second stream, concurrent with decode calls on
     the main stream: the compressed records are bit-identical to a compression
