@@ -377,6 +377,67 @@ def test_decode_with_fp16_tail(k_bits, v_bits):
     assert float((out2 - ref2).abs().max()) <= 1e-5 * max(1.0, float(ref2.abs().max()))
 
 
+def test_serving_loop_with_fp16_tail_and_trigger():
+    """The recent-token pattern of the pages, step by step: a compressed
+    prefill; each decode step appends its token to an fp16 tail; once the
+    tail holds `trigger` tokens they are compressed into the packed cache
+    (from their fp16 values) and the tail is cleared.  At checkpoints the
+    decode output over packed cache + tail is checked against the oracle on
+    the GPU's caches; at the end the moved tokens' records are checked against
+    the oracle's compression of the same fp16 values."""
+    import kv_cache_quantization_norm_amd as tq
+    _say("serving loop")
+    L, H, HQ, P0, steps, trigger = 2, 2, 14, 200, 150, 64
+    fmt, fmt16 = quant.Format(128, 4, 4), quant.Format(128, 0, 0)
+    tfmt, tfmt16 = pu.tq_format(fmt), pu.tq_format(fmt16)
+    tables = tq.Tables.create(tfmt, list(range(L)))
+    g = torch.Generator().manual_seed(31)
+    K = torch.randn(L, P0 + steps, H, 128, generator=g).to("cuda", torch.float16)
+    V = torch.randn(L, P0 + steps, H, 128, generator=g).to("cuda", torch.float16)
+    Q = torch.randn(L, 1, HQ, 128, generator=g).cuda()
+    packed = tq.Cache.allocate(tfmt, L, H, 512)
+    tail = tq.Cache.allocate(tfmt16, L, H, trigger)
+    tq.tq_compress_kv(tfmt, tables, packed, K[:, :P0].contiguous(), V[:, :P0].contiguous(), slot0=0)
+    n_packed, n_tail = P0, 0
+    zero64 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ws = tq.tail_workspace_for(tfmt, packed, 1, HQ, 512, trigger)
+    out = torch.empty(L, 1, HQ, 128, device="cuda")
+    checks = 0
+    for step in range(steps):
+        tok = P0 + step
+        tq.tq_compress_kv(tfmt16, tables, tail, K[:, tok:tok + 1].contiguous(), V[:, tok:tok + 1].contiguous(),
+                          slot0=n_tail)
+        n_tail += 1
+        if n_tail == trigger:
+            lo = tok + 1 - trigger
+            tq.tq_compress_kv(tfmt, tables, packed, K[:, lo:tok + 1].contiguous(), V[:, lo:tok + 1].contiguous(),
+                              slot0=n_packed)
+            n_packed += trigger
+            n_tail = 0
+        if step % 37 == 0 or step == steps - 1:
+            ln = torch.full((1,), n_packed, dtype=torch.int32, device="cuda")
+            tln = torch.full((1,), n_tail, dtype=torch.int32, device="cuda")
+            tq.tq_decode_attention_tail(tfmt, tables, packed, tail, Q, zero64, ln, 512, zero64, tln, trigger, out, ws)
+            torch.cuda.synchronize()
+            ora, ora_t = pu.download_cache(packed, fmt), pu.download_cache(tail, fmt16)
+            for layer in range(L):
+                pi, s, cbk, cbv = pu.oracle_tables(fmt, layer)
+                ref = attention.decode_attention_with_tail(ora[layer], ora_t[layer], Q[layer].cpu().numpy(), [0],
+                                                           [n_packed], [0], [n_tail], pi, s, cbk, cbv)
+                pu.check_outputs(out[layer].cpu().numpy(), ref)
+            checks += 1
+    assert n_packed == P0 + 2 * trigger and checks >= 4
+    # the moved tokens against the oracle's compression of the same fp16 values
+    moved = np.arange(P0, n_packed)
+    gpu = pu.download_cache(packed, fmt)
+    kh, vh = K.cpu().numpy().astype(np.float64), V.cpu().numpy().astype(np.float64)
+    for layer in range(L):
+        pi, s, cbk, cbv = pu.oracle_tables(fmt, layer)
+        ora = quant.empty_cache(fmt, H, 512)
+        det = quant.compress_into(ora, kh[layer, P0:n_packed], vh[layer, P0:n_packed], moved, pi, s, cbk, cbv)
+        pu.compare_layer(gpu[layer], ora, det, fmt, moved, cbk, cbv)
+
+
 def test_background_recompression_on_second_stream():
     """Bulk compression on a second stream, concurrent with decode calls on
     the main stream: the compressed records are bit-identical to a compression
