@@ -269,6 +269,28 @@ def main():
     bnd_steps_ms, bnd_compress_ms, bnd_wall_ms = overlapped(free_cus, n_bnd)
     del target
 
+    # ---------------- decode over the packed cache plus an fp16 tail of 255
+    # recent tokens (the largest tail under a 256-token compression trigger)
+    TT = 255
+    fmt16 = tq.make_format(D, 0, 0)
+    tail = tq.Cache.allocate(fmt16, L, H, 256, dev)
+    tq.tq_compress_kv(fmt16, tables, tail, K[:, :TT].contiguous(), V[:, :TT].contiguous(), slot0=0)
+    tst = torch.zeros(1, dtype=torch.int64, device=dev)
+    tln = torch.full((1,), TT, dtype=torch.int32, device=dev)
+    tws = tq.tail_workspace_for(fmt, base, 1, HQ, T, TT, dev)
+    for i in range(args.warmup):
+        tq.tq_decode_attention_tail(fmt, tables, caches[i % n_copies], tail, Q, seq_start, seq_len, T, tst, tln, TT,
+                                    out, tws, stream=stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        tq.tq_decode_attention_tail(fmt, tables, caches[i % n_copies], tail, Q, seq_start, seq_len, T, tst, tln, TT,
+                                    out, tws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    tail_ms = e0.elapsed_time(e1) / args.steps
+    del tail, tws
+
     per_layer_ms = None
     if args.per_layer:
         per_layer_ms = time_per_layer(tq, fmt, tables, base, Q, seq_start, seq_len, T, stream, dev)
@@ -325,6 +347,9 @@ def main():
                      "ms": round(bulk_ms, 4),
                      "mtokens_per_s_per_kv_head": round(bulk_tokens / (bulk_ms * 1e-3) / 1e6, 2),
                      "mtoken_heads_per_s": round(bulk_tokens * H / (bulk_ms * 1e-3) / 1e6, 2)},
+        "decode_with_tail": {"tail_tokens": TT, "packed_tokens": T, "us": round(tail_ms * 1e3, 2),
+                             "decode_call_us": round(decode_ms * 1e3, 2),
+                             "kernels": "qprep_kernel x 2 + decode_kernel (packed) + decode_kernel (fp16 tail) + combine_kernel"},
         "background_recompress": {
             "what": f"bulk compress of the {L} x {T}-token prefill on a second stream while decode steps run",
             "decode_steps": n_ov, "step_us_alone": round(step_ms * 1e3, 2),
