@@ -238,6 +238,14 @@ tq_status tq_decode_prepare(const tq_format* fmt, const tq_tables* tables, const
                             int32_t batch, int32_t n_q_heads, int64_t max_seq_len, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+tq_status tq_decode_partials(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, int32_t batch,
+                             int32_t n_q_heads, const int64_t* seq_start, const int32_t* seq_len,
+                             int64_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
+                             void* stream);
+tq_status tq_decode_combine(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, int32_t batch,
+                            int32_t n_q_heads, int64_t max_seq_len, float* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Device.  A decode step's append and query preparation in one launch: the
  * same result as tq_compress_kv(fmt, tables, cache, k, v, dtype, layer0,
  * n_layers, n_tokens, slots, slot0, stream) followed by
@@ -254,19 +262,19 @@ tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const
                             int64_t n_tokens, const int64_t* slots, int64_t slot0, const float* q, int32_t batch,
                             int32_t n_q_heads, int64_t max_seq_len, void* workspace, size_t workspace_bytes,
                             void* stream);
-tq_status tq_decode_partials(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, int32_t batch,
-                             int32_t n_q_heads, const int64_t* seq_start, const int32_t* seq_len,
-                             int64_t max_seq_len, float scale, void* workspace, size_t workspace_bytes,
-                             void* stream);
-tq_status tq_decode_combine(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, int32_t batch,
-                            int32_t n_q_heads, int64_t max_seq_len, float* out, void* workspace,
-                            size_t workspace_bytes, void* stream);
 
 /* Device.  The scoring half of tq_decode_attention alone (the pages' separate
  * MSE-score and QJL-score kernels, QJL deep-dive section 6): writes the
  * logits l_t defined above to logits[n_layers][batch][n_q_heads][max_seq_len]
  * (device float; entries at t >= seq_len[b] are left untouched).  Same
- * arguments and workspace as tq_decode_attention. */
+ * arguments and workspace as tq_decode_attention.
+ *
+ * Several queries per sequence (a prefill chunk scored against the cache):
+ * pass n_q query rows per head as n_q_heads * n_q heads, query j of head h at
+ * index h * n_q + j (q viewed as [n_layers][batch][n_q_heads][n_q][d]); head
+ * index / (n_q_heads * n_q / n_kv_heads) is still the KV head, so the logits
+ * (and tq_decode_attention's outputs) come out as [..][n_q_heads][n_q][..].
+ * The kernels take up to 8 such rows per pass over a KV head's codes. */
 tq_status tq_score(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
                    const float* q, int32_t batch, int32_t n_q_heads, const int64_t* seq_start,
                    const int32_t* seq_len, int64_t max_seq_len, float scale, float* logits,

@@ -438,6 +438,52 @@ def test_serving_loop_with_fp16_tail_and_trigger():
         pu.compare_layer(gpu[layer], ora, det, fmt, moved, cbk, cbv)
 
 
+def test_multi_query_scoring_as_query_rows():
+    """Several queries per sequence (a prefill chunk scored against the cache)
+    passed as n_q_heads * n_q query rows: logits and outputs against the
+    oracle (which maps rows to KV heads the same way), and each query row
+    equal to a single-query call (to the last bits of the dynamic dealing)."""
+    import kv_cache_quantization_norm_amd as tq
+    _say("multi-query")
+    L, H, HQ, NQ = 2, 2, 14, 5
+    lens, starts, cap = [300, 97], [0, 320], 448
+    fmt = quant.Format(128, 4, 2)
+    tfmt = pu.tq_format(fmt)
+    tables = tq.Tables.create(tfmt, list(range(L)))
+    g = torch.Generator().manual_seed(41)
+    dev = tq.Cache.allocate(tfmt, L, H, cap)
+    for b in range(2):
+        k = torch.randn(L, lens[b], H, 128, generator=g).to("cuda", torch.bfloat16)
+        v = torch.randn(L, lens[b], H, 128, generator=g).to("cuda", torch.bfloat16)
+        tq.tq_compress_kv(tfmt, tables, dev, k, v, slot0=starts[b])
+    Q5 = torch.randn(L, 2, HQ, NQ, 128, generator=g).cuda()
+    Qr = Q5.reshape(L, 2, HQ * NQ, 128)
+    st = torch.tensor(starts, dtype=torch.int64, device="cuda")
+    ln = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    T = max(lens)
+    ws = tq.workspace_for(tfmt, dev, 2, HQ * NQ, T)
+    out = torch.empty(L, 2, HQ * NQ, 128, device="cuda")
+    logits = torch.full((L, 2, HQ * NQ, T), float("nan"), device="cuda")
+    tq.tq_decode_attention(tfmt, tables, dev, Qr, st, ln, T, out, ws)
+    tq.tq_score(tfmt, tables, dev, Qr, st, ln, T, logits, ws)
+    torch.cuda.synchronize()
+    ora = pu.download_cache(dev, fmt)
+    qn, on, lg = Qr.cpu().numpy(), out.cpu().numpy(), logits.cpu().numpy()
+    for layer in range(L):
+        pi, s, cbk, cbv = pu.oracle_tables(fmt, layer)
+        ref, ref_logits = attention.decode_attention(ora[layer], qn[layer], starts, lens, pi, s, cbk, cbv,
+                                                     return_logits=True)
+        pu.check_logits(lg[layer], ref_logits, lens, HQ * NQ)
+        pu.check_outputs(on[layer], ref)
+    ws1 = tq.workspace_for(tfmt, dev, 2, HQ, T)
+    o1 = torch.empty(L, 2, HQ, 128, device="cuda")
+    for j in range(NQ):
+        tq.tq_decode_attention(tfmt, tables, dev, Q5[:, :, :, j].contiguous(), st, ln, T, o1, ws1)
+        torch.cuda.synchronize()
+        oj = out.reshape(L, 2, HQ, NQ, 128)[:, :, :, j]
+        assert float((oj - o1).abs().max()) <= 1e-5 * max(1.0, float(o1.abs().max()))
+
+
 def test_background_recompression_on_second_stream():
     """Bulk compression on a second stream, concurrent with decode calls on
     the main stream: the compressed records are bit-identical to a compression
