@@ -266,8 +266,9 @@ __device__ __forceinline__ void split8(const float (&v)[8], half8& hi, half8& lo
 // y[16 tile + 4 q + r] of token t in y[tile][r].  The B operand is
 // x' = x 2^e with 2^e ||x|| in [2^14, 2^15), in fp16: exact for bf16 and fp16
 // inputs (their significands fit), a high part plus a remainder (times 2^11)
-// for fp32 inputs (xhl).  a1 collects hi(Pi) hi(x'), a2 the remainder products.
-__device__ __forceinline__ float rotate16(const CompressSmem& sm, const float (&xr)[32], int lane, bool xhl,
+// for fp32 inputs (XHL).  a1 collects hi(Pi) hi(x'), a2 the remainder products.
+template <bool XHL>
+__device__ __forceinline__ float rotate16(const CompressSmem& sm, const float (&xr)[32], int lane,
                                           float (&y)[8][4]) {
   float ss = 0.f;
 #pragma unroll
@@ -284,7 +285,7 @@ __device__ __forceinline__ float rotate16(const CompressSmem& sm, const float (&
     float v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = __builtin_amdgcn_ldexpf(xr[8 * s + k], e);
-    split8(v, xh[s], xl[s], xhl);
+    split8(v, xh[s], xl[s], XHL);
   }
   const float sc = __builtin_amdgcn_ldexpf(inv, -e);
 #pragma unroll
@@ -295,7 +296,7 @@ __device__ __forceinline__ float rotate16(const CompressSmem& sm, const float (&
       const half8 ah = sm.ph[(tile * 4 + s) * 64 + lane], al = sm.pl[(tile * 4 + s) * 64 + lane];
       a1 = mfma16x16x32(ah, xh[s], a1);
       a2 = mfma16x16x32(al, xh[s], a2);
-      if (xhl) a2 = mfma16x16x32(ah, xl[s], a2);
+      if constexpr (XHL) a2 = mfma16x16x32(ah, xl[s], a2);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) y[tile][r] = fmaf(a2[r], 0x1p-11f, a1[r]) * sc;
@@ -350,14 +351,15 @@ __device__ __forceinline__ void or_bits(uint32_t* rec, int bitpos, uint32_t chun
   if (sh + nbits > 32) atomicOr(&rec[w + 1], chunk >> (32 - sh));
 }
 
-template <int MK, int BV>
+// XHL: fp32 inputs, whose slabs need a remainder operand (bf16 / fp16 inputs
+// are exact fp16 operands).
+template <int MK, int BV, bool XHL>
 __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   CompressSmem& sm = *reinterpret_cast<CompressSmem*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = lane & 15, q = lane >> 4;
   const bool need_rot = MK > 0 || BV > 0;
-  const bool xhl = a.dtype == TQ_DTYPE_F32;   // fp32 inputs need a remainder operand
   if (tid < 16) {
     const int nk = MK > 0 ? (1 << MK) : 0, nv = BV > 0 ? (1 << BV) : 0;
     // Reconstruction values are applied at their stored (fp16) precision.
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressA
         }
       }
     } else {
-      const float n = rotate16(sm, xr, lane, xhl, y);
+      const float n = rotate16<XHL>(sm, xr, lane, y);
       for (int e = lane; e < kCompressTile * 16; e += 64) rec[e] = 0u;
       srec[lane] = 0u;
       wave_sync();
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressA
         for (int s = 0; s < 32; ++s) dst[(32 * q + s) * kVBlock] = f16_bits(xr[s]);
       }
     } else {
-      const float n = rotate16(sm, xr, lane, xhl, y);
+      const float n = rotate16<XHL>(sm, xr, lane, y);
       if (valid && q == 0) a.v_norm[plane * a.capacity + slot] = n;
       uint32_t vidx[8][4];
 #pragma unroll
@@ -2327,7 +2329,10 @@ tq_status tq_compress_kv_bounded(const tq_format* fmt, const tq_tables* tables, 
   }
   const size_t smem = sizeof(CompressSmem);
   const void* fn = nullptr;
-#define TQ_CMP(MK_, BV_) if (a.mk == MK_ && a.bv == BV_) fn = reinterpret_cast<const void*>(compress_kernel<MK_, BV_>);
+#define TQ_CMP(MK_, BV_)                                                                            \
+  if (a.mk == MK_ && a.bv == BV_)                                                                   \
+    fn = a.dtype == TQ_DTYPE_F32 ? reinterpret_cast<const void*>(compress_kernel<MK_, BV_, true>)   \
+                                 : reinterpret_cast<const void*>(compress_kernel<MK_, BV_, false>);
 #define TQ_CMP_V(MK_) TQ_CMP(MK_, 0) TQ_CMP(MK_, 1) TQ_CMP(MK_, 2) TQ_CMP(MK_, 4)
   TQ_CMP_V(0) TQ_CMP_V(1) TQ_CMP_V(2) TQ_CMP_V(3) TQ_CMP_V(4)
 #undef TQ_CMP_V
