@@ -568,10 +568,15 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressA
 // almost all waste.  Here one workgroup takes up to 8 (token, head) items of
 // one layer, flattened as item = token * H + head, and the MFMA columns are
 // the items' vectors: 8 keys and 8 values for the rotation, the 8 key
-// residuals for the sketch.  Wave w owns rows 32 w .. 32 w + 31 (two 16-row
-// blocks) of every product and reads its A operands (rows of Pi and S Pi^T)
-// straight from global memory; all global loads are issued at the start.
+// residuals for the sketch.  Wave w owns rows 16 w .. 16 w + 15 of every
+// product; its A operands (those rows of Pi and S Pi^T) come straight from
+// global memory, all global loads issued at the start, and are split in
+// registers into fp16 high parts and remainders (times 2^11) for
+// v_mfma_f32_16x16x32_f16, as in the tile kernel; the k order of step s is
+// columns 32 q + 8 s + e (lane q = lane / 16).
 constexpr int kAppendItems = 8;
+constexpr int kAppendWaves = 8;
+constexpr int kAppendThreads = kAppendWaves * 64;
 constexpr int kAppendStride = D + 4;  // padded LDS rows
 
 template <int MK, int BV>
@@ -586,57 +591,54 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
   __shared__ float cb[4][16];  // key centroids, key boundaries, value centroids, value boundaries
   constexpr bool ROT = MK > 0 || BV > 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r16 = lane & 15, kq = lane >> 4;
+  const int col = lane & 15, q = lane >> 4;
   const int layer = a.layer0 + layer_rel;
   const int64_t n_items = a.n_tokens * a.H;
   const int64_t item0 = int64_t(group) * kAppendItems;
   const int ni = n_items - item0 < kAppendItems ? int(n_items - item0) : kAppendItems;
 
   // ---------------- all global loads
-  // A operands, block n: row 32 wave + 16 n + r16, step v: columns 16 v + 4 kq .. + 3.
-  float4 ap[ROT ? 2 : 1][8], am[MK > 0 ? 2 : 1][8];
+  // A operands: row 16 wave + col, columns 32 q .. 32 q + 31 (step s: float4s 2 s, 2 s + 1).
+  float4 pa[ROT ? 8 : 1], ma[MK > 0 ? 8 : 1];
   if constexpr (ROT) {
+    const float4* src =
+        reinterpret_cast<const float4*>(a.pi + int64_t(layer) * D * D + int64_t(16 * wave + col) * D + 32 * q);
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const float4* src = reinterpret_cast<const float4*>(a.pi + int64_t(layer) * D * D +
-                                                          int64_t(32 * wave + 16 * n + r16) * D + 4 * kq);
-#pragma unroll
-      for (int v = 0; v < 8; ++v) ap[n][v] = src[4 * v];
-    }
+    for (int v = 0; v < 8; ++v) pa[v] = src[v];
   }
   if constexpr (MK > 0) {
+    const float4* src =
+        reinterpret_cast<const float4*>(a.pi_s + int64_t(layer) * D * D + int64_t(16 * wave + col) * D + 32 * q);
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const float4* src = reinterpret_cast<const float4*>(a.pi_s + int64_t(layer) * D * D +
-                                                          int64_t(32 * wave + 16 * n + r16) * D + 4 * kq);
-#pragma unroll
-      for (int v = 0; v < 8; ++v) am[n][v] = src[4 * v];
-    }
+    for (int v = 0; v < 8; ++v) ma[v] = src[v];
   }
-  float xin[8];
+  // Item vectors: thread value u is element e = tid + 512 u of the 16 x 128
+  // (keys, then values) block.
+  constexpr int XU = 2 * kAppendItems * D / kAppendThreads;
+  float xin[XU];
   {
-    int64_t offs[8];
+    int64_t offs[XU];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = tid + 256 * u, c = e >> 7, j = e & 127;
+    for (int u = 0; u < XU; ++u) {
+      const int e = tid + kAppendThreads * u, c = e >> 7, j = e & 127;
       const int it = c & (kAppendItems - 1);
       const int64_t item = item0 + (it < ni ? it : ni - 1);
       offs[u] = ((int64_t(layer_rel) * a.n_tokens + item / a.H) * a.H + item % a.H) * D + j;
     }
-    // u < 4: keys, u >= 4: values (e = tid + 256 u, vector e / 128).
+    // u < XU / 2: keys, the others values.
     if (a.dtype == TQ_DTYPE_F32) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) xin[u] = static_cast<const float*>(u < 4 ? a.k : a.v)[offs[u]];
+      for (int u = 0; u < XU; ++u) xin[u] = static_cast<const float*>(u < XU / 2 ? a.k : a.v)[offs[u]];
     } else {
-      uint16_t hv[8];
+      uint16_t hv[XU];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) hv[u] = static_cast<const uint16_t*>(u < 4 ? a.k : a.v)[offs[u]];
+      for (int u = 0; u < XU; ++u) hv[u] = static_cast<const uint16_t*>(u < XU / 2 ? a.k : a.v)[offs[u]];
       if (a.dtype == TQ_DTYPE_BF16) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) xin[u] = __uint_as_float(uint32_t(hv[u]) << 16);
+        for (int u = 0; u < XU; ++u) xin[u] = __uint_as_float(uint32_t(hv[u]) << 16);
       } else {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < XU; ++u) {
           _Float16 f;
           __builtin_memcpy(&f, &hv[u], 2);
           xin[u] = float(f);
@@ -644,8 +646,8 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
       }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int it = ((tid + 256 * u) >> 7) & (kAppendItems - 1);
+    for (int u = 0; u < XU; ++u) {
+      const int it = ((tid + kAppendThreads * u) >> 7) & (kAppendItems - 1);
       if (it >= ni) xin[u] = 0.f;
     }
   }
@@ -654,8 +656,8 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
     const int64_t tok = (item0 + (tid < ni ? tid : 0)) / a.H;
     if (tid < kAppendItems && tid < ni) slot = a.slots ? a.slots[tok] : a.slot0 + tok;
   }
-  // Codebooks: lane j of wave w holds entry j of table w (0 past the end; the
-  // boundary tables are padded with +inf).
+  // Codebooks: lane j of wave w < 4 holds entry j of table w (0 past the end;
+  // the boundary tables are padded with +inf).
   float cbv = 0.f;
   {
     const int nk = MK > 0 ? (1 << MK) : 0, nv = BV > 0 ? (1 << BV) : 0;
@@ -670,19 +672,19 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
   // Every global load above is in flight before any of them is waited on.
   __builtin_amdgcn_sched_barrier(0);
   if (tid < kAppendItems) slot_of[tid] = (slot < 0 || slot >= a.capacity) ? -1 : slot;
-  if (lane < 16) cb[wave][lane] = cbv;
-  for (int e = tid; e < kAppendItems * 16; e += 256) (&krec[0][0])[e] = 0u;
+  if (wave < 4 && lane < 16) cb[wave][lane] = cbv;
+  for (int e = tid; e < kAppendItems * 16; e += kAppendThreads) (&krec[0][0])[e] = 0u;
   if (tid < kAppendItems * 4) (&srec[0][0])[tid] = 0u;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int e = tid + 256 * u;
+  for (int u = 0; u < XU; ++u) {
+    const int e = tid + kAppendThreads * u;
     xs[e >> 7][e & 127] = xin[u];
   }
   __syncthreads();
-  // Norms: wave w reduces vectors 4w .. 4w + 3.
+  // Norms: wave w reduces vectors 2 w and 2 w + 1.
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int c = 4 * wave + k;
+  for (int k = 0; k < 2; ++k) {
+    const int c = 2 * wave + k;
     const float x0 = xs[c][lane], x1 = xs[c][lane + 64];
     const float ss = wave_sum(fmaf(x0, x0, x1 * x1));
     if (lane == 0) nrm[c] = sqrtf(ss);
@@ -690,41 +692,55 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
   __syncthreads();
 
   const int64_t vblocks = a.capacity / kVBlock;
-  // ---------------- rotation y = Pi x / ||x|| (column r16 = vector), quantisation
+  const int row = 16 * wave + 4 * q;   // this lane's output rows row .. row + 3
+  // ---------------- rotation y = Pi x / ||x|| (column col = item vector), quantisation
   if constexpr (ROT) {
-    const float4* bx = reinterpret_cast<const float4*>(&xs[r16][4 * kq]);
-    float4 b4[8];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) b4[v] = bx[4 * v];
-    const bool is_k = r16 < kAppendItems;
-    const int it = r16 & (kAppendItems - 1);
-    const float n = nrm[r16];
+    const bool is_k = col < kAppendItems;
+    const int it = col & (kAppendItems - 1);
+    const float n = nrm[col];
     // n = 0 -> y = 0; NaN -> NaN everywhere.
     const float inv = n > 0.f ? 1.0f / n : (n == 0.f ? 0.f : n);
+    // B operand x 2^e with 2^e ||x|| in [2^14, 2^15): exact fp16 for bf16 /
+    // fp16 inputs; fp32 inputs leave a remainder (times 2^11), zero otherwise.
+    const int ex = (n > 0.f && n < INFINITY) ? 15 - __builtin_amdgcn_frexp_expf(n) : 0;
+    floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      half8 ah, al, xh, xl;
+      {
+        const float v[8] = {pa[2 * s].x, pa[2 * s].y, pa[2 * s].z, pa[2 * s].w,
+                            pa[2 * s + 1].x, pa[2 * s + 1].y, pa[2 * s + 1].z, pa[2 * s + 1].w};
+        split8(v, ah, al, true);
+      }
+      {
+        const float4 x0 = *reinterpret_cast<const float4*>(&xs[col][32 * q + 8 * s]);
+        const float4 x1 = *reinterpret_cast<const float4*>(&xs[col][32 * q + 8 * s + 4]);
+        const float v[8] = {__builtin_amdgcn_ldexpf(x0.x, ex), __builtin_amdgcn_ldexpf(x0.y, ex),
+                            __builtin_amdgcn_ldexpf(x0.z, ex), __builtin_amdgcn_ldexpf(x0.w, ex),
+                            __builtin_amdgcn_ldexpf(x1.x, ex), __builtin_amdgcn_ldexpf(x1.y, ex),
+                            __builtin_amdgcn_ldexpf(x1.z, ex), __builtin_amdgcn_ldexpf(x1.w, ex)};
+        split8(v, xh, xl, true);
+      }
+      a1 = mfma16x16x32(ah, xh, a1);
+      a2 = mfma16x16x32(al, xh, a2);
+      a2 = mfma16x16x32(ah, xl, a2);
+    }
+    const float sc = __builtin_amdgcn_ldexpf(inv, -ex);
+    float y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = fmaf(a2[r], 0x1p-11f, a1[r]) * sc;
     const int64_t slot = slot_of[it];
     const int64_t plane = int64_t(layer) * a.H + (item0 + it) % a.H;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        acc = mfma16x16x4f32(ap[nb][v].x, b4[v].x, acc);
-        acc = mfma16x16x4f32(ap[nb][v].y, b4[v].y, acc);
-        acc = mfma16x16x4f32(ap[nb][v].z, b4[v].z, acc);
-        acc = mfma16x16x4f32(ap[nb][v].w, b4[v].w, acc);
-      }
-      const int row = 32 * wave + 16 * nb + 4 * kq;  // rows row .. row + 3 of this lane
-      if (it >= ni) continue;
+    if (it < ni) {
       if (is_k) {
         if constexpr (MK > 0) {
           uint32_t chunk = 0;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float y = acc[r] * inv;
             uint32_t idx = 0;
 #pragma unroll
-            for (int b = 0; b < (1 << MK) - 1; ++b) idx += (y >= cb[1][b]) ? 1u : 0u;
-            rs[it][row + r] = y - cb[0][idx];
+            for (int b = 0; b < (1 << MK) - 1; ++b) idx += (y[r] >= cb[1][b]) ? 1u : 0u;
+            rs[it][row + r] = y[r] - cb[0][idx];
             chunk |= idx << (r * MK);
           }
           or_bits(&krec[it][0], row * MK, chunk, 4 * MK);
@@ -734,10 +750,9 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
           const int bitp = int(slot % kVBlock) * BV;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float y = acc[r] * inv;
             uint32_t idx = 0;
 #pragma unroll
-            for (int b = 0; b < (1 << BV) - 1; ++b) idx += (y >= cb[3][b]) ? 1u : 0u;
+            for (int b = 0; b < (1 << BV) - 1; ++b) idx += (y[r] >= cb[3][b]) ? 1u : 0u;
             uint32_t* g = reinterpret_cast<uint32_t*>(a.v_idx + ((plane * vblocks + slot / kVBlock) * D + row + r) *
                                                                      (4 * BV)) +
                           (bitp >> 5);
@@ -752,44 +767,47 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
 
   // ---------------- key residual norm and QJL signs
   if constexpr (MK > 0) {
-    // Residual norms: wave w reduces items 2w, 2w + 1.
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int it = 2 * wave + k;
-      const float r0 = rs[it][lane], r1 = rs[it][lane + 64];
+    // Residual norms: wave w reduces item w.
+    {
+      const float r0 = rs[wave][lane], r1 = rs[wave][lane + 64];
       const float ss = wave_sum(fmaf(r0, r0, r1 * r1));
-      if (lane == 0) rnrm[it] = nrm[it] * sqrtf(ss);
+      if (lane == 0) rnrm[wave] = nrm[wave] * sqrtf(ss);
     }
-    // z = (S Pi^T)(y - c[idx]) for columns r16 < 8; bit = [n z >= 0].
-    const int it = r16 & (kAppendItems - 1);
-    const float4* br = reinterpret_cast<const float4*>(&rs[it][4 * kq]);
-    float4 b4[8];
+    // z = (S Pi^T)(y - c[idx]) for columns col < 8; bit = [n z >= 0].  The
+    // residual (times 2^14) is split into a high part and a remainder.
+    const int it = col & (kAppendItems - 1);
+    floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int v = 0; v < 8; ++v) b4[v] = br[4 * v];
+    for (int s = 0; s < 4; ++s) {
+      half8 mh, ml, rh, rl;
+      {
+        const float v[8] = {ma[2 * s].x, ma[2 * s].y, ma[2 * s].z, ma[2 * s].w,
+                            ma[2 * s + 1].x, ma[2 * s + 1].y, ma[2 * s + 1].z, ma[2 * s + 1].w};
+        split8(v, mh, ml, true);
+      }
+      {
+        const float4 x0 = *reinterpret_cast<const float4*>(&rs[it][32 * q + 8 * s]);
+        const float4 x1 = *reinterpret_cast<const float4*>(&rs[it][32 * q + 8 * s + 4]);
+        const float v[8] = {x0.x * 16384.f, x0.y * 16384.f, x0.z * 16384.f, x0.w * 16384.f,
+                            x1.x * 16384.f, x1.y * 16384.f, x1.z * 16384.f, x1.w * 16384.f};
+        split8(v, rh, rl, true);
+      }
+      a1 = mfma16x16x32(mh, rh, a1);
+      a2 = mfma16x16x32(mh, rl, a2);
+      a2 = mfma16x16x32(ml, rh, a2);
+    }
     const float n = nrm[it];
+    if (col < kAppendItems && it < ni) {
+      uint32_t bits = 0;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        acc = mfma16x16x4f32(am[nb][v].x, b4[v].x, acc);
-        acc = mfma16x16x4f32(am[nb][v].y, b4[v].y, acc);
-        acc = mfma16x16x4f32(am[nb][v].z, b4[v].z, acc);
-        acc = mfma16x16x4f32(am[nb][v].w, b4[v].w, acc);
-      }
-      const int row = 32 * wave + 16 * nb + 4 * kq;
-      if (r16 < kAppendItems && it < ni) {
-        uint32_t bits = 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) bits |= (acc[r] * n >= 0.f ? 1u : 0u) << r;
-        atomicOr(&srec[it][row >> 5], bits << (row & 31));
-      }
+      for (int r = 0; r < 4; ++r) bits |= (fmaf(a2[r], 0x1p-11f, a1[r]) * n >= 0.f ? 1u : 0u) << r;
+      atomicOr(&srec[it][row >> 5], bits << (row & 31));
     }
   }
   __syncthreads();
 
   // ---------------- records
-  for (int e = tid; e < kAppendItems * 32; e += 256) {
+  for (int e = tid; e < kAppendItems * 32; e += kAppendThreads) {
     const int it = e >> 5, w = e & 31;
     const int64_t slot = slot_of[it];
     if (it >= ni || slot < 0) continue;
@@ -806,7 +824,7 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
     }
   }
   if constexpr (MK == 0 || BV == 0) {
-    for (int e = tid; e < kAppendItems * D; e += 256) {
+    for (int e = tid; e < kAppendItems * D; e += kAppendThreads) {
       const int it = e >> 7, j = e & 127;
       const int64_t slot = slot_of[it];
       if (it >= ni || slot < 0) continue;
@@ -819,8 +837,7 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
   }
 }
 template <int MK, int BV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void compress_append_kernel(
-    CompressArgs a) {
+__global__ __launch_bounds__(kAppendThreads) void compress_append_kernel(CompressArgs a) {
   append_body<MK, BV>(a, blockIdx.x, blockIdx.y);
 }
 
@@ -1811,7 +1828,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 // the append blocks (item group, layer), the others the query preparation
 // blocks (4 KV head + quarter, sequence, layer).
 template <int MK, int BV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void append_prepare_kernel(
+__global__ __launch_bounds__(kAppendThreads) void append_prepare_kernel(
     CompressArgs a, int app_groups, int n_append, const float* q, const float* pi, const float* s, float* qprep,
     int batch, int H, int Hq) {
   const int bid = blockIdx.x;
@@ -1819,6 +1836,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     append_body<MK, BV>(a, bid % app_groups, bid / app_groups);
     return;
   }
+  if (threadIdx.x >= 256) return;   // the query preparation blocks take 4 waves
   const int r = bid - n_append, nx = H * 4;
   qprep_body<(MK > 0)>(q, pi, s, qprep, batch, H, Hq, r % nx, (r / nx) % batch, r / (nx * batch));
 }
@@ -2318,7 +2336,7 @@ tq_status tq_compress_kv_bounded(const tq_format* fmt, const tq_tables* tables, 
 #define TQ_APP(MK_, BV_)                                                                               \
   if (a.mk == MK_ && a.bv == BV_) {                                                                    \
     hipLaunchKernelGGL((compress_append_kernel<MK_, BV_>), dim3(unsigned(groups), unsigned(n_layers)), \
-                       dim3(256), 0, hs, a);                                                           \
+                       dim3(kAppendThreads), 0, hs, a);                                                \
     return launch_status("compress (append)");                                                         \
   }
 #define TQ_APP_V(MK_) TQ_APP(MK_, 0) TQ_APP(MK_, 1) TQ_APP(MK_, 2) TQ_APP(MK_, 4)
@@ -2380,7 +2398,8 @@ tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const
   const dim3 grid(unsigned(n_append + n_prep));
 #define TQ_AP(MK_, BV_)                                                                                          \
   if (a.mk == MK_ && a.bv == BV_) {                                                                              \
-    hipLaunchKernelGGL((append_prepare_kernel<MK_, BV_>), grid, dim3(256), 0, hs, a, int(groups), int(n_append), \
+    hipLaunchKernelGGL((append_prepare_kernel<MK_, BV_>), grid, dim3(kAppendThreads), 0, hs, a, int(groups),     \
+                       int(n_append),                                                                          \
                        q, tables->pi, tables->s, qprep, batch, cache->n_kv_heads, n_q_heads);                  \
     return launch_status("append + prepare");                                                                  \
   }

@@ -216,11 +216,13 @@ def test_staged_decode_matches_one_call(case):
         assert float(np.max(np.abs(a - b))) <= 1e-5 * scale
 
 
-def test_degenerate_vectors_and_nan():
+@pytest.mark.parametrize("chunk", [None, 3])
+def test_degenerate_vectors_and_nan(chunk):
     """Zero keys/values compress to zero norms and contribute nothing; a NaN key
-    makes its sequence's outputs NaN and leaves other sequences finite."""
+    makes its sequence's outputs NaN and leaves other sequences finite.  chunk:
+    tokens per compression call (None: one call; 3: the few-token kernel)."""
     import kv_cache_quantization_norm_amd as tq
-    _say("degenerate")
+    _say("degenerate", chunk)
     w = wl.Workload("degenerate", 1, 1, 2, (40, 40), 4, 4, "f32", 0.0, 0, 1.0)
     fmt = pu.layer_format(w, 0)
     starts, lens, cap, slots = pu.slots_of(w)
@@ -231,8 +233,13 @@ def test_degenerate_vectors_and_nan():
     tfmt = pu.tq_format(fmt)
     tables = tq.Tables.create(tfmt, [0])
     dev = tq.Cache.allocate(tfmt, 1, 1, cap)
-    tq.tq_compress_kv(tfmt, tables, dev, torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(),
-                      slots=torch.from_numpy(slots).cuda())
+    kt, vt, st = torch.from_numpy(K).cuda(), torch.from_numpy(V).cuda(), torch.from_numpy(slots).cuda()
+    if chunk is None:
+        tq.tq_compress_kv(tfmt, tables, dev, kt, vt, slots=st)
+    else:
+        for i in range(0, K.shape[1], chunk):
+            tq.tq_compress_kv(tfmt, tables, dev, kt[:, i:i + chunk].contiguous(), vt[:, i:i + chunk].contiguous(),
+                              slots=st[i:i + chunk].contiguous())
     torch.cuda.synchronize()
     g = pu.download_cache(dev, fmt)[0]
     s3 = slots[3]
@@ -253,19 +260,20 @@ def test_degenerate_vectors_and_nan():
     pu.check_outputs(out[0, :1], ref)
 
 
-def test_overwrite_slot_and_append():
+@pytest.mark.parametrize("k_bits,v_bits,dtype", [(4, 2, "bf16"), (3, 4, "f32"), (5, 1, "f16"), (2, 0, "f32")])
+def test_overwrite_slot_and_append(k_bits, v_bits, dtype):
     """Re-compressing into used slots replaces their records (value codes are
     rewritten inside shared 32-slot groups), one token at a time."""
     import kv_cache_quantization_norm_amd as tq
-    _say("append")
-    w = wl.Workload("append", 2, 2, 4, (70,), 4, 2, "bf16", 0.5, 1, 10.0)
+    _say("append", k_bits, v_bits, dtype)
+    w = wl.Workload("append", 2, 2, 4, (70,), k_bits, v_bits, dtype, 0.5, 1, 10.0)
     fmt = pu.layer_format(w, 0)
     starts, lens, cap, slots = pu.slots_of(w)
     K, V = _inputs(w, [0, 1])
     tfmt = pu.tq_format(fmt)
     tables = tq.Tables.create(tfmt, [0, 1])
     dev = tq.Cache.allocate(tfmt, 2, 2, cap)
-    dt = torch.bfloat16
+    dt = _torch_dtype(w)
     # first fill with garbage (shifted tokens), then append the real tokens one by one
     kt = torch.from_numpy(np.roll(K, 3, axis=1)).to("cuda", dt).contiguous()
     vt = torch.from_numpy(np.roll(V, 5, axis=1)).to("cuda", dt).contiguous()
