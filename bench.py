@@ -7,7 +7,8 @@ One step = one pass of the whole path over the dense 28-layer workload
      into slot 8191 of the packed cache and prepare the step's queries (one
      tq_append_prepare call: one launch);
   2. decode attention for all 28 query heads of all 28 layers over the 8192
-     packed tokens (tq_decode_partials, tq_decode_combine).
+     packed tokens (tq_decode_attend: one launch, the pieces of each problem
+     merged inside the decode kernel by its last workgroup).
 The same step made of tq_compress_kv + tq_decode_attention is timed beside it.
 Inputs are seeded synthetic bf16 K/V (per-channel log-normal scales, two
 outlier channels per head) already resident in HBM.  The timed loop rotates
@@ -142,8 +143,7 @@ def main():
 
     def step(c):
         tq.tq_append_prepare(fmt, tables, c, k_new, v_new, Q, T, ws, slot0=T - 1, stream=stream)
-        tq.tq_decode_partials(fmt, tables, c, 1, HQ, seq_start, seq_len, T, ws, stream=stream)
-        tq.tq_decode_combine(fmt, tables, c, 1, HQ, T, out, ws, stream=stream)
+        tq.tq_decode_attend(fmt, tables, c, 1, HQ, seq_start, seq_len, T, out, ws, stream=stream)
 
     def step_two_calls(c):
         tq.tq_compress_kv(fmt, tables, c, k_new, v_new, slot0=T - 1, stream=stream)
@@ -166,7 +166,7 @@ def main():
     wall = time.perf_counter() - wall0
     step_ms = e0.elapsed_time(e1) / args.steps
 
-    # the same step as tq_compress_kv + tq_decode_attention (four launches)
+    # the same step as tq_compress_kv + tq_decode_attention (three launches)
     for i in range(args.warmup):
         step_two_calls(caches[i % n_copies])
     torch.cuda.synchronize()
@@ -177,7 +177,7 @@ def main():
     torch.cuda.synchronize()
     step_two_calls_ms = e0.elapsed_time(e1) / args.steps
 
-    # decode call alone (query prep + decode kernel + combine), same rotation
+    # decode call alone (query prep + decode kernel), same rotation
     for i in range(args.warmup):
         decode_only(caches[i % n_copies])
     torch.cuda.synchronize()
@@ -189,15 +189,14 @@ def main():
     decode_ms = e0.elapsed_time(e1) / args.steps
 
     # the dominant kernel alone: the staged entry points, with events around
-    # the partials launch (decode_kernel) only, on the stream it runs on
+    # the tq_decode_attend launch (decode_kernel) only, on the stream it runs on
     def staged(c, ev=None):
         tq.tq_decode_prepare(fmt, tables, c, Q, T, ws, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        tq.tq_decode_partials(fmt, tables, c, 1, HQ, seq_start, seq_len, T, ws, stream=stream)
+        tq.tq_decode_attend(fmt, tables, c, 1, HQ, seq_start, seq_len, T, out, ws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        tq.tq_decode_combine(fmt, tables, c, 1, HQ, T, out, ws, stream=stream)
 
     for i in range(args.warmup):
         staged(caches[i % n_copies])
@@ -212,11 +211,11 @@ def main():
     # time without an event pair per launch
     tq.tq_decode_prepare(fmt, tables, base, Q, T, ws, stream=stream)
     for i in range(args.warmup):
-        tq.tq_decode_partials(fmt, tables, caches[i % n_copies], 1, HQ, seq_start, seq_len, T, ws, stream=stream)
+        tq.tq_decode_attend(fmt, tables, caches[i % n_copies], 1, HQ, seq_start, seq_len, T, out, ws, stream=stream)
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b0.record(stream)
     for i in range(args.steps):
-        tq.tq_decode_partials(fmt, tables, caches[i % n_copies], 1, HQ, seq_start, seq_len, T, ws, stream=stream)
+        tq.tq_decode_attend(fmt, tables, caches[i % n_copies], 1, HQ, seq_start, seq_len, T, out, ws, stream=stream)
     b1.record(stream)
     torch.cuda.synchronize()
     kern_batch_us = b0.elapsed_time(b1) * 1e3 / args.steps
@@ -304,9 +303,12 @@ def main():
     new_tok = L * H * 2 * D * (2 if dt != torch.float32 else 4) + L * H * (k_rec + v_rec)
     step_bytes = records + qo + tables_bytes + new_tok
     decode_bytes = records + qo + L * 2 * D * D * 4   # Pi and S
-    kernel_bytes = records + L * HQ * 2 * D * 4       # packed records + the prepared queries (Pi q, S q)
+    # decode_kernel with the in-kernel merge: packed records, the prepared
+    # queries (Pi q, S q), Pi for the output rotation (once per layer) and the
+    # outputs
+    kernel_bytes = records + L * HQ * 2 * D * 4 + L * D * D * 4 + L * HQ * D * 4
     pieces = decode_pieces(L * H * -(-(HQ // H) // 8), T)
-    split_overhead = pieces * (HQ // H) * (D + 2) * 4  # fp32 partials written for the combine
+    split_overhead = pieces * (HQ // H) * (D + 2) * 4  # fp32 partials written (and read back by the merge)
     step_gbs = step_bytes / (step_ms * 1e-3) / 1e9
     decode_gbs = decode_bytes / (decode_ms * 1e-3) / 1e9
     kern_mean = kern_batch_us
@@ -339,9 +341,9 @@ def main():
                                                   "p90": round(float(np.percentile(kern_us, 90)), 2)},
                      "split_partials_bytes": split_overhead},
         "decode_call": {"us": round(decode_ms * 1e3, 2), "GBs": round(decode_gbs, 1),
-                        "bytes": decode_bytes, "kernels": "qprep_kernel + decode_kernel + combine_kernel"},
+                        "bytes": decode_bytes, "kernels": "qprep_kernel + decode_kernel (pieces merged in-kernel)"},
         "decode_step_bytes": step_bytes,
-        "step_launches": "append_prepare_kernel + decode_kernel + combine_kernel",
+        "step_launches": "append_prepare_kernel + decode_kernel (pieces merged in-kernel)",
         "step_two_calls_us": round(step_two_calls_ms * 1e3, 2),
         "compress": {"what": f"bulk prefill {T} tokens x {L} layers x {H} KV heads, one call",
                      "ms": round(bulk_ms, 4),

@@ -246,6 +246,19 @@ tq_status tq_decode_combine(const tq_format* fmt, const tq_tables* tables, const
                             int32_t n_q_heads, int64_t max_seq_len, float* out, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* Device.  tq_decode_partials and tq_decode_combine in one launch (the
+ * attention of the QJL deep-dive, section 6, on queries already prepared by
+ * tq_decode_prepare or tq_append_prepare on the same workspace): each
+ * problem's pieces are merged by the workgroup that writes its last piece, so
+ * out is written by the decode kernel itself.  Same arguments, layouts and
+ * errors as those two calls; out as in tq_decode_attention.  The workspace
+ * holds one piece counter per problem: the preparation sets them to zero and
+ * every completed call leaves them at zero, so two calls on one workspace
+ * must not overlap. */
+tq_status tq_decode_attend(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, int32_t batch,
+                           int32_t n_q_heads, const int64_t* seq_start, const int32_t* seq_len, int64_t max_seq_len,
+                           float scale, float* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Device.  A decode step's append and query preparation in one launch: the
  * same result as tq_compress_kv(fmt, tables, cache, k, v, dtype, layer0,
  * n_layers, n_tokens, slots, slot0, stream) followed by
@@ -255,8 +268,8 @@ tq_status tq_decode_combine(const tq_format* fmt, const tq_tables* tables, const
  * new tokens' records (QJL deep-dive, sections 2 and 5) and the sketched
  * queries (section 6) do not depend on each other, so for fewer than 16
  * tokens one kernel computes both; for 16 or more tokens the two calls are
- * made one after the other.  Follow it with tq_decode_partials and
- * tq_decode_combine on the same workspace. */
+ * made one after the other.  Follow it with tq_decode_attend (or
+ * tq_decode_partials and tq_decode_combine) on the same workspace. */
 tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
                             const void* k, const void* v, int32_t dtype, int32_t layer0, int32_t n_layers,
                             int64_t n_tokens, const int64_t* slots, int64_t slot0, const float* q, int32_t batch,

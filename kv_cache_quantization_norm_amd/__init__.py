@@ -84,6 +84,7 @@ def _load(path: str = LIB_PATH):
                                     P]),
         "tq_decode_partials": (I32, [fmtp, tabp, cachep, I32, I32, P, P, I64, F32, P, SZ, P]),
         "tq_decode_combine": (I32, [fmtp, tabp, cachep, I32, I32, I64, P, P, SZ, P]),
+        "tq_decode_attend": (I32, [fmtp, tabp, cachep, I32, I32, P, P, I64, F32, P, P, SZ, P]),
         "tq_status_string": (ctypes.c_char_p, [I32]),
         "tq_last_error": (ctypes.c_char_p, []),
     }
@@ -97,7 +98,7 @@ def _load(path: str = LIB_PATH):
 _lib = _load()
 EXPORTED = ("tq_layer_seed", "tq_make_rotations", "tq_make_codebook", "tq_cache_plane_bytes",
             "tq_decode_workspace_bytes", "tq_decode_split", "tq_compress_kv", "tq_decode_attention", "tq_score",
-            "tq_decode_prepare", "tq_decode_partials", "tq_decode_combine", "tq_append_prepare",
+            "tq_decode_prepare", "tq_decode_partials", "tq_decode_combine", "tq_decode_attend", "tq_append_prepare",
             "tq_compress_kv_bounded", "tq_decode_attention_tail", "tq_decode_tail_workspace_bytes",
             "tq_status_string", "tq_last_error")
 
@@ -379,6 +380,16 @@ def tq_decode_combine(fmt: tq_format, tables: Tables, cache: Cache, batch: int, 
     _check(_lib.tq_decode_combine(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), batch, n_q_heads,
                                   max_seq_len, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _stream(stream)), "tq_decode_combine")
+
+
+def tq_decode_attend(fmt: tq_format, tables: Tables, cache: Cache, batch: int, n_q_heads: int, seq_start, seq_len,
+                     max_seq_len: int, out, workspace, scale: float = 0.0, stream=None):
+    """Partials and their merge in one launch, on queries prepared in `workspace`."""
+    tb, cs = tables.struct(), cache.struct()
+    _check(_lib.tq_decode_attend(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), batch, n_q_heads,
+                                 _ptr(seq_start), _ptr(seq_len), max_seq_len, scale, _ptr(out), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "tq_decode_attend")
 
 
 def tq_score(fmt: tq_format, tables: Tables, cache: Cache, q, seq_start, seq_len, max_seq_len: int, logits,

@@ -867,6 +867,13 @@ struct DecodeArgs {
   const int32_t* seq_len;
   float* partial;       // [L][B][Hq][seg_max][D + 2]
   float* logits;        // score mode: [L][B][Hq][max_len]
+  // In-kernel merge (non-null `done`): per problem, the count of its pieces
+  // whose partial is written; the workgroup that completes the count merges
+  // them into out [L][B][Hq][D] (Pi^T applied for rotated values) and sets the
+  // count back to zero.
+  uint32_t* done;
+  const float* pi;
+  float* out;
   int64_t max_len;
   float scale;
   float kappa;
@@ -1571,14 +1578,141 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
             av += (live ? rv[w] : 0.f) * f;
             ls += (live ? lv[w] : 0.f) * f;
           }
+          // agent-scope stores: visible to every XCD once complete (the
+          // in-kernel merge reads them from other workgroups)
           float* P = a.partial + ((pbase + g) * a.seg_max + a.seg_base + seg) * (D + 2);
-          P[2 + i] = av;
+          __hip_atomic_store(P + 2 + i, av, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (i == 0) {
-            P[0] = M;
-            P[1] = ls;
+            __hip_atomic_store(P, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(P + 1, ls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
       }
+    }
+  };
+
+  // In-kernel merge of a problem whose pieces are all written (the same
+  // arithmetic, in the same order, as combine_kernel): thread t merges
+  // coordinate t % 128 of heads t / 128 and t / 128 + 4 over the pieces in
+  // batches of 4 with a running maximum; then wave w forms output rows
+  // 16 w .. 16 w + 15 of Pi^T res on fp32 MFMA 16x16x4 (res in LDS, over the
+  // wave tables' reduction area, which is free after the merge).
+  auto finish = [&](int prob, const Run& Rp) {
+    if constexpr (!SCORE) {
+      const int ng = a.G - Rp.hg * kMaxGroup < kMaxGroup ? a.G - Rp.hg * kMaxGroup : kMaxGroup;
+      const int64_t row0 = (int64_t(Rp.layer) * a.batch + Rp.b) * a.Hq + Rp.hk * a.G + Rp.hg * kMaxGroup;
+      const int first = prob * cpp;
+      const int nseg = (first + cpp - 1) / a.chunks_per_wg - first / a.chunks_per_wg + 1;
+      const int i = tid & (D - 1), r16 = lane & 15, kq = lane >> 4;
+      constexpr bool ROT = BV > 0;
+      float pa[ROT ? 32 : 1];
+      if constexpr (ROT) {
+        // A operands (columns of Pi), step (v, c): Pi[16 v + 4 kq + c][16 wave + r16]
+        const float* pil = a.pi + int64_t(Rp.layer) * D * D + 16 * wave + r16;
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) pa[4 * v + c] = pil[int64_t(16 * v + 4 * kq + c) * D];
+      }
+      constexpr int SB = 4;
+      float M[2], L[2], A[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        M[k] = -INFINITY;
+        L[k] = 0.f;
+        A[k] = 0.f;
+      }
+      for (int sp0 = 0; sp0 < nseg; sp0 += SB) {
+        float ms[2][SB], ls[2][SB], as[2][SB];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int g = (tid >> 7) + 4 * k < ng ? (tid >> 7) + 4 * k : ng - 1;
+          const float* P = a.partial + ((row0 + g) * a.seg_max + a.seg_base) * (D + 2);
+#pragma unroll
+          for (int u = 0; u < SB; ++u) {
+            const int64_t sp = sp0 + u < nseg ? sp0 + u : nseg - 1;
+            ms[k][u] = __hip_atomic_load(P + sp * (D + 2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ls[k][u] = __hip_atomic_load(P + sp * (D + 2) + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            as[k][u] = __hip_atomic_load(P + sp * (D + 2) + 2 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          float Mn = M[k];
+#pragma unroll
+          for (int u = 0; u < SB; ++u)
+            if (sp0 + u < nseg) Mn = fmaxf(Mn, ms[k][u]);
+          const float f0 = M[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[k] - Mn);
+          L[k] *= f0;
+          A[k] *= f0;
+#pragma unroll
+          for (int u = 0; u < SB; ++u) {
+            const float f = (sp0 + u >= nseg || ms[k][u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[k][u] - Mn);
+            L[k] = fmaf(ls[k][u], f, L[k]);
+            A[k] = fmaf(as[k][u], f, A[k]);
+          }
+          M[k] = Mn;
+        }
+      }
+      float* const res = red;   // [16][D]: heads, rows >= ng zero
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int g = (tid >> 7) + 4 * k;
+        // L is 0 only for an empty sequence; NaN must propagate.
+        const bool has = L[k] > 0.f || L[k] != L[k];
+        const float v = has ? A[k] / L[k] : 0.f;
+        if constexpr (ROT) {
+          res[g * D + i] = g < ng ? v : 0.f;
+          res[(g + 8) * D + i] = 0.f;
+        } else if (g < ng) {
+          a.out[(row0 + g) * D + i] = v;
+        }
+      }
+      if constexpr (ROT) {
+        __syncthreads();
+        const float4* bres = reinterpret_cast<const float4*>(res + r16 * D + 4 * kq);
+        float4 b4[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) b4[v] = bres[4 * v];
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          acc = mfma16x16x4f32(pa[4 * v + 0], b4[v].x, acc);
+          acc = mfma16x16x4f32(pa[4 * v + 1], b4[v].y, acc);
+          acc = mfma16x16x4f32(pa[4 * v + 2], b4[v].z, acc);
+          acc = mfma16x16x4f32(pa[4 * v + 3], b4[v].w, acc);
+        }
+        if (r16 < ng) {
+          const float4 o = {acc[0], acc[1], acc[2], acc[3]};
+          *reinterpret_cast<float4*>(a.out + (row0 + r16) * D + 16 * wave + 4 * kq) = o;
+        }
+      }
+    }
+  };
+  // Counts the piece of problem `prob` just written by merge; the workgroup
+  // that brings the count to the problem's number of pieces resets it and
+  // runs finish.  Hand-off: the partials are written and read with
+  // agent-scope (device-coherent) stores and loads, and every wave waits for
+  // its stores to complete before the barrier that precedes the count's
+  // increment, so a workgroup that sees the full count (its loads issued
+  // after that atomic returned) reads every piece complete.  A release fence
+  // at agent scope would order the same, but it also writes back the XCD's
+  // whole L2 (one pass per fence), which cost more than the merge saves.
+  auto arrive = [&](int prob, const Run& Rp) {
+    if constexpr (!SCORE) {
+      if (a.done == nullptr) return;
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are complete
+      __syncthreads();
+      if (tid == 0) {
+        const int first = prob * cpp;
+        const uint32_t nseg = uint32_t((first + cpp - 1) / a.chunks_per_wg - first / a.chunks_per_wg + 1);
+        const uint32_t old = __hip_atomic_fetch_add(a.done + prob, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old + 1 == nseg;
+        if (last) __hip_atomic_store(a.done + prob, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        counter[1] = last ? 1u : 0u;
+      }
+      __syncthreads();
+      if (counter[1]) finish(prob, Rp);
     }
   };
 
@@ -1753,11 +1887,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     __syncthreads();
     const int next_base = uni(counter[0]);   // every draw of the group is done
     merge(G.ra, int(blockIdx.x) - (G.pa * cpp) / a.chunks_per_wg);
+    arrive(G.pa, G.ra);
     if (G.has_b) {
       __syncthreads();
       flush(had_b);
       __syncthreads();
       merge(G.rb, int(blockIdx.x) - G.a_end / a.chunks_per_wg);
+      arrive(G.pa + 1, G.rb);
     }
     __syncthreads();
     base = next_base - 3 * kDecodeWaves;
@@ -1772,13 +1908,19 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
 // 16 bi + l % 16 and query head l % 16 of the head block; its float4 pieces
 // 16 v + 4 (l / 16) .. + 3 of both are step v's four k-values, the same k on
 // the A and the B side, so the sum over k is exact in any order.
+// `done` (if not null): the in-kernel merge counts of the decode that follows,
+// zeroed here for the block's problems.
 template <bool ROT>
 __device__ __forceinline__ void qprep_body(const float* q, const float* pi, const float* s, float* qprep, int batch,
-                                           int H, int Hq, int bx, int b, int layer) {
+                                           int H, int Hq, int bx, int b, int layer, uint32_t* done) {
   const int hk = bx >> 2, quarter = bx & 3;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = Hq / H;
   const int64_t row0 = (int64_t(layer) * batch + b) * Hq + int64_t(hk) * G;
+  if (done != nullptr && quarter == 0) {
+    const int n_hg = (G + kMaxGroup - 1) / kMaxGroup;
+    for (int hg = tid; hg < n_hg; hg += 256) done[((int64_t(layer) * batch + b) * H + hk) * n_hg + hg] = 0u;
+  }
   if constexpr (!ROT) {
     // fp16 keys are scored against q itself; no sketch.
     for (int e = quarter * 256 + tid; e < G * D; e += 1024) {
@@ -1819,8 +1961,8 @@ __device__ __forceinline__ void qprep_body(const float* q, const float* pi, cons
 }
 template <bool ROT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void qprep_kernel(
-    const float* q, const float* pi, const float* s, float* qprep, int batch, int H, int Hq) {
-  qprep_body<ROT>(q, pi, s, qprep, batch, H, Hq, blockIdx.x, blockIdx.y, blockIdx.z);
+    const float* q, const float* pi, const float* s, float* qprep, int batch, int H, int Hq, uint32_t* done) {
+  qprep_body<ROT>(q, pi, s, qprep, batch, H, Hq, blockIdx.x, blockIdx.y, blockIdx.z, done);
 }
 
 // The append of a few tokens and the query preparation of the same decode
@@ -1830,7 +1972,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 template <int MK, int BV>
 __global__ __launch_bounds__(kAppendThreads) void append_prepare_kernel(
     CompressArgs a, int app_groups, int n_append, const float* q, const float* pi, const float* s, float* qprep,
-    int batch, int H, int Hq) {
+    int batch, int H, int Hq, uint32_t* done) {
   const int bid = blockIdx.x;
   if (bid < n_append) {
     append_body<MK, BV>(a, bid % app_groups, bid / app_groups);
@@ -1838,7 +1980,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_prepare_kernel(
   }
   if (threadIdx.x >= 256) return;   // the query preparation blocks take 4 waves
   const int r = bid - n_append, nx = H * 4;
-  qprep_body<(MK > 0)>(q, pi, s, qprep, batch, H, Hq, r % nx, (r / nx) % batch, r / (nx * batch));
+  qprep_body<(MK > 0)>(q, pi, s, qprep, batch, H, Hq, r % nx, (r / nx) % batch, r / (nx * batch), done);
 }
 
 // Merges the piece partials of one (layer, batch, KV head) for every query
@@ -2092,6 +2234,9 @@ DecodeArgs make_args(const tq_format* fmt, const tq_tables* tables, const tq_cac
   a.seq_len = seq_len;
   a.partial = partial;
   a.logits = out;
+  a.done = nullptr;
+  a.pi = tables->pi;
+  a.out = nullptr;
   a.max_len = max_seq_len;
   a.scale = scale != 0.f ? scale : 1.0f / std::sqrt(float(fmt->d));
   a.kappa = float(std::sqrt(M_PI / 2.0) / fmt->d);
@@ -2099,8 +2244,16 @@ DecodeArgs make_args(const tq_format* fmt, const tq_tables* tables, const tq_cac
 }
 
 // Decode stages: prepare the query operands (qprep_kernel), score / accumulate
-// the chunk runs (decode_kernel), merge the pieces (combine_kernel).
-enum { kStagePrepare = 1, kStagePartials = 2, kStageCombine = 4, kStageAll = 7, kStageCheckOnly = 8 };
+// the chunk runs (decode_kernel), merge the pieces (combine_kernel, or inside
+// decode_kernel by the last workgroup of each problem: kStageMerge).
+enum {
+  kStagePrepare = 1,
+  kStagePartials = 2,
+  kStageCombine = 4,
+  kStageCheckOnly = 8,
+  kStageMerge = 16,
+  kStageAll = kStagePrepare | kStagePartials | kStageMerge
+};
 
 template <bool SCORE>
 tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
@@ -2115,7 +2268,7 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   if ((stages & kStagePrepare) && !q) return fail(TQ_ERR_INVALID_ARG, "q is NULL");
   if ((stages & kStagePartials) && (!seq_start || !seq_len))
     return fail(TQ_ERR_INVALID_ARG, "seq_start/seq_len is NULL");
-  if (((stages & kStageCombine) || (SCORE && (stages & kStagePartials))) && !out)
+  if (((stages & (kStageCombine | kStageMerge)) || (SCORE && (stages & kStagePartials))) && !out)
     return fail(TQ_ERR_INVALID_ARG, "output is NULL");
   if (batch <= 0 || n_q_heads <= 0 || n_q_heads % cache->n_kv_heads)
     return fail(TQ_ERR_INVALID_ARG, "batch=%d n_q_heads=%d (must be a positive multiple of n_kv_heads=%d)",
@@ -2132,28 +2285,33 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   hipStream_t hs = static_cast<hipStream_t>(stream);
   float* qprep = static_cast<float*>(workspace);
   float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.qprep_bytes);
+  uint32_t* done = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + plan.qprep_bytes + plan.partial_bytes);
   const int mk = fmt->k_bits > 0 ? fmt->k_bits - 1 : 0;
   const int bv = fmt->v_bits;
   if (stages & kStagePrepare) {
     const dim3 qgrid(cache->n_kv_heads * 4, batch, cache->n_layers);
     if (fmt->k_bits > 0)
       hipLaunchKernelGGL(qprep_kernel<true>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qprep, batch,
-                         cache->n_kv_heads, n_q_heads);
+                         cache->n_kv_heads, n_q_heads, done);
     else
       hipLaunchKernelGGL(qprep_kernel<false>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qprep, batch,
-                         cache->n_kv_heads, n_q_heads);
+                         cache->n_kv_heads, n_q_heads, done);
     if ((st = launch_status("qprep"))) return st;
   }
   if (max_seq_len == 0 && SCORE) return TQ_OK;
 
-  const DecodeArgs a = make_args(fmt, tables, cache, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, plan,
-                                 qprep, partial, out);
+  DecodeArgs a = make_args(fmt, tables, cache, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, plan,
+                           qprep, partial, out);
+  if (!SCORE && (stages & kStageMerge)) {
+    a.done = done;
+    a.out = out;
+  }
   const dim3 grid(unsigned(plan.n_workgroups));
   if (stages & kStagePartials) {
     if ((st = launch_decode<SCORE>(mk, SCORE ? 0 : bv, a, grid, hs))) return st;
     if ((st = launch_status("decode"))) return st;
   }
-  if (!SCORE && (stages & kStageCombine)) {
+  if (!SCORE && (stages & kStageCombine) && !(stages & kStageMerge)) {
     const dim3 cgrid(cache->n_kv_heads, batch, cache->n_layers);
     if (bv > 0)
       hipLaunchKernelGGL(combine_kernel<true>, cgrid, dim3(256), 0, hs, partial, tables->pi, out, batch,
@@ -2216,12 +2374,12 @@ tq_status decode_tail(const tq_format* fmt, const tq_tables* tables, const tq_ca
   const dim3 qgrid(cache->n_kv_heads * 4, batch, cache->n_layers);
   if (fmt->k_bits > 0)
     hipLaunchKernelGGL(qprep_kernel<true>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qrot, batch,
-                       cache->n_kv_heads, n_q_heads);
+                       cache->n_kv_heads, n_q_heads, nullptr);
   else
     hipLaunchKernelGGL(qprep_kernel<false>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qrot, batch,
-                       cache->n_kv_heads, n_q_heads);
+                       cache->n_kv_heads, n_q_heads, nullptr);
   hipLaunchKernelGGL(qprep_kernel<false>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qplain, batch,
-                     cache->n_kv_heads, n_q_heads);
+                     cache->n_kv_heads, n_q_heads, nullptr);
   if ((st = launch_status("qprep"))) return st;
   DecodeArgs ap = make_args(fmt, tables, cache, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, tp.packed,
                             qrot, partial, nullptr);
@@ -2395,12 +2553,14 @@ tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const
   if (n_append + n_prep > 0x7FFFFFFF) return fail(TQ_ERR_INVALID_ARG, "too many workgroups");
   hipStream_t hs = static_cast<hipStream_t>(stream);
   float* qprep = static_cast<float*>(workspace);
+  const SplitPlan plan = plan_decode(fmt->d, cache->n_layers, batch, cache->n_kv_heads, n_q_heads, max_seq_len);
+  uint32_t* done = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + plan.qprep_bytes + plan.partial_bytes);
   const dim3 grid(unsigned(n_append + n_prep));
 #define TQ_AP(MK_, BV_)                                                                                          \
   if (a.mk == MK_ && a.bv == BV_) {                                                                              \
     hipLaunchKernelGGL((append_prepare_kernel<MK_, BV_>), grid, dim3(kAppendThreads), 0, hs, a, int(groups),     \
                        int(n_append),                                                                          \
-                       q, tables->pi, tables->s, qprep, batch, cache->n_kv_heads, n_q_heads);                  \
+                       q, tables->pi, tables->s, qprep, batch, cache->n_kv_heads, n_q_heads, done);            \
     return launch_status("append + prepare");                                                                  \
   }
 #define TQ_AP_V(MK_) TQ_AP(MK_, 0) TQ_AP(MK_, 1) TQ_AP(MK_, 2) TQ_AP(MK_, 4)
@@ -2442,6 +2602,14 @@ tq_status tq_decode_partials(const tq_format* fmt, const tq_tables* tables, cons
                              void* stream) {
   return tq::decode_common<false>(fmt, tables, cache, nullptr, batch, n_q_heads, seq_start, seq_len, max_seq_len,
                                   scale, nullptr, workspace, workspace_bytes, stream, tq::kStagePartials);
+}
+
+tq_status tq_decode_attend(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, int32_t batch,
+                           int32_t n_q_heads, const int64_t* seq_start, const int32_t* seq_len, int64_t max_seq_len,
+                           float scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return tq::decode_common<false>(fmt, tables, cache, nullptr, batch, n_q_heads, seq_start, seq_len, max_seq_len,
+                                  scale, out, workspace, workspace_bytes, stream,
+                                  tq::kStagePartials | tq::kStageMerge);
 }
 
 tq_status tq_decode_combine(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, int32_t batch,

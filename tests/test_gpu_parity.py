@@ -385,6 +385,66 @@ def test_decode_with_fp16_tail(k_bits, v_bits):
     assert float((out2 - ref2).abs().max()) <= 1e-5 * max(1.0, float(ref2.abs().max()))
 
 
+@pytest.mark.parametrize("k_bits,v_bits,hq,lens", [(4, 4, 28, (300, 45, 0, 129)), (3, 0, 8, (70, 200)),
+                                                     (5, 1, 40, (257, 31))])
+def test_decode_steps_append_prepare_attend(k_bits, v_bits, hq, lens):
+    """The decode step as two launches: tq_append_prepare (each sequence's new
+    token into the packed cache, and the prepared queries), then
+    tq_decode_attend (the pieces merged inside the decode kernel by the last
+    workgroup of each problem).  The workspace starts as all-ones bytes (the
+    preparation zeroes the piece counters); every step is checked against the
+    oracle on the GPU's cache, and a second tq_decode_attend on the same
+    prepared workspace (counters left at zero by the first) agrees with the
+    first.  An empty sequence stays empty (its new token's slot is -1)."""
+    import kv_cache_quantization_norm_amd as tq
+    _say("append_prepare + attend", k_bits, v_bits, hq, lens)
+    L, H, steps, stride = 2, 4, 3, 320
+    B = len(lens)
+    fmt = quant.Format(128, k_bits, v_bits)
+    tfmt = pu.tq_format(fmt)
+    tables = tq.Tables.create(tfmt, list(range(L)))
+    g = torch.Generator().manual_seed(41)
+    starts = [b * stride for b in range(B)]
+    dev = tq.Cache.allocate(tfmt, L, H, B * stride)
+    for b, n in enumerate(lens):
+        if n:
+            k = torch.randn(L, n, H, 128, generator=g).to("cuda", torch.bfloat16)
+            v = torch.randn(L, n, H, 128, generator=g).to("cuda", torch.bfloat16)
+            tq.tq_compress_kv(tfmt, tables, dev, k, v, slot0=starts[b])
+    max_len = max(lens) + steps
+    ws = tq.workspace_for(tfmt, dev, B, hq, max_len)
+    ws.fill_(0xFF)
+    st = torch.tensor(starts, dtype=torch.int64, device="cuda")
+    cur = list(lens)
+    worst = 0.0
+    for step in range(steps):
+        slots = torch.tensor([starts[b] + cur[b] if cur[b] else -1 for b in range(B)], dtype=torch.int64,
+                             device="cuda")
+        cur = [n + 1 if n else 0 for n in cur]
+        kn = torch.randn(L, B, H, 128, generator=g).to("cuda", torch.bfloat16)
+        vn = torch.randn(L, B, H, 128, generator=g).to("cuda", torch.bfloat16)
+        Q = torch.randn(L, B, hq, 128, generator=g).cuda()
+        ln = torch.tensor(cur, dtype=torch.int32, device="cuda")
+        out = torch.full((L, B, hq, 128), float("nan"), device="cuda")
+        out2 = torch.full_like(out, float("nan"))
+        tq.tq_append_prepare(tfmt, tables, dev, kn, vn, Q, max_len, ws, slots=slots)
+        tq.tq_decode_attend(tfmt, tables, dev, B, hq, st, ln, max_len, out, ws)
+        tq.tq_decode_attend(tfmt, tables, dev, B, hq, st, ln, max_len, out2, ws)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        ora = pu.download_cache(dev, fmt)
+        qn = Q.cpu().numpy()
+        for layer in range(L):
+            pi, s, cbk, cbv = pu.oracle_tables(fmt, layer)
+            ref = attention.decode_attention(ora[layer], qn[layer], starts, cur, pi, s, cbk, cbv)
+            worst = max(worst, pu.check_outputs(o[layer], ref))
+            for b, n in enumerate(cur):
+                if n == 0:
+                    assert np.all(o[layer, b] == 0)
+        assert float((out2 - out).abs().max()) <= 1e-5 * max(1.0, float(out.abs().max()))
+    _say("worst out abs", f"{worst:.2e}")
+
+
 def test_serving_loop_with_fp16_tail_and_trigger():
     """The recent-token pattern of the pages, step by step: a compressed
     prefill; each decode step appends its token to an fp16 tail; once the
