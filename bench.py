@@ -4,12 +4,15 @@ One step = one pass of the whole path over the dense 28-layer workload
 (28 layers, 4 KV heads, 28 query heads (GQA 7), head_dim 128, batch 1,
 8192 cached tokens, K 4 bits = 3 Lloyd-Max + 1 QJL, V 4 bits MSE-only):
   1. compress the step's new token (K and V, all 4 KV heads of all 28 layers)
-     into slot 8191 of the packed cache and prepare the step's queries (one
-     tq_append_prepare call: one launch);
+     into slot 8191 of the packed cache;
   2. decode attention for all 28 query heads of all 28 layers over the 8192
-     packed tokens (tq_decode_attend: one launch, the pieces of each problem
-     merged inside the decode kernel by its last workgroup).
-The same step made of tq_compress_kv + tq_decode_attention is timed beside it.
+     packed tokens.
+One tq_decode_step call: the query preparation, then one decode launch whose
+first 28 workgroups compress the new token while the others attend (a wave
+waits for its layer's append only before the chunk that holds slot 8191), the
+pieces of each problem merged inside the kernel by its last workgroup.
+The same step as tq_append_prepare + tq_decode_attend and as tq_compress_kv +
+tq_decode_attention is timed beside it.
 Inputs are seeded synthetic bf16 K/V (per-channel log-normal scales, two
 outlier channels per head) already resident in HBM.  The timed loop rotates
 among enough cache copies to exceed twice the 256 MB Infinity Cache, so
@@ -72,7 +75,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=500)
     p.add_argument("--workload", default="w2")
     p.add_argument("--copies", type=int, default=0, help="cache copies (0 = enough to exceed 2x the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -142,6 +145,10 @@ def main():
     out = torch.empty((L, 1, HQ, D), device=dev)
 
     def step(c):
+        tq.tq_decode_step(fmt, tables, c, k_new, v_new, Q, seq_start, seq_len, T, out, ws, slot0=T - 1,
+                          stream=stream)
+
+    def step_prepare_attend(c):
         tq.tq_append_prepare(fmt, tables, c, k_new, v_new, Q, T, ws, slot0=T - 1, stream=stream)
         tq.tq_decode_attend(fmt, tables, c, 1, HQ, seq_start, seq_len, T, out, ws, stream=stream)
 
@@ -167,15 +174,20 @@ def main():
     step_ms = e0.elapsed_time(e1) / args.steps
 
     # the same step as tq_compress_kv + tq_decode_attention (three launches)
-    for i in range(args.warmup):
-        step_two_calls(caches[i % n_copies])
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        step_two_calls(caches[i % n_copies])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    step_two_calls_ms = e0.elapsed_time(e1) / args.steps
+    # and as tq_append_prepare + tq_decode_attend (two launches)
+    def time_steps(fn):
+        for i in range(args.warmup):
+            fn(caches[i % n_copies])
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(caches[i % n_copies])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    step_two_calls_ms = time_steps(step_two_calls)
+    step_prepare_attend_ms = time_steps(step_prepare_attend)
 
     # decode call alone (query prep + decode kernel), same rotation
     for i in range(args.warmup):
@@ -343,8 +355,9 @@ def main():
         "decode_call": {"us": round(decode_ms * 1e3, 2), "GBs": round(decode_gbs, 1),
                         "bytes": decode_bytes, "kernels": "qprep_kernel + decode_kernel (pieces merged in-kernel)"},
         "decode_step_bytes": step_bytes,
-        "step_launches": "append_prepare_kernel + decode_kernel (pieces merged in-kernel)",
+        "step_launches": "qprep_kernel + decode_kernel (append workgroups, decode, pieces merged in-kernel)",
         "step_two_calls_us": round(step_two_calls_ms * 1e3, 2),
+        "step_append_prepare_attend_us": round(step_prepare_attend_ms * 1e3, 2),
         "compress": {"what": f"bulk prefill {T} tokens x {L} layers x {H} KV heads, one call",
                      "ms": round(bulk_ms, 4),
                      "mtokens_per_s_per_kv_head": round(bulk_tokens / (bulk_ms * 1e-3) / 1e6, 2),

@@ -276,6 +276,26 @@ tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const
                             int32_t n_q_heads, int64_t max_seq_len, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* Device.  A whole decode step: tq_compress_kv(fmt, tables, cache, k, v,
+ * dtype, layer0, n_layers, n_tokens, slots, slot0, stream) followed by
+ * tq_decode_attention(fmt, tables, cache, q, batch, n_q_heads, seq_start,
+ * seq_len, max_seq_len, scale, out, workspace, workspace_bytes, stream), with
+ * their arguments, layouts, ownership and errors; both are checked before
+ * anything is enqueued.  For fewer than 16 tokens it takes two launches: the
+ * query preparation, then the decode kernel, whose first workgroups compress
+ * the new tokens (QJL deep-dive, sections 2 and 5) while the others start
+ * the attention (section 6); a decode wave waits for its layer's append only
+ * before it reads a chunk that may hold a new token (slots [slot0, slot0 +
+ * n_tokens) of each appended plane, or any slot when `slots` is given).  For
+ * 16 or more tokens the two calls are made one after the other.  The
+ * workspace is tq_decode_attention's; calls on one workspace must not
+ * overlap. */
+tq_status tq_decode_step(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, const void* k,
+                         const void* v, int32_t dtype, int32_t layer0, int32_t n_layers, int64_t n_tokens,
+                         const int64_t* slots, int64_t slot0, const float* q, int32_t batch, int32_t n_q_heads,
+                         const int64_t* seq_start, const int32_t* seq_len, int64_t max_seq_len, float scale,
+                         float* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Device.  The scoring half of tq_decode_attention alone (the pages' separate
  * MSE-score and QJL-score kernels, QJL deep-dive section 6): writes the
  * logits l_t defined above to logits[n_layers][batch][n_q_heads][max_seq_len]

@@ -85,6 +85,8 @@ def _load(path: str = LIB_PATH):
         "tq_decode_partials": (I32, [fmtp, tabp, cachep, I32, I32, P, P, I64, F32, P, SZ, P]),
         "tq_decode_combine": (I32, [fmtp, tabp, cachep, I32, I32, I64, P, P, SZ, P]),
         "tq_decode_attend": (I32, [fmtp, tabp, cachep, I32, I32, P, P, I64, F32, P, P, SZ, P]),
+        "tq_decode_step": (I32, [fmtp, tabp, cachep, P, P, I32, I32, I32, I64, P, I64, P, I32, I32, P, P, I64, F32, P,
+                                 P, SZ, P]),
         "tq_status_string": (ctypes.c_char_p, [I32]),
         "tq_last_error": (ctypes.c_char_p, []),
     }
@@ -98,7 +100,8 @@ def _load(path: str = LIB_PATH):
 _lib = _load()
 EXPORTED = ("tq_layer_seed", "tq_make_rotations", "tq_make_codebook", "tq_cache_plane_bytes",
             "tq_decode_workspace_bytes", "tq_decode_split", "tq_compress_kv", "tq_decode_attention", "tq_score",
-            "tq_decode_prepare", "tq_decode_partials", "tq_decode_combine", "tq_decode_attend", "tq_append_prepare",
+            "tq_decode_prepare", "tq_decode_partials", "tq_decode_combine", "tq_decode_attend", "tq_decode_step",
+            "tq_append_prepare",
             "tq_compress_kv_bounded", "tq_decode_attention_tail", "tq_decode_tail_workspace_bytes",
             "tq_status_string", "tq_last_error")
 
@@ -340,6 +343,21 @@ def tq_append_prepare(fmt: tq_format, tables: Tables, cache: Cache, k, v, q, max
                                   _dtype_code(k), layer0, n_layers, n_tokens, _ptr(slots), slot0, _ptr(q), batch, hq,
                                   max_seq_len, _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _stream(stream)), "tq_append_prepare")
+
+
+def tq_decode_step(fmt: tq_format, tables: Tables, cache: Cache, k, v, q, seq_start, seq_len, max_seq_len: int, out,
+                   workspace, layer0: int = 0, slots=None, slot0: int = 0, scale: float = 0.0, stream=None):
+    """tq_compress_kv(k, v, ...) then tq_decode_attention(q, ...): for fewer
+    than 16 tokens two launches, the append inside the decode launch."""
+    assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape and k.dtype == v.dtype
+    n_layers, n_tokens = int(k.shape[0]), int(k.shape[1])
+    _, batch, hq, _ = q.shape
+    assert q.is_contiguous() and out.is_contiguous()
+    tb, cs = tables.struct(), cache.struct()
+    _check(_lib.tq_decode_step(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(k), _ptr(v), _dtype_code(k),
+                               layer0, n_layers, n_tokens, _ptr(slots), slot0, _ptr(q), batch, hq, _ptr(seq_start),
+                               _ptr(seq_len), max_seq_len, scale, _ptr(out), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)), "tq_decode_step")
 
 
 def tail_workspace_for(fmt: tq_format, cache: Cache, batch: int, n_q_heads: int, max_seq_len: int,

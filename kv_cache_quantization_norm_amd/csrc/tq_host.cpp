@@ -77,7 +77,7 @@ SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_he
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   p.qprep_bytes = align(size_t(n_layers) * batch * n_q_heads * 2 * d * sizeof(float));
   p.partial_bytes = align(size_t(n_layers) * batch * n_q_heads * p.seg_max * (d + 2) * sizeof(float));
-  p.counter_bytes = align(size_t(p.problems) * sizeof(uint32_t));
+  p.counter_bytes = align(size_t(p.problems + n_layers) * sizeof(uint32_t));
   p.total_bytes = p.qprep_bytes + p.partial_bytes + p.counter_bytes;
   return p;
 }

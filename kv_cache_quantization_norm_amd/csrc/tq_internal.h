@@ -41,7 +41,7 @@ struct SplitPlan {
   int n_head_groups = 0;
   size_t qprep_bytes = 0;    // [L][B][Hq][2][d] fp32
   size_t partial_bytes = 0;  // [L][B][Hq][seg_max][d + 2] fp32
-  size_t counter_bytes = 0;  // [problems] uint32: pieces written (in-kernel merge)
+  size_t counter_bytes = 0;  // uint32 [problems] pieces written (in-kernel merge), then [n_layers] append counts
   size_t total_bytes = 0;
 };
 

@@ -579,16 +579,31 @@ constexpr int kAppendWaves = 8;
 constexpr int kAppendThreads = kAppendWaves * 64;
 constexpr int kAppendStride = D + 4;  // padded LDS rows
 
+struct AppendSmem {
+  float xs[2 * kAppendItems][kAppendStride];  // K items, then V items
+  float rs[kAppendItems][kAppendStride];      // key residual y - c[idx]
+  float nrm[2 * kAppendItems];
+  float rnrm[kAppendItems];
+  uint32_t krec[kAppendItems][16];
+  uint32_t srec[kAppendItems][4];
+  int64_t slot_of[kAppendItems];
+  float cb[4][16];  // key centroids, key boundaries, value centroids, value boundaries
+};
+
+// `done` (if not null): per layer, a count of finished append workgroups; the
+// workgroup's stores are released at agent scope before its increment (for
+// readers in the same launch).
 template <int MK, int BV>
-__device__ __forceinline__ void append_body(const CompressArgs& a, int group, int layer_rel) {
-  __shared__ __align__(16) float xs[2 * kAppendItems][kAppendStride];  // K items, then V items
-  __shared__ __align__(16) float rs[kAppendItems][kAppendStride];      // key residual y - c[idx]
-  __shared__ float nrm[2 * kAppendItems];
-  __shared__ float rnrm[kAppendItems];
-  __shared__ uint32_t krec[kAppendItems][16];
-  __shared__ uint32_t srec[kAppendItems][4];
-  __shared__ int64_t slot_of[kAppendItems];
-  __shared__ float cb[4][16];  // key centroids, key boundaries, value centroids, value boundaries
+__device__ __forceinline__ void append_body(const CompressArgs& a, int group, int layer_rel, AppendSmem& sm,
+                                            uint32_t* done = nullptr) {
+  auto& xs = sm.xs;
+  auto& rs = sm.rs;
+  auto& nrm = sm.nrm;
+  auto& rnrm = sm.rnrm;
+  auto& krec = sm.krec;
+  auto& srec = sm.srec;
+  auto& slot_of = sm.slot_of;
+  auto& cb = sm.cb;
   constexpr bool ROT = MK > 0 || BV > 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, q = lane >> 4;
@@ -835,10 +850,21 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
             f16_bits(xs[kAppendItems + it][j]);
     }
   }
+  if (done != nullptr) {
+    // every wave's stores and atomics complete (so that the L2 write-back
+    // below covers them), then one release and the count
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_fetch_add(done + layer, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 template <int MK, int BV>
 __global__ __launch_bounds__(kAppendThreads) void compress_append_kernel(CompressArgs a) {
-  append_body<MK, BV>(a, blockIdx.x, blockIdx.y);
+  __shared__ AppendSmem sm;
+  append_body<MK, BV>(a, blockIdx.x, blockIdx.y, sm);
 }
 
 // ===========================================================================
@@ -877,6 +903,14 @@ struct DecodeArgs {
   int64_t max_len;
   float scale;
   float kappa;
+  // Append in the same launch (n_app > 0): workgroups [0, n_app) compress the
+  // call's new tokens (app_groups per layer, layers [app_layer0, app_layer0 +
+  // app_layers) of the cache) and count themselves in app_done[layer]; a
+  // decode wave about to load a chunk that holds one of the plane slots
+  // [app_lo, app_hi) of an appended layer first waits for that count.
+  int n_app, app_groups, app_layer0, app_layers;
+  int64_t app_lo, app_hi;
+  uint32_t* app_done;
 };
 
 // DPP row broadcast: every lane of a 16-lane row reads lane E of its row.
@@ -1067,7 +1101,7 @@ __device__ __forceinline__ half8 deq8_vrep(uint32_t bits, uint32_t lane4, const 
 // wave order, into the piece's partial.
 template <int MK, int BV, bool SCORE>
 __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(
-    DecodeArgs a) {
+    DecodeArgs a, CompressArgs ca) {
   using KL = KLut<(MK > 0 ? MK : 1)>;
   constexpr int NT = kDecodeWaves * 64;
   constexpr int KT = MK > 0 ? KL::E * KL::EW : 1;                        // dwords of the key table
@@ -1101,6 +1135,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   float(*const lw)[16] = reinterpret_cast<float(*)[16]>(dsm + OFF_LW);
   uint32_t* const counter = reinterpret_cast<uint32_t*>(dsm + OFF_CNT);
   half8* const qstage = reinterpret_cast<half8*>(dsm + OFF_Q);
+  static_assert(LDS_BYTES >= int(sizeof(AppendSmem)), "the append role reuses the decode LDS");
+  if constexpr (!SCORE) {
+    // append workgroups first (lowest indices, so they are dispatched first and
+    // never wait behind decode workgroups that wait for them)
+    if (int(blockIdx.x) < a.n_app) {
+      append_body<MK, BV>(ca, int(blockIdx.x) % a.app_groups, int(blockIdx.x) / a.app_groups,
+                          *reinterpret_cast<AppendSmem*>(dsm), a.app_done);
+      return;
+    }
+  }
+  const int wg = int(blockIdx.x) - a.n_app;   // decode workgroup
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1124,6 +1169,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     int64_t slot_base;   // slot of token 0 of the sequence in its (layer, KV head) plane
     int64_t vblk0;       // value block of token 0
     int64_t len;         // tokens of the sequence (clamped)
+    int64_t start;       // plane-local slot of token 0
     int layer, b, hk, hg;
   };
   auto ctx_of = [&](int prob) {
@@ -1147,6 +1193,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     r.slot_base = plane * a.capacity + start;
     r.vblk0 = plane * vblocks + start / kVBlock;
     r.len = len;
+    r.start = start;
     return r;
   };
   // A group: chunks [g0, b_end) of the workgroup's range, covering piece A
@@ -1157,7 +1204,23 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     Run ra, rb;
     int64_t sa, sb, va, vb;   // ticket u's first slot: (u < live_a ? sa : sb) + 32 u; value block likewise + u
     int pa, a_end, b_end, rel_a0, live_a, n_tickets;
+    int xa0, xa1, xb0, xb1;   // tickets [xa0, xa1) (piece A), [xb0, xb1) (B) whose chunks may hold appended slots
     bool has_b;
+  };
+  // Tickets of a piece whose chunks (chunk c: plane slots start + 32 c ..
+  // + 31) meet the appended slots, as [t0, t1) with ticket = c + shift,
+  // within [lo, hi); empty unless the piece's layer is appended.
+  auto app_tickets = [&](const Run& r, int shift, int lo, int hi, int& t0, int& t1) {
+    t0 = 0;
+    t1 = 0;
+    if constexpr (!SCORE) {
+      if (a.n_app == 0 || r.layer < a.app_layer0 || r.layer >= a.app_layer0 + a.app_layers) return;
+      const int64_t c0 = a.app_lo - r.start > 0 ? (a.app_lo - r.start) / kChunk : 0;
+      const int64_t c1 = a.app_hi - r.start > 0 ? (a.app_hi - r.start + kChunk - 1) / kChunk : 0;
+      const int64_t u0 = c0 + shift, u1 = c1 + shift;
+      t0 = int(u0 < lo ? lo : (u0 > hi ? hi : u0));
+      t1 = int(u1 < lo ? lo : (u1 > hi ? hi : u1));
+    }
   };
   auto group_of = [&](int g0, int c_last) {
     Group G;
@@ -1182,6 +1245,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     G.sb = G.rb.slot_base - int64_t(live_a) * kChunk;
     G.va = G.ra.vblk0 + G.rel_a0;
     G.vb = G.rb.vblk0 - live_a;
+    app_tickets(G.ra, -G.rel_a0, 0, live_a, G.xa0, G.xa1);
+    app_tickets(G.rb, live_a, live_a, G.n_tickets, G.xb0, G.xb1);
+    if (!G.has_b) G.xb0 = G.xb1 = 0;
     return G;
   };
 
@@ -1189,6 +1255,27 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   // or piece B's chunk u - live_a.
   auto slot_of = [&](const Group& G, int u) -> int64_t { return (u < G.live_a ? G.sa : G.sb) + int64_t(u) * kChunk; };
   auto vblk_of = [&](const Group& G, int u) -> int64_t { return (u < G.live_a ? G.va : G.vb) + u; };
+
+  // Before the loads of ticket u's chunk: if the chunk may hold a slot that
+  // this launch's append workgroups write, wait (once per piece and wave) for
+  // the layer's append count, then acquire at agent scope so that the loads
+  // see the new records.  Bounded: after about a second the wave goes on.
+  bool app_ok_a = false, app_ok_b = false;
+  auto gate = [&](const Group& G, int u) {
+    if constexpr (!SCORE) {
+      const bool in_xa = u >= G.xa0 && u < G.xa1 && !app_ok_a;
+      const bool in_xb = u >= G.xb0 && u < G.xb1 && !app_ok_b;
+      if (!(in_xa || in_xb)) return;
+      const int layer = in_xa ? G.ra.layer : G.rb.layer;
+      const uint32_t want = uint32_t(a.app_groups);
+      for (int spin = 0; spin < (1 << 20); ++spin) {
+        if (__hip_atomic_load(a.app_done + layer, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) break;
+        __builtin_amdgcn_s_sleep(8);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (in_xa) app_ok_a = true; else app_ok_b = true;
+    }
+  };
 
   // ---- staged query operands (MFMA B operands), per piece: columns 0..7 are
   // the group's query heads as fp16 high parts, columns 8..15 the same heads
@@ -1735,7 +1822,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   float kcl = 0.f, vcl = 0.f;   // lane l: key / value centroid l mod (number of centroids)
   if constexpr (MK > 0) kcl = a.kc[lane & ((1 << MK) - 1)];
   if constexpr (BV > 0) vcl = a.vc[lane & ((1 << BV) - 1)];
-  const int c_first = int(blockIdx.x) * a.chunks_per_wg;
+  const int c_first = wg * a.chunks_per_wg;
   const int c_last = c_first + a.chunks_per_wg < a.total_chunks ? c_first + a.chunks_per_wg : a.total_chunks;
   QItem qitem;
   {
@@ -1751,13 +1838,21 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     // Issued by every wave (no branch, so that the table build below waits
     // only for the codebook loads); a wave without a ticket reads chunk 0 of
     // piece A's sequence, which is in bounds and never used.
+    // (With an append in the launch, a wave without a ticket reads ticket 0's
+    // chunk instead, and every chunk read passes the gate first.)
     const int t0 = wave, t1 = wave + kDecodeWaves;
     pre = t0 < G.n_tickets;
     const int u1 = t1 < G.n_tickets ? t1 : t0;
-    const int64_t s0 = pre ? slot_of(G, t0) : G.ra.slot_base, s1 = pre ? slot_of(G, u1) : G.ra.slot_base;
+    const bool any = G.n_tickets > 0;
+    const int d0 = pre ? t0 : 0, d1 = pre ? u1 : 0;
+    if (any) {
+      gate(G, d0);
+      gate(G, d1);
+    }
+    const int64_t s0 = any ? slot_of(G, d0) : G.ra.slot_base, s1 = any ? slot_of(G, d1) : G.ra.slot_base;
     load_k(s0, K0);
     load_k(s1, K1);
-    load_v(s0, pre ? vblk_of(G, t0) : G.ra.vblk0, V0);
+    load_v(s0, any ? vblk_of(G, d0) : G.ra.vblk0, V0);
   }
 
   // ---- tables (built once, used for every chunk of the workgroup)
@@ -1795,6 +1890,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     if (g0 != c_first) {
       pre = false;
       G = group_of(g0, c_last);
+      app_ok_a = app_ok_b = false;
       stage_load(G.pa, G.has_b, qitem);
       stage_store(G.pa, G.has_b, qitem);
       __syncthreads();
@@ -1820,7 +1916,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
         const ChunkLate late{};
         const int n = G.n_tickets;
         floatx4 m0[2], s0[2], m1[2], s1[2];
+        // (value loads follow the key loads of the same ticket, which passed
+        // the gate)
         if (!pre) {
+          gate(G, t0);
+          gate(G, t1 < n ? t1 : t0);
           load_k(slot_of(G, t0), K0);
           load_k(slot_of(G, t1 < n ? t1 : t0), K1);
           load_v(slot_of(G, t0), vblk_of(G, t0), V0);
@@ -1831,6 +1931,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
 #pragma unroll 1
         for (;;) {
           const uint32_t d3 = draw();
+          gate(G, t2 < n ? t2 : (t1 < n ? t1 : t0));
           load_k(slot_of(G, t2 < n ? t2 : (t1 < n ? t1 : t0)), K0);
           {
             const int u = t1 < n ? t1 : t0;
@@ -1841,6 +1942,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
           const int t3 = uni(d3) - base;
           if (t1 >= limit) { t0 = t1; t1 = t2; t2 = t3; swap = true; break; }
           const uint32_t d4 = draw();
+          gate(G, t3 < n ? t3 : (t2 < n ? t2 : t1));
           load_k(slot_of(G, t3 < n ? t3 : (t2 < n ? t2 : t1)), K1);
           {
             const int u = t2 < n ? t2 : t1;
@@ -1866,6 +1968,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
         while (t0 < limit) {
           const uint32_t d3 = draw();
           ChunkLate late;
+          gate(G, t0);
           load_k(slot_of(G, t0), K0);
           load_v(slot_of(G, t0), vblk_of(G, t0), V0);
           if constexpr (MK == 0 || BV == 0) load_late(rel0 + t0, late);
@@ -1886,13 +1989,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     if (!had_a) flush(false);
     __syncthreads();
     const int next_base = uni(counter[0]);   // every draw of the group is done
-    merge(G.ra, int(blockIdx.x) - (G.pa * cpp) / a.chunks_per_wg);
+    merge(G.ra, wg - (G.pa * cpp) / a.chunks_per_wg);
     arrive(G.pa, G.ra);
     if (G.has_b) {
       __syncthreads();
       flush(had_b);
       __syncthreads();
-      merge(G.rb, int(blockIdx.x) - G.a_end / a.chunks_per_wg);
+      merge(G.rb, wg - G.a_end / a.chunks_per_wg);
       arrive(G.pa + 1, G.rb);
     }
     __syncthreads();
@@ -1909,10 +2012,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
 // 16 v + 4 (l / 16) .. + 3 of both are step v's four k-values, the same k on
 // the A and the B side, so the sum over k is exact in any order.
 // `done` (if not null): the in-kernel merge counts of the decode that follows,
-// zeroed here for the block's problems.
+// zeroed here for the block's problems, followed by one append count per layer.
 template <bool ROT>
 __device__ __forceinline__ void qprep_body(const float* q, const float* pi, const float* s, float* qprep, int batch,
-                                           int H, int Hq, int bx, int b, int layer, uint32_t* done) {
+                                           int H, int Hq, int bx, int b, int layer, int n_layers, uint32_t* done) {
   const int hk = bx >> 2, quarter = bx & 3;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = Hq / H;
@@ -1920,6 +2023,7 @@ __device__ __forceinline__ void qprep_body(const float* q, const float* pi, cons
   if (done != nullptr && quarter == 0) {
     const int n_hg = (G + kMaxGroup - 1) / kMaxGroup;
     for (int hg = tid; hg < n_hg; hg += 256) done[((int64_t(layer) * batch + b) * H + hk) * n_hg + hg] = 0u;
+    if (hk == 0 && b == 0 && tid == 0) done[int64_t(n_layers) * batch * H * n_hg + layer] = 0u;
   }
   if constexpr (!ROT) {
     // fp16 keys are scored against q itself; no sketch.
@@ -1962,7 +2066,7 @@ __device__ __forceinline__ void qprep_body(const float* q, const float* pi, cons
 template <bool ROT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void qprep_kernel(
     const float* q, const float* pi, const float* s, float* qprep, int batch, int H, int Hq, uint32_t* done) {
-  qprep_body<ROT>(q, pi, s, qprep, batch, H, Hq, blockIdx.x, blockIdx.y, blockIdx.z, done);
+  qprep_body<ROT>(q, pi, s, qprep, batch, H, Hq, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, done);
 }
 
 // The append of a few tokens and the query preparation of the same decode
@@ -1973,14 +2077,16 @@ template <int MK, int BV>
 __global__ __launch_bounds__(kAppendThreads) void append_prepare_kernel(
     CompressArgs a, int app_groups, int n_append, const float* q, const float* pi, const float* s, float* qprep,
     int batch, int H, int Hq, uint32_t* done) {
+  __shared__ AppendSmem sm;
   const int bid = blockIdx.x;
   if (bid < n_append) {
-    append_body<MK, BV>(a, bid % app_groups, bid / app_groups);
+    append_body<MK, BV>(a, bid % app_groups, bid / app_groups, sm);
     return;
   }
   if (threadIdx.x >= 256) return;   // the query preparation blocks take 4 waves
   const int r = bid - n_append, nx = H * 4;
-  qprep_body<(MK > 0)>(q, pi, s, qprep, batch, H, Hq, r % nx, (r / nx) % batch, r / (nx * batch), done);
+  qprep_body<(MK > 0)>(q, pi, s, qprep, batch, H, Hq, r % nx, (r / nx) % batch, r / (nx * batch),
+                       (int(gridDim.x) - n_append) / (nx * batch), done);
 }
 
 // Merges the piece partials of one (layer, batch, KV head) for every query
@@ -2152,10 +2258,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 }
 
 template <bool SCORE>
-tq_status launch_decode(int mk, int bv, const DecodeArgs& args, dim3 grid, hipStream_t st) {
+tq_status launch_decode(int mk, int bv, const DecodeArgs& args, dim3 grid, hipStream_t st,
+                        const CompressArgs& ca = CompressArgs{}) {
 #define TQ_DEC(MK_, BV_)                                                                       \
   if (mk == MK_ && bv == BV_) {                                                                \
-    hipLaunchKernelGGL((decode_kernel<MK_, BV_, SCORE>), grid, dim3(kDecodeWaves * 64), 0, st, args); \
+    hipLaunchKernelGGL((decode_kernel<MK_, BV_, SCORE>), grid, dim3(kDecodeWaves * 64), 0, st, args, ca); \
     return TQ_OK;                                                                              \
   }
 #define TQ_DEC_V(MK_) TQ_DEC(MK_, 0) TQ_DEC(MK_, 1) TQ_DEC(MK_, 2) TQ_DEC(MK_, 4)
@@ -2255,11 +2362,20 @@ enum {
   kStageAll = kStagePrepare | kStagePartials | kStageMerge
 };
 
+// An append run by the decode launch's first workgroups (tq_decode_step).
+struct FusedAppend {
+  CompressArgs ca;
+  int groups = 0;            // append workgroups per layer
+  int layers = 0;            // appended layers, from ca.layer0
+  int64_t lo = 0, hi = 0;    // plane slots the append may write
+};
+
 template <bool SCORE>
 tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
                         const float* q, int32_t batch, int32_t n_q_heads, const int64_t* seq_start,
                         const int32_t* seq_len, int64_t max_seq_len, float scale, float* out,
-                        void* workspace, size_t workspace_bytes, void* stream, int stages) {
+                        void* workspace, size_t workspace_bytes, void* stream, int stages,
+                        const FusedAppend* app = nullptr) {
   clear_error();
   tq_status st = check_format(fmt, true);
   if (st) return st;
@@ -2306,9 +2422,19 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
     a.done = done;
     a.out = out;
   }
-  const dim3 grid(unsigned(plan.n_workgroups));
+  if (!SCORE && app != nullptr) {
+    a.n_app = app->groups * app->layers;
+    a.app_groups = app->groups;
+    a.app_layer0 = app->ca.layer0;
+    a.app_layers = app->layers;
+    a.app_lo = app->lo;
+    a.app_hi = app->hi;
+    a.app_done = done + plan.problems;
+  }
+  if (int64_t(a.n_app) + plan.n_workgroups > 0x7FFFFFFF) return fail(TQ_ERR_INVALID_ARG, "too many workgroups");
+  const dim3 grid(unsigned(a.n_app + plan.n_workgroups));
   if (stages & kStagePartials) {
-    if ((st = launch_decode<SCORE>(mk, SCORE ? 0 : bv, a, grid, hs))) return st;
+    if ((st = launch_decode<SCORE>(mk, SCORE ? 0 : bv, a, grid, hs, app ? app->ca : CompressArgs{}))) return st;
     if ((st = launch_status("decode"))) return st;
   }
   if (!SCORE && (stages & kStageCombine) && !(stages & kStageMerge)) {
@@ -2568,6 +2694,40 @@ tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const
 #undef TQ_AP_V
 #undef TQ_AP
   return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for key bits %d / value bits %d", a.mk, a.bv);
+}
+
+tq_status tq_decode_step(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, const void* k,
+                         const void* v, int32_t dtype, int32_t layer0, int32_t n_layers, int64_t n_tokens,
+                         const int64_t* slots, int64_t slot0, const float* q, int32_t batch, int32_t n_q_heads,
+                         const int64_t* seq_start, const int32_t* seq_len, int64_t max_seq_len, float scale,
+                         float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace tq;
+  // Both halves are checked before anything is launched.
+  tq_status st = decode_common<false>(fmt, tables, cache, q, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale,
+                                      out, workspace, workspace_bytes, stream, kStageAll | kStageCheckOnly);
+  if (st) return st;
+  FusedAppend app;
+  int64_t wgs = 0;
+  bool nothing = false;
+  if ((st = compress_setup(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0, 0, app.ca, wgs,
+                           nothing)))
+    return st;
+  if (nothing || n_tokens >= kCompressTile) {
+    // Bulk (or no) compression first, then the decode.
+    if (!nothing && (st = tq_compress_kv(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0,
+                                         stream)))
+      return st;
+    return tq_decode_attention(fmt, tables, cache, q, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, out,
+                               workspace, workspace_bytes, stream);
+  }
+  app.groups = int((n_tokens * app.ca.H + kAppendItems - 1) / kAppendItems);
+  app.layers = n_layers;
+  // Slots the append may write: known on the host for consecutive slots,
+  // otherwise any slot of the plane.
+  app.lo = slots ? 0 : slot0;
+  app.hi = slots ? cache->capacity : slot0 + n_tokens;
+  return decode_common<false>(fmt, tables, cache, q, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, out,
+                              workspace, workspace_bytes, stream, kStageAll, &app);
 }
 
 tq_status tq_decode_attention_tail(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,

@@ -445,6 +445,74 @@ def test_decode_steps_append_prepare_attend(k_bits, v_bits, hq, lens):
     _say("worst out abs", f"{worst:.2e}")
 
 
+@pytest.mark.parametrize("mode,k_bits,v_bits,hq,lens,n_new,layer0", [
+    ("slots", 4, 4, 28, (300, 45, 0, 129), 1, 0),
+    ("slots", 3, 0, 8, (70, 200), 1, 0),
+    ("slot0", 5, 1, 40, (31,), 1, 0),
+    ("slot0", 2, 2, 12, (5,), 3, 0),
+    ("slot0", 0, 4, 16, (100,), 2, 1),
+])
+def test_decode_step_append_inside_decode_launch(mode, k_bits, v_bits, hq, lens, n_new, layer0):
+    """tq_decode_step: the new tokens are compressed by the decode launch's
+    first workgroups while the others attend, each decode wave waiting for its
+    layer's append before it reads a chunk that may hold a new token.  Every
+    step is checked against the oracle on the GPU's cache (which then holds the
+    new tokens).  Cases: one token per sequence through a slots array (any
+    slot may change), consecutive slots from slot0 (new tokens in the first
+    chunk of a 5-token sequence, or crossing into a new chunk), fp16 keys or
+    values, and an append to layer 1 only of a 2-layer cache."""
+    import kv_cache_quantization_norm_amd as tq
+    _say("decode step", mode, k_bits, v_bits, hq, lens, n_new, layer0)
+    L, H, steps, stride = 2, 4, 3, 320
+    B = len(lens)
+    fmt = quant.Format(128, k_bits, v_bits)
+    tfmt = pu.tq_format(fmt)
+    tables = tq.Tables.create(tfmt, list(range(L)))
+    g = torch.Generator().manual_seed(43)
+    starts = [b * stride for b in range(B)]
+    dev = tq.Cache.allocate(tfmt, L, H, B * stride)
+    for b, n in enumerate(lens):
+        if n:
+            k = torch.randn(L, n, H, 128, generator=g).to("cuda", torch.bfloat16)
+            v = torch.randn(L, n, H, 128, generator=g).to("cuda", torch.bfloat16)
+            tq.tq_compress_kv(tfmt, tables, dev, k, v, slot0=starts[b])
+    max_len = max(lens) + steps * n_new
+    ws = tq.workspace_for(tfmt, dev, B, hq, max_len)
+    ws.fill_(0xFF)
+    st = torch.tensor(starts, dtype=torch.int64, device="cuda")
+    cur = list(lens)
+    n_app_layers = L - layer0
+    worst = 0.0
+    for step in range(steps):
+        Q = torch.randn(L, B, hq, 128, generator=g).cuda()
+        if mode == "slots":
+            slots = torch.tensor([starts[b] + cur[b] if cur[b] else -1 for b in range(B)], dtype=torch.int64,
+                                 device="cuda")
+            kn = torch.randn(n_app_layers, B, H, 128, generator=g).to("cuda", torch.bfloat16)
+            vn = torch.randn(n_app_layers, B, H, 128, generator=g).to("cuda", torch.bfloat16)
+            extra = dict(slots=slots)
+            cur = [n + 1 if n else 0 for n in cur]
+        else:
+            kn = torch.randn(n_app_layers, n_new, H, 128, generator=g).to("cuda", torch.bfloat16)
+            vn = torch.randn(n_app_layers, n_new, H, 128, generator=g).to("cuda", torch.bfloat16)
+            extra = dict(slot0=starts[0] + cur[0])
+            cur = [cur[0] + n_new]
+        ln = torch.tensor(cur, dtype=torch.int32, device="cuda")
+        out = torch.full((L, B, hq, 128), float("nan"), device="cuda")
+        tq.tq_decode_step(tfmt, tables, dev, kn, vn, Q, st, ln, max_len, out, ws, layer0=layer0, **extra)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        ora = pu.download_cache(dev, fmt)
+        qn = Q.cpu().numpy()
+        for layer in range(L):
+            pi, s, cbk, cbv = pu.oracle_tables(fmt, layer)
+            # (layers below layer0 get no new tokens: their new slots keep the
+            # zero records of the allocation, read alike by both sides)
+            ref = attention.decode_attention(ora[layer], qn[layer], starts, cur, pi, s, cbk, cbv)
+            worst = max(worst, pu.check_outputs(o[layer], ref))
+    _say("worst out abs", f"{worst:.2e}")
+
+
 def test_serving_loop_with_fp16_tail_and_trigger():
     """The recent-token pattern of the pages, step by step: a compressed
     prefill; each decode step appends its token to an fp16 tail; once the
