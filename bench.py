@@ -240,7 +240,9 @@ def main():
     # decode kernel leaves free (tq_compress_kv_bounded), it runs beside it.
     side = torch.cuda.Stream()
     target = tq.Cache.allocate(fmt, L, H, cap, dev)
-    free_cus = max(1, 256 - tq.tq_decode_split(fmt, L, 1, H, HQ, T)["n_workgroups"])
+    # CUs the step's decode launch leaves free: its decode workgroups and its
+    # append workgroups (one per layer and 8 (token, head) items)
+    free_cus = max(1, 256 - tq.tq_decode_split(fmt, L, 1, H, HQ, T)["n_workgroups"] - L * -(-H // 8))
 
     def overlapped(max_wgs, n_steps):
         ov = []
