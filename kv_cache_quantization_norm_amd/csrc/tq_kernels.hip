@@ -162,14 +162,19 @@ constexpr int kCompressTile = 16;  // tokens per wave step
 constexpr int kCompressWaves = 8;
 constexpr int kCompressWorkgroups = 256;   // one per CU
 constexpr int kQBuckets = 512;
+// Key codes of up to 4 bits per record pack into 16 dwords a token, 7-bit
+// codes (8-bit keys) into 28.
+template <int MK> constexpr int kRecStride = MK > 4 ? 28 : 16;
 struct CompressSmem {
   half8 ph[8 * 4 * 64], pl[8 * 4 * 64];
   half8 mh[8 * 4 * 64], ml[8 * 4 * 64];
   u32x2 kq[kQBuckets], vq[kQBuckets];
-  float kc[16], vc[16];
-  uint32_t rec[kCompressWaves][kCompressTile * 16];   // packed key codes per token (<= 16 dwords)
+  float kc[128], vc[16];
+  // Per wave: the packed key codes of 16 tokens (kRecStride dwords each),
+  // later the value codes of 16 tokens per coordinate (2 D dwords); the key
+  // records are written out before the values are coded.
+  uint32_t recv[kCompressWaves][kCompressTile * 28];
   uint32_t srec[kCompressWaves][kCompressTile * 4];   // packed signs per token
-  uint32_t vrec[kCompressWaves][D * 2];               // value codes of 16 tokens per coordinate
 };
 
 // Lane (t = lane % 16, q = lane / 16) holds coordinates 32q .. 32q+31 of token t.
@@ -212,18 +217,24 @@ __device__ __forceinline__ void load_token_slab(const CompressArgs& a, const voi
   }
 }
 
-// Quantisation table of a codebook with nb < 16 ascending boundaries t_k:
-// bucket u covers y in [-1/2 + u / 512, -1/2 + (u + 1) / 512), the first and
-// last buckets extended to -inf and +inf.  Entry u holds the number of
-// boundaries below L_u = -1/2 + (u - 1/2) / 512 and the first boundary at or
-// above L_u if it lies below L_u + 2 / 512 (+inf otherwise).  The rounded
-// bucket arithmetic puts y in a bucket u with y in [L_u, L_u + 2 / 512), so
-// the code #{k : y >= t_k} is count + [y >= boundary] as long as no two
-// boundaries are closer than 2 / 512: those of the d = 128 codebooks lie in
-// (-0.25, 0.25), more than 0.02 apart.
-__device__ __forceinline__ void build_qtab(u32x2* tab, const float* bnd, int nb, int tid, int nt) {
+// Quantisation table of a codebook with nb ascending boundaries t_k, at
+// scale S (512 buckets of width 1/S over [-256/S, 256/S)): bucket u covers y
+// in [(u - 256) / S, (u - 255) / S), the first and last buckets extended to
+// -inf and +inf.  Entry u holds the number of boundaries below
+// L_u = (u - 256 - 1/2) / S and the first boundary at or above L_u if it lies
+// below L_u + 2 / S (+inf otherwise).  The rounded bucket arithmetic puts y in
+// a bucket u with y in [L_u, L_u + 2 / S), so the code #{k : y >= t_k} is
+// count + [y >= boundary] as long as no two boundaries are closer than 2 / S
+// and all lie inside the table.  S = 512 for up to 4 bits: the d = 128
+// boundaries lie in (-0.25, 0.25), more than 0.02 apart.  S = 512 / 0.7 for 7
+// bits: boundaries within +-0.339, at least 0.00295 apart, against 2 / S =
+// 0.00273.
+constexpr float kQScale = 512.f;
+constexpr float kQScaleWide = 512.f / 0.7f;
+__device__ __forceinline__ void build_qtab(u32x2* tab, const float* bnd, int nb, int tid, int nt,
+                                           float scale = kQScale) {
   for (int u = tid; u < kQBuckets; u += nt) {
-    const float lo = -0.5f + (float(u) - 0.5f) / kQBuckets, hi = lo + 2.f / kQBuckets;
+    const float lo = (float(u - kQBuckets / 2) - 0.5f) / scale, hi = lo + 2.f / scale;
     uint32_t cnt = 0;
     float first = INFINITY;
     for (int k = 0; k < nb; ++k) {
@@ -236,8 +247,8 @@ __device__ __forceinline__ void build_qtab(u32x2* tab, const float* bnd, int nb,
     tab[u] = u32x2{cnt, __float_as_uint(first < hi ? first : INFINITY)};
   }
 }
-__device__ __forceinline__ uint32_t qcode(float y, const u32x2* tab) {
-  float u = fmaf(y, float(kQBuckets), 0.5f * kQBuckets);
+__device__ __forceinline__ uint32_t qcode(float y, const u32x2* tab, float scale = kQScale) {
+  float u = fmaf(y, scale, 0.5f * kQBuckets);
   u = fminf(fmaxf(u, 0.f), float(kQBuckets - 1));   // NaN -> bucket 0 -> code 0
   const u32x2 e = tab[int(u)];
   return e[0] + (y >= __uint_as_float(e[1]) ? 1u : 0u);
@@ -360,13 +371,14 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressA
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = lane & 15, q = lane >> 4;
   const bool need_rot = MK > 0 || BV > 0;
-  if (tid < 16) {
+  constexpr float KQS = MK > 4 ? kQScaleWide : kQScale;
+  if (tid < 128) {
     const int nk = MK > 0 ? (1 << MK) : 0, nv = BV > 0 ? (1 << BV) : 0;
     // Reconstruction values are applied at their stored (fp16) precision.
     sm.kc[tid] = tid < nk ? float(_Float16(a.kc[tid])) : 0.f;
-    sm.vc[tid] = tid < nv ? float(_Float16(a.vc[tid])) : 0.f;
+    if (tid < 16) sm.vc[tid] = tid < nv ? float(_Float16(a.vc[tid])) : 0.f;
   }
-  if constexpr (MK > 0) build_qtab(sm.kq, a.kb, (1 << MK) - 1, tid, kCompressWaves * 64);
+  if constexpr (MK > 0) build_qtab(sm.kq, a.kb, (1 << MK) - 1, tid, kCompressWaves * 64, KQS);
   if constexpr (BV > 0) build_qtab(sm.vq, a.vb, (1 << BV) - 1, tid, kCompressWaves * 64);
   __syncthreads();
 
@@ -400,9 +412,10 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressA
                     ((a.slot0 + tok0) % kCompressTile == 0) && (a.slot0 + tok0 >= 0) &&
                     (a.slot0 + tok0 + kCompressTile <= a.capacity);
 
-  uint32_t* rec = sm.rec[wave];
+  uint32_t* rec = sm.recv[wave];
   uint32_t* srec = sm.srec[wave];
-  uint32_t* vrec = sm.vrec[wave];
+  uint32_t* vrec = sm.recv[wave];   // after the key records are out
+  constexpr int KSTR = kRecStride<MK>;
   const int kwords = 4 * MK;  // dwords per key code record
 
   {
@@ -425,7 +438,7 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressA
       }
     } else {
       const float n = rotate16<XHL>(sm, xr, lane, y);
-      for (int e = lane; e < kCompressTile * 16; e += 64) rec[e] = 0u;
+      for (int e = lane; e < kCompressTile * KSTR; e += 64) rec[e] = 0u;
       srec[lane] = 0u;
       wave_sync();
       float a2 = 0.f;
@@ -435,12 +448,12 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressA
         uint32_t chunk = 0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint32_t idx = qcode(y[tile][r], sm.kq);
+          const uint32_t idx = qcode(y[tile][r], sm.kq, KQS);
           chunk |= idx << (r * MK);
           res[tile][r] = y[tile][r] - sm.kc[idx];
           a2 = fmaf(res[tile][r], res[tile][r], a2);
         }
-        or_bits(rec + t * 16, (16 * tile + 4 * q) * MK, chunk, 4 * MK);
+        or_bits(rec + t * KSTR, (16 * tile + 4 * q) * MK, chunk, 4 * MK);
       }
       a2 += shfl_xor(a2, 16);
       a2 += shfl_xor(a2, 32);
@@ -483,7 +496,7 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressA
         if (tk >= a.n_tokens) continue;
         const int64_t sl = a.slots ? a.slots[tk] : a.slot0 + tk;
         if (sl < 0 || sl >= a.capacity) continue;
-        reinterpret_cast<uint32_t*>(a.k_idx + (plane * a.capacity + sl) * (16 * MK))[w] = rec[tt * 16 + w];
+        reinterpret_cast<uint32_t*>(a.k_idx + (plane * a.capacity + sl) * (16 * MK))[w] = rec[tt * KSTR + w];
       }
       {
         const int tt = lane >> 2, w = lane & 3;
@@ -584,10 +597,12 @@ struct AppendSmem {
   float rs[kAppendItems][kAppendStride];      // key residual y - c[idx]
   float nrm[2 * kAppendItems];
   float rnrm[kAppendItems];
-  uint32_t krec[kAppendItems][16];
+  uint32_t krec[kAppendItems][28];
   uint32_t srec[kAppendItems][4];
   int64_t slot_of[kAppendItems];
-  float cb[4][16];  // key centroids, key boundaries, value centroids, value boundaries
+  // key centroids, key boundaries, value centroids, value boundaries (the
+  // boundary tables padded with +inf)
+  float cb[4][128];
 };
 
 // `done` (if not null): per layer, a count of finished append workgroups; the
@@ -671,24 +686,25 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
     const int64_t tok = (item0 + (tid < ni ? tid : 0)) / a.H;
     if (tid < kAppendItems && tid < ni) slot = a.slots ? a.slots[tok] : a.slot0 + tok;
   }
-  // Codebooks: lane j of wave w < 4 holds entry j of table w (0 past the end;
-  // the boundary tables are padded with +inf).
+  // Codebooks: thread j holds entry j % 128 of table j / 128 (0 past the
+  // end; the boundary tables are padded with +inf).
+  constexpr int NCB = MK > 4 ? 128 : 16;   // entries used per table
   float cbv = 0.f;
   {
     const int nk = MK > 0 ? (1 << MK) : 0, nv = BV > 0 ? (1 << BV) : 0;
-    const int j = lane;
-    if (j < 16) {
-      if (wave == 0 && j < nk) cbv = float(_Float16(a.kc[j]));   // stored (fp16) reconstruction value
-      if (wave == 1) cbv = j + 1 < nk ? a.kb[j] : INFINITY;
-      if (wave == 2 && j < nv) cbv = float(_Float16(a.vc[j]));
-      if (wave == 3) cbv = j + 1 < nv ? a.vb[j] : INFINITY;
+    const int tb = tid >> 7, j = tid & 127;
+    if (j < NCB) {
+      if (tb == 0 && j < nk) cbv = float(_Float16(a.kc[j]));   // stored (fp16) reconstruction value
+      if (tb == 1) cbv = j + 1 < nk ? a.kb[j] : INFINITY;
+      if (tb == 2 && j < nv) cbv = float(_Float16(a.vc[j]));
+      if (tb == 3) cbv = j + 1 < nv ? a.vb[j] : INFINITY;
     }
   }
   // Every global load above is in flight before any of them is waited on.
   __builtin_amdgcn_sched_barrier(0);
   if (tid < kAppendItems) slot_of[tid] = (slot < 0 || slot >= a.capacity) ? -1 : slot;
-  if (wave < 4 && lane < 16) cb[wave][lane] = cbv;
-  for (int e = tid; e < kAppendItems * 16; e += kAppendThreads) (&krec[0][0])[e] = 0u;
+  if ((tid & 127) < NCB) cb[tid >> 7][tid & 127] = cbv;
+  for (int e = tid; e < kAppendItems * 28; e += kAppendThreads) (&krec[0][0])[e] = 0u;
   if (tid < kAppendItems * 4) (&srec[0][0])[tid] = 0u;
 #pragma unroll
   for (int u = 0; u < XU; ++u) {
@@ -753,8 +769,15 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             uint32_t idx = 0;
+            if constexpr (MK > 4) {
+              // binary search: #{k : y >= t_k} over the ascending boundaries
 #pragma unroll
-            for (int b = 0; b < (1 << MK) - 1; ++b) idx += (y[r] >= cb[1][b]) ? 1u : 0u;
+              for (int step = 1 << (MK - 1); step >= 1; step >>= 1)
+                if (y[r] >= cb[1][idx + step - 1]) idx += step;
+            } else {
+#pragma unroll
+              for (int b = 0; b < (1 << MK) - 1; ++b) idx += (y[r] >= cb[1][b]) ? 1u : 0u;
+            }
             rs[it][row + r] = y[r] - cb[0][idx];
             chunk |= idx << (r * MK);
           }
@@ -821,21 +844,23 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
   }
   __syncthreads();
 
-  // ---------------- records
-  for (int e = tid; e < kAppendItems * 32; e += kAppendThreads) {
-    const int it = e >> 5, w = e & 31;
+  // ---------------- records: per item, code words [0, 4 MK), sign words
+  // [SB, SB + 4), then the three norms
+  constexpr int NE = MK > 4 ? 64 : 32, SB = MK > 4 ? 32 : 16;
+  for (int e = tid; e < kAppendItems * NE; e += kAppendThreads) {
+    const int it = e / NE, w = e % NE;
     const int64_t slot = slot_of[it];
     if (it >= ni || slot < 0) continue;
     const int64_t plane = int64_t(layer) * a.H + (item0 + it) % a.H;
     const int64_t rec = plane * a.capacity + slot;
     if constexpr (MK > 0) {
       if (w < 4 * MK) reinterpret_cast<uint32_t*>(a.k_idx + rec * (16 * MK))[w] = krec[it][w];
-      if (w >= 16 && w < 20) reinterpret_cast<uint32_t*>(a.k_sign + rec * 16)[w - 16] = srec[it][w - 16];
-      if (w == 20) a.k_norm[rec] = nrm[it];
-      if (w == 21) a.k_rnorm[rec] = rnrm[it];
+      if (w >= SB && w < SB + 4) reinterpret_cast<uint32_t*>(a.k_sign + rec * 16)[w - SB] = srec[it][w - SB];
+      if (w == SB + 4) a.k_norm[rec] = nrm[it];
+      if (w == SB + 5) a.k_rnorm[rec] = rnrm[it];
     }
     if constexpr (BV > 0) {
-      if (w == 22) a.v_norm[rec] = nrm[kAppendItems + it];
+      if (w == SB + 6) a.v_norm[rec] = nrm[kAppendItems + it];
     }
   }
   if constexpr (MK == 0 || BV == 0) {
@@ -1055,6 +1080,24 @@ __device__ __forceinline__ half8 deq8_k(uint32_t bits, const uint32_t* khi) {
   }
 }
 
+// 8 consecutive m-bit key codes, m > 4 (bits [8 m s, 8 m s + 8 m) of a
+// lane's 32-coordinate slab of m dwords) -> 8 fp16 centroids from the
+// 2^m-entry fp16 table: one lookup per code (a table of code pairs would not
+// fit beside the value tables).
+template <int M, int N>
+__device__ __forceinline__ half8 deq8_wide(const uint32_t (&w)[N], int s, const uint16_t* lut) {
+  constexpr uint32_t mask = (1u << M) - 1u;
+  uint32_t h[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int p = 8 * M * s + M * j, lo = p >> 5, sh = p & 31;
+    const uint32_t c =
+        sh + M <= 32 ? (w[lo] >> sh) & mask : __builtin_amdgcn_alignbit(w[lo + 1 < N ? lo + 1 : lo], w[lo], sh) & mask;
+    h[j] = lut[c];
+  }
+  return as_half8(u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)});
+}
+
 // Bits [8 m s, 8 m s + 8 m) of a lane's 32-coordinate slab (m dwords).
 template <int M, int N>
 __device__ __forceinline__ uint32_t slab_bits(const uint32_t (&w)[N], int s) {
@@ -1102,10 +1145,11 @@ __device__ __forceinline__ half8 deq8_vrep(uint32_t bits, uint32_t lane4, const 
 template <int MK, int BV, bool SCORE>
 __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(
     DecodeArgs a, CompressArgs ca) {
-  using KL = KLut<(MK > 0 ? MK : 1)>;
+  constexpr bool KWIDE = MK > 4;   // 7-bit codes: one fp16 table entry per code
+  using KL = KLut<(MK > 0 && !KWIDE ? MK : 1)>;
   constexpr int NT = kDecodeWaves * 64;
-  constexpr int KT = MK > 0 ? KL::E * KL::EW : 1;                        // dwords of the key table
-  constexpr int KP = MK > 0 && KL::NC > 2 ? KL::PAIRS : 1;                // pair-table dwords (if separate)
+  constexpr int KT = MK > 0 ? (KWIDE ? (1 << MK) / 2 : KL::E * KL::EW) : 1;   // dwords of the key table
+  constexpr int KP = MK > 0 && !KWIDE && KL::NC > 2 ? KL::PAIRS : 1;          // pair-table dwords (if separate)
   constexpr bool VREP = BV == 4;                                          // lane-private value table
   constexpr int VW = VREP ? 256 * 64 : (BV > 0 ? Lut<BV, false>::WORDS : 1);
   // Tables first, each starting below 64 KB so that lookups carry the table
@@ -1443,7 +1487,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
         half8 kh[4], sd[4];
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-          kh[s2] = deq8_k<MK>(slab_bits<MK>(K.kw[T], s2), lut_k);
+          if constexpr (KWIDE)
+            kh[s2] = deq8_wide<MK>(K.kw[T], s2, reinterpret_cast<const uint16_t*>(lut_k));
+          else
+            kh[s2] = deq8_k<MK>(slab_bits<MK>(K.kw[T], s2), lut_k);
           sd[s2] = *reinterpret_cast<const half8*>(lut_s + ((K.sg[T] >> (8 * s2)) & 0xFFu) * 4);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1856,7 +1903,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   }
 
   // ---- tables (built once, used for every chunk of the workgroup)
-  if constexpr (MK > 0) {
+  if constexpr (KWIDE) {
+    // stored (fp16) reconstruction values, straight from the codebook
+    for (int x = tid; x < (1 << MK); x += NT) reinterpret_cast<uint16_t*>(lut_k)[x] = f16_bits(a.kc[x]);
+  } else if constexpr (MK > 0) {
     if constexpr (KL::NC > 2)
       build_kpairs<MK>(pair_hi, kcl, tid, NT);
     else
@@ -1879,7 +1929,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   stage_store(G.pa, G.has_b, qitem);
   if (tid == 0) counter[0] = 0;
   __syncthreads();
-  if constexpr (MK > 0 && KL::NC > 2) {
+  if constexpr (MK > 0 && !KWIDE && KL::NC > 2) {
     build_ktab<MK, NT>(lut_k, pair_hi, tid);
     __syncthreads();
   }
@@ -2268,9 +2318,9 @@ tq_status launch_decode(int mk, int bv, const DecodeArgs& args, dim3 grid, hipSt
 #define TQ_DEC_V(MK_) TQ_DEC(MK_, 0) TQ_DEC(MK_, 1) TQ_DEC(MK_, 2) TQ_DEC(MK_, 4)
   if constexpr (SCORE) {
     // Scores do not read values: one instantiation per key format.
-    TQ_DEC(0, 0) TQ_DEC(1, 0) TQ_DEC(2, 0) TQ_DEC(3, 0) TQ_DEC(4, 0)
+    TQ_DEC(0, 0) TQ_DEC(1, 0) TQ_DEC(2, 0) TQ_DEC(3, 0) TQ_DEC(4, 0) TQ_DEC(7, 0)
   } else {
-    TQ_DEC_V(0) TQ_DEC_V(1) TQ_DEC_V(2) TQ_DEC_V(3) TQ_DEC_V(4)
+    TQ_DEC_V(0) TQ_DEC_V(1) TQ_DEC_V(2) TQ_DEC_V(3) TQ_DEC_V(4) TQ_DEC_V(7)
   }
 #undef TQ_DEC_V
 #undef TQ_DEC
@@ -2624,7 +2674,7 @@ tq_status tq_compress_kv_bounded(const tq_format* fmt, const tq_tables* tables, 
     return launch_status("compress (append)");                                                         \
   }
 #define TQ_APP_V(MK_) TQ_APP(MK_, 0) TQ_APP(MK_, 1) TQ_APP(MK_, 2) TQ_APP(MK_, 4)
-    TQ_APP_V(0) TQ_APP_V(1) TQ_APP_V(2) TQ_APP_V(3) TQ_APP_V(4)
+    TQ_APP_V(0) TQ_APP_V(1) TQ_APP_V(2) TQ_APP_V(3) TQ_APP_V(4) TQ_APP_V(7)
 #undef TQ_APP_V
 #undef TQ_APP
     return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for key bits %d / value bits %d", a.mk, a.bv);
@@ -2636,7 +2686,7 @@ tq_status tq_compress_kv_bounded(const tq_format* fmt, const tq_tables* tables, 
     fn = a.dtype == TQ_DTYPE_F32 ? reinterpret_cast<const void*>(compress_kernel<MK_, BV_, true>)   \
                                  : reinterpret_cast<const void*>(compress_kernel<MK_, BV_, false>);
 #define TQ_CMP_V(MK_) TQ_CMP(MK_, 0) TQ_CMP(MK_, 1) TQ_CMP(MK_, 2) TQ_CMP(MK_, 4)
-  TQ_CMP_V(0) TQ_CMP_V(1) TQ_CMP_V(2) TQ_CMP_V(3) TQ_CMP_V(4)
+  TQ_CMP_V(0) TQ_CMP_V(1) TQ_CMP_V(2) TQ_CMP_V(3) TQ_CMP_V(4) TQ_CMP_V(7)
 #undef TQ_CMP_V
 #undef TQ_CMP
   if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for key bits %d / value bits %d", a.mk, a.bv);
@@ -2690,7 +2740,7 @@ tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const
     return launch_status("append + prepare");                                                                  \
   }
 #define TQ_AP_V(MK_) TQ_AP(MK_, 0) TQ_AP(MK_, 1) TQ_AP(MK_, 2) TQ_AP(MK_, 4)
-  TQ_AP_V(0) TQ_AP_V(1) TQ_AP_V(2) TQ_AP_V(3) TQ_AP_V(4)
+  TQ_AP_V(0) TQ_AP_V(1) TQ_AP_V(2) TQ_AP_V(3) TQ_AP_V(4) TQ_AP_V(7)
 #undef TQ_AP_V
 #undef TQ_AP
   return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for key bits %d / value bits %d", a.mk, a.bv);

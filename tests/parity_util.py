@@ -124,7 +124,14 @@ def compare_layer(gpu: dict, ora: dict, details: Dict, fmt: quant.Format, slots:
             stats["coords"] += bad.size
             # norms
             np.testing.assert_allclose(gpu["k_norm"][h, slots], det["norm"], rtol=1e-6, atol=1e-30)
-            np.testing.assert_allclose(gpu["k_rnorm"][h, slots], det["rnorm"], rtol=2e-6, atol=1e-6 * det["norm"].max())
+            # residual norm rho = ||x|| ||y - c[idx]||, taken with the device's own
+            # codes: a near-boundary code flip moves the residual, and with the
+            # fp16-stored centroids of a 128-level codebook the two sides of a
+            # boundary differ by up to ~1e-3 of rho
+            y = np.asarray(det["y"], np.float64)
+            cst = np.asarray(cbk[0], np.float64)
+            rho_dev = det["norm"] * np.sqrt(np.sum((y - cst[gi]) ** 2, axis=1))
+            np.testing.assert_allclose(gpu["k_rnorm"][h, slots], rho_dev, rtol=2e-6, atol=1e-6 * det["norm"].max())
             # signs, on tokens whose codes agree (a code flip changes the residual)
             same = ~bad.any(axis=1)
             stats["tokens_skipped_for_signs"] += int((~same).sum())

@@ -53,6 +53,9 @@ CASES = {
     # 320 short problems: several groups of pieces per workgroup
     "many_short_b40": wl.Workload("many_short_b40", 1, 8, 16, wl.ragged_lengths(39, 1, 200, seed=4) + (200,),
                                   3, 2, "f32", 0.3, 0, 1.0),
+    # 8-bit keys (7 Lloyd-Max bits + QJL) with 4-bit values, the wide key path
+    "k8v4_ragged": wl.Workload("k8v4_ragged", 2, 2, 14, (300, 77), 8, 4, "bf16", 0.5, 1, 10.0),
+    "k8v2_f32": wl.Workload("k8v2_f32", 1, 4, 32, (129,), 8, 2, "f32", 0.0, 0, 1.0),
 }
 
 
@@ -161,7 +164,7 @@ def test_decode_parity_on_oracle_cache(case):
         _say("format", fmt, "worst logit rel", f"{worst_l:.2e}", "worst out abs", f"{worst_o:.2e}")
 
 
-@pytest.mark.parametrize("case", ["w1", "w2_4L_ragged", "w3_6L_asym", "w5_ragged5"])
+@pytest.mark.parametrize("case", ["w1", "w2_4L_ragged", "w3_6L_asym", "w5_ragged5", "k8v4_ragged"])
 def test_end_to_end(case):
     """GPU compress + GPU decode against oracle compress + oracle decode, on
     inputs with no decision within 1e-6 of its threshold (there the output is
@@ -260,7 +263,8 @@ def test_degenerate_vectors_and_nan(chunk):
     pu.check_outputs(out[0, :1], ref)
 
 
-@pytest.mark.parametrize("k_bits,v_bits,dtype", [(4, 2, "bf16"), (3, 4, "f32"), (5, 1, "f16"), (2, 0, "f32")])
+@pytest.mark.parametrize("k_bits,v_bits,dtype", [(4, 2, "bf16"), (3, 4, "f32"), (5, 1, "f16"), (2, 0, "f32"),
+                                                 (8, 4, "bf16")])
 def test_overwrite_slot_and_append(k_bits, v_bits, dtype):
     """Re-compressing into used slots replaces their records (value codes are
     rewritten inside shared 32-slot groups), one token at a time."""
@@ -283,6 +287,7 @@ def test_overwrite_slot_and_append(k_bits, v_bits, dtype):
     for i in range(70):
         tq.tq_compress_kv(tfmt, tables, dev, kr[:, i:i + 1].contiguous(), vr[:, i:i + 1].contiguous(), slot0=i)
     torch.cuda.synchronize()
+    _say("appends done")
     gpu = pu.download_cache(dev, fmt)
     for layer in (0, 1):
         c, det = pu.oracle_compress_layer(w, layer, fmt, K[layer], V[layer], slots, cap)
@@ -451,6 +456,7 @@ def test_decode_steps_append_prepare_attend(k_bits, v_bits, hq, lens):
     ("slot0", 5, 1, 40, (31,), 1, 0),
     ("slot0", 2, 2, 12, (5,), 3, 0),
     ("slot0", 0, 4, 16, (100,), 2, 1),
+    ("slots", 8, 4, 28, (300, 45, 0, 129), 1, 0),
 ])
 def test_decode_step_append_inside_decode_launch(mode, k_bits, v_bits, hq, lens, n_new, layer0):
     """tq_decode_step: the new tokens are compressed by the decode launch's

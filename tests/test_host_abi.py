@@ -62,12 +62,17 @@ def test_rotations_match_oracle(d, layer):
     assert np.max(np.abs(p64.T @ p64 - np.eye(d))) < 2e-6
 
 
-@pytest.mark.parametrize("d,bits", [(128, 1), (128, 2), (128, 3), (128, 4), (64, 2), (32, 3)])
+@pytest.mark.parametrize("d,bits", [(128, 1), (128, 2), (128, 3), (128, 4), (128, 7), (64, 2), (32, 3)])
 def test_codebook_matches_oracle(d, bits):
     c, t = tq.tq_make_codebook(d, bits)
     oc, ot = codebook.codebook(d, bits)
-    assert np.max(np.abs(c - oc)) < 1e-12
-    assert np.max(np.abs(t - ot)) < 1e-12
+    # 128 levels: the Lloyd iteration converges slowly and settles at a
+    # rounding floor; the two solvers stop at different points near the fixed
+    # point (a few 1e-12 apart); the fp32 tables the device uses are identical
+    # (below)
+    tol = 1e-11 if bits >= 7 else 1e-12
+    assert np.max(np.abs(c - oc)) < tol
+    assert np.max(np.abs(t - ot)) < tol
     assert np.array_equal(c, -c[::-1]) and t[len(t) // 2] == 0.0
     # fp32 tables (what the device uses) round identically
     assert np.array_equal(c.astype(np.float32), oc.astype(np.float32))
@@ -78,7 +83,7 @@ def test_codebook_matches_oracle(d, bits):
     assert np.array_equal(c.astype(np.float32).astype(np.float16).astype(np.float64), sc)
 
 
-@pytest.mark.parametrize("kb,vb", [(3, 2), (4, 4), (0, 4), (0, 0), (5, 1), (2, 2)])
+@pytest.mark.parametrize("kb,vb", [(3, 2), (4, 4), (0, 4), (0, 0), (5, 1), (2, 2), (8, 4)])
 def test_plane_sizes_match_oracle_layout(kb, vb):
     fmt = tq.make_format(128, kb, vb)
     sizes = dict(zip(tq.PLANES, tq.tq_cache_plane_bytes(fmt, 3, 2, 96)))
@@ -115,6 +120,9 @@ def test_device_calls_validate_before_launch():
     tb, cs = _tables_struct(fmt), _cache_struct()
     # unsupported format on device
     assert r("tq_compress_kv", P(tq.make_format(64, 4, 4)), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_UNSUPPORTED
+    for kb in (6, 7, 9):   # 8-bit keys (7 Lloyd-Max bits) are the one wide format
+        assert r("tq_compress_kv", P(tq.make_format(128, kb, 4)), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_UNSUPPORTED
+    assert r("tq_compress_kv", P(tq.make_format(128, 8, 4)), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 0, None, 0, None) == tq.TQ_OK
     assert r("tq_compress_kv", P(tq.make_format(128, 4, 3)), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_UNSUPPORTED
     assert r("tq_compress_kv", P(tq.make_format(128, 6, 4)), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_UNSUPPORTED
     # NULL and inconsistent arguments

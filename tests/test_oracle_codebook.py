@@ -23,7 +23,7 @@ def test_density_matches_beta_law_and_normalises(d):
     assert abs(total - 1) < 1e-10
 
 
-@pytest.mark.parametrize("d,bits", [(128, 1), (128, 2), (128, 3), (128, 4), (64, 3), (32, 2)])
+@pytest.mark.parametrize("d,bits", [(128, 1), (128, 2), (128, 3), (128, 4), (128, 7), (64, 3), (32, 2)])
 def test_lloyd_max_conditions_by_independent_quadrature(d, bits):
     c, t = codebook.codebook(d, bits)
     n = 1 << bits
