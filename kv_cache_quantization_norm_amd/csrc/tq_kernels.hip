@@ -605,9 +605,11 @@ struct AppendSmem {
   float cb[4][128];
 };
 
-// `done` (if not null): per layer, a count of finished append workgroups; the
-// workgroup's stores are released at agent scope before its increment (for
-// readers in the same launch).
+// `done` (if not null): per layer, a count of finished append workgroups, for
+// readers in the same launch.  The records are written with agent-scope
+// (device-coherent) stores, the value codes with device atomics, and every
+// wave waits for them to complete before the barrier that precedes the
+// increment.
 template <int MK, int BV>
 __device__ __forceinline__ void append_body(const CompressArgs& a, int group, int layer_rel, AppendSmem& sm,
                                             uint32_t* done = nullptr) {
@@ -853,14 +855,16 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
     if (it >= ni || slot < 0) continue;
     const int64_t plane = int64_t(layer) * a.H + (item0 + it) % a.H;
     const int64_t rec = plane * a.capacity + slot;
+    auto st32 = [](uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    auto stf = [](float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
     if constexpr (MK > 0) {
-      if (w < 4 * MK) reinterpret_cast<uint32_t*>(a.k_idx + rec * (16 * MK))[w] = krec[it][w];
-      if (w >= SB && w < SB + 4) reinterpret_cast<uint32_t*>(a.k_sign + rec * 16)[w - SB] = srec[it][w - SB];
-      if (w == SB + 4) a.k_norm[rec] = nrm[it];
-      if (w == SB + 5) a.k_rnorm[rec] = rnrm[it];
+      if (w < 4 * MK) st32(reinterpret_cast<uint32_t*>(a.k_idx + rec * (16 * MK)) + w, krec[it][w]);
+      if (w >= SB && w < SB + 4) st32(reinterpret_cast<uint32_t*>(a.k_sign + rec * 16) + (w - SB), srec[it][w - SB]);
+      if (w == SB + 4) stf(a.k_norm + rec, nrm[it]);
+      if (w == SB + 5) stf(a.k_rnorm + rec, rnrm[it]);
     }
     if constexpr (BV > 0) {
-      if (w == SB + 6) a.v_norm[rec] = nrm[kAppendItems + it];
+      if (w == SB + 6) stf(a.v_norm + rec, nrm[kAppendItems + it]);
     }
   }
   if constexpr (MK == 0 || BV == 0) {
@@ -869,21 +873,20 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
       const int64_t slot = slot_of[it];
       if (it >= ni || slot < 0) continue;
       const int64_t plane = int64_t(layer) * a.H + (item0 + it) % a.H;
-      if constexpr (MK == 0) a.k_f16[(plane * a.capacity + slot) * D + j] = f16_bits(xs[it][j]);
+      if constexpr (MK == 0)
+        __hip_atomic_store(a.k_f16 + (plane * a.capacity + slot) * D + j, f16_bits(xs[it][j]), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       if constexpr (BV == 0)
-        a.v_f16[((plane * vblocks + slot / kVBlock) * D + j) * kVBlock + slot % kVBlock] =
-            f16_bits(xs[kAppendItems + it][j]);
+        __hip_atomic_store(a.v_f16 + ((plane * vblocks + slot / kVBlock) * D + j) * kVBlock + slot % kVBlock,
+                           f16_bits(xs[kAppendItems + it][j]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (done != nullptr) {
-    // every wave's stores and atomics complete (so that the L2 write-back
-    // below covers them), then one release and the count
+    // every wave's stores and atomics complete, then the count (an agent-scope
+    // release fence would also write back the XCD's whole L2)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __hip_atomic_fetch_add(done + layer, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (tid == 0) __hip_atomic_fetch_add(done + layer, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 template <int MK, int BV>
@@ -1189,7 +1192,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       return;
     }
   }
-  const int wg = int(blockIdx.x) - a.n_app;   // decode workgroup
+  // Decode workgroup, XCD-aware: workgroups are dispatched to the 8 XCDs
+  // round robin, so physical decode index i runs on the XCD of i % 8; logical
+  // index j gives each XCD one contiguous range of the chunk sequence (both
+  // pieces of a problem, and the problems of a layer, share an L2).
+  int wg;
+  {
+    const int i = int(blockIdx.x) - a.n_app, nd = int(gridDim.x) - a.n_app;
+    const int r = i & 7, qd = nd >> 3, rem = nd & 7;
+    wg = r * qd + (r < rem ? r : rem) + (i >> 3);
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
