@@ -366,7 +366,7 @@ def main():
                      "mtoken_heads_per_s": round(bulk_tokens * H / (bulk_ms * 1e-3) / 1e6, 2)},
         "decode_with_tail": {"tail_tokens": TT, "packed_tokens": T, "us": round(tail_ms * 1e3, 2),
                              "decode_call_us": round(decode_ms * 1e3, 2),
-                             "kernels": "qprep_kernel x 2 + decode_kernel (packed) + decode_kernel (fp16 tail) + combine_kernel"},
+                             "kernels": "qprep_kernel (rotated and plain) + decode_kernel (fp16 tail) + decode_kernel (packed, merges both piece sets)"},
         "background_recompress": {
             "what": f"bulk compress of the {L} x {T}-token prefill on a second stream while decode steps run",
             "decode_steps": n_ov, "step_us_alone": round(step_ms * 1e3, 2),

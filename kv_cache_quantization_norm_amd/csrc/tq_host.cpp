@@ -91,8 +91,9 @@ TailPlan plan_decode_tail(int d, int n_layers, int batch, int n_kv_heads, int n_
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   t.qplain_offset = t.packed.qprep_bytes;
   t.partial_offset = 2 * t.packed.qprep_bytes;
-  t.total_bytes =
+  t.counter_offset =
       t.partial_offset + align(size_t(n_layers) * batch * n_q_heads * t.seg_total * (d + 2) * sizeof(float));
+  t.total_bytes = t.counter_offset + t.packed.counter_bytes;
   return t;
 }
 

@@ -51,12 +51,12 @@ SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_he
 
 // Decode over a packed cache plus an fp16 tail: each part has its own split;
 // the workspace holds the prepared queries twice (for the packed part, then
-// plain for the tail) and the partials of both parts, the tail's pieces in
-// the slots after the packed part's: [L][B][Hq][packed.seg_max +
-// tail.seg_max][d + 2] fp32.
+// plain for the tail), the partials of both parts, the tail's pieces in the
+// slots after the packed part's: [L][B][Hq][packed.seg_max +
+// tail.seg_max][d + 2] fp32, and the packed part's merge counters.
 struct TailPlan {
   SplitPlan packed, tail;
-  size_t qplain_offset = 0, partial_offset = 0, total_bytes = 0;
+  size_t qplain_offset = 0, partial_offset = 0, counter_offset = 0, total_bytes = 0;
   int64_t seg_total = 0;
 };
 TailPlan plan_decode_tail(int d, int n_layers, int batch, int n_kv_heads, int n_q_heads, int64_t max_seq_len,

@@ -939,6 +939,12 @@ struct DecodeArgs {
   int n_app, app_groups, app_layer0, app_layers;
   int64_t app_lo, app_hi;
   uint32_t* app_done;
+  // In-kernel merge over a second piece set (tail_cpp > 0): the pieces of a
+  // decode over an fp16 tail of the same sequences, written by an earlier
+  // launch into the slots from tail_base on (its split: tail_cpp chunks per
+  // problem, tail_cpw per workgroup); fp16 values accumulate as stored, so
+  // with rotated values their part is added after Pi^T.
+  int tail_base, tail_cpp, tail_cpw;
 };
 
 // DPP row broadcast: every lane of a 16-lane row reads lane E of its row.
@@ -1800,7 +1806,51 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
           M[k] = Mn;
         }
       }
-      float* const res = red;   // [16][D]: heads, rows >= ng zero
+      // the tail's pieces, after the packed ones (into At with rotated values)
+      float At[2] = {0.f, 0.f};
+      if (a.tail_cpp > 0) {
+        const int ft = prob * a.tail_cpp;
+        const int nsegt = (ft + a.tail_cpp - 1) / a.tail_cpw - ft / a.tail_cpw + 1;
+        for (int sp0 = 0; sp0 < nsegt; sp0 += SB) {
+          float ms[2][SB], ls[2][SB], as[2][SB];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int g = (tid >> 7) + 4 * k < ng ? (tid >> 7) + 4 * k : ng - 1;
+            const float* P = a.partial + ((row0 + g) * a.seg_max + a.tail_base) * (D + 2);
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+              const int64_t sp = sp0 + u < nsegt ? sp0 + u : nsegt - 1;
+              ms[k][u] = P[sp * (D + 2)];
+              ls[k][u] = P[sp * (D + 2) + 1];
+              as[k][u] = P[sp * (D + 2) + 2 + i];
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            float Mn = M[k];
+#pragma unroll
+            for (int u = 0; u < SB; ++u)
+              if (sp0 + u < nsegt) Mn = fmaxf(Mn, ms[k][u]);
+            const float f0 = M[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[k] - Mn);
+            L[k] *= f0;
+            A[k] *= f0;
+            At[k] *= f0;
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+              const float f =
+                  (sp0 + u >= nsegt || ms[k][u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[k][u] - Mn);
+              L[k] = fmaf(ls[k][u], f, L[k]);
+              if constexpr (ROT)
+                At[k] = fmaf(as[k][u], f, At[k]);
+              else
+                A[k] = fmaf(as[k][u], f, A[k]);
+            }
+            M[k] = Mn;
+          }
+        }
+      }
+      float* const res = red;            // [16][D]: heads, rows >= ng zero
+      float* const resp = red + 16 * D;  // [16][D]: the tail's part (stored domain)
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int g = (tid >> 7) + 4 * k;
@@ -1810,6 +1860,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
         if constexpr (ROT) {
           res[g * D + i] = g < ng ? v : 0.f;
           res[(g + 8) * D + i] = 0.f;
+          resp[g * D + i] = (g < ng && has) ? At[k] / L[k] : 0.f;
         } else if (g < ng) {
           a.out[(row0 + g) * D + i] = v;
         }
@@ -1829,7 +1880,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
           acc = mfma16x16x4f32(pa[4 * v + 3], b4[v].w, acc);
         }
         if (r16 < ng) {
-          const float4 o = {acc[0], acc[1], acc[2], acc[3]};
+          const float4 t = *reinterpret_cast<const float4*>(resp + r16 * D + 16 * wave + 4 * kq);
+          const float4 o = {acc[0] + t.x, acc[1] + t.y, acc[2] + t.z, acc[3] + t.w};
           *reinterpret_cast<float4*>(a.out + (row0 + r16) * D + 16 * wave + 4 * kq) = o;
         }
       }
@@ -2075,9 +2127,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
 // the A and the B side, so the sum over k is exact in any order.
 // `done` (if not null): the in-kernel merge counts of the decode that follows,
 // zeroed here for the block's problems, followed by one append count per layer.
+// `qplain` (if not null, rotated preparation only): q itself, as the fp16-key
+// preparation writes it, for a decode over an fp16 tail in the same call.
 template <bool ROT>
 __device__ __forceinline__ void qprep_body(const float* q, const float* pi, const float* s, float* qprep, int batch,
-                                           int H, int Hq, int bx, int b, int layer, int n_layers, uint32_t* done) {
+                                           int H, int Hq, int bx, int b, int layer, int n_layers, uint32_t* done,
+                                           float* qplain = nullptr) {
   const int hk = bx >> 2, quarter = bx & 3;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = Hq / H;
@@ -2096,6 +2151,13 @@ __device__ __forceinline__ void qprep_body(const float* q, const float* pi, cons
     }
     return;
   } else {
+    if (qplain != nullptr) {
+      for (int e = quarter * 256 + tid; e < G * D; e += 1024) {
+        const int g = e >> 7, i = e & 127;
+        qplain[(row0 + g) * 2 * D + i] = q[(row0 + g) * D + i];
+        qplain[(row0 + g) * 2 * D + D + i] = 0.f;
+      }
+    }
     const int bi = 4 * quarter + wave, mat = bi >> 3, i0 = 16 * (bi & 7);
     const int r16 = lane & 15, kq = lane >> 4;
     const float4* arow =
@@ -2127,8 +2189,9 @@ __device__ __forceinline__ void qprep_body(const float* q, const float* pi, cons
 }
 template <bool ROT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void qprep_kernel(
-    const float* q, const float* pi, const float* s, float* qprep, int batch, int H, int Hq, uint32_t* done) {
-  qprep_body<ROT>(q, pi, s, qprep, batch, H, Hq, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, done);
+    const float* q, const float* pi, const float* s, float* qprep, int batch, int H, int Hq, uint32_t* done,
+    float* qplain = nullptr) {
+  qprep_body<ROT>(q, pi, s, qprep, batch, H, Hq, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, done, qplain);
 }
 
 // The append of a few tokens and the query preparation of the same decode
@@ -2557,38 +2620,36 @@ tq_status decode_tail(const tq_format* fmt, const tq_tables* tables, const tq_ca
   float* qrot = reinterpret_cast<float*>(ws);
   float* qplain = reinterpret_cast<float*>(ws + tp.qplain_offset);
   float* partial = reinterpret_cast<float*>(ws + tp.partial_offset);
+  uint32_t* done = reinterpret_cast<uint32_t*>(ws + tp.counter_offset);
   const int mk = fmt->k_bits > 0 ? fmt->k_bits - 1 : 0;
   const int bv = fmt->v_bits;
+  // One query preparation for both parts (rotated and plain; the plain copy
+  // alone for fp16 keys), which also zeroes the merge counts.
   const dim3 qgrid(cache->n_kv_heads * 4, batch, cache->n_layers);
   if (fmt->k_bits > 0)
     hipLaunchKernelGGL(qprep_kernel<true>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qrot, batch,
-                       cache->n_kv_heads, n_q_heads, nullptr);
+                       cache->n_kv_heads, n_q_heads, done, qplain);
   else
     hipLaunchKernelGGL(qprep_kernel<false>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qrot, batch,
-                       cache->n_kv_heads, n_q_heads, nullptr);
-  hipLaunchKernelGGL(qprep_kernel<false>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qplain, batch,
-                     cache->n_kv_heads, n_q_heads, nullptr);
+                       cache->n_kv_heads, n_q_heads, done, nullptr);
   if ((st = launch_status("qprep"))) return st;
-  DecodeArgs ap = make_args(fmt, tables, cache, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, tp.packed,
-                            qrot, partial, nullptr);
-  ap.seg_max = int(tp.seg_total);
-  if ((st = launch_decode<false>(mk, bv, ap, dim3(unsigned(tp.packed.n_workgroups)), hs))) return st;
+  // The tail first (partials only), then the packed part, whose last
+  // workgroup per problem merges both piece sets into out.
   DecodeArgs at = make_args(&f16, tables, tail, batch, n_q_heads, tail_start, tail_len, max_tail_len, scale,
-                            tp.tail, qplain, partial, nullptr);
+                            tp.tail, fmt->k_bits > 0 ? qplain : qrot, partial, nullptr);
   at.seg_max = int(tp.seg_total);
   at.seg_base = int(tp.packed.seg_max);
   if ((st = launch_decode<false>(0, 0, at, dim3(unsigned(tp.tail.n_workgroups)), hs))) return st;
-  if ((st = launch_status("decode"))) return st;
-  const dim3 cgrid(cache->n_kv_heads, batch, cache->n_layers);
-  if (bv > 0)
-    hipLaunchKernelGGL(combine_kernel<true>, cgrid, dim3(256), 0, hs, partial, tables->pi, out, batch,
-                       cache->n_kv_heads, n_q_heads, ap.n_hg, ap.chunks_per_problem, ap.chunks_per_wg,
-                       int(tp.seg_total), at.chunks_per_problem, at.chunks_per_wg, int(tp.packed.seg_max));
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, cgrid, dim3(256), 0, hs, partial, tables->pi, out, batch,
-                       cache->n_kv_heads, n_q_heads, ap.n_hg, ap.chunks_per_problem, ap.chunks_per_wg,
-                       int(tp.seg_total), at.chunks_per_problem, at.chunks_per_wg, int(tp.packed.seg_max));
-  return launch_status("combine");
+  DecodeArgs ap = make_args(fmt, tables, cache, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, tp.packed,
+                            qrot, partial, nullptr);
+  ap.seg_max = int(tp.seg_total);
+  ap.done = done;
+  ap.out = out;
+  ap.tail_base = int(tp.packed.seg_max);
+  ap.tail_cpp = at.chunks_per_problem;
+  ap.tail_cpw = at.chunks_per_wg;
+  if ((st = launch_decode<false>(mk, bv, ap, dim3(unsigned(tp.packed.n_workgroups)), hs))) return st;
+  return launch_status("decode");
 }
 
 // Checks a compression call and fills its kernel arguments and bulk
