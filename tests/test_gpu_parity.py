@@ -332,14 +332,14 @@ def test_append_prepare_matches_separate_calls(k_bits, v_bits, dtype, n_new):
     assert torch.equal(ws[0], ws[1])
 
 
-@pytest.mark.parametrize("k_bits,v_bits", [(4, 4), (3, 2), (0, 4)])
-def test_decode_with_fp16_tail(k_bits, v_bits):
+@pytest.mark.parametrize("k_bits,v_bits,HQ", [(4, 4, 14), (3, 2, 14), (0, 4, 14), (4, 4, 20), (8, 0, 16)])
+def test_decode_with_fp16_tail(k_bits, v_bits, HQ):
     """Decode over a packed cache plus an fp16 tail of recent tokens (one
     softmax over both parts) against the oracle on the GPU's own caches, for
     ragged packed and tail lengths including empty parts."""
     import kv_cache_quantization_norm_amd as tq
-    _say("tail", k_bits, v_bits)
-    L, H, HQ = 2, 2, 14
+    _say("tail", k_bits, v_bits, HQ)
+    L, H = 2, 2
     lens, tlens = [300, 0, 97, 64], [40, 12, 0, 33]
     starts = [0, 320, 320, 448]
     tstarts = [0, 64, 128, 128]
@@ -457,6 +457,7 @@ def test_decode_steps_append_prepare_attend(k_bits, v_bits, hq, lens):
     ("slot0", 2, 2, 12, (5,), 3, 0),
     ("slot0", 0, 4, 16, (100,), 2, 1),
     ("slots", 8, 4, 28, (300, 45, 0, 129), 1, 0),
+    ("slot0", 4, 4, 28, (100,), 20, 0),   # 16 or more tokens: bulk compression, then the decode
 ])
 def test_decode_step_append_inside_decode_launch(mode, k_bits, v_bits, hq, lens, n_new, layer0):
     """tq_decode_step: the new tokens are compressed by the decode launch's
