@@ -89,7 +89,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not part of it",
+        print(json.dumps({"error": "the benchmark runs on one GPU only (the path is measured on one GPU's share)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
