@@ -67,7 +67,11 @@ def _check(shape):
         first = p * cpp
         nseg = (first + cpp - 1) // cpw - first // cpw + 1
         assert all((p, s) in slots for s in range(nseg)) and (p, nseg) not in slots
-    need = L * B * HQ * seg_max * (128 + 2) * 4
+    # prepared queries, partials and the counters (the in-kernel merge's one
+    # per problem, then the step's append count per layer)
+    align = lambda x: (x + 255) // 256 * 256
+    need = (align(L * B * HQ * 2 * 128 * 4) + align(L * B * HQ * seg_max * (128 + 2) * 4)
+            + align((P + L) * 4))
     assert tq.tq_decode_workspace_bytes(fmt, L, B, H, HQ, T) >= need
     return sp
 
