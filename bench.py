@@ -304,6 +304,24 @@ def main():
     tail_ms = e0.elapsed_time(e1) / args.steps
     del tail, tws
 
+    # ---------------- a plain streaming read for reference (tq_stream_read_probe
+    # over 2 GiB, two buffers in turn, past the Infinity Cache): the best of a
+    # few workgroup counts
+    bufs = [torch.ones(1 << 29, device=dev) for _ in range(2)]
+    read_gbs = 0.0
+    for nwg in (1024, 2048, 4096):
+        part = torch.zeros(nwg, device=dev)
+        for i in range(4):
+            tq.tq_stream_read_probe(bufs[i % 2], part, nwg, stream=stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(10):
+            tq.tq_stream_read_probe(bufs[i % 2], part, nwg, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        read_gbs = max(read_gbs, (1 << 31) / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9)
+    del bufs
+
     per_layer_ms = None
     if args.per_layer:
         per_layer_ms = time_per_layer(tq, fmt, tables, base, Q, seq_start, seq_len, T, stream, dev)
@@ -353,7 +371,9 @@ def main():
                                                   "median": round(float(np.median(kern_us)), 2),
                                                   "p10": round(float(np.percentile(kern_us, 10)), 2),
                                                   "p90": round(float(np.percentile(kern_us, 90)), 2)},
-                     "split_partials_bytes": split_overhead},
+                     "split_partials_bytes": split_overhead,
+                     "measured_stream_read_GBs": round(read_gbs, 1),
+                     "frac_of_measured_read": round(kern_gbs / read_gbs, 4)},
         "decode_call": {"us": round(decode_ms * 1e3, 2), "GBs": round(decode_gbs, 1),
                         "bytes": decode_bytes, "kernels": "qprep_kernel + decode_kernel (pieces merged in-kernel)"},
         "decode_step_bytes": step_bytes,

@@ -215,6 +215,13 @@ tq_status tq_decode_attention_tail(const tq_format* fmt, const tq_tables* tables
                                    const int64_t* tail_start, const int32_t* tail_len, int64_t max_tail_len,
                                    float scale, float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Device, measurement only.  Reads `bytes` (a multiple of 16) of device
+ * memory at `data` once, as a plain streaming read by n_workgroups workgroups
+ * of 256 threads, and adds one sum per workgroup into partial[n_workgroups]
+ * (device float, caller-zeroed): the reference for the achievable HBM read
+ * bandwidth against which the decode kernel's rate can also be read. */
+tq_status tq_stream_read_probe(const void* data, size_t bytes, float* partial, int32_t n_workgroups, void* stream);
+
 /* Host.  Workspace bytes of tq_decode_attention_tail (0 for invalid sizes). */
 size_t tq_decode_tail_workspace_bytes(const tq_format* fmt, int32_t n_layers, int32_t batch, int32_t n_kv_heads,
                                       int32_t n_q_heads, int64_t max_seq_len, int64_t max_tail_len);

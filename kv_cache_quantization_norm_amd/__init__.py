@@ -85,6 +85,7 @@ def _load(path: str = LIB_PATH):
         "tq_decode_partials": (I32, [fmtp, tabp, cachep, I32, I32, P, P, I64, F32, P, SZ, P]),
         "tq_decode_combine": (I32, [fmtp, tabp, cachep, I32, I32, I64, P, P, SZ, P]),
         "tq_decode_attend": (I32, [fmtp, tabp, cachep, I32, I32, P, P, I64, F32, P, P, SZ, P]),
+        "tq_stream_read_probe": (I32, [P, SZ, P, I32, P]),
         "tq_decode_step": (I32, [fmtp, tabp, cachep, P, P, I32, I32, I32, I64, P, I64, P, I32, I32, P, P, I64, F32, P,
                                  P, SZ, P]),
         "tq_status_string": (ctypes.c_char_p, [I32]),
@@ -101,6 +102,7 @@ _lib = _load()
 EXPORTED = ("tq_layer_seed", "tq_make_rotations", "tq_make_codebook", "tq_cache_plane_bytes",
             "tq_decode_workspace_bytes", "tq_decode_split", "tq_compress_kv", "tq_decode_attention", "tq_score",
             "tq_decode_prepare", "tq_decode_partials", "tq_decode_combine", "tq_decode_attend", "tq_decode_step",
+            "tq_stream_read_probe",
             "tq_append_prepare",
             "tq_compress_kv_bounded", "tq_decode_attention_tail", "tq_decode_tail_workspace_bytes",
             "tq_status_string", "tq_last_error")
@@ -358,6 +360,12 @@ def tq_decode_step(fmt: tq_format, tables: Tables, cache: Cache, k, v, q, seq_st
                                layer0, n_layers, n_tokens, _ptr(slots), slot0, _ptr(q), batch, hq, _ptr(seq_start),
                                _ptr(seq_len), max_seq_len, scale, _ptr(out), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)), "tq_decode_step")
+
+
+def tq_stream_read_probe(data, partial, n_workgroups: int, stream=None):
+    """Plain streaming read of the device tensor `data` (measurement reference)."""
+    _check(_lib.tq_stream_read_probe(_ptr(data), data.numel() * data.element_size(), _ptr(partial), n_workgroups,
+                                     _stream(stream)), "tq_stream_read_probe")
 
 
 def tail_workspace_for(fmt: tq_format, cache: Cache, batch: int, n_q_heads: int, max_seq_len: int,

@@ -2714,7 +2714,44 @@ tq_status compress_setup(const tq_format* fmt, const tq_tables* tables, const tq
 }  // namespace
 }  // namespace tq
 
+namespace tq {
+namespace {
+// A plain streaming read of n float4s (grid-stride, 4 loads in flight per
+// thread, non-temporal), one partial sum per workgroup: the reference for the
+// achievable HBM read bandwidth.
+__global__ __launch_bounds__(256) void stream_read_kernel(const floatx4* __restrict__ p, int64_t n,
+                                                          float* __restrict__ out) {
+  float acc = 0.f;
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    floatx4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += (v[u][0] + v[u][1]) + (v[u][2] + v[u][3]);
+  }
+  for (; i < n; i += stride) {
+    const floatx4 v = __builtin_nontemporal_load(p + i);
+    acc += (v[0] + v[1]) + (v[2] + v[3]);
+  }
+  acc = wave_sum(acc);
+  if ((threadIdx.x & 63) == 0) atomicAdd(out + blockIdx.x, acc);
+}
+}  // namespace
+}  // namespace tq
+
 extern "C" {
+
+tq_status tq_stream_read_probe(const void* data, size_t bytes, float* partial, int32_t n_workgroups, void* stream) {
+  tq::clear_error();
+  if (!data || !partial || n_workgroups <= 0 || bytes % 16 != 0)
+    return tq::fail(TQ_ERR_INVALID_ARG, "stream probe: data/partial NULL, n_workgroups <= 0 or bytes not a multiple of 16");
+  hipLaunchKernelGGL(tq::stream_read_kernel, dim3(unsigned(n_workgroups)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const tq::floatx4*>(data), int64_t(bytes / 16),
+                     partial);
+  return tq::launch_status("stream read probe");
+}
 
 tq_status tq_compress_kv(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
                          const void* k, const void* v, int32_t dtype, int32_t layer0,

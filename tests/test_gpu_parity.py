@@ -219,6 +219,20 @@ def test_staged_decode_matches_one_call(case):
         assert float(np.max(np.abs(a - b))) <= 1e-5 * scale
 
 
+def test_stream_read_probe_reads_every_element_once():
+    """The bandwidth reference reads each float4 exactly once: the per-workgroup
+    sums of an all-ones buffer (with a ragged tail past the unrolled loop) add up to
+    its length."""
+    import kv_cache_quantization_norm_amd as tq
+    _say("stream read probe")
+    n = (1 << 20) + 4 * 37
+    data = torch.ones(n, device="cuda")
+    part = torch.zeros(96, device="cuda")
+    tq.tq_stream_read_probe(data, part, 96)
+    torch.cuda.synchronize()
+    assert float(part.double().sum()) == n
+
+
 @pytest.mark.parametrize("chunk", [None, 3])
 def test_degenerate_vectors_and_nan(chunk):
     """Zero keys/values compress to zero norms and contribute nothing; a NaN key

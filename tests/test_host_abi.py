@@ -147,6 +147,9 @@ def test_device_calls_validate_before_launch():
     assert r("tq_decode_attention", P(fmt), P(tb), P(cs4), FAKE, 1, 8, FAKE, FAKE, 64, 0.0, FAKE, FAKE, 16, None) == tq.TQ_ERR_WORKSPACE
     assert r("tq_score", P(fmt), P(tb), P(cs4), FAKE, 1, 8, FAKE, FAKE, 64, 0.0, FAKE, None, 1 << 30, None) == tq.TQ_ERR_WORKSPACE
     assert r("tq_decode_attention", P(fmt), P(tb), P(cs4), None, 1, 8, FAKE, FAKE, 64, 0.0, FAKE, FAKE, 1 << 30, None) == tq.TQ_ERR_INVALID_ARG
+    # streaming-read probe: sizes checked before launch
+    assert r("tq_stream_read_probe", FAKE, 24, FAKE, 4, None) == tq.TQ_ERR_INVALID_ARG
+    assert r("tq_stream_read_probe", FAKE, 32, FAKE, 0, None) == tq.TQ_ERR_INVALID_ARG
     # partials + in-kernel merge: output required, workspace (with the piece counters) checked
     assert r("tq_decode_attend", P(fmt), P(tb), P(cs4), 1, 8, FAKE, FAKE, 64, 0.0, None, FAKE, 1 << 30, None) == tq.TQ_ERR_INVALID_ARG
     assert r("tq_decode_attend", P(fmt), P(tb), P(cs4), 1, 8, None, FAKE, 64, 0.0, FAKE, FAKE, 1 << 30, None) == tq.TQ_ERR_INVALID_ARG
