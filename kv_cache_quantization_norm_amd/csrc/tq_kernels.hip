@@ -2118,86 +2118,107 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   }
 }
 
-// qr = Pi q (q itself for fp16 keys), qs = S q.  The products are
-// [Pi; S] (256 x 128) times the group's queries (128 x G) on fp32 MFMA
-// 16x16x4, with no LDS: wave w of block (quarter, KV head, batch, layer) owns
-// rows 16 bi .. 16 bi + 15 of [Pi; S], bi = 4 quarter + w.  Lane l holds row
-// 16 bi + l % 16 and query head l % 16 of the head block; its float4 pieces
-// 16 v + 4 (l / 16) .. + 3 of both are step v's four k-values, the same k on
-// the A and the B side, so the sum over k is exact in any order.
-// `done` (if not null): the in-kernel merge counts of the decode that follows,
-// zeroed here for the block's problems, followed by one append count per layer.
-// `qplain` (if not null, rotated preparation only): q itself, as the fp16-key
-// preparation writes it, for a decode over an fp16 tail in the same call.
+// The query preparation of a decode call, one workgroup per (quarter,
+// layer): wave w owns row block 4 quarter + w of [Pi; S] (16 rows), read once
+// and split into fp16 high parts and remainders (times 2^11); the layer's
+// query rows (batch x Hq) are the MFMA columns, 16 at a time, each scaled by
+// the power of two that puts its norm in [2^14, 2^15) and split likewise, so
+// three v_mfma_f32_16x16x32_f16 per 32-wide step keep about 22 bits (Pi and S
+// are loaded once per layer and quarter instead of once per KV head).
+// Quarter 0 also zeroes the layer's merge counts and its append count;
+// `qplain` (if not null) receives q itself, for a decode over an fp16 tail.
+// fp16 keys (ROT false): q itself and zeros.
 template <bool ROT>
-__device__ __forceinline__ void qprep_body(const float* q, const float* pi, const float* s, float* qprep, int batch,
-                                           int H, int Hq, int bx, int b, int layer, int n_layers, uint32_t* done,
-                                           float* qplain = nullptr) {
-  const int hk = bx >> 2, quarter = bx & 3;
+__device__ __forceinline__ void qprep_quarter(const float* q, const float* pi, const float* s, float* qprep,
+                                              int batch, int H, int Hq, int quarter, int layer, int n_layers,
+                                              uint32_t* done, float* qplain) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, kq = lane >> 4;
   const int G = Hq / H;
-  const int64_t row0 = (int64_t(layer) * batch + b) * Hq + int64_t(hk) * G;
+  const int64_t base = int64_t(layer) * batch * Hq;   // the layer's first query row
+  const int nrows = batch * Hq;
   if (done != nullptr && quarter == 0) {
     const int n_hg = (G + kMaxGroup - 1) / kMaxGroup;
-    for (int hg = tid; hg < n_hg; hg += 256) done[((int64_t(layer) * batch + b) * H + hk) * n_hg + hg] = 0u;
-    if (hk == 0 && b == 0 && tid == 0) done[int64_t(n_layers) * batch * H * n_hg + layer] = 0u;
+    const int64_t per_layer = int64_t(batch) * H * n_hg;   // problems of a layer (consecutive)
+    for (int64_t e = tid; e < per_layer; e += 256) done[int64_t(layer) * per_layer + e] = 0u;
+    if (tid == 0) done[int64_t(n_layers) * per_layer + layer] = 0u;
   }
-  if constexpr (!ROT) {
-    // fp16 keys are scored against q itself; no sketch.
-    for (int e = quarter * 256 + tid; e < G * D; e += 1024) {
-      const int g = e >> 7, i = e & 127;
-      qprep[(row0 + g) * 2 * D + i] = q[(row0 + g) * D + i];
-      qprep[(row0 + g) * 2 * D + D + i] = 0.f;
+  if (!ROT || qplain != nullptr) {
+    float* dst = ROT ? qplain : qprep;
+    for (int64_t e = int64_t(quarter) * 256 + tid; e < int64_t(nrows) * D; e += 1024) {
+      const int64_t r = e >> 7;
+      const int i = int(e & 127);
+      dst[(base + r) * 2 * D + i] = q[(base + r) * D + i];
+      dst[(base + r) * 2 * D + D + i] = 0.f;
     }
-    return;
-  } else {
-    if (qplain != nullptr) {
-      for (int e = quarter * 256 + tid; e < G * D; e += 1024) {
-        const int g = e >> 7, i = e & 127;
-        qplain[(row0 + g) * 2 * D + i] = q[(row0 + g) * D + i];
-        qplain[(row0 + g) * 2 * D + D + i] = 0.f;
+  }
+  if constexpr (ROT) {
+    const int rb = 4 * quarter + wave, mat = rb >> 3, i0 = 16 * (rb & 7);
+    half8 ah[4], al[4];
+    {
+      const float4* src =
+          reinterpret_cast<const float4*>((mat ? s : pi) + int64_t(layer) * D * D + int64_t(i0 + col) * D + 32 * kq);
+      float4 v4[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) v4[v] = src[v];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float v[8] = {v4[2 * t].x, v4[2 * t].y, v4[2 * t].z, v4[2 * t].w,
+                            v4[2 * t + 1].x, v4[2 * t + 1].y, v4[2 * t + 1].z, v4[2 * t + 1].w};
+        split8(v, ah[t], al[t], true);
       }
     }
-    const int bi = 4 * quarter + wave, mat = bi >> 3, i0 = 16 * (bi & 7);
-    const int r16 = lane & 15, kq = lane >> 4;
-    const float4* arow =
-        reinterpret_cast<const float4*>((mat ? s : pi) + int64_t(layer) * D * D + int64_t(i0 + r16) * D + 4 * kq);
-    float4 a4[8];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) a4[v] = arow[4 * v];
-    for (int g0 = 0; g0 < G; g0 += 16) {
-      const int g = g0 + r16;
-      const float4* qrow = reinterpret_cast<const float4*>(q + (row0 + (g < G ? g : G - 1)) * D + 4 * kq);
-      float4 b4[8];
-#pragma unroll
-      for (int v = 0; v < 8; ++v) b4[v] = qrow[4 * v];
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int r0 = 0; r0 < nrows; r0 += 16) {
+      const int r = r0 + col < nrows ? r0 + col : nrows - 1;
+      const float4* qs4 = reinterpret_cast<const float4*>(q + (base + r) * D + 32 * kq);
+      float x[32];
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
-        acc = mfma16x16x4f32(a4[v].x, b4[v].x, acc);
-        acc = mfma16x16x4f32(a4[v].y, b4[v].y, acc);
-        acc = mfma16x16x4f32(a4[v].z, b4[v].z, acc);
-        acc = mfma16x16x4f32(a4[v].w, b4[v].w, acc);
+        const float4 f = qs4[v];
+        x[4 * v] = f.x; x[4 * v + 1] = f.y; x[4 * v + 2] = f.z; x[4 * v + 3] = f.w;
       }
-      // D: rows i0 + 4 kq + r, column (head) l % 16.
-      if (g < G) {
-        float4 o = {acc[0], acc[1], acc[2], acc[3]};
-        *reinterpret_cast<float4*>(qprep + (row0 + g) * 2 * D + mat * D + i0 + 4 * kq) = o;
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) ss = fmaf(x[e], x[e], ss);
+      ss += shfl_xor(ss, 16);
+      ss += shfl_xor(ss, 32);
+      const float nq = sqrtf(ss);
+      const int ex = (nq > 0.f && nq < INFINITY) ? 15 - __builtin_amdgcn_frexp_expf(nq) : 0;
+      floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = __builtin_amdgcn_ldexpf(x[8 * t + e], ex);
+        half8 xh, xl;
+        split8(v, xh, xl, true);
+        a1 = mfma16x16x32(ah[t], xh, a1);
+        a2 = mfma16x16x32(al[t], xh, a2);
+        a2 = mfma16x16x32(ah[t], xl, a2);
+      }
+      // D: rows i0 + 4 kq + k of the block, column (query row) r0 + col
+      if (r0 + col < nrows) {
+        float4 o;
+        o.x = __builtin_amdgcn_ldexpf(fmaf(a2[0], 0x1p-11f, a1[0]), -ex);
+        o.y = __builtin_amdgcn_ldexpf(fmaf(a2[1], 0x1p-11f, a1[1]), -ex);
+        o.z = __builtin_amdgcn_ldexpf(fmaf(a2[2], 0x1p-11f, a1[2]), -ex);
+        o.w = __builtin_amdgcn_ldexpf(fmaf(a2[3], 0x1p-11f, a1[3]), -ex);
+        *reinterpret_cast<float4*>(qprep + (base + r0 + col) * 2 * D + mat * D + i0 + 4 * kq) = o;
       }
     }
   }
 }
 template <bool ROT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void qprep_kernel(
-    const float* q, const float* pi, const float* s, float* qprep, int batch, int H, int Hq, uint32_t* done,
-    float* qplain = nullptr) {
-  qprep_body<ROT>(q, pi, s, qprep, batch, H, Hq, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.z, done, qplain);
+__global__ __launch_bounds__(256) void qprep_kernel(const float* q, const float* pi, const float* s, float* qprep,
+                                                    int batch, int H, int Hq, uint32_t* done,
+                                                    float* qplain = nullptr) {
+  qprep_quarter<ROT>(q, pi, s, qprep, batch, H, Hq, blockIdx.x, blockIdx.y, gridDim.y, done, qplain);
 }
 
 // The append of a few tokens and the query preparation of the same decode
 // step in one launch (they are independent): workgroups [0, n_append) run
 // the append blocks (item group, layer), the others the query preparation
-// blocks (4 KV head + quarter, sequence, layer).
+// blocks (quarter, layer) of qprep_kernel.
 template <int MK, int BV>
 __global__ __launch_bounds__(kAppendThreads) void append_prepare_kernel(
     CompressArgs a, int app_groups, int n_append, const float* q, const float* pi, const float* s, float* qprep,
@@ -2209,9 +2230,9 @@ __global__ __launch_bounds__(kAppendThreads) void append_prepare_kernel(
     return;
   }
   if (threadIdx.x >= 256) return;   // the query preparation blocks take 4 waves
-  const int r = bid - n_append, nx = H * 4;
-  qprep_body<(MK > 0)>(q, pi, s, qprep, batch, H, Hq, r % nx, (r / nx) % batch, r / (nx * batch),
-                       (int(gridDim.x) - n_append) / (nx * batch), done);
+  const int r = bid - n_append;
+  qprep_quarter<(MK > 0)>(q, pi, s, qprep, batch, H, Hq, r & 3, r >> 2, (int(gridDim.x) - n_append) >> 2, done,
+                          nullptr);
 }
 
 // Merges the piece partials of one (layer, batch, KV head) for every query
@@ -2530,13 +2551,13 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   const int mk = fmt->k_bits > 0 ? fmt->k_bits - 1 : 0;
   const int bv = fmt->v_bits;
   if (stages & kStagePrepare) {
-    const dim3 qgrid(cache->n_kv_heads * 4, batch, cache->n_layers);
+    const dim3 qgrid(4, cache->n_layers);
     if (fmt->k_bits > 0)
       hipLaunchKernelGGL(qprep_kernel<true>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qprep, batch,
-                         cache->n_kv_heads, n_q_heads, done);
+                         cache->n_kv_heads, n_q_heads, done, nullptr);
     else
       hipLaunchKernelGGL(qprep_kernel<false>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qprep, batch,
-                         cache->n_kv_heads, n_q_heads, done);
+                         cache->n_kv_heads, n_q_heads, done, nullptr);
     if ((st = launch_status("qprep"))) return st;
   }
   if (max_seq_len == 0 && SCORE) return TQ_OK;
@@ -2625,7 +2646,7 @@ tq_status decode_tail(const tq_format* fmt, const tq_tables* tables, const tq_ca
   const int bv = fmt->v_bits;
   // One query preparation for both parts (rotated and plain; the plain copy
   // alone for fp16 keys), which also zeroes the merge counts.
-  const dim3 qgrid(cache->n_kv_heads * 4, batch, cache->n_layers);
+  const dim3 qgrid(4, cache->n_layers);
   if (fmt->k_bits > 0)
     hipLaunchKernelGGL(qprep_kernel<true>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qrot, batch,
                        cache->n_kv_heads, n_q_heads, done, qplain);
@@ -2835,7 +2856,7 @@ tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const
   }
   const int64_t groups = (n_tokens * a.H + kAppendItems - 1) / kAppendItems;
   const int64_t n_append = groups * n_layers;
-  const int64_t n_prep = int64_t(cache->n_kv_heads) * 4 * batch * cache->n_layers;
+  const int64_t n_prep = int64_t(4) * cache->n_layers;   // (quarter, layer) preparation blocks
   if (n_append + n_prep > 0x7FFFFFFF) return fail(TQ_ERR_INVALID_ARG, "too many workgroups");
   hipStream_t hs = static_cast<hipStream_t>(stream);
   float* qprep = static_cast<float*>(workspace);
