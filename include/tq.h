@@ -208,7 +208,9 @@ tq_status tq_decode_attention(const tq_format* fmt, const tq_tables* tables, con
  * scale and the head mapping as in tq_decode_attention.  Tokens enter the
  * tail with tq_compress_kv on the fp16 format (the values stored as fp16),
  * and move to the packed cache with tq_compress_kv from those fp16 values.
- * workspace: at least tq_decode_tail_workspace_bytes(...) bytes. */
+ * workspace: at least tq_decode_tail_workspace_bytes(...) bytes; it holds the
+ * packed decode's piece counters (zeroed by the call's own query
+ * preparation), so calls on one workspace must not overlap. */
 tq_status tq_decode_attention_tail(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
                                    const tq_cache* tail, const float* q, int32_t batch, int32_t n_q_heads,
                                    const int64_t* seq_start, const int32_t* seq_len, int64_t max_seq_len,
