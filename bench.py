@@ -476,8 +476,8 @@ def cpu_baseline(w, budget_s, gpu_result):
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     fmt = quant.Format(w.head_dim, w.k_bits, w.v_bits)
-    cbk = codebook.stored_codebook(w.head_dim, fmt.k_mse_bits)
-    cbv = codebook.stored_codebook(w.head_dim, fmt.v_bits)
+    cbk = codebook.table_codebook(w.head_dim, fmt.k_mse_bits)
+    cbv = codebook.table_codebook(w.head_dim, fmt.v_bits)
     T = w.seq_lens[0]
     cap = (T + 31) // 32 * 32
     k_rec = fmt.k_record_bytes()

@@ -80,9 +80,10 @@ typedef struct tq_format {
  * tq_make_rotations.  Codebooks are shared by all layers: 2^m ascending
  * centroids and 2^m - 1 boundaries for the key (m = k_bits-1) and value
  * (m = v_bits) quantisers, as written by tq_make_codebook (rounded to fp32).
- * The kernels apply the centroids (reconstruction values) at their stored
- * precision, fp16 (each rounded to nearest); the boundaries are compared in
- * fp32. */
+ * Compression compares rotated coordinates with the fp32 boundaries and forms
+ * the key residual with the fp32 centroids.  Decode rounds the centroids to
+ * fp16 for its MFMA operands, an approximation that moves a logit by about
+ * 1e-4 of its row's largest logit (the tolerance is 1e-3). */
 typedef struct tq_tables {
   const float* pi;
   const float* s;

@@ -24,13 +24,12 @@ Readings:
     unique because f_d is log-concave for d >= 3).  The final centroids are
     projected onto exact antisymmetry, c_k = -c_{n-1-k}, which only removes
     rounding noise and makes the middle boundary exactly 0 for every even n.
-  * Storage precision (the pages store the codebook but do not say at what
-    precision): the reconstruction values are stored in fp16, the precision
-    the attention kernels consume, and dequantisation and the key residual use
-    these stored values; the decision boundaries stay the midpoints of the
-    exact solution (compared in fp32).  Rounding moves each centroid by at
-    most 2^-11 of its value; the coordinate MSE changes by far less than the
-    gap between bit widths (pinned in the tests).
+  * Storage precision (the pages store the codebook as a precomputed table
+    but do not say at what precision): the table is fp32, the precision in
+    which the pages keep the rotation (QJL deep-dive §二: Pi is a 64 KB table,
+    128 x 128 four-byte values).  Dequantisation and the key residual apply the
+    Lloyd-Max centroids rounded to the nearest fp32; decisions compare fp32
+    rotated coordinates with the fp32 roundings of the exact midpoints.
 """
 import math
 
@@ -104,14 +103,14 @@ def codebook(d: int, bits: int):
     return _CACHE[key]
 
 
-def stored_centroids(c) -> np.ndarray:
-    """Reconstruction values as stored: rounded to fp16 (nearest, ties to
-    even), returned as float64."""
-    return np.asarray(c, np.float64).astype(np.float16).astype(np.float64)
+def table_centroids(c) -> np.ndarray:
+    """Reconstruction values as held in the fp32 codebook table: each centroid
+    rounded to the nearest fp32, returned as float64."""
+    return np.asarray(c, np.float64).astype(np.float32).astype(np.float64)
 
 
-def stored_codebook(d: int, bits: int):
-    """(stored centroids, exact boundaries): the codebook that compression and
-    dequantisation apply."""
+def table_codebook(d: int, bits: int):
+    """(fp32-table centroids, exact boundaries): the codebook that compression
+    and dequantisation apply (decide() rounds the boundaries to fp32)."""
     c, t = codebook(d, bits)
-    return stored_centroids(c), t
+    return table_centroids(c), t

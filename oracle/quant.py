@@ -100,19 +100,31 @@ def compress_v(x: np.ndarray, pi: np.ndarray, centroids, boundaries, return_y: b
     return decide(y, boundaries), n
 
 
-def compress_k(x: np.ndarray, pi: np.ndarray, s: np.ndarray, centroids, boundaries):
-    """TurboQuantProd compression of rows of x [N, d] with a (k_bits-1)-bit
-    codebook.  Returns dict(idx, sign (0/1 uint8), norm, rnorm)."""
+def residual_sketch(x: np.ndarray, idx: np.ndarray, n: np.ndarray, pi: np.ndarray, s: np.ndarray, centroids):
+    """QJL page §二 step 3 for rows of x [N, d] whose codes idx and norms n are
+    given: x~ = ||x|| Pi^T c[idx], r = x - x~ (original space), the sign bits
+    [(S r)_j >= 0] and ||r||.  Returns (sign uint8 [N, d], rnorm [N],
+    S r / ||x|| [N, d])."""
     x = np.asarray(x, np.float64)
-    idx, n, y = compress_v(x, pi, centroids, boundaries, return_y=True)
-    xt = n[..., None] * (np.asarray(centroids)[idx] @ pi)   # ||x|| Pi^T c[idx]
+    xt = np.asarray(n, np.float64)[..., None] * (np.asarray(centroids)[idx] @ pi)   # ||x|| Pi^T c[idx]
     r = x - xt
-    sr = r @ s.T                                             # S r
+    sr = r @ s.T                                                                    # S r
     sign = (sr >= 0).astype(np.uint8)
     rnorm = np.linalg.norm(r, axis=-1)
-    # y and S r / ||x|| are returned for locating decisions near a boundary.
+    # S r / ||x|| is returned for locating sign decisions near zero.
     with np.errstate(invalid="ignore", divide="ignore"):
         sr_rel = sr / np.where(n > 0, n, 1.0)[..., None]
+    return sign, rnorm, sr_rel
+
+
+def compress_k(x: np.ndarray, pi: np.ndarray, s: np.ndarray, centroids, boundaries):
+    """TurboQuantProd compression of rows of x [N, d] with a (k_bits-1)-bit
+    codebook.  Returns dict(idx, sign (0/1 uint8), norm, rnorm) and, for
+    locating decisions near a boundary, y (the rotated unit vectors) and
+    sr_rel (S r / ||x||)."""
+    x = np.asarray(x, np.float64)
+    idx, n, y = compress_v(x, pi, centroids, boundaries, return_y=True)
+    sign, rnorm, sr_rel = residual_sketch(x, idx, n, pi, s, centroids)
     return dict(idx=idx, sign=sign, norm=n, rnorm=rnorm, y=y, sr_rel=sr_rel)
 
 

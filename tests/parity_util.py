@@ -2,8 +2,14 @@
 move packed planes between the oracle layout and the device, and compare
 codes with the near-boundary allowance.
 
-Test infrastructure: it calls the oracle and the HIP library side by side,
-and never feeds anything the library produced into the oracle.
+Test infrastructure: it calls the oracle and the HIP library side by side.
+Every expected value comes from the oracle on the seeded inputs.  The one
+place where the device's output selects what is expected: a key code that
+differs from the oracle's is first checked to be a valid alternative (its
+coordinate lies within 1e-6 of the boundary between the two codes); the
+oracle then computes that token's residual, signs and residual norm from the
+codes with the alternative taken (both records are correct encodings of the
+key, and the residual of each is unique).
 """
 import math
 from typing import Dict, List, Tuple
@@ -52,8 +58,8 @@ def slots_of(w: wl.Workload):
 
 def oracle_tables(fmt: quant.Format, layer: int):
     pi, s = rotation.layer_rotations(D, layer)
-    cbk = codebook.stored_codebook(D, fmt.k_mse_bits) if fmt.k_bits else None
-    cbv = codebook.stored_codebook(D, fmt.v_bits) if fmt.v_bits else None
+    cbk = codebook.table_codebook(D, fmt.k_mse_bits) if fmt.k_bits else None
+    cbv = codebook.table_codebook(D, fmt.v_bits) if fmt.v_bits else None
     return pi, s, cbk, cbv
 
 
@@ -61,6 +67,7 @@ def oracle_compress_layer(w: wl.Workload, layer: int, fmt: quant.Format, k, v, s
     pi, s, cbk, cbv = oracle_tables(fmt, layer)
     cache = quant.empty_cache(fmt, w.n_kv_heads, capacity)
     details = quant.compress_into(cache, k.astype(np.float64), v.astype(np.float64), slots, pi, s, cbk, cbv)
+    details["keys"] = np.asarray(k, np.float64)
     return cache, details
 
 
@@ -108,37 +115,62 @@ def near_boundary(y: np.ndarray, boundaries) -> np.ndarray:
     return np.min(np.abs(np.asarray(y, np.float64)[..., None] - t), axis=-1) < NEAR
 
 
+def alternative_codes(ora_idx: np.ndarray, gpu_idx: np.ndarray, y: np.ndarray, boundaries) -> np.ndarray:
+    """Codes of the tokens whose device codes differ from the oracle's, with
+    every differing coordinate checked to be a valid alternative: the two
+    codes are neighbours and the rotated coordinate lies within NEAR of the
+    boundary between them.  Returns the codes with the alternatives taken."""
+    t = np.asarray(boundaries, np.float64)
+    bad = gpu_idx != ora_idx
+    lo = np.minimum(gpu_idx, ora_idx).astype(np.int64)
+    assert np.all(np.abs(gpu_idx[bad].astype(np.int64) - ora_idx[bad].astype(np.int64)) == 1), \
+        "a code differs from the oracle's by more than one cell"
+    # boundary between cells lo and lo + 1 is t[lo]
+    assert np.all(np.abs(np.asarray(y, np.float64)[bad] - t[lo[bad]]) < NEAR), "code mismatch away from a boundary"
+    alt = ora_idx.copy()
+    alt[bad] = gpu_idx[bad]
+    return alt
+
+
 def compare_layer(gpu: dict, ora: dict, details: Dict, fmt: quant.Format, slots: np.ndarray,
-                  cbk, cbv) -> Dict[str, int]:
-    """Checks one layer's device planes against the oracle.  Returns counts."""
-    stats = dict(coords=0, k_mismatch=0, s_mismatch=0, v_mismatch=0, tokens_skipped_for_signs=0)
+                  layer: int) -> Dict[str, int]:
+    """Checks one layer's device planes against the oracle's compression of
+    the same inputs.  details: the per-head results of quant.compress_into
+    plus "keys", the inputs [n][H][d] (float64, row i at slot slots[i]), used
+    for the records of tokens with an alternative key code.  Returns counts:
+    decisions compared (key codes, sign bits, value codes) and mismatches of
+    each."""
+    pi, s, cbk, cbv = oracle_tables(fmt, layer)
+    keys = details.get("keys")
+    stats = dict(coords=0, k_mismatch=0, s_mismatch=0, v_mismatch=0, tokens_alt_codes=0)
     h_n = ora["n_kv_heads"]
     for h in range(h_n):
         if fmt.k_bits > 0:
             det = details[("k", h)]
             gi = quant.unpack_bits(gpu["k_idx"][h, slots], fmt.k_mse_bits, D)
             bad = gi != det["idx"]
+            idx = det["idx"]
+            sign, rnorm, sr_rel = det["sign"], det["rnorm"], det["sr_rel"]
             if bad.any():
-                assert np.all(near_boundary(det["y"][bad], cbk[1])), "key code mismatch away from a boundary"
+                idx = alternative_codes(det["idx"], gi, det["y"], cbk[1])
+                rows = np.nonzero(bad.any(axis=1))[0]
+                assert keys is not None, "tokens with alternative codes need the keys"
+                a_sign, a_rnorm, a_sr = quant.residual_sketch(keys[rows, h], idx[rows], det["norm"][rows], pi, s,
+                                                              cbk[0])
+                sign, rnorm, sr_rel = sign.copy(), rnorm.copy(), sr_rel.copy()
+                sign[rows], rnorm[rows], sr_rel[rows] = a_sign, a_rnorm, a_sr
+                stats["tokens_alt_codes"] += len(rows)
             stats["k_mismatch"] += int(bad.sum())
-            stats["coords"] += bad.size
+            stats["coords"] += 2 * bad.size   # codes and sign bits
             # norms
             np.testing.assert_allclose(gpu["k_norm"][h, slots], det["norm"], rtol=1e-6, atol=1e-30)
-            # residual norm rho = ||x|| ||y - c[idx]||, taken with the device's own
-            # codes: a near-boundary code flip moves the residual, and with the
-            # fp16-stored centroids of a 128-level codebook the two sides of a
-            # boundary differ by up to ~1e-3 of rho
-            y = np.asarray(det["y"], np.float64)
-            cst = np.asarray(cbk[0], np.float64)
-            rho_dev = det["norm"] * np.sqrt(np.sum((y - cst[gi]) ** 2, axis=1))
-            np.testing.assert_allclose(gpu["k_rnorm"][h, slots], rho_dev, rtol=2e-6, atol=1e-6 * det["norm"].max())
-            # signs, on tokens whose codes agree (a code flip changes the residual)
-            same = ~bad.any(axis=1)
-            stats["tokens_skipped_for_signs"] += int((~same).sum())
+            # residual norm: the oracle's, for the codes compared
+            np.testing.assert_allclose(gpu["k_rnorm"][h, slots], rnorm, rtol=2e-6, atol=1e-6 * det["norm"].max())
+            # sign bits: exact except where (S r)_j / ||x|| is within NEAR of zero
             gs = quant.unpack_bits(gpu["k_sign"][h, slots], 1, D)
-            sbad = (gs != det["sign"]) & same[:, None]
+            sbad = gs != sign
             if sbad.any():
-                assert np.all(np.abs(det["sr_rel"][sbad]) < NEAR), "sign mismatch away from zero"
+                assert np.all(np.abs(sr_rel[sbad]) < NEAR), "sign mismatch away from zero"
             stats["s_mismatch"] += int(sbad.sum())
             if not bad.any() and not sbad.any():
                 assert np.array_equal(gpu["k_idx"][h, slots], ora["k_idx"][h, slots])
@@ -150,7 +182,7 @@ def compare_layer(gpu: dict, ora: dict, details: Dict, fmt: quant.Format, slots:
             gv = quant.unpack_v_blocks(gpu["v_idx"][h], fmt.v_bits)[slots]
             bad = gv != det["idx"]
             if bad.any():
-                assert np.all(near_boundary(det["y"][bad], cbv[1])), "value code mismatch away from a boundary"
+                alternative_codes(det["idx"], gv, det["y"], cbv[1])
             stats["v_mismatch"] += int(bad.sum())
             stats["coords"] += bad.size
             np.testing.assert_allclose(gpu["v_norm"][h, slots], det["norm"], rtol=1e-6, atol=1e-30)
@@ -159,6 +191,13 @@ def compare_layer(gpu: dict, ora: dict, details: Dict, fmt: quant.Format, slots:
             ov = quant.f16_v_unblock(ora["v_f16"][h])[slots].view(np.uint16)
             assert np.array_equal(gv, ov)
     return stats
+
+
+def mismatch_rate(stats: Dict[str, int]) -> float:
+    """(key code + sign bit + value code mismatches) / decisions compared."""
+    if not stats["coords"]:
+        return 0.0
+    return (stats["k_mismatch"] + stats["s_mismatch"] + stats["v_mismatch"]) / stats["coords"]
 
 
 def check_logits(gpu_logits: np.ndarray, ora_logits: Dict, lens, hq, tol=1e-3):

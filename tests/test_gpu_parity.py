@@ -102,13 +102,12 @@ def _run_group(w, fmt, layers, dev_compress=True, sanitize=False):
 def test_compress_parity(case):
     w = CASES[case]
     _say("compress", case)
-    total = dict(coords=0, k_mismatch=0, s_mismatch=0, v_mismatch=0)
+    total = dict(coords=0, k_mismatch=0, s_mismatch=0, v_mismatch=0, tokens_alt_codes=0)
     for fmt, layers in pu.layer_groups(w):
         tables, dev, ora_caches, ora_details, (starts, lens, cap, slots) = _run_group(w, fmt, layers)
         gpu_caches = pu.download_cache(dev, fmt)
         for i, layer in enumerate(layers):
-            _, _, cbk, cbv = pu.oracle_tables(fmt, layer)
-            st = pu.compare_layer(gpu_caches[i], ora_caches[i], ora_details[i], fmt, slots, cbk, cbv)
+            st = pu.compare_layer(gpu_caches[i], ora_caches[i], ora_details[i], fmt, slots, layer)
             for k in total:
                 total[k] += st[k]
             # slots outside the sequences stay zero
@@ -118,9 +117,7 @@ def test_compress_parity(case):
                 if name in gpu_caches[i]:
                     assert np.all(gpu_caches[i][name][:, ~used] == 0)
     _say("mismatches", total)
-    if total["coords"]:
-        rate = (total["k_mismatch"] + total["v_mismatch"]) / total["coords"]
-        assert rate <= pu.MAX_MISMATCH_RATE, rate
+    assert pu.mismatch_rate(total) <= pu.MAX_MISMATCH_RATE, total
 
 
 def _decode_gpu(fmt, tables, dev, Q, starts, lens, want_logits=True):
@@ -175,8 +172,7 @@ def test_end_to_end(case):
         tables, dev, ora_caches, ora_details, (starts, lens, cap, slots) = _run_group(w, fmt, layers, sanitize=True)
         gpu_caches = pu.download_cache(dev, fmt)
         for i, layer in enumerate(layers):
-            _, _, cbk, cbv = pu.oracle_tables(fmt, layer)
-            st = pu.compare_layer(gpu_caches[i], ora_caches[i], ora_details[i], fmt, slots, cbk, cbv)
+            st = pu.compare_layer(gpu_caches[i], ora_caches[i], ora_details[i], fmt, slots, layer)
             assert st["k_mismatch"] == st["v_mismatch"] == st["s_mismatch"] == 0, st
         Q = np.stack([wl.gen_q(w, layer) for layer in layers])
         out, _ = _decode_gpu(fmt, tables, dev, Q, starts, lens, want_logits=False)
@@ -305,8 +301,7 @@ def test_overwrite_slot_and_append(k_bits, v_bits, dtype):
     gpu = pu.download_cache(dev, fmt)
     for layer in (0, 1):
         c, det = pu.oracle_compress_layer(w, layer, fmt, K[layer], V[layer], slots, cap)
-        _, _, cbk, cbv = pu.oracle_tables(fmt, layer)
-        pu.compare_layer(gpu[layer], c, det, fmt, slots, cbk, cbv)
+        pu.compare_layer(gpu[layer], c, det, fmt, slots, layer)
 
 
 @pytest.mark.parametrize("k_bits,v_bits,dtype,n_new", [(4, 4, "bf16", 1), (3, 2, "f32", 3), (0, 4, "bf16", 1),
@@ -592,7 +587,8 @@ def test_serving_loop_with_fp16_tail_and_trigger():
         pi, s, cbk, cbv = pu.oracle_tables(fmt, layer)
         ora = quant.empty_cache(fmt, H, 512)
         det = quant.compress_into(ora, kh[layer, P0:n_packed], vh[layer, P0:n_packed], moved, pi, s, cbk, cbv)
-        pu.compare_layer(gpu[layer], ora, det, fmt, moved, cbk, cbv)
+        det["keys"] = kh[layer, P0:n_packed]
+        pu.compare_layer(gpu[layer], ora, det, fmt, moved, layer)
 
 
 def test_multi_query_scoring_as_query_rows():
@@ -726,7 +722,7 @@ def test_full_size_sampled(short):
         gl = pu.download_cache(dev, fmt)[li]
         sub = {n: (a[kvh:kvh + 1] if isinstance(a, np.ndarray) else a) for n, a in gl.items()}
         sub["n_kv_heads"] = 1
-        st = pu.compare_layer(sub, c, det, fmt, slots, cbk, cbv)
+        st = pu.compare_layer(sub, c, det, fmt, slots, layer)
         _say("sample", layer, kvh, st)
         qh = Q[li][:, kvh * G:(kvh + 1) * G]
         ref = attention.decode_attention(c, qh, starts, lens, pi, s, cbk, cbv)

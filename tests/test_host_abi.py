@@ -77,10 +77,9 @@ def test_codebook_matches_oracle(d, bits):
     # fp32 tables (what the device uses) round identically
     assert np.array_equal(c.astype(np.float32), oc.astype(np.float32))
     assert np.array_equal(t.astype(np.float32), ot.astype(np.float32))
-    # the kernels apply the fp32 centroids rounded to fp16; that equals the
-    # oracle's stored values (fp16 of the exact centroids, no double rounding)
-    sc, _ = codebook.stored_codebook(d, bits)
-    assert np.array_equal(c.astype(np.float32).astype(np.float16).astype(np.float64), sc)
+    # and equal the oracle's table codebook
+    tc, _ = codebook.table_codebook(d, bits)
+    assert np.array_equal(c.astype(np.float32).astype(np.float64), tc)
 
 
 @pytest.mark.parametrize("kb,vb", [(3, 2), (4, 4), (0, 4), (0, 0), (5, 1), (2, 2), (8, 4)])

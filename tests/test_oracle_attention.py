@@ -96,17 +96,52 @@ def test_fine_value_codebook_approaches_exact_attention():
     assert err < 2e-2 * np.max(np.abs(ref)) and err > 0
 
 
-def test_turboquant_logits_are_unbiased_estimates():
-    # Averaged over many keys the QJL-corrected score has no systematic offset
-    # from the true <q, k> (QJL page, section 5); the MSE-only score does.
+def _logit_bias_z(n_draws=1500, n_keys=8, seed=4):
+    """z-scores of the mean TurboQuant logit over independent sketches S
+    against the exact scale * <q, x>, per key: the keys, the query and Pi are
+    fixed; every draw compresses the keys with its own Gaussian S into a
+    packed cache and scores them through the decode path's logits."""
+    d = 128
+    fmt = quant.Format(d, 3, 2)
+    pi, _ = rotation.make_rotations(d, 42 + seed)
+    cbk, cbv = codebook.codebook(d, 2), codebook.codebook(d, 2)
+    rs = np.random.default_rng(seed)
+    k = rs.standard_normal((n_keys, 1, d)) * 2.0
+    v = rs.standard_normal((n_keys, 1, d))
+    q = rs.standard_normal((1, 1, d))
+    scale = 1.0 / math.sqrt(d)
+    truth = scale * (k[:, 0] @ q[0, 0])
+    lg = np.empty((n_draws, n_keys))
+    for i in range(n_draws):
+        s = rs.standard_normal((d, d))
+        cache = quant.empty_cache(fmt, 1, 32)
+        quant.compress_into(cache, k, v, np.arange(n_keys), pi, s, cbk, cbv)
+        _, logits = attention.decode_attention(cache, q, [0], [n_keys], pi, s, cbk, cbv, return_logits=True)
+        lg[i] = logits[(0, 0)]
+    return (lg.mean(axis=0) - truth) / (lg.std(axis=0) / math.sqrt(n_draws))
+
+
+def test_turboquant_logits_are_unbiased_estimates(monkeypatch):
+    """QJL page §五: over independent sketches the decode logits average to
+    the exact scale * <q, x> for every key; with the QJL constant scaled by
+    0.5 or 1.5 they do not (the residual's part <q, r> is then missed or
+    overcounted)."""
+    z = _logit_bias_z()
+    assert np.max(np.abs(z)) < 4.5, z
+    kappa = quant.kappa
+    for f in (0.5, 1.5):
+        monkeypatch.setattr(quant, "kappa", lambda d, f=f: f * kappa(d))
+        z = _logit_bias_z(n_draws=800)
+        assert np.max(np.abs(z)) > 10, (f, z)
+    monkeypatch.setattr(quant, "kappa", kappa)
+
+
+def test_mse_only_logits_are_biased_by_the_distortion():
+    # the MSE-only part is biased toward zero by the factor 1 - D
     fmt = quant.Format(128, 3, 2)
     cache, q, st, ln, pi, s, cbk, cbv, kv = _build(fmt, 1, [4000], seed=4, g=1, scale_k=1.0)
-    _, lg = attention.decode_attention(cache, q, st, ln, pi, s, cbk, cbv, return_logits=True)
     k = kv[0][0][:, 0]
     true = (k @ q[0, 0]) / math.sqrt(128)
-    err = lg[(0, 0)] - true
-    assert abs(err.mean()) < 4 * err.std() / math.sqrt(len(err))
-    # the MSE-only part is biased toward zero by the factor 1 - D
     kp, _ = quant.dequantize_cache(cache, pi, cbk, cbv, 0, np.arange(4000))
     mse_only = (kp["xt"] @ q[0, 0]) / math.sqrt(128)
     slope = np.sum(mse_only * true) / np.sum(true * true)

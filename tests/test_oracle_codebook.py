@@ -101,18 +101,18 @@ def test_distortion_falls_with_bits():
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
-def test_stored_centroids_are_fp16_and_cost_almost_nothing(bits):
-    """The stored reconstruction values are the fp16 roundings of the exact
-    centroids: representable in fp16, still antisymmetric, within half an fp16
+def test_table_centroids_are_fp32_and_cost_nothing(bits):
+    """The table reconstruction values are the fp32 roundings of the exact
+    centroids: representable in fp32, still antisymmetric, within half an fp32
     ulp of the exact values, and their distortion (independent quadrature,
-    exact boundaries) exceeds the optimum by less than 1e-5 of it."""
+    exact boundaries) equals the optimum to 1e-12 of it."""
     d = 128
     c, t = codebook.codebook(d, bits)
-    cs, ts = codebook.stored_codebook(d, bits)
+    cs, ts = codebook.table_codebook(d, bits)
     assert np.array_equal(ts, t)
-    assert np.array_equal(cs.astype(np.float16).astype(np.float64), cs)
+    assert np.array_equal(cs.astype(np.float32).astype(np.float64), cs)
     assert np.array_equal(cs, -cs[::-1])
-    ulp = np.spacing(np.abs(c).astype(np.float16)).astype(np.float64)
+    ulp = np.spacing(np.abs(c).astype(np.float32)).astype(np.float64)
     assert np.all(np.abs(cs - c) <= 0.5 * ulp)
 
     def distortion(cc):
@@ -124,5 +124,5 @@ def test_stored_centroids_are_fp16_and_cost_almost_nothing(bits):
             tot += v
         return tot
 
-    base, stored = distortion(c), distortion(cs)
-    assert base <= stored < base * (1 + 1e-5)
+    base, table = distortion(c), distortion(cs)
+    assert base <= table * (1 + 1e-12) and table < base * (1 + 1e-10)

@@ -106,22 +106,20 @@ def test_v_cosine_two_bit_from_page():
 
 
 def _estimates_over_sketches(x, y, pi, c, t, n_draws, seed, d):
-    """Estimator samples with Pi fixed and S redrawn n_draws times."""
+    """quant.estimate_inner over n_draws independent Gaussian sketches S, with
+    Pi, x and y fixed: each draw compresses x with its own S
+    (quant.compress_k) and estimates <y, x> from the record."""
     rs = np.random.default_rng(seed)
-    idx, n = quant.compress_v(x[None], pi, c, t)
-    xt = quant.dequantize_mse(idx, n, pi, c)[0]
-    r = x - xt
-    rho = np.linalg.norm(r)
     out = np.empty(n_draws)
-    done = 0
-    while done < n_draws:
-        m = min(500, n_draws - done)
-        s = rs.standard_normal((m, d, d))
-        signs = np.where(np.einsum("mij,j->mi", s, r) >= 0, 1.0, -1.0)
-        sy = np.einsum("mij,j->mi", s, y)
-        out[done:done + m] = y @ xt + quant.kappa(d) * rho * np.sum(sy * signs, axis=1)
-        done += m
-    return out, r, rho
+    rec = None
+    for i in range(n_draws):
+        s = rs.standard_normal((d, d))
+        rec = quant.compress_k(x[None], pi, s, c, t)
+        out[i] = quant.estimate_inner(y, rec, pi, s, c)[0]
+    # the residual does not depend on S
+    xt = quant.dequantize_mse(rec["idx"], rec["norm"], pi, c)[0]
+    r = x - xt
+    return out, r, float(np.linalg.norm(r))
 
 
 def test_estimator_is_unbiased_with_closed_form_variance():
@@ -139,6 +137,31 @@ def test_estimator_is_unbiased_with_closed_form_variance():
     # and the MSE-only part alone is biased by exactly <y, r>
     xt = x - r
     assert abs((y @ xt) + (y @ r) - truth) < 1e-9
+
+
+def _bias_in_standard_errors(d=D, n_draws=2000):
+    """(mean estimate - <y, x>) / standard error, for a query with a large
+    component along the key's residual, so that the QJL term carries the
+    estimate."""
+    pi, _, (c, t) = _tables(2, d)
+    rs = np.random.default_rng(21)
+    x = rs.standard_normal(d) * 2.0
+    idx, n = quant.compress_v(x[None], pi, c, t)
+    r = x - quant.dequantize_mse(idx, n, pi, c)[0]
+    y = rs.standard_normal(d) + 3.0 * r / np.linalg.norm(r)
+    est, _, _ = _estimates_over_sketches(x, y, pi, c, t, n_draws, 5, d)
+    return (est.mean() - float(x @ y)) / (est.std() / math.sqrt(len(est)))
+
+
+def test_estimator_pins_the_qjl_constant(monkeypatch):
+    """Unbiasedness fixes sqrt(pi/2)/d: the estimator with the QJL constant
+    scaled by 0.5 or 1.5 is biased by many standard errors."""
+    assert abs(_bias_in_standard_errors()) < 4
+    kappa = quant.kappa
+    for f in (0.5, 1.5):
+        monkeypatch.setattr(quant, "kappa", lambda d, f=f: f * kappa(d))
+        assert abs(_bias_in_standard_errors()) > 20, f
+    monkeypatch.setattr(quant, "kappa", kappa)
 
 
 def test_estimator_variance_scales_as_one_over_d():
