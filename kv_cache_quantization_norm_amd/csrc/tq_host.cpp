@@ -77,8 +77,10 @@ SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_he
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   p.qprep_bytes = align(size_t(n_layers) * batch * n_q_heads * 2 * d * sizeof(float));
   p.partial_bytes = align(size_t(n_layers) * batch * n_q_heads * p.seg_max * (d + 2) * sizeof(float));
-  p.counter_bytes = align(size_t(p.problems + n_layers) * sizeof(uint32_t));
-  p.total_bytes = p.qprep_bytes + p.partial_bytes + p.counter_bytes;
+  p.counter_bytes = align(size_t(p.problems + n_layers + 2) * sizeof(uint32_t));
+  p.red_offset = p.qprep_bytes + p.partial_bytes + p.counter_bytes;
+  p.red_bytes = align(size_t(p.n_workgroups) * kDecodeWaves * kMaxGroup * d * sizeof(float));
+  p.total_bytes = p.red_offset + p.red_bytes;
   return p;
 }
 
@@ -93,7 +95,8 @@ TailPlan plan_decode_tail(int d, int n_layers, int batch, int n_kv_heads, int n_
   t.partial_offset = 2 * t.packed.qprep_bytes;
   t.counter_offset =
       t.partial_offset + align(size_t(n_layers) * batch * n_q_heads * t.seg_total * (d + 2) * sizeof(float));
-  t.total_bytes = t.counter_offset + t.packed.counter_bytes;
+  t.red_offset = t.counter_offset + t.packed.counter_bytes;
+  t.total_bytes = t.red_offset + (t.packed.red_bytes > t.tail.red_bytes ? t.packed.red_bytes : t.tail.red_bytes);
   return t;
 }
 

@@ -41,7 +41,10 @@ struct SplitPlan {
   int n_head_groups = 0;
   size_t qprep_bytes = 0;    // [L][B][Hq][2][d] fp32
   size_t partial_bytes = 0;  // [L][B][Hq][seg_max][d + 2] fp32
-  size_t counter_bytes = 0;  // uint32 [problems] pieces written (in-kernel merge), then [n_layers] append counts
+  size_t counter_bytes = 0;  // uint32 [problems] pieces written (in-kernel merge), then [n_layers] append counts,
+                             // then the two fp32 operand scales of the decode's centroid tables
+  size_t red_offset = 0;     // fp32 [n_workgroups][waves][kMaxGroup][d]: the wave merge of a decode workgroup
+  size_t red_bytes = 0;      // (kept in LDS when the tables leave room for it)
   size_t total_bytes = 0;
 };
 
@@ -56,7 +59,7 @@ SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_he
 // tail.seg_max][d + 2] fp32, and the packed part's merge counters.
 struct TailPlan {
   SplitPlan packed, tail;
-  size_t qplain_offset = 0, partial_offset = 0, counter_offset = 0, total_bytes = 0;
+  size_t qplain_offset = 0, partial_offset = 0, counter_offset = 0, red_offset = 0, total_bytes = 0;
   int64_t seg_total = 0;
 };
 TailPlan plan_decode_tail(int d, int n_layers, int batch, int n_kv_heads, int n_q_heads, int64_t max_seq_len,

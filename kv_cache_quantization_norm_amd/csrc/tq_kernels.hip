@@ -39,6 +39,12 @@ namespace {
 
 constexpr int D = 128;
 
+// Keys of up to 2 Lloyd-Max bits take one scaled fp16 value per centroid;
+// wider key codebooks take an fp16 high part and remainder (exact to about
+// 2^-22), where no scale is needed.
+constexpr bool key_split(int mk) { return mk >= 3; }
+
+
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -58,6 +64,17 @@ __device__ __forceinline__ floatx4 mfma16x16x4f32(float a, float b, floatx4 c) {
 }
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// A wave-uniform pointer made opaque to the optimiser (an empty asm on its
+// scalar registers), so that (uniform base + per-lane offset) addresses are
+// formed per load as scalar base + 32-bit lane offset instead of being
+// re-associated into 64-bit per-lane loop invariants that take two vector
+// registers each.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  __asm__ volatile("" : "+s"(p));
+  return p;
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -374,9 +391,9 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressA
   constexpr float KQS = MK > 4 ? kQScaleWide : kQScale;
   if (tid < 128) {
     const int nk = MK > 0 ? (1 << MK) : 0, nv = BV > 0 ? (1 << BV) : 0;
-    // Reconstruction values are applied at their stored (fp16) precision.
-    sm.kc[tid] = tid < nk ? float(_Float16(a.kc[tid])) : 0.f;
-    if (tid < 16) sm.vc[tid] = tid < nv ? float(_Float16(a.vc[tid])) : 0.f;
+    // The key residual applies the fp32 table centroids.
+    sm.kc[tid] = tid < nk ? a.kc[tid] : 0.f;
+    if (tid < 16) sm.vc[tid] = tid < nv ? a.vc[tid] : 0.f;
   }
   if constexpr (MK > 0) build_qtab(sm.kq, a.kb, (1 << MK) - 1, tid, kCompressWaves * 64, KQS);
   if constexpr (BV > 0) build_qtab(sm.vq, a.vb, (1 << BV) - 1, tid, kCompressWaves * 64);
@@ -696,9 +713,9 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
     const int nk = MK > 0 ? (1 << MK) : 0, nv = BV > 0 ? (1 << BV) : 0;
     const int tb = tid >> 7, j = tid & 127;
     if (j < NCB) {
-      if (tb == 0 && j < nk) cbv = float(_Float16(a.kc[j]));   // stored (fp16) reconstruction value
+      if (tb == 0 && j < nk) cbv = a.kc[j];   // fp32 table centroid (the key residual)
       if (tb == 1) cbv = j + 1 < nk ? a.kb[j] : INFINITY;
-      if (tb == 2 && j < nv) cbv = float(_Float16(a.vc[j]));
+      if (tb == 2 && j < nv) cbv = a.vc[j];
       if (tb == 3) cbv = j + 1 < nv ? a.vb[j] : INFINITY;
     }
   }
@@ -920,6 +937,8 @@ struct DecodeArgs {
   const int64_t* seq_start;
   const int32_t* seq_len;
   float* partial;       // [L][B][Hq][seg_max][D + 2]
+  const float* alpha;   // the operand scales alpha_k, alpha_v (written by the query preparation)
+  float* red_g;         // per decode workgroup [8 waves][8 heads][D] fp32: the wave merge, when not in LDS
   float* logits;        // score mode: [L][B][Hq][max_len]
   // In-kernel merge (non-null `done`): per problem, the count of its pieces
   // whose partial is written; the workgroup that completes the count merges
@@ -1023,32 +1042,48 @@ __device__ __forceinline__ half8 deq8(uint32_t bits, const uint32_t* lut) {
 }
 
 // Key tables.  A key code group of NC codes (NC m = 12 bits for m = 3, 8
-// bits otherwise) indexes one table entry holding its NC centroids in fp16
-// (the stored precision of the reconstruction values, so the lookup is exact).
-// Each lookup lands straight in an MFMA operand (8 consecutive coordinates =
-// 8 / NC entries), with no repacking.  The NC-code table is assembled from a
-// two-code pair table.
+// bits otherwise) indexes one table entry holding its NC centroids as fp16
+// MFMA operands, so each lookup lands straight in an operand (8 consecutive
+// coordinates = 8 / NC entries), with no repacking.  Two representations
+// (key_split): up to 2 Lloyd-Max bits, one fp16 value per centroid, the
+// codebook scaled by alpha_k (exact to about 2^-20 for such codebooks); 3 or
+// more bits, an fp16 high part and an fp16 remainder per centroid (HILO),
+// the entry holding the NC high parts, then the NC remainders.  The NC-code
+// table is assembled from a two-code pair table.
 template <int M> struct KLut {
+  static constexpr bool HILO = M >= 3;
   static constexpr int NC = M == 1 ? 8 : (M == 4 ? 2 : 4);  // codes per entry
   static constexpr int E = 1 << (NC * M);                   // entries
-  static constexpr int EW = NC / 2;                         // dwords per entry
+  static constexpr int EW = (NC / 2) * (HILO ? 2 : 1);      // dwords per entry
   static constexpr int PAIRS = 1 << (2 * M);                // two-code pair entries
+  static constexpr int PW = HILO ? 2 : 1;                   // dwords per pair entry (high, remainder)
 };
 
-// Pair table: entry x (two codes, x = c0 | c1 << M) = fp16 pair (c0, c1).
+// Pair table: entry x (two codes, x = c0 | c1 << M) = fp16 pair (c0, c1),
+// then (HILO) the fp16 pair of their remainders.  cl: lane l holds centroid
+// l mod 2^M (already scaled by alpha_k where the keys are scaled).
 template <int M>
 __device__ __forceinline__ void build_kpairs(uint32_t* phi, float cl, int tid, int nt = 256) {
-  constexpr int P = KLut<M>::PAIRS;
+  using K = KLut<M>;
+  constexpr int P = K::PAIRS;
   for (int x0 = 0; x0 < P; x0 += nt) {
     if (x0 + (tid & ~63) >= P) break;
     const int x = x0 + tid;
     const float c0 = lane_cent(cl, x & ((1 << M) - 1)), c1 = lane_cent(cl, (x >> M) & ((1 << M) - 1));
-    if (x < P) phi[x] = uint32_t(f16_bits(c0)) | (uint32_t(f16_bits(c1)) << 16);
+    const uint16_t h0 = f16_bits(c0), h1 = f16_bits(c1);
+    if (x < P) {
+      phi[x * K::PW] = uint32_t(h0) | (uint32_t(h1) << 16);
+      if constexpr (K::HILO) {
+        const float r0 = c0 - float(__builtin_bit_cast(_Float16, h0)), r1 = c1 - float(__builtin_bit_cast(_Float16, h1));
+        phi[x * K::PW + 1] = uint32_t(f16_bits(r0)) | (uint32_t(f16_bits(r1)) << 16);
+      }
+    }
   }
 }
-// NC-code table from the pair table (after a barrier): dword k of entry x is
-// the pair of codes 2k, 2k + 1.  Thread t of NT writes entries t + NT u; all
-// its pair-table reads are issued before its writes.
+// NC-code table from the pair table (after a barrier): high dword k of entry
+// x is the pair of codes 2k, 2k + 1 (and remainder dword k likewise).  Thread
+// t of NT writes entries t + NT u; all its pair-table reads are issued before
+// its writes.
 template <int M, int NT = 256>
 __device__ __forceinline__ void build_ktab(uint32_t* khi, const uint32_t* phi, int tid) {
   using K = KLut<M>;
@@ -1056,12 +1091,17 @@ __device__ __forceinline__ void build_ktab(uint32_t* khi, const uint32_t* phi, i
   else {
     static_assert(K::E % NT == 0 || NT % K::E == 0, "key table entries per thread");
     constexpr int U = (K::E + NT - 1) / NT;
+    constexpr int H = K::NC / 2;   // pairs per entry
     if (K::E < NT && tid >= K::E) return;
     uint32_t w[U][K::EW];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int k = 0; k < K::EW; ++k) w[u][k] = phi[((tid + NT * u) >> (2 * M * k)) & (K::PAIRS - 1)];
+      for (int k = 0; k < H; ++k) {
+        const int pr = ((tid + NT * u) >> (2 * M * k)) & (K::PAIRS - 1);
+        w[u][k] = phi[pr * K::PW];
+        if constexpr (K::HILO) w[u][H + k] = phi[pr * K::PW + 1];
+      }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       uint32_t* dst = khi + (tid + NT * u) * K::EW;
@@ -1074,37 +1114,58 @@ __device__ __forceinline__ void build_ktab(uint32_t* khi, const uint32_t* phi, i
   }
 }
 
-// 8 consecutive m-bit key codes (LSB-first in `bits`) -> 8 fp16 centroids.
+// 8 consecutive m-bit key codes (LSB-first in `bits`) -> 8 fp16 centroids
+// (hi), and for split keys their remainders (lo).
 template <int M>
-__device__ __forceinline__ half8 deq8_k(uint32_t bits, const uint32_t* khi) {
+__device__ __forceinline__ void deq8_k(uint32_t bits, const uint32_t* khi, half8& hi, half8& lo) {
   if constexpr (M == 1) {
-    return as_half8(*reinterpret_cast<const u32x4*>(khi + (bits & 0xFFu) * 4));
+    hi = as_half8(*reinterpret_cast<const u32x4*>(khi + (bits & 0xFFu) * 4));
   } else if constexpr (M == 4) {
-    return as_half8(u32x4{khi[bits & 0xFFu], khi[(bits >> 8) & 0xFFu], khi[(bits >> 16) & 0xFFu], khi[bits >> 24]});
+    // pair entries (high pair, remainder pair), one per code byte; each dword
+    // read on its own so that it lands in its operand register
+    const uint32_t* e0 = khi + (bits & 0xFFu) * 2;
+    const uint32_t* e1 = khi + ((bits >> 8) & 0xFFu) * 2;
+    const uint32_t* e2 = khi + ((bits >> 16) & 0xFFu) * 2;
+    const uint32_t* e3 = khi + (bits >> 24) * 2;
+    hi = as_half8(u32x4{e0[0], e1[0], e2[0], e3[0]});
+    lo = as_half8(u32x4{e0[1], e1[1], e2[1], e3[1]});
+  } else if constexpr (M == 3) {
+    // four-code entries: 4 high parts, 4 remainders; each half read on its
+    // own so that it lands in its operand registers
+    const uint32_t* e0 = khi + (bits & 0xFFFu) * 4;
+    const uint32_t* e1 = khi + ((bits >> 12) & 0xFFFu) * 4;
+    const u32x2 h0 = *reinterpret_cast<const u32x2*>(e0), h1 = *reinterpret_cast<const u32x2*>(e1);
+    const u32x2 l0 = *reinterpret_cast<const u32x2*>(e0 + 2), l1 = *reinterpret_cast<const u32x2*>(e1 + 2);
+    hi = as_half8(u32x4{h0[0], h0[1], h1[0], h1[1]});
+    lo = as_half8(u32x4{l0[0], l0[1], l1[0], l1[1]});
   } else {
-    constexpr uint32_t mask = M == 3 ? 0xFFFu : 0xFFu;
-    const u32x2 h0 = *reinterpret_cast<const u32x2*>(khi + (bits & mask) * 2);
-    const u32x2 h1 = *reinterpret_cast<const u32x2*>(khi + ((bits >> (4 * M)) & mask) * 2);
-    return as_half8(u32x4{h0[0], h0[1], h1[0], h1[1]});
+    const u32x2 h0 = *reinterpret_cast<const u32x2*>(khi + (bits & 0xFFu) * 2);
+    const u32x2 h1 = *reinterpret_cast<const u32x2*>(khi + ((bits >> 8) & 0xFFu) * 2);
+    hi = as_half8(u32x4{h0[0], h0[1], h1[0], h1[1]});
   }
 }
 
 // 8 consecutive m-bit key codes, m > 4 (bits [8 m s, 8 m s + 8 m) of a
-// lane's 32-coordinate slab of m dwords) -> 8 fp16 centroids from the
-// 2^m-entry fp16 table: one lookup per code (a table of code pairs would not
-// fit beside the value tables).
+// lane's 32-coordinate slab of m dwords) -> 8 fp16 centroids and their
+// remainders from the 2^m-entry fp16 tables (high parts, then remainders):
+// one lookup per code and part (a table of code pairs would not fit beside
+// the value tables).
 template <int M, int N>
-__device__ __forceinline__ half8 deq8_wide(const uint32_t (&w)[N], int s, const uint16_t* lut) {
+__device__ __forceinline__ void deq8_wide(const uint32_t (&w)[N], int s, const uint16_t* lut, half8& hi,
+                                          half8& lo) {
   constexpr uint32_t mask = (1u << M) - 1u;
-  uint32_t h[8];
+  uint32_t h[8], l[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int p = 8 * M * s + M * j, lo = p >> 5, sh = p & 31;
+    const int p = 8 * M * s + M * j, lo_w = p >> 5, sh = p & 31;
     const uint32_t c =
-        sh + M <= 32 ? (w[lo] >> sh) & mask : __builtin_amdgcn_alignbit(w[lo + 1 < N ? lo + 1 : lo], w[lo], sh) & mask;
+        sh + M <= 32 ? (w[lo_w] >> sh) & mask
+                     : __builtin_amdgcn_alignbit(w[lo_w + 1 < N ? lo_w + 1 : lo_w], w[lo_w], sh) & mask;
     h[j] = lut[c];
+    l[j] = lut[(1 << M) + c];
   }
-  return as_half8(u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)});
+  hi = as_half8(u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)});
+  lo = as_half8(u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)});
 }
 
 // Bits [8 m s, 8 m s + 8 m) of a lane's 32-coordinate slab (m dwords).
@@ -1124,7 +1185,9 @@ __device__ __forceinline__ uint32_t slab_bits(const uint32_t (&w)[N], int s) {
 // Lane-private value table for 4-bit values: entry e (two codes) of lane l's
 // copy sits at byte e * 256 + 4 l, so the 64 lanes of a lookup always hit 64
 // different banks.  One byte permute forms the address from the code byte and
-// the lane offset.
+// the lane offset; `lane4` holds 4 l in byte 0 and the table's 64 KB page in
+// byte 2, so that a table placed past the first 64 KB of LDS is still
+// addressed by that one permute plus the instruction's immediate offset.
 __device__ __forceinline__ void build_vrep(uint32_t* lut, float cl, int tid, int nt) {
   for (int x = tid; x < 256 * 16; x += nt) {   // entry x / 16, copies 4 (x % 16) .. + 3 (nt divides 4096)
     const int e = x >> 4;
@@ -1132,13 +1195,14 @@ __device__ __forceinline__ void build_vrep(uint32_t* lut, float cl, int tid, int
     *reinterpret_cast<u32x4*>(lut + e * 64 + (x & 15) * 4) = u32x4{w, w, w, w};
   }
 }
-__device__ __forceinline__ half8 deq8_vrep(uint32_t bits, uint32_t lane4, const uint32_t* lut) {
-  // byte 0 of the address: 4 lane; byte 1: code byte k; bytes 2, 3: zero
-  const unsigned char* base = reinterpret_cast<const unsigned char*>(lut);
-  const uint32_t a0 = __builtin_amdgcn_perm(bits, lane4, 0x0C0C0400u);
-  const uint32_t a1 = __builtin_amdgcn_perm(bits, lane4, 0x0C0C0500u);
-  const uint32_t a2 = __builtin_amdgcn_perm(bits, lane4, 0x0C0C0600u);
-  const uint32_t a3 = __builtin_amdgcn_perm(bits, lane4, 0x0C0C0700u);
+template <bool PAGE>
+__device__ __forceinline__ half8 deq8_vrep(uint32_t bits, uint32_t lane4, const unsigned char* base) {
+  // byte 0 of the address: 4 lane; byte 1: code byte k; byte 2: the page (PAGE) or zero; byte 3: zero
+  constexpr uint32_t b2 = PAGE ? 0x00020000u : 0x000C0000u;
+  const uint32_t a0 = __builtin_amdgcn_perm(bits, lane4, 0x0C000400u | b2);
+  const uint32_t a1 = __builtin_amdgcn_perm(bits, lane4, 0x0C000500u | b2);
+  const uint32_t a2 = __builtin_amdgcn_perm(bits, lane4, 0x0C000600u | b2);
+  const uint32_t a3 = __builtin_amdgcn_perm(bits, lane4, 0x0C000700u | b2);
   return as_half8(u32x4{*reinterpret_cast<const uint32_t*>(base + a0), *reinterpret_cast<const uint32_t*>(base + a1),
                         *reinterpret_cast<const uint32_t*>(base + a2), *reinterpret_cast<const uint32_t*>(base + a3)});
 }
@@ -1154,40 +1218,58 @@ __device__ __forceinline__ half8 deq8_vrep(uint32_t bits, uint32_t lane4, const 
 template <int MK, int BV, bool SCORE>
 __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(
     DecodeArgs a, CompressArgs ca) {
-  constexpr bool KWIDE = MK > 4;   // 7-bit codes: one fp16 table entry per code
+  constexpr bool KWIDE = MK > 4;   // 7-bit codes: one fp16 table entry per code (high parts, then remainders)
+  constexpr bool KSPLIT = MK > 0 && key_split(MK);   // key centroids as fp16 high part + remainder
   using KL = KLut<(MK > 0 && !KWIDE ? MK : 1)>;
   constexpr int NT = kDecodeWaves * 64;
-  constexpr int KT = MK > 0 ? (KWIDE ? (1 << MK) / 2 : KL::E * KL::EW) : 1;   // dwords of the key table
-  constexpr int KP = MK > 0 && !KWIDE && KL::NC > 2 ? KL::PAIRS : 1;          // pair-table dwords (if separate)
+  constexpr int KT = MK > 0 ? (KWIDE ? (1 << MK) : KL::E * KL::EW) : 1;   // dwords of the key table
+  constexpr int KP = MK > 0 && !KWIDE && KL::NC > 2 ? KL::PAIRS * KL::PW : 1;   // pair-table dwords (if separate)
   constexpr bool VREP = BV == 4;                                          // lane-private value table
   constexpr int VW = VREP ? 256 * 64 : (BV > 0 ? Lut<BV, false>::WORDS : 1);
   // Tables first, each starting below 64 KB so that lookups carry the table
-  // offset as an instruction immediate.
-  constexpr int OFF_K = 0;
-  constexpr int OFF_PHI = OFF_K + KT * 4;
-  constexpr int OFF_S = ((OFF_PHI + KP * 4 + 15) / 16) * 16;
-  constexpr int OFF_V = ((OFF_S + 256 * 16 + 255) / 256) * 256;
-  constexpr int OFF_RED = ((OFF_V + VW * 4 + 15) / 16) * 16;
-  constexpr int RED_BYTES = SCORE ? 0 : kDecodeWaves * kMaxGroup * D * 4;
+  // offset as an instruction immediate (the lane-private value table may
+  // start past 64 KB: its addresses carry the page, see deq8_vrep).
+  // Order: signs, then the small value tables (1 or 2 bits), the key table
+  // and its pair table, then the lane-private 4-bit value table.
+  constexpr int OFF_S = 0;
+  constexpr int S_END = MK > 0 ? 256 * 16 : 0;
+  constexpr int OFF_K = VREP ? S_END : ((S_END + VW * 4 + 255) / 256) * 256;
+  constexpr int OFF_PHI = OFF_K + KT * 4;   // read only while the key table is built
+  constexpr int OFF_V = VREP ? ((OFF_PHI + KP * 4 + 255) / 256) * 256 : S_END;
+  constexpr int V_PAGE = VREP && OFF_V >= 65536 ? 1 : 0;
+  constexpr int OFF_TAB_END = VREP ? ((OFF_V + VW * 4 + 15) / 16) * 16 : ((OFF_PHI + KP * 4 + 15) / 16) * 16;
+  constexpr int MISC_BYTES = kDecodeWaves * 128 * 4 + 2 * kDecodeWaves * 16 * 4 + 2 * 2 * 4 * 64 * 16 + 16;
+  constexpr int RED_FULL = kDecodeWaves * kMaxGroup * D * 4;
+  // The wave merge ([wave][head][coordinate] fp32) stays in LDS when the
+  // tables leave room for it, else it goes through the workgroup's slice of
+  // the workspace (L2).
+  constexpr bool RED_LDS = !SCORE && OFF_TAB_END + RED_FULL + MISC_BYTES <= 160 * 1024;
+  constexpr int OFF_RED = OFF_TAB_END;
+  constexpr int RED_BYTES = RED_LDS ? RED_FULL : 0;
   constexpr int OFF_NX = OFF_RED + RED_BYTES;
   constexpr int OFF_MW = OFF_NX + kDecodeWaves * 128 * 4;
   constexpr int OFF_LW = OFF_MW + kDecodeWaves * 16 * 4;
   constexpr int OFF_Q = OFF_LW + kDecodeWaves * 16 * 4;    // staged query operands [piece][r / z][s][lane]
   constexpr int OFF_CNT = OFF_Q + 2 * 2 * 4 * 64 * 16;
   constexpr int LDS_BYTES = OFF_CNT + 16;
-  static_assert(OFF_V < 65536, "tables must start below 64 KB");
+  static_assert(OFF_K < 65536, "the key table must start below 64 KB");
+  static_assert(VREP ? OFF_V - V_PAGE * 65536 < 65536 : OFF_V < 65536, "value table offset");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
+  static_assert(2 * 2 * 4 * 64 * 16 >= 2 * 16 * D * 4, "the in-kernel merge's result area fits the query staging");
   __shared__ __align__(256) unsigned char dsm[LDS_BYTES];
   uint32_t* const lut_k = reinterpret_cast<uint32_t*>(dsm + OFF_K);
   uint32_t* const pair_hi = reinterpret_cast<uint32_t*>(dsm + OFF_PHI);
   uint32_t* const lut_s = reinterpret_cast<uint32_t*>(dsm + OFF_S);
   uint32_t* const lut_v = reinterpret_cast<uint32_t*>(dsm + OFF_V);
-  float* const red = reinterpret_cast<float*>(dsm + OFF_RED);   // [wave][head][coordinate]
+  const unsigned char* const vrep_base = dsm + OFF_V - V_PAGE * 65536;
+  float* const red = reinterpret_cast<float*>(dsm + OFF_RED);   // [wave][head][coordinate] (RED_LDS)
   float* const nxch = reinterpret_cast<float*>(dsm + OFF_NX);
   float(*const mw)[16] = reinterpret_cast<float(*)[16]>(dsm + OFF_MW);
   float(*const lw)[16] = reinterpret_cast<float(*)[16]>(dsm + OFF_LW);
   uint32_t* const counter = reinterpret_cast<uint32_t*>(dsm + OFF_CNT);
   half8* const qstage = reinterpret_cast<half8*>(dsm + OFF_Q);
+  // the in-kernel merge's result area ([16][D] heads, [16][D] the tail's part)
+  float* const fin = RED_LDS ? red : reinterpret_cast<float*>(dsm + OFF_Q);
   static_assert(LDS_BYTES >= int(sizeof(AppendSmem)), "the append role reuses the decode LDS");
   if constexpr (!SCORE) {
     // append workgroups first (lowest indices, so they are dispatched first and
@@ -1208,18 +1290,28 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     const int r = i & 7, qd = nd >> 3, rem = nd & 7;
     wg = r * qd + (r < rem ? r : rem) + (i >> 3);
   }
+  // this workgroup's slice of the workspace for the wave merge (when not in LDS)
+  float* const red_wg = RED_LDS ? nullptr : a.red_g + int64_t(wg) * (kDecodeWaves * kMaxGroup * D);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, q = lane >> 4;   // MFMA column (head / coordinate) and k-group
   const bool lo_half = col >= 8;
-  const uint32_t lane4 = uint32_t(lane) * 4;
+  const uint32_t lane4 = uint32_t(lane) * 4 | uint32_t(V_PAGE << 16);
 
   // Scores are kept in base-2 units (scaled by log2 e) so that the softmax
   // weights are plain exp2; tq_score writes natural-unit logits.
   constexpr float kLog2e = 1.4426950408889634f;
   const float kscale = SCORE ? a.scale : a.scale * kLog2e;
   const float kscale_r = kscale * a.kappa;
+  // Operand scales of the centroid tables (see fp16_operand_scale): keys of
+  // <= 2 Lloyd-Max bits and every value table are held as fp16(alpha c); the
+  // rotated query carries 1 / alpha_k, the accumulated values 1 / alpha_v.
+  constexpr bool KSCALED = MK > 0 && !KSPLIT;
+  const float alpha_k = KSCALED ? a.alpha[0] : 1.f;
+  const float alpha_v = BV > 0 && !SCORE ? a.alpha[1] : 1.f;
+  const float kscale_k = kscale / alpha_k;
+  const float inv_alpha_v = 1.f / alpha_v;
   constexpr int KREC = MK > 0 ? 16 * MK : 2 * D;   // bytes per key code record
   constexpr int MKW = MK > 0 ? MK : 1;
   constexpr bool kPrefetch = MK > 0 && BV > 0 && !SCORE;
@@ -1372,7 +1464,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       const int piece = it >> 9, kind = (it >> 8) & 1, l = it & 63;
       const Run Rp = ctx_of(pa + (piece && has_b ? 1 : 0));
       const bool ok = Rp.hg * kMaxGroup + (l & 7) < a.G;
-      const float sc = ok ? (kind ? kscale_r : kscale) : 0.f;
+      const float sc = ok ? (kind ? kscale_r : kscale_k) : 0.f;
       const bool lo = (l & 15) >= 8;
       half8 o;
 #pragma unroll
@@ -1441,8 +1533,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   // slot0: the chunk's first slot in its (layer, KV head) plane; vblk: its value block.
   auto load_k = [&](int64_t slot0, KData& K) {
     if constexpr (MK > 0) {
-      const uint8_t* kp = a.k_idx + slot0 * KREC;
-      const uint8_t* sp = a.k_sign + slot0 * 16;
+      const uint8_t* kp = uniform_ptr(a.k_idx + slot0 * KREC);
+      const uint8_t* sp = uniform_ptr(a.k_sign + slot0 * 16);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         if constexpr (MK == 4) {
@@ -1463,13 +1555,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   };
   auto load_v = [&](int64_t slot0, int64_t vblk, VData& V) {
     if constexpr (MK > 0) {
-      const float nk = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.k_norm + slot0) + noff);
-      const float nr = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.k_rnorm + slot0) + noff);
+      const float nk = *reinterpret_cast<const float*>(uniform_ptr(reinterpret_cast<const uint8_t*>(a.k_norm + slot0)) + noff);
+      const float nr = *reinterpret_cast<const float*>(uniform_ptr(reinterpret_cast<const uint8_t*>(a.k_rnorm + slot0)) + noff);
       V.nrm[0] = col < 8 ? nk : nr;
     }
     if constexpr (BV > 0) {
-      V.nrm[1] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.v_norm + slot0) + noff);
-      const uint8_t* vp = a.v_idx + vblk * D * (4 * BV);
+      V.nrm[1] = *reinterpret_cast<const float*>(uniform_ptr(reinterpret_cast<const uint8_t*>(a.v_norm + slot0)) + noff);
+      const uint8_t* vp = uniform_ptr(a.v_idx + vblk * D * (4 * BV));
 #pragma unroll
       for (int vb = 0; vb < 8; ++vb)
         V.vw[vb] = *reinterpret_cast<const uint32_t*>(vp + voff + 16 * vb * (4 * BV));
@@ -1500,22 +1592,29 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       sm_[T] = floatx4{0.f, 0.f, 0.f, 0.f};
       sq_[T] = floatx4{0.f, 0.f, 0.f, 0.f};
       if constexpr (MK > 0) {
-        // all table lookups of the tile first, so that they are in flight
-        // together, then the products
-        half8 kh[4], sd[4];
+        // the table lookups of a step group first, so that they are in
+        // flight together, then its products (split keys: two steps per
+        // group, to bound the live operand registers; else the whole tile)
+        constexpr int SG = KSPLIT ? 2 : 4;
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          if constexpr (KWIDE)
-            kh[s2] = deq8_wide<MK>(K.kw[T], s2, reinterpret_cast<const uint16_t*>(lut_k));
-          else
-            kh[s2] = deq8_k<MK>(slab_bits<MK>(K.kw[T], s2), lut_k);
-          sd[s2] = *reinterpret_cast<const half8*>(lut_s + ((K.sg[T] >> (8 * s2)) & 0xFFu) * 4);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int g0 = 0; g0 < 4; g0 += SG) {
+          half8 kh[SG], kl[SG], sd[SG];
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          sm_[T] = mfma16x16x32(kh[s2], qr[s2], sm_[T]);
-          sq_[T] = mfma16x16x32(sd[s2], qs[s2], sq_[T]);
+          for (int u = 0; u < SG; ++u) {
+            const int s2 = g0 + u;
+            if constexpr (KWIDE)
+              deq8_wide<MK>(K.kw[T], s2, reinterpret_cast<const uint16_t*>(lut_k), kh[u], kl[u]);
+            else
+              deq8_k<MK>(slab_bits<MK>(K.kw[T], s2), lut_k, kh[u], kl[u]);
+            sd[u] = *reinterpret_cast<const half8*>(lut_s + ((K.sg[T] >> (8 * s2)) & 0xFFu) * 4);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < SG; ++u) {
+            sm_[T] = mfma16x16x32(kh[u], qr[g0 + u], sm_[T]);
+            if constexpr (KSPLIT) sm_[T] = mfma16x16x32(kl[u], qr[g0 + u], sm_[T]);
+            sq_[T] = mfma16x16x32(sd[u], qs[g0 + u], sq_[T]);
+          }
         }
       } else {
 #pragma unroll
@@ -1642,7 +1741,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
         for (int u = 0; u < 4; ++u) {
           const int vb = v0 + u;
           if constexpr (BV == 4) {
-            vd[u] = deq8_vrep(V.vw[vb], lane4, lut_v);
+            vd[u] = deq8_vrep<V_PAGE != 0>(V.vw[vb], lane4, vrep_base);
           } else if constexpr (BV > 0) {
             uint32_t bits = V.vw[vb];
             if constexpr (BV == 2) bits = (bits >> (16 * (q & 1))) & 0xFFFFu;
@@ -1687,10 +1786,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
         lw[wave][col] = live ? l_tot : 0.f;
       }
       if (live && !lo_half) {
-        float* rw = red + (wave * kMaxGroup + col) * D;
+        float* rw = (RED_LDS ? red : red_wg) + (wave * kMaxGroup + col) * D;
+        const float so = sig * inv_alpha_v;   // the value norms' normaliser and the value tables' scale
 #pragma unroll
         for (int vb = 0; vb < 8; ++vb) {
-          const float4 v4 = {acc[vb][0] * sig, acc[vb][1] * sig, acc[vb][2] * sig, acc[vb][3] * sig};
+          const float4 v4 = {acc[vb][0] * so, acc[vb][1] * so, acc[vb][2] * so, acc[vb][3] * so};
           *reinterpret_cast<float4*>(rw + 16 * vb + 4 * q) = v4;
         }
       }
@@ -1716,7 +1816,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
 #pragma unroll
           for (int w = 0; w < kDecodeWaves; ++w) {
             mv[w] = mw[w][g];
-            rv[w] = red[(w * kMaxGroup + g) * D + i];
+            if constexpr (RED_LDS)
+              rv[w] = red[(w * kMaxGroup + g) * D + i];
+            else   // written by other waves of this workgroup: read past the vector L1
+              rv[w] = __hip_atomic_load(const_cast<float*>(uniform_ptr(red_wg + w * kMaxGroup * D)) + g * D + i,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             lv[w] = lw[w][g];
           }
           float M = -INFINITY;
@@ -1849,8 +1953,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
           }
         }
       }
-      float* const res = red;            // [16][D]: heads, rows >= ng zero
-      float* const resp = red + 16 * D;  // [16][D]: the tail's part (stored domain)
+      float* const res = fin;            // [16][D]: heads, rows >= ng zero
+      float* const resp = fin + 16 * D;  // [16][D]: the tail's part (stored domain)
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int g = (tid >> 7) + 4 * k;
@@ -1930,9 +2034,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   // Load order: codebooks, then the staged query operands, then the sequence
   // table, so that the table build below (which needs only the codebooks)
   // does not wait for the chunk loads that the sequence data unlocks.
-  float kcl = 0.f, vcl = 0.f;   // lane l: key / value centroid l mod (number of centroids)
-  if constexpr (MK > 0) kcl = a.kc[lane & ((1 << MK) - 1)];
-  if constexpr (BV > 0) vcl = a.vc[lane & ((1 << BV) - 1)];
+  float kcl = 0.f, vcl = 0.f;   // lane l: key / value centroid l mod (number of centroids), times its scale
+  if constexpr (MK > 0) kcl = a.kc[lane & ((1 << MK) - 1)] * alpha_k;
+  if constexpr (BV > 0) vcl = a.vc[lane & ((1 << BV) - 1)] * alpha_v;
   const int c_first = wg * a.chunks_per_wg;
   const int c_last = c_first + a.chunks_per_wg < a.total_chunks ? c_first + a.chunks_per_wg : a.total_chunks;
   QItem qitem;
@@ -1968,8 +2072,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
 
   // ---- tables (built once, used for every chunk of the workgroup)
   if constexpr (KWIDE) {
-    // stored (fp16) reconstruction values, straight from the codebook
-    for (int x = tid; x < (1 << MK); x += NT) reinterpret_cast<uint16_t*>(lut_k)[x] = f16_bits(a.kc[x]);
+    // fp16 high parts [2^MK], then the remainders [2^MK]
+    for (int x = tid; x < (1 << MK); x += NT) {
+      const float c = a.kc[x];
+      const uint16_t h = f16_bits(c);
+      reinterpret_cast<uint16_t*>(lut_k)[x] = h;
+      reinterpret_cast<uint16_t*>(lut_k)[(1 << MK) + x] = f16_bits(c - float(__builtin_bit_cast(_Float16, h)));
+    }
   } else if constexpr (MK > 0) {
     if constexpr (KL::NC > 2)
       build_kpairs<MK>(pair_hi, kcl, tid, NT);
@@ -2101,6 +2210,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     }
     // ---- merge the group's pieces
     if (!had_a) flush(false);
+    if constexpr (!RED_LDS) __builtin_amdgcn_s_waitcnt(0);   // this wave's merge stores are complete
     __syncthreads();
     const int next_base = uni(counter[0]);   // every draw of the group is done
     merge(G.ra, wg - (G.pa * cpp) / a.chunks_per_wg);
@@ -2108,6 +2218,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     if (G.has_b) {
       __syncthreads();
       flush(had_b);
+      if constexpr (!RED_LDS) __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       merge(G.rb, wg - G.a_end / a.chunks_per_wg);
       arrive(G.pa + 1, G.rb);
@@ -2115,6 +2226,100 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     __syncthreads();
     base = next_base - 3 * kDecodeWaves;
     g0 = G.b_end;
+  }
+}
+
+// Per-codebook scale of the decode's fp16 centroid operands.  An fp16
+// operand carries 11 significant bits, so a centroid rounded to fp16 is off
+// by up to 2^-12 of its value, which on sharp softmaxes moves outputs past
+// the tolerance.  Scaling a codebook by alpha in [1, 2) before the rounding
+// moves every centroid to another point of the fp16 grid; the alpha kept is
+// the one whose largest relative rounding error over the nonzero centroid
+// magnitudes is smallest, among the candidates that put one magnitude m
+// exactly on an fp16 value v (alpha = v / m, v in [m, 2 m)).  A codebook with
+// one or two magnitudes is then exact to about 2^-20, the 16-level one to
+// about 2^-13.5.  The operand that meets the table (the rotated query, or the
+// output for values) carries 1 / alpha.  NT threads (the whole workgroup,
+// s_* holding NT entries); every thread returns alpha (ties go to the lowest
+// candidate index).
+template <int NT>
+__device__ float fp16_operand_scale(const float* c, int n, int tid, float* s_err, int* s_idx, float* s_alpha) {
+  float cv[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) cv[k] = k < n ? fabsf(c[k]) : 0.f;
+  float best = INFINITY, best_alpha = 1.f;
+  int best_idx = 0x7FFFFFFF;
+  for (int cand = tid; cand < n * 1024; cand += NT) {
+    const int i = cand >> 10, j = cand & 1023;
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) m = k == i ? cv[k] : m;
+    bool dup = false;   // an earlier centroid of the same magnitude has the same candidates
+#pragma unroll
+    for (int k = 0; k < 16; ++k) dup = dup || (k < i && cv[k] == m);
+    if (m == 0.f || dup || !(m < INFINITY)) continue;
+    // fp16 values in [m, 2 m): the binade of m from its first fp16 value at or
+    // above m, then the next binade up to 2 m
+    const int e = __builtin_amdgcn_frexp_expf(m) - 1;          // m in [2^e, 2^(e+1))
+    const float ulp = __builtin_amdgcn_ldexpf(1.f, e - 10);
+    const float v = ceilf(m / ulp) * ulp + float(j) * ulp;      // j-th grid point from m up (spacing doubles past 2^(e+1))
+    const float vv = v < __builtin_amdgcn_ldexpf(1.f, e + 1) ? v
+                     : __builtin_amdgcn_ldexpf(1.f, e + 1) + (v - __builtin_amdgcn_ldexpf(1.f, e + 1)) * 2.f;
+    const float alpha = vv / m;
+    if (!(alpha >= 1.f && alpha < 2.f)) continue;
+    float err = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float x = alpha * cv[k];
+      if (k < n && x > 0.f) err = fmaxf(err, fabsf(float(_Float16(x)) - x) / x);
+    }
+    if (err < best) {
+      best = err;
+      best_idx = cand;
+      best_alpha = alpha;
+    }
+  }
+  s_err[tid] = best;
+  s_idx[tid] = best_idx;
+  s_alpha[tid] = best_alpha;
+  __syncthreads();
+  for (int h = NT / 2; h > 0; h >>= 1) {
+    if (tid < h) {
+      const float e2 = s_err[tid + h];
+      const int i2 = s_idx[tid + h];
+      if (e2 < s_err[tid] || (e2 == s_err[tid] && i2 < s_idx[tid])) {
+        s_err[tid] = e2;
+        s_idx[tid] = i2;
+        s_alpha[tid] = s_alpha[tid + h];
+      }
+    }
+    __syncthreads();
+  }
+  const float a = s_idx[0] == 0x7FFFFFFF ? 1.f : s_alpha[0];
+  __syncthreads();
+  return a;
+}
+
+// The two operand scales of a decode call live in the workspace after the
+// merge and append counters: [problems][n_layers][alpha_k, alpha_v].
+__device__ __forceinline__ float* alpha_slot(uint32_t* done, int batch, int H, int Hq, int n_layers) {
+  const int G = Hq / H, n_hg = (G + kMaxGroup - 1) / kMaxGroup;
+  return reinterpret_cast<float*>(done + int64_t(n_layers) * batch * H * n_hg + n_layers);
+}
+
+// alpha_k (keys of <= 2 Lloyd-Max bits; 1 otherwise) and alpha_v from the
+// fp32 codebooks (nk, nv centroids; 0 for fp16 keys / values).
+template <int NT>
+__device__ void operand_scales(const float* kc, int nk, const float* vc, int nv, float* alpha) {
+  __shared__ float s_err[NT], s_alpha[NT];
+  __shared__ int s_idx[NT];
+  const int tid = threadIdx.x;
+  const bool scaled_k = nk > 0 && !key_split(__builtin_ctz(nk));
+  const float ak = scaled_k ? fp16_operand_scale<NT>(kc, nk, tid, s_err, s_idx, s_alpha) : 1.f;
+  const float av = nv > 0 ? fp16_operand_scale<NT>(vc, nv, tid, s_err, s_idx, s_alpha) : 1.f;
+  if (tid == 0) {
+    alpha[0] = ak;
+    alpha[1] = av;
   }
 }
 
@@ -2208,31 +2413,41 @@ __device__ __forceinline__ void qprep_quarter(const float* q, const float* pi, c
     }
   }
 }
+// Grid (5, n_layers): blocks x < 4 prepare quarter x of a layer's queries;
+// block (4, 0) finds the decode's operand scales.
 template <bool ROT>
 __global__ __launch_bounds__(256) void qprep_kernel(const float* q, const float* pi, const float* s, float* qprep,
-                                                    int batch, int H, int Hq, uint32_t* done,
-                                                    float* qplain = nullptr) {
+                                                    int batch, int H, int Hq, uint32_t* done, float* qplain,
+                                                    const float* kc, int nk, const float* vc, int nv) {
+  if (blockIdx.x == 4) {
+    if (blockIdx.y == 0) operand_scales<256>(kc, nk, vc, nv, alpha_slot(done, batch, H, Hq, gridDim.y));
+    return;
+  }
   qprep_quarter<ROT>(q, pi, s, qprep, batch, H, Hq, blockIdx.x, blockIdx.y, gridDim.y, done, qplain);
 }
 
 // The append of a few tokens and the query preparation of the same decode
 // step in one launch (they are independent): workgroups [0, n_append) run
-// the append blocks (item group, layer), the others the query preparation
-// blocks (quarter, layer) of qprep_kernel.
+// the append blocks (item group, layer), then the query preparation blocks
+// (quarter, layer) of qprep_kernel, then one block for the operand scales.
 template <int MK, int BV>
 __global__ __launch_bounds__(kAppendThreads) void append_prepare_kernel(
     CompressArgs a, int app_groups, int n_append, const float* q, const float* pi, const float* s, float* qprep,
-    int batch, int H, int Hq, uint32_t* done) {
+    int batch, int H, int Hq, uint32_t* done, int n_layers) {
   __shared__ AppendSmem sm;
   const int bid = blockIdx.x;
   if (bid < n_append) {
     append_body<MK, BV>(a, bid % app_groups, bid / app_groups, sm);
     return;
   }
-  if (threadIdx.x >= 256) return;   // the query preparation blocks take 4 waves
   const int r = bid - n_append;
-  qprep_quarter<(MK > 0)>(q, pi, s, qprep, batch, H, Hq, r & 3, r >> 2, (int(gridDim.x) - n_append) >> 2, done,
-                          nullptr);
+  if (r == 4 * n_layers) {
+    operand_scales<kAppendThreads>(a.kc, MK > 0 ? 1 << MK : 0, a.vc, BV > 0 ? 1 << BV : 0,
+                                   alpha_slot(done, batch, H, Hq, n_layers));
+    return;
+  }
+  if (threadIdx.x >= 256) return;   // the query preparation blocks take 4 waves
+  qprep_quarter<(MK > 0)>(q, pi, s, qprep, batch, H, Hq, r & 3, r >> 2, n_layers, done, nullptr);
 }
 
 // Merges the piece partials of one (layer, batch, KV head) for every query
@@ -2550,20 +2765,25 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   uint32_t* done = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + plan.qprep_bytes + plan.partial_bytes);
   const int mk = fmt->k_bits > 0 ? fmt->k_bits - 1 : 0;
   const int bv = fmt->v_bits;
+  const int nk = mk > 0 ? 1 << mk : 0, nv = bv > 0 ? 1 << bv : 0;
   if (stages & kStagePrepare) {
-    const dim3 qgrid(4, cache->n_layers);
+    const dim3 qgrid(5, cache->n_layers);
     if (fmt->k_bits > 0)
       hipLaunchKernelGGL(qprep_kernel<true>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qprep, batch,
-                         cache->n_kv_heads, n_q_heads, done, nullptr);
+                         cache->n_kv_heads, n_q_heads, done, nullptr, tables->k_centroids, nk, tables->v_centroids,
+                         nv);
     else
       hipLaunchKernelGGL(qprep_kernel<false>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qprep, batch,
-                         cache->n_kv_heads, n_q_heads, done, nullptr);
+                         cache->n_kv_heads, n_q_heads, done, nullptr, tables->k_centroids, nk, tables->v_centroids,
+                         nv);
     if ((st = launch_status("qprep"))) return st;
   }
   if (max_seq_len == 0 && SCORE) return TQ_OK;
 
   DecodeArgs a = make_args(fmt, tables, cache, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, plan,
                            qprep, partial, out);
+  a.alpha = reinterpret_cast<const float*>(done + plan.problems + cache->n_layers);
+  a.red_g = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.red_offset);
   if (!SCORE && (stages & kStageMerge)) {
     a.done = done;
     a.out = out;
@@ -2646,24 +2866,32 @@ tq_status decode_tail(const tq_format* fmt, const tq_tables* tables, const tq_ca
   const int bv = fmt->v_bits;
   // One query preparation for both parts (rotated and plain; the plain copy
   // alone for fp16 keys), which also zeroes the merge counts.
-  const dim3 qgrid(4, cache->n_layers);
+  const dim3 qgrid(5, cache->n_layers);
+  const int nk = mk > 0 ? 1 << mk : 0, nv = bv > 0 ? 1 << bv : 0;
   if (fmt->k_bits > 0)
     hipLaunchKernelGGL(qprep_kernel<true>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qrot, batch,
-                       cache->n_kv_heads, n_q_heads, done, qplain);
+                       cache->n_kv_heads, n_q_heads, done, qplain, tables->k_centroids, nk, tables->v_centroids, nv);
   else
     hipLaunchKernelGGL(qprep_kernel<false>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qrot, batch,
-                       cache->n_kv_heads, n_q_heads, done, nullptr);
+                       cache->n_kv_heads, n_q_heads, done, nullptr, tables->k_centroids, nk, tables->v_centroids,
+                       nv);
   if ((st = launch_status("qprep"))) return st;
   // The tail first (partials only), then the packed part, whose last
   // workgroup per problem merges both piece sets into out.
+  const float* alpha = reinterpret_cast<const float*>(done + tp.packed.problems + cache->n_layers);
+  float* red_g = reinterpret_cast<float*>(ws + tp.red_offset);
   DecodeArgs at = make_args(&f16, tables, tail, batch, n_q_heads, tail_start, tail_len, max_tail_len, scale,
                             tp.tail, fmt->k_bits > 0 ? qplain : qrot, partial, nullptr);
+  at.alpha = alpha;
+  at.red_g = red_g;
   at.seg_max = int(tp.seg_total);
   at.seg_base = int(tp.packed.seg_max);
   if ((st = launch_decode<false>(0, 0, at, dim3(unsigned(tp.tail.n_workgroups)), hs))) return st;
   DecodeArgs ap = make_args(fmt, tables, cache, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, tp.packed,
                             qrot, partial, nullptr);
   ap.seg_max = int(tp.seg_total);
+  ap.alpha = alpha;
+  ap.red_g = red_g;
   ap.done = done;
   ap.out = out;
   ap.tail_base = int(tp.packed.seg_max);
@@ -2856,7 +3084,7 @@ tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const
   }
   const int64_t groups = (n_tokens * a.H + kAppendItems - 1) / kAppendItems;
   const int64_t n_append = groups * n_layers;
-  const int64_t n_prep = int64_t(4) * cache->n_layers;   // (quarter, layer) preparation blocks
+  const int64_t n_prep = int64_t(4) * cache->n_layers + 1;   // (quarter, layer) preparation blocks + the scales
   if (n_append + n_prep > 0x7FFFFFFF) return fail(TQ_ERR_INVALID_ARG, "too many workgroups");
   hipStream_t hs = static_cast<hipStream_t>(stream);
   float* qprep = static_cast<float*>(workspace);
@@ -2867,7 +3095,8 @@ tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const
   if (a.mk == MK_ && a.bv == BV_) {                                                                              \
     hipLaunchKernelGGL((append_prepare_kernel<MK_, BV_>), grid, dim3(kAppendThreads), 0, hs, a, int(groups),     \
                        int(n_append),                                                                          \
-                       q, tables->pi, tables->s, qprep, batch, cache->n_kv_heads, n_q_heads, done);            \
+                       q, tables->pi, tables->s, qprep, batch, cache->n_kv_heads, n_q_heads, done,            \
+                       cache->n_layers);                                                                       \
     return launch_status("append + prepare");                                                                  \
   }
 #define TQ_AP_V(MK_) TQ_AP(MK_, 0) TQ_AP(MK_, 1) TQ_AP(MK_, 2) TQ_AP(MK_, 4)
