@@ -324,6 +324,27 @@ tq_status tq_score(const tq_format* fmt, const tq_tables* tables, const tq_cache
                    const int32_t* seq_len, int64_t max_seq_len, float scale, float* logits,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the static device scratch of tq_decode_attention_noalloc. */
+#define TQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* Device.  tq_decode_attention for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments, result and errors, without the
+ * workspace arguments.  The workspace lives in a static device array of
+ * TQ_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU the library runs on holds
+ * until the process ends; the call allocates nothing (no hipMalloc / hipFree,
+ * no allocating library routine).  Sizes whose workspace
+ * (tq_decode_workspace_bytes) exceeds that return TQ_ERR_WORKSPACE before
+ * anything is enqueued.  Every call on one GPU shares that GPU's array (the
+ * query preparation of each call rewrites what the call reads), so calls that
+ * overlap on one GPU (on different streams, or from different threads) race;
+ * serialise them.  The first call on a device looks up the array's address
+ * on that device (hipGetSymbolAddress); a failure there is TQ_ERR_HIP. */
+tq_status tq_decode_attention_noalloc(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                                      const float* q, int32_t batch, int32_t n_q_heads,
+                                      const int64_t* seq_start, const int32_t* seq_len, int64_t max_seq_len,
+                                      float scale, float* out, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* tq_status_string(tq_status status);
 

@@ -78,6 +78,7 @@ def _load(path: str = LIB_PATH):
                                            SZ, P]),
         "tq_decode_tail_workspace_bytes": (SZ, [fmtp, I32, I32, I32, I32, I64, I64]),
         "tq_decode_attention": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P, SZ, P]),
+        "tq_decode_attention_noalloc": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P]),
         "tq_score": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P, SZ, P]),
         "tq_decode_prepare": (I32, [fmtp, tabp, cachep, P, I32, I32, I64, P, SZ, P]),
         "tq_append_prepare": (I32, [fmtp, tabp, cachep, P, P, I32, I32, I32, I64, P, I64, P, I32, I32, I64, P, SZ,
@@ -105,6 +106,7 @@ EXPORTED = ("tq_layer_seed", "tq_make_rotations", "tq_make_codebook", "tq_cache_
             "tq_stream_read_probe",
             "tq_append_prepare",
             "tq_compress_kv_bounded", "tq_decode_attention_tail", "tq_decode_tail_workspace_bytes",
+            "tq_decode_attention_noalloc",
             "tq_status_string", "tq_last_error")
 
 
@@ -323,6 +325,21 @@ def tq_decode_attention(fmt: tq_format, tables: Tables, cache: Cache, q, seq_sta
                                     _ptr(seq_start), _ptr(seq_len), max_seq_len, scale, _ptr(out), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream)),
            "tq_decode_attention")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def tq_decode_attention_noalloc(fmt: tq_format, tables: Tables, cache: Cache, q, seq_start, seq_len, max_seq_len: int,
+                                out, scale: float = 0.0, stream=None):
+    """tq_decode_attention with its workspace in the library's static device
+    scratch (nothing is allocated; calls that overlap on one GPU race)."""
+    n_layers, batch, hq, d = q.shape
+    assert n_layers == cache.n_layers and q.is_contiguous() and out.is_contiguous()
+    tb, cs = tables.struct(), cache.struct()
+    _check(_lib.tq_decode_attention_noalloc(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(q), batch, hq,
+                                            _ptr(seq_start), _ptr(seq_len), max_seq_len, scale, _ptr(out),
+                                            _stream(stream)), "tq_decode_attention_noalloc")
 
 
 def tq_decode_prepare(fmt: tq_format, tables: Tables, cache: Cache, q, max_seq_len: int, workspace, stream=None):

@@ -31,6 +31,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "tq_internal.h"
 
@@ -2990,7 +2991,70 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const floatx4* __restr
 }  // namespace
 }  // namespace tq
 
+namespace tq {
+namespace {
+// Scratch of tq_decode_attention_noalloc: the decode workspace (prepared
+// queries, piece partials, merge counters, operand scales, wave-merge slices)
+// in a file-scope device array, one copy per GPU, held until the process
+// ends.  Host code never passes `scratch` itself to a kernel (on the host it
+// names a stand-in, not the device copy): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(TQ_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The calling thread's current device's copy of `scratch` (NULL with an
+// error recorded on failure).
+void* scratch_for_current_device() {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    fail(TQ_ERR_HIP, "no current device (%s, device %d)", hipGetErrorString(e), dev);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t se = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (se != hipSuccess || ptr == nullptr) {
+      fail(TQ_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev, hipGetErrorString(se));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+}  // namespace tq
+
 extern "C" {
+
+tq_status tq_decode_attention_noalloc(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
+                                      const float* q, int32_t batch, int32_t n_q_heads, const int64_t* seq_start,
+                                      const int32_t* seq_len, int64_t max_seq_len, float scale, float* out,
+                                      void* stream) {
+  using namespace tq;
+  clear_error();
+  tq_status st = check_format(fmt, true);
+  if (st) return st;
+  if (!cache) return fail(TQ_ERR_INVALID_ARG, "cache is NULL");
+  if (batch <= 0 || n_q_heads <= 0 || cache->n_kv_heads <= 0 || n_q_heads % cache->n_kv_heads ||
+      max_seq_len < 0 || cache->n_layers <= 0)
+    return fail(TQ_ERR_INVALID_ARG, "batch=%d n_q_heads=%d n_kv_heads=%d n_layers=%d max_seq_len=%lld", batch,
+                n_q_heads, cache->n_kv_heads, cache->n_layers, (long long)max_seq_len);
+  const size_t need = plan_decode(fmt->d, cache->n_layers, batch, cache->n_kv_heads, n_q_heads, max_seq_len)
+                          .total_bytes;
+  if (need > kNoAllocScratchBytes)
+    return fail(TQ_ERR_WORKSPACE, "these sizes need %zu bytes of decode scratch; the static scratch holds %zu",
+                need, kNoAllocScratchBytes);
+  void* ws = scratch_for_current_device();
+  if (!ws) return TQ_ERR_HIP;
+  return decode_common<false>(fmt, tables, cache, q, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, out,
+                              ws, kNoAllocScratchBytes, stream, kStageAll);
+}
 
 tq_status tq_stream_read_probe(const void* data, size_t bytes, float* partial, int32_t n_workgroups, void* stream) {
   tq::clear_error();
