@@ -18,8 +18,11 @@
  *   - d (head_dim) is 128 for the device calls.
  *   - All device pointers are plain device (HBM) addresses owned by the
  *     caller; the library never allocates, frees or retains device memory and
- *     keeps no mutable global state, so calls on different streams may run
- *     concurrently.  `stream` is a hipStream_t (NULL = the default stream).
+ *     keeps no mutable global state (apart from the per-thread error message,
+ *     the per-device address of tq_decode_attention_noalloc's static scratch
+ *     and the test hook tq_set_append_wait), so calls on different streams
+ *     may run concurrently.  `stream` is a hipStream_t (NULL = the default
+ *     stream).
  *   - Device calls validate their host-side arguments synchronously and
  *     return a status; kernels are then enqueued on `stream` and never trap.
  *     TQ_ERR_HIP reports a failed launch.  tq_last_error() gives a
@@ -59,7 +62,8 @@ enum {
   TQ_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad layout */
   TQ_ERR_UNSUPPORTED = 2, /* d != 128 on device, bit width out of range */
   TQ_ERR_WORKSPACE = 3,   /* workspace too small */
-  TQ_ERR_HIP = 4          /* a HIP launch failed */
+  TQ_ERR_HIP = 4,         /* a HIP launch failed */
+  TQ_ERR_APPEND_TIMEOUT = 5 /* tq_decode_step_check: a decode wave stopped waiting for the step's append */
 };
 
 enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_BF16 = 1, TQ_DTYPE_F16 = 2 };
@@ -81,9 +85,14 @@ typedef struct tq_format {
  * centroids and 2^m - 1 boundaries for the key (m = k_bits-1) and value
  * (m = v_bits) quantisers, as written by tq_make_codebook (rounded to fp32).
  * Compression compares rotated coordinates with the fp32 boundaries and forms
- * the key residual with the fp32 centroids.  Decode rounds the centroids to
- * fp16 for its MFMA operands, an approximation that moves a logit by about
- * 1e-4 of its row's largest logit (the tolerance is 1e-3). */
+ * the key residual with the fp32 centroids.  Decode feeds the centroids to
+ * fp16 MFMA operands: keys of 3 or more Lloyd-Max bits as an fp16 high part
+ * and remainder (about 22 significant bits); keys of 1 or 2 Lloyd-Max bits and
+ * all values as one fp16 value per centroid of the codebook scaled by
+ * k_operand_scale / v_operand_scale, numbers in [1, 2) that the caller takes
+ * from tq_fp16_operand_scale (host) for the same fp32 centroids; a value
+ * outside [1, 2) (e.g. 0) means 1, plain fp16 rounding, which on sharp
+ * softmaxes can move outputs by more than 1e-3. */
 typedef struct tq_tables {
   const float* pi;
   const float* s;
@@ -92,6 +101,8 @@ typedef struct tq_tables {
   const float* k_boundaries;
   const float* v_centroids;
   const float* v_boundaries;
+  float k_operand_scale;
+  float v_operand_scale;
 } tq_tables;
 
 /* Device planes of a packed cache (layout above). */
@@ -126,6 +137,17 @@ tq_status tq_make_rotations(int32_t d, uint64_t seed, float* pi, float* s, float
  * Writes 2^bits ascending centroids and 2^bits - 1 boundaries (midpoints) in
  * double to caller-owned host arrays.  1 <= bits <= 8, 3 <= d <= 65536. */
 tq_status tq_make_codebook(int32_t d, int32_t bits, double* centroids, double* boundaries);
+
+/* Host.  The scale alpha in [1, 2) of a codebook's fp16 decode operands: the
+ * one, among the alphas that put some centroid magnitude exactly on an fp16
+ * value, for which the largest relative rounding error of fp16(alpha |c_k|)
+ * over the nonzero magnitudes is smallest (ties: the smallest such alpha).
+ * An fp16 operand keeps 11 significant bits, so a centroid rounded to fp16 is
+ * off by up to 2^-12 of its value; scaled, a codebook with one or two
+ * magnitudes is exact to about 2^-20 and the 16-level one to about 2^-13.5.
+ * centroids: n fp32 values in host memory (1 <= n <= 256).  Returns 1 for
+ * invalid input or a codebook without a nonzero finite magnitude. */
+float tq_fp16_operand_scale(const float* centroids, int32_t n);
 
 /* Byte sizes of the eight cache planes for a format, in the order
  * k_idx, k_sign, k_norm, k_rnorm, k_f16, v_idx, v_norm, v_f16 (0 = unused). */
@@ -292,13 +314,16 @@ tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const
  * tq_decode_attention(fmt, tables, cache, q, batch, n_q_heads, seq_start,
  * seq_len, max_seq_len, scale, out, workspace, workspace_bytes, stream), with
  * their arguments, layouts, ownership and errors; both are checked before
- * anything is enqueued.  For fewer than 16 tokens it takes two launches: the
- * query preparation, then the decode kernel, whose first workgroups compress
- * the new tokens (QJL deep-dive, sections 2 and 5) while the others start
- * the attention (section 6); a decode wave waits for its layer's append only
- * before it reads a chunk that may hold a new token (slots [slot0, slot0 +
- * n_tokens) of each appended plane, or any slot when `slots` is given).  For
- * 16 or more tokens the two calls are made one after the other.  The
+ * anything is enqueued.  When the append takes at most 32 workgroups (one
+ * per 8 (token, KV head) items per layer) it takes two launches: the query
+ * preparation, then the decode kernel, whose first workgroups compress the
+ * new tokens (QJL deep-dive, sections 2 and 5) while the others start the
+ * attention (section 6) on the CUs the append leaves; a decode wave waits for
+ * its layer's append only before it reads a chunk that may hold a new token
+ * (slots [slot0, slot0 + n_tokens) of each appended plane, or any slot when
+ * `slots` is given).  Larger appends run before the decode: in the query
+ * preparation's launch for fewer than 16 tokens (tq_append_prepare, then
+ * tq_decode_attend), else as tq_compress_kv then tq_decode_attention.  The
  * workspace is tq_decode_attention's; calls on one workspace must not
  * overlap. */
 tq_status tq_decode_step(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, const void* k,
@@ -306,6 +331,27 @@ tq_status tq_decode_step(const tq_format* fmt, const tq_tables* tables, const tq
                          const int64_t* slots, int64_t slot0, const float* q, int32_t batch, int32_t n_q_heads,
                          const int64_t* seq_start, const int32_t* seq_len, int64_t max_seq_len, float scale,
                          float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host, synchronous.  Whether the last tq_decode_step on `workspace` (made
+ * with these sizes) ran its append inside the decode launch without a decode
+ * wave giving up its wait.  A wave that must read a chunk holding a new token
+ * waits for the layer's append workgroups with a bounded wait (about a
+ * second); if the wait ends unmet it records that in a flag word of the
+ * workspace (zeroed by every call's query preparation) and reads the chunk
+ * anyway, which may then miss the new tokens.  Synchronizes `stream`, reads
+ * the flag; TQ_OK if clear, TQ_ERR_APPEND_TIMEOUT if set, TQ_ERR_WORKSPACE /
+ * TQ_ERR_INVALID_ARG for bad arguments, TQ_ERR_HIP if the read fails. */
+tq_status tq_decode_step_check(const tq_format* fmt, int32_t n_layers, int32_t batch, int32_t n_kv_heads,
+                               int32_t n_q_heads, int64_t max_seq_len, const void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Host, test hook.  Sets the bounded wait of later tq_decode_step launches:
+ * at most max_polls polls of the append count (default 1 << 20), waiting for
+ * extra_groups more append workgroups than the launch has (default 0: any
+ * other value makes the wait unmeetable, for testing the give-up path).
+ * Process-wide; not for concurrent use with decode calls.  max_polls = 0 or
+ * extra_groups < 0 is TQ_ERR_INVALID_ARG. */
+tq_status tq_set_append_wait(uint32_t max_polls, int32_t extra_groups);
 
 /* Device.  The scoring half of tq_decode_attention alone (the pages' separate
  * MSE-score and QJL-score kernels, QJL deep-dive section 6): writes the

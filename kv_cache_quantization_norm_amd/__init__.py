@@ -23,7 +23,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtq.so")
 
-TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = range(5)
+TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP, TQ_ERR_APPEND_TIMEOUT = range(6)
 TQ_DTYPE_F32, TQ_DTYPE_BF16, TQ_DTYPE_F16 = 0, 1, 2
 VBLOCK = 32
 
@@ -40,7 +40,8 @@ class tq_format(ctypes.Structure):
 
 class tq_tables(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("pi", "s", "pi_s", "k_centroids", "k_boundaries", "v_centroids", "v_boundaries")]
+                ("pi", "s", "pi_s", "k_centroids", "k_boundaries", "v_centroids", "v_boundaries")] + \
+               [("k_operand_scale", ctypes.c_float), ("v_operand_scale", ctypes.c_float)]
 
 
 class tq_cache(ctypes.Structure):
@@ -69,6 +70,7 @@ def _load(path: str = LIB_PATH):
         "tq_layer_seed": (ctypes.c_uint64, [I32]),
         "tq_make_rotations": (I32, [I32, ctypes.c_uint64, P, P, P]),
         "tq_make_codebook": (I32, [I32, I32, P, P]),
+        "tq_fp16_operand_scale": (F32, [P, I32]),
         "tq_cache_plane_bytes": (I32, [fmtp, I32, I32, I64, P]),
         "tq_decode_workspace_bytes": (SZ, [fmtp, I32, I32, I32, I32, I64]),
         "tq_decode_split": (I32, [fmtp, I32, I32, I32, I32, I64, P]),
@@ -89,6 +91,8 @@ def _load(path: str = LIB_PATH):
         "tq_stream_read_probe": (I32, [P, SZ, P, I32, P]),
         "tq_decode_step": (I32, [fmtp, tabp, cachep, P, P, I32, I32, I32, I64, P, I64, P, I32, I32, P, P, I64, F32, P,
                                  P, SZ, P]),
+        "tq_decode_step_check": (I32, [fmtp, I32, I32, I32, I32, I64, P, SZ, P]),
+        "tq_set_append_wait": (I32, [ctypes.c_uint32, I32]),
         "tq_status_string": (ctypes.c_char_p, [I32]),
         "tq_last_error": (ctypes.c_char_p, []),
     }
@@ -106,7 +110,7 @@ EXPORTED = ("tq_layer_seed", "tq_make_rotations", "tq_make_codebook", "tq_cache_
             "tq_stream_read_probe",
             "tq_append_prepare",
             "tq_compress_kv_bounded", "tq_decode_attention_tail", "tq_decode_tail_workspace_bytes",
-            "tq_decode_attention_noalloc",
+            "tq_decode_attention_noalloc", "tq_decode_step_check", "tq_set_append_wait", "tq_fp16_operand_scale",
             "tq_status_string", "tq_last_error")
 
 
@@ -120,12 +124,16 @@ def _check(st: int, what: str):
 
 
 def _ptr(t) -> Optional[int]:
+    """Device pointer of a tensor the binding itself allocated (Tables, Cache),
+    a raw integer address, or None; host arrays are refused."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
     if isinstance(t, np.ndarray):
-        return t.ctypes.data
+        raise TypeError("a host (numpy) array was passed where the library expects device memory")
+    if not t.is_cuda:
+        raise ValueError("a host tensor was passed where the library expects device memory")
     return t.data_ptr()
 
 
@@ -162,6 +170,12 @@ def tq_make_codebook(d: int, bits: int):
     t = np.empty(max(1, (1 << bits) - 1), np.float64)
     _check(_lib.tq_make_codebook(d, bits, c.ctypes.data, t.ctypes.data), "tq_make_codebook")
     return c, t[: (1 << bits) - 1]
+
+
+def tq_fp16_operand_scale(centroids) -> float:
+    """Scale of a codebook's fp16 decode operands (fp32 centroids, host)."""
+    c = np.ascontiguousarray(np.asarray(centroids, np.float32))
+    return float(_lib.tq_fp16_operand_scale(c.ctypes.data, len(c)))
 
 
 def make_format(d: int = 128, k_bits: int = 4, v_bits: int = 4) -> tq_format:
@@ -210,6 +224,8 @@ class Tables:
     v_centroids: object
     v_boundaries: object
     host: dict
+    k_operand_scale: float = 1.0
+    v_operand_scale: float = 1.0
 
     @classmethod
     def create(cls, fmt: tq_format, layers: Sequence[int], device="cuda"):
@@ -235,11 +251,14 @@ class Tables:
 
         kc, kb = cb(fmt.k_bits - 1 if fmt.k_bits > 0 else 0)
         vc, vb = cb(fmt.v_bits)
-        return cls(fmt, dev["pi"], dev["s"], dev["pi_s"], kc, kb, vc, vb, host)
+        ks = tq_fp16_operand_scale(host[f"c{fmt.k_bits - 1}"][0]) if fmt.k_bits > 0 else 1.0
+        vs = tq_fp16_operand_scale(host[f"c{fmt.v_bits}"][0]) if fmt.v_bits > 0 else 1.0
+        return cls(fmt, dev["pi"], dev["s"], dev["pi_s"], kc, kb, vc, vb, host, ks, vs)
 
     def struct(self) -> tq_tables:
         return tq_tables(*[_ptr(x) for x in (self.pi, self.s, self.pi_s, self.k_centroids, self.k_boundaries,
-                                             self.v_centroids, self.v_boundaries)])
+                                             self.v_centroids, self.v_boundaries)],
+                         self.k_operand_scale, self.v_operand_scale)
 
 
 @dataclass
@@ -282,6 +301,95 @@ def _dtype_code(t) -> int:
 
 
 # ----------------------------------------------------------------------------
+# Argument checks: the C side takes raw device pointers, so every tensor is
+# checked here for being a contiguous device tensor of the dtype and shape the
+# call reads or writes (a wrong one would make the kernels read or write out of
+# bounds).
+
+
+def _dev(t, dtypes, shape, name: str) -> int:
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a device torch.Tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device (cuda) tensor, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    return t.data_ptr()
+
+
+def _f32():
+    import torch
+    return (torch.float32,)
+
+
+def _kv_types():
+    import torch
+    return (torch.float32, torch.bfloat16, torch.float16)
+
+
+def _i64():
+    import torch
+    return (torch.int64,)
+
+
+def _i32():
+    import torch
+    return (torch.int32,)
+
+
+def _u8():
+    import torch
+    return (torch.uint8,)
+
+
+def _kv(fmt: tq_format, cache: Cache, k, v):
+    """k, v [n_layers][n_tokens][n_kv_heads][d], same shape and dtype."""
+    import torch
+    if not isinstance(k, torch.Tensor):
+        raise TypeError(f"k: expected a device torch.Tensor, got {type(k).__name__}")
+    if k.dim() != 4:
+        raise ValueError("k: expected a 4-d tensor [n_layers][n_tokens][n_kv_heads][d]")
+    n_layers, n_tokens = int(k.shape[0]), int(k.shape[1])
+    shape = (n_layers, n_tokens, cache.n_kv_heads, fmt.d)
+    pk = _dev(k, _kv_types(), shape, "k")
+    pv = _dev(v, (k.dtype,), shape, "v")
+    return pk, pv, n_layers, n_tokens
+
+
+def _slots(slots, n_tokens: int):
+    return None if slots is None else _dev(slots, _i64(), (n_tokens,), "slots")
+
+
+def _q(fmt: tq_format, cache: Cache, q, name="q"):
+    """q [n_layers][batch][n_q_heads][d] float32 with n_layers = cache's."""
+    import torch
+    if not isinstance(q, torch.Tensor):
+        raise TypeError(f"{name}: expected a device torch.Tensor, got {type(q).__name__}")
+    if q.dim() != 4:
+        raise ValueError(f"{name}: expected a 4-d tensor [n_layers][batch][n_q_heads][d]")
+    _, batch, hq, _ = q.shape
+    return _dev(q, _f32(), (cache.n_layers, batch, hq, fmt.d), name), int(batch), int(hq)
+
+
+def _seq(seq_start, seq_len, batch: int, a="seq_start", b="seq_len"):
+    return _dev(seq_start, _i64(), (batch,), a), _dev(seq_len, _i32(), (batch,), b)
+
+
+def _out(fmt: tq_format, cache: Cache, out, batch: int, hq: int):
+    return _dev(out, _f32(), (cache.n_layers, batch, hq, fmt.d), "out")
+
+
+def _ws(workspace):
+    p = _dev(workspace, _u8(), None, "workspace")
+    return p, workspace.numel()
+
+
+# ----------------------------------------------------------------------------
 # Device calls
 
 
@@ -289,23 +397,20 @@ def tq_compress_kv(fmt: tq_format, tables: Tables, cache: Cache, k, v, layer0: i
                    slot0: int = 0, stream=None):
     """k, v: contiguous device tensors [n_layers][n_tokens][n_kv_heads][d]
     (float32, bfloat16 or float16); slots: optional device int64 [n_tokens]."""
-    assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape and k.dtype == v.dtype
-    n_layers, n_tokens = int(k.shape[0]), int(k.shape[1])
+    pk, pv, n_layers, n_tokens = _kv(fmt, cache, k, v)
     tb, cs = tables.struct(), cache.struct()
-    _check(_lib.tq_compress_kv(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(k), _ptr(v),
-                               _dtype_code(k), layer0, n_layers, n_tokens, _ptr(slots), slot0, _stream(stream)),
-           "tq_compress_kv")
+    _check(_lib.tq_compress_kv(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), pk, pv, _dtype_code(k), layer0,
+                               n_layers, n_tokens, _slots(slots, n_tokens), slot0, _stream(stream)), "tq_compress_kv")
 
 
 def tq_compress_kv_bounded(fmt: tq_format, tables: Tables, cache: Cache, k, v, max_workgroups: int, layer0: int = 0,
                            slots=None, slot0: int = 0, stream=None):
     """tq_compress_kv with the bulk kernel held to at most max_workgroups CUs."""
-    assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape and k.dtype == v.dtype
-    n_layers, n_tokens = int(k.shape[0]), int(k.shape[1])
+    pk, pv, n_layers, n_tokens = _kv(fmt, cache, k, v)
     tb, cs = tables.struct(), cache.struct()
-    _check(_lib.tq_compress_kv_bounded(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(k), _ptr(v),
-                                       _dtype_code(k), layer0, n_layers, n_tokens, _ptr(slots), slot0,
-                                       max_workgroups, _stream(stream)), "tq_compress_kv_bounded")
+    _check(_lib.tq_compress_kv_bounded(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), pk, pv, _dtype_code(k),
+                                       layer0, n_layers, n_tokens, _slots(slots, n_tokens), slot0, max_workgroups,
+                                       _stream(stream)), "tq_compress_kv_bounded")
 
 
 def workspace_for(fmt: tq_format, cache: Cache, batch: int, n_q_heads: int, max_seq_len: int, device="cuda"):
@@ -318,13 +423,13 @@ def tq_decode_attention(fmt: tq_format, tables: Tables, cache: Cache, q, seq_sta
                         out, workspace, scale: float = 0.0, stream=None):
     """q, out: device float32 [n_layers][batch][n_q_heads][d]; seq_start int64 and
     seq_len int32 device tensors [batch]."""
-    n_layers, batch, hq, d = q.shape
-    assert n_layers == cache.n_layers and q.is_contiguous() and out.is_contiguous()
+    pq, batch, hq = _q(fmt, cache, q)
+    ps, pl = _seq(seq_start, seq_len, batch)
+    po = _out(fmt, cache, out, batch, hq)
+    pw, nw = _ws(workspace)
     tb, cs = tables.struct(), cache.struct()
-    _check(_lib.tq_decode_attention(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(q), batch, hq,
-                                    _ptr(seq_start), _ptr(seq_len), max_seq_len, scale, _ptr(out), _ptr(workspace),
-                                    workspace.numel() * workspace.element_size(), _stream(stream)),
-           "tq_decode_attention")
+    _check(_lib.tq_decode_attention(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), pq, batch, hq, ps, pl,
+                                    max_seq_len, scale, po, pw, nw, _stream(stream)), "tq_decode_attention")
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -334,55 +439,73 @@ def tq_decode_attention_noalloc(fmt: tq_format, tables: Tables, cache: Cache, q,
                                 out, scale: float = 0.0, stream=None):
     """tq_decode_attention with its workspace in the library's static device
     scratch (nothing is allocated; calls that overlap on one GPU race)."""
-    n_layers, batch, hq, d = q.shape
-    assert n_layers == cache.n_layers and q.is_contiguous() and out.is_contiguous()
+    pq, batch, hq = _q(fmt, cache, q)
+    ps, pl = _seq(seq_start, seq_len, batch)
+    po = _out(fmt, cache, out, batch, hq)
     tb, cs = tables.struct(), cache.struct()
-    _check(_lib.tq_decode_attention_noalloc(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(q), batch, hq,
-                                            _ptr(seq_start), _ptr(seq_len), max_seq_len, scale, _ptr(out),
-                                            _stream(stream)), "tq_decode_attention_noalloc")
+    _check(_lib.tq_decode_attention_noalloc(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), pq, batch, hq, ps,
+                                            pl, max_seq_len, scale, po, _stream(stream)),
+           "tq_decode_attention_noalloc")
 
 
 def tq_decode_prepare(fmt: tq_format, tables: Tables, cache: Cache, q, max_seq_len: int, workspace, stream=None):
-    n_layers, batch, hq, d = q.shape
+    pq, batch, hq = _q(fmt, cache, q)
+    pw, nw = _ws(workspace)
     tb, cs = tables.struct(), cache.struct()
-    _check(_lib.tq_decode_prepare(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(q), batch, hq,
-                                  max_seq_len, _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                  _stream(stream)), "tq_decode_prepare")
+    _check(_lib.tq_decode_prepare(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), pq, batch, hq, max_seq_len,
+                                  pw, nw, _stream(stream)), "tq_decode_prepare")
 
 
 def tq_append_prepare(fmt: tq_format, tables: Tables, cache: Cache, k, v, q, max_seq_len: int, workspace,
                       layer0: int = 0, slots=None, slot0: int = 0, stream=None):
     """tq_compress_kv(k, v, ...) then tq_decode_prepare(q, ...), in one launch
     for fewer than 16 tokens."""
-    assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape and k.dtype == v.dtype
-    n_layers, n_tokens = int(k.shape[0]), int(k.shape[1])
-    _, batch, hq, _ = q.shape
+    pk, pv, n_layers, n_tokens = _kv(fmt, cache, k, v)
+    pq, batch, hq = _q(fmt, cache, q)
+    pw, nw = _ws(workspace)
     tb, cs = tables.struct(), cache.struct()
-    _check(_lib.tq_append_prepare(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(k), _ptr(v),
-                                  _dtype_code(k), layer0, n_layers, n_tokens, _ptr(slots), slot0, _ptr(q), batch, hq,
-                                  max_seq_len, _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                  _stream(stream)), "tq_append_prepare")
+    _check(_lib.tq_append_prepare(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), pk, pv, _dtype_code(k),
+                                  layer0, n_layers, n_tokens, _slots(slots, n_tokens), slot0, pq, batch, hq,
+                                  max_seq_len, pw, nw, _stream(stream)), "tq_append_prepare")
 
 
 def tq_decode_step(fmt: tq_format, tables: Tables, cache: Cache, k, v, q, seq_start, seq_len, max_seq_len: int, out,
                    workspace, layer0: int = 0, slots=None, slot0: int = 0, scale: float = 0.0, stream=None):
-    """tq_compress_kv(k, v, ...) then tq_decode_attention(q, ...): for fewer
-    than 16 tokens two launches, the append inside the decode launch."""
-    assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape and k.dtype == v.dtype
-    n_layers, n_tokens = int(k.shape[0]), int(k.shape[1])
-    _, batch, hq, _ = q.shape
-    assert q.is_contiguous() and out.is_contiguous()
+    """tq_compress_kv(k, v, ...) then tq_decode_attention(q, ...): for a small
+    append two launches, the append inside the decode launch."""
+    pk, pv, n_layers, n_tokens = _kv(fmt, cache, k, v)
+    pq, batch, hq = _q(fmt, cache, q)
+    ps, pl = _seq(seq_start, seq_len, batch)
+    po = _out(fmt, cache, out, batch, hq)
+    pw, nw = _ws(workspace)
     tb, cs = tables.struct(), cache.struct()
-    _check(_lib.tq_decode_step(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(k), _ptr(v), _dtype_code(k),
-                               layer0, n_layers, n_tokens, _ptr(slots), slot0, _ptr(q), batch, hq, _ptr(seq_start),
-                               _ptr(seq_len), max_seq_len, scale, _ptr(out), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(stream)), "tq_decode_step")
+    _check(_lib.tq_decode_step(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), pk, pv, _dtype_code(k), layer0,
+                               n_layers, n_tokens, _slots(slots, n_tokens), slot0, pq, batch, hq, ps, pl, max_seq_len,
+                               scale, po, pw, nw, _stream(stream)), "tq_decode_step")
+
+
+def tq_decode_step_check(fmt: tq_format, cache: Cache, batch: int, n_q_heads: int, max_seq_len: int, workspace,
+                         stream=None):
+    """Raises TQError(TQ_ERR_APPEND_TIMEOUT) if a decode wave of the last
+    tq_decode_step on `workspace` gave up waiting for the step's append
+    (synchronizes the stream)."""
+    pw, nw = _ws(workspace)
+    _check(_lib.tq_decode_step_check(ctypes.byref(fmt), cache.n_layers, batch, cache.n_kv_heads, n_q_heads,
+                                     max_seq_len, pw, nw, _stream(stream)), "tq_decode_step_check")
+
+
+def tq_set_append_wait(max_polls: int = 1 << 20, extra_groups: int = 0):
+    """Test hook: the bounded wait of later tq_decode_step launches."""
+    _check(_lib.tq_set_append_wait(max_polls, extra_groups), "tq_set_append_wait")
 
 
 def tq_stream_read_probe(data, partial, n_workgroups: int, stream=None):
     """Plain streaming read of the device tensor `data` (measurement reference)."""
-    _check(_lib.tq_stream_read_probe(_ptr(data), data.numel() * data.element_size(), _ptr(partial), n_workgroups,
-                                     _stream(stream)), "tq_stream_read_probe")
+    import torch
+    pd = _dev(data, (data.dtype,) if isinstance(data, torch.Tensor) else (), None, "data")
+    pp = _dev(partial, _f32(), (n_workgroups,), "partial")
+    _check(_lib.tq_stream_read_probe(pd, data.numel() * data.element_size(), pp, n_workgroups, _stream(stream)),
+           "tq_stream_read_probe")
 
 
 def tail_workspace_for(fmt: tq_format, cache: Cache, batch: int, n_q_heads: int, max_seq_len: int,
@@ -399,52 +522,58 @@ def tq_decode_attention_tail(fmt: tq_format, tables: Tables, cache: Cache, tail:
                              max_seq_len: int, tail_start, tail_len, max_tail_len: int, out, workspace,
                              scale: float = 0.0, stream=None):
     """Decode over a packed cache plus an fp16-format tail (one softmax)."""
-    n_layers, batch, hq, d = q.shape
+    pq, batch, hq = _q(fmt, cache, q)
+    ps, pl = _seq(seq_start, seq_len, batch)
+    pts, ptl = _seq(tail_start, tail_len, batch, "tail_start", "tail_len")
+    po = _out(fmt, cache, out, batch, hq)
+    pw, nw = _ws(workspace)
+    if tail.n_layers != cache.n_layers or tail.n_kv_heads != cache.n_kv_heads:
+        raise ValueError("tail: must have the cache's layers and KV heads")
     tb, cs, ts = tables.struct(), cache.struct(), tail.struct()
-    _check(_lib.tq_decode_attention_tail(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), ctypes.byref(ts),
-                                         _ptr(q), batch, hq, _ptr(seq_start), _ptr(seq_len), max_seq_len,
-                                         _ptr(tail_start), _ptr(tail_len), max_tail_len, scale, _ptr(out),
-                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+    _check(_lib.tq_decode_attention_tail(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), ctypes.byref(ts), pq,
+                                         batch, hq, ps, pl, max_seq_len, pts, ptl, max_tail_len, scale, po, pw, nw,
                                          _stream(stream)), "tq_decode_attention_tail")
 
 
 def tq_decode_partials(fmt: tq_format, tables: Tables, cache: Cache, batch: int, n_q_heads: int, seq_start, seq_len,
                        max_seq_len: int, workspace, scale: float = 0.0, stream=None):
+    ps, pl = _seq(seq_start, seq_len, batch)
+    pw, nw = _ws(workspace)
     tb, cs = tables.struct(), cache.struct()
-    _check(_lib.tq_decode_partials(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), batch, n_q_heads,
-                                   _ptr(seq_start), _ptr(seq_len), max_seq_len, scale, _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), _stream(stream)),
-           "tq_decode_partials")
+    _check(_lib.tq_decode_partials(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), batch, n_q_heads, ps, pl,
+                                   max_seq_len, scale, pw, nw, _stream(stream)), "tq_decode_partials")
 
 
 def tq_decode_combine(fmt: tq_format, tables: Tables, cache: Cache, batch: int, n_q_heads: int, max_seq_len: int,
                       out, workspace, stream=None):
+    po = _out(fmt, cache, out, batch, n_q_heads)
+    pw, nw = _ws(workspace)
     tb, cs = tables.struct(), cache.struct()
-    _check(_lib.tq_decode_combine(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), batch, n_q_heads,
-                                  max_seq_len, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                  _stream(stream)), "tq_decode_combine")
+    _check(_lib.tq_decode_combine(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), batch, n_q_heads, max_seq_len,
+                                  po, pw, nw, _stream(stream)), "tq_decode_combine")
 
 
 def tq_decode_attend(fmt: tq_format, tables: Tables, cache: Cache, batch: int, n_q_heads: int, seq_start, seq_len,
                      max_seq_len: int, out, workspace, scale: float = 0.0, stream=None):
     """Partials and their merge in one launch, on queries prepared in `workspace`."""
+    ps, pl = _seq(seq_start, seq_len, batch)
+    po = _out(fmt, cache, out, batch, n_q_heads)
+    pw, nw = _ws(workspace)
     tb, cs = tables.struct(), cache.struct()
-    _check(_lib.tq_decode_attend(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), batch, n_q_heads,
-                                 _ptr(seq_start), _ptr(seq_len), max_seq_len, scale, _ptr(out), _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(), _stream(stream)),
-           "tq_decode_attend")
+    _check(_lib.tq_decode_attend(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), batch, n_q_heads, ps, pl,
+                                 max_seq_len, scale, po, pw, nw, _stream(stream)), "tq_decode_attend")
 
 
 def tq_score(fmt: tq_format, tables: Tables, cache: Cache, q, seq_start, seq_len, max_seq_len: int, logits,
              workspace, scale: float = 0.0, stream=None):
     """logits: device float32 [n_layers][batch][n_q_heads][max_seq_len]."""
-    n_layers, batch, hq, d = q.shape
-    assert n_layers == cache.n_layers and q.is_contiguous() and logits.is_contiguous()
+    pq, batch, hq = _q(fmt, cache, q)
+    ps, pl = _seq(seq_start, seq_len, batch)
+    plg = _dev(logits, _f32(), (cache.n_layers, batch, hq, max(max_seq_len, 1)), "logits")
+    pw, nw = _ws(workspace)
     tb, cs = tables.struct(), cache.struct()
-    _check(_lib.tq_score(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), _ptr(q), batch, hq,
-                         _ptr(seq_start), _ptr(seq_len), max_seq_len, scale, _ptr(logits), _ptr(workspace),
-                         workspace.numel() * workspace.element_size(), _stream(stream)),
-           "tq_score")
+    _check(_lib.tq_score(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), pq, batch, hq, ps, pl, max_seq_len,
+                         scale, plg, pw, nw, _stream(stream)), "tq_score")
 
 
 def raw_call(name: str, *args):

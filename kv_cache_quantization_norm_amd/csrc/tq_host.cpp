@@ -4,6 +4,7 @@
 // Pages: "TurboQuant QJL投影深度剖析", section 2 (rotation from a QR
 // decomposition, Lloyd-Max codebook for the rotated-coordinate law, Gaussian
 // QJL sketch) and section 6 (seed 42 + 7 * layer per layer).
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -40,7 +41,7 @@ tq_status check_format(const tq_format* f, bool device) {
 }
 
 SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_heads,
-                      int64_t max_seq_len) {
+                      int64_t max_seq_len, int max_workgroups) {
   SplitPlan p;
   const int group = n_q_heads / n_kv_heads;
   p.n_head_groups = (group + kMaxGroup - 1) / kMaxGroup;
@@ -51,7 +52,7 @@ SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_he
   // Balanced split: one workgroup per CU, equal runs of chunks, each with at
   // least one chunk per wave; a run may cross from one problem into the next.
   int64_t wgs = (total + kDecodeWaves - 1) / kDecodeWaves;
-  if (wgs > kDecodeWorkgroups) wgs = kDecodeWorkgroups;
+  if (wgs > max_workgroups) wgs = max_workgroups;
   const int64_t cpw_b = (total + wgs - 1) / wgs;
   p.chunks_per_problem = cpp;
   p.chunks_per_wg = cpw_b;
@@ -62,7 +63,7 @@ SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_he
   // when its runs are at most that much longer than the balanced ones.  The
   // problem is then padded to k runs of equal length; padding chunks hold no
   // tokens and are never dealt.
-  int64_t k = kDecodeWorkgroups / p.problems;
+  int64_t k = max_workgroups / p.problems;
   if (k > cpp / kDecodeWaves) k = cpp / kDecodeWaves;   // at least one chunk per wave
   if (k >= 1 && cpp % cpw_b != 0) {
     const int64_t cpw_a = (cpp + k - 1) / k;
@@ -76,9 +77,11 @@ SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_he
   p.seg_max = (p.chunks_per_problem - 1 + p.chunks_per_wg - 1) / p.chunks_per_wg + 1;
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   p.qprep_bytes = align(size_t(n_layers) * batch * n_q_heads * 2 * d * sizeof(float));
+  p.counter_offset = p.qprep_bytes;
+  p.counter_bytes = align(size_t(p.problems + n_layers + 1) * sizeof(uint32_t));
+  p.partial_offset = p.counter_offset + p.counter_bytes;
   p.partial_bytes = align(size_t(n_layers) * batch * n_q_heads * p.seg_max * (d + 2) * sizeof(float));
-  p.counter_bytes = align(size_t(p.problems + n_layers + 2) * sizeof(uint32_t));
-  p.red_offset = p.qprep_bytes + p.partial_bytes + p.counter_bytes;
+  p.red_offset = p.partial_offset + p.partial_bytes;
   p.red_bytes = align(size_t(p.n_workgroups) * kDecodeWaves * kMaxGroup * d * sizeof(float));
   p.total_bytes = p.red_offset + p.red_bytes;
   return p;
@@ -349,6 +352,46 @@ tq_status tq_make_codebook(int32_t d, int32_t bits, double* centroids, double* b
   return TQ_OK;
 }
 
+float tq_fp16_operand_scale(const float* centroids, int32_t n) {
+  if (!centroids || n < 1 || n > 256) return 1.f;
+  // distinct nonzero finite magnitudes, ascending
+  std::vector<float> m;
+  for (int k = 0; k < n; ++k) {
+    const float a = std::fabs(centroids[k]);
+    if (a > 0.f && std::isfinite(a)) m.push_back(a);
+  }
+  std::sort(m.begin(), m.end());
+  m.erase(std::unique(m.begin(), m.end()), m.end());
+  if (m.empty()) return 1.f;
+  auto rel_err = [&](double alpha) {
+    double worst = 0.0;
+    for (float mk : m) {
+      const float x = float(alpha * double(mk));
+      const double r = double(float(_Float16(x)));
+      worst = std::fmax(worst, std::fabs(r - double(x)) / double(x));
+    }
+    return worst;
+  };
+  double best = INFINITY, best_alpha = 1.0;
+  for (float mi : m) {
+    // the fp16 values v in [mi, 2 mi): alpha = v / mi
+    int e = 0;
+    std::frexp(double(mi), &e);   // mi in [2^(e-1), 2^e)
+    const double ulp = std::ldexp(1.0, e - 1 - 10);
+    for (double v = std::ceil(double(mi) / ulp) * ulp; v < 2.0 * double(mi);
+         v += (v < std::ldexp(1.0, e) ? ulp : 2.0 * ulp)) {
+      const double alpha = v / double(mi);
+      if (!(alpha >= 1.0 && alpha < 2.0)) continue;
+      const double err = rel_err(alpha);
+      if (err < best || (err == best && alpha < best_alpha)) {
+        best = err;
+        best_alpha = alpha;
+      }
+    }
+  }
+  return float(best_alpha);
+}
+
 tq_status tq_cache_plane_bytes(const tq_format* fmt, int32_t n_layers, int32_t n_kv_heads,
                                int64_t capacity, size_t out_bytes[8]) {
   using namespace tq;
@@ -423,6 +466,7 @@ const char* tq_status_string(tq_status st) {
     case TQ_ERR_UNSUPPORTED: return "TQ_ERR_UNSUPPORTED";
     case TQ_ERR_WORKSPACE: return "TQ_ERR_WORKSPACE";
     case TQ_ERR_HIP: return "TQ_ERR_HIP";
+    case TQ_ERR_APPEND_TIMEOUT: return "TQ_ERR_APPEND_TIMEOUT";
     default: return "TQ_ERR_UNKNOWN";
   }
 }

@@ -39,18 +39,21 @@ struct SplitPlan {
   int64_t n_workgroups = 0;
   int64_t seg_max = 0;
   int n_head_groups = 0;
-  size_t qprep_bytes = 0;    // [L][B][Hq][2][d] fp32
-  size_t partial_bytes = 0;  // [L][B][Hq][seg_max][d + 2] fp32
-  size_t counter_bytes = 0;  // uint32 [problems] pieces written (in-kernel merge), then [n_layers] append counts,
-                             // then the two fp32 operand scales of the decode's centroid tables
-  size_t red_offset = 0;     // fp32 [n_workgroups][waves][kMaxGroup][d]: the wave merge of a decode workgroup
-  size_t red_bytes = 0;      // (kept in LDS when the tables leave room for it)
+  // Workspace layout, in this order; the counters sit right after the
+  // prepared queries, at an offset that does not depend on the work split.
+  size_t qprep_bytes = 0;     // [L][B][Hq][2][d] fp32, at offset 0
+  size_t counter_offset = 0;  // uint32 [problems] pieces written (in-kernel merge), then [n_layers] append
+  size_t counter_bytes = 0;   // counts, then the append wait's give-up flag
+  size_t partial_offset = 0;  // [L][B][Hq][seg_max][d + 2] fp32
+  size_t partial_bytes = 0;
+  size_t red_offset = 0;      // fp32 [n_workgroups][waves][kMaxGroup][d]: the wave merge of a decode workgroup
+  size_t red_bytes = 0;       // (kept in LDS when the tables leave room for it)
   size_t total_bytes = 0;
 };
 
 // Work decomposition and workspace layout of a decode / score call.
 SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_heads,
-                      int64_t max_seq_len);
+                      int64_t max_seq_len, int max_workgroups = kDecodeWorkgroups);
 
 // Decode over a packed cache plus an fp16 tail: each part has its own split;
 // the workspace holds the prepared queries twice (for the packed part, then

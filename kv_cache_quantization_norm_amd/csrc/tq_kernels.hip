@@ -938,7 +938,7 @@ struct DecodeArgs {
   const int64_t* seq_start;
   const int32_t* seq_len;
   float* partial;       // [L][B][Hq][seg_max][D + 2]
-  const float* alpha;   // the operand scales alpha_k, alpha_v (written by the query preparation)
+  float alpha_k, alpha_v;   // the operand scales of the centroid tables (1 = plain fp16 rounding)
   float* red_g;         // per decode workgroup [8 waves][8 heads][D] fp32: the wave merge, when not in LDS
   float* logits;        // score mode: [L][B][Hq][max_len]
   // In-kernel merge (non-null `done`): per problem, the count of its pieces
@@ -957,6 +957,13 @@ struct DecodeArgs {
   // decode wave about to load a chunk that holds one of the plane slots
   // [app_lo, app_hi) of an appended layer first waits for that count.
   int n_app, app_groups, app_layer0, app_layers;
+  // The wait is bounded: after app_polls polls of the count (each followed by
+  // a short sleep) the wave sets *app_flag (a sticky word of the workspace,
+  // zeroed by the call's query preparation) and goes on.  app_extra (0 but in
+  // tests) raises the count waited for, so that the wait cannot be met.
+  uint32_t app_polls;
+  int app_extra;
+  uint32_t* app_flag;
   int64_t app_lo, app_hi;
   uint32_t* app_done;
   // In-kernel merge over a second piece set (tail_cpp > 0): the pieces of a
@@ -1049,13 +1056,15 @@ __device__ __forceinline__ half8 deq8(uint32_t bits, const uint32_t* lut) {
 // (key_split): up to 2 Lloyd-Max bits, one fp16 value per centroid, the
 // codebook scaled by alpha_k (exact to about 2^-20 for such codebooks); 3 or
 // more bits, an fp16 high part and an fp16 remainder per centroid (HILO),
-// the entry holding the NC high parts, then the NC remainders.  The NC-code
-// table is assembled from a two-code pair table.
+// the entry holding the NC high parts, then the NC remainders (measured: one
+// table of such entries is faster than separate high and remainder tables).
+// The NC-code table is assembled from a two-code pair table.
 template <int M> struct KLut {
   static constexpr bool HILO = M >= 3;
   static constexpr int NC = M == 1 ? 8 : (M == 4 ? 2 : 4);  // codes per entry
   static constexpr int E = 1 << (NC * M);                   // entries
-  static constexpr int EW = (NC / 2) * (HILO ? 2 : 1);      // dwords per entry
+  static constexpr int H = NC / 2;                          // dwords of one part (high or remainder)
+  static constexpr int EW = H * (HILO ? 2 : 1);             // dwords per entry
   static constexpr int PAIRS = 1 << (2 * M);                // two-code pair entries
   static constexpr int PW = HILO ? 2 : 1;                   // dwords per pair entry (high, remainder)
 };
@@ -1082,35 +1091,34 @@ __device__ __forceinline__ void build_kpairs(uint32_t* phi, float cl, int tid, i
   }
 }
 // NC-code table from the pair table (after a barrier): high dword k of entry
-// x is the pair of codes 2k, 2k + 1 (and remainder dword k likewise).  Thread
-// t of NT writes entries t + NT u; all its pair-table reads are issued before
-// its writes.
+// x is the pair of codes 2k, 2k + 1 (remainder dword k likewise, after the
+// high ones).  Thread t of NT writes entries t + NT u; all its pair-table
+// reads are issued before its writes.
 template <int M, int NT = 256>
 __device__ __forceinline__ void build_ktab(uint32_t* khi, const uint32_t* phi, int tid) {
   using K = KLut<M>;
-  if constexpr (K::NC == 2) return;  // the pair table is the table
-  else {
-    static_assert(K::E % NT == 0 || NT % K::E == 0, "key table entries per thread");
-    constexpr int U = (K::E + NT - 1) / NT;
-    constexpr int H = K::NC / 2;   // pairs per entry
-    if (K::E < NT && tid >= K::E) return;
-    uint32_t w[U][K::EW];
+  static_assert(K::E % NT == 0 || NT % K::E == 0, "key table entries per thread");
+  constexpr int U = (K::E + NT - 1) / NT;
+  constexpr int H = K::H;   // pairs per entry
+  if (K::E < NT && tid >= K::E) return;
+  uint32_t w[U][K::EW];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+  for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int k = 0; k < H; ++k) {
-        const int pr = ((tid + NT * u) >> (2 * M * k)) & (K::PAIRS - 1);
-        w[u][k] = phi[pr * K::PW];
-        if constexpr (K::HILO) w[u][H + k] = phi[pr * K::PW + 1];
-      }
+    for (int k = 0; k < H; ++k) {
+      const int pr = ((tid + NT * u) >> (2 * M * k)) & (K::PAIRS - 1);
+      w[u][k] = phi[pr * K::PW];
+      if constexpr (K::HILO) w[u][H + k] = phi[pr * K::PW + 1];
+    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      uint32_t* dst = khi + (tid + NT * u) * K::EW;
-      if constexpr (K::EW == 2) {
-        *reinterpret_cast<u32x2*>(dst) = u32x2{w[u][0], w[u][1]};
-      } else {
-        *reinterpret_cast<u32x4*>(dst) = u32x4{w[u][0], w[u][1], w[u][2], w[u][3]};
-      }
+  for (int u = 0; u < U; ++u) {
+    uint32_t* dst = khi + (tid + NT * u) * K::EW;
+    if constexpr (K::EW == 1) {
+      *dst = w[u][0];
+    } else if constexpr (K::EW == 2) {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{w[u][0], w[u][1]};
+    } else {
+      *reinterpret_cast<u32x4*>(dst) = u32x4{w[u][0], w[u][1], w[u][2], w[u][3]};
     }
   }
 }
@@ -1122,8 +1130,8 @@ __device__ __forceinline__ void deq8_k(uint32_t bits, const uint32_t* khi, half8
   if constexpr (M == 1) {
     hi = as_half8(*reinterpret_cast<const u32x4*>(khi + (bits & 0xFFu) * 4));
   } else if constexpr (M == 4) {
-    // pair entries (high pair, remainder pair), one per code byte; each dword
-    // read on its own so that it lands in its operand register
+    // two-code entries (high pair, remainder pair), one per code byte; each
+    // dword read on its own so that it lands in its operand register
     const uint32_t* e0 = khi + (bits & 0xFFu) * 2;
     const uint32_t* e1 = khi + ((bits >> 8) & 0xFFu) * 2;
     const uint32_t* e2 = khi + ((bits >> 16) & 0xFFu) * 2;
@@ -1223,7 +1231,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   constexpr bool KSPLIT = MK > 0 && key_split(MK);   // key centroids as fp16 high part + remainder
   using KL = KLut<(MK > 0 && !KWIDE ? MK : 1)>;
   constexpr int NT = kDecodeWaves * 64;
-  constexpr int KT = MK > 0 ? (KWIDE ? (1 << MK) : KL::E * KL::EW) : 1;   // dwords of the key table
+  constexpr int KT = MK > 0 ? (KWIDE ? (1 << MK) : KL::E * KL::EW) : 1;   // key table dwords
   constexpr int KP = MK > 0 && !KWIDE && KL::NC > 2 ? KL::PAIRS * KL::PW : 1;   // pair-table dwords (if separate)
   constexpr bool VREP = BV == 4;                                          // lane-private value table
   constexpr int VW = VREP ? 256 * 64 : (BV > 0 ? Lut<BV, false>::WORDS : 1);
@@ -1309,13 +1317,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   // <= 2 Lloyd-Max bits and every value table are held as fp16(alpha c); the
   // rotated query carries 1 / alpha_k, the accumulated values 1 / alpha_v.
   constexpr bool KSCALED = MK > 0 && !KSPLIT;
-  const float alpha_k = KSCALED ? a.alpha[0] : 1.f;
-  const float alpha_v = BV > 0 && !SCORE ? a.alpha[1] : 1.f;
+  const float alpha_k = KSCALED ? a.alpha_k : 1.f;
+  const float alpha_v = BV > 0 && !SCORE ? a.alpha_v : 1.f;
   const float kscale_k = kscale / alpha_k;
   const float inv_alpha_v = 1.f / alpha_v;
   constexpr int KREC = MK > 0 ? 16 * MK : 2 * D;   // bytes per key code record
   constexpr int MKW = MK > 0 ? MK : 1;
-  constexpr bool kPrefetch = MK > 0 && BV > 0 && !SCORE;
+  constexpr bool kPrefetch = !SCORE;
   const int cpp = a.chunks_per_problem;
   const int64_t vblocks = a.capacity / kVBlock;
 
@@ -1414,7 +1422,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   // Before the loads of ticket u's chunk: if the chunk may hold a slot that
   // this launch's append workgroups write, wait (once per piece and wave) for
   // the layer's append count, then acquire at agent scope so that the loads
-  // see the new records.  Bounded: after about a second the wave goes on.
+  // see the new records.  Bounded: after app_polls polls (about a second by
+  // default) the wave records the give-up in the workspace's flag word, which
+  // the host reads with tq_decode_step_check, and goes on.
   bool app_ok_a = false, app_ok_b = false;
   auto gate = [&](const Group& G, int u) {
     if constexpr (!SCORE) {
@@ -1422,11 +1432,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       const bool in_xb = u >= G.xb0 && u < G.xb1 && !app_ok_b;
       if (!(in_xa || in_xb)) return;
       const int layer = in_xa ? G.ra.layer : G.rb.layer;
-      const uint32_t want = uint32_t(a.app_groups);
-      for (int spin = 0; spin < (1 << 20); ++spin) {
-        if (__hip_atomic_load(a.app_done + layer, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) break;
+      const uint32_t want = uint32_t(a.app_groups + a.app_extra);
+      bool met = false;
+      for (uint32_t spin = 0; spin < a.app_polls; ++spin) {
+        if (__hip_atomic_load(a.app_done + layer, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) {
+          met = true;
+          break;
+        }
         __builtin_amdgcn_s_sleep(8);
       }
+      if (!met && lane == 0) __hip_atomic_fetch_or(a.app_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       if (in_xa) app_ok_a = true; else app_ok_b = true;
     }
@@ -1509,16 +1524,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   // sequence are masked after loading.  Norms: lane (col, q) loads one key
   // norm (col < 8) or residual norm (col >= 8) of token 8 q + col % 8 and one
   // value norm.
+  // fp16 keys (kf: tile T, 32-wide step s2) and fp16 values (vf: 16-coordinate
+  // block vb) travel in the same structures as the codes.
   struct KData {
     uint32_t kw[2][MKW];
     uint32_t sg[2];
+    half8 kf[MK > 0 ? 1 : 2][MK > 0 ? 1 : 4];
   };
   struct VData {
     uint32_t vw[8];
     float nrm[2];
-  };
-  struct ChunkLate {
-    half8 kf[MK > 0 ? 1 : 2][MK > 0 ? 1 : 4];
     half8 vf[BV > 0 ? 1 : 8];
   };
   uint32_t koff[2], soff[2];
@@ -1533,6 +1548,15 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   // rel: chunk index within the problem (tokens 32 rel ..)
   // slot0: the chunk's first slot in its (layer, KV head) plane; vblk: its value block.
   auto load_k = [&](int64_t slot0, KData& K) {
+    if constexpr (MK == 0) {
+      const unsigned char* kp = uniform_ptr(reinterpret_cast<const unsigned char*>(a.k_f16 + slot0 * D));
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        const uint32_t off = (8 * (col >> 2) + 4 * T + (col & 3)) * (2 * D) + 64 * q;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) K.kf[T][s2] = *reinterpret_cast<const half8*>(kp + off + 16 * s2);
+      }
+    }
     if constexpr (MK > 0) {
       const uint8_t* kp = uniform_ptr(a.k_idx + slot0 * KREC);
       const uint8_t* sp = uniform_ptr(a.k_sign + slot0 * 16);
@@ -1560,6 +1584,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       const float nr = *reinterpret_cast<const float*>(uniform_ptr(reinterpret_cast<const uint8_t*>(a.k_rnorm + slot0)) + noff);
       V.nrm[0] = col < 8 ? nk : nr;
     }
+    if constexpr (BV == 0) {
+      const unsigned char* vp = uniform_ptr(reinterpret_cast<const unsigned char*>(a.v_f16 + vblk * D * kVBlock));
+#pragma unroll
+      for (int vb = 0; vb < 8; ++vb)
+        V.vf[vb] = *reinterpret_cast<const half8*>(vp + (16 * vb + col) * (2 * kVBlock) + 16 * q);
+    }
     if constexpr (BV > 0) {
       V.nrm[1] = *reinterpret_cast<const float*>(uniform_ptr(reinterpret_cast<const uint8_t*>(a.v_norm + slot0)) + noff);
       const uint8_t* vp = uniform_ptr(a.v_idx + vblk * D * (4 * BV));
@@ -1568,26 +1598,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
         V.vw[vb] = *reinterpret_cast<const uint32_t*>(vp + voff + 16 * vb * (4 * BV));
     }
   };
-  auto load_late = [&](int rel, ChunkLate& C) {
-    if constexpr (MK == 0) {
-#pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        const int64_t tk = R.slot_base + int64_t(rel) * kChunk + 8 * (col >> 2) + 4 * T + (col & 3);
-        const half8* kp = reinterpret_cast<const half8*>(a.k_f16 + tk * D + 32 * q);
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) C.kf[T][s2] = kp[s2];
-      }
-    }
-    if constexpr (BV == 0) {
-#pragma unroll
-      for (int vb = 0; vb < 8; ++vb)
-        C.vf[vb] = *reinterpret_cast<const half8*>(
-            a.v_f16 + ((R.vblk0 + rel) * D + 16 * vb + col) * kVBlock + 8 * q);
-    }
-  };
-
   // ---- scores of one chunk: tile T row col -> token 8 (col/4) + 4 T + col%4
-  auto score = [&](const KData& K, const ChunkLate& late, floatx4 (&sm_)[2], floatx4 (&sq_)[2]) {
+  auto score = [&](const KData& K, floatx4 (&sm_)[2], floatx4 (&sq_)[2]) {
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
       sm_[T] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -1619,14 +1631,14 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
         }
       } else {
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) sm_[T] = mfma16x16x32(late.kf[T][s2], qr[s2], sm_[T]);
+        for (int s2 = 0; s2 < 4; ++s2) sm_[T] = mfma16x16x32(K.kf[T][s2], qr[s2], sm_[T]);
       }
     }
   };
 
   // ---- logits, online softmax and value accumulation of one chunk (tokens
   // 32 rel .. of the current run's sequence).
-  auto attend = [&](int rel, const VData& V, const ChunkLate& late, const floatx4 (&sm_)[2],
+  auto attend = [&](int rel, const VData& V, const floatx4 (&sm_)[2],
                     const floatx4 (&sq_)[2]) {
     const int64_t crel = int64_t(rel) * kChunk;
     const bool full = crel + kChunk <= R.len;                                  // uniform over the wave
@@ -1749,7 +1761,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
             else if constexpr (BV == 1) bits = (bits >> (8 * q)) & 0xFFu;
             vd[u] = deq8<BV>(bits, lut_v);
           } else {
-            vd[u] = late.vf[vb];
+            vd[u] = V.vf[vb];
             if (!full) {   // fp16 values past the end may hold anything
 #pragma unroll
               for (int e = 0; e < 8; ++e)
@@ -2137,7 +2149,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
         // in flight (its first chunk is scored again with its own queries); a
         // ticket past the group's end reloads the latest chunk (still in
         // L2), whose copy is scored but never attended.
-        const ChunkLate late{};
         const int n = G.n_tickets;
         floatx4 m0[2], s0[2], m1[2], s1[2];
         // (value loads follow the key loads of the same ticket, which passed
@@ -2150,7 +2161,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
           load_v(slot_of(G, t0), vblk_of(G, t0), V0);
         }
         start_run(in_a ? 0 : 1);
-        score(K0, late, m0, s0);
+        score(K0, m0, s0);
         bool swap = false;
 #pragma unroll 1
         for (;;) {
@@ -2161,8 +2172,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
             const int u = t1 < n ? t1 : t0;
             load_v(slot_of(G, u), vblk_of(G, u), V1);
           }
-          score(K1, late, m1, s1);
-          attend(rel0 + t0, V0, late, m0, s0);
+          score(K1, m1, s1);
+          attend(rel0 + t0, V0, m0, s0);
           const int t3 = uni(d3) - base;
           if (t1 >= limit) { t0 = t1; t1 = t2; t2 = t3; swap = true; break; }
           const uint32_t d4 = draw();
@@ -2172,8 +2183,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
             const int u = t2 < n ? t2 : t1;
             load_v(slot_of(G, u), vblk_of(G, u), V0);
           }
-          score(K0, late, m0, s0);
-          attend(rel0 + t1, V1, late, m1, s1);
+          score(K0, m0, s0);
+          attend(rel0 + t1, V1, m1, s1);
           const int t4 = uni(d4) - base;
           if (t2 >= limit) { t0 = t2; t1 = t3; t2 = t4; break; }
           t0 = t2; t1 = t3; t2 = t4;
@@ -2191,14 +2202,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
 #pragma unroll 1
         while (t0 < limit) {
           const uint32_t d3 = draw();
-          ChunkLate late;
           gate(G, t0);
           load_k(slot_of(G, t0), K0);
           load_v(slot_of(G, t0), vblk_of(G, t0), V0);
-          if constexpr (MK == 0 || BV == 0) load_late(rel0 + t0, late);
           floatx4 sm_[2], sq_[2];
-          score(K0, late, sm_, sq_);
-          attend(rel0 + t0, V0, late, sm_, sq_);
+          score(K0, sm_, sq_);
+          attend(rel0 + t0, V0, sm_, sq_);
           t0 = t1; t1 = t2; t2 = uni(d3) - base;
         }
       }
@@ -2230,124 +2239,35 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   }
 }
 
-// Per-codebook scale of the decode's fp16 centroid operands.  An fp16
-// operand carries 11 significant bits, so a centroid rounded to fp16 is off
-// by up to 2^-12 of its value, which on sharp softmaxes moves outputs past
-// the tolerance.  Scaling a codebook by alpha in [1, 2) before the rounding
-// moves every centroid to another point of the fp16 grid; the alpha kept is
-// the one whose largest relative rounding error over the nonzero centroid
-// magnitudes is smallest, among the candidates that put one magnitude m
-// exactly on an fp16 value v (alpha = v / m, v in [m, 2 m)).  A codebook with
-// one or two magnitudes is then exact to about 2^-20, the 16-level one to
-// about 2^-13.5.  The operand that meets the table (the rotated query, or the
-// output for values) carries 1 / alpha.  NT threads (the whole workgroup,
-// s_* holding NT entries); every thread returns alpha (ties go to the lowest
-// candidate index).
-template <int NT>
-__device__ float fp16_operand_scale(const float* c, int n, int tid, float* s_err, int* s_idx, float* s_alpha) {
-  float cv[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) cv[k] = k < n ? fabsf(c[k]) : 0.f;
-  float best = INFINITY, best_alpha = 1.f;
-  int best_idx = 0x7FFFFFFF;
-  for (int cand = tid; cand < n * 1024; cand += NT) {
-    const int i = cand >> 10, j = cand & 1023;
-    float m = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) m = k == i ? cv[k] : m;
-    bool dup = false;   // an earlier centroid of the same magnitude has the same candidates
-#pragma unroll
-    for (int k = 0; k < 16; ++k) dup = dup || (k < i && cv[k] == m);
-    if (m == 0.f || dup || !(m < INFINITY)) continue;
-    // fp16 values in [m, 2 m): the binade of m from its first fp16 value at or
-    // above m, then the next binade up to 2 m
-    const int e = __builtin_amdgcn_frexp_expf(m) - 1;          // m in [2^e, 2^(e+1))
-    const float ulp = __builtin_amdgcn_ldexpf(1.f, e - 10);
-    const float v = ceilf(m / ulp) * ulp + float(j) * ulp;      // j-th grid point from m up (spacing doubles past 2^(e+1))
-    const float vv = v < __builtin_amdgcn_ldexpf(1.f, e + 1) ? v
-                     : __builtin_amdgcn_ldexpf(1.f, e + 1) + (v - __builtin_amdgcn_ldexpf(1.f, e + 1)) * 2.f;
-    const float alpha = vv / m;
-    if (!(alpha >= 1.f && alpha < 2.f)) continue;
-    float err = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float x = alpha * cv[k];
-      if (k < n && x > 0.f) err = fmaxf(err, fabsf(float(_Float16(x)) - x) / x);
-    }
-    if (err < best) {
-      best = err;
-      best_idx = cand;
-      best_alpha = alpha;
-    }
-  }
-  s_err[tid] = best;
-  s_idx[tid] = best_idx;
-  s_alpha[tid] = best_alpha;
-  __syncthreads();
-  for (int h = NT / 2; h > 0; h >>= 1) {
-    if (tid < h) {
-      const float e2 = s_err[tid + h];
-      const int i2 = s_idx[tid + h];
-      if (e2 < s_err[tid] || (e2 == s_err[tid] && i2 < s_idx[tid])) {
-        s_err[tid] = e2;
-        s_idx[tid] = i2;
-        s_alpha[tid] = s_alpha[tid + h];
-      }
-    }
-    __syncthreads();
-  }
-  const float a = s_idx[0] == 0x7FFFFFFF ? 1.f : s_alpha[0];
-  __syncthreads();
-  return a;
-}
-
-// The two operand scales of a decode call live in the workspace after the
-// merge and append counters: [problems][n_layers][alpha_k, alpha_v].
-__device__ __forceinline__ float* alpha_slot(uint32_t* done, int batch, int H, int Hq, int n_layers) {
-  const int G = Hq / H, n_hg = (G + kMaxGroup - 1) / kMaxGroup;
-  return reinterpret_cast<float*>(done + int64_t(n_layers) * batch * H * n_hg + n_layers);
-}
-
-// alpha_k (keys of <= 2 Lloyd-Max bits; 1 otherwise) and alpha_v from the
-// fp32 codebooks (nk, nv centroids; 0 for fp16 keys / values).
-template <int NT>
-__device__ void operand_scales(const float* kc, int nk, const float* vc, int nv, float* alpha) {
-  __shared__ float s_err[NT], s_alpha[NT];
-  __shared__ int s_idx[NT];
-  const int tid = threadIdx.x;
-  const bool scaled_k = nk > 0 && !key_split(__builtin_ctz(nk));
-  const float ak = scaled_k ? fp16_operand_scale<NT>(kc, nk, tid, s_err, s_idx, s_alpha) : 1.f;
-  const float av = nv > 0 ? fp16_operand_scale<NT>(vc, nv, tid, s_err, s_idx, s_alpha) : 1.f;
-  if (tid == 0) {
-    alpha[0] = ak;
-    alpha[1] = av;
-  }
-}
-
-// The query preparation of a decode call, one workgroup per (quarter,
-// layer): wave w owns row block 4 quarter + w of [Pi; S] (16 rows), read once
-// and split into fp16 high parts and remainders (times 2^11); the layer's
-// query rows (batch x Hq) are the MFMA columns, 16 at a time, each scaled by
+// The query preparation of a decode call, one workgroup per (quarter, layer,
+// run of kQprepRows query rows): wave w owns row block 4 quarter + w of
+// [Pi; S] (16 rows), read once per workgroup and split into fp16 high parts
+// and remainders (times 2^11); the run's query rows (of the layer's batch x
+// Hq) are the MFMA columns, 16 at a time, each scaled by
 // the power of two that puts its norm in [2^14, 2^15) and split likewise, so
 // three v_mfma_f32_16x16x32_f16 per 32-wide step keep about 22 bits (Pi and S
-// are loaded once per layer and quarter instead of once per KV head).
-// Quarter 0 also zeroes the layer's merge counts and its append count;
+// are loaded once per layer, quarter and run instead of once per KV head).
+// Quarter 0 of run 0 also zeroes the layer's merge counts and its append count;
 // `qplain` (if not null) receives q itself, for a decode over an fp16 tail.
 // fp16 keys (ROT false): q itself and zeros.
+constexpr int kQprepRows = 64;
 template <bool ROT>
 __device__ __forceinline__ void qprep_quarter(const float* q, const float* pi, const float* s, float* qprep,
                                               int batch, int H, int Hq, int quarter, int layer, int n_layers,
-                                              uint32_t* done, float* qplain) {
+                                              int run, uint32_t* done, float* qplain) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, kq = lane >> 4;
   const int G = Hq / H;
-  const int64_t base = int64_t(layer) * batch * Hq;   // the layer's first query row
-  const int nrows = batch * Hq;
-  if (done != nullptr && quarter == 0) {
+  const int row_lo = run * kQprepRows;                // the run's rows of the layer
+  const int nrows = min(batch * Hq - row_lo, kQprepRows);
+  const int64_t base = int64_t(layer) * batch * Hq + row_lo;   // the run's first query row
+  if (done != nullptr && quarter == 0 && run == 0) {
     const int n_hg = (G + kMaxGroup - 1) / kMaxGroup;
     const int64_t per_layer = int64_t(batch) * H * n_hg;   // problems of a layer (consecutive)
     for (int64_t e = tid; e < per_layer; e += 256) done[int64_t(layer) * per_layer + e] = 0u;
     if (tid == 0) done[int64_t(n_layers) * per_layer + layer] = 0u;
+    // the append wait's give-up flag, after the append counts
+    if (tid == 0 && layer == 0) done[int64_t(n_layers) * per_layer + n_layers] = 0u;
   }
   if (!ROT || qplain != nullptr) {
     float* dst = ROT ? qplain : qprep;
@@ -2414,23 +2334,21 @@ __device__ __forceinline__ void qprep_quarter(const float* q, const float* pi, c
     }
   }
 }
-// Grid (5, n_layers): blocks x < 4 prepare quarter x of a layer's queries;
-// block (4, 0) finds the decode's operand scales.
+// Grid (4 quarters, n_layers, runs of kQprepRows query rows).
 template <bool ROT>
 __global__ __launch_bounds__(256) void qprep_kernel(const float* q, const float* pi, const float* s, float* qprep,
-                                                    int batch, int H, int Hq, uint32_t* done, float* qplain,
-                                                    const float* kc, int nk, const float* vc, int nv) {
-  if (blockIdx.x == 4) {
-    if (blockIdx.y == 0) operand_scales<256>(kc, nk, vc, nv, alpha_slot(done, batch, H, Hq, gridDim.y));
-    return;
-  }
-  qprep_quarter<ROT>(q, pi, s, qprep, batch, H, Hq, blockIdx.x, blockIdx.y, gridDim.y, done, qplain);
+                                                    int batch, int H, int Hq, uint32_t* done, float* qplain) {
+  qprep_quarter<ROT>(q, pi, s, qprep, batch, H, Hq, blockIdx.x, blockIdx.y, gridDim.y, blockIdx.z, done, qplain);
+}
+// Grid of the query preparation for n_layers layers of batch x Hq query rows.
+inline dim3 qprep_grid(int n_layers, int batch, int Hq) {
+  return dim3(4, unsigned(n_layers), unsigned((batch * Hq + kQprepRows - 1) / kQprepRows));
 }
 
 // The append of a few tokens and the query preparation of the same decode
 // step in one launch (they are independent): workgroups [0, n_append) run
 // the append blocks (item group, layer), then the query preparation blocks
-// (quarter, layer) of qprep_kernel, then one block for the operand scales.
+// (quarter, layer, run) of qprep_kernel.
 template <int MK, int BV>
 __global__ __launch_bounds__(kAppendThreads) void append_prepare_kernel(
     CompressArgs a, int app_groups, int n_append, const float* q, const float* pi, const float* s, float* qprep,
@@ -2442,13 +2360,9 @@ __global__ __launch_bounds__(kAppendThreads) void append_prepare_kernel(
     return;
   }
   const int r = bid - n_append;
-  if (r == 4 * n_layers) {
-    operand_scales<kAppendThreads>(a.kc, MK > 0 ? 1 << MK : 0, a.vc, BV > 0 ? 1 << BV : 0,
-                                   alpha_slot(done, batch, H, Hq, n_layers));
-    return;
-  }
   if (threadIdx.x >= 256) return;   // the query preparation blocks take 4 waves
-  qprep_quarter<(MK > 0)>(q, pi, s, qprep, batch, H, Hq, r & 3, r >> 2, n_layers, done, nullptr);
+  qprep_quarter<(MK > 0)>(q, pi, s, qprep, batch, H, Hq, r & 3, (r >> 2) % n_layers, n_layers, (r >> 2) / n_layers,
+                          done, nullptr);
 }
 
 // Merges the piece partials of one (layer, batch, KV head) for every query
@@ -2708,6 +2622,8 @@ DecodeArgs make_args(const tq_format* fmt, const tq_tables* tables, const tq_cac
   a.out = nullptr;
   a.max_len = max_seq_len;
   a.scale = scale != 0.f ? scale : 1.0f / std::sqrt(float(fmt->d));
+  a.alpha_k = tables->k_operand_scale >= 1.f && tables->k_operand_scale < 2.f ? tables->k_operand_scale : 1.f;
+  a.alpha_v = tables->v_operand_scale >= 1.f && tables->v_operand_scale < 2.f ? tables->v_operand_scale : 1.f;
   a.kappa = float(std::sqrt(M_PI / 2.0) / fmt->d);
   return a;
 }
@@ -2724,7 +2640,13 @@ enum {
   kStageAll = kStagePrepare | kStagePartials | kStageMerge
 };
 
-// An append run by the decode launch's first workgroups (tq_decode_step).
+// An append run by the decode launch's first workgroups (tq_decode_step), when
+// it takes at most kMaxFusedAppend workgroups.
+constexpr int kMaxFusedAppend = 32;
+// The bounded wait of a decode wave for the append (see DecodeArgs.app_polls);
+// changed only by the test hook tq_set_append_wait.
+uint32_t g_append_wait_polls = 1u << 20;
+int g_append_wait_extra = 0;
 struct FusedAppend {
   CompressArgs ca;
   int groups = 0;            // append workgroups per layer
@@ -2754,7 +2676,14 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   if (max_seq_len < 0) return fail(TQ_ERR_INVALID_ARG, "max_seq_len < 0");
   if (int64_t(cache->n_layers) * batch > 65535)
     return fail(TQ_ERR_INVALID_ARG, "n_layers * batch exceeds 65535");
-  const SplitPlan plan = plan_decode(fmt->d, cache->n_layers, batch, cache->n_kv_heads, n_q_heads, max_seq_len);
+  if ((int64_t(batch) * n_q_heads + kQprepRows - 1) / kQprepRows > 65535)
+    return fail(TQ_ERR_INVALID_ARG, "batch * n_q_heads exceeds %d", 65535 * kQprepRows);
+  // With an append in the launch, its workgroups take CUs first: the decode
+  // split is made for the CUs they leave, so that no decode workgroup waits
+  // for a CU (one decode workgroup per CU).
+  const int app_wgs = app != nullptr ? app->groups * app->layers : 0;
+  const SplitPlan plan = plan_decode(fmt->d, cache->n_layers, batch, cache->n_kv_heads, n_q_heads, max_seq_len,
+                                     kDecodeWorkgroups - app_wgs);
   if (plan.problems * plan.chunks_per_problem > (int64_t(1) << 30))
     return fail(TQ_ERR_INVALID_ARG, "too many 32-token chunks in one call");
   if (!workspace || workspace_bytes < plan.total_bytes)
@@ -2762,28 +2691,24 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   if (stages & kStageCheckOnly) return TQ_OK;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   float* qprep = static_cast<float*>(workspace);
-  float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.qprep_bytes);
-  uint32_t* done = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + plan.qprep_bytes + plan.partial_bytes);
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.partial_offset);
+  uint32_t* done = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + plan.counter_offset);
   const int mk = fmt->k_bits > 0 ? fmt->k_bits - 1 : 0;
   const int bv = fmt->v_bits;
-  const int nk = mk > 0 ? 1 << mk : 0, nv = bv > 0 ? 1 << bv : 0;
   if (stages & kStagePrepare) {
-    const dim3 qgrid(5, cache->n_layers);
+    const dim3 qgrid = qprep_grid(cache->n_layers, batch, n_q_heads);
     if (fmt->k_bits > 0)
       hipLaunchKernelGGL(qprep_kernel<true>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qprep, batch,
-                         cache->n_kv_heads, n_q_heads, done, nullptr, tables->k_centroids, nk, tables->v_centroids,
-                         nv);
+                         cache->n_kv_heads, n_q_heads, done, nullptr);
     else
       hipLaunchKernelGGL(qprep_kernel<false>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qprep, batch,
-                         cache->n_kv_heads, n_q_heads, done, nullptr, tables->k_centroids, nk, tables->v_centroids,
-                         nv);
+                         cache->n_kv_heads, n_q_heads, done, nullptr);
     if ((st = launch_status("qprep"))) return st;
   }
   if (max_seq_len == 0 && SCORE) return TQ_OK;
 
   DecodeArgs a = make_args(fmt, tables, cache, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, plan,
                            qprep, partial, out);
-  a.alpha = reinterpret_cast<const float*>(done + plan.problems + cache->n_layers);
   a.red_g = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.red_offset);
   if (!SCORE && (stages & kStageMerge)) {
     a.done = done;
@@ -2797,6 +2722,9 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
     a.app_lo = app->lo;
     a.app_hi = app->hi;
     a.app_done = done + plan.problems;
+    a.app_polls = g_append_wait_polls;
+    a.app_extra = g_append_wait_extra;
+    a.app_flag = done + plan.problems + cache->n_layers;
   }
   if (int64_t(a.n_app) + plan.n_workgroups > 0x7FFFFFFF) return fail(TQ_ERR_INVALID_ARG, "too many workgroups");
   const dim3 grid(unsigned(a.n_app + plan.n_workgroups));
@@ -2850,6 +2778,8 @@ tq_status decode_tail(const tq_format* fmt, const tq_tables* tables, const tq_ca
                 n_q_heads, cache->n_kv_heads);
   if (max_seq_len < 0 || max_tail_len < 0) return fail(TQ_ERR_INVALID_ARG, "max_seq_len or max_tail_len < 0");
   if (int64_t(cache->n_layers) * batch > 65535) return fail(TQ_ERR_INVALID_ARG, "n_layers * batch exceeds 65535");
+  if ((int64_t(batch) * n_q_heads + kQprepRows - 1) / kQprepRows > 65535)
+    return fail(TQ_ERR_INVALID_ARG, "batch * n_q_heads exceeds %d", 65535 * kQprepRows);
   const TailPlan tp =
       plan_decode_tail(fmt->d, cache->n_layers, batch, cache->n_kv_heads, n_q_heads, max_seq_len, max_tail_len);
   if (tp.packed.problems * tp.packed.chunks_per_problem > (int64_t(1) << 30) ||
@@ -2867,23 +2797,19 @@ tq_status decode_tail(const tq_format* fmt, const tq_tables* tables, const tq_ca
   const int bv = fmt->v_bits;
   // One query preparation for both parts (rotated and plain; the plain copy
   // alone for fp16 keys), which also zeroes the merge counts.
-  const dim3 qgrid(5, cache->n_layers);
-  const int nk = mk > 0 ? 1 << mk : 0, nv = bv > 0 ? 1 << bv : 0;
+  const dim3 qgrid = qprep_grid(cache->n_layers, batch, n_q_heads);
   if (fmt->k_bits > 0)
     hipLaunchKernelGGL(qprep_kernel<true>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qrot, batch,
-                       cache->n_kv_heads, n_q_heads, done, qplain, tables->k_centroids, nk, tables->v_centroids, nv);
+                       cache->n_kv_heads, n_q_heads, done, qplain);
   else
     hipLaunchKernelGGL(qprep_kernel<false>, qgrid, dim3(256), 0, hs, q, tables->pi, tables->s, qrot, batch,
-                       cache->n_kv_heads, n_q_heads, done, nullptr, tables->k_centroids, nk, tables->v_centroids,
-                       nv);
+                       cache->n_kv_heads, n_q_heads, done, nullptr);
   if ((st = launch_status("qprep"))) return st;
   // The tail first (partials only), then the packed part, whose last
   // workgroup per problem merges both piece sets into out.
-  const float* alpha = reinterpret_cast<const float*>(done + tp.packed.problems + cache->n_layers);
   float* red_g = reinterpret_cast<float*>(ws + tp.red_offset);
   DecodeArgs at = make_args(&f16, tables, tail, batch, n_q_heads, tail_start, tail_len, max_tail_len, scale,
                             tp.tail, fmt->k_bits > 0 ? qplain : qrot, partial, nullptr);
-  at.alpha = alpha;
   at.red_g = red_g;
   at.seg_max = int(tp.seg_total);
   at.seg_base = int(tp.packed.seg_max);
@@ -2891,7 +2817,6 @@ tq_status decode_tail(const tq_format* fmt, const tq_tables* tables, const tq_ca
   DecodeArgs ap = make_args(fmt, tables, cache, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, tp.packed,
                             qrot, partial, nullptr);
   ap.seg_max = int(tp.seg_total);
-  ap.alpha = alpha;
   ap.red_g = red_g;
   ap.done = done;
   ap.out = out;
@@ -3148,12 +3073,13 @@ tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const
   }
   const int64_t groups = (n_tokens * a.H + kAppendItems - 1) / kAppendItems;
   const int64_t n_append = groups * n_layers;
-  const int64_t n_prep = int64_t(4) * cache->n_layers + 1;   // (quarter, layer) preparation blocks + the scales
+  // (quarter, layer, run) preparation blocks
+  const int64_t n_prep = int64_t(4) * cache->n_layers * ((int64_t(batch) * n_q_heads + kQprepRows - 1) / kQprepRows);
   if (n_append + n_prep > 0x7FFFFFFF) return fail(TQ_ERR_INVALID_ARG, "too many workgroups");
   hipStream_t hs = static_cast<hipStream_t>(stream);
   float* qprep = static_cast<float*>(workspace);
   const SplitPlan plan = plan_decode(fmt->d, cache->n_layers, batch, cache->n_kv_heads, n_q_heads, max_seq_len);
-  uint32_t* done = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + plan.qprep_bytes + plan.partial_bytes);
+  uint32_t* done = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + plan.counter_offset);
   const dim3 grid(unsigned(n_append + n_prep));
 #define TQ_AP(MK_, BV_)                                                                                          \
   if (a.mk == MK_ && a.bv == BV_) {                                                                              \
@@ -3186,15 +3112,27 @@ tq_status tq_decode_step(const tq_format* fmt, const tq_tables* tables, const tq
   if ((st = compress_setup(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0, 0, app.ca, wgs,
                            nothing)))
     return st;
-  if (nothing || n_tokens >= kCompressTile) {
-    // Bulk (or no) compression first, then the decode.
-    if (!nothing && (st = tq_compress_kv(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0,
-                                         stream)))
+  if (nothing)
+    return tq_decode_attention(fmt, tables, cache, q, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, out,
+                               workspace, workspace_bytes, stream);
+  const int64_t groups = (n_tokens * app.ca.H + kAppendItems - 1) / kAppendItems;
+  if (groups * n_layers > kMaxFusedAppend) {
+    // Many append workgroups would take too many of the decode's CUs: the
+    // append runs before the decode, in the query preparation's launch (few
+    // tokens) or as the bulk compression (16 or more).
+    if (n_tokens < kCompressTile) {
+      if ((st = tq_append_prepare(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0, q,
+                                  batch, n_q_heads, max_seq_len, workspace, workspace_bytes, stream)))
+        return st;
+      return tq_decode_attend(fmt, tables, cache, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, out,
+                              workspace, workspace_bytes, stream);
+    }
+    if ((st = tq_compress_kv(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0, stream)))
       return st;
     return tq_decode_attention(fmt, tables, cache, q, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, out,
                                workspace, workspace_bytes, stream);
   }
-  app.groups = int((n_tokens * app.ca.H + kAppendItems - 1) / kAppendItems);
+  app.groups = int(groups);
   app.layers = n_layers;
   // Slots the append may write: known on the host for consecutive slots,
   // otherwise any slot of the plane.
@@ -3202,6 +3140,40 @@ tq_status tq_decode_step(const tq_format* fmt, const tq_tables* tables, const tq
   app.hi = slots ? cache->capacity : slot0 + n_tokens;
   return decode_common<false>(fmt, tables, cache, q, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, out,
                               workspace, workspace_bytes, stream, kStageAll, &app);
+}
+
+tq_status tq_decode_step_check(const tq_format* fmt, int32_t n_layers, int32_t batch, int32_t n_kv_heads,
+                               int32_t n_q_heads, int64_t max_seq_len, const void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  using namespace tq;
+  clear_error();
+  tq_status st = check_format(fmt, false);
+  if (st) return st;
+  if (n_layers <= 0 || batch <= 0 || n_kv_heads <= 0 || n_q_heads <= 0 || n_q_heads % n_kv_heads || max_seq_len < 0)
+    return fail(TQ_ERR_INVALID_ARG, "sizes");
+  const SplitPlan plan = plan_decode(fmt->d, n_layers, batch, n_kv_heads, n_q_heads, max_seq_len);
+  if (!workspace || workspace_bytes < plan.total_bytes)
+    return fail(TQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, plan.total_bytes);
+  const hipError_t se = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (se != hipSuccess) return fail(TQ_ERR_HIP, "stream synchronize: %s", hipGetErrorString(se));
+  uint32_t flag = 0;
+  const char* p = static_cast<const char*>(workspace) + plan.counter_offset +
+                  (size_t(plan.problems) + size_t(n_layers)) * sizeof(uint32_t);
+  const hipError_t ce = hipMemcpy(&flag, p, sizeof(flag), hipMemcpyDeviceToHost);
+  if (ce != hipSuccess) return fail(TQ_ERR_HIP, "reading the step flag: %s", hipGetErrorString(ce));
+  if (flag != 0)
+    return fail(TQ_ERR_APPEND_TIMEOUT, "a decode wave stopped waiting for the step's append and read chunks that "
+                                       "may not hold the new tokens");
+  return TQ_OK;
+}
+
+tq_status tq_set_append_wait(uint32_t max_polls, int32_t extra_groups) {
+  tq::clear_error();
+  if (max_polls == 0 || extra_groups < 0) return tq::fail(TQ_ERR_INVALID_ARG, "max_polls=%u extra_groups=%d",
+                                                          max_polls, extra_groups);
+  tq::g_append_wait_polls = max_polls;
+  tq::g_append_wait_extra = extra_groups;
+  return TQ_OK;
 }
 
 tq_status tq_decode_attention_tail(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,

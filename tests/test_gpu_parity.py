@@ -466,7 +466,9 @@ def test_decode_steps_append_prepare_attend(k_bits, v_bits, hq, lens):
     ("slot0", 2, 2, 12, (5,), 3, 0),
     ("slot0", 0, 4, 16, (100,), 2, 1),
     ("slots", 8, 4, 28, (300, 45, 0, 129), 1, 0),
-    ("slot0", 4, 4, 28, (100,), 20, 0),   # 16 or more tokens: bulk compression, then the decode
+    ("slot0", 4, 4, 28, (100,), 20, 0),   # 20 tokens: 10 append workgroups per layer, inside the decode launch
+    ("slots", 4, 4, 16, (60, 33, 1, 0, 7, 300, 95, 64, 2, 18, 250, 77, 3, 40, 121, 9), 1, 0),   # 16 sequences
+    ("slot0", 3, 2, 8, (100,), 40, 0),    # 40 appended workgroups: bulk compression, then the decode
 ])
 def test_decode_step_append_inside_decode_launch(mode, k_bits, v_bits, hq, lens, n_new, layer0):
     """tq_decode_step: the new tokens are compressed by the decode launch's
@@ -527,6 +529,48 @@ def test_decode_step_append_inside_decode_launch(mode, k_bits, v_bits, hq, lens,
             ref = attention.decode_attention(ora[layer], qn[layer], starts, cur, pi, s, cbk, cbv)
             worst = max(worst, pu.check_outputs(o[layer], ref))
     _say("worst out abs", f"{worst:.2e}")
+
+
+def test_decode_step_append_wait_give_up_is_reported():
+    """The decode waves' wait for the step's append is bounded; when it ends
+    unmet the wave records it and tq_decode_step_check reports it.  The host
+    makes the wait unmeetable (test hook: more append workgroups waited for
+    than launched, 16 polls), so the waves give up and every kernel still
+    exits normally; the flag is set for that call, and the next call (normal
+    wait) clears it and matches the oracle."""
+    import kv_cache_quantization_norm_amd as tq
+    _say("append wait give-up")
+    L, H, HQ, T = 2, 4, 16, 300
+    fmt = quant.Format(128, 4, 4)
+    tfmt = pu.tq_format(fmt)
+    tables = tq.Tables.create(tfmt, list(range(L)))
+    g = torch.Generator().manual_seed(47)
+    dev = tq.Cache.allocate(tfmt, L, H, 320)
+    k = torch.randn(L, T, H, 128, generator=g).to("cuda", torch.bfloat16)
+    v = torch.randn(L, T, H, 128, generator=g).to("cuda", torch.bfloat16)
+    tq.tq_compress_kv(tfmt, tables, dev, k[:, :T - 1].contiguous(), v[:, :T - 1].contiguous(), slot0=0)
+    Q = torch.randn(L, 1, HQ, 128, generator=g).cuda()
+    st = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ln = torch.full((1,), T, dtype=torch.int32, device="cuda")
+    ws = tq.workspace_for(tfmt, dev, 1, HQ, T)
+    out = torch.empty(L, 1, HQ, 128, device="cuda")
+    kn, vn = k[:, T - 1:].contiguous(), v[:, T - 1:].contiguous()
+    try:
+        tq.tq_set_append_wait(16, 1000)
+        tq.tq_decode_step(tfmt, tables, dev, kn, vn, Q, st, ln, T, out, ws, slot0=T - 1)
+        with pytest.raises(tq.TQError) as e:
+            tq.tq_decode_step_check(tfmt, dev, 1, HQ, T, ws)
+        assert e.value.status == tq.TQ_ERR_APPEND_TIMEOUT
+    finally:
+        tq.tq_set_append_wait()
+    tq.tq_decode_step(tfmt, tables, dev, kn, vn, Q, st, ln, T, out, ws, slot0=T - 1)
+    tq.tq_decode_step_check(tfmt, dev, 1, HQ, T, ws)
+    o = out.cpu().numpy()
+    ora = pu.download_cache(dev, fmt)
+    for layer in range(L):
+        pi, s, cbk, cbv = pu.oracle_tables(fmt, layer)
+        ref = attention.decode_attention(ora[layer], Q[layer].cpu().numpy(), [0], [T], pi, s, cbk, cbv)
+        pu.check_outputs(o[layer], ref)
 
 
 def test_serving_loop_with_fp16_tail_and_trigger():

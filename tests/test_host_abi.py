@@ -159,3 +159,41 @@ def test_device_calls_validate_before_launch():
     # host generators
     assert r("tq_make_rotations", 2, 1, FAKE, FAKE, None) == tq.TQ_ERR_INVALID_ARG
     assert r("tq_make_codebook", 128, 9, FAKE, FAKE) == tq.TQ_ERR_INVALID_ARG
+
+
+def test_binding_checks_tensor_arguments_before_the_call():
+    """The Python binding refuses host tensors, numpy arrays, wrong dtypes and
+    wrong shapes before anything reaches the C library (which takes raw device
+    pointers)."""
+    import torch
+    fmt = tq.make_format(128, 4, 4)
+    cache = tq.Cache(fmt, 2, 4, 64, {n: None for n in tq.PLANES})
+    q = torch.zeros(2, 1, 8, 128)
+    with pytest.raises(ValueError, match="device"):
+        tq.tq_decode_attention(fmt, None, cache, q, None, None, 64, None, None)
+    with pytest.raises(TypeError, match="torch.Tensor"):
+        tq.tq_decode_attention(fmt, None, cache, q.numpy(), None, None, 64, None, None)
+    with pytest.raises(ValueError, match="device"):
+        tq.tq_compress_kv(fmt, None, cache, torch.zeros(1, 3, 4, 128), torch.zeros(1, 3, 4, 128))
+    with pytest.raises(ValueError, match="4-d"):
+        tq.tq_compress_kv(fmt, None, cache, torch.zeros(3, 4, 128), torch.zeros(3, 4, 128))
+    with pytest.raises(TypeError, match="numpy"):
+        tq._ptr(np.zeros(4))
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 7])
+def test_fp16_operand_scale_matches_the_search_definition(bits):
+    """The library's operand scale (host) is as good as the direct search of
+    its definition (written in the decode precision test) on the fp32 table
+    codebooks: same largest relative rounding error over the magnitudes."""
+    from tests.test_decode_precision import fp16_scale
+    c, _ = codebook.table_codebook(128, bits)
+    alpha = tq.tq_fp16_operand_scale(c.astype(np.float32))
+    assert 1.0 <= alpha < 2.0
+    m = np.unique(np.abs(c.astype(np.float32)).astype(np.float64))
+    v = np.float32(alpha) * m
+    err = np.max(np.abs(v.astype(np.float16).astype(np.float64) - v) / v)
+    _, best = fp16_scale(c)
+    # (alpha is returned in fp32: its rounding adds up to about 2^-23 of each value)
+    assert err <= best + 2.0 ** -22
+    assert tq.tq_fp16_operand_scale(np.zeros(4, np.float32)) == 1.0
