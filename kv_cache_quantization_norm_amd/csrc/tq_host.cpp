@@ -75,12 +75,18 @@ SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_he
   p.n_workgroups = (p.problems * p.chunks_per_problem + p.chunks_per_wg - 1) / p.chunks_per_wg;
   // A problem of C chunks overlaps at most ceil((C - 1) / W) + 1 ranges of W.
   p.seg_max = (p.chunks_per_problem - 1 + p.chunks_per_wg - 1) / p.chunks_per_wg + 1;
+  // Ragged split: ranges of at least half the balanced length (so a batch
+  // whose sequences fill at least half of max_len is split evenly).
+  p.cpp_real = cpp;
+  p.cpw_min = cpw_b / 2 > 1 ? cpw_b / 2 : 1;
+  const int64_t seg_r = batch > 1 ? (cpp + kCrossingChunks - 1 + p.cpw_min - 1) / p.cpw_min + 1 : 0;
+  p.seg_cap = seg_r > p.seg_max ? seg_r : p.seg_max;
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   p.qprep_bytes = align(size_t(n_layers) * batch * n_q_heads * 2 * d * sizeof(float));
   p.counter_offset = p.qprep_bytes;
   p.counter_bytes = align(size_t(p.problems + n_layers + 1) * sizeof(uint32_t));
   p.partial_offset = p.counter_offset + p.counter_bytes;
-  p.partial_bytes = align(size_t(n_layers) * batch * n_q_heads * p.seg_max * (d + 2) * sizeof(float));
+  p.partial_bytes = align(size_t(n_layers) * batch * n_q_heads * p.seg_cap * (d + 2) * sizeof(float));
   p.red_offset = p.partial_offset + p.partial_bytes;
   p.red_bytes = align(size_t(p.n_workgroups) * kDecodeWaves * kMaxGroup * d * sizeof(float));
   p.total_bytes = p.red_offset + p.red_bytes;
@@ -92,7 +98,7 @@ TailPlan plan_decode_tail(int d, int n_layers, int batch, int n_kv_heads, int n_
   TailPlan t;
   t.packed = plan_decode(d, n_layers, batch, n_kv_heads, n_q_heads, max_seq_len);
   t.tail = plan_decode(d, n_layers, batch, n_kv_heads, n_q_heads, max_tail_len);
-  t.seg_total = t.packed.seg_max + t.tail.seg_max;
+  t.seg_total = t.packed.seg_cap + t.tail.seg_cap;
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   t.qplain_offset = t.packed.qprep_bytes;
   t.partial_offset = 2 * t.packed.qprep_bytes;

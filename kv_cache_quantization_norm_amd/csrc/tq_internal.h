@@ -18,6 +18,7 @@ constexpr int kDecodeWaves = 8;  // waves per decode workgroup (one workgroup pe
 constexpr int kDecodeWorkgroups = 256;   // decode workgroups: one per CU of an MI355X
 constexpr int kMaxGroup = 8;     // query heads handled by one decode wave
 constexpr int kCrossingChunks = 16;   // measured cost of a problem change inside a decode workgroup, in chunks
+constexpr int kRaggedMaxBatch = 1024;  // largest batch whose decode may take the ragged split (its prefix sits in LDS)
 
 // Format checks shared by all entry points.  `device` additionally requires
 // d == 128 and the bit widths the kernels implement.
@@ -39,12 +40,21 @@ struct SplitPlan {
   int64_t n_workgroups = 0;
   int64_t seg_max = 0;
   int n_head_groups = 0;
+  // Ragged split (decided by the kernel from the sequence lengths, batch > 1):
+  // the workgroups share the chunks that hold tokens (each problem followed
+  // by kCrossingChunks of padding), in ranges of at least cpw_min chunks, so
+  // that a problem (at most cpp_real = ceil(max_len / 32) chunks plus the
+  // padding) leaves at most seg_cap pieces; seg_cap >= seg_max is the partial
+  // slots per query head in the workspace.
+  int64_t cpp_real = 0;
+  int64_t cpw_min = 0;
+  int64_t seg_cap = 0;
   // Workspace layout, in this order; the counters sit right after the
   // prepared queries, at an offset that does not depend on the work split.
   size_t qprep_bytes = 0;     // [L][B][Hq][2][d] fp32, at offset 0
   size_t counter_offset = 0;  // uint32 [problems] pieces written (in-kernel merge), then [n_layers] append
   size_t counter_bytes = 0;   // counts, then the append wait's give-up flag
-  size_t partial_offset = 0;  // [L][B][Hq][seg_max][d + 2] fp32
+  size_t partial_offset = 0;  // [L][B][Hq][seg_cap][d + 2] fp32
   size_t partial_bytes = 0;
   size_t red_offset = 0;      // fp32 [n_workgroups][waves][kMaxGroup][d]: the wave merge of a decode workgroup
   size_t red_bytes = 0;       // (kept in LDS when the tables leave room for it)
@@ -58,8 +68,8 @@ SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_he
 // Decode over a packed cache plus an fp16 tail: each part has its own split;
 // the workspace holds the prepared queries twice (for the packed part, then
 // plain for the tail), the partials of both parts, the tail's pieces in the
-// slots after the packed part's: [L][B][Hq][packed.seg_max +
-// tail.seg_max][d + 2] fp32, and the packed part's merge counters.
+// slots after the packed part's: [L][B][Hq][packed.seg_cap +
+// tail.seg_cap][d + 2] fp32, and the packed part's merge counters.
 struct TailPlan {
   SplitPlan packed, tail;
   size_t qplain_offset = 0, partial_offset = 0, counter_offset = 0, red_offset = 0, total_bytes = 0;

@@ -49,6 +49,7 @@ constexpr bool key_split(int mk) { return mk >= 3; }
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ half8 as_half8(u32x4 w) {
@@ -75,6 +76,28 @@ template <typename T>
 __device__ __forceinline__ const T* uniform_ptr(const T* p) {
   __asm__ volatile("" : "+s"(p));
   return p;
+}
+// Chunk loads go through buffer resources: the chunk's base address and
+// extent in scalar registers, a 32-bit byte offset per lane, so that no lane
+// holds a 64-bit address; loads past `bytes` return zero.  (Loads through a
+// generic pointer would be flat loads, which also count on the LDS counter:
+// every wait for an LDS read would then wait for the chunk loads in flight.)
+// 0x00020000: the resource word 3 of an untyped 32-bit buffer.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(bytes), 0x00020000);
+}
+template <typename T>
+__device__ __forceinline__ T bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0));
+  } else if constexpr (sizeof(T) == 8) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, int(off), 0, 0));
+  } else if constexpr (__is_same(T, u32x3)) {
+    return __builtin_amdgcn_raw_buffer_load_b96(r, int(off), 0, 0);
+  } else {
+    static_assert(sizeof(T) == 16, "buffer load width");
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0));
+  }
 }
 
 template <int CTRL>
@@ -922,7 +945,12 @@ struct DecodeArgs {
   int chunks_per_problem;   // 32-token chunks per problem (from max_len)
   int chunks_per_wg;        // chunks of every workgroup but the last
   int total_chunks;         // problems x chunks_per_problem
-  int seg_max;              // partial slots per query head
+  int seg_max;              // partial slots per query head (the row stride of `partial`)
+  // Ragged split (ragged != 0, in-kernel merge only): when the sequences'
+  // chunks that hold tokens are fewer than problems x cpp_real, the decode
+  // workgroups share those chunks instead, in equal ranges of at least
+  // cpw_min (the ranges then never reach the chunks past a sequence's end).
+  int ragged, cpp_real, cpw_min;
   int seg_base;             // first slot of this call's pieces
   const uint8_t* k_idx;
   const uint8_t* k_sign;
@@ -1247,7 +1275,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   constexpr int OFF_V = VREP ? ((OFF_PHI + KP * 4 + 255) / 256) * 256 : S_END;
   constexpr int V_PAGE = VREP && OFF_V >= 65536 ? 1 : 0;
   constexpr int OFF_TAB_END = VREP ? ((OFF_V + VW * 4 + 15) / 16) * 16 : ((OFF_PHI + KP * 4 + 15) / 16) * 16;
-  constexpr int MISC_BYTES = kDecodeWaves * 128 * 4 + 2 * kDecodeWaves * 16 * 4 + 2 * 2 * 4 * 64 * 16 + 16;
+  constexpr int LIVE_BYTES = (kRaggedMaxBatch + 1) * 4;
+  constexpr int MISC_BYTES = kDecodeWaves * 128 * 4 + 2 * kDecodeWaves * 16 * 4 + 2 * 2 * 4 * 64 * 16 + 16 + LIVE_BYTES;
   constexpr int RED_FULL = kDecodeWaves * kMaxGroup * D * 4;
   // The wave merge ([wave][head][coordinate] fp32) stays in LDS when the
   // tables leave room for it, else it goes through the workgroup's slice of
@@ -1260,7 +1289,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   constexpr int OFF_LW = OFF_MW + kDecodeWaves * 16 * 4;
   constexpr int OFF_Q = OFF_LW + kDecodeWaves * 16 * 4;    // staged query operands [piece][r / z][s][lane]
   constexpr int OFF_CNT = OFF_Q + 2 * 2 * 4 * 64 * 16;
-  constexpr int LDS_BYTES = OFF_CNT + 16;
+  constexpr int OFF_LIVE = OFF_CNT + 16;   // ragged split: prefix of the sequences' live chunk counts
+  constexpr int LDS_BYTES = OFF_LIVE + LIVE_BYTES;
   static_assert(OFF_K < 65536, "the key table must start below 64 KB");
   static_assert(VREP ? OFF_V - V_PAGE * 65536 < 65536 : OFF_V < 65536, "value table offset");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
@@ -1276,6 +1306,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   float(*const mw)[16] = reinterpret_cast<float(*)[16]>(dsm + OFF_MW);
   float(*const lw)[16] = reinterpret_cast<float(*)[16]>(dsm + OFF_LW);
   uint32_t* const counter = reinterpret_cast<uint32_t*>(dsm + OFF_CNT);
+  int* const live_s = reinterpret_cast<int*>(dsm + OFF_LIVE);
   half8* const qstage = reinterpret_cast<half8*>(dsm + OFF_Q);
   // the in-kernel merge's result area ([16][D] heads, [16][D] the tail's part)
   float* const fin = RED_LDS ? red : reinterpret_cast<float*>(dsm + OFF_Q);
@@ -1327,6 +1358,50 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   const int cpp = a.chunks_per_problem;
   const int64_t vblocks = a.capacity / kVBlock;
 
+  // ---- the chunk sequence dealt to the workgroups in ranges of cpw: every
+  // problem's cpp chunks, problem-major; or (rag) only the chunks that hold
+  // tokens, each problem followed by kCrossingChunks chunks of padding (never
+  // dealt: they stand for the cost of a problem change in a workgroup):
+  // problem p = ((layer * batch + b) * H + hk) * n_hg + hg has n(b) = live(b)
+  // + padding chunks (0 for an empty sequence) from P(p) = layer * HG * S(B) +
+  // HG * S(b) + (hk * n_hg + hg) * n(b), with HG = H * n_hg and S the prefix
+  // of n (in LDS).
+  // (All of it is uniform over the workgroup; values read from LDS are made
+  // scalar with readfirstlane, so that the loops over chunks stay scalar.)
+  bool rag = false;
+  int cpw = a.chunks_per_wg, total = a.total_chunks;
+  const int HG = a.H * a.n_hg;
+  auto lds_s = [&](int b) -> int { return __builtin_amdgcn_readfirstlane(live_s[b]); };
+  auto pcount = [&](int p) -> int {
+    if (!rag) return cpp;
+    const int b = (p / HG) % a.batch;
+    return lds_s(b + 1) - lds_s(b);
+  };
+  auto pfirst = [&](int p) -> int {
+    if (!rag) return p * cpp;
+    const int lb = p / HG, b = lb % a.batch, layer = lb / a.batch;
+    const int s0 = lds_s(b);
+    return layer * HG * lds_s(a.batch) + HG * s0 + (p - lb * HG) * (lds_s(b + 1) - s0);
+  };
+  // the problem holding chunk c (c < total)
+  auto prob_of = [&](int c) -> int {
+    if (!rag) return c / cpp;
+    const int per_layer = HG * lds_s(a.batch);
+    const int layer = c / per_layer, r = c - layer * per_layer;
+    int lo = 0, hi = a.batch;   // HG S(lo) <= r < HG S(hi): the last such lo has chunks
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (HG * lds_s(mid) <= r) lo = mid; else hi = mid;
+    }
+    const int s0 = lds_s(lo);
+    return (layer * a.batch + lo) * HG + (r - HG * s0) / (lds_s(lo + 1) - s0);
+  };
+  // pieces (workgroup ranges) that meet problem p
+  auto pieces_of = [&](int p) -> int {
+    const int f = pfirst(p), n = pcount(p);
+    return n > 0 ? (f + n - 1) / cpw - f / cpw + 1 : 0;
+  };
+
   // ---- problem context: problem = ((layer * batch + b) * H + hk) * n_hg + hg
   struct Run {
     int64_t slot_base;   // slot of token 0 of the sequence in its (layer, KV head) plane
@@ -1345,13 +1420,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   };
   // A sequence with an invalid start gets no tokens and slot 0 as its start,
   // so that the chunk-0 loads issued for waves without work stay in bounds.
-  auto fill_run = [&](Run r, int64_t start, int64_t len) {
+  auto clamp_run = [&](int64_t& start, int64_t& len) {
     if (start < 0 || (start % kVBlock) != 0 || start >= a.capacity || len < 0) {
       len = 0;
       start = 0;
     }
     if (len > a.capacity - start) len = a.capacity - start;
     if (len > a.max_len) len = a.max_len;   // tokens past max_seq_len are ignored
+  };
+  auto fill_run = [&](Run r, int64_t start, int64_t len) {
+    clamp_run(start, len);
     const int64_t plane = int64_t(r.layer) * a.H + r.hk;
     r.slot_base = plane * a.capacity + start;
     r.vblk0 = plane * vblocks + start / kVBlock;
@@ -1366,7 +1444,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   struct Group {
     Run ra, rb;
     int64_t sa, sb, va, vb;   // ticket u's first slot: (u < live_a ? sa : sb) + 32 u; value block likewise + u
-    int pa, a_end, b_end, rel_a0, live_a, n_tickets;
+    int pa, pb, a_end, b_end, rel_a0, live_a, n_tickets;   // pb: piece B's problem (pa without a piece B)
     int xa0, xa1, xb0, xb1;   // tickets [xa0, xa1) (piece A), [xb0, xb1) (B) whose chunks may hold appended slots
     bool has_b;
   };
@@ -1387,13 +1465,15 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   };
   auto group_of = [&](int g0, int c_last) {
     Group G;
-    G.pa = g0 / cpp;
-    G.a_end = (G.pa + 1) * cpp < c_last ? (G.pa + 1) * cpp : c_last;
+    G.pa = prob_of(g0);
+    const int fa = pfirst(G.pa);
+    G.a_end = fa + pcount(G.pa) < c_last ? fa + pcount(G.pa) : c_last;
     G.has_b = G.a_end < c_last;
-    G.b_end = G.has_b ? (G.a_end + cpp < c_last ? G.a_end + cpp : c_last) : G.a_end;
-    G.rel_a0 = g0 - G.pa * cpp;
+    G.pb = G.has_b ? prob_of(G.a_end) : G.pa;
+    G.b_end = G.has_b ? (G.a_end + pcount(G.pb) < c_last ? G.a_end + pcount(G.pb) : c_last) : G.a_end;
+    G.rel_a0 = g0 - fa;
     // both sequences' (start, length) are loaded together
-    const Run ca = ctx_of(G.pa), cb = ctx_of(G.has_b ? G.pa + 1 : G.pa);
+    const Run ca = ctx_of(G.pa), cb = ctx_of(G.pb);
     const int64_t sa = a.seq_start[ca.b], sb = a.seq_start[cb.b];
     const int64_t la = a.seq_len[ca.b], lb = a.seq_len[cb.b];
     G.ra = fill_run(ca, sa, la);
@@ -1457,13 +1537,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   struct QItem {
     float v[2][8];
   };
-  // pa: problem of piece A; piece B is problem pa + 1 when has_b (else A again).
-  auto stage_load = [&](int pa, bool has_b, QItem& Q) {
+  // pa, pb: problems of pieces A and B (pb = pa without a piece B).
+  auto stage_load = [&](int pa, int pb, QItem& Q) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int it = tid + NT * u;
       const int piece = it >> 9, kind = (it >> 8) & 1, s4 = (it >> 6) & 3, l = it & 63;
-      const Run Rp = ctx_of(pa + (piece && has_b ? 1 : 0));
+      const Run Rp = ctx_of(piece ? pb : pa);
       const int g_local = Rp.hg * kMaxGroup + (l & 7);
       const int hh = Rp.hk * a.G + (g_local < a.G ? g_local : 0);
       const float4* src = reinterpret_cast<const float4*>(
@@ -1473,12 +1553,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       Q.v[u][4] = x1.x; Q.v[u][5] = x1.y; Q.v[u][6] = x1.z; Q.v[u][7] = x1.w;
     }
   };
-  auto stage_store = [&](int pa, bool has_b, const QItem& Q) {
+  auto stage_store = [&](int pa, int pb, const QItem& Q) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int it = tid + NT * u;
       const int piece = it >> 9, kind = (it >> 8) & 1, l = it & 63;
-      const Run Rp = ctx_of(pa + (piece && has_b ? 1 : 0));
+      const Run Rp = ctx_of(piece ? pb : pa);
       const bool ok = Rp.hg * kMaxGroup + (l & 7) < a.G;
       const float sc = ok ? (kind ? kscale_r : kscale_k) : 0.f;
       const bool lo = (l & 15) >= 8;
@@ -1533,7 +1613,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   };
   struct VData {
     uint32_t vw[8];
-    float nrm[2];
+    float nrm[3];   // key norm, residual norm, value norm of the lane's token
     half8 vf[BV > 0 ? 1 : 8];
   };
   uint32_t koff[2], soff[2];
@@ -1549,53 +1629,56 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   // slot0: the chunk's first slot in its (layer, KV head) plane; vblk: its value block.
   auto load_k = [&](int64_t slot0, KData& K) {
     if constexpr (MK == 0) {
-      const unsigned char* kp = uniform_ptr(reinterpret_cast<const unsigned char*>(a.k_f16 + slot0 * D));
+      const auto kr = chunk_rsrc(a.k_f16 + slot0 * D, kChunk * 2 * D);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         const uint32_t off = (8 * (col >> 2) + 4 * T + (col & 3)) * (2 * D) + 64 * q;
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) K.kf[T][s2] = *reinterpret_cast<const half8*>(kp + off + 16 * s2);
+        for (int s2 = 0; s2 < 4; ++s2) K.kf[T][s2] = bload<half8>(kr, off + 16 * s2);
       }
     }
     if constexpr (MK > 0) {
-      const uint8_t* kp = uniform_ptr(a.k_idx + slot0 * KREC);
-      const uint8_t* sp = uniform_ptr(a.k_sign + slot0 * 16);
+      const auto kr = chunk_rsrc(a.k_idx + slot0 * KREC, kChunk * KREC);
+      const auto sr = chunk_rsrc(a.k_sign + slot0 * 16, kChunk * 16);
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
         if constexpr (MK == 4) {
-          const u32x4 v4 = *reinterpret_cast<const u32x4*>(kp + koff[T]);
+          const u32x4 v4 = bload<u32x4>(kr, koff[T]);
 #pragma unroll
           for (int u = 0; u < 4; ++u) K.kw[T][u] = v4[u];
+        } else if constexpr (MK == 3) {
+          const u32x3 v3 = bload<u32x3>(kr, koff[T]);
+#pragma unroll
+          for (int u = 0; u < 3; ++u) K.kw[T][u] = v3[u];
         } else if constexpr (MK == 2) {
-          const u32x2 v2 = *reinterpret_cast<const u32x2*>(kp + koff[T]);
+          const u32x2 v2 = bload<u32x2>(kr, koff[T]);
           K.kw[T][0] = v2[0];
           K.kw[T][1] = v2[1];
         } else {
 #pragma unroll
-          for (int u = 0; u < MK; ++u) K.kw[T][u] = *reinterpret_cast<const uint32_t*>(kp + koff[T] + 4 * u);
+          for (int u = 0; u < MK; ++u) K.kw[T][u] = bload<uint32_t>(kr, koff[T] + 4 * u);
         }
-        K.sg[T] = *reinterpret_cast<const uint32_t*>(sp + soff[T]);
+        K.sg[T] = bload<uint32_t>(sr, soff[T]);
       }
     }
   };
   auto load_v = [&](int64_t slot0, int64_t vblk, VData& V) {
     if constexpr (MK > 0) {
-      const float nk = *reinterpret_cast<const float*>(uniform_ptr(reinterpret_cast<const uint8_t*>(a.k_norm + slot0)) + noff);
-      const float nr = *reinterpret_cast<const float*>(uniform_ptr(reinterpret_cast<const uint8_t*>(a.k_rnorm + slot0)) + noff);
-      V.nrm[0] = col < 8 ? nk : nr;
+      // both norms, selected where they are used: work on loaded data placed
+      // here would make the compiler wait for these loads at once
+      V.nrm[0] = bload<float>(chunk_rsrc(a.k_norm + slot0, kChunk * 4), noff);
+      V.nrm[2] = bload<float>(chunk_rsrc(a.k_rnorm + slot0, kChunk * 4), noff);
     }
     if constexpr (BV == 0) {
-      const unsigned char* vp = uniform_ptr(reinterpret_cast<const unsigned char*>(a.v_f16 + vblk * D * kVBlock));
+      const auto vr = chunk_rsrc(a.v_f16 + vblk * D * kVBlock, D * kVBlock * 2);
 #pragma unroll
-      for (int vb = 0; vb < 8; ++vb)
-        V.vf[vb] = *reinterpret_cast<const half8*>(vp + (16 * vb + col) * (2 * kVBlock) + 16 * q);
+      for (int vb = 0; vb < 8; ++vb) V.vf[vb] = bload<half8>(vr, (16 * vb + col) * (2 * kVBlock) + 16 * q);
     }
     if constexpr (BV > 0) {
-      V.nrm[1] = *reinterpret_cast<const float*>(uniform_ptr(reinterpret_cast<const uint8_t*>(a.v_norm + slot0)) + noff);
-      const uint8_t* vp = uniform_ptr(a.v_idx + vblk * D * (4 * BV));
+      V.nrm[1] = bload<float>(chunk_rsrc(a.v_norm + slot0, kChunk * 4), noff);
+      const auto vr = chunk_rsrc(a.v_idx + vblk * D * (4 * BV), D * 4 * BV);
 #pragma unroll
-      for (int vb = 0; vb < 8; ++vb)
-        V.vw[vb] = *reinterpret_cast<const uint32_t*>(vp + voff + 16 * vb * (4 * BV));
+      for (int vb = 0; vb < 8; ++vb) V.vw[vb] = bload<uint32_t>(vr, voff + 16 * vb * (4 * BV));
     }
   };
   // ---- scores of one chunk: tile T row col -> token 8 (col/4) + 4 T + col%4
@@ -1670,7 +1753,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       // a row need all 8 tokens' norms: exchange them through this wave's LDS
       // slot (in-order within the wave, so no barrier).
       float* nx = nxch + wave * 128;
-      if constexpr (MK > 0) nx[lane] = V.nrm[0];
+      if constexpr (MK > 0) nx[lane] = col < 8 ? V.nrm[0] : V.nrm[2];
       if constexpr (BV > 0 && !SCORE) nx[64 + lane] = vl * inv_sig;
       const float4* n4 = reinterpret_cast<const float4*>(nx + 16 * q);
       if constexpr (MK > 0) {
@@ -1870,8 +1953,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     if constexpr (!SCORE) {
       const int ng = a.G - Rp.hg * kMaxGroup < kMaxGroup ? a.G - Rp.hg * kMaxGroup : kMaxGroup;
       const int64_t row0 = (int64_t(Rp.layer) * a.batch + Rp.b) * a.Hq + Rp.hk * a.G + Rp.hg * kMaxGroup;
-      const int first = prob * cpp;
-      const int nseg = (first + cpp - 1) / a.chunks_per_wg - first / a.chunks_per_wg + 1;
+      const int nseg = pieces_of(prob);
       const int i = tid & (D - 1), r16 = lane & 15, kq = lane >> 4;
       constexpr bool ROT = BV > 0;
       float pa[ROT ? 32 : 1];
@@ -2019,8 +2101,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       __builtin_amdgcn_s_waitcnt(0);   // this wave's partial stores are complete
       __syncthreads();
       if (tid == 0) {
-        const int first = prob * cpp;
-        const uint32_t nseg = uint32_t((first + cpp - 1) / a.chunks_per_wg - first / a.chunks_per_wg + 1);
+        const uint32_t nseg = uint32_t(pieces_of(prob));
         const uint32_t old = __hip_atomic_fetch_add(a.done + prob, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool last = old + 1 == nseg;
         if (last) __hip_atomic_store(a.done + prob, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2050,12 +2131,65 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   float kcl = 0.f, vcl = 0.f;   // lane l: key / value centroid l mod (number of centroids), times its scale
   if constexpr (MK > 0) kcl = a.kc[lane & ((1 << MK) - 1)] * alpha_k;
   if constexpr (BV > 0) vcl = a.vc[lane & ((1 << BV) - 1)] * alpha_v;
-  const int c_first = wg * a.chunks_per_wg;
-  const int c_last = c_first + a.chunks_per_wg < a.total_chunks ? c_first + a.chunks_per_wg : a.total_chunks;
+  if (a.ragged) {
+    for (int b = tid; b < a.batch; b += NT) {
+      int64_t st = a.seq_start[b], ln = a.seq_len[b];
+      clamp_run(st, ln);
+      const int live = int((ln + kChunk - 1) / kChunk);
+      live_s[b + 1] = live > 0 ? live + kCrossingChunks : 0;
+    }
+    __syncthreads();
+    if (wave == 0) {   // inclusive prefix, 64 sequences at a time
+      int carry = 0;
+      for (int b0 = 0; b0 < a.batch; b0 += 64) {
+        const int b = b0 + lane;
+        int v = b < a.batch ? live_s[b + 1] : 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int t = __shfl_up(v, o);
+          if (lane >= o) v += t;
+        }
+        if (b < a.batch) live_s[b + 1] = carry + v;
+        carry += __shfl(v, 63);
+      }
+      if (lane == 0) live_s[0] = 0;
+    }
+    __syncthreads();
+    // ragged when the chunks that hold tokens are fewer than problems x cpp_real
+    int nonempty = 0;
+    for (int b = lane; b < a.batch; b += 64) nonempty += live_s[b + 1] != live_s[b] ? 1 : 0;
+    for (int o = 32; o > 0; o >>= 1) nonempty += __shfl_xor(nonempty, o);
+    nonempty = __builtin_amdgcn_readfirstlane(nonempty);
+    const int64_t per_seq = int64_t(a.n_layers) * HG;
+    const int64_t padded_total = per_seq * lds_s(a.batch);
+    if (padded_total - per_seq * nonempty * kCrossingChunks < int64_t(a.total_chunks / cpp) * a.cpp_real) {
+      rag = true;
+      total = int(padded_total);
+      const int64_t nd = int64_t(gridDim.x) - a.n_app;
+      const int even = int((padded_total + nd - 1) / nd);
+      cpw = even > a.cpw_min ? even : a.cpw_min;
+    }
+  }
+  if (rag) {
+    // the outputs of sequences without tokens (no range reaches them)
+    if (wg == 0) {
+      for (int b = 0; b < a.batch; ++b) {
+        if (live_s[b + 1] != live_s[b]) continue;
+        for (int64_t e = tid; e < int64_t(a.n_layers) * a.Hq * D; e += NT) {
+          const int64_t layer = e / (int64_t(a.Hq) * D), r = e % (int64_t(a.Hq) * D);
+          a.out[(layer * a.batch + b) * a.Hq * D + r] = 0.f;
+        }
+      }
+    }
+  }
+  const int c_first = wg * cpw;
+  const int c_last = c_first + cpw < total ? c_first + cpw : total;
+  if (c_first >= c_last) return;   // a workgroup without chunks (ragged split)
   QItem qitem;
   {
-    const int pa = c_first / cpp;
-    stage_load(pa, (pa + 1) * cpp < c_last, qitem);
+    const int pa = prob_of(c_first);
+    const int pa_end = pfirst(pa) + pcount(pa);
+    stage_load(pa, pa_end < c_last ? prob_of(pa_end) : pa, qitem);
   }
   __builtin_amdgcn_sched_barrier(0);
   Group G = group_of(c_first, c_last);
@@ -2112,7 +2246,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       }
     }
   }
-  stage_store(G.pa, G.has_b, qitem);
+  stage_store(G.pa, G.pb, qitem);
   if (tid == 0) counter[0] = 0;
   __syncthreads();
   if constexpr (MK > 0 && !KWIDE && KL::NC > 2) {
@@ -2127,8 +2261,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       pre = false;
       G = group_of(g0, c_last);
       app_ok_a = app_ok_b = false;
-      stage_load(G.pa, G.has_b, qitem);
-      stage_store(G.pa, G.has_b, qitem);
+      stage_load(G.pa, G.pb, qitem);
+      stage_store(G.pa, G.pb, qitem);
       __syncthreads();
     }
     // the wave's next three tickets (relative to base)
@@ -2223,15 +2357,15 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     if constexpr (!RED_LDS) __builtin_amdgcn_s_waitcnt(0);   // this wave's merge stores are complete
     __syncthreads();
     const int next_base = uni(counter[0]);   // every draw of the group is done
-    merge(G.ra, wg - (G.pa * cpp) / a.chunks_per_wg);
+    merge(G.ra, wg - pfirst(G.pa) / cpw);
     arrive(G.pa, G.ra);
     if (G.has_b) {
       __syncthreads();
       flush(had_b);
       if constexpr (!RED_LDS) __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      merge(G.rb, wg - G.a_end / a.chunks_per_wg);
-      arrive(G.pa + 1, G.rb);
+      merge(G.rb, wg - G.a_end / cpw);
+      arrive(G.pb, G.rb);
     }
     __syncthreads();
     base = next_base - 3 * kDecodeWaves;
@@ -2601,7 +2735,10 @@ DecodeArgs make_args(const tq_format* fmt, const tq_tables* tables, const tq_cac
   a.chunks_per_problem = int(plan.chunks_per_problem);
   a.chunks_per_wg = int(plan.chunks_per_wg);
   a.total_chunks = int(plan.problems * plan.chunks_per_problem);
-  a.seg_max = int(plan.seg_max);
+  a.seg_max = int(plan.seg_cap);
+  a.cpp_real = int(plan.cpp_real);
+  a.cpw_min = int(plan.cpw_min);
+  a.ragged = 0;
   a.k_idx = cache->k_idx;
   a.k_sign = cache->k_sign;
   a.k_norm = cache->k_norm;
@@ -2713,6 +2850,7 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   if (!SCORE && (stages & kStageMerge)) {
     a.done = done;
     a.out = out;
+    a.ragged = batch > 1 && batch <= kRaggedMaxBatch ? 1 : 0;
   }
   if (!SCORE && app != nullptr) {
     a.n_app = app->groups * app->layers;
@@ -2812,7 +2950,7 @@ tq_status decode_tail(const tq_format* fmt, const tq_tables* tables, const tq_ca
                             tp.tail, fmt->k_bits > 0 ? qplain : qrot, partial, nullptr);
   at.red_g = red_g;
   at.seg_max = int(tp.seg_total);
-  at.seg_base = int(tp.packed.seg_max);
+  at.seg_base = int(tp.packed.seg_cap);
   if ((st = launch_decode<false>(0, 0, at, dim3(unsigned(tp.tail.n_workgroups)), hs))) return st;
   DecodeArgs ap = make_args(fmt, tables, cache, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, tp.packed,
                             qrot, partial, nullptr);
@@ -2820,7 +2958,7 @@ tq_status decode_tail(const tq_format* fmt, const tq_tables* tables, const tq_ca
   ap.red_g = red_g;
   ap.done = done;
   ap.out = out;
-  ap.tail_base = int(tp.packed.seg_max);
+  ap.tail_base = int(tp.packed.seg_cap);
   ap.tail_cpp = at.chunks_per_problem;
   ap.tail_cpw = at.chunks_per_wg;
   if ((st = launch_decode<false>(mk, bv, ap, dim3(unsigned(tp.packed.n_workgroups)), hs))) return st;
