@@ -71,7 +71,7 @@ enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_BF16 = 1, TQ_DTYPE_F16 = 2 };
 /* Storage format.  k_bits: 0 keeps keys in fp16, else 2..5 or 8 total bits
  * per coordinate = (k_bits-1) Lloyd-Max bits + 1 QJL sign bit (8: the 8-bit
  * key codec, turbo8, of the long-context write-up's benchmarks).  v_bits: 0
- * keeps values in fp16, else 1, 2 or 4 MSE-only bits. */
+ * keeps values in fp16, else 1 to 4 MSE-only bits. */
 typedef struct tq_format {
   int32_t d;
   int32_t k_bits;

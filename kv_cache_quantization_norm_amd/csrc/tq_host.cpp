@@ -34,8 +34,8 @@ tq_status check_format(const tq_format* f, bool device) {
   if (f->d < 8 || f->d % 8 != 0) return fail(TQ_ERR_INVALID_ARG, "d=%d must be a positive multiple of 8", f->d);
   if (f->k_bits < 0 || f->k_bits == 1 || (f->k_bits > 5 && f->k_bits != 8))
     return fail(TQ_ERR_UNSUPPORTED, "k_bits=%d (0 for fp16 keys, else 2..5 or 8)", f->k_bits);
-  if (!(f->v_bits == 0 || f->v_bits == 1 || f->v_bits == 2 || f->v_bits == 4))
-    return fail(TQ_ERR_UNSUPPORTED, "v_bits=%d (0 for fp16 values, else 1, 2 or 4)", f->v_bits);
+  if (f->v_bits < 0 || f->v_bits > 4)
+    return fail(TQ_ERR_UNSUPPORTED, "v_bits=%d (0 for fp16 values, else 1 to 4)", f->v_bits);
   if (device && f->d != 128) return fail(TQ_ERR_UNSUPPORTED, "device kernels need d=128, got %d", f->d);
   return TQ_OK;
 }

@@ -403,6 +403,22 @@ __device__ __forceinline__ void or_bits(uint32_t* rec, int bitpos, uint32_t chun
   if (sh + nbits > 32) atomicOr(&rec[w + 1], chunk >> (32 - sh));
 }
 
+// Writes the BV-bit value code of slot p of a (block, coordinate) group of
+// 32 codes (4 BV bytes, LSB-first: code p at bits [BV p, BV p + BV)); a 3-bit
+// code may straddle two dwords.  Other codes of the group are left as they are.
+template <int BV>
+__device__ __forceinline__ void put_vcode(uint32_t* group, int p, uint32_t idx) {
+  const int bit = p * BV, w = bit >> 5, sh = bit & 31;
+  const uint32_t m = (1u << BV) - 1u;
+  atomicAnd(group + w, ~(m << sh));
+  atomicOr(group + w, idx << sh);
+  if (sh + BV > 32) {
+    const int rs = 32 - sh;
+    atomicAnd(group + w + 1, ~(m >> rs));
+    atomicOr(group + w + 1, idx >> rs);
+  }
+}
+
 // XHL: fp32 inputs, whose slabs need a remainder operand (bf16 / fp16 inputs
 // are exact fp16 operands).
 template <int MK, int BV, bool XHL>
@@ -569,7 +585,7 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressA
         for (int r = 0; r < 4; ++r) vidx[tile][r] = qcode(y[tile][r], sm.vq);
       const int64_t gbytes = 4 * BV;  // bytes per (block, coordinate) group
       uint8_t* vplane = a.v_idx + plane * (a.capacity / kVBlock) * D * gbytes;
-      if (contiguous && BV >= 2) {
+      if (contiguous && (BV == 2 || BV == 4)) {
         // The wave owns whole dwords: 16 tokens x bv bits per coordinate.
         const int dw = BV / 2;  // dwords per coordinate for 16 tokens
         for (int e = lane; e < D * dw; e += 64) vrec[e] = 0u;
@@ -596,17 +612,12 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressA
       } else if (valid) {
         const int64_t blk = slot / kVBlock;
         const int p = int(slot % kVBlock);
-        const int bit = p * BV;
-        const uint32_t mask = ((1u << BV) - 1u) << (bit & 31);
 #pragma unroll
         for (int tile = 0; tile < 8; ++tile)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint32_t idx = vidx[tile][r];
             const int c = 16 * tile + 4 * q + r;
-            uint32_t* g = reinterpret_cast<uint32_t*>(vplane + (blk * D + c) * gbytes) + (bit >> 5);
-            atomicAnd(g, ~mask);
-            atomicOr(g, idx << (bit & 31));
+            put_vcode<BV>(reinterpret_cast<uint32_t*>(vplane + (blk * D + c) * gbytes), p, vidx[tile][r]);
           }
       }
     }
@@ -828,17 +839,14 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
         }
       } else if constexpr (BV > 0) {
         if (slot >= 0) {
-          const int bitp = int(slot % kVBlock) * BV;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             uint32_t idx = 0;
 #pragma unroll
             for (int b = 0; b < (1 << BV) - 1; ++b) idx += (y[r] >= cb[3][b]) ? 1u : 0u;
-            uint32_t* g = reinterpret_cast<uint32_t*>(a.v_idx + ((plane * vblocks + slot / kVBlock) * D + row + r) *
-                                                                     (4 * BV)) +
-                          (bitp >> 5);
-            atomicAnd(g, ~(((1u << BV) - 1u) << (bitp & 31)));
-            atomicOr(g, idx << (bitp & 31));
+            put_vcode<BV>(reinterpret_cast<uint32_t*>(a.v_idx + ((plane * vblocks + slot / kVBlock) * D + row + r) *
+                                                               (4 * BV)),
+                          int(slot % kVBlock), idx);
           }
         }
       }
@@ -1613,6 +1621,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   };
   struct VData {
     uint32_t vw[8];
+    uint32_t vw2[BV == 3 ? 8 : 1];   // 3-bit values: the next dword (a lane's 24 bits may straddle two)
     float nrm[3];   // key norm, residual norm, value norm of the lane's token
     half8 vf[BV > 0 ? 1 : 8];
   };
@@ -1624,7 +1633,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     soff[T] = tk * 16 + 4 * q;
   }
   const uint32_t noff = 4 * (8 * q + (col & 7));
-  const uint32_t voff = col * (4 * (BV > 0 ? BV : 1)) + 4 * (BV == 4 ? q : (BV == 2 ? (q >> 1) : 0));
+  // value codes of coordinate 16 vb + col, tokens 8 q .. 8 q + 7: bits [8 BV q,
+  // 8 BV q + 8 BV) of the coordinate's 4 BV-byte group, from dword voff / 4
+  const uint32_t voff = col * (4 * (BV > 0 ? BV : 1)) + 4 * ((8 * (BV > 0 ? BV : 1) * q) >> 5);
   // rel: chunk index within the problem (tokens 32 rel ..)
   // slot0: the chunk's first slot in its (layer, KV head) plane; vblk: its value block.
   auto load_k = [&](int64_t slot0, KData& K) {
@@ -1678,7 +1689,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       V.nrm[1] = bload<float>(chunk_rsrc(a.v_norm + slot0, kChunk * 4), noff);
       const auto vr = chunk_rsrc(a.v_idx + vblk * D * (4 * BV), D * 4 * BV);
 #pragma unroll
-      for (int vb = 0; vb < 8; ++vb) V.vw[vb] = bload<uint32_t>(vr, voff + 16 * vb * (4 * BV));
+      for (int vb = 0; vb < 8; ++vb) {
+        V.vw[vb] = bload<uint32_t>(vr, voff + 16 * vb * (4 * BV));
+        if constexpr (BV == 3) V.vw2[vb] = bload<uint32_t>(vr, voff + 4 + 16 * vb * (4 * BV));   // past the block: 0
+      }
     }
   };
   // ---- scores of one chunk: tile T row col -> token 8 (col/4) + 4 T + col%4
@@ -1840,7 +1854,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
             vd[u] = deq8_vrep<V_PAGE != 0>(V.vw[vb], lane4, vrep_base);
           } else if constexpr (BV > 0) {
             uint32_t bits = V.vw[vb];
-            if constexpr (BV == 2) bits = (bits >> (16 * (q & 1))) & 0xFFFFu;
+            if constexpr (BV == 3) bits = __builtin_amdgcn_alignbit(V.vw2[vb], bits, (24 * q) & 31) & 0xFFFFFFu;
+            else if constexpr (BV == 2) bits = (bits >> (16 * (q & 1))) & 0xFFFFu;
             else if constexpr (BV == 1) bits = (bits >> (8 * q)) & 0xFFu;
             vd[u] = deq8<BV>(bits, lut_v);
           } else {
@@ -2675,7 +2690,7 @@ tq_status launch_decode(int mk, int bv, const DecodeArgs& args, dim3 grid, hipSt
     hipLaunchKernelGGL((decode_kernel<MK_, BV_, SCORE>), grid, dim3(kDecodeWaves * 64), 0, st, args, ca); \
     return TQ_OK;                                                                              \
   }
-#define TQ_DEC_V(MK_) TQ_DEC(MK_, 0) TQ_DEC(MK_, 1) TQ_DEC(MK_, 2) TQ_DEC(MK_, 4)
+#define TQ_DEC_V(MK_) TQ_DEC(MK_, 0) TQ_DEC(MK_, 1) TQ_DEC(MK_, 2) TQ_DEC(MK_, 3) TQ_DEC(MK_, 4)
   if constexpr (SCORE) {
     // Scores do not read values: one instantiation per key format.
     TQ_DEC(0, 0) TQ_DEC(1, 0) TQ_DEC(2, 0) TQ_DEC(3, 0) TQ_DEC(4, 0) TQ_DEC(7, 0)
@@ -3159,7 +3174,7 @@ tq_status tq_compress_kv_bounded(const tq_format* fmt, const tq_tables* tables, 
                        dim3(kAppendThreads), 0, hs, a);                                                \
     return launch_status("compress (append)");                                                         \
   }
-#define TQ_APP_V(MK_) TQ_APP(MK_, 0) TQ_APP(MK_, 1) TQ_APP(MK_, 2) TQ_APP(MK_, 4)
+#define TQ_APP_V(MK_) TQ_APP(MK_, 0) TQ_APP(MK_, 1) TQ_APP(MK_, 2) TQ_APP(MK_, 3) TQ_APP(MK_, 4)
     TQ_APP_V(0) TQ_APP_V(1) TQ_APP_V(2) TQ_APP_V(3) TQ_APP_V(4) TQ_APP_V(7)
 #undef TQ_APP_V
 #undef TQ_APP
@@ -3171,7 +3186,7 @@ tq_status tq_compress_kv_bounded(const tq_format* fmt, const tq_tables* tables, 
   if (a.mk == MK_ && a.bv == BV_)                                                                   \
     fn = a.dtype == TQ_DTYPE_F32 ? reinterpret_cast<const void*>(compress_kernel<MK_, BV_, true>)   \
                                  : reinterpret_cast<const void*>(compress_kernel<MK_, BV_, false>);
-#define TQ_CMP_V(MK_) TQ_CMP(MK_, 0) TQ_CMP(MK_, 1) TQ_CMP(MK_, 2) TQ_CMP(MK_, 4)
+#define TQ_CMP_V(MK_) TQ_CMP(MK_, 0) TQ_CMP(MK_, 1) TQ_CMP(MK_, 2) TQ_CMP(MK_, 3) TQ_CMP(MK_, 4)
   TQ_CMP_V(0) TQ_CMP_V(1) TQ_CMP_V(2) TQ_CMP_V(3) TQ_CMP_V(4) TQ_CMP_V(7)
 #undef TQ_CMP_V
 #undef TQ_CMP
@@ -3227,7 +3242,7 @@ tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const
                        cache->n_layers);                                                                       \
     return launch_status("append + prepare");                                                                  \
   }
-#define TQ_AP_V(MK_) TQ_AP(MK_, 0) TQ_AP(MK_, 1) TQ_AP(MK_, 2) TQ_AP(MK_, 4)
+#define TQ_AP_V(MK_) TQ_AP(MK_, 0) TQ_AP(MK_, 1) TQ_AP(MK_, 2) TQ_AP(MK_, 3) TQ_AP(MK_, 4)
   TQ_AP_V(0) TQ_AP_V(1) TQ_AP_V(2) TQ_AP_V(3) TQ_AP_V(4) TQ_AP_V(7)
 #undef TQ_AP_V
 #undef TQ_AP

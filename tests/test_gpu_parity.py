@@ -56,6 +56,10 @@ CASES = {
     # 8-bit keys (7 Lloyd-Max bits + QJL) with 4-bit values, the wide key path
     "k8v4_ragged": wl.Workload("k8v4_ragged", 2, 2, 14, (300, 77), 8, 4, "bf16", 0.5, 1, 10.0),
     "k8v2_f32": wl.Workload("k8v2_f32", 1, 4, 32, (129,), 8, 2, "f32", 0.0, 0, 1.0),
+    # 3-bit values: a coordinate's 32 codes fill 12 bytes, codes 10 and 21 of a
+    # group straddle two dwords
+    "k3v3_ragged": wl.Workload("k3v3_ragged", 2, 2, 14, (300, 45, 0, 129), 3, 3, "bf16", 0.5, 1, 10.0),
+    "k4v3_t1000": wl.Workload("k4v3_t1000", 1, 4, 28, (1000,), 4, 3, "bf16", 0.5, 2, 10.0),
 }
 
 
@@ -161,7 +165,8 @@ def test_decode_parity_on_oracle_cache(case):
         _say("format", fmt, "worst logit rel", f"{worst_l:.2e}", "worst out abs", f"{worst_o:.2e}")
 
 
-@pytest.mark.parametrize("case", ["w1", "w2_4L_ragged", "w3_6L_asym", "w5_ragged5", "k8v4_ragged"])
+@pytest.mark.parametrize("case", ["w1", "w2_4L_ragged", "w3_6L_asym", "w5_ragged5", "k8v4_ragged", "k3v3_ragged",
+                                  "k4v3_t1000"])
 def test_end_to_end(case):
     """GPU compress + GPU decode against oracle compress + oracle decode, on
     inputs with no decision within 1e-6 of its threshold (there the output is
@@ -274,7 +279,7 @@ def test_degenerate_vectors_and_nan(chunk):
 
 
 @pytest.mark.parametrize("k_bits,v_bits,dtype", [(4, 2, "bf16"), (3, 4, "f32"), (5, 1, "f16"), (2, 0, "f32"),
-                                                 (8, 4, "bf16")])
+                                                 (8, 4, "bf16"), (4, 3, "bf16")])
 def test_overwrite_slot_and_append(k_bits, v_bits, dtype):
     """Re-compressing into used slots replaces their records (value codes are
     rewritten inside shared 32-slot groups), one token at a time."""
@@ -305,7 +310,7 @@ def test_overwrite_slot_and_append(k_bits, v_bits, dtype):
 
 
 @pytest.mark.parametrize("k_bits,v_bits,dtype,n_new", [(4, 4, "bf16", 1), (3, 2, "f32", 3), (0, 4, "bf16", 1),
-                                                         (5, 1, "f16", 20)])
+                                                         (5, 1, "f16", 20), (3, 3, "bf16", 2)])
 def test_append_prepare_matches_separate_calls(k_bits, v_bits, dtype, n_new):
     """tq_append_prepare leaves the same cache records and workspace, bit for
     bit, as tq_compress_kv followed by tq_decode_prepare (one kernel for a
@@ -469,6 +474,7 @@ def test_decode_steps_append_prepare_attend(k_bits, v_bits, hq, lens):
     ("slot0", 4, 4, 28, (100,), 20, 0),   # 20 tokens: 10 append workgroups per layer, inside the decode launch
     ("slots", 4, 4, 16, (60, 33, 1, 0, 7, 300, 95, 64, 2, 18, 250, 77, 3, 40, 121, 9), 1, 0),   # 16 sequences
     ("slot0", 3, 2, 8, (100,), 40, 0),    # 40 appended workgroups: bulk compression, then the decode
+    ("slots", 3, 3, 28, (300, 45, 0, 129), 1, 0),   # 3-bit values
 ])
 def test_decode_step_append_inside_decode_launch(mode, k_bits, v_bits, hq, lens, n_new, layer0):
     """tq_decode_step: the new tokens are compressed by the decode launch's

@@ -122,7 +122,9 @@ def test_device_calls_validate_before_launch():
     for kb in (6, 7, 9):   # 8-bit keys (7 Lloyd-Max bits) are the one wide format
         assert r("tq_compress_kv", P(tq.make_format(128, kb, 4)), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_UNSUPPORTED
     assert r("tq_compress_kv", P(tq.make_format(128, 8, 4)), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 0, None, 0, None) == tq.TQ_OK
-    assert r("tq_compress_kv", P(tq.make_format(128, 4, 3)), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_UNSUPPORTED
+    for vb in (-1, 5, 8):
+        assert r("tq_compress_kv", P(tq.make_format(128, 4, vb)), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_UNSUPPORTED
+    assert r("tq_compress_kv", P(tq.make_format(128, 4, 3)), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 0, None, 0, None) == tq.TQ_OK
     assert r("tq_compress_kv", P(tq.make_format(128, 6, 4)), P(tb), P(cs), FAKE, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_UNSUPPORTED
     # NULL and inconsistent arguments
     assert r("tq_compress_kv", P(fmt), None, P(cs), FAKE, FAKE, 0, 0, 1, 1, None, 0, None) == tq.TQ_ERR_INVALID_ARG
