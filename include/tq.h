@@ -247,6 +247,55 @@ tq_status tq_decode_attention_tail(const tq_format* fmt, const tq_tables* tables
  * bandwidth against which the decode kernel's rate can also be read. */
 tq_status tq_stream_read_probe(const void* data, size_t bytes, float* partial, int32_t n_workgroups, void* stream);
 
+/* The recent-token ring of a hybrid cache (packed history + fp16 tail).
+ * The pages keep the most recent tokens at full precision in a ring buffer,
+ * take the compressed path only once there is history enough (16 tokens or
+ * more: the QJL deep-dive, section 6), and compress only sequences of at
+ * least min_compress_tokens tokens (default 256: the MLX write-up, section on
+ * the quality scripts).  Convention here: a ring of ring_cap slots (a
+ * multiple of 32) lives in a tail cache of the fp16 format with capacity >=
+ * 2 ring_cap, every token stored at its ring slot p and again at p +
+ * ring_cap, so that any run of at most ring_cap consecutive ring positions
+ * starting at p < ring_cap is the contiguous slot range [p, p + n) of the
+ * tail; a sequence's tail is then one range for tq_decode_attention_tail even
+ * when it wraps around the ring.  Tokens leave the ring, oldest first, in
+ * whole 32-token blocks (tq_tail_policy), so ring heads stay multiples of 32
+ * and the packed part of a sequence, once non-empty, holds 32 tokens or more.
+ *
+ * Host.  Per sequence b (host arrays of `batch`): n_flush[b] = the largest
+ * multiple of 32 that leaves at least keep_recent tokens in the tail, when
+ * packed_len[b] + tail_len[b] >= min_compress_tokens, else 0.
+ * TQ_ERR_INVALID_ARG for negative lengths or parameters or NULL arrays. */
+tq_status tq_tail_policy(int32_t batch, const int32_t* packed_len, const int32_t* tail_len,
+                         int32_t min_compress_tokens, int32_t keep_recent, int32_t* n_flush);
+
+/* Device.  Writes n_tokens new tokens into the ring of `tail` (fp16 format
+ * with d = fmt->d): token i (k, v as in tq_compress_kv, [n_layers][n_tokens]
+ * [H][d]) at tail slots ring_slots[i] and ring_slots[i] + ring_cap (device
+ * int64 [n_tokens], each in [0, ring_cap)).  Two compression launches on
+ * `stream`.  TQ_ERR_INVALID_ARG unless ring_cap is a positive multiple of 32
+ * with 2 ring_cap <= tail->capacity. */
+tq_status tq_tail_append(const tq_format* fmt, const tq_tables* tables, const tq_cache* tail, const void* k,
+                         const void* v, int32_t dtype, int32_t layer0, int32_t n_layers, int64_t n_tokens,
+                         const int64_t* ring_slots, int64_t ring_cap, void* stream);
+
+/* Host.  Workspace bytes of tq_tail_flush (0 for invalid sizes). */
+size_t tq_tail_flush_workspace_bytes(const tq_format* fmt, const tq_cache* packed, int32_t batch, int32_t max_flush);
+
+/* Device.  Moves tail tokens into the packed cache: for every layer of the
+ * caches, token i < n_flush[b] of sequence b (tail slot tail_pos[b] + i) is
+ * compressed from its fp16 key and value into packed slot dst_slot[b] + i
+ * (device arrays of `batch`: int64 tail_pos, int32 n_flush (each <=
+ * max_flush), int64 dst_slot).  The tail is not modified (the caller advances
+ * its ring head).  A gather launch into the workspace (fp16 staging of
+ * batch x max_flush tokens, then their packed slots), then the compression;
+ * tokens whose tail or packed slot is outside its cache are skipped.
+ * workspace: at least tq_tail_flush_workspace_bytes(fmt, packed, batch,
+ * max_flush) bytes, not shared by overlapping calls. */
+tq_status tq_tail_flush(const tq_format* fmt, const tq_tables* tables, const tq_cache* packed, const tq_cache* tail,
+                        int32_t batch, int32_t max_flush, const int64_t* tail_pos, const int32_t* n_flush,
+                        const int64_t* dst_slot, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Host.  Workspace bytes of tq_decode_attention_tail (0 for invalid sizes). */
 size_t tq_decode_tail_workspace_bytes(const tq_format* fmt, int32_t n_layers, int32_t batch, int32_t n_kv_heads,
                                       int32_t n_q_heads, int64_t max_seq_len, int64_t max_tail_len);

@@ -93,6 +93,10 @@ def _load(path: str = LIB_PATH):
                                  P, SZ, P]),
         "tq_decode_step_check": (I32, [fmtp, I32, I32, I32, I32, I64, P, SZ, P]),
         "tq_set_append_wait": (I32, [ctypes.c_uint32, I32]),
+        "tq_tail_policy": (I32, [I32, P, P, I32, I32, P]),
+        "tq_tail_append": (I32, [fmtp, tabp, cachep, P, P, I32, I32, I32, I64, P, I64, P]),
+        "tq_tail_flush_workspace_bytes": (SZ, [fmtp, cachep, I32, I32]),
+        "tq_tail_flush": (I32, [fmtp, tabp, cachep, cachep, I32, I32, P, P, P, P, SZ, P]),
         "tq_status_string": (ctypes.c_char_p, [I32]),
         "tq_last_error": (ctypes.c_char_p, []),
     }
@@ -111,6 +115,7 @@ EXPORTED = ("tq_layer_seed", "tq_make_rotations", "tq_make_codebook", "tq_cache_
             "tq_append_prepare",
             "tq_compress_kv_bounded", "tq_decode_attention_tail", "tq_decode_tail_workspace_bytes",
             "tq_decode_attention_noalloc", "tq_decode_step_check", "tq_set_append_wait", "tq_fp16_operand_scale",
+            "tq_tail_policy", "tq_tail_append", "tq_tail_flush_workspace_bytes", "tq_tail_flush",
             "tq_status_string", "tq_last_error")
 
 
@@ -516,6 +521,55 @@ def tail_workspace_for(fmt: tq_format, cache: Cache, batch: int, n_q_heads: int,
     if nbytes == 0:
         raise TQError(TQ_ERR_INVALID_ARG, "tq_decode_tail_workspace_bytes", "invalid sizes")
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def tq_tail_policy(packed_len, tail_len, min_compress_tokens: int = 256, keep_recent: int = 16):
+    """Host: tokens each sequence moves from its fp16 tail ring into the
+    packed cache (multiples of 32), from host int sequences of lengths."""
+    pl = np.ascontiguousarray(packed_len, dtype=np.int32)
+    tl = np.ascontiguousarray(tail_len, dtype=np.int32)
+    if pl.shape != tl.shape or pl.ndim != 1:
+        raise ValueError("packed_len and tail_len: 1-d of the same length")
+    out = np.zeros(pl.shape, np.int32)
+    _check(_lib.tq_tail_policy(len(pl), pl.ctypes.data, tl.ctypes.data, min_compress_tokens, keep_recent,
+                               out.ctypes.data), "tq_tail_policy")
+    return out
+
+
+def tq_tail_append(fmt: tq_format, tables: Tables, tail: Cache, k, v, ring_slots, ring_cap: int, layer0: int = 0,
+                   stream=None):
+    """New tokens into the tail ring (slot p and its mirror p + ring_cap):
+    k, v [n_layers][n_tokens][n_kv_heads][d]; ring_slots device int64 [n_tokens]."""
+    pk, pv, n_layers, n_tokens = _kv(fmt, tail, k, v)
+    ps = _dev(ring_slots, _i64(), (n_tokens,), "ring_slots")
+    tb, ts = tables.struct(), tail.struct()
+    _check(_lib.tq_tail_append(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(ts), pk, pv, _dtype_code(k), layer0,
+                               n_layers, n_tokens, ps, ring_cap, _stream(stream)), "tq_tail_append")
+
+
+def tail_flush_workspace_for(fmt: tq_format, packed: Cache, batch: int, max_flush: int, device="cuda"):
+    import torch
+    nbytes = int(_lib.tq_tail_flush_workspace_bytes(ctypes.byref(fmt), ctypes.byref(packed.struct()), batch, max_flush))
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def tq_tail_flush(fmt: tq_format, tables: Tables, packed: Cache, tail: Cache, max_flush: int, tail_pos, n_flush,
+                  dst_slot, workspace, stream=None):
+    """Moves n_flush[b] tail tokens (from tail slot tail_pos[b]) of each
+    sequence into packed slots dst_slot[b] ..; device int64 / int32 / int64 [batch]."""
+    import torch
+    if not isinstance(tail_pos, torch.Tensor) or tail_pos.dim() != 1:
+        raise TypeError("tail_pos: expected a 1-d device int64 tensor")
+    batch = int(tail_pos.shape[0])
+    pp = _dev(tail_pos, _i64(), (batch,), "tail_pos")
+    pn = _dev(n_flush, _i32(), (batch,), "n_flush")
+    pd = _dev(dst_slot, _i64(), (batch,), "dst_slot")
+    pw, nw = _ws(workspace)
+    if tail.n_layers != packed.n_layers or tail.n_kv_heads != packed.n_kv_heads:
+        raise ValueError("tail: must have the packed cache's layers and KV heads")
+    tb, cs, ts = tables.struct(), packed.struct(), tail.struct()
+    _check(_lib.tq_tail_flush(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), ctypes.byref(ts), batch,
+                              max_flush, pp, pn, pd, pw, nw, _stream(stream)), "tq_tail_flush")
 
 
 def tq_decode_attention_tail(fmt: tq_format, tables: Tables, cache: Cache, tail: Cache, q, seq_start, seq_len,

@@ -273,6 +273,26 @@ struct CoordinateLaw {
 
 extern "C" {
 
+tq_status tq_tail_policy(int32_t batch, const int32_t* packed_len, const int32_t* tail_len,
+                         int32_t min_compress_tokens, int32_t keep_recent, int32_t* n_flush) {
+  using namespace tq;
+  clear_error();
+  if (batch < 0 || min_compress_tokens < 0 || keep_recent < 0)
+    return fail(TQ_ERR_INVALID_ARG, "batch=%d min_compress_tokens=%d keep_recent=%d", batch, min_compress_tokens,
+                keep_recent);
+  if (batch > 0 && (!packed_len || !tail_len || !n_flush))
+    return fail(TQ_ERR_INVALID_ARG, "packed_len, tail_len or n_flush is NULL");
+  for (int32_t b = 0; b < batch; ++b)
+    if (packed_len[b] < 0 || tail_len[b] < 0)
+      return fail(TQ_ERR_INVALID_ARG, "sequence %d: packed_len=%d tail_len=%d", b, packed_len[b], tail_len[b]);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t total = int64_t(packed_len[b]) + tail_len[b];
+    const int64_t movable = int64_t(tail_len[b]) - keep_recent;
+    n_flush[b] = total >= min_compress_tokens && movable >= kVBlock ? int32_t(movable / kVBlock * kVBlock) : 0;
+  }
+  return TQ_OK;
+}
+
 uint64_t tq_layer_seed(int32_t layer) { return uint64_t(42 + 7 * int64_t(layer)); }
 
 tq_status tq_make_rotations(int32_t d, uint64_t seed, float* pi, float* s, float* pi_s) {

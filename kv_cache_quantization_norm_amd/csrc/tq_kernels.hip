@@ -167,6 +167,7 @@ struct CompressArgs {
   int64_t n_tokens;
   const int64_t* slots;
   int64_t slot0;
+  int64_t slot_shift;   // added to slots[i] (a ring's mirror copy); 0 for the public calls
   int H;
   int64_t capacity;
   int mk;  // key MSE bits, 0 = fp16 keys
@@ -462,7 +463,7 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressA
   const int64_t tok = tok0 + t;
   const bool tok_ok = tok < a.n_tokens;
   int64_t slot = -1;
-  if (tok_ok) slot = a.slots ? a.slots[tok] : a.slot0 + tok;
+  if (tok_ok) slot = a.slots ? a.slots[tok] + a.slot_shift : a.slot0 + tok;
   const bool valid = tok_ok && slot >= 0 && slot < a.capacity;
   // Fast value path: 16 contiguous, 16-aligned, all-valid slots.
   bool contiguous = (a.slots == nullptr) && (tok0 + kCompressTile <= a.n_tokens) &&
@@ -551,7 +552,7 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressA
         const int tt = e / kwords, w = e - tt * kwords;
         const int64_t tk = tok0 + tt;
         if (tk >= a.n_tokens) continue;
-        const int64_t sl = a.slots ? a.slots[tk] : a.slot0 + tk;
+        const int64_t sl = a.slots ? a.slots[tk] + a.slot_shift : a.slot0 + tk;
         if (sl < 0 || sl >= a.capacity) continue;
         reinterpret_cast<uint32_t*>(a.k_idx + (plane * a.capacity + sl) * (16 * MK))[w] = rec[tt * KSTR + w];
       }
@@ -559,7 +560,7 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressA
         const int tt = lane >> 2, w = lane & 3;
         const int64_t tk = tok0 + tt;
         if (tk < a.n_tokens) {
-          const int64_t sl = a.slots ? a.slots[tk] : a.slot0 + tk;
+          const int64_t sl = a.slots ? a.slots[tk] + a.slot_shift : a.slot0 + tk;
           if (sl >= 0 && sl < a.capacity)
             reinterpret_cast<uint32_t*>(a.k_sign + (plane * a.capacity + sl) * 16)[w] = srec[tt * 4 + w];
         }
@@ -738,7 +739,7 @@ __device__ __forceinline__ void append_body(const CompressArgs& a, int group, in
   int64_t slot = -1;
   {
     const int64_t tok = (item0 + (tid < ni ? tid : 0)) / a.H;
-    if (tid < kAppendItems && tid < ni) slot = a.slots ? a.slots[tok] : a.slot0 + tok;
+    if (tid < kAppendItems && tid < ni) slot = a.slots ? a.slots[tok] + a.slot_shift : a.slot0 + tok;
   }
   // Codebooks: thread j holds entry j % 128 of table j / 128 (0 past the
   // end; the boundary tables are padded with +inf).
@@ -2800,7 +2801,7 @@ constexpr int kMaxFusedAppend = 32;
 uint32_t g_append_wait_polls = 1u << 20;
 int g_append_wait_extra = 0;
 struct FusedAppend {
-  CompressArgs ca;
+  CompressArgs ca{};
   int groups = 0;            // append workgroups per layer
   int layers = 0;            // appended layers, from ca.layer0
   int64_t lo = 0, hi = 0;    // plane slots the append may write
@@ -3017,6 +3018,7 @@ tq_status compress_setup(const tq_format* fmt, const tq_tables* tables, const tq
   a.n_tokens = n_tokens;
   a.slots = slots;
   a.slot0 = slot0;
+  a.slot_shift = 0;
   a.H = cache->n_kv_heads;
   a.capacity = cache->capacity;
   a.mk = fmt->k_bits > 0 ? fmt->k_bits - 1 : 0;
@@ -3108,6 +3110,82 @@ void* scratch_for_current_device() {
 }  // namespace
 }  // namespace tq
 
+namespace tq {
+namespace {
+// The fp16 tail tokens that a flush moves into the packed cache: staging row
+// r = b * max_flush + i holds token i of sequence b (i < n_flush[b]), tail
+// slot tail_pos[b] + i, as [L][rows][H][D] fp16 keys and values; slots[r] is
+// its packed slot dst_slot[b] + i, or -1 for a row without a token (or a tail
+// slot outside the tail), which the compression skips.  Grid (rows, L).
+__global__ __launch_bounds__(256) void tail_gather_kernel(const uint16_t* k16, const uint16_t* v16, int64_t tail_cap,
+                                                         int H, int max_flush, const int64_t* tail_pos,
+                                                         const int32_t* n_flush, const int64_t* dst_slot,
+                                                         uint16_t* sk, uint16_t* sv, int64_t* slots) {
+  const int64_t r = blockIdx.x, rows = gridDim.x;
+  const int layer = blockIdx.y;
+  const int b = int(r / max_flush), i = int(r % max_flush);
+  const int64_t ts = tail_pos[b] + i;
+  const bool ok = i < n_flush[b] && ts >= 0 && ts < tail_cap;
+  if (layer == 0 && threadIdx.x == 0) slots[r] = ok ? dst_slot[b] + i : -1;
+  uint16_t* dk = sk + (int64_t(layer) * rows + r) * H * D;
+  uint16_t* dv = sv + (int64_t(layer) * rows + r) * H * D;
+  for (int e = threadIdx.x; e < H * D; e += blockDim.x) {
+    const int h = e / D, j = e % D;
+    const int64_t plane = int64_t(layer) * H + h;
+    dk[e] = ok ? k16[(plane * tail_cap + ts) * D + j] : uint16_t(0);
+    dv[e] = ok ? v16[((plane * (tail_cap / kVBlock) + ts / kVBlock) * D + j) * kVBlock + ts % kVBlock] : uint16_t(0);
+  }
+}
+
+// Compression (tq_compress_kv_bounded) with slot_shift added to each slots[i].
+tq_status compress_run(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, const void* k,
+                       const void* v, int32_t dtype, int32_t layer0, int32_t n_layers, int64_t n_tokens,
+                       const int64_t* slots, int64_t slot0, int32_t max_workgroups, int64_t slot_shift, void* stream) {
+  CompressArgs a{};
+  int64_t wgs = 0;
+  bool nothing = false;
+  tq_status st = compress_setup(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0,
+                                max_workgroups, a, wgs, nothing);
+  if (st || nothing) return st;
+  a.slot_shift = slot_shift;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (n_tokens < kCompressTile) {
+    // Appends: 8 (token, head) items per workgroup.
+    const int64_t groups = (n_tokens * a.H + kAppendItems - 1) / kAppendItems;
+#define TQ_APP(MK_, BV_)                                                                               \
+  if (a.mk == MK_ && a.bv == BV_) {                                                                    \
+    hipLaunchKernelGGL((compress_append_kernel<MK_, BV_>), dim3(unsigned(groups), unsigned(n_layers)), \
+                       dim3(kAppendThreads), 0, hs, a);                                                \
+    return launch_status("compress (append)");                                                         \
+  }
+#define TQ_APP_V(MK_) TQ_APP(MK_, 0) TQ_APP(MK_, 1) TQ_APP(MK_, 2) TQ_APP(MK_, 3) TQ_APP(MK_, 4)
+    TQ_APP_V(0) TQ_APP_V(1) TQ_APP_V(2) TQ_APP_V(3) TQ_APP_V(4) TQ_APP_V(7)
+#undef TQ_APP_V
+#undef TQ_APP
+    return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for key bits %d / value bits %d", a.mk, a.bv);
+  }
+  const size_t smem = sizeof(CompressSmem);
+  const void* fn = nullptr;
+#define TQ_CMP(MK_, BV_)                                                                            \
+  if (a.mk == MK_ && a.bv == BV_)                                                                   \
+    fn = a.dtype == TQ_DTYPE_F32 ? reinterpret_cast<const void*>(compress_kernel<MK_, BV_, true>)   \
+                                 : reinterpret_cast<const void*>(compress_kernel<MK_, BV_, false>);
+#define TQ_CMP_V(MK_) TQ_CMP(MK_, 0) TQ_CMP(MK_, 1) TQ_CMP(MK_, 2) TQ_CMP(MK_, 3) TQ_CMP(MK_, 4)
+  TQ_CMP_V(0) TQ_CMP_V(1) TQ_CMP_V(2) TQ_CMP_V(3) TQ_CMP_V(4) TQ_CMP_V(7)
+#undef TQ_CMP_V
+#undef TQ_CMP
+  if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for key bits %d / value bits %d", a.mk, a.bv);
+  const hipError_t ae = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+  if (ae != hipSuccess)
+    return fail(TQ_ERR_HIP, "cannot raise the LDS limit to %zu bytes: %s", smem, hipGetErrorString(ae));
+  void* args[] = {&a};
+  if (hipLaunchKernel(fn, dim3(unsigned(wgs)), dim3(kCompressWaves * 64), args, smem, hs) != hipSuccess)
+    return fail(TQ_ERR_HIP, "compress launch failed: %s", hipGetErrorString(hipGetLastError()));
+  return launch_status("compress");
+}
+}  // namespace
+}  // namespace tq
+
 extern "C" {
 
 tq_status tq_decode_attention_noalloc(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
@@ -3156,48 +3234,66 @@ tq_status tq_compress_kv_bounded(const tq_format* fmt, const tq_tables* tables, 
                                  const void* k, const void* v, int32_t dtype, int32_t layer0, int32_t n_layers,
                                  int64_t n_tokens, const int64_t* slots, int64_t slot0, int32_t max_workgroups,
                                  void* stream) {
+  tq::clear_error();
+  return tq::compress_run(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0, max_workgroups,
+                          0, stream);
+}
+
+tq_status tq_tail_append(const tq_format* fmt, const tq_tables* tables, const tq_cache* tail, const void* k,
+                         const void* v, int32_t dtype, int32_t layer0, int32_t n_layers, int64_t n_tokens,
+                         const int64_t* ring_slots, int64_t ring_cap, void* stream) {
   using namespace tq;
   clear_error();
-  CompressArgs a{};
-  int64_t wgs = 0;
-  bool nothing = false;
-  tq_status st = compress_setup(fmt, tables, cache, k, v, dtype, layer0, n_layers, n_tokens, slots, slot0,
-                                max_workgroups, a, wgs, nothing);
-  if (st || nothing) return st;
+  if (!fmt) return fail(TQ_ERR_INVALID_ARG, "format is NULL");
+  if (!tail) return fail(TQ_ERR_INVALID_ARG, "tail is NULL");
+  if (ring_cap <= 0 || ring_cap % kVBlock != 0 || 2 * ring_cap > tail->capacity)
+    return fail(TQ_ERR_INVALID_ARG, "ring_cap=%lld (a positive multiple of 32, at most half the tail's capacity %lld)",
+                (long long)ring_cap, (long long)tail->capacity);
+  if (n_tokens > 0 && !ring_slots) return fail(TQ_ERR_INVALID_ARG, "ring_slots is NULL");
+  const tq_format f16{fmt->d, 0, 0};
+  tq_status st = compress_run(&f16, tables, tail, k, v, dtype, layer0, n_layers, n_tokens, ring_slots, 0, 0, 0, stream);
+  if (st) return st;
+  return compress_run(&f16, tables, tail, k, v, dtype, layer0, n_layers, n_tokens, ring_slots, 0, 0, ring_cap, stream);
+}
+
+size_t tq_tail_flush_workspace_bytes(const tq_format* fmt, const tq_cache* packed, int32_t batch, int32_t max_flush) {
+  if (!fmt || !packed || batch <= 0 || max_flush < 0) return 0;
+  const size_t rows = size_t(batch) * size_t(max_flush);
+  const size_t plane = (size_t(packed->n_layers) * rows * packed->n_kv_heads * fmt->d * 2 + 255) & ~size_t(255);
+  return 2 * plane + rows * sizeof(int64_t);
+}
+
+tq_status tq_tail_flush(const tq_format* fmt, const tq_tables* tables, const tq_cache* packed, const tq_cache* tail,
+                        int32_t batch, int32_t max_flush, const int64_t* tail_pos, const int32_t* n_flush,
+                        const int64_t* dst_slot, void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace tq;
+  clear_error();
+  tq_status st = check_format(fmt, true);
+  if (st) return st;
+  if (!packed || !tail) return fail(TQ_ERR_INVALID_ARG, "packed or tail is NULL");
+  const tq_format f16{fmt->d, 0, 0};
+  if ((st = check_cache(fmt, packed)) || (st = check_cache(&f16, tail))) return st;
+  if (tail->n_layers != packed->n_layers || tail->n_kv_heads != packed->n_kv_heads)
+    return fail(TQ_ERR_INVALID_ARG, "tail has %d layers x %d KV heads, the packed cache %d x %d", tail->n_layers,
+                tail->n_kv_heads, packed->n_layers, packed->n_kv_heads);
+  if (batch <= 0 || max_flush < 0) return fail(TQ_ERR_INVALID_ARG, "batch=%d max_flush=%d", batch, max_flush);
+  if (max_flush == 0) return TQ_OK;
+  if (!tail_pos || !n_flush || !dst_slot) return fail(TQ_ERR_INVALID_ARG, "tail_pos, n_flush or dst_slot is NULL");
+  const int64_t rows = int64_t(batch) * max_flush;
+  if (rows > 0x7FFFFFFF || packed->n_layers > 65535) return fail(TQ_ERR_INVALID_ARG, "flush too large");
+  const size_t need = tq_tail_flush_workspace_bytes(fmt, packed, batch, max_flush);
+  if (!workspace || workspace_bytes < need)
+    return fail(TQ_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  const size_t plane = (need - size_t(rows) * sizeof(int64_t)) / 2;
+  uint16_t* sk = static_cast<uint16_t*>(workspace);
+  uint16_t* sv = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + plane);
+  int64_t* slots = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + 2 * plane);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (n_tokens < kCompressTile) {
-    // Appends: 8 (token, head) items per workgroup.
-    const int64_t groups = (n_tokens * a.H + kAppendItems - 1) / kAppendItems;
-#define TQ_APP(MK_, BV_)                                                                               \
-  if (a.mk == MK_ && a.bv == BV_) {                                                                    \
-    hipLaunchKernelGGL((compress_append_kernel<MK_, BV_>), dim3(unsigned(groups), unsigned(n_layers)), \
-                       dim3(kAppendThreads), 0, hs, a);                                                \
-    return launch_status("compress (append)");                                                         \
-  }
-#define TQ_APP_V(MK_) TQ_APP(MK_, 0) TQ_APP(MK_, 1) TQ_APP(MK_, 2) TQ_APP(MK_, 3) TQ_APP(MK_, 4)
-    TQ_APP_V(0) TQ_APP_V(1) TQ_APP_V(2) TQ_APP_V(3) TQ_APP_V(4) TQ_APP_V(7)
-#undef TQ_APP_V
-#undef TQ_APP
-    return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for key bits %d / value bits %d", a.mk, a.bv);
-  }
-  const size_t smem = sizeof(CompressSmem);
-  const void* fn = nullptr;
-#define TQ_CMP(MK_, BV_)                                                                            \
-  if (a.mk == MK_ && a.bv == BV_)                                                                   \
-    fn = a.dtype == TQ_DTYPE_F32 ? reinterpret_cast<const void*>(compress_kernel<MK_, BV_, true>)   \
-                                 : reinterpret_cast<const void*>(compress_kernel<MK_, BV_, false>);
-#define TQ_CMP_V(MK_) TQ_CMP(MK_, 0) TQ_CMP(MK_, 1) TQ_CMP(MK_, 2) TQ_CMP(MK_, 3) TQ_CMP(MK_, 4)
-  TQ_CMP_V(0) TQ_CMP_V(1) TQ_CMP_V(2) TQ_CMP_V(3) TQ_CMP_V(4) TQ_CMP_V(7)
-#undef TQ_CMP_V
-#undef TQ_CMP
-  if (!fn) return fail(TQ_ERR_UNSUPPORTED, "no compress kernel for key bits %d / value bits %d", a.mk, a.bv);
-  const hipError_t ae = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
-  if (ae != hipSuccess)
-    return fail(TQ_ERR_HIP, "cannot raise the LDS limit to %zu bytes: %s", smem, hipGetErrorString(ae));
-  void* args[] = {&a};
-  if (hipLaunchKernel(fn, dim3(unsigned(wgs)), dim3(kCompressWaves * 64), args, smem, hs) != hipSuccess)
-    return fail(TQ_ERR_HIP, "compress launch failed: %s", hipGetErrorString(hipGetLastError()));
-  return launch_status("compress");
+  hipLaunchKernelGGL(tail_gather_kernel, dim3(unsigned(rows), unsigned(packed->n_layers)), dim3(256), 0, hs,
+                     static_cast<const uint16_t*>(tail->k_f16), static_cast<const uint16_t*>(tail->v_f16),
+                     tail->capacity, packed->n_kv_heads, max_flush, tail_pos, n_flush, dst_slot, sk, sv, slots);
+  if ((st = launch_status("tail gather"))) return st;
+  return compress_run(fmt, tables, packed, sk, sv, TQ_DTYPE_F16, 0, packed->n_layers, rows, slots, 0, 0, 0, stream);
 }
 
 tq_status tq_append_prepare(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,

@@ -778,3 +778,104 @@ def test_full_size_sampled(short):
         ref = attention.decode_attention(c, qh, starts, lens, pi, s, cbk, cbv)
         err = pu.check_outputs(out[li][:, kvh * G:(kvh + 1) * G], ref)
         _say("sample out err", f"{err:.2e}")
+
+
+def test_tail_ring_policy_flush_and_decode():
+    """The library's recent-token ring: tokens enter an fp16 ring (each at its
+    ring slot and its mirror, tq_tail_append), tq_tail_policy decides when the
+    oldest whole 32-token blocks move to the packed cache (min_compress_tokens,
+    keep_recent) and tq_tail_flush moves them from their fp16 values.  Three
+    sequences (prefills of 300, 40 and 0 tokens) run 150 steps, so the rings
+    wrap; the decode over packed part + ring range (one contiguous range even
+    when it wraps) is checked against the oracle on the GPU's caches, the ring
+    ranges against the tokens they should hold, and at the end every moved
+    token's record against the oracle's compression of its fp16 values."""
+    import kv_cache_quantization_norm_amd as tq
+    _say("tail ring")
+    L, H, HQ, B, R, steps = 2, 2, 14, 3, 96, 150
+    min_compress, keep = 64, 16
+    P0 = (300, 40, 0)
+    span = 1024                      # packed slots per sequence
+    fmt, fmt16 = quant.Format(128, 4, 4), quant.Format(128, 0, 0)
+    tfmt, tfmt16 = pu.tq_format(fmt), pu.tq_format(fmt16)
+    tables = tq.Tables.create(tfmt, list(range(L)))
+    g = torch.Generator().manual_seed(41)
+    K = torch.randn(L, B, max(P0) + steps, H, 128, generator=g).to("cuda", torch.float16)
+    V = torch.randn(L, B, max(P0) + steps, H, 128, generator=g).to("cuda", torch.float16)
+    Q = torch.randn(L, B, HQ, 128, generator=g).cuda()
+    packed = tq.Cache.allocate(tfmt, L, H, B * span)
+    tails = [tq.Cache.allocate(tfmt16, L, H, 2 * R) for _ in range(B)]   # one ring per sequence
+    n_packed, head, n_tail, n_seen = [0] * B, [0] * B, [0] * B, list(P0)
+    # prefill: what the policy would move goes to the packed cache, the rest into the ring
+    for b in range(B):
+        m = int(tq.tq_tail_policy([0], [P0[b]], min_compress, keep)[0])
+        if m:
+            tq.tq_compress_kv(tfmt, tables, packed, K[:, b, :m].contiguous(), V[:, b, :m].contiguous(), slot0=b * span)
+        n_packed[b] = m
+        rest = P0[b] - m
+        if rest:
+            rs = torch.arange(rest, dtype=torch.int64, device="cuda") % R
+            tq.tq_tail_append(tfmt16, tables, tails[b], K[:, b, m:P0[b]].contiguous(), V[:, b, m:P0[b]].contiguous(), rs, R)
+        n_tail[b] = rest
+    ws_flush = tq.tail_flush_workspace_for(tfmt, packed, 1, R)
+    ws = tq.tail_workspace_for(tfmt, packed, 1, HQ, span, R)
+    out = torch.empty(L, 1, HQ, 128, device="cuda")
+    flushes, wraps, checks = 0, 0, 0
+    for step in range(steps):
+        for b in range(B):
+            tok = n_seen[b]
+            rs = torch.tensor([(head[b] + n_tail[b]) % R], dtype=torch.int64, device="cuda")
+            tq.tq_tail_append(tfmt16, tables, tails[b], K[:, b, tok:tok + 1].contiguous(),
+                              V[:, b, tok:tok + 1].contiguous(), rs, R)
+            n_seen[b] += 1
+            n_tail[b] += 1
+        nf = tq.tq_tail_policy(n_packed, n_tail, min_compress, keep)
+        for b in range(B):
+            if nf[b] == 0:
+                continue
+            assert nf[b] % 32 == 0 and n_tail[b] - nf[b] >= keep
+            one = lambda x, dt: torch.tensor([x], dtype=dt, device="cuda")
+            tq.tq_tail_flush(tfmt, tables, packed, tails[b], R, one(head[b], torch.int64), one(int(nf[b]), torch.int32),
+                             one(b * span + n_packed[b], torch.int64), ws_flush)
+            n_packed[b] += int(nf[b])
+            wraps += head[b] + int(nf[b]) >= R
+            head[b] = (head[b] + int(nf[b])) % R
+            n_tail[b] -= int(nf[b])
+            flushes += 1
+        if step % 29 == 0 or step == steps - 1:
+            torch.cuda.synchronize()
+            ora = pu.download_cache(packed, fmt)
+            for b in range(B):
+                ora_t = pu.download_cache(tails[b], fmt16)
+                # the ring range holds the sequence's last n_tail tokens, in order
+                got_k = np.stack([ora_t[layer]["k_f16"][:, head[b]:head[b] + n_tail[b]] for layer in range(L)])
+                want_k = K[:, b, n_seen[b] - n_tail[b]:n_seen[b]].permute(0, 2, 1, 3).cpu().numpy()
+                assert np.array_equal(got_k, want_k)
+                st = torch.tensor([b * span], dtype=torch.int64, device="cuda")
+                ln = torch.tensor([n_packed[b]], dtype=torch.int32, device="cuda")
+                tst = torch.tensor([head[b]], dtype=torch.int64, device="cuda")
+                tln = torch.tensor([n_tail[b]], dtype=torch.int32, device="cuda")
+                tq.tq_decode_attention_tail(tfmt, tables, packed, tails[b], Q[:, b:b + 1].contiguous(), st, ln, span,
+                                            tst, tln, R, out, ws)
+                torch.cuda.synchronize()
+                for layer in range(L):
+                    pi, s, cbk, cbv = pu.oracle_tables(fmt, layer)
+                    ref = attention.decode_attention_with_tail(ora[layer], ora_t[layer], Q[layer, b:b + 1].cpu().numpy(),
+                                                               [b * span], [n_packed[b]], [head[b]], [n_tail[b]],
+                                                               pi, s, cbk, cbv)
+                    pu.check_outputs(out[layer].cpu().numpy(), ref)
+            checks += 1
+    _say("flushes", flushes, "wraps", wraps, "packed", n_packed, "tail", n_tail)
+    assert flushes >= 8 and wraps >= 2 and checks >= 5
+    # every moved token's record against the oracle's compression of its fp16 values
+    gpu = pu.download_cache(packed, fmt)
+    kh, vh = K.cpu().numpy().astype(np.float64), V.cpu().numpy().astype(np.float64)
+    for layer in range(L):
+        pi, s, cbk, cbv = pu.oracle_tables(fmt, layer)
+        ora = quant.empty_cache(fmt, H, B * span)
+        slots = np.concatenate([b * span + np.arange(n_packed[b]) for b in range(B)])
+        kk = np.concatenate([kh[layer, b, :n_packed[b]] for b in range(B)])
+        vv = np.concatenate([vh[layer, b, :n_packed[b]] for b in range(B)])
+        det = quant.compress_into(ora, kk, vv, slots, pi, s, cbk, cbv)
+        det["keys"] = kk
+        pu.compare_layer(gpu[layer], ora, det, fmt, slots, layer)
