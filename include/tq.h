@@ -419,6 +419,20 @@ tq_status tq_score(const tq_format* fmt, const tq_tables* tables, const tq_cache
                    const int32_t* seq_len, int64_t max_seq_len, float scale, float* logits,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Device.  tq_score for many query rows per KV head (a prefill chunk's
+ * queries against the compressed cache: the pages' separate MSE-score and
+ * QJL-score kernels, QJL deep-dive section 6, with the query rows as the
+ * columns of one contraction).  Same arguments, logits and workspace as
+ * tq_score; query rows are heads, n_q_heads / n_kv_heads (G) of them per KV
+ * head, e.g. 8 heads x 8 query tokens.  Where tq_score's kernel reads and
+ * decodes a KV head's codes once per 8 rows, this one does once per 64 rows
+ * (rows 64 g .. 64 g + 63 of a KV head per pass), its scores on fp16 MFMA
+ * with the same operand precision. */
+tq_status tq_score_multi(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, const float* q,
+                         int32_t batch, int32_t n_q_heads, const int64_t* seq_start, const int32_t* seq_len,
+                         int64_t max_seq_len, float scale, float* logits, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* Bytes of the static device scratch of tq_decode_attention_noalloc. */
 #define TQ_NOALLOC_SCRATCH_BYTES (64u << 20)
 

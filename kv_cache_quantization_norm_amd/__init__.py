@@ -82,6 +82,7 @@ def _load(path: str = LIB_PATH):
         "tq_decode_attention": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P, SZ, P]),
         "tq_decode_attention_noalloc": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P]),
         "tq_score": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P, SZ, P]),
+        "tq_score_multi": (I32, [fmtp, tabp, cachep, P, I32, I32, P, P, I64, F32, P, P, SZ, P]),
         "tq_decode_prepare": (I32, [fmtp, tabp, cachep, P, I32, I32, I64, P, SZ, P]),
         "tq_append_prepare": (I32, [fmtp, tabp, cachep, P, P, I32, I32, I32, I64, P, I64, P, I32, I32, I64, P, SZ,
                                     P]),
@@ -115,7 +116,7 @@ EXPORTED = ("tq_layer_seed", "tq_make_rotations", "tq_make_codebook", "tq_cache_
             "tq_append_prepare",
             "tq_compress_kv_bounded", "tq_decode_attention_tail", "tq_decode_tail_workspace_bytes",
             "tq_decode_attention_noalloc", "tq_decode_step_check", "tq_set_append_wait", "tq_fp16_operand_scale",
-            "tq_tail_policy", "tq_tail_append", "tq_tail_flush_workspace_bytes", "tq_tail_flush",
+            "tq_tail_policy", "tq_tail_append", "tq_tail_flush_workspace_bytes", "tq_tail_flush", "tq_score_multi",
             "tq_status_string", "tq_last_error")
 
 
@@ -628,6 +629,19 @@ def tq_score(fmt: tq_format, tables: Tables, cache: Cache, q, seq_start, seq_len
     tb, cs = tables.struct(), cache.struct()
     _check(_lib.tq_score(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), pq, batch, hq, ps, pl, max_seq_len,
                          scale, plg, pw, nw, _stream(stream)), "tq_score")
+
+
+def tq_score_multi(fmt: tq_format, tables: Tables, cache: Cache, q, seq_start, seq_len, max_seq_len: int, logits,
+                   workspace, scale: float = 0.0, stream=None):
+    """tq_score with the multi-query kernel (64 query rows per pass over a KV
+    head's codes); logits: device float32 [n_layers][batch][n_q_heads][max_seq_len]."""
+    pq, batch, hq = _q(fmt, cache, q)
+    ps, pl = _seq(seq_start, seq_len, batch)
+    plg = _dev(logits, _f32(), (cache.n_layers, batch, hq, max(max_seq_len, 1)), "logits")
+    pw, nw = _ws(workspace)
+    tb, cs = tables.struct(), cache.struct()
+    _check(_lib.tq_score_multi(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), pq, batch, hq, ps, pl,
+                               max_seq_len, scale, plg, pw, nw, _stream(stream)), "tq_score_multi")
 
 
 def raw_call(name: str, *args):

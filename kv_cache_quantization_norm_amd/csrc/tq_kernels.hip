@@ -2683,6 +2683,283 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }
 }
 
+// ===========================================================================
+// Multi-query scores
+
+// Query rows per pass of the multi-query score kernel over a KV head's codes:
+// 8 MFMA column blocks of 8 rows (fp16 high parts in columns 0..7, their
+// remainders in columns 8..15, as in decode).
+constexpr int kMultiRows = 64;
+constexpr int kMultiWaves = 8;
+
+// Multi-query scores (a prefill chunk's query rows scored against the
+// cache): problem p = ((layer * batch + b) * H + hk) * n_rg + rg holds rows
+// [64 rg, 64 rg + 64) of the KV head's G query rows.  Workgroup w takes the
+// chunks [w a.chunks_per_wg, + a.chunks_per_wg) of the problem-major chunk
+// sequence (a.chunks_per_problem per problem): it builds its tables once,
+// stages each problem's query operands in LDS, and its 8 waves take the
+// problem's chunks round robin, one chunk loaded ahead.  Per 32-wide step a
+// wave forms the key operands of its chunk once (the decode kernel's table
+// lookups) and multiplies them with the 8 column blocks' query operands, so a
+// KV head's codes are read and decoded once per 64 rows (the decode kernel's
+// scoring takes 8 rows per pass).  Logits as in tq_score (natural units;
+// positions past the sequence untouched).
+template <int MK>
+__global__ __launch_bounds__(kMultiWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void score_multi_kernel(
+    DecodeArgs a, int n_rg) {
+  constexpr bool KWIDE = MK > 4;
+  constexpr bool KSPLIT = MK > 0 && key_split(MK);
+  using KL = KLut<(MK > 0 && !KWIDE ? MK : 1)>;
+  constexpr int NT = kMultiWaves * 64;
+  constexpr int KT = MK > 0 ? (KWIDE ? (1 << MK) : KL::E * KL::EW) : 1;
+  constexpr int KP = MK > 0 && !KWIDE && KL::NC > 2 ? KL::PAIRS * KL::PW : 1;
+  constexpr int OFF_S = 0;
+  constexpr int OFF_K = MK > 0 ? 256 * 16 : 0;
+  constexpr int OFF_PHI = OFF_K + KT * 4;
+  constexpr int OFF_Q = ((OFF_PHI + KP * 4 + 255) / 256) * 256;
+  constexpr int NQ = 8 * 2 * 4 * 64;   // staged query operands [block][r / z][step][lane]
+  constexpr int LDS_BYTES = OFF_Q + NQ * 16;
+  static_assert(OFF_K < 65536, "the key table must start below 64 KB");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
+  __shared__ __align__(256) unsigned char dsm[LDS_BYTES];
+  uint32_t* const lut_k = reinterpret_cast<uint32_t*>(dsm + OFF_K);
+  uint32_t* const pair_hi = reinterpret_cast<uint32_t*>(dsm + OFF_PHI);
+  uint32_t* const lut_s = reinterpret_cast<uint32_t*>(dsm + OFF_S);
+  half8* const qst = reinterpret_cast<half8*>(dsm + OFF_Q);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, q = lane >> 4;
+  const int cpp = a.chunks_per_problem;
+  const int g_lo = int(blockIdx.x) * a.chunks_per_wg;
+  const int g_hi = g_lo + a.chunks_per_wg < a.total_chunks ? g_lo + a.chunks_per_wg : a.total_chunks;
+
+  constexpr bool KSCALED = MK > 0 && !KSPLIT;
+  const float alpha_k = KSCALED ? a.alpha_k : 1.f;
+  const float kscale_k = a.scale / alpha_k, kscale_r = a.scale * a.kappa;
+  // ---- tables (as in decode)
+  if constexpr (KWIDE) {
+    for (int x = tid; x < (1 << MK); x += NT) {
+      const float c = a.kc[x];
+      const uint16_t h = f16_bits(c);
+      reinterpret_cast<uint16_t*>(lut_k)[x] = h;
+      reinterpret_cast<uint16_t*>(lut_k)[(1 << MK) + x] = f16_bits(c - float(__builtin_bit_cast(_Float16, h)));
+    }
+  } else if constexpr (MK > 0) {
+    const float kcl = a.kc[lane & ((1 << MK) - 1)] * alpha_k;
+    if constexpr (KL::NC > 2)
+      build_kpairs<MK>(pair_hi, kcl, tid, NT);
+    else
+      build_kpairs<MK>(lut_k, kcl, tid, NT);
+  }
+  if constexpr (MK > 0) {
+    for (int x = tid; x < 256; x += NT) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t lo = ((x >> e) & 1) ? 0x3C00u : 0xBC00u;
+        const uint32_t hi = ((x >> (e + 1)) & 1) ? 0x3C00u : 0xBC00u;
+        lut_s[x * 4 + e / 2] = lo | (hi << 16);
+      }
+    }
+  }
+  __syncthreads();
+  if constexpr (MK > 0 && !KWIDE && KL::NC > 2) {
+    build_ktab<MK, NT>(lut_k, pair_hi, tid);
+    __syncthreads();
+  }
+
+  // the current problem: its query rows, sequence length, first slot and logits row
+  int rows = 0;
+  int64_t len = 0, slot_base = 0, out_row0 = 0;
+
+  // ---- chunk data of one lane (tile T row col -> token 8 (col / 4) + 4 T + col % 4)
+  constexpr int KREC = MK > 0 ? 16 * MK : 2 * D;
+  constexpr int MKW = MK > 0 ? MK : 1;
+  struct KData {
+    uint32_t kw[2][MKW];
+    uint32_t sg[2];
+    half8 kf[MK > 0 ? 1 : 2][MK > 0 ? 1 : 4];
+    float kn[MK > 0 ? 8 : 1], rn[MK > 0 ? 8 : 1];   // norms of tokens 8 q .. 8 q + 7
+  };
+  uint32_t koff[2], soff[2];
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    const uint32_t tk = 8 * (col >> 2) + 4 * T + (col & 3);
+    koff[T] = tk * KREC + 4 * q * MKW;
+    soff[T] = tk * 16 + 4 * q;
+  }
+  auto load_k = [&](int c, KData& K) {
+    const int64_t slot0 = slot_base + int64_t(c) * kChunk;
+    if constexpr (MK == 0) {
+      const auto kr = chunk_rsrc(a.k_f16 + slot0 * D, kChunk * 2 * D);
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        const uint32_t off = (8 * (col >> 2) + 4 * T + (col & 3)) * (2 * D) + 64 * q;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) K.kf[T][s2] = bload<half8>(kr, off + 16 * s2);
+      }
+    } else {
+      const auto kr = chunk_rsrc(a.k_idx + slot0 * KREC, kChunk * KREC);
+      const auto sr = chunk_rsrc(a.k_sign + slot0 * 16, kChunk * 16);
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+#pragma unroll
+        for (int u = 0; u < MK; ++u) K.kw[T][u] = bload<uint32_t>(kr, koff[T] + 4 * u);
+        K.sg[T] = bload<uint32_t>(sr, soff[T]);
+      }
+      const auto nr = chunk_rsrc(a.k_norm + slot0, kChunk * 4), rr = chunk_rsrc(a.k_rnorm + slot0, kChunk * 4);
+#pragma unroll
+      for (int h4 = 0; h4 < 2; ++h4) {
+        const floatx4 n4 = bload<floatx4>(nr, 32 * q + 16 * h4), r4 = bload<floatx4>(rr, 32 * q + 16 * h4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          K.kn[4 * h4 + e] = n4[e];
+          K.rn[4 * h4 + e] = r4[e];
+        }
+      }
+    }
+  };
+
+  floatx4 sm[8][2], sq[MK > 0 ? 8 : 1][2];
+  auto compute = [&](const KData& K, int c) {
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        sm[cb][T] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (MK > 0) sq[cb][T] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      half8 kh[2], kl[2], sd[2];
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        if constexpr (MK == 0) {
+          kh[T] = K.kf[T][s2];
+        } else {
+          if constexpr (KWIDE)
+            deq8_wide<MK>(K.kw[T], s2, reinterpret_cast<const uint16_t*>(lut_k), kh[T], kl[T]);
+          else
+            deq8_k<MK>(slab_bits<MK>(K.kw[T], s2), lut_k, kh[T], kl[T]);
+          sd[T] = *reinterpret_cast<const half8*>(lut_s + ((K.sg[T] >> (8 * s2)) & 0xFFu) * 4);
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        if (cb * 8 < rows) {   // uniform
+          const half8 qr = qst[((cb * 2 + 0) * 4 + s2) * 64 + lane];
+#pragma unroll
+          for (int T = 0; T < 2; ++T) {
+            sm[cb][T] = mfma16x16x32(kh[T], qr, sm[cb][T]);
+            if constexpr (KSPLIT) sm[cb][T] = mfma16x16x32(kl[T], qr, sm[cb][T]);
+          }
+          if constexpr (MK > 0) {
+            const half8 qz = qst[((cb * 2 + 1) * 4 + s2) * 64 + lane];
+#pragma unroll
+            for (int T = 0; T < 2; ++T) sq[cb][T] = mfma16x16x32(sd[T], qz, sq[cb][T]);
+          }
+        }
+      }
+    }
+    // ---- logits: lane (col, q) holds tokens 8 q + e (e = 4 T + i) of column col
+    const int64_t crel = int64_t(c) * kChunk;
+    const int rem = int(len - crel > kChunk ? kChunk : len - crel) - 8 * q;
+    float kn[8], rn[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kn[e] = MK > 0 ? K.kn[MK > 0 ? e : 0] : 1.f;
+      rn[e] = MK > 0 ? K.rn[MK > 0 ? e : 0] : 0.f;
+    }
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      if (cb * 8 < rows) {
+        float lg[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float smv = sm[cb][e >> 2][e & 3];
+          float t = smv;
+          if constexpr (MK > 0) t = fmaf(kn[e], smv, rn[e] * sq[cb][e >> 2][e & 3]);
+          lg[e] = t + dpp_f<0x128>(t);   // high part + remainder part (row rotate by 8)
+        }
+        if (col < 8 && cb * 8 + col < rows) {
+          float* out = a.logits + out_row0 + int64_t(cb * 8 + col) * a.max_len + crel + 8 * q;
+          if (rem >= 8 && ((a.max_len & 3) == 0)) {   // 16-byte aligned rows: two vector stores
+            *reinterpret_cast<float4*>(out) = float4{lg[0], lg[1], lg[2], lg[3]};
+            *reinterpret_cast<float4*>(out + 4) = float4{lg[4], lg[5], lg[6], lg[7]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (e < rem) out[e] = lg[e];
+          }
+        }
+      }
+    }
+  };
+
+  // ---- query operands: item ((cb * 2 + kind) * 4 + s) * 64 + l; lane (col,
+  // q') of block cb, step s holds coordinates 32 q' + 8 s + e of row 8 cb +
+  // col % 8 of Pi q * scale / alpha_k (kind 0) or S q * scale * kappa (kind 1)
+  auto stage = [&](int layer, int b, int hk, int rg, int rows) {
+  for (int it = tid; it < NQ; it += NT) {
+    const int l = it & 63, s4 = (it >> 6) & 3, kind = (it >> 8) & 1, cb = it >> 9;
+    const int r = cb * 8 + (l & 7);
+    const bool ok = r < rows && (MK > 0 || kind == 0);
+    const int h = hk * a.G + rg * kMultiRows + (ok ? r : 0);
+    const float* src =
+        a.qprep + ((int64_t(layer) * a.batch + b) * a.Hq + h) * 2 * D + kind * D + 32 * (l >> 4) + 8 * s4;
+    const float sc = ok ? (kind ? kscale_r : kscale_k) : 0.f;
+    const bool lo = (l & 15) >= 8;
+    half8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = src[e] * sc;
+      const _Float16 xh = _Float16(x);
+      o[e] = lo ? _Float16(x - float(xh)) : xh;
+    }
+    qst[it] = o;
+  }
+  };
+
+  KData K0, K1;
+#pragma unroll 1
+  for (int g = g_lo; g < g_hi;) {
+    const int prob = g / cpp;
+    const int seg_hi = (prob + 1) * cpp < g_hi ? (prob + 1) * cpp : g_hi;
+    const int rg = prob % n_rg, hk = (prob / n_rg) % a.H, b = (prob / (n_rg * a.H)) % a.batch;
+    const int layer = prob / (n_rg * a.H * a.batch);
+    rows = a.G - rg * kMultiRows < kMultiRows ? a.G - rg * kMultiRows : kMultiRows;
+    // the sequence, with decode's rules (misaligned or negative starts empty)
+    int64_t start = a.seq_start[b];
+    len = a.seq_len[b];
+    if (start < 0 || (start % kVBlock) != 0 || start >= a.capacity || len < 0) {
+      len = 0;
+      start = 0;
+    }
+    if (len > a.capacity - start) len = a.capacity - start;
+    if (len > a.max_len) len = a.max_len;
+    slot_base = (int64_t(layer) * a.H + hk) * a.capacity + start;
+    out_row0 = ((int64_t(layer) * a.batch + b) * a.Hq + hk * a.G + rg * kMultiRows) * a.max_len;
+    const int n_chunks = int((len + kChunk - 1) / kChunk);
+    const int c0 = g - prob * cpp, c1 = seg_hi - prob * cpp < n_chunks ? seg_hi - prob * cpp : n_chunks;
+    g = seg_hi;
+    if (c0 >= c1) continue;   // uniform over the workgroup
+    __syncthreads();          // the previous problem's operands are no longer read
+    stage(layer, b, hk, rg, rows);
+    __syncthreads();
+    int c = c0 + wave;
+    if (c < c1) load_k(c, K0);
+#pragma unroll 1
+    for (; c < c1; c += 2 * kMultiWaves) {
+      const int cn = c + kMultiWaves;
+      if (cn < c1) load_k(cn, K1);
+      compute(K0, c);
+      if (cn >= c1) break;
+      if (cn + kMultiWaves < c1) load_k(cn + kMultiWaves, K0);
+      compute(K1, cn);
+    }
+  }
+}
+
 template <bool SCORE>
 tq_status launch_decode(int mk, int bv, const DecodeArgs& args, dim3 grid, hipStream_t st,
                         const CompressArgs& ca = CompressArgs{}) {
@@ -3472,6 +3749,53 @@ tq_status tq_decode_combine(const tq_format* fmt, const tq_tables* tables, const
                             size_t workspace_bytes, void* stream) {
   return tq::decode_common<false>(fmt, tables, cache, nullptr, batch, n_q_heads, nullptr, nullptr, max_seq_len, 0.f,
                                   out, workspace, workspace_bytes, stream, tq::kStageCombine);
+}
+
+tq_status tq_score_multi(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache, const float* q,
+                         int32_t batch, int32_t n_q_heads, const int64_t* seq_start, const int32_t* seq_len,
+                         int64_t max_seq_len, float scale, float* logits, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  using namespace tq;
+  clear_error();
+  // the checks and the query preparation of tq_score
+  tq_status st = decode_common<true>(fmt, tables, cache, q, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale,
+                                     logits, workspace, workspace_bytes, stream, kStagePrepare | kStagePartials |
+                                                                                     kStageCheckOnly);
+  if (st) return st;
+  if (!seq_start || !seq_len) return fail(TQ_ERR_INVALID_ARG, "seq_start/seq_len is NULL");
+  st = decode_common<true>(fmt, tables, cache, q, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, logits,
+                           workspace, workspace_bytes, stream, kStagePrepare);
+  if (st || max_seq_len == 0) return st;
+  const int G = n_q_heads / cache->n_kv_heads;
+  const int n_rg = (G + kMultiRows - 1) / kMultiRows;
+  const int64_t problems = int64_t(cache->n_layers) * batch * cache->n_kv_heads * n_rg;
+  const int64_t cpp = (max_seq_len + kChunk - 1) / kChunk;
+  const int64_t total = problems * cpp;
+  if (total > (int64_t(1) << 30)) return fail(TQ_ERR_INVALID_ARG, "too many 32-token chunks in one call");
+  const int mk = fmt->k_bits > 0 ? fmt->k_bits - 1 : 0;
+  // the workgroups one launch keeps resident (one per CU with the 64 KB key
+  // table of 3-bit codes, else two), each with at least one chunk per wave
+  const int64_t resident = int64_t(kDecodeWorkgroups) * (mk == 3 ? 1 : 2);
+  int64_t wgs = (total + kMultiWaves - 1) / kMultiWaves;
+  if (wgs > resident) wgs = resident;
+  const int64_t cpw = (total + wgs - 1) / wgs;
+  wgs = (total + cpw - 1) / cpw;
+  const SplitPlan plan = plan_decode(fmt->d, cache->n_layers, batch, cache->n_kv_heads, n_q_heads, max_seq_len);
+  DecodeArgs a = make_args(fmt, tables, cache, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, plan,
+                           static_cast<const float*>(workspace), nullptr, logits);
+  a.chunks_per_problem = int(cpp);
+  a.total_chunks = int(total);
+  a.chunks_per_wg = int(cpw);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(wgs));
+#define TQ_SM(MK_)                                                                                   \
+  if (mk == MK_) {                                                                                   \
+    hipLaunchKernelGGL((score_multi_kernel<MK_>), grid, dim3(kMultiWaves * 64), 0, hs, a, n_rg);     \
+    return launch_status("score (multi-query)");                                                     \
+  }
+  TQ_SM(0) TQ_SM(1) TQ_SM(2) TQ_SM(3) TQ_SM(4) TQ_SM(7)
+#undef TQ_SM
+  return fail(TQ_ERR_UNSUPPORTED, "no multi-query score kernel for key bits %d", mk);
 }
 
 tq_status tq_score(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,

@@ -879,3 +879,56 @@ def test_tail_ring_policy_flush_and_decode():
         det = quant.compress_into(ora, kk, vv, slots, pi, s, cbk, cbv)
         det["keys"] = kk
         pu.compare_layer(gpu[layer], ora, det, fmt, slots, layer)
+
+
+MULTI_CASES = {
+    # 64 query rows per KV head (8 heads x 8 query tokens), two sequences
+    "k4v4_g64": wl.Workload("k4v4_g64", 1, 2, 128, (700, 333), 4, 4, "bf16", 0.5, 2, 10.0),
+    # 128 rows per KV head: two passes over the codes
+    "k3v2_g128": wl.Workload("k3v2_g128", 1, 1, 128, (500,), 3, 2, "bf16", 0.5, 0, 1.0),
+    # 72 rows: a full pass and a pass of one column block
+    "k2v2_g72": wl.Workload("k2v2_g72", 1, 1, 72, (129, 0), 2, 2, "f32", 0.0, 0, 1.0),
+    # fp16 keys, 20 rows (partly filled column blocks), ragged
+    "k0v4_g20": wl.Workload("k0v4_g20", 2, 2, 40, (257, 31), 0, 4, "bf16", 0.5, 1, 10.0),
+    # the wide key codes
+    "k8v4_g64": wl.Workload("k8v4_g64", 1, 1, 64, (300,), 8, 4, "bf16", 0.5, 1, 10.0),
+    "k5v1_g64": wl.Workload("k5v1_g64", 1, 1, 64, (96,), 5, 1, "f16", 0.3, 1, 5.0),
+}
+
+
+@pytest.mark.parametrize("case", list(MULTI_CASES))
+def test_score_multi_on_oracle_cache(case):
+    """tq_score_multi (64 query rows per pass over a KV head's codes) against
+    the oracle's logits on the oracle's own packed cache, and against
+    tq_score's kernel (8 rows per pass) on the same inputs."""
+    import kv_cache_quantization_norm_amd as tq
+    w = MULTI_CASES[case]
+    _say("multi-query scores", case)
+    for fmt, layers in pu.layer_groups(w):
+        tables, _, ora_caches, _, (starts, lens, cap, slots) = _run_group(w, fmt, layers, dev_compress=False)
+        dev = pu.upload_cache(ora_caches, fmt)
+        Q = np.stack([wl.gen_q(w, layer) for layer in layers])
+        tfmt = pu.tq_format(fmt)
+        n_layers, batch, hq, _ = Q.shape
+        max_len = int(max(lens))
+        qt = torch.from_numpy(Q).cuda().contiguous()
+        st = torch.from_numpy(np.asarray(starts, np.int64)).cuda()
+        ln = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+        ws = tq.workspace_for(tfmt, dev, batch, hq, max_len)
+        multi = torch.full((n_layers, batch, hq, max_len), float("nan"), device="cuda")
+        tq.tq_score_multi(tfmt, tables, dev, qt, st, ln, max_len, multi, ws)
+        single = torch.full_like(multi, float("nan"))
+        tq.tq_score(tfmt, tables, dev, qt, st, ln, max_len, single, ws)
+        torch.cuda.synchronize()
+        multi, single = multi.cpu().numpy(), single.cpu().numpy()
+        for i, layer in enumerate(layers):
+            pi, s, cbk, cbv = pu.oracle_tables(fmt, layer)
+            _, ref_logits = attention.decode_attention(ora_caches[i], Q[i], starts, lens, pi, s, cbk, cbv,
+                                                       return_logits=True)
+            worst = pu.check_logits(multi[i], ref_logits, lens, hq)
+            for b, n in enumerate(lens):
+                assert np.all(np.isnan(multi[i, b, :, n:])), "positions past the sequence are left untouched"
+                if n:
+                    scale = np.max(np.abs(single[i, b, :, :n]))
+                    assert np.max(np.abs(multi[i, b, :, :n] - single[i, b, :, :n])) <= 1e-5 * scale
+            _say("format", fmt, "layer", layer, "worst logit rel", f"{worst:.2e}")
