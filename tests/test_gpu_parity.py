@@ -732,36 +732,9 @@ def test_background_recompression_on_second_stream():
         assert float((o - ref_out).abs().max()) <= 1e-5 * scale
 
 
-@pytest.mark.parametrize("short", ["w2", "w4"])
-def test_full_size_sampled(short):
-    """Full workload size in the benchmark's launch configuration (every layer in
-    one compress call and one decode call); the oracle recomputes sampled
-    (layer, KV head) pairs end to end."""
-    import kv_cache_quantization_norm_amd as tq
-    w = wl.BY_SHORT[short]
-    _say("full-size", w.name)
-    fmt, layers = pu.layer_groups(w)[0]
-    starts, lens, cap, slots = pu.slots_of(w)
-    tfmt = pu.tq_format(fmt)
-    tables = tq.Tables.create(tfmt, layers)
-    dev = tq.Cache.allocate(tfmt, len(layers), w.n_kv_heads, cap)
-    dt = _torch_dtype(w)
-    rs = np.random.default_rng(1)
-    samples = [(int(rs.integers(len(layers))), int(rs.integers(w.n_kv_heads))) for _ in range(2)]
-    sampled_inputs = {}
-    for i, layer in enumerate(layers):
-        k, v = wl.gen_kv(w, layer)
-        heads = [kvh for li, kvh in samples if li == i]
-        if heads:
-            # sampled heads: no decision within 1e-6 of its threshold (see test_end_to_end)
-            k, v, n = pu.sanitize_near_boundary(fmt, layer, k, v, heads=heads)
-            _say("layer", layer, "heads", heads, "zeroed", n)
-            sampled_inputs[i] = (k, v)
-        kt = torch.from_numpy(k).to("cuda", dt)[None].contiguous()
-        vt = torch.from_numpy(v).to("cuda", dt)[None].contiguous()
-        tq.tq_compress_kv(tfmt, tables, dev, kt, vt, layer0=i, slot0=0)
-    Q = np.stack([wl.gen_q(w, layer) for layer in layers])
-    out, _ = _decode_gpu(fmt, tables, dev, Q, starts, lens, want_logits=False)
+def _check_sampled_heads(w, fmt, layers, dev, samples, sampled_inputs, slots, cap, out, Q, starts, lens):
+    """The oracle's compression and decode of sampled (layer, KV head) pairs
+    against the device cache and decode outputs."""
     G = w.group
     for li, kvh in samples:
         layer = layers[li]
@@ -773,11 +746,74 @@ def test_full_size_sampled(short):
         sub = {n: (a[kvh:kvh + 1] if isinstance(a, np.ndarray) else a) for n, a in gl.items()}
         sub["n_kv_heads"] = 1
         st = pu.compare_layer(sub, c, det, fmt, slots, layer)
-        _say("sample", layer, kvh, st)
-        qh = Q[li][:, kvh * G:(kvh + 1) * G]
-        ref = attention.decode_attention(c, qh, starts, lens, pi, s, cbk, cbv)
-        err = pu.check_outputs(out[li][:, kvh * G:(kvh + 1) * G], ref)
-        _say("sample out err", f"{err:.2e}")
+        _say("sample", fmt, layer, kvh, st)
+        if out is not None:
+            qh = Q[li][:, kvh * G:(kvh + 1) * G]
+            ref = attention.decode_attention(c, qh, starts, lens, pi, s, cbk, cbv)
+            err = pu.check_outputs(out[li][:, kvh * G:(kvh + 1) * G], ref)
+            _say("sample out err", f"{err:.2e}")
+
+
+@pytest.mark.parametrize("short", ["w2", "w3", "w4", "w5"])
+def test_full_size_sampled(short):
+    """Full workload size in the benchmark's launch configuration (each
+    storage format's layers in one cache and one decode call; a ragged batch
+    compressed through a slot list); the oracle recomputes sampled (layer, KV
+    head) pairs end to end in every format group (the 28-layer asymmetric
+    workload: fp16 boundary layers and fp16-key / 4-bit-value layers).  The
+    16-sequence workload also compresses its 32768-token prefill of 8 KV heads
+    in one bulk call, checked on sampled heads."""
+    import kv_cache_quantization_norm_amd as tq
+    w = wl.BY_SHORT[short]
+    _say("full-size", w.name)
+    starts, lens, cap, slots = pu.slots_of(w)
+    dt = _torch_dtype(w)
+    rs = np.random.default_rng(1)
+    groups = pu.layer_groups(w)
+    n_samples = 2 if len(groups) == 1 else 1
+    st = torch.from_numpy(slots).cuda()
+    for fmt, layers in groups:
+        tfmt = pu.tq_format(fmt)
+        tables = tq.Tables.create(tfmt, layers)
+        dev = tq.Cache.allocate(tfmt, len(layers), w.n_kv_heads, cap)
+        samples = [(int(rs.integers(len(layers))), int(rs.integers(w.n_kv_heads))) for _ in range(n_samples)]
+        sampled_inputs = {}
+        for i, layer in enumerate(layers):
+            k, v = wl.gen_kv(w, layer)
+            heads = [kvh for li, kvh in samples if li == i]
+            if heads:
+                # sampled heads: no decision within 1e-6 of its threshold (see test_end_to_end)
+                k, v, n = pu.sanitize_near_boundary(fmt, layer, k, v, heads=heads)
+                _say("layer", layer, "heads", heads, "zeroed", n)
+                sampled_inputs[i] = (k, v)
+            kt = torch.from_numpy(k).to("cuda", dt)[None].contiguous()
+            vt = torch.from_numpy(v).to("cuda", dt)[None].contiguous()
+            if len(w.seq_lens) == 1:
+                tq.tq_compress_kv(tfmt, tables, dev, kt, vt, layer0=i, slot0=int(starts[0]))
+            else:
+                tq.tq_compress_kv(tfmt, tables, dev, kt, vt, layer0=i, slots=st)
+            del kt, vt
+        Q = np.stack([wl.gen_q(w, layer) for layer in layers])
+        out, _ = _decode_gpu(fmt, tables, dev, Q, starts, lens, want_logits=False)
+        _check_sampled_heads(w, fmt, layers, dev, samples, sampled_inputs, slots, cap, out, Q, starts, lens)
+        del dev
+    if short == "w5":
+        P = 32768
+        pw = w.with_(seq_lens=(P,), name=w.name + "_prefill")
+        fmt, layers = pu.layer_groups(pw)[0]
+        tfmt = pu.tq_format(fmt)
+        tables = tq.Tables.create(tfmt, layers)
+        dev = tq.Cache.allocate(tfmt, 1, pw.n_kv_heads, P)
+        k, v = wl.gen_kv(pw, 0, stream=2)
+        heads = [int(h) for h in rs.choice(pw.n_kv_heads, 2, replace=False)]
+        k, v, n = pu.sanitize_near_boundary(fmt, 0, k, v, heads=heads)
+        _say("prefill heads", heads, "zeroed", n)
+        tq.tq_compress_kv(tfmt, tables, dev, torch.from_numpy(k).to("cuda", dt)[None].contiguous(),
+                          torch.from_numpy(v).to("cuda", dt)[None].contiguous(), slot0=0)
+        torch.cuda.synchronize()
+        pslots = np.arange(P, dtype=np.int64)
+        _check_sampled_heads(pw, fmt, layers, dev, [(0, h) for h in heads], {0: (k, v)}, pslots, P, None, None,
+                             None, None)
 
 
 def test_tail_ring_policy_flush_and_decode():
