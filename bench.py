@@ -13,7 +13,8 @@ Headline workload (config.workload, the largest single-GPU configuration):
       4 fp16 layers, the 24 fp16-K / 4-bit-V layers): 1.29 GB of cache read.
 Reported beside it in the same line, each with its own roofline:
   w4  one layer, 8 KV heads, 64 query heads, 262,144 tokens, K 3 bits (2
-      Lloyd-Max + 1 QJL), V 2 bits;
+      Lloyd-Max + 1 QJL), V 2 bits; with multi-query scores of 64 query rows
+      per KV head over the same cache (tq_score_multi against tq_score);
   w5  16 sequences of ragged length (4,096..32,768), 8 KV heads, 64 query
       heads, K 4 bits, V 4 bits; with the bulk compression of a 32,768-token
       bf16 prefill of all 8 heads (Mtokens/s per KV head), alone and on a
@@ -58,6 +59,11 @@ def kernel_source_digest() -> str:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
+
+
+def traffic_key(short, k_bits, v_bits):
+    """Name of a decode kernel's committed HBM traffic summary."""
+    return f"decode_{short}_k{k_bits}v{v_bits}"
 
 
 def measured_traffic(name):
@@ -221,7 +227,7 @@ def timed(torch, stream, fn, warmup, steps):
     return e0.elapsed_time(e1) / steps
 
 
-def run_workload(tq, torch, w, args, stream, dev):
+def run_workload(tq, torch, w, short, args, stream, dev):
     t0 = time.time()
     parts = build_parts(tq, torch, w, dev)
     total_cache = sum(p.cache.nbytes() for p in parts)
@@ -256,9 +262,44 @@ def run_workload(tq, torch, w, args, stream, dev):
                      "us_per_launch": round(us, 2), "bytes_per_launch": kb,
                      "GBs": round(kb / (us * 1e-6) / 1e9, 1),
                      "frac_of_hbm_peak": round(kb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                     "workgroups": tq.tq_decode_split(p.fmt, p.L, B, H, Hq, p.T)["n_workgroups"]})
+                     "workgroups": tq.tq_decode_split(p.fmt, p.L, B, H, Hq, p.T)["n_workgroups"],
+                     "traffic": measured_traffic(traffic_key(short, p.k_bits, p.v_bits))})
     res["decode_kernels"] = kern
+    dom = max(kern, key=lambda k: k["bytes_per_launch"])
+    res["roofline"] = {"bound": "hbm", "achieved": dom["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": dom["frac_of_hbm_peak"], "traffic": dom["traffic"], "kernel": dom["kernel"]}
     return res, parts
+
+
+def multi_query_scores(tq, torch, p, args, stream, dev, rows=64):
+    """Scores of `rows` query rows per KV head (say 8 heads x 8 query tokens of
+    a prefill chunk) over a workload part's cache: tq_score_multi reads and
+    decodes each KV head's key codes once per 64 rows, tq_score's decode
+    kernel once per 8 rows.  Both include the query preparation."""
+    H = p.cache.n_kv_heads
+    Hq = H * rows
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    q = torch.randn((p.L, p.B, Hq, D), generator=g, device=dev)
+    ws = tq.workspace_for(p.fmt, p.cache, p.B, Hq, p.T, dev)
+    lg = torch.empty((p.L, p.B, Hq, p.T), device=dev)
+    n = len(p.copies)
+    res = {"what": f"{rows} query rows per KV head scored against the cache ({Hq} rows in all)"}
+    for name, fn in (("multi", tq.tq_score_multi), ("decode_kernel_8_rows_per_pass", tq.tq_score)):
+        us = timed(torch, stream, lambda i, fn=fn: fn(p.fmt, p.tables, p.copies[i % n], q, p.seq_start, p.seq_len,
+                                                      p.T, lg, ws, stream=stream), args.warmup, args.steps) * 1e3
+        res[name + "_us"] = round(us, 2)
+    kr, _ = rec_bytes(p.k_bits, p.v_bits)
+    tokens = int(p.seq_len.sum().item())
+    key_bytes = p.L * H * tokens * kr
+    logit_bytes = p.L * Hq * tokens * 4
+    res["key_record_bytes_read_once"] = key_bytes
+    res["key_record_bytes_read_8_rows_per_pass"] = key_bytes * ((rows + 7) // 8)
+    res["logit_bytes_written"] = logit_bytes
+    res["multi_GBs_algorithmic"] = round((key_bytes + logit_bytes) / (res["multi_us"] * 1e-6) / 1e9, 1)
+    res["speedup"] = round(res["decode_kernel_8_rows_per_pass_us"] / res["multi_us"], 3)
+    del lg, ws, q
+    return res
 
 
 def bulk_compress(tq, torch, w, args, stream, dev, decode_parts=None):
@@ -343,8 +384,9 @@ def cpu_baseline(w, budget_s):
     """The float64 oracle decoding a bounded sample of the headline workload:
     whole layers (all KV and query heads, every cached token; the packed layers
     oracle-compressed first, untimed), in layer order, until about budget_s
-    seconds of decode work; then one layer again with the BLAS pool held to
-    one thread."""
+    seconds of decode work; then the slowest of those layers again with the
+    BLAS pool held to one thread (its rate beside the same layer's on all
+    threads)."""
     import workloads as wl
     from oracle import attention, codebook, quant, rotation
     from threadpoolctl import threadpool_info, threadpool_limits
@@ -378,22 +420,25 @@ def cpu_baseline(w, budget_s):
         kr, vr = rec_bytes(fmt.k_bits, fmt.v_bits)
         return dt, w.n_kv_heads * sum(lens) * (kr + vr) + 2 * w.batch * w.n_q_heads * D * 4
 
-    dec_s, nbytes, done = 0.0, 0, []
+    dec_s, nbytes, done, per = 0.0, 0, [], {}
     for layer in range(w.n_layers):
         dt, b = one_layer(layer)
         dec_s += dt
         nbytes += b
         done.append(layer)
+        per[layer] = (dt, b)
         log(f"cpu oracle layer {layer}: {dt:.2f}s (total {dec_s:.1f}s)")
         if dec_s >= budget_s:
             break
+    slow = max(per, key=lambda x: per[x][0])
     with threadpool_limits(limits=1):
-        dt1, b1 = one_layer(done[-1])
+        dt1, b1 = one_layer(slow)
     return {"value": round(nbytes / dec_s / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(done)} of {w.n_layers} layers of {w.name} (layers {done[0]}..{done[-1]}, every KV and "
                       f"query head, every cached token), decode only ({dec_s:.1f}s on {threads} threads)",
             "one_thread_GBs": round(b1 / dt1 / 1e9, 4),
-            "one_thread_sample": f"layer {done[-1]} alone with one BLAS thread ({dt1:.1f}s)",
+            "one_thread_sample": f"layer {slow} alone with one BLAS thread ({dt1:.1f}s)",
+            "same_layer_all_threads_GBs": round(per[slow][1] / per[slow][0] / 1e9, 4),
             "cpu_model": cpu_info(), "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -415,9 +460,11 @@ def main():
     results = {}
     for short in order:
         w = wl.BY_SHORT[short]
-        res, parts = run_workload(tq, torch, w, args, stream, dev)
+        res, parts = run_workload(tq, torch, w, short, args, stream, dev)
         if short == "w5":
             res["bulk_compress"] = bulk_compress(tq, torch, w, args, stream, dev, parts)
+        if short == "w4":
+            res["multi_query_scores"] = multi_query_scores(tq, torch, parts[0], args, stream, dev)
         results[short] = res
         log(json.dumps(res))
         del parts
@@ -427,8 +474,6 @@ def main():
     # the dominant kernel of the headline step: the part with the most bytes
     dom = max(hr["decode_kernels"], key=lambda k: k["bytes_per_launch"])
     read_gbs = None if args.no_stream_probe else stream_read(tq, torch, stream, dev)
-    traffic_name = {"w3": "decode_w3_kf16v4_24L", "w2": "decode_w2_dense28L", "w4": "decode_w4_longctx",
-                    "w5": "decode_w5_ragged16"}.get(head, "decode_" + head)
     result = {
         "metric": "decode-attention GB/s & % HBM roofline; compress Mtokens/s per KV head",
         "value": hr["step_GBs"],
@@ -448,7 +493,7 @@ def main():
                    "step": "append-compress the new token of every sequence x every layer + decode attention "
                            "x every layer (one tq_decode_step per storage format)"},
         "roofline": {"bound": "hbm", "achieved": dom["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": dom["frac_of_hbm_peak"], "traffic": measured_traffic(traffic_name),
+                     "frac": dom["frac_of_hbm_peak"], "traffic": dom["traffic"],
                      "kernel": dom["kernel"], "bytes_per_launch": dom["bytes_per_launch"],
                      "us_per_launch": dom["us_per_launch"], "measured_stream_read_GBs": read_gbs,
                      "frac_of_measured_read": round(dom["GBs"] / read_gbs, 4) if read_gbs else None},
