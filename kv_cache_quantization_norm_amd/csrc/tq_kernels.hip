@@ -10,23 +10,37 @@
 // MLX write-up, 背景: values take the MSE-only path.
 //
 // Kernels
-//   compress_kernel  one workgroup per (16-token tile, layer); each wave takes
-//                    heads w, w+4, ...  Rotation y = Pi x and the sketch
-//                    z = (S Pi^T)(y - c[idx]) run as fp32 MFMA 16x16x4 with Pi
-//                    and S Pi^T staged in LDS in operand order.
-//   qprep_kernel     Pi q and S q per (layer, batch, query head).
-//   decode_kernel    workgroups of 4 waves, at most two per CU, each given an
-//                    equal run of 32-token chunks of the problem-major chunk
-//                    sequence (a problem is one layer x sequence x KV head x
-//                    group of <= 8 query heads).  Each wave streams chunks:
-//                    unpack codes through LDS tables into fp16 MFMA operands,
-//                    score the query heads with v_mfma_f32_16x16x32_f16 (codes
-//                    x Pi q, signs x S q), run the online softmax, and
-//                    accumulate values in the rotated domain with a second
-//                    MFMA (P x codes).  Every (problem, workgroup) piece leaves
-//                    one partial per query head.
-//   combine_kernel   merges the partials of a (layer, batch, KV head) and
-//                    applies Pi^T once.
+//   compress_kernel        bulk compression (>= 16 tokens): at most one
+//                          workgroup of 8 waves per CU over equal ranges of the
+//                          flattened (layer, 16-token tile) sequence; Pi and
+//                          S Pi^T staged in LDS as fp16 high + remainder MFMA
+//                          operands, rotation and sketch on
+//                          v_mfma_f32_16x16x32_f16, codes from a bucket table.
+//   compress_append_kernel few-token compression (appends): 8 (token, head)
+//                          items per workgroup as the MFMA columns.
+//   qprep_kernel           Pi q and S q of every query row, per (quarter of
+//                          [Pi; S], layer, run of 64 rows), fp16 MFMA with
+//                          high + remainder operands.
+//   decode_kernel          one workgroup of 8 waves per CU (its first
+//                          workgroups may do a step's append first), each
+//                          given an equal range of the problem-major sequence
+//                          of 32-token chunks (a problem is one layer x
+//                          sequence x KV head x group of <= 8 query heads;
+//                          for ragged batches only the chunks that hold
+//                          tokens); its waves draw chunks from an LDS ticket
+//                          counter, load them through buffer resources two
+//                          chunks ahead, form the key and value operands
+//                          through LDS tables, score on
+//                          v_mfma_f32_16x16x32_f16 (codes x Pi q, signs x
+//                          S q), run the online softmax and accumulate values
+//                          in the rotated domain (P x codes).  The workgroup
+//                          that writes a problem's last piece merges its
+//                          pieces and applies Pi^T (fp32 MFMA).
+//   combine_kernel         the same merge as a launch of its own (staged calls).
+//   score_multi_kernel     multi-query scores: the key operands of a chunk
+//                          formed once per 64 query rows.
+//   tail_gather_kernel     the fp16 tail tokens a ring flush moves, gathered
+//                          for compression.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
