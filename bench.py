@@ -205,11 +205,35 @@ def build_parts(tq, torch, w, dev):
             key = (0, 0)
         groups.setdefault(key, []).append(layer)
     parts = []
-    for (kb, vb), layers in groups.items():
+    # the fp16 / fp16 part last: two parts whose second is fp16 / fp16 share one
+    # decode launch (tq_decode_step_parts)
+    for (kb, vb), layers in sorted(groups.items(), key=lambda kv: kv[0] == (0, 0)):
         p = Part(tq, torch, w, layers, kb, vb, starts, lens, cap, dev, new_slots)
         p.new_slot0 = new_slots[0]
         parts.append(p)
     return parts
+
+
+def step_parts(tq, parts, i, stream):
+    """One decode step over every part: one tq_decode_step call for a single
+    format, else one tq_decode_step_parts call over all of them."""
+    if len(parts) == 1:
+        parts[0].step(i, stream)
+        return
+    p0 = parts[0]
+    sp = [tq.StepPart(p.fmt, p.tables, p.copies[i % len(p.copies)], p.k_new, p.v_new, p.q, p.out, p.ws)
+          for p in parts]
+    if p0.B == 1:
+        tq.tq_decode_step_parts(sp, p0.seq_start, p0.seq_len, p0.T, slot0=int(p0.new_slot0), stream=stream)
+    else:
+        tq.tq_decode_step_parts(sp, p0.seq_start, p0.seq_len, p0.T, slots=p0.new_slots, stream=stream)
+
+
+def attend_parts(tq, parts, i, stream):
+    """The decode launch of step_parts alone, on prepared queries."""
+    p0 = parts[0]
+    sp = [tq.StepPart(p.fmt, p.tables, p.copies[i % len(p.copies)], None, None, p.q, p.out, p.ws) for p in parts]
+    tq.tq_decode_attend_parts(sp, p0.seq_start, p0.seq_len, p0.T, stream=stream)
 
 
 def timed(torch, stream, fn, warmup, steps):
@@ -237,8 +261,8 @@ def run_workload(tq, torch, w, short, args, stream, dev):
     log(f"{w.name}: {len(parts)} format(s), cache {total_cache / 1e6:.1f} MB x {n_copies} copies, "
         f"setup {time.time() - t0:.1f}s")
     H, Hq, B = w.n_kv_heads, w.n_q_heads, w.batch
-    # one step: every part's tq_decode_step
-    step_ms = timed(torch, stream, lambda i: [p.step(i, stream) for p in parts], args.warmup, args.steps)
+    # one step over every part (one tq_decode_step_parts call for several formats)
+    step_ms = timed(torch, stream, lambda i: step_parts(tq, parts, i, stream), args.warmup, args.steps)
     records = sum(p.record_bytes for p in parts)
     new_tok = w.n_layers * B * H * 2 * D * 2 + sum(p.L * B * H * sum(rec_bytes(p.k_bits, p.v_bits)) for p in parts)
     qo = 2 * w.n_layers * B * Hq * D * 4
@@ -264,6 +288,17 @@ def run_workload(tq, torch, w, short, args, stream, dev):
                      "frac_of_hbm_peak": round(kb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                      "workgroups": tq.tq_decode_split(p.fmt, p.L, B, H, Hq, p.T)["n_workgroups"],
                      "traffic": measured_traffic(traffic_key(short, p.k_bits, p.v_bits))})
+    if len(parts) == 2 and (parts[1].k_bits, parts[1].v_bits) == (0, 0):
+        # the step's decode: both parts in one launch of decode_pair_kernel
+        us = timed(torch, stream, lambda i: attend_parts(tq, parts, i, stream), args.warmup, args.steps) * 1e3
+        kb = sum(p.kernel_bytes() for p in parts)
+        mk = max(parts[0].k_bits - 1, 0)
+        kern.append({"kernel": f"decode_pair_kernel<{mk}, {parts[0].v_bits}>", "layers": sum(p.L for p in parts),
+                     "us_per_launch": round(us, 2), "bytes_per_launch": kb,
+                     "GBs": round(kb / (us * 1e-6) / 1e9, 1),
+                     "frac_of_hbm_peak": round(kb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "workgroups": 256,
+                     "traffic": measured_traffic(f"decode_pair_{short}")})
     res["decode_kernels"] = kern
     dom = max(kern, key=lambda k: k["bytes_per_launch"])
     res["roofline"] = {"bound": "hbm", "achieved": dom["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -381,6 +381,59 @@ tq_status tq_decode_step(const tq_format* fmt, const tq_tables* tables, const tq
                          const int64_t* seq_start, const int32_t* seq_len, int64_t max_seq_len, float scale,
                          float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* One part of a decode step over a model whose layers use different formats
+ * (tq_decode_step_parts): the arguments of tq_decode_step that belong to the
+ * part, with their meaning there.  k, v: the new tokens of cache layers
+ * [layer0, layer0 + n_layers) of this part's cache, laid out as for
+ * tq_compress_kv; q, out: [cache->n_layers][batch][n_q_heads][d] fp32;
+ * workspace: at least tq_decode_workspace_bytes for this part's cache. */
+typedef struct tq_step_part {
+  const tq_format* fmt;
+  const tq_tables* tables;
+  const tq_cache* cache;
+  const void* k;
+  const void* v;
+  int32_t layer0;
+  int32_t n_layers;
+  const float* q;
+  float* out;
+  void* workspace;
+  size_t workspace_bytes;
+} tq_step_part;
+
+/* Device.  A decode step over n_parts caches of different formats that share
+ * the batch, its sequences and the new tokens' slots (say a model that keeps
+ * its first and last two KV layers in fp16 and its other layers with fp16
+ * keys and quantized values: the asymmetric mode with boundary-layer
+ * protection of the TurboQuant Apple-MLX port write-up, section on symmetric
+ * and asymmetric compression): the same result as tq_decode_step for parts[0], then
+ * parts[1], ..., each with its part's arguments and the shared ones given
+ * here (dtype, n_tokens, slots, slot0, batch, n_q_heads, seq_start, seq_len,
+ * max_seq_len, scale), with their layouts, ownership and errors.  Every part
+ * is checked before anything is enqueued.  With two parts, the second with
+ * fp16 keys and values (k_bits = v_bits = 0), and both appends small enough to
+ * run inside the decode launch (at most 32 append workgroups in all), the two
+ * decodes run in one launch: the decode workgroups are shared between the
+ * parts in proportion to the bytes each reads per token, so the launch pays
+ * one start and one end instead of two.  Otherwise the parts' tq_decode_step
+ * calls are made one after the other.  n_parts: 1 to 8; parts must not be
+ * NULL; calls on one workspace must not overlap. */
+tq_status tq_decode_step_parts(const tq_step_part* parts, int32_t n_parts, int32_t dtype, int64_t n_tokens,
+                               const int64_t* slots, int64_t slot0, int32_t batch, int32_t n_q_heads,
+                               const int64_t* seq_start, const int32_t* seq_len, int64_t max_seq_len, float scale,
+                               void* stream);
+
+/* Device.  The decode of tq_decode_step_parts alone, on queries already
+ * prepared in each part's workspace (tq_decode_prepare or tq_append_prepare
+ * for each part): the same result as tq_decode_attend for parts[0], then
+ * parts[1], ..., with the shared arguments given here, their layouts,
+ * ownership and errors, and two parts in one launch on the same condition as
+ * tq_decode_step_parts (no append here).  The parts' k, v, layer0 and n_layers
+ * are not read. */
+tq_status tq_decode_attend_parts(const tq_step_part* parts, int32_t n_parts, int32_t batch, int32_t n_q_heads,
+                                 const int64_t* seq_start, const int32_t* seq_len, int64_t max_seq_len, float scale,
+                                 void* stream);
+
 /* Host, synchronous.  Whether the last tq_decode_step on `workspace` (made
  * with these sizes) ran its append inside the decode launch without a decode
  * wave giving up its wait.  A wave that must read a chunk holding a new token

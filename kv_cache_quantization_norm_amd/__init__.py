@@ -50,6 +50,13 @@ class tq_cache(ctypes.Structure):
                 ("k_idx", "k_sign", "k_norm", "k_rnorm", "k_f16", "v_idx", "v_norm", "v_f16")]
 
 
+class tq_step_part(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.POINTER(tq_format)), ("tables", ctypes.POINTER(tq_tables)),
+                ("cache", ctypes.POINTER(tq_cache)), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("layer0", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("q", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 def _load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"libtq.so is not built ({path}); run __graft_entry__.build() or "
@@ -92,6 +99,9 @@ def _load(path: str = LIB_PATH):
         "tq_stream_read_probe": (I32, [P, SZ, P, I32, P]),
         "tq_decode_step": (I32, [fmtp, tabp, cachep, P, P, I32, I32, I32, I64, P, I64, P, I32, I32, P, P, I64, F32, P,
                                  P, SZ, P]),
+        "tq_decode_step_parts": (I32, [ctypes.POINTER(tq_step_part), I32, I32, I64, P, I64, I32, I32, P, P, I64,
+                                       F32, P]),
+        "tq_decode_attend_parts": (I32, [ctypes.POINTER(tq_step_part), I32, I32, I32, P, P, I64, F32, P]),
         "tq_decode_step_check": (I32, [fmtp, I32, I32, I32, I32, I64, P, SZ, P]),
         "tq_set_append_wait": (I32, [ctypes.c_uint32, I32]),
         "tq_tail_policy": (I32, [I32, P, P, I32, I32, P]),
@@ -117,7 +127,7 @@ EXPORTED = ("tq_layer_seed", "tq_make_rotations", "tq_make_codebook", "tq_cache_
             "tq_compress_kv_bounded", "tq_decode_attention_tail", "tq_decode_tail_workspace_bytes",
             "tq_decode_attention_noalloc", "tq_decode_step_check", "tq_set_append_wait", "tq_fp16_operand_scale",
             "tq_tail_policy", "tq_tail_append", "tq_tail_flush_workspace_bytes", "tq_tail_flush", "tq_score_multi",
-            "tq_status_string", "tq_last_error")
+            "tq_decode_step_parts", "tq_decode_attend_parts", "tq_status_string", "tq_last_error")
 
 
 def status_name(st: int) -> str:
@@ -488,6 +498,81 @@ def tq_decode_step(fmt: tq_format, tables: Tables, cache: Cache, k, v, q, seq_st
     _check(_lib.tq_decode_step(ctypes.byref(fmt), ctypes.byref(tb), ctypes.byref(cs), pk, pv, _dtype_code(k), layer0,
                                n_layers, n_tokens, _slots(slots, n_tokens), slot0, pq, batch, hq, ps, pl, max_seq_len,
                                scale, po, pw, nw, _stream(stream)), "tq_decode_step")
+
+
+@dataclass
+class StepPart:
+    """One part of tq_decode_step_parts: a cache of one format (its layers),
+    the new tokens of its layers [layer0, layer0 + k.shape[0]), its queries,
+    outputs and workspace."""
+    fmt: tq_format
+    tables: "Tables"
+    cache: "Cache"
+    k: object
+    v: object
+    q: object
+    out: object
+    workspace: object
+    layer0: int = 0
+
+
+def tq_decode_step_parts(parts: Sequence[StepPart], seq_start, seq_len, max_seq_len: int, slots=None, slot0: int = 0,
+                         scale: float = 0.0, stream=None):
+    """tq_decode_step over each part in order, the parts sharing the batch, its
+    sequences and the new tokens' slots; two parts whose second is fp16 / fp16
+    run their decodes in one launch."""
+    if not parts:
+        raise ValueError("no parts")
+    arr = (tq_step_part * len(parts))()
+    keep = []
+    shared = None
+    for i, p in enumerate(parts):
+        pk, pv, n_layers, n_tokens = _kv(p.fmt, p.cache, p.k, p.v)
+        pq, batch, hq = _q(p.fmt, p.cache, p.q)
+        po = _out(p.fmt, p.cache, p.out, batch, hq)
+        pw, nw = _ws(p.workspace)
+        mine = (n_tokens, batch, hq, _dtype_code(p.k))
+        if shared is None:
+            shared = mine
+        elif mine != shared:
+            raise ValueError(f"part {i}: (tokens, batch, q heads, dtype) {mine} differ from part 0's {shared}")
+        tb, cs = p.tables.struct(), p.cache.struct()
+        keep += [tb, cs]
+        arr[i] = tq_step_part(ctypes.pointer(p.fmt), ctypes.pointer(tb), ctypes.pointer(cs), pk, pv, p.layer0, n_layers,
+                              pq, po, pw, nw)
+    n_tokens, batch, hq, dtype = shared
+    ps, pl = _seq(seq_start, seq_len, batch)
+    _check(_lib.tq_decode_step_parts(arr, len(parts), dtype, n_tokens, _slots(slots, n_tokens), slot0, batch, hq, ps, pl,
+                                     max_seq_len, scale, _stream(stream)), "tq_decode_step_parts")
+    del keep
+
+
+def tq_decode_attend_parts(parts: Sequence[StepPart], seq_start, seq_len, max_seq_len: int, scale: float = 0.0,
+                           stream=None):
+    """The decode of tq_decode_step_parts alone, on queries prepared in each
+    part's workspace (the parts' k and v are not read and may be None)."""
+    if not parts:
+        raise ValueError("no parts")
+    arr = (tq_step_part * len(parts))()
+    keep = []
+    shared = None
+    for i, p in enumerate(parts):
+        pq, batch, hq = _q(p.fmt, p.cache, p.q)
+        po = _out(p.fmt, p.cache, p.out, batch, hq)
+        pw, nw = _ws(p.workspace)
+        if shared is None:
+            shared = (batch, hq)
+        elif (batch, hq) != shared:
+            raise ValueError(f"part {i}: (batch, q heads) {(batch, hq)} differ from part 0's {shared}")
+        tb, cs = p.tables.struct(), p.cache.struct()
+        keep += [tb, cs]
+        arr[i] = tq_step_part(ctypes.pointer(p.fmt), ctypes.pointer(tb), ctypes.pointer(cs), None, None, 0, 0, pq, po,
+                              pw, nw)
+    batch, hq = shared
+    ps, pl = _seq(seq_start, seq_len, batch)
+    _check(_lib.tq_decode_attend_parts(arr, len(parts), batch, hq, ps, pl, max_seq_len, scale, _stream(stream)),
+           "tq_decode_attend_parts")
+    del keep
 
 
 def tq_decode_step_check(fmt: tq_format, cache: Cache, batch: int, n_q_heads: int, max_seq_len: int, workspace,

@@ -1267,6 +1267,49 @@ __device__ __forceinline__ half8 deq8_vrep(uint32_t bits, uint32_t lane4, const 
                         *reinterpret_cast<const uint32_t*>(base + a2), *reinterpret_cast<const uint32_t*>(base + a3)});
 }
 
+// LDS layout of a decode workgroup of format <MK, BV> (see decode_body).
+template <int MK, int BV, bool SCORE>
+struct DecodeLayout {
+  static constexpr bool KWIDE = MK > 4;   // 7-bit codes: one fp16 table entry per code (high parts, then remainders)
+  using KL = KLut<(MK > 0 && !KWIDE ? MK : 1)>;
+  static constexpr int KT = MK > 0 ? (KWIDE ? (1 << MK) : KL::E * KL::EW) : 1;   // key table dwords
+  static constexpr int KP = MK > 0 && !KWIDE && KL::NC > 2 ? KL::PAIRS * KL::PW : 1;   // pair-table dwords (if separate)
+  static constexpr bool VREP = BV == 4;                                          // lane-private value table
+  static constexpr int VW = VREP ? 256 * 64 : (BV > 0 ? Lut<BV, false>::WORDS : 1);
+  // Tables first, each starting below 64 KB so that lookups carry the table
+  // offset as an instruction immediate (the lane-private value table may
+  // start past 64 KB: its addresses carry the page, see deq8_vrep).
+  // Order: signs, then the small value tables (1 or 2 bits), the key table
+  // and its pair table, then the lane-private 4-bit value table.
+  static constexpr int OFF_S = 0;
+  static constexpr int S_END = MK > 0 ? 256 * 16 : 0;
+  static constexpr int OFF_K = VREP ? S_END : ((S_END + VW * 4 + 255) / 256) * 256;
+  static constexpr int OFF_PHI = OFF_K + KT * 4;   // read only while the key table is built
+  static constexpr int OFF_V = VREP ? ((OFF_PHI + KP * 4 + 255) / 256) * 256 : S_END;
+  static constexpr int V_PAGE = VREP && OFF_V >= 65536 ? 1 : 0;
+  static constexpr int OFF_TAB_END = VREP ? ((OFF_V + VW * 4 + 15) / 16) * 16 : ((OFF_PHI + KP * 4 + 15) / 16) * 16;
+  static constexpr int LIVE_BYTES = (kRaggedMaxBatch + 1) * 4;
+  static constexpr int MISC_BYTES = kDecodeWaves * 128 * 4 + 2 * kDecodeWaves * 16 * 4 + 2 * 2 * 4 * 64 * 16 + 16 + LIVE_BYTES;
+  static constexpr int RED_FULL = kDecodeWaves * kMaxGroup * D * 4;
+  // The wave merge ([wave][head][coordinate] fp32) stays in LDS when the
+  // tables leave room for it, else it goes through the workgroup's slice of
+  // the workspace (L2).
+  static constexpr bool RED_LDS = !SCORE && OFF_TAB_END + RED_FULL + MISC_BYTES <= 160 * 1024;
+  static constexpr int OFF_RED = OFF_TAB_END;
+  static constexpr int RED_BYTES = RED_LDS ? RED_FULL : 0;
+  static constexpr int OFF_NX = OFF_RED + RED_BYTES;
+  static constexpr int OFF_MW = OFF_NX + kDecodeWaves * 128 * 4;
+  static constexpr int OFF_LW = OFF_MW + kDecodeWaves * 16 * 4;
+  static constexpr int OFF_Q = OFF_LW + kDecodeWaves * 16 * 4;    // staged query operands [piece][r / z][s][lane]
+  static constexpr int OFF_CNT = OFF_Q + 2 * 2 * 4 * 64 * 16;
+  static constexpr int OFF_LIVE = OFF_CNT + 16;   // ragged split: prefix of the sequences' live chunk counts
+  static constexpr int LDS_BYTES = OFF_LIVE + LIVE_BYTES;
+  static_assert(OFF_K < 65536, "the key table must start below 64 KB");
+  static_assert(VREP ? OFF_V - V_PAGE * 65536 < 65536 : OFF_V < 65536, "value table offset");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
+  static_assert(2 * 2 * 4 * 64 * 16 >= 2 * 16 * D * 4, "the in-kernel merge's result area fits the query staging");
+};
+
 // Decode / score kernel: one workgroup of 8 waves per CU.  Workgroup w owns
 // the chunks [w * chunks_per_wg, ...) of the problem-major chunk sequence; it
 // takes them in groups of at most two problems (pieces A and B).  Inside a
@@ -1276,49 +1319,37 @@ __device__ __forceinline__ half8 deq8_vrep(uint32_t bits, uint32_t lane4, const 
 // at the end of the group the wave states of a piece are merged in LDS, in
 // wave order, into the piece's partial.
 template <int MK, int BV, bool SCORE>
-__global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(
-    DecodeArgs a, CompressArgs ca) {
-  constexpr bool KWIDE = MK > 4;   // 7-bit codes: one fp16 table entry per code (high parts, then remainders)
+__device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsigned char* const dsm,
+                                            const int blk, const int nblk) {
+  using LY = DecodeLayout<MK, BV, SCORE>;
+  constexpr bool KWIDE = LY::KWIDE;
   constexpr bool KSPLIT = MK > 0 && key_split(MK);   // key centroids as fp16 high part + remainder
-  using KL = KLut<(MK > 0 && !KWIDE ? MK : 1)>;
+  using KL = typename LY::KL;
   constexpr int NT = kDecodeWaves * 64;
-  constexpr int KT = MK > 0 ? (KWIDE ? (1 << MK) : KL::E * KL::EW) : 1;   // key table dwords
-  constexpr int KP = MK > 0 && !KWIDE && KL::NC > 2 ? KL::PAIRS * KL::PW : 1;   // pair-table dwords (if separate)
-  constexpr bool VREP = BV == 4;                                          // lane-private value table
-  constexpr int VW = VREP ? 256 * 64 : (BV > 0 ? Lut<BV, false>::WORDS : 1);
-  // Tables first, each starting below 64 KB so that lookups carry the table
-  // offset as an instruction immediate (the lane-private value table may
-  // start past 64 KB: its addresses carry the page, see deq8_vrep).
-  // Order: signs, then the small value tables (1 or 2 bits), the key table
-  // and its pair table, then the lane-private 4-bit value table.
-  constexpr int OFF_S = 0;
-  constexpr int S_END = MK > 0 ? 256 * 16 : 0;
-  constexpr int OFF_K = VREP ? S_END : ((S_END + VW * 4 + 255) / 256) * 256;
-  constexpr int OFF_PHI = OFF_K + KT * 4;   // read only while the key table is built
-  constexpr int OFF_V = VREP ? ((OFF_PHI + KP * 4 + 255) / 256) * 256 : S_END;
-  constexpr int V_PAGE = VREP && OFF_V >= 65536 ? 1 : 0;
-  constexpr int OFF_TAB_END = VREP ? ((OFF_V + VW * 4 + 15) / 16) * 16 : ((OFF_PHI + KP * 4 + 15) / 16) * 16;
-  constexpr int LIVE_BYTES = (kRaggedMaxBatch + 1) * 4;
-  constexpr int MISC_BYTES = kDecodeWaves * 128 * 4 + 2 * kDecodeWaves * 16 * 4 + 2 * 2 * 4 * 64 * 16 + 16 + LIVE_BYTES;
-  constexpr int RED_FULL = kDecodeWaves * kMaxGroup * D * 4;
-  // The wave merge ([wave][head][coordinate] fp32) stays in LDS when the
-  // tables leave room for it, else it goes through the workgroup's slice of
-  // the workspace (L2).
-  constexpr bool RED_LDS = !SCORE && OFF_TAB_END + RED_FULL + MISC_BYTES <= 160 * 1024;
-  constexpr int OFF_RED = OFF_TAB_END;
-  constexpr int RED_BYTES = RED_LDS ? RED_FULL : 0;
-  constexpr int OFF_NX = OFF_RED + RED_BYTES;
-  constexpr int OFF_MW = OFF_NX + kDecodeWaves * 128 * 4;
-  constexpr int OFF_LW = OFF_MW + kDecodeWaves * 16 * 4;
-  constexpr int OFF_Q = OFF_LW + kDecodeWaves * 16 * 4;    // staged query operands [piece][r / z][s][lane]
-  constexpr int OFF_CNT = OFF_Q + 2 * 2 * 4 * 64 * 16;
-  constexpr int OFF_LIVE = OFF_CNT + 16;   // ragged split: prefix of the sequences' live chunk counts
-  constexpr int LDS_BYTES = OFF_LIVE + LIVE_BYTES;
-  static_assert(OFF_K < 65536, "the key table must start below 64 KB");
-  static_assert(VREP ? OFF_V - V_PAGE * 65536 < 65536 : OFF_V < 65536, "value table offset");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
-  static_assert(2 * 2 * 4 * 64 * 16 >= 2 * 16 * D * 4, "the in-kernel merge's result area fits the query staging");
-  __shared__ __align__(256) unsigned char dsm[LDS_BYTES];
+  [[maybe_unused]] constexpr auto KT = LY::KT;
+  [[maybe_unused]] constexpr auto KP = LY::KP;
+  [[maybe_unused]] constexpr auto VREP = LY::VREP;
+  [[maybe_unused]] constexpr auto VW = LY::VW;
+  [[maybe_unused]] constexpr auto OFF_S = LY::OFF_S;
+  [[maybe_unused]] constexpr auto S_END = LY::S_END;
+  [[maybe_unused]] constexpr auto OFF_K = LY::OFF_K;
+  [[maybe_unused]] constexpr auto OFF_PHI = LY::OFF_PHI;
+  [[maybe_unused]] constexpr auto OFF_V = LY::OFF_V;
+  [[maybe_unused]] constexpr auto V_PAGE = LY::V_PAGE;
+  [[maybe_unused]] constexpr auto OFF_TAB_END = LY::OFF_TAB_END;
+  [[maybe_unused]] constexpr auto LIVE_BYTES = LY::LIVE_BYTES;
+  [[maybe_unused]] constexpr auto MISC_BYTES = LY::MISC_BYTES;
+  [[maybe_unused]] constexpr auto RED_FULL = LY::RED_FULL;
+  [[maybe_unused]] constexpr auto RED_LDS = LY::RED_LDS;
+  [[maybe_unused]] constexpr auto OFF_RED = LY::OFF_RED;
+  [[maybe_unused]] constexpr auto RED_BYTES = LY::RED_BYTES;
+  [[maybe_unused]] constexpr auto OFF_NX = LY::OFF_NX;
+  [[maybe_unused]] constexpr auto OFF_MW = LY::OFF_MW;
+  [[maybe_unused]] constexpr auto OFF_LW = LY::OFF_LW;
+  [[maybe_unused]] constexpr auto OFF_Q = LY::OFF_Q;
+  [[maybe_unused]] constexpr auto OFF_CNT = LY::OFF_CNT;
+  [[maybe_unused]] constexpr auto OFF_LIVE = LY::OFF_LIVE;
+  [[maybe_unused]] constexpr auto LDS_BYTES = LY::LDS_BYTES;
   uint32_t* const lut_k = reinterpret_cast<uint32_t*>(dsm + OFF_K);
   uint32_t* const pair_hi = reinterpret_cast<uint32_t*>(dsm + OFF_PHI);
   uint32_t* const lut_s = reinterpret_cast<uint32_t*>(dsm + OFF_S);
@@ -1337,8 +1368,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   if constexpr (!SCORE) {
     // append workgroups first (lowest indices, so they are dispatched first and
     // never wait behind decode workgroups that wait for them)
-    if (int(blockIdx.x) < a.n_app) {
-      append_body<MK, BV>(ca, int(blockIdx.x) % a.app_groups, int(blockIdx.x) / a.app_groups,
+    if (blk < a.n_app) {
+      append_body<MK, BV>(ca, blk % a.app_groups, blk / a.app_groups,
                           *reinterpret_cast<AppendSmem*>(dsm), a.app_done);
       return;
     }
@@ -1349,7 +1380,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   // pieces of a problem, and the problems of a layer, share an L2).
   int wg;
   {
-    const int i = int(blockIdx.x) - a.n_app, nd = int(gridDim.x) - a.n_app;
+    const int i = blk - a.n_app, nd = nblk - a.n_app;
     const int r = i & 7, qd = nd >> 3, rem = nd & 7;
     wg = r * qd + (r < rem ? r : rem) + (i >> 3);
   }
@@ -2195,7 +2226,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     if (padded_total - per_seq * nonempty * kCrossingChunks < int64_t(a.total_chunks / cpp) * a.cpp_real) {
       rag = true;
       total = int(padded_total);
-      const int64_t nd = int64_t(gridDim.x) - a.n_app;
+      const int64_t nd = int64_t(nblk) - a.n_app;
       const int even = int((padded_total + nd - 1) / nd);
       cpw = even > a.cpw_min ? even : a.cpw_min;
     }
@@ -2403,6 +2434,43 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   }
 }
 
+template <int MK, int BV, bool SCORE>
+__global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(
+    DecodeArgs a, CompressArgs ca) {
+  __shared__ __align__(256) unsigned char dsm[DecodeLayout<MK, BV, SCORE>::LDS_BYTES];
+  decode_body<MK, BV, SCORE>(a, ca, dsm, int(blockIdx.x), int(gridDim.x));
+}
+
+// Two decode calls in one launch: part 1 in format <MK, BV>, part 2 with fp16
+// keys and values (say a model's uncompressed boundary layers beside its
+// quantized ones), each with its own arguments, append and workspace.  Blocks,
+// in dispatch order: part 1's append workgroups, part 2's, then nd1 decode
+// workgroups of part 1 and the rest for part 2.  Each part sees its own
+// blocks numbered from 0 (appends first), so its work split and XCD-aware
+// mapping are those of a launch of its own with that many workgroups; both
+// parts' workgroups share every XCD, and the launch pays one start and one end.
+template <int MK, int BV>
+__global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_pair_kernel(
+    DecodeArgs a1, CompressArgs c1, DecodeArgs a2, CompressArgs c2, int nd1) {
+  constexpr int L1 = DecodeLayout<MK, BV, false>::LDS_BYTES, L2 = DecodeLayout<0, 0, false>::LDS_BYTES;
+  __shared__ __align__(256) unsigned char dsm[L1 > L2 ? L1 : L2];
+  const int b = int(blockIdx.x), apps = a1.n_app + a2.n_app;
+  const int nd2 = int(gridDim.x) - apps - nd1;
+  bool first;
+  int blk;
+  if (b < apps) {
+    first = b < a1.n_app;
+    blk = first ? b : b - a1.n_app;
+  } else {
+    first = b - apps < nd1;
+    blk = first ? a1.n_app + (b - apps) : a2.n_app + (b - apps - nd1);
+  }
+  if (first)
+    decode_body<MK, BV, false>(a1, c1, dsm, blk, a1.n_app + nd1);
+  else
+    decode_body<0, 0, false>(a2, c2, dsm, blk, a2.n_app + nd2);
+}
+
 // The query preparation of a decode call, one workgroup per (quarter, layer,
 // run of kQprepRows query rows): wave w owns row block 4 quarter + w of
 // [Pi; S] (16 rows), read once per workgroup and split into fp16 high parts
@@ -2507,6 +2575,25 @@ __global__ __launch_bounds__(256) void qprep_kernel(const float* q, const float*
 // Grid of the query preparation for n_layers layers of batch x Hq query rows.
 inline dim3 qprep_grid(int n_layers, int batch, int Hq) {
   return dim3(4, unsigned(n_layers), unsigned((batch * Hq + kQprepRows - 1) / kQprepRows));
+}
+
+// The query preparations of two decode calls in one launch (the parts of
+// decode_pair_kernel; part 2 has fp16 keys): blocks [0, 4 L1 runs) are part
+// 1's (quarter, layer, run) blocks of qprep_kernel, flattened, the rest part 2's.
+template <bool ROT1>
+__global__ __launch_bounds__(256) void qprep_pair_kernel(const float* q1, const float* pi1, const float* s1,
+                                                         float* qp1, uint32_t* done1, int H1, int L1, const float* q2,
+                                                         float* qp2, uint32_t* done2, int H2, int L2, int batch,
+                                                         int Hq) {
+  const int runs = (batch * Hq + kQprepRows - 1) / kQprepRows;
+  int i = int(blockIdx.x);
+  if (i < 4 * L1 * runs) {
+    qprep_quarter<ROT1>(q1, pi1, s1, qp1, batch, H1, Hq, i & 3, (i >> 2) % L1, L1, (i >> 2) / L1, done1, nullptr);
+  } else {
+    i -= 4 * L1 * runs;
+    qprep_quarter<false>(q2, nullptr, nullptr, qp2, batch, H2, Hq, i & 3, (i >> 2) % L2, L2, (i >> 2) / L2, done2,
+                         nullptr);
+  }
 }
 
 // The append of a few tokens and the query preparation of the same decode
@@ -2994,6 +3081,21 @@ tq_status launch_decode(int mk, int bv, const DecodeArgs& args, dim3 grid, hipSt
   return fail(TQ_ERR_UNSUPPORTED, "no decode kernel for key bits %d / value bits %d", mk, bv);
 }
 
+// Launches decode_pair_kernel for part 1's format (part 2: fp16 keys and values).
+tq_status launch_decode_pair(int mk, int bv, const DecodeArgs& a1, const CompressArgs& c1, const DecodeArgs& a2,
+                             const CompressArgs& c2, int nd1, dim3 grid, hipStream_t st) {
+#define TQ_DECP(MK_, BV_)                                                                                      \
+  if (mk == MK_ && bv == BV_) {                                                                                \
+    hipLaunchKernelGGL((decode_pair_kernel<MK_, BV_>), grid, dim3(kDecodeWaves * 64), 0, st, a1, c1, a2, c2, nd1); \
+    return TQ_OK;                                                                                              \
+  }
+#define TQ_DECP_V(MK_) TQ_DECP(MK_, 0) TQ_DECP(MK_, 1) TQ_DECP(MK_, 2) TQ_DECP(MK_, 3) TQ_DECP(MK_, 4)
+  TQ_DECP_V(0) TQ_DECP_V(1) TQ_DECP_V(2) TQ_DECP_V(3) TQ_DECP_V(4) TQ_DECP_V(7)
+#undef TQ_DECP_V
+#undef TQ_DECP
+  return fail(TQ_ERR_UNSUPPORTED, "no decode kernel for key bits %d / value bits %d", mk, bv);
+}
+
 tq_status check_tables(const tq_format* f, const tq_tables* t, bool need_sketch) {
   if (!t) return fail(TQ_ERR_INVALID_ARG, "tables is NULL");
   const bool rot = f->k_bits > 0 || f->v_bits > 0;
@@ -3103,7 +3205,8 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
                         const float* q, int32_t batch, int32_t n_q_heads, const int64_t* seq_start,
                         const int32_t* seq_len, int64_t max_seq_len, float scale, float* out,
                         void* workspace, size_t workspace_bytes, void* stream, int stages,
-                        const FusedAppend* app = nullptr) {
+                        const FusedAppend* app = nullptr, int wg_budget = 0, DecodeArgs* args_out = nullptr,
+                        int* decode_wgs_out = nullptr) {
   clear_error();
   tq_status st = check_format(fmt, true);
   if (st) return st;
@@ -3125,9 +3228,11 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   // With an append in the launch, its workgroups take CUs first: the decode
   // split is made for the CUs they leave, so that no decode workgroup waits
   // for a CU (one decode workgroup per CU).
+  // (wg_budget > 0: the decode workgroups this call may use, for a launch
+  // shared with another call)
   const int app_wgs = app != nullptr ? app->groups * app->layers : 0;
   const SplitPlan plan = plan_decode(fmt->d, cache->n_layers, batch, cache->n_kv_heads, n_q_heads, max_seq_len,
-                                     kDecodeWorkgroups - app_wgs);
+                                     wg_budget > 0 ? wg_budget : kDecodeWorkgroups - app_wgs);
   if (plan.problems * plan.chunks_per_problem > (int64_t(1) << 30))
     return fail(TQ_ERR_INVALID_ARG, "too many 32-token chunks in one call");
   if (!workspace || workspace_bytes < plan.total_bytes)
@@ -3173,6 +3278,11 @@ tq_status decode_common(const tq_format* fmt, const tq_tables* tables, const tq_
   }
   if (int64_t(a.n_app) + plan.n_workgroups > 0x7FFFFFFF) return fail(TQ_ERR_INVALID_ARG, "too many workgroups");
   const dim3 grid(unsigned(a.n_app + plan.n_workgroups));
+  if (args_out != nullptr) {   // the caller launches the decode (the preparation is enqueued)
+    *args_out = a;
+    if (decode_wgs_out != nullptr) *decode_wgs_out = int(plan.n_workgroups);
+    return TQ_OK;
+  }
   if (stages & kStagePartials) {
     if ((st = launch_decode<SCORE>(mk, SCORE ? 0 : bv, a, grid, hs, app ? app->ca : CompressArgs{}))) return st;
     if ((st = launch_status("decode"))) return st;
@@ -3477,6 +3587,125 @@ tq_status compress_run(const tq_format* fmt, const tq_tables* tables, const tq_c
 }  // namespace
 }  // namespace tq
 
+namespace tq {
+namespace {
+// tq_decode_step_parts (step: each part's append, query preparation and
+// decode) and tq_decode_attend_parts (!step: the decode alone, on queries
+// prepared in each part's workspace).
+tq_status decode_parts(const tq_step_part* parts, int32_t n_parts, bool step, int32_t dtype, int64_t n_tokens,
+                       const int64_t* slots, int64_t slot0, int32_t batch, int32_t n_q_heads, const int64_t* seq_start,
+                       const int32_t* seq_len, int64_t max_seq_len, float scale, void* stream) {
+  clear_error();
+  constexpr int kMaxParts = 8;
+  if (!parts || n_parts < 1 || n_parts > kMaxParts)
+    return fail(TQ_ERR_INVALID_ARG, "n_parts=%d (1 to %d, parts not NULL)", n_parts, kMaxParts);
+  // Every part is checked before anything is enqueued.
+  FusedAppend app[kMaxParts];
+  bool nothing[kMaxParts] = {};
+  int64_t app_wgs = 0;
+  for (int i = 0; i < n_parts; ++i) {
+    const tq_step_part& P = parts[i];
+    tq_status st = decode_common<false>(P.fmt, P.tables, P.cache, P.q, batch, n_q_heads, seq_start, seq_len,
+                                        max_seq_len, scale, P.out, P.workspace, P.workspace_bytes, stream,
+                                        (step ? kStageAll : kStagePartials | kStageMerge) | kStageCheckOnly);
+    if (st) return st;
+    nothing[i] = true;
+    int64_t wgs = 0;
+    if (step && (st = compress_setup(P.fmt, P.tables, P.cache, P.k, P.v, dtype, P.layer0, P.n_layers, n_tokens, slots,
+                                     slot0, 0, app[i].ca, wgs, nothing[i])))
+      return st;
+    if (!nothing[i]) {
+      const int64_t groups = (n_tokens * app[i].ca.H + kAppendItems - 1) / kAppendItems;
+      app[i].groups = int(groups < 0x7FFFFFFF ? groups : 0x7FFFFFFF);
+      app[i].layers = P.n_layers;
+      app[i].lo = slots ? 0 : slot0;
+      app[i].hi = slots ? P.cache->capacity : slot0 + n_tokens;
+      app_wgs += groups * P.n_layers;
+    }
+  }
+  // One launch for two parts whose second is fp16 / fp16: the decode
+  // workgroups are shared in proportion to the bytes each part reads per token
+  // of the batch, and each part's split is made for its share (taken only when
+  // both splits fit the given workspaces, which are sized for a launch of
+  // their own).
+  bool pair = n_parts == 2 && parts[1].fmt->k_bits == 0 && parts[1].fmt->v_bits == 0 &&
+              app_wgs <= kMaxFusedAppend && kDecodeWorkgroups - app_wgs >= 2;
+  const int nd_total = kDecodeWorkgroups - int(pair ? app_wgs : 0);
+  int b1 = 1;
+  if (pair) {
+    double w[2];
+    for (int i = 0; i < 2; ++i) {
+      const tq_format* f = parts[i].fmt;
+      const int d = f->d;
+      const double kb = f->k_bits > 0 ? d * (f->k_bits - 1) / 8 + d / 8 + 8 : 2 * d;
+      const double vb = f->v_bits > 0 ? d * f->v_bits / 8 + 4 : 2 * d;
+      w[i] = double(parts[i].cache->n_layers) * parts[i].cache->n_kv_heads * (kb + vb);
+    }
+    b1 = int(double(nd_total) * w[0] / (w[0] + w[1]) + 0.5);
+    b1 = b1 < 1 ? 1 : (b1 > nd_total - 1 ? nd_total - 1 : b1);
+    for (int i = 0; i < 2; ++i) {
+      const tq_step_part& P = parts[i];
+      const SplitPlan plan = plan_decode(P.fmt->d, P.cache->n_layers, batch, P.cache->n_kv_heads, n_q_heads,
+                                         max_seq_len, i == 0 ? b1 : nd_total - b1);
+      if (P.workspace_bytes < plan.total_bytes) pair = false;
+    }
+  }
+  if (!pair) {
+    for (int i = 0; i < n_parts; ++i) {
+      const tq_step_part& P = parts[i];
+      const tq_status st =
+          step ? tq_decode_step(P.fmt, P.tables, P.cache, P.k, P.v, dtype, P.layer0, P.n_layers, n_tokens, slots,
+                                slot0, P.q, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, P.out,
+                                P.workspace, P.workspace_bytes, stream)
+               : tq_decode_attend(P.fmt, P.tables, P.cache, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale,
+                                  P.out, P.workspace, P.workspace_bytes, stream);
+      if (st) return st;
+    }
+    return TQ_OK;
+  }
+  DecodeArgs a[2];
+  int nd[2] = {0, 0};
+  for (int i = 0; i < 2; ++i) {
+    const tq_step_part& P = parts[i];
+    // the part's decode arguments (nothing is enqueued)
+    const tq_status st = decode_common<false>(P.fmt, P.tables, P.cache, P.q, batch, n_q_heads, seq_start, seq_len,
+                                              max_seq_len, scale, P.out, P.workspace, P.workspace_bytes, stream,
+                                              kStagePartials | kStageMerge, nothing[i] ? nullptr : &app[i],
+                                              i == 0 ? b1 : nd_total - b1, &a[i], &nd[i]);
+    if (st) return st;
+  }
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const tq_format* f0 = parts[0].fmt;
+  if (step) {
+    // both query preparations in one launch (they also zero the parts' merge
+    // and append counts)
+    const int runs = (batch * n_q_heads + kQprepRows - 1) / kQprepRows;
+    const int64_t blocks = int64_t(4) * (parts[0].cache->n_layers + parts[1].cache->n_layers) * runs;
+    if (blocks > 0x7FFFFFFF) return fail(TQ_ERR_INVALID_ARG, "too many query preparation blocks");
+    float* qp[2] = {static_cast<float*>(parts[0].workspace), static_cast<float*>(parts[1].workspace)};
+    if (f0->k_bits > 0)
+      hipLaunchKernelGGL(qprep_pair_kernel<true>, dim3(unsigned(blocks)), dim3(256), 0, hs, parts[0].q,
+                         parts[0].tables->pi, parts[0].tables->s, qp[0], a[0].done, parts[0].cache->n_kv_heads,
+                         parts[0].cache->n_layers, parts[1].q, qp[1], a[1].done, parts[1].cache->n_kv_heads,
+                         parts[1].cache->n_layers, batch, n_q_heads);
+    else
+      hipLaunchKernelGGL(qprep_pair_kernel<false>, dim3(unsigned(blocks)), dim3(256), 0, hs, parts[0].q,
+                         parts[0].tables->pi, parts[0].tables->s, qp[0], a[0].done, parts[0].cache->n_kv_heads,
+                         parts[0].cache->n_layers, parts[1].q, qp[1], a[1].done, parts[1].cache->n_kv_heads,
+                         parts[1].cache->n_layers, batch, n_q_heads);
+    tq_status st = launch_status("qprep (two parts)");
+    if (st) return st;
+  }
+  const dim3 grid(unsigned(a[0].n_app + a[1].n_app + nd[0] + nd[1]));
+  const tq_status st = launch_decode_pair(f0->k_bits > 0 ? f0->k_bits - 1 : 0, f0->v_bits, a[0], app[0].ca, a[1],
+                                          app[1].ca, nd[0], grid, hs);
+  if (st) return st;
+  return launch_status("decode (two parts)");
+}
+
+}  // namespace
+}  // namespace tq
+
 extern "C" {
 
 tq_status tq_decode_attention_noalloc(const tq_format* fmt, const tq_tables* tables, const tq_cache* cache,
@@ -3680,6 +3909,21 @@ tq_status tq_decode_step(const tq_format* fmt, const tq_tables* tables, const tq
   app.hi = slots ? cache->capacity : slot0 + n_tokens;
   return decode_common<false>(fmt, tables, cache, q, batch, n_q_heads, seq_start, seq_len, max_seq_len, scale, out,
                               workspace, workspace_bytes, stream, kStageAll, &app);
+}
+
+tq_status tq_decode_step_parts(const tq_step_part* parts, int32_t n_parts, int32_t dtype, int64_t n_tokens,
+                               const int64_t* slots, int64_t slot0, int32_t batch, int32_t n_q_heads,
+                               const int64_t* seq_start, const int32_t* seq_len, int64_t max_seq_len, float scale,
+                               void* stream) {
+  return tq::decode_parts(parts, n_parts, true, dtype, n_tokens, slots, slot0, batch, n_q_heads, seq_start, seq_len,
+                          max_seq_len, scale, stream);
+}
+
+tq_status tq_decode_attend_parts(const tq_step_part* parts, int32_t n_parts, int32_t batch, int32_t n_q_heads,
+                                 const int64_t* seq_start, const int32_t* seq_len, int64_t max_seq_len, float scale,
+                                 void* stream) {
+  return tq::decode_parts(parts, n_parts, false, TQ_DTYPE_F32, 0, nullptr, 0, batch, n_q_heads, seq_start, seq_len,
+                          max_seq_len, scale, stream);
 }
 
 tq_status tq_decode_step_check(const tq_format* fmt, int32_t n_layers, int32_t batch, int32_t n_kv_heads,

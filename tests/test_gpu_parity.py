@@ -537,6 +537,88 @@ def test_decode_step_append_inside_decode_launch(mode, k_bits, v_bits, hq, lens,
     _say("worst out abs", f"{worst:.2e}")
 
 
+@pytest.mark.parametrize("formats,hq,lens,mode", [
+    (((0, 4, 3), (0, 0, 2)), 28, (700,), "slot0"),                   # fp16 keys / 4-bit values beside fp16 layers
+    (((4, 4, 2), (0, 0, 2)), 16, (300, 45, 0, 129), "slots"),        # ragged batch, packed keys
+    (((3, 2, 1), (0, 0, 1)), 8, (100,), "slot0"),                     # one layer each
+    (((3, 2, 2), (4, 4, 1)), 8, (70, 200), "slots"),                  # second part not fp16: one call per part
+    (((0, 4, 1), (0, 0, 1), (4, 4, 1)), 8, (90,), "slot0"),           # three parts: one call per part
+])
+def test_decode_step_parts(formats, hq, lens, mode):
+    """tq_decode_step_parts: a model whose layers use different formats, one
+    cache per format sharing the batch and the new tokens' slots.  Two parts
+    whose second is fp16 / fp16 run both appends and decodes in one launch;
+    other layouts make one tq_decode_step per part.  Every step's outputs are
+    checked against the oracle on the GPU's caches (which then hold the new
+    tokens), and tq_decode_attend_parts on queries prepared per part likewise."""
+    import kv_cache_quantization_norm_amd as tq
+    _say("decode step parts", formats, hq, lens, mode)
+    H, steps, stride = 4, 2, 1024
+    B = len(lens)
+    g = torch.Generator().manual_seed(47)
+    starts = [b * stride for b in range(B)]
+    st = torch.tensor(starts, dtype=torch.int64, device="cuda")
+    parts, fmts = [], []
+    max_len = max(lens) + steps
+    for kb, vb, L in formats:
+        fmt = quant.Format(128, kb, vb)
+        tfmt = pu.tq_format(fmt)
+        tables = tq.Tables.create(tfmt, list(range(L)))
+        dev = tq.Cache.allocate(tfmt, L, H, B * stride)
+        for b, n in enumerate(lens):
+            if n:
+                k = torch.randn(L, n, H, 128, generator=g).to("cuda", torch.bfloat16)
+                v = torch.randn(L, n, H, 128, generator=g).to("cuda", torch.bfloat16)
+                tq.tq_compress_kv(tfmt, tables, dev, k, v, slot0=starts[b])
+        ws = tq.workspace_for(tfmt, dev, B, hq, max_len)
+        ws.fill_(0xFF)
+        parts.append(tq.StepPart(tfmt, tables, dev, None, None, None, None, ws))
+        fmts.append(fmt)
+    cur = list(lens)
+    worst = 0.0
+
+    def check(outs, Qs):
+        nonlocal worst
+        for fmt, part, o, qn in zip(fmts, parts, outs, Qs):
+            ora = pu.download_cache(part.cache, fmt)
+            for layer in range(part.cache.n_layers):
+                pi, s, cbk, cbv = pu.oracle_tables(fmt, layer)
+                ref = attention.decode_attention(ora[layer], qn[layer], starts, cur, pi, s, cbk, cbv)
+                worst = max(worst, pu.check_outputs(o[layer], ref))
+
+    for step in range(steps):
+        if mode == "slots":
+            slots = torch.tensor([starts[b] + cur[b] if cur[b] else -1 for b in range(B)], dtype=torch.int64,
+                                 device="cuda")
+            extra = dict(slots=slots)
+            n_new = B
+            cur = [n + 1 if n else 0 for n in cur]
+        else:
+            extra = dict(slot0=starts[0] + cur[0])
+            n_new = 1
+            cur = [cur[0] + 1]
+        Qs = []
+        for part in parts:
+            L = part.cache.n_layers
+            part.k = torch.randn(L, n_new, H, 128, generator=g).to("cuda", torch.bfloat16)
+            part.v = torch.randn(L, n_new, H, 128, generator=g).to("cuda", torch.bfloat16)
+            part.q = torch.randn(L, B, hq, 128, generator=g).cuda()
+            part.out = torch.full((L, B, hq, 128), float("nan"), device="cuda")
+            Qs.append(part.q.cpu().numpy())
+        ln = torch.tensor(cur, dtype=torch.int32, device="cuda")
+        tq.tq_decode_step_parts(parts, st, ln, max_len, **extra)
+        torch.cuda.synchronize()
+        check([part.out.cpu().numpy() for part in parts], Qs)
+    # the decode alone, on queries prepared per part
+    for part in parts:
+        tq.tq_decode_prepare(part.fmt, part.tables, part.cache, part.q, max_len, part.workspace)
+        part.out = torch.full_like(part.out, float("nan"))
+    tq.tq_decode_attend_parts(parts, st, ln, max_len)
+    torch.cuda.synchronize()
+    check([part.out.cpu().numpy() for part in parts], Qs)
+    _say("worst out abs", f"{worst:.2e}")
+
+
 def test_decode_step_append_wait_give_up_is_reported():
     """The decode waves' wait for the step's append is bounded; when it ends
     unmet the wave records it and tq_decode_step_check reports it.  The host
