@@ -238,20 +238,32 @@ def attend_parts(tq, parts, i, stream):
 
 def timed(torch, stream, fn, warmup, steps):
     """Mean ms per call of fn(i) over `steps` calls after `warmup` calls, with
-    two HIP events on `stream` around the timed calls."""
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(steps):
-        fn(warmup + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    two HIP events on `stream` around the timed calls.  Python's garbage
+    collector stays off meanwhile: a collection that frees device memory
+    synchronizes the device and would stall the launches being timed."""
+    import gc
+    gc.collect()
+    gc.disable()
+    try:
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            fn(warmup + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
     return e0.elapsed_time(e1) / steps
 
 
 def run_workload(tq, torch, w, short, args, stream, dev):
+    import gc
+    gc.collect()                 # the previous workload's buffers, freed before anything is timed
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     t0 = time.time()
     parts = build_parts(tq, torch, w, dev)
     total_cache = sum(p.cache.nbytes() for p in parts)

@@ -2386,9 +2386,33 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
         }
         // K0, K1 and V0 now hold the chunks of tickets t0 and t1
         if (swap) {
-          const KData k = K0;
-          K0 = K1;
-          K1 = k;
+          // member by member, only what the format uses: a whole-struct copy
+          // also moves the members it leaves unwritten, which the compiler
+          // then keeps in per-thread memory (placed in LDS and addressed
+          // through the dispatch packet, read by every wave at its start)
+          if constexpr (MK > 0) {
+#pragma unroll
+            for (int T = 0; T < 2; ++T) {
+#pragma unroll
+              for (int u = 0; u < MKW; ++u) {
+                const uint32_t t = K0.kw[T][u];
+                K0.kw[T][u] = K1.kw[T][u];
+                K1.kw[T][u] = t;
+              }
+              const uint32_t t = K0.sg[T];
+              K0.sg[T] = K1.sg[T];
+              K1.sg[T] = t;
+            }
+          } else {
+#pragma unroll
+            for (int T = 0; T < 2; ++T)
+#pragma unroll
+              for (int s2 = 0; s2 < 4; ++s2) {
+                const half8 t = K0.kf[T][s2];
+                K0.kf[T][s2] = K1.kf[T][s2];
+                K1.kf[T][s2] = t;
+              }
+          }
           V0 = V1;
         }
         pre = true;
@@ -3624,10 +3648,12 @@ tq_status decode_parts(const tq_step_part* parts, int32_t n_parts, bool step, in
     }
   }
   // One launch for two parts whose second is fp16 / fp16: the decode
-  // workgroups are shared in proportion to the bytes each part reads per token
-  // of the batch, and each part's split is made for its share (taken only when
-  // both splits fit the given workspaces, which are sized for a launch of
-  // their own).
+  // workgroups are shared in proportion to each part's cost per token of the
+  // batch, taken as the bytes it reads per token-head plus 128 (a 32-token
+  // chunk costs a workgroup about as long as reading 4 KB besides its bytes,
+  // measured on fp16 keys with 4-bit or fp16 values), and each part's split is
+  // made for its share (taken only when both splits fit the given workspaces,
+  // which are sized for a launch of their own).
   bool pair = n_parts == 2 && parts[1].fmt->k_bits == 0 && parts[1].fmt->v_bits == 0 &&
               app_wgs <= kMaxFusedAppend && kDecodeWorkgroups - app_wgs >= 2;
   const int nd_total = kDecodeWorkgroups - int(pair ? app_wgs : 0);
@@ -3639,7 +3665,7 @@ tq_status decode_parts(const tq_step_part* parts, int32_t n_parts, bool step, in
       const int d = f->d;
       const double kb = f->k_bits > 0 ? d * (f->k_bits - 1) / 8 + d / 8 + 8 : 2 * d;
       const double vb = f->v_bits > 0 ? d * f->v_bits / 8 + 4 : 2 * d;
-      w[i] = double(parts[i].cache->n_layers) * parts[i].cache->n_kv_heads * (kb + vb);
+      w[i] = double(parts[i].cache->n_layers) * parts[i].cache->n_kv_heads * (kb + vb + 128);
     }
     b1 = int(double(nd_total) * w[0] / (w[0] + w[1]) + 0.5);
     b1 = b1 < 1 ? 1 : (b1 > nd_total - 1 ? nd_total - 1 : b1);
