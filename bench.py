@@ -238,13 +238,23 @@ def attend_parts(tq, parts, i, stream):
 
 def timed(torch, stream, fn, warmup, steps):
     """Mean ms per call of fn(i) over `steps` calls after `warmup` calls, with
-    two HIP events on `stream` around the timed calls.  Python's garbage
+    two HIP events on `stream` around the timed calls; about 0.1 s of the same
+    calls comes first, untimed, besides the warm-up calls.  Python's garbage
     collector stays off meanwhile: a collection that frees device memory
     synchronizes the device and would stall the launches being timed."""
     import gc
     gc.collect()
     gc.disable()
     try:
+        # spin-up: about 0.1 s of the same work first (after seconds of host-side
+        # setup the GPU's clocks take longer to rise than a few launches last)
+        t_end = time.perf_counter() + 0.1
+        j = 0
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                fn(j)
+                j += 1
+            torch.cuda.synchronize()
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
