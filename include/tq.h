@@ -414,8 +414,9 @@ typedef struct tq_step_part {
  * fp16 keys and values (k_bits = v_bits = 0), and both appends small enough to
  * run inside the decode launch (at most 32 append workgroups in all), the two
  * decodes run in one launch: the decode workgroups are shared between the
- * parts in proportion to the bytes each reads per token, so the launch pays
- * one start and one end instead of two.  Otherwise the parts' tq_decode_step
+ * parts in proportion to an estimate of each part's work per token (the bytes
+ * it reads plus a fixed cost per token), so the launch pays one start and one
+ * end instead of two.  Otherwise the parts' tq_decode_step
  * calls are made one after the other.  n_parts: 1 to 8; parts must not be
  * NULL; calls on one workspace must not overlap. */
 tq_status tq_decode_step_parts(const tq_step_part* parts, int32_t n_parts, int32_t dtype, int64_t n_tokens,
