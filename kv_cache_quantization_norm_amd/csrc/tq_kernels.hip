@@ -1255,6 +1255,28 @@ __device__ __forceinline__ void build_vrep(uint32_t* lut, float cl, int tid, int
     *reinterpret_cast<u32x4*>(lut + e * 64 + (x & 15) * 4) = u32x4{w, w, w, w};
   }
 }
+// The 2-bit value table in 32 lane-private copies (64 KB): entry e (a byte of
+// four codes) holds their four alpha-scaled fp16 centroids (8 bytes) in copy c
+// at byte e * 256 + 8 c; lanes l and l + 32 share a copy, and the 16 lanes of
+// a read pass hit 16 different copies.
+__device__ __forceinline__ void build_vrep2(uint32_t* lut, float cl, int tid, int nt) {
+  for (int x = tid; x < 256 * 16; x += nt) {   // entry x / 16, copies 2 (x % 16) and 2 (x % 16) + 1
+    const int e = x >> 4;
+    const uint32_t w0 = uint32_t(f16_bits(lane_cent(cl, e & 3))) | (uint32_t(f16_bits(lane_cent(cl, (e >> 2) & 3))) << 16);
+    const uint32_t w1 = uint32_t(f16_bits(lane_cent(cl, (e >> 4) & 3))) | (uint32_t(f16_bits(lane_cent(cl, e >> 6))) << 16);
+    *reinterpret_cast<u32x4*>(lut + e * 64 + (x & 15) * 4) = u32x4{w0, w1, w0, w1};
+  }
+}
+// Two bytes of code word `bits` (the byte selectors s0 and s1, per lane) ->
+// 8 fp16 centroids; each address is one byte permute: byte 0 = 8 (lane % 32),
+// byte 1 = the code byte, byte 2 = the table's 64 KB page (in lane8) or zero.
+__device__ __forceinline__ half8 deq8_vrep2(uint32_t bits, uint32_t lane8, uint32_t s0, uint32_t s1,
+                                            const unsigned char* base) {
+  const uint32_t a0 = __builtin_amdgcn_perm(bits, lane8, s0);
+  const uint32_t a1 = __builtin_amdgcn_perm(bits, lane8, s1);
+  const u32x2 w0 = *reinterpret_cast<const u32x2*>(base + a0), w1 = *reinterpret_cast<const u32x2*>(base + a1);
+  return as_half8(u32x4{w0[0], w0[1], w1[0], w1[1]});
+}
 template <bool PAGE>
 __device__ __forceinline__ half8 deq8_vrep(uint32_t bits, uint32_t lane4, const unsigned char* base) {
   // byte 0 of the address: 4 lane; byte 1: code byte k; byte 2: the page (PAGE) or zero; byte 3: zero
@@ -1274,13 +1296,21 @@ struct DecodeLayout {
   using KL = KLut<(MK > 0 && !KWIDE ? MK : 1)>;
   static constexpr int KT = MK > 0 ? (KWIDE ? (1 << MK) : KL::E * KL::EW) : 1;   // key table dwords
   static constexpr int KP = MK > 0 && !KWIDE && KL::NC > 2 ? KL::PAIRS * KL::PW : 1;   // pair-table dwords (if separate)
-  static constexpr bool VREP = BV == 4;                                          // lane-private value table
+  static constexpr int RED_FULL = kDecodeWaves * kMaxGroup * D * 4;
+  static constexpr int LIVE_BYTES = (kRaggedMaxBatch + 1) * 4;
+  static constexpr int MISC_BYTES = kDecodeWaves * 128 * 4 + 2 * kDecodeWaves * 16 * 4 + 2 * 2 * 4 * 64 * 16 + 16 + LIVE_BYTES;
+  // Lane-private value table (64 KB): 4-bit values always; 2-bit values when
+  // it fits beside the key tables with the wave merge still in LDS.
+  static constexpr bool VREP2 =
+      BV == 2 && (MK > 0 ? 256 * 16 : 0) + (KT + KP) * 4 + 1024 + 256 * 64 * 4 + RED_FULL + MISC_BYTES <= 160 * 1024;
+  static constexpr bool VREP = BV == 4 || VREP2;
   static constexpr int VW = VREP ? 256 * 64 : (BV > 0 ? Lut<BV, false>::WORDS : 1);
   // Tables first, each starting below 64 KB so that lookups carry the table
   // offset as an instruction immediate (the lane-private value table may
   // start past 64 KB: its addresses carry the page, see deq8_vrep).
-  // Order: signs, then the small value tables (1 or 2 bits), the key table
-  // and its pair table, then the lane-private 4-bit value table.
+  // Order: signs, then the small value tables (1 bit, or 2 bits when not
+  // lane-private), the key table and its pair table, then the lane-private
+  // value table (4 bits, or 2 bits when it fits).
   static constexpr int OFF_S = 0;
   static constexpr int S_END = MK > 0 ? 256 * 16 : 0;
   static constexpr int OFF_K = VREP ? S_END : ((S_END + VW * 4 + 255) / 256) * 256;
@@ -1288,9 +1318,6 @@ struct DecodeLayout {
   static constexpr int OFF_V = VREP ? ((OFF_PHI + KP * 4 + 255) / 256) * 256 : S_END;
   static constexpr int V_PAGE = VREP && OFF_V >= 65536 ? 1 : 0;
   static constexpr int OFF_TAB_END = VREP ? ((OFF_V + VW * 4 + 15) / 16) * 16 : ((OFF_PHI + KP * 4 + 15) / 16) * 16;
-  static constexpr int LIVE_BYTES = (kRaggedMaxBatch + 1) * 4;
-  static constexpr int MISC_BYTES = kDecodeWaves * 128 * 4 + 2 * kDecodeWaves * 16 * 4 + 2 * 2 * 4 * 64 * 16 + 16 + LIVE_BYTES;
-  static constexpr int RED_FULL = kDecodeWaves * kMaxGroup * D * 4;
   // The wave merge ([wave][head][coordinate] fp32) stays in LDS when the
   // tables leave room for it, else it goes through the workgroup's slice of
   // the workspace (L2).
@@ -1341,6 +1368,7 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
   [[maybe_unused]] constexpr auto MISC_BYTES = LY::MISC_BYTES;
   [[maybe_unused]] constexpr auto RED_FULL = LY::RED_FULL;
   [[maybe_unused]] constexpr auto RED_LDS = LY::RED_LDS;
+  [[maybe_unused]] constexpr auto VREP2 = LY::VREP2;
   [[maybe_unused]] constexpr auto OFF_RED = LY::OFF_RED;
   [[maybe_unused]] constexpr auto RED_BYTES = LY::RED_BYTES;
   [[maybe_unused]] constexpr auto OFF_NX = LY::OFF_NX;
@@ -1392,6 +1420,11 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
   const int col = lane & 15, q = lane >> 4;   // MFMA column (head / coordinate) and k-group
   const bool lo_half = col >= 8;
   const uint32_t lane4 = uint32_t(lane) * 4 | uint32_t(V_PAGE << 16);
+  // 2-bit values (VREP2): lane (col, q) reads code bytes 2 (q % 2) and 2 (q % 2) + 1
+  // of its word (tokens 8 q .. 8 q + 3 and 8 q + 4 .. 8 q + 7)
+  const uint32_t lane8 = uint32_t(lane & 31) * 8 | uint32_t(V_PAGE << 16);
+  const uint32_t vsel0 = 0x0C000000u | (V_PAGE ? 0x00020000u : 0x000C0000u) | ((4u + 2u * (q & 1)) << 8);
+  const uint32_t vsel1 = vsel0 + 0x100u;
 
   // Scores are kept in base-2 units (scaled by log2 e) so that the softmax
   // weights are plain exp2; tq_score writes natural-unit logits.
@@ -1898,6 +1931,8 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
           const int vb = v0 + u;
           if constexpr (BV == 4) {
             vd[u] = deq8_vrep<V_PAGE != 0>(V.vw[vb], lane4, vrep_base);
+          } else if constexpr (VREP2) {
+            vd[u] = deq8_vrep2(V.vw[vb], lane8, vsel0, vsel1, vrep_base);
           } else if constexpr (BV > 0) {
             uint32_t bits = V.vw[vb];
             if constexpr (BV == 3) bits = __builtin_amdgcn_alignbit(V.vw2[vb], bits, (24 * q) & 31) & 0xFFFFFFu;
@@ -2293,7 +2328,9 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
     else
       build_kpairs<MK>(lut_k, kcl, tid, NT);
   }
-  if constexpr (VREP)
+  if constexpr (VREP2)
+    build_vrep2(lut_v, vcl, tid, NT);
+  else if constexpr (VREP)
     build_vrep(lut_v, vcl, tid, NT);
   else if constexpr (BV > 0)
     build_lut<BV, false>(lut_v, vcl, tid, NT);
