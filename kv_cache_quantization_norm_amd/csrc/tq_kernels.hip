@@ -1324,6 +1324,11 @@ struct DecodeLayout {
   static constexpr bool RED_LDS = !SCORE && OFF_TAB_END + RED_FULL + MISC_BYTES <= 160 * 1024;
   static constexpr int OFF_RED = OFF_TAB_END;
   static constexpr int RED_BYTES = RED_LDS ? RED_FULL : 0;
+  // Without room for it, a workgroup's last group holds the wave merge over a
+  // table it no longer needs (the key table, else the lane-private value
+  // table) when that holds its 32 KB; earlier groups use the workspace.
+  static constexpr int OFF_OVL = !RED_LDS && !SCORE ? (KT * 4 >= RED_FULL ? OFF_K : (VREP ? OFF_V : -1)) : -1;
+  static constexpr bool OVL = OFF_OVL >= 0;
   static constexpr int OFF_NX = OFF_RED + RED_BYTES;
   static constexpr int OFF_MW = OFF_NX + kDecodeWaves * 128 * 4;
   static constexpr int OFF_LW = OFF_MW + kDecodeWaves * 16 * 4;
@@ -1368,6 +1373,7 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
   [[maybe_unused]] constexpr auto MISC_BYTES = LY::MISC_BYTES;
   [[maybe_unused]] constexpr auto RED_FULL = LY::RED_FULL;
   [[maybe_unused]] constexpr auto RED_LDS = LY::RED_LDS;
+  [[maybe_unused]] constexpr auto OVL = LY::OVL;
   [[maybe_unused]] constexpr auto VREP2 = LY::VREP2;
   [[maybe_unused]] constexpr auto OFF_RED = LY::OFF_RED;
   [[maybe_unused]] constexpr auto RED_BYTES = LY::RED_BYTES;
@@ -1414,6 +1420,8 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
   }
   // this workgroup's slice of the workspace for the wave merge (when not in LDS)
   float* const red_wg = RED_LDS ? nullptr : a.red_g + int64_t(wg) * (kDecodeWaves * kMaxGroup * D);
+  // the wave merge over a dead table (last group only, see DecodeLayout)
+  float* const red_ov = OVL ? reinterpret_cast<float*>(dsm + (OVL ? LY::OFF_OVL : 0)) : nullptr;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1957,7 +1965,7 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
 
   // Writes the wave's state into its merge slot (`have`), or marks the slot
   // empty without touching the registers (which may hold another piece).
-  auto flush = [&](bool have) {
+  auto flush = [&](bool have, bool ov = false) {
     if constexpr (!SCORE) {
       if (!have) {
         if (q == 0 && !lo_half) {
@@ -1978,7 +1986,7 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
         lw[wave][col] = live ? l_tot : 0.f;
       }
       if (live && !lo_half) {
-        float* rw = (RED_LDS ? red : red_wg) + (wave * kMaxGroup + col) * D;
+        float* rw = (RED_LDS ? red : (OVL && ov ? red_ov : red_wg)) + (wave * kMaxGroup + col) * D;
         const float so = sig * inv_alpha_v;   // the value norms' normaliser and the value tables' scale
 #pragma unroll
         for (int vb = 0; vb < 8; ++vb) {
@@ -1992,7 +2000,7 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
   // problem context Rp, slot `seg`: (max, sum of exponentials, accumulator[D])
   // per head, the waves summed in wave order (the same for every thread).
   // Thread t handles coordinate t % 128 of heads t / 128 and t / 128 + 4.
-  auto merge = [&](const Run& Rp, int seg) {
+  auto merge = [&](const Run& Rp, int seg, bool ov = false) {
     if constexpr (!SCORE) {
       const int ng = a.G - Rp.hg * kMaxGroup < kMaxGroup ? a.G - Rp.hg * kMaxGroup : kMaxGroup;
       const int64_t pbase = (int64_t(Rp.layer) * a.batch + Rp.b) * a.Hq + Rp.hk * a.G + Rp.hg * kMaxGroup;
@@ -2005,12 +2013,16 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
           // empty wave slot (maximum -inf) contributes nothing, whatever its
           // accumulator holds
           float mv[kDecodeWaves], rv[kDecodeWaves], lv[kDecodeWaves];
+          if (OVL && ov) {
+#pragma unroll
+            for (int w = 0; w < kDecodeWaves; ++w) rv[w] = red_ov[(w * kMaxGroup + g) * D + i];
+          }
 #pragma unroll
           for (int w = 0; w < kDecodeWaves; ++w) {
             mv[w] = mw[w][g];
             if constexpr (RED_LDS)
               rv[w] = red[(w * kMaxGroup + g) * D + i];
-            else   // written by other waves of this workgroup: read past the vector L1
+            else if (!(OVL && ov))   // written by other waves of this workgroup: read past the vector L1
               rv[w] = __hip_atomic_load(const_cast<float*>(uniform_ptr(red_wg + w * kMaxGroup * D)) + g * D + i,
                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             lv[w] = lw[w][g];
@@ -2365,6 +2377,7 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
     }
     // the wave's next three tickets (relative to base)
     int t0 = wave, t1 = wave + kDecodeWaves, t2 = wave + 2 * kDecodeWaves;
+    const bool last_ov = OVL && G.b_end >= c_last;   // the workgroup's last group: merge over a dead table
     bool had_a = false, had_b = false;
 #pragma unroll 1
     while (t0 < G.n_tickets) {
@@ -2468,7 +2481,7 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
         }
       }
       if (in_a) {
-        flush(true);
+        if (!(last_ov && !G.has_b)) flush(true);   // (else after the barrier below)
         had_a = true;
       } else {
         had_b = true;
@@ -2476,17 +2489,21 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
     }
     // ---- merge the group's pieces
     if (!had_a) flush(false);
+    if (last_ov && !G.has_b) {
+      __syncthreads();   // every wave is done with the tables
+      if (had_a) flush(true, true);
+    }
     if constexpr (!RED_LDS) __builtin_amdgcn_s_waitcnt(0);   // this wave's merge stores are complete
     __syncthreads();
     const int next_base = uni(counter[0]);   // every draw of the group is done
-    merge(G.ra, wg - pfirst(G.pa) / cpw);
+    merge(G.ra, wg - pfirst(G.pa) / cpw, last_ov && !G.has_b);
     arrive(G.pa, G.ra);
     if (G.has_b) {
-      __syncthreads();
-      flush(had_b);
+      __syncthreads();   // (and every wave is done with the tables)
+      flush(had_b, last_ov);
       if constexpr (!RED_LDS) __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      merge(G.rb, wg - G.a_end / cpw);
+      merge(G.rb, wg - G.a_end / cpw, last_ov);
       arrive(G.pb, G.rb);
     }
     __syncthreads();
