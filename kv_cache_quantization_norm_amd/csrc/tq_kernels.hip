@@ -3723,6 +3723,14 @@ tq_status decode_parts(const tq_step_part* parts, int32_t n_parts, bool step, in
     }
     b1 = int(double(nd_total) * w[0] / (w[0] + w[1]) + 0.5);
     b1 = b1 < 1 ? 1 : (b1 > nd_total - 1 ? nd_total - 1 : b1);
+    // workgroups part 2's split leaves unused (an aligned split may take
+    // fewer than its share) go to part 1
+    {
+      const tq_step_part& P = parts[1];
+      const SplitPlan p2 = plan_decode(P.fmt->d, P.cache->n_layers, batch, P.cache->n_kv_heads, n_q_heads,
+                                       max_seq_len, nd_total - b1);
+      b1 = nd_total - int(p2.n_workgroups);
+    }
     for (int i = 0; i < 2; ++i) {
       const tq_step_part& P = parts[i];
       const SplitPlan plan = plan_decode(P.fmt->d, P.cache->n_layers, batch, P.cache->n_kv_heads, n_q_heads,
