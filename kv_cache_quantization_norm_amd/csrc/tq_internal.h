@@ -18,6 +18,13 @@ constexpr int kDecodeWaves = 8;  // waves per decode workgroup (one workgroup pe
 constexpr int kDecodeWorkgroups = 256;   // decode workgroups: one per CU of an MI355X
 constexpr int kMaxGroup = 8;     // query heads handled by one decode wave
 constexpr int kCrossingChunks = 16;   // measured cost of a problem change inside a decode workgroup, in chunks
+// Ragged split: a problem shorter than the mean range is charged up to
+// kContainChunks more, in proportion to how much shorter it is (a range that
+// holds a problem whole, with pieces of others on both sides, takes a second
+// group: a merge and a pipeline restart in mid-range, measured at about 90
+// chunks of time; the weight was tuned on 16-sequence batches of 4 k - 32 k
+// tokens).
+constexpr int kContainChunks = 160;
 constexpr int kRaggedMaxBatch = 1024;  // largest batch whose decode may take the ragged split (its prefix sits in LDS)
 
 // Format checks shared by all entry points.  `device` additionally requires
@@ -42,10 +49,11 @@ struct SplitPlan {
   int n_head_groups = 0;
   // Ragged split (decided by the kernel from the sequence lengths, batch > 1):
   // the workgroups share the chunks that hold tokens (each problem followed
-  // by kCrossingChunks of padding), in ranges of at least cpw_min chunks, so
-  // that a problem (at most cpp_real = ceil(max_len / 32) chunks plus the
-  // padding) leaves at most seg_cap pieces; seg_cap >= seg_max is the partial
-  // slots per query head in the workspace.
+  // by kCrossingChunks to kCrossingChunks + kContainChunks of padding), in
+  // ranges of at least cpw_min chunks, so that a problem (at most cpp_real =
+  // ceil(max_len / 32) chunks plus the padding) leaves at most seg_cap
+  // pieces; seg_cap >= seg_max is the partial slots per query head in the
+  // workspace.
   int64_t cpp_real = 0;
   int64_t cpw_min = 0;
   int64_t seg_cap = 0;

@@ -1455,10 +1455,12 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
 
   // ---- the chunk sequence dealt to the workgroups in ranges of cpw: every
   // problem's cpp chunks, problem-major; or (rag) only the chunks that hold
-  // tokens, each problem followed by kCrossingChunks chunks of padding (never
-  // dealt: they stand for the cost of a problem change in a workgroup):
-  // problem p = ((layer * batch + b) * H + hk) * n_hg + hg has n(b) = live(b)
-  // + padding chunks (0 for an empty sequence) from P(p) = layer * HG * S(B) +
+  // tokens, each problem followed by chunks of padding (never dealt: they
+  // stand for the cost of a problem change in a workgroup, kCrossingChunks,
+  // plus for a problem shorter than the mean range w0 the cost of the second
+  // group that a range holding it whole takes, kContainChunks (w0 - live) /
+  // w0): problem p = ((layer * batch + b) * H + hk) * n_hg + hg has n(b) =
+  // live(b) + padding chunks (0 for an empty sequence) from P(p) = layer * HG * S(B) +
   // HG * S(b) + (hk * n_hg + hg) * n(b), with HG = H * n_hg and S the prefix
   // of n (in LDS).
   // (All of it is uniform over the workgroup; values read from LDS are made
@@ -2243,15 +2245,25 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
     for (int b = tid; b < a.batch; b += NT) {
       int64_t st = a.seq_start[b], ln = a.seq_len[b];
       clamp_run(st, ln);
-      const int live = int((ln + kChunk - 1) / kChunk);
-      live_s[b + 1] = live > 0 ? live + kCrossingChunks : 0;
+      live_s[b + 1] = int((ln + kChunk - 1) / kChunk);
     }
     __syncthreads();
-    if (wave == 0) {   // inclusive prefix, 64 sequences at a time
+    const int64_t per_seq = int64_t(a.n_layers) * HG;
+    const int64_t nd = int64_t(nblk) - a.n_app;
+    if (wave == 0) {
+      // the live chunks of all sequences, and the mean range w0 over them
+      int sum = 0;
+      for (int b = lane; b < a.batch; b += 64) sum += live_s[b + 1];
+      for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+      const int64_t w0 = (per_seq * sum + nd - 1) / nd;   // >= 1 when any sequence has tokens
+      // padded counts, then their inclusive prefix, 64 sequences at a time
       int carry = 0;
       for (int b0 = 0; b0 < a.batch; b0 += 64) {
         const int b = b0 + lane;
-        int v = b < a.batch ? live_s[b + 1] : 0;
+        const int live = b < a.batch ? live_s[b + 1] : 0;
+        int v = 0;
+        if (live > 0)
+          v = live + kCrossingChunks + (live < w0 ? int(int64_t(kContainChunks) * (w0 - live) / w0) : 0);
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
           const int t = __shfl_up(v, o);
@@ -2260,20 +2272,18 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
         if (b < a.batch) live_s[b + 1] = carry + v;
         carry += __shfl(v, 63);
       }
-      if (lane == 0) live_s[0] = 0;
+      if (lane == 0) {
+        live_s[0] = 0;
+        counter[2] = uint32_t(sum);
+      }
     }
     __syncthreads();
     // ragged when the chunks that hold tokens are fewer than problems x cpp_real
-    int nonempty = 0;
-    for (int b = lane; b < a.batch; b += 64) nonempty += live_s[b + 1] != live_s[b] ? 1 : 0;
-    for (int o = 32; o > 0; o >>= 1) nonempty += __shfl_xor(nonempty, o);
-    nonempty = __builtin_amdgcn_readfirstlane(nonempty);
-    const int64_t per_seq = int64_t(a.n_layers) * HG;
     const int64_t padded_total = per_seq * lds_s(a.batch);
-    if (padded_total - per_seq * nonempty * kCrossingChunks < int64_t(a.total_chunks / cpp) * a.cpp_real) {
+    const int64_t live_total = per_seq * int64_t(__builtin_amdgcn_readfirstlane(counter[2]));
+    if (live_total < int64_t(a.total_chunks / cpp) * a.cpp_real) {
       rag = true;
       total = int(padded_total);
-      const int64_t nd = int64_t(nblk) - a.n_app;
       const int even = int((padded_total + nd - 1) / nd);
       cpw = even > a.cpw_min ? even : a.cpw_min;
     }
