@@ -95,3 +95,78 @@ def test_split_rejects_bad_sizes():
     fmt = tq.make_format(128, 4, 4)
     with pytest.raises(RuntimeError):
         tq.tq_decode_split(fmt, 1, 1, 4, 6, 10)
+
+
+# The ragged split the decode kernel builds for itself (batch > 1) from the
+# sequence lengths: each sequence's live chunks plus padding (16 chunks, plus
+# 160 (w0 - live) / w0 for a sequence shorter than the mean range w0), laid
+# out layer-major, then sequence, then KV head and head group; the decode
+# workgroups take equal ranges of that sequence, at least half the static
+# range long.  The constants restate the kernel's (kCrossingChunks,
+# kContainChunks).
+CROSSING, CONTAIN = 16, 160
+
+
+def _ragged_pieces_max(L, lens, H, HQ, T, nd=256):
+    n_hg = math.ceil(HQ // H / 8)
+    HG = H * n_hg
+    cpp = math.ceil(max(T, 1) / 32)
+    P = L * len(lens) * HG
+    wgs = min(math.ceil(P * cpp / 8), nd)
+    cpw_min = max(1, math.ceil(P * cpp / wgs) // 2)
+    live = [min(math.ceil(n / 32), cpp) for n in lens]
+    s = sum(live)
+    if L * HG * s >= P * cpp:
+        return None   # no sequence is short of max_len: the static split applies
+    w0 = math.ceil(L * HG * s / nd)
+    n = [lv + CROSSING + (CONTAIN * (w0 - lv) // w0 if lv < w0 else 0) if lv > 0 else 0 for lv in live]
+    total = L * HG * sum(n)
+    cpw = max(math.ceil(total / nd), cpw_min)
+    worst, first = 0, 0
+    for _layer in range(L):
+        for nb in n:
+            for _ in range(HG):
+                if nb > 0:
+                    worst = max(worst, (first + nb - 1) // cpw - first // cpw + 1)
+                first += nb
+    return worst
+
+
+def _ragged_batches(count, seed=1):
+    r = random.Random(seed)
+    out = []
+    for _ in range(count):
+        T = r.choice([64, 1000, 4096, 32768, 100000])
+        B = r.choice([2, 3, 16, 40, 200, 1024])
+        mode = r.choice(["uniform", "short", "one_long", "zeros"])
+        if mode == "uniform":
+            lens = [r.randint(0, T) for _ in range(B)]
+        elif mode == "short":
+            lens = [r.randint(1, max(1, T // 50)) for _ in range(B)]
+        elif mode == "one_long":
+            lens = [T] + [r.randint(1, 64) for _ in range(B - 1)]
+        else:
+            lens = [0 if r.random() < 0.7 else r.randint(1, T) for _ in range(B)]
+        h = r.choice([1, 4, 8])
+        out.append((r.randint(1, 3), lens, h, h * r.choice([1, 7, 8]), T))
+    return out
+
+
+@pytest.mark.parametrize("case", _ragged_batches(60))
+def test_ragged_split_pieces_fit_the_workspace(case):
+    """Whatever the length mix, no problem of the kernel's ragged split leaves
+    more pieces than the workspace has partial slots: the workspace holds
+    queries, counters, L x B x Hq x (most pieces) partials of d + 2 floats and
+    the per-workgroup wave-merge area after them."""
+    L, lens, H, HQ, T = case
+    worst = _ragged_pieces_max(L, lens, H, HQ, T)
+    if worst is None:
+        pytest.skip("every sequence fills max_len: static split")
+    fmt = tq.make_format(128, 4, 4)
+    B = len(lens)
+    sp = tq.tq_decode_split(fmt, L, B, H, HQ, T)
+    P = sp["problems"]
+    align = lambda x: (x + 255) // 256 * 256
+    need = (align(L * B * HQ * 2 * 128 * 4) + align((P + L + 1) * 4) + align(L * B * HQ * worst * (128 + 2) * 4)
+            + align(sp["n_workgroups"] * 8 * 8 * 128 * 4))
+    assert tq.tq_decode_workspace_bytes(fmt, L, B, H, HQ, T) >= need, (worst, sp)
