@@ -52,12 +52,40 @@ KERNEL_SOURCES = [os.path.join(ROOT, "kv_cache_quantization_norm_amd", "csrc", f
 D = 128
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without its comments and with whitespace runs collapsed,
+    so that an edit to comments alone leaves the digest unchanged (string
+    and character literals are kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_digest() -> str:
+    """sha256 of the kernel and host sources' code (comments and layout
+    excluded): the key under which committed counter summaries are valid."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 

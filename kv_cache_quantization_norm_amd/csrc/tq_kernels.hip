@@ -36,9 +36,18 @@
 //                          in the rotated domain (P x codes).  The workgroup
 //                          that writes a problem's last piece merges its
 //                          pieces and applies Pi^T (fp32 MFMA).
+//   decode_pair_kernel     the decode of two caches of different formats (a
+//                          compressed part and an fp16 part) in one launch:
+//                          the workgroups are split between the parts in
+//                          proportion to their bytes, each part dealt as by a
+//                          launch of its own; the LDS is the larger layout.
+//   qprep_pair_kernel      the query preparation of both parts, one launch.
+//   append_prepare_kernel  a step's append and its query preparation in one
+//                          launch.
 //   combine_kernel         the same merge as a launch of its own (staged calls).
 //   score_multi_kernel     multi-query scores: the key operands of a chunk
 //                          formed once per 64 query rows.
+//   stream_read_kernel     a plain streaming read, the bandwidth reference.
 //   tail_gather_kernel     the fp16 tail tokens a ring flush moves, gathered
 //                          for compression.
 #include <hip/hip_runtime.h>
