@@ -53,6 +53,11 @@ CASES = {
     # 320 short problems: several groups of pieces per workgroup
     "many_short_b40": wl.Workload("many_short_b40", 1, 8, 16, wl.ragged_lengths(39, 1, 200, seed=4) + (200,),
                                   3, 2, "f32", 0.3, 0, 1.0),
+    # ragged split with problems far shorter than the mean range: the short
+    # sequences' problems carry the largest padding (81 chunks against ranges
+    # of 23), so ranges hold them whole and some ranges hold padding only
+    # (pieces without tokens)
+    "pad_contain_b4": wl.Workload("pad_contain_b4", 1, 8, 64, (8000, 300, 300, 8000), 4, 4, "bf16", 0.5, 2, 10.0),
     # 8-bit keys (7 Lloyd-Max bits + QJL) with 4-bit values, the wide key path
     "k8v4_ragged": wl.Workload("k8v4_ragged", 2, 2, 14, (300, 77), 8, 4, "bf16", 0.5, 1, 10.0),
     "k8v2_f32": wl.Workload("k8v2_f32", 1, 4, 32, (129,), 8, 2, "f32", 0.0, 0, 1.0),
