@@ -124,6 +124,10 @@ __device__ __forceinline__ T bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 
 template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   // bound_ctrl set and every lane a valid source: the move can fold into the
   // arithmetic that consumes it (a DPP operand).
@@ -610,18 +614,26 @@ __global__ __launch_bounds__(kCompressWaves * 64) void compress_kernel(CompressA
       const int64_t gbytes = 4 * BV;  // bytes per (block, coordinate) group
       uint8_t* vplane = a.v_idx + plane * (a.capacity / kVBlock) * D * gbytes;
       if (contiguous && (BV == 2 || BV == 4)) {
-        // The wave owns whole dwords: 16 tokens x bv bits per coordinate.
-        const int dw = BV / 2;  // dwords per coordinate for 16 tokens
-        for (int e = lane; e < D * dw; e += 64) vrec[e] = 0u;
-        wave_sync();
+        // The wave owns whole dwords: 16 tokens x bv bits per coordinate.  The
+        // 32 / BV lanes of a dword (same q, consecutive t, inside one 16-lane
+        // row) OR their shifted codes together across lanes (DPP quad swaps,
+        // then the half-row and row mirrors), and the first of them stores
+        // the dword: no LDS atomics, no clearing pass.
+        const int dw = BV / 2;           // dwords per coordinate for 16 tokens
+        constexpr int TPW = 32 / BV;     // tokens per dword
+        const int tw = t & (TPW - 1);    // this token's place in its dword
+        const bool writer = tw == 0;
+        const int wsel = t / TPW;        // which dword of the coordinate
 #pragma unroll
         for (int tile = 0; tile < 8; ++tile)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint32_t idx = vidx[tile][r];
-            const int c = 16 * tile + 4 * q + r;
-            const int bit = t * BV;
-            atomicOr(&vrec[c * dw + (bit >> 5)], idx << (bit & 31));
+            uint32_t v = vidx[tile][r] << (BV * tw);
+            v |= dpp_u<0xB1>(v);    // quad_perm [1,0,3,2]
+            v |= dpp_u<0x4E>(v);    // quad_perm [2,3,0,1]
+            v |= dpp_u<0x141>(v);   // row_half_mirror: the 8-lane OR
+            if constexpr (BV == 2) v |= dpp_u<0x140>(v);   // row_mirror: the 16-lane OR
+            if (writer) vrec[(16 * tile + 4 * q + r) * dw + wsel] = v;
           }
         wave_sync();
         const int64_t s0 = a.slot0 + tok0;
