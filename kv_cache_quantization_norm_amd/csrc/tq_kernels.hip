@@ -231,9 +231,11 @@ constexpr int kCompressTile = 16;  // tokens per wave step
 constexpr int kCompressWaves = 8;
 constexpr int kCompressWorkgroups = 256;   // one per CU
 constexpr int kQBuckets = 512;
-// Key codes of up to 4 bits per record pack into 16 dwords a token, 7-bit
-// codes (8-bit keys) into 28.
-template <int MK> constexpr int kRecStride = MK > 4 ? 28 : 16;
+// Key codes of up to 4 bits pack into at most 16 dwords a token, 7-bit codes
+// (8-bit keys) into 28.  While a tile's records are assembled in LDS their
+// row stride is one dword more, odd, so that the 16 tokens fall in 16
+// different banks.
+template <int MK> constexpr int kRecStride = MK > 4 ? 29 : 17;
 struct CompressSmem {
   half8 ph[8 * 4 * 64], pl[8 * 4 * 64];
   half8 mh[8 * 4 * 64], ml[8 * 4 * 64];
@@ -242,7 +244,7 @@ struct CompressSmem {
   // Per wave: the packed key codes of 16 tokens (kRecStride dwords each),
   // later the value codes of 16 tokens per coordinate (2 D dwords); the key
   // records are written out before the values are coded.
-  uint32_t recv[kCompressWaves][kCompressTile * 28];
+  uint32_t recv[kCompressWaves][kCompressTile * 29];
   uint32_t srec[kCompressWaves][kCompressTile * 4];   // packed signs per token
 };
 
