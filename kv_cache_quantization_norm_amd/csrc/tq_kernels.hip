@@ -1029,7 +1029,9 @@ struct DecodeArgs {
   // call's new tokens (app_groups per layer, layers [app_layer0, app_layer0 +
   // app_layers) of the cache) and count themselves in app_done[layer]; a
   // decode wave about to load a chunk that holds one of the plane slots
-  // [app_lo, app_hi) of an appended layer first waits for that count.
+  // [app_lo, app_hi) of an appended layer first waits for that count.  With a
+  // slot list (the append's slots) the range is taken per sequence instead:
+  // from the first to the last listed slot inside the sequence's slots.
   int n_app, app_groups, app_layer0, app_layers;
   // The wait is bounded: after app_polls polls of the count (each followed by
   // a short sleep) the wave sets *app_flag (a sticky word of the workspace,
@@ -1576,8 +1578,25 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
     t1 = 0;
     if constexpr (!SCORE) {
       if (a.n_app == 0 || r.layer < a.app_layer0 || r.layer >= a.app_layer0 + a.app_layers) return;
-      const int64_t c0 = a.app_lo - r.start > 0 ? (a.app_lo - r.start) / kChunk : 0;
-      const int64_t c1 = a.app_hi - r.start > 0 ? (a.app_hi - r.start + kChunk - 1) / kChunk : 0;
+      int64_t lo_s = a.app_lo, hi_s = a.app_hi;
+      // (marked unlikely: laid out apart, the scan leaves the decode's code
+      // for contiguous appends as it was)
+      if (__builtin_expect(ca.slots != nullptr, 0)) {
+        // the listed slots inside this sequence (one scan per piece and group;
+        // a decode step's list holds a few tokens per sequence)
+        lo_s = INT64_MAX;
+        hi_s = 0;
+        for (int64_t i = 0; i < ca.n_tokens; ++i) {
+          const int64_t sl = ca.slots[i] + ca.slot_shift;
+          if (sl >= r.start && sl < r.start + r.len) {
+            lo_s = sl < lo_s ? sl : lo_s;
+            hi_s = sl + 1 > hi_s ? sl + 1 : hi_s;
+          }
+        }
+        if (hi_s == 0) return;   // none: no chunk of the piece waits
+      }
+      const int64_t c0 = lo_s - r.start > 0 ? (lo_s - r.start) / kChunk : 0;
+      const int64_t c1 = hi_s - r.start > 0 ? (hi_s - r.start + kChunk - 1) / kChunk : 0;
       const int64_t u0 = c0 + shift, u1 = c1 + shift;
       t0 = int(u0 < lo ? lo : (u0 > hi ? hi : u0));
       t1 = int(u1 < lo ? lo : (u1 > hi ? hi : u1));
