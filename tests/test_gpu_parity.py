@@ -480,6 +480,9 @@ def test_decode_steps_append_prepare_attend(k_bits, v_bits, hq, lens):
     ("slots", 4, 4, 16, (60, 33, 1, 0, 7, 300, 95, 64, 2, 18, 250, 77, 3, 40, 121, 9), 1, 0),   # 16 sequences
     ("slot0", 3, 2, 8, (100,), 40, 0),    # 40 appended workgroups: bulk compression, then the decode
     ("slots", 3, 3, 28, (300, 45, 0, 129), 1, 0),   # 3-bit values
+    # listed slots inside the sequences: each sequence's middle token rewritten,
+    # and sequence 0's first token too (its waits span several chunks)
+    ("slots_mid", 4, 4, 28, (300, 45, 0, 129), 1, 0),
 ])
 def test_decode_step_append_inside_decode_launch(mode, k_bits, v_bits, hq, lens, n_new, layer0):
     """tq_decode_step: the new tokens are compressed by the decode launch's
@@ -489,7 +492,8 @@ def test_decode_step_append_inside_decode_launch(mode, k_bits, v_bits, hq, lens,
     new tokens).  Cases: one token per sequence through a slots array (any
     slot may change), consecutive slots from slot0 (new tokens in the first
     chunk of a 5-token sequence, or crossing into a new chunk), fp16 keys or
-    values, and an append to layer 1 only of a 2-layer cache."""
+    values, an append to layer 1 only of a 2-layer cache, and tokens rewritten
+    inside the sequences (the middle one of each, and the first of sequence 0)."""
     import kv_cache_quantization_norm_amd as tq
     _say("decode step", mode, k_bits, v_bits, hq, lens, n_new, layer0)
     L, H, steps, stride = 2, 4, 3, 320
@@ -514,7 +518,13 @@ def test_decode_step_append_inside_decode_launch(mode, k_bits, v_bits, hq, lens,
     worst = 0.0
     for step in range(steps):
         Q = torch.randn(L, B, hq, 128, generator=g).cuda()
-        if mode == "slots":
+        if mode == "slots_mid":
+            lst = [starts[b] + cur[b] // 2 if cur[b] else -1 for b in range(B)] + [starts[0] if cur[0] else -1]
+            slots = torch.tensor(lst, dtype=torch.int64, device="cuda")
+            kn = torch.randn(n_app_layers, len(lst), H, 128, generator=g).to("cuda", torch.bfloat16)
+            vn = torch.randn(n_app_layers, len(lst), H, 128, generator=g).to("cuda", torch.bfloat16)
+            extra = dict(slots=slots)
+        elif mode == "slots":
             slots = torch.tensor([starts[b] + cur[b] if cur[b] else -1 for b in range(B)], dtype=torch.int64,
                                  device="cuda")
             kn = torch.randn(n_app_layers, B, H, 128, generator=g).to("cuda", torch.bfloat16)
