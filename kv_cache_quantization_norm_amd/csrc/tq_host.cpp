@@ -79,7 +79,7 @@ SplitPlan plan_decode(int d, int n_layers, int batch, int n_kv_heads, int n_q_he
   // whose sequences fill at least half of max_len is split evenly).
   p.cpp_real = cpp;
   p.cpw_min = cpw_b / 2 > 1 ? cpw_b / 2 : 1;
-  const int64_t pad_max = kCrossingChunks + kContainChunks;
+  const int64_t pad_max = kRaggedCrossChunks + kContainChunks;
   const int64_t seg_r = batch > 1 ? (cpp + pad_max - 1 + p.cpw_min - 1) / p.cpw_min + 1 : 0;
   p.seg_cap = seg_r > p.seg_max ? seg_r : p.seg_max;
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };

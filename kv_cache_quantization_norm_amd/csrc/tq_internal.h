@@ -18,6 +18,12 @@ constexpr int kDecodeWaves = 8;  // waves per decode workgroup (one workgroup pe
 constexpr int kDecodeWorkgroups = 256;   // decode workgroups: one per CU of an MI355X
 constexpr int kMaxGroup = 8;     // query heads handled by one decode wave
 constexpr int kCrossingChunks = 16;   // measured cost of a problem change inside a decode workgroup, in chunks
+// The ragged split's padding per problem (its share of a problem change: a
+// second piece's merge and pipeline start).  Set apart from kCrossingChunks,
+// which decides the static splits: per-workgroup timings on a 16-sequence
+// ragged batch of 4 k - 32 k tokens put the change's cost there higher, and
+// 16 -> 32 took its decode from 116 to 114 us and its step from 132 to 127 us.
+constexpr int kRaggedCrossChunks = 32;
 // Ragged split: a problem shorter than the mean range is charged up to
 // kContainChunks more, in proportion to how much shorter it is (a range that
 // holds a problem whole, with pieces of others on both sides, takes a second
@@ -49,7 +55,7 @@ struct SplitPlan {
   int n_head_groups = 0;
   // Ragged split (decided by the kernel from the sequence lengths, batch > 1):
   // the workgroups share the chunks that hold tokens (each problem followed
-  // by kCrossingChunks to kCrossingChunks + kContainChunks of padding), in
+  // by kRaggedCrossChunks to kRaggedCrossChunks + kContainChunks of padding), in
   // ranges of at least cpw_min chunks, so that a problem (at most cpp_real =
   // ceil(max_len / 32) chunks plus the padding) leaves at most seg_cap
   // pieces; seg_cap >= seg_max is the partial slots per query head in the

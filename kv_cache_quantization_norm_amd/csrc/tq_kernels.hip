@@ -1481,7 +1481,7 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
   // ---- the chunk sequence dealt to the workgroups in ranges of cpw: every
   // problem's cpp chunks, problem-major; or (rag) only the chunks that hold
   // tokens, each problem followed by chunks of padding (never dealt: they
-  // stand for the cost of a problem change in a workgroup, kCrossingChunks,
+  // stand for the cost of a problem change in a workgroup, kRaggedCrossChunks,
   // plus for a problem shorter than the mean range w0 the cost of the second
   // group that a range holding it whole takes, kContainChunks (w0 - live) /
   // w0): problem p = ((layer * batch + b) * H + hk) * n_hg + hg has n(b) =
@@ -2305,7 +2305,7 @@ __device__ __forceinline__ void decode_body(DecodeArgs a, CompressArgs ca, unsig
         const int live = b < a.batch ? live_s[b + 1] : 0;
         int v = 0;
         if (live > 0)
-          v = live + kCrossingChunks + (live < w0 ? int(int64_t(kContainChunks) * (w0 - live) / w0) : 0);
+          v = live + kRaggedCrossChunks + (live < w0 ? int(int64_t(kContainChunks) * (w0 - live) / w0) : 0);
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
           const int t = __shfl_up(v, o);

@@ -98,13 +98,13 @@ def test_split_rejects_bad_sizes():
 
 
 # The ragged split the decode kernel builds for itself (batch > 1) from the
-# sequence lengths: each sequence's live chunks plus padding (16 chunks, plus
+# sequence lengths: each sequence's live chunks plus padding (32 chunks, plus
 # 160 (w0 - live) / w0 for a sequence shorter than the mean range w0), laid
 # out layer-major, then sequence, then KV head and head group; the decode
 # workgroups take equal ranges of that sequence, at least half the static
-# range long.  The constants restate the kernel's (kCrossingChunks,
+# range long.  The constants restate the kernel's (kRaggedCrossChunks,
 # kContainChunks).
-CROSSING, CONTAIN = 16, 160
+CROSSING, CONTAIN = 32, 160
 
 
 def _ragged_pieces_max(L, lens, H, HQ, T, nd=256):
